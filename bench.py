@@ -1,0 +1,204 @@
+"""Benchmark of the DiT forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
+
+One step is one full DiT forward (every block, with the projections in and
+out) over one batch of seeded synthetic input whose weights and inputs were
+staged to HBM before timing.  The default workload is the music-style fp32
+acoustic DiT (24 blocks, hidden 2560, 20 heads x 128, ffn 10240, LayerNorm,
+partial rotary on 64 dims, 2 CFG branches x 86 frames = 172 tokens): the
+configuration the pages time (page "the 2.4B fp32 DiT onto the device, staged
+once", section "Speed").
+
+Prints one JSON line.  `value` is tokens per second (tokens of the batch /
+seconds per forward); `roofline` reports the kernel family that takes the most
+device time, from per-launch HIP events recorded on the launch stream during a
+second pass of K forwards; `cpu_baseline` times the CPU oracle on a bounded
+sample (a few blocks) of the same workload and scales it to a whole forward.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "ms per DiT forward + tokens/s at 1 GPU; % of MFMA / HBM peak"
+# MI355X published peaks.
+PEAK = {"mfma_f64": 78.6, "mfma_bf16": 2500.0, "mfma_f32": 157.3, "hbm_gbs": 8000.0}
+GEMM_FAMILY_PEAK = {"gemm_f32": ("mfma_f64", "f64 MFMA: fp32 operands, fp64 accumulation"),
+                    "gemm_bf16": ("mfma_bf16", "bf16 MFMA"),
+                    "attention_bf16": ("mfma_bf16", "bf16 MFMA")}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def gemm_shapes(cfg):
+    """(M, N, K) of every GEMM launch of one forward, in launch order."""
+    N = cfg.n_tokens
+    D, F = cfg.hidden, cfg.ffn
+    out = []
+    if cfg.io:
+        for s in cfg.segments:
+            out.append((s.n_tokens, D, cfg.modalities[s.modality].token_width))
+    for _ in range(cfg.n_blocks):
+        out += [(N, 3 * D, D), (N, D, D), (N, 2 * F, D), (N, D, F)]
+    if cfg.io:
+        for s in cfg.segments:
+            out.append((s.n_tokens, cfg.modalities[s.modality].token_width, D))
+    return out
+
+
+def attention_flops(cfg):
+    per_block = 4 * cfg.head_dim * cfg.n_heads * sum(s.n_tokens ** 2 for s in cfg.segments)
+    return per_block * cfg.n_blocks
+
+
+def cpu_baseline(cfg, weights_fn, islands, inp, sample_blocks: int, log=log):
+    """Time the oracle on `sample_blocks` blocks of this workload and scale to a forward."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    mode = "bf16" if cfg.stream == "bf16" else "fp64"
+    lay = O.pack_layout(cfg)
+    cos, sin = O.rope_cache(cfg)
+    if cfg.cond_kind == "timestep":
+        emb = O.cond_embeddings(cfg, [float(inp["t"][r.source]) for r in cfg.cond_rows])
+    else:
+        emb = O.cond_embeddings(cfg, None, inp["cond"])
+    x = np.random.default_rng(0).standard_normal((cfg.n_tokens, cfg.hidden))
+    ws = [weights_fn(b) for b in range(sample_blocks)]
+    t0 = time.perf_counter()
+    for b in range(sample_blocks):
+        mod = O.adaln_table(cfg, ws[b], b, emb, mode)
+        x = O.block_forward(cfg, x, mod, ws[b], b, lay, cos, sin, mode, threads=min(cores, 16))
+    dt = time.perf_counter() - t0
+    per_forward = dt / sample_blocks * cfg.n_blocks
+    log(f"cpu oracle: {sample_blocks} blocks in {dt:.2f}s -> {per_forward:.2f}s per forward")
+    return {"value": cfg.n_tokens / per_forward, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{sample_blocks} of {cfg.n_blocks} blocks ({mode}, numpy/OpenBLAS), "
+                      f"{dt:.2f}s, scaled x{cfg.n_blocks / sample_blocks:.1f} to one forward "
+                      f"({per_forward:.1f}s)"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-blocks", type=int, default=4)
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported by this build "
+              "(the path runs on a single device)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synthetic as S
+    from video_audio_gen_amd import dit, harness
+
+    cfg = S.get_config(a.workload)
+    dev = torch.cuda.get_device_name(0)
+    log(f"workload {cfg.name}: {cfg.n_blocks} blocks, hidden {cfg.hidden}, {cfg.n_tokens} tokens on {dev}")
+    t0 = time.time()
+    model = harness.stage_model(cfg, threads=16, log=log)
+    log(f"staged {model.weight_bytes / 1e9:.2f} GB of weights in {time.time() - t0:.1f}s")
+    r = harness.Runner(cfg, model=model)
+    torch.cuda.synchronize()
+
+    for _ in range(a.warmup):
+        r.forward()
+    torch.cuda.synchronize()
+    log(f"warmup {a.warmup} done")
+
+    # timed region: exactly K forwards between two synchronisations
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(a.steps):
+        r.forward()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(stop) / a.steps
+    log(f"timed {a.steps} forwards: {ms:.3f} ms per forward (host wall {wall * 1e3 / a.steps:.3f} ms)")
+
+    # per-kernel device time: HIP events recorded around every launch on its stream
+    dit.dit_profile_begin()
+    for _ in range(a.steps):
+        r.forward()
+    prof = dit.dit_profile_end()
+    total_dev = sum(v[1] for v in prof.values())
+    for k, (n, t) in sorted(prof.items(), key=lambda kv: -kv[1][1]):
+        if n:
+            log(f"  {k:16s} launches {n:6d}  total {t:9.3f} ms  avg {t / n * 1e3:9.2f} us  "
+                f"share {t / total_dev * 100:5.1f}%")
+    fam = max(prof.items(), key=lambda kv: kv[1][1])[0]
+    n_launch, fam_ms = prof[fam]
+    if fam in ("gemm_f32", "gemm_bf16"):
+        flops = sum(2.0 * m * n * k for m, n, k in gemm_shapes(cfg)) * a.steps
+        peak_key, peak_note = GEMM_FAMILY_PEAK[fam]
+        achieved = flops / (fam_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK[peak_key], "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK[peak_key], 4), "traffic": None, "kernel": fam,
+                "launches": n_launch, "avg_launch_us": round(fam_ms / n_launch * 1e3, 2), "peak_kind": peak_note}
+    elif fam == "attention_bf16":
+        flops = attention_flops(cfg) * a.steps
+        achieved = flops / (fam_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK["mfma_bf16"], "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK["mfma_bf16"], 4), "traffic": None, "kernel": fam,
+                "launches": n_launch, "avg_launch_us": round(fam_ms / n_launch * 1e3, 2)}
+    else:
+        roof = {"bound": "unknown", "achieved": None, "peak": None, "unit": None, "frac": None,
+                "traffic": None, "kernel": fam}
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        import oracle  # noqa: F401
+        cpu = cpu_baseline(cfg, lambda b: S.block_weights(cfg, b, threads=8), None, r.inp,
+                           min(a.cpu_sample_blocks, cfg.n_blocks))
+
+    tokens = cfg.n_tokens
+    line = {
+        "metric": METRIC,
+        "value": round(tokens / (ms * 1e-3), 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if cfg.stream == "f32" else "bf16",
+        "data": "synthetic (seeded; weights N(0,0.02), random init)",
+        "config": {"workload": cfg.name, "n_blocks": cfg.n_blocks, "hidden": cfg.hidden,
+                   "heads": cfg.n_heads, "head_dim": cfg.head_dim, "ffn": cfg.ffn,
+                   "tokens": tokens, "documents": [s.n_tokens for s in cfg.segments],
+                   "device": dev},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,302 @@
+/*
+ * dit.h -- C ABI of the MI355X (gfx950) diffusion-transformer block forward.
+ *
+ * The library computes the non-causal DiT block that a diffusion denoise loop
+ * runs at every step: AdaLN shift/scale/gate modulation around RMSNorm or
+ * LayerNorm, a fused QKV GEMM, NeoX rotate_half RoPE from a per-row cos/sin
+ * cache, packed varlen non-causal attention over cu_seqlens, the output
+ * projection, a gated residual, a gated-SiLU MLP and a second gated residual
+ * (page "port the MiniMax-H3 omni-modal video+audio DiT", section "The
+ * device-resident forward (W2b)"; page "the 2.4B fp32 DiT onto the device,
+ * staged once", section "What moved, and onto what").
+ *
+ * Conventions for every call:
+ *   - Every function returns a dit_status.  Nothing aborts the process and no
+ *     C++ exception crosses this boundary; dit_last_error() gives a message
+ *     naming the offending argument or tensor (thread-local).
+ *   - "dev" pointers are HIP device pointers on the current device; "host"
+ *     pointers are ordinary host memory.  The library allocates no device
+ *     memory: weights live in a caller-allocated slab, batch tables in a
+ *     caller-allocated buffer, scratch in a caller-allocated workspace.
+ *   - Device work is enqueued on the hipStream_t passed in (NULL = the default
+ *     stream) and is asynchronous; no forward call synchronises the host.
+ *     Host buffers passed to staging calls are copied before those calls return.
+ *   - Matrices are row-major.  Weights use the nn.Linear layout [out, in].
+ *   - A sticky HIP error (for example an illegal address) is reported as
+ *     DIT_E_HIP; the device context is then unusable and there is no recovery.
+ */
+#ifndef DIT_H
+#define DIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* dit_stream_t; /* same type as hipStream_t */
+
+typedef enum dit_status {
+  DIT_OK = 0,
+  DIT_E_INVALID = 1,        /* a bad argument; the message names it */
+  DIT_E_STATE = 2,          /* call out of order (stage after finalize, forward before finalize) */
+  DIT_E_UNKNOWN_WEIGHT = 3, /* staging a name outside the weight contract */
+  DIT_E_SHAPE = 4,          /* a weight's shape differs from the contract */
+  DIT_E_DTYPE = 5,          /* a weight's dtype cannot be staged into its slot */
+  DIT_E_MISSING_WEIGHT = 6, /* finalize found a tensor never staged; the message names it */
+  DIT_E_WORKSPACE = 7,      /* a caller buffer is smaller than the required size */
+  DIT_E_HIP = 8,            /* a HIP runtime error */
+  DIT_E_UNSUPPORTED = 9     /* a shape outside what the kernels handle (message says which) */
+} dit_status;
+
+enum { DIT_F32 = 0, DIT_BF16 = 1 };
+enum { DIT_NORM_RMS = 0, DIT_NORM_LAYER = 1 };
+enum { DIT_MLP_GATE_UP = 0, DIT_MLP_VALUE_GATE = 1 };
+enum { DIT_IO_NONE = 0, DIT_IO_PATCH3D = 1, DIT_IO_CHANNEL_MAJOR = 2 };
+
+#define DIT_MAX_MODALITIES 4
+#define DIT_MAX_SEGMENTS 64
+#define DIT_MAX_COND 64
+
+/* One modality: its in/out projection geometry and its rope axes. */
+typedef struct dit_modality {
+  int io;          /* DIT_IO_*; must be DIT_IO_NONE iff dit_config.io == 0 */
+  int channels;    /* latent channels C */
+  int patch[3];    /* (pt, ph, pw) for DIT_IO_PATCH3D, else (1,1,1) */
+  int n_axes;      /* 1 or 3 position axes */
+  int axis_dim[3]; /* rotary sub-dimension per axis; sums to rot_dim; each even */
+} dit_modality;
+
+/* Model shape.  All fields are read at dit_model_create and copied. */
+typedef struct dit_config {
+  int n_blocks, hidden, n_heads, head_dim, ffn;
+  int norm;          /* DIT_NORM_*: row norm without affine weights */
+  float norm_eps;
+  int mlp;           /* DIT_MLP_GATE_UP: mlp.in rows are [gate | up];
+                        DIT_MLP_VALUE_GATE: [value | gate], swapped at stage time */
+  int rot_dim;       /* rotary dims at the start of each head (<= head_dim, even) */
+  double theta;      /* rope base */
+  int stream_dtype;  /* DIT_F32 or DIT_BF16: dtype of block weights and of the GEMM operands */
+  int cond_dim;      /* width d_t of the conditioning vector feeding the AdaLN linears */
+  int n_mod;         /* modalities (one AdaLN linear and one projection pair each) */
+  int io;            /* 1: latents in / velocities out through fp32 projections; 0: tokens in/out */
+  dit_modality mod[DIT_MAX_MODALITIES];
+} dit_config;
+
+/* One document of a packed batch: a contiguous run of tokens of one modality
+ * with one position grid and one modulation row.  Tokens are counted by the
+ * grid: grid[0] (1 axis) or grid[0]*grid[1]*grid[2] (3 axes, raster order with
+ * the last axis fastest).  Segments are packed end to end in array order. */
+typedef struct dit_segment {
+  int modality;  /* index into dit_config.mod */
+  int cond_row;  /* modulation row of every token in the segment */
+  int grid[3];   /* token grid; unused axes 1 */
+} dit_segment;
+
+/* ------------------------------------------------------------------ host builders
+ * Pure host functions: no device, no allocation.  Each is the single source of
+ * the table it builds; the forward uses exactly these values. */
+
+/* Packed layout (page "port the MiniMax-H3 omni-modal video+audio DiT", section
+ * "Correctness gates": packed layout gated exact).  Writes cu_seqlens[n_segs+1]
+ * (running token offsets), cond_idx[N] and doc_id[N]; *n_tokens = N.  Pass NULL
+ * for cond_idx/doc_id to get only N and cu_seqlens.  DIT_E_INVALID for a
+ * non-positive extent, a segment count outside [1, DIT_MAX_SEGMENTS] or N >= 2^31. */
+int dit_pack_layout(const dit_config* cfg, const dit_segment* segs, int n_segs,
+                    int32_t* cu_seqlens, int32_t* cond_idx, int32_t* doc_id, int* n_tokens);
+
+/* Per-row rope cache cos/sin [N, rot_dim/2] float32 (page "stream the ORIGINAL
+ * bf16 DiT to the device", section "What this enables": built on the host
+ * before any kernel).  Integer positions restart at 0 in each segment; the
+ * angle of row n, column j is pos_a(n) * inv_freq_a[j'] for the axis block a
+ * holding j, inv_freq_a[j'] = 1 / theta^(2j'/axis_dim[a]); cos and sin in fp64,
+ * rounded once to float32.  Caller owns both outputs (N * rot_dim/2 floats each). */
+int dit_rope_cache_build(const dit_config* cfg, const dit_segment* segs, int n_segs,
+                         float* cos_host, float* sin_host);
+
+/* Sinusoidal timestep embedding: out[i, j] = cos(t_i f_j), out[i, dim/2 + j] =
+ * sin(t_i f_j), f_j = 10000^(-j/(dim/2)), fp64 math, float32 out [n, dim]. */
+int dit_timestep_embedding(const float* t_host, int n, int dim, float* out_host);
+
+/* Time-shifted rectified-flow sigmas: s_i = 1 - i/n_steps,
+ * sigma_i = shift s_i / (1 + (shift - 1) s_i), i = 0..n_steps (fp64), and
+ * dt_i = float32(sigma_{i+1} - sigma_i), i < n_steps.  Either output may be NULL. */
+int dit_sigma_schedule(double shift, int n_steps, double* sigma_host, float* dt_host);
+
+/* ------------------------------------------------------------------ model and staging */
+
+typedef struct dit_model dit_model;
+
+typedef struct dit_weight_view {
+  const char* name;     /* weight-name contract below */
+  int dtype;            /* DIT_F32 or DIT_BF16 (bf16 as raw uint16 bits) */
+  int ndim;
+  int64_t shape[4];
+  const void* host;     /* host data, row-major, caller-owned */
+} dit_weight_view;
+
+typedef struct dit_stage_stats_t {
+  int64_t tensors;      /* tensors staged */
+  int64_t bytes;        /* device bytes written */
+  int64_t direct;       /* staged without conversion */
+  int64_t converted;    /* converted on the host (f32 -> bf16 RNE, bf16 -> f32, half swap) */
+  int64_t host_peak;    /* largest host conversion buffer held at once (one tensor) */
+} dit_stage_stats_t;
+
+/* Bytes of the weight slab for this config (256-byte aligned views). */
+int dit_weight_bytes(const dit_config* cfg, size_t* bytes);
+
+/* Validate cfg and bind a caller-owned device slab of at least dit_weight_bytes.
+ * The handle is library-owned (free with dit_model_destroy); the slab is not. */
+int dit_model_create(const dit_config* cfg, void* weight_slab_dev, size_t slab_bytes,
+                     dit_model** out);
+void dit_model_destroy(dit_model* m);
+
+/* Stage weights, any subset per call, each name at most once.  Weight-name
+ * contract (nn.Linear layout [out, in]; D hidden, F ffn, d cond_dim, c_m the
+ * token width of modality m = C*pt*ph*pw or C):
+ *   blocks.{b}.adaln.{m}.weight [6D, d]   blocks.{b}.adaln.{m}.bias [6D]
+ *   blocks.{b}.attn.qkv.weight  [3D, D]   rows [q_all | k_all | v_all]
+ *   blocks.{b}.attn.qkv.bias    [3D]
+ *   blocks.{b}.attn.out.weight  [D, D]    blocks.{b}.attn.out.bias [D]
+ *   blocks.{b}.mlp.in.weight    [2F, D]   blocks.{b}.mlp.in.bias [2F]
+ *   blocks.{b}.mlp.out.weight   [D, F]    blocks.{b}.mlp.out.bias [D]
+ *   in.{m}.weight [D, c_m]  in.{m}.bias [D]  out.{m}.weight [c_m, D]  out.{m}.bias [c_m]
+ * Block weight matrices are stored in the stream dtype (an f32 view for a bf16
+ * stream is rounded to nearest-even on the host through one tensor-sized
+ * buffer); biases and the projections in and out stay float32 ("fp32 islands",
+ * page "port the MiniMax-H3 omni-modal video+audio DiT", update "quantized arms
+ * land").  For DIT_MLP_VALUE_GATE the two row halves of mlp.in are swapped so
+ * the kernel computes silu(first) * second (page "the 2.4B fp32 DiT onto the
+ * device, staged once", section "What moved").  Copies are synchronous on
+ * `stream`.  Errors: DIT_E_UNKNOWN_WEIGHT, DIT_E_SHAPE, DIT_E_DTYPE (named),
+ * DIT_E_STATE after finalize, DIT_E_INVALID for a repeat. */
+int dit_stage_weights(dit_model* m, const dit_weight_view* views, int n, dit_stream_t stream);
+
+/* Close staging.  DIT_E_MISSING_WEIGHT names the first tensor never staged. */
+int dit_stage_finalize(dit_model* m);
+int dit_stage_stats(const dit_model* m, dit_stage_stats_t* out);
+
+/* ------------------------------------------------------------------ batch */
+
+typedef struct dit_batch dit_batch;
+
+/* Device bytes of the batch tables (cu_seqlens, cond_idx, cos, sin, segment
+ * table) for these segments. */
+int dit_batch_bytes(const dit_model* m, const dit_segment* segs, int n_segs, size_t* bytes);
+
+/* Build the batch on the host (layout, rope cache) and copy it into the
+ * caller's device buffer `tables_dev` (synchronous on `stream`).  n_cond rows of
+ * modulation; cond_modality[c] selects the AdaLN linear of row c.  The handle
+ * is library-owned; free with dit_batch_destroy.  The buffer must outlive it. */
+int dit_batch_create(const dit_model* m, const dit_segment* segs, int n_segs, int n_cond,
+                     const int* cond_modality, void* tables_dev, size_t tables_bytes,
+                     dit_stream_t stream, dit_batch** out);
+void dit_batch_destroy(dit_batch* b);
+/* N, number of segments, longest segment; latent floats of the whole batch
+ * (sum over segments of C*T*pt*H*ph*W*pw or C*L; 0 without io). */
+int dit_batch_info(const dit_batch* b, int* n_tokens, int* n_segs, int* max_seqlen,
+                   int64_t* latent_floats);
+/* Device pointers into the batch tables (for callers driving the op-level calls). */
+int dit_batch_tables(const dit_batch* b, const int32_t** cu_seqlens_dev,
+                     const int32_t** cond_idx_dev, const float** cos_dev, const float** sin_dev);
+
+/* Workspace bytes that dit_block_forward / dit_forward / dit_denoise_step need. */
+int dit_workspace_bytes(const dit_model* m, const dit_batch* b, size_t* bytes);
+
+/* ------------------------------------------------------------------ forward */
+
+/* AdaLN table of blocks [block0, block0 + n_blocks): mod[b][c][k][D] =
+ * (W_ada[b][cond_modality[c]] . cond[c] + bias)[k*D + j], k = shift_msa,
+ * scale_msa, gate_msa, shift_mlp, scale_mlp, gate_mlp.  cond_dev [n_cond,
+ * cond_dim] float32 (an embedded timestep or a conditioning vector); mod_dev
+ * [n_blocks, n_cond, 6, D] float32. */
+int dit_modulation(dit_model* m, const dit_batch* b, int block0, int n_blocks,
+                   const float* cond_dev, float* mod_dev, dit_stream_t stream);
+
+/* One block on the packed residual stream x_dev [N, D] float32, in place.
+ * mod_dev [n_cond, 6, D] float32 (this block's rows of dit_modulation). */
+int dit_block_forward(dit_model* m, int block, float* x_dev, const float* mod_dev,
+                      const dit_batch* b, void* ws_dev, size_t ws_bytes, dit_stream_t stream);
+
+/* The whole forward.  With io: in_dev holds every segment's latent, segment
+ * after segment ([C, T*pt, H*ph, W*pw] or [C, L], float32); out_dev receives
+ * the velocities in the same layout.  Without io: in_dev is tokens [N, D]
+ * float32 and out_dev the tokens after the last block.  cond_dev as in
+ * dit_modulation.  in_dev and out_dev may alias. */
+int dit_forward(dit_model* m, const dit_batch* b, const float* in_dev, const float* cond_dev,
+                float* out_dev, void* ws_dev, size_t ws_bytes, dit_stream_t stream);
+
+/* One Euler step of the denoise loop, device-resident: v = dit_forward(latents,
+ * cond), then latents += dt[modality] * v per segment, in float32 without
+ * contraction (euler eta=0 with rf_v_to_x0 reduces to this; page "port the
+ * MiniMax-H3 omni-modal video+audio DiT", milestone "the whole t2va path
+ * composes end to end").  dt_dev [n_mod] float32.  Requires io. */
+int dit_denoise_step(dit_model* m, const dit_batch* b, float* latents_dev, const float* cond_dev,
+                     const float* dt_dev, void* ws_dev, size_t ws_bytes, dit_stream_t stream);
+
+/* n_steps consecutive steps with no host round trip: step i reads
+ * cond_table_dev + i*n_cond*cond_dim and dt_table_dev + i*n_mod. */
+int dit_denoise_loop(dit_model* m, const dit_batch* b, float* latents_dev,
+                     const float* cond_table_dev, const float* dt_table_dev, int n_steps,
+                     void* ws_dev, size_t ws_bytes, dit_stream_t stream);
+
+/* ------------------------------------------------------------------ op-level calls
+ * The kernels the block is made of, exposed for per-op parity checks and
+ * timing.  dtype arguments are DIT_F32 or DIT_BF16 (bf16 = uint16 bits). */
+
+/* C[M,N] = A[M,K] . B[N,K]^T + bias[N] (bias may be NULL).  bf16: A, B bf16,
+ * fp32 accumulation, C in c_dtype.  f32: A, B float32, products exact and sums
+ * in fp64, C float32 (rounded once).  ws is split-K scratch
+ * (dit_gemm_workspace_bytes). */
+int dit_gemm_workspace_bytes(int dtype, int M, int N, int K, size_t* bytes);
+int dit_gemm(int dtype, int M, int N, int K, const void* A, const void* B, const float* bias,
+             void* C, int c_dtype, void* ws, size_t ws_bytes, dit_stream_t stream);
+
+/* h[N,D] (dtype) = norm(x[N,D] f32) * (1 + mod[c][scale_k]) + mod[c][shift_k],
+ * c = cond_idx[n]; mod [n_cond, 6, D] f32; which = 0 (msa: shift 0, scale 1) or
+ * 1 (mlp: shift 3, scale 4); mod NULL = plain norm.  norm = DIT_NORM_*. */
+int dit_modnorm(int dtype, int norm, float eps, int N, int D, const float* x, const float* mod,
+                int which, const int32_t* cond_idx, void* h, dit_stream_t stream);
+
+/* qkv [N, 3D] (dtype) -> q, k, v head-major [H, N, hd] (dtype); rotate_half
+ * RoPE on the first rot dims of q and k from cos/sin [N, rot/2]; v copied. */
+int dit_rope_split(int dtype, int N, int H, int hd, int rot, const void* qkv, const float* cos,
+                   const float* sin, void* q, void* k, void* v, dit_stream_t stream);
+
+/* o [N, H*hd] (dtype) = per-document softmax(q k^T / sqrt(hd)) v; q, k, v
+ * head-major [H, N, hd]; cu_seqlens [n_docs+1] device, max_seqlen its
+ * largest gap. */
+int dit_attention(int dtype, int N, int H, int hd, int n_docs, const int32_t* cu_seqlens,
+                  int max_seqlen, const void* q, const void* k, const void* v, void* o,
+                  dit_stream_t stream);
+
+/* m [N, F] (dtype) = silu(u[:, :F]) * u[:, F:]; u [N, 2F] (dtype). */
+int dit_silu_gate(int dtype, int N, int F, const void* u, void* m, dit_stream_t stream);
+
+/* x[N,D] f32 += mod[c][gate_k] * a[N,D] f32, c = cond_idx[n]; which 0 (gate 2) or 1 (gate 5). */
+int dit_gated_residual(int N, int D, float* x, const float* a, const float* mod, int which,
+                       const int32_t* cond_idx, dit_stream_t stream);
+
+/* ------------------------------------------------------------------ diagnostics */
+
+const char* dit_last_error(void);
+/* Launch counters per kernel family (index order: gemm_bf16, gemm_f32, attention_bf16,
+ * attention_f32, modnorm, rope_split, silu_gate, gated_residual, adaln, patch_in,
+ * patch_out, euler, gemm_f32_reduce); n_max entries written; returns DIT_OK. */
+int dit_counters(int64_t* out, int n_max);
+void dit_counters_reset(void);
+
+/* Per-kernel timing.  Between dit_profile_begin and dit_profile_end every
+ * launch records a HIP event pair around itself on its own stream (a few
+ * microseconds of host time per launch).  dit_profile_end waits for those
+ * events and writes, per kernel family (index order as dit_counters), the
+ * number of launches and their summed device time in milliseconds. */
+int dit_profile_begin(void);
+int dit_profile_end(int64_t* counts, double* total_ms, int n_max);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DIT_H */

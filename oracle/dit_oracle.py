@@ -56,7 +56,7 @@ __all__ = [
     "timestep_embedding", "cond_embeddings", "norm", "modulate", "linear", "apply_rope",
     "attention_varlen", "attention_dense_masked", "silu", "adaln_table", "block_forward",
     "patchify", "unpatchify", "forward", "sigma_schedule", "sigma_dt", "euler_step",
-    "denoise_step_conditions", "split_mlp",
+    "denoise_step_conditions", "denoise_loop", "split_mlp",
 ]
 
 
@@ -262,9 +262,17 @@ def modulate(y: np.ndarray, shift: np.ndarray, scale: np.ndarray) -> np.ndarray:
     return y * (1.0 + scale) + shift
 
 
-def linear(x: np.ndarray, W: np.ndarray, b: np.ndarray) -> np.ndarray:
+def linear(x: np.ndarray, W: np.ndarray, b: np.ndarray, accum: str = "fp64") -> np.ndarray:
     """y = x W^T + b with W in nn.Linear layout [out, in] (MatmulBT plus a rank-1 bias add,
-    page "the 2.4B fp32 DiT onto the device, staged once", section "What moved")."""
+    page "the 2.4B fp32 DiT onto the device, staged once", section "What moved").
+
+    accum='fp32' runs the product in float32 (numpy's sgemm) instead: the
+    control arm, a second valid accumulation order used to measure how far two
+    correct implementations drift apart through the storage roundings.
+    """
+    if accum == "fp32":
+        y = np.asarray(x, np.float32) @ np.asarray(W, np.float32).T
+        return y.astype(np.float64) + np.asarray(b, np.float64)
     return np.asarray(x, np.float64) @ np.asarray(W, np.float64).T + np.asarray(b, np.float64)
 
 
@@ -373,7 +381,8 @@ def split_mlp(u: np.ndarray, mlp: str, F: int) -> np.ndarray:
 
 def block_forward(cfg, x: np.ndarray, mod: np.ndarray, bw: Dict[str, np.ndarray], b: int,
                   layout: Dict[str, np.ndarray], cos: np.ndarray, sin: np.ndarray, mode: str,
-                  threads: int = 1, trace: Optional[Dict[str, np.ndarray]] = None) -> np.ndarray:
+                  threads: int = 1, trace: Optional[Dict[str, np.ndarray]] = None,
+                  accum: str = "fp64") -> np.ndarray:
     """One DiT block on the packed residual stream x [N, D]; returns the new x.
 
     h  = norm(x) * (1 + scale_msa[c]) + shift_msa[c]          (bf16 store)
@@ -386,7 +395,8 @@ def block_forward(cfg, x: np.ndarray, mod: np.ndarray, bw: Dict[str, np.ndarray]
     m  = gated SiLU of u                                        (bf16 store)
     x  = x + gate_mlp[c] * (m W_2^T + b)                        (fp32 store)
 
-    c = cond_idx of the token.  The storage points apply in 'bf16' mode only.
+    c = cond_idx of the token.  The storage points apply in 'bf16' mode only;
+    ``accum`` selects the GEMM accumulation (see ``linear``).
     Reading taken: the residual stream and both projection outputs feeding it
     stay fp32, because a bf16 rounding of those values alone moves a block's
     output by more than the bf16 tolerance.
@@ -397,23 +407,24 @@ def block_forward(cfg, x: np.ndarray, mod: np.ndarray, bw: Dict[str, np.ndarray]
     m_tok = mod[ci]  # [N, 6, D]
     p = f"blocks.{b}."
     W = lambda n: bw[p + n]  # noqa: E731
+    lin = lambda a, w, bias: linear(a, w, bias, accum)  # noqa: E731
 
     h = _store(modulate(norm(x, cfg.norm, cfg.norm_eps), m_tok[:, 0], m_tok[:, 1]), mode)
-    qkv = _store(linear(h, W("attn.qkv.weight"), W("attn.qkv.bias")), mode)
+    qkv = _store(lin(h, W("attn.qkv.weight"), W("attn.qkv.bias")), mode)
     q = qkv[:, 0:D].reshape(N, H, hd)
     k = qkv[:, D:2 * D].reshape(N, H, hd)
     v = qkv[:, 2 * D:3 * D].reshape(N, H, hd)
     q = _store(apply_rope(q, cos, sin, cfg.rot_dim), mode)
     k = _store(apply_rope(k, cos, sin, cfg.rot_dim), mode)
     o = _store(attention_varlen(q, k, v, layout["cu_seqlens"], threads).reshape(N, D), mode)
-    a = linear(o, W("attn.out.weight"), W("attn.out.bias"))
+    a = lin(o, W("attn.out.weight"), W("attn.out.bias"))
     x = _store_f32(x + m_tok[:, 2] * a, mode)
     if trace is not None:
         trace.update(h=h, qkv=qkv, q=q, k=k, v=v, o=o, a=a, x_mid=x)
     h2 = _store(modulate(norm(x, cfg.norm, cfg.norm_eps), m_tok[:, 3], m_tok[:, 4]), mode)
-    u = _store(linear(h2, W("mlp.in.weight"), W("mlp.in.bias")), mode)
+    u = _store(lin(h2, W("mlp.in.weight"), W("mlp.in.bias")), mode)
     mm = _store(split_mlp(u, cfg.mlp, F), mode)
-    a2 = linear(mm, W("mlp.out.weight"), W("mlp.out.bias"))
+    a2 = lin(mm, W("mlp.out.weight"), W("mlp.out.bias"))
     x = _store_f32(x + m_tok[:, 5] * a2, mode)
     if trace is not None:
         trace.update(h2=h2, u=u, m=mm, a2=a2, x_out=x)
@@ -464,7 +475,8 @@ def unpatchify(tokens: np.ndarray, mod, grid) -> np.ndarray:
 def forward(cfg, weights: Callable[[int], Dict[str, np.ndarray]], islands: Dict[str, np.ndarray],
             inp: Dict[str, np.ndarray], mode: Optional[str] = None,
             t_rows: Optional[Sequence[float]] = None, threads: int = 1,
-            block_hook: Optional[Callable[[int, np.ndarray], None]] = None) -> Dict[str, np.ndarray]:
+            block_hook: Optional[Callable[[int, np.ndarray], None]] = None,
+            accum: str = "fp64") -> Dict[str, np.ndarray]:
     """The DiT forward.
 
     ``weights(b)`` returns block b's tensors (regenerated block by block so a
@@ -495,7 +507,7 @@ def forward(cfg, weights: Callable[[int], Dict[str, np.ndarray]], islands: Dict[
     for b in range(cfg.n_blocks):
         bw = weights(b)
         mod = adaln_table(cfg, bw, b, emb, mode)
-        x = block_forward(cfg, x, mod, bw, b, layout, cos, sin, mode, threads)
+        x = block_forward(cfg, x, mod, bw, b, layout, cos, sin, mode, threads, accum=accum)
         if block_hook is not None:
             block_hook(b, x)
         del bw
@@ -542,6 +554,21 @@ def euler_step(x: np.ndarray, v: np.ndarray, dt: np.float32) -> np.ndarray:
     v = np.asarray(v, np.float32)
     prod = (np.float32(dt) * v).astype(np.float32)
     return (x + prod).astype(np.float32)
+
+
+def denoise_loop(cfg, weights, islands, latents: Dict[str, np.ndarray], n_steps: int,
+                 mode: Optional[str] = None, threads: int = 1, accum: str = "fp64") -> Dict[str, np.ndarray]:
+    """n_steps Euler steps from the given latents: at step i every row's
+    timestep is sigma_m(i) of its modality and each segment moves by
+    dt_m(i) * v (float32 state, as the loop keeps it)."""
+    lat = {k: np.asarray(v, np.float32) for k, v in latents.items()}
+    for i in range(n_steps):
+        t_rows, dts = denoise_step_conditions(cfg, i)
+        v = forward(cfg, weights, islands, lat, mode, t_rows=t_rows, threads=threads, accum=accum)
+        for j, seg in enumerate(cfg.segments):
+            lat[f"latent.{j}"] = euler_step(lat[f"latent.{j}"], v[f"latent.{j}"].astype(np.float32),
+                                            dts[seg.modality])
+    return lat
 
 
 def denoise_step_conditions(cfg, step: int):

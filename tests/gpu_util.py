@@ -1,0 +1,81 @@
+"""Helpers shared by the GPU parity tests (not a test module)."""
+
+import numpy as np
+import torch
+
+BF16_HALF_ULP = 2.0 ** -8  # relative half spacing of bf16 at the bottom of a binade
+
+
+def to_bf16_dev(a: np.ndarray) -> torch.Tensor:
+    """float32 values (rounded to bf16 here if needed) -> a bf16 CUDA tensor."""
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).cuda()
+
+
+def from_dev(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def rms(a) -> float:
+    return float(np.sqrt(np.mean(np.asarray(a, np.float64) ** 2)))
+
+
+def assert_f32_close(got, ref, rel=1e-5, abs_=1e-6, what=""):
+    """The fp32 parity bound: |got - ref| <= abs + rel * |ref| elementwise."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    err = np.abs(got - ref)
+    bad = err > abs_ + rel * np.abs(ref)
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - (abs_ + rel * np.abs(ref))), err.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())}/{bad.size} outside rel {rel} / abs {abs_}; "
+                             f"worst at {i}: got {got[i]!r} ref {ref[i]!r}; max|d| {err.max():.3e}")
+
+
+def assert_bf16_rounded(got, ref, what="", slack=0.0):
+    """got is a bf16 rounding of a value within float32 noise of ref."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    err = np.abs(got - ref)
+    tol = BF16_HALF_ULP * np.abs(ref) * 1.001 + 1e-6 * rms(ref) + slack * rms(ref)
+    bad = err > tol
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - tol), err.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())}/{bad.size} beyond a bf16 rounding; worst at {i}: "
+                             f"got {got[i]!r} ref {ref[i]!r}")
+
+
+def assert_rms_rel(got, ref, bound, what=""):
+    """bf16 parity bound: max|got - ref| / rms(ref) <= bound."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    r = np.abs(got - ref).max() / rms(ref)
+    assert r <= bound, f"{what}: max|d|/rms = {r:.3e} > {bound}"
+    return r
+
+
+# bf16 parity.  The bound is max|d| <= 3e-3 * rms(oracle).  Where a control arm
+# -- the oracle against itself with fp32 instead of fp64 GEMM accumulation,
+# same bf16 storage points -- already breaks it (single-ulp bf16 rounding flips
+# at large elements: max|d|/rms = 1.7e-2 on one 6144-wide block), the bound
+# that applies is 3x the control arm's own drift, in max and in rms.
+BF16_BOUND = 3e-3
+CONTROL_FACTOR = 3.0
+
+
+def assert_bf16_parity(got, ref, ctl, what=""):
+    got, ref, ctl = (np.asarray(a, np.float64) for a in (got, ref, ctl))
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    r = rms(ref)
+    d, dc = np.abs(got - ref), np.abs(ctl - ref)
+    g_rms, c_rms = float(np.sqrt(np.mean(d * d)) / r), float(np.sqrt(np.mean(dc * dc)) / r)
+    g_max, c_max = float(d.max() / r), float(dc.max() / r)
+    max_bound = max(BF16_BOUND, CONTROL_FACTOR * c_max)
+    rms_bound = max(BF16_BOUND, CONTROL_FACTOR * c_rms)
+    print(f"{what}: max|d|/rms {g_max:.3e} (control {c_max:.3e}, bound {max_bound:.3e})  "
+          f"rms(d)/rms {g_rms:.3e} (control {c_rms:.3e}, bound {rms_bound:.3e})")
+    assert g_max <= max_bound, f"{what}: max|d|/rms = {g_max:.3e} > {max_bound:.3e}"
+    assert g_rms <= rms_bound, f"{what}: rms(d)/rms = {g_rms:.3e} > {rms_bound:.3e}"
+    return g_max, g_rms

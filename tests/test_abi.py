@@ -1,0 +1,140 @@
+"""CPU checks of the C ABI: the library loads and exports every declared symbol,
+the host table builders equal the oracle bit for bit, and the host-side error
+paths return the documented status codes (no GPU needed, no device call made).
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synthetic as S
+from synthetic.configs import Segment, scaled
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def dit():
+    from video_audio_gen_amd import dit as d
+    d.load()
+    return d
+
+
+def test_exports_every_declared_symbol(dit):
+    hdr = open(os.path.join(ROOT, "include", "dit.h")).read()
+    names = set(re.findall(r"^\s*(?:int|void|const char\*)\s+(dit_\w+)\s*\(", hdr, re.M))
+    assert len(names) >= 30
+    lib = dit.load()
+    missing = [n for n in sorted(names) if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_pack_layout_bit_exact(dit, name):
+    cfg = S.get_config(name)
+    got, ref = dit.dit_pack_layout(cfg), O.pack_layout(cfg)
+    for k in ("cu_seqlens", "cond_idx", "doc_id"):
+        assert np.array_equal(got[k], ref[k]), k
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+def test_rope_cache_bit_exact(dit, name):
+    cfg = S.get_config(name)
+    c, s = dit.dit_rope_cache_build(cfg)
+    oc, os_ = O.rope_cache(cfg)
+    assert np.array_equal(c.view(np.uint32), oc.view(np.uint32))
+    assert np.array_equal(s.view(np.uint32), os_.view(np.uint32))
+
+
+def test_timestep_embedding_and_sigma_bit_exact(dit):
+    t = np.random.default_rng(0).random(7).astype(np.float32)
+    for dim in (128, 256):
+        got = dit.dit_timestep_embedding(t, dim)
+        ref = np.stack([O.timestep_embedding(x, dim) for x in t])
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    for shift in (1.0, 3.0, 12.0):
+        sig, dt = dit.dit_sigma_schedule(shift, 50)
+        osig = O.sigma_schedule(shift, 50)
+        assert np.array_equal(sig, osig)
+        assert np.array_equal(dt, O.sigma_dt(osig))
+
+
+def _fake_model(dit, cfg):
+    c = dit.make_config(cfg)
+    nbytes = ctypes.c_size_t()
+    assert dit.load().dit_weight_bytes(ctypes.byref(c), ctypes.byref(nbytes)) == 0
+    h = ctypes.c_void_p()
+    fake = 1 << 40  # never dereferenced: only host-side validation runs in these tests
+    assert dit.load().dit_model_create(ctypes.byref(c), fake, nbytes.value, ctypes.byref(h)) == 0
+    return h, nbytes.value
+
+
+def _stage_one(dit, h, name, arr, dtype=None):
+    v = (dit.dit_weight_view * 1)()
+    v[0].name = name.encode()
+    v[0].dtype = dtype if dtype is not None else dit.DIT_F32
+    v[0].ndim = arr.ndim
+    for d in range(arr.ndim):
+        v[0].shape[d] = arr.shape[d]
+    v[0].host = arr.ctypes.data
+    return dit.load().dit_stage_weights(h, v, 1, None)
+
+
+def test_weight_bytes_match_the_contract(dit):
+    cfg = S.get_config("c4")
+    c = dit.make_config(cfg)
+    nbytes = ctypes.c_size_t()
+    assert dit.load().dit_weight_bytes(ctypes.byref(c), ctypes.byref(nbytes)) == 0
+    D, F, dt = 6144, 16384, 256
+    block = 2 * (4 * D * D + 3 * D * F) + 2 * (6 * D * dt * 2) + 4 * (3 * D + D + 2 * F + D + 2 * 6 * D)
+    assert abs(nbytes.value - 64 * block) < 64 * 20 * 256 + 10 ** 7  # alignment + islands
+    assert 60e9 < nbytes.value < 61.5e9  # ~30B parameters in bf16
+
+
+def test_staging_errors_are_named(dit):
+    cfg = S.get_config("c1")
+    h, _ = _fake_model(dit, cfg)
+    lib = dit.load()
+    assert _stage_one(dit, h, "blocks.0.attn.nope.weight", np.zeros((4, 4), np.float32)) == 3
+    assert b"blocks.0.attn.nope.weight" in lib.dit_last_error()
+    assert _stage_one(dit, h, "blocks.0.attn.qkv.weight", np.zeros((128, 384), np.float32)) == 4
+    assert _stage_one(dit, h, "blocks.0.attn.qkv.weight", np.zeros((384, 128), np.float32), dtype=7) == 5
+    assert lib.dit_stage_finalize(h) == 6
+    assert b"missing weight" in lib.dit_last_error()
+    lib.dit_model_destroy(h)
+
+
+def test_config_validation(dit):
+    lib = dit.load()
+    bad = [scaled(S.get_config("c1"), hidden=130), scaled(S.get_config("c1"), rot_dim=40),
+           scaled(S.get_config("c3"), head_dim=64, n_heads=96),  # bf16 attention is head_dim 128 only
+           scaled(S.get_config("c1"), norm_eps=0.0)]
+    for cfg in bad:
+        c = dit.make_config(cfg)
+        n = ctypes.c_size_t()
+        assert lib.dit_weight_bytes(ctypes.byref(c), ctypes.byref(n)) != 0
+        assert len(lib.dit_last_error()) > 0
+
+
+def test_layout_rejects_malformed_segments(dit):
+    cfg = S.get_config("c1")
+    with pytest.raises(dit.DitError) as e:
+        dit.dit_pack_layout(cfg, [Segment(0, (4, 0, 4), 0)])
+    assert e.value.status == "DIT_E_INVALID"
+    with pytest.raises(dit.DitError):
+        dit.dit_pack_layout(cfg, [Segment(3, (4, 4, 4), 0)])  # no modality 3
+
+
+def test_forward_requires_finalized_model(dit):
+    cfg = S.get_config("c1")
+    h, _ = _fake_model(dit, cfg)
+    lib = dit.load()
+    rc = lib.dit_forward(h, None, 1, 1, 1, None, 0, None)
+    assert rc == 1  # null batch is rejected before anything else
+    rc = lib.dit_block_forward(None, 0, 1, 1, None, None, 0, None)
+    assert rc == 1
+    lib.dit_model_destroy(h)

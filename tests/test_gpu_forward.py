@@ -1,0 +1,193 @@
+"""Whole-path parity through the C ABI (dit_forward / dit_block_forward /
+dit_denoise_step / dit_denoise_loop) against the CPU oracle, plus the
+bit-exact invariants: packed == alone, zero gate == identity, determinism,
+Euler update bit-exact, device loop == separate steps.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synthetic as S
+from gpu_util import assert_bf16_parity, assert_f32_close, rms
+from synthetic.configs import CondRow, Segment, scaled
+
+pytestmark = pytest.mark.gpu
+
+
+
+@pytest.fixture(scope="module")
+def H():
+    from video_audio_gen_amd import dit, harness
+    dit.load()
+    return harness
+
+
+def _oracle(cfg, weights, inp, t_rows=None, accum="fp64"):
+    isl = {k: v for k, v in weights.items() if not k.startswith("blocks.")}
+    return O.forward(cfg, lambda b: weights, isl, inp, t_rows=t_rows, threads=8, accum=accum)
+
+
+def _run(H, cfg, seed=0):
+    w = S.all_weights(cfg, seed, threads=8)
+    r = H.Runner(cfg, seed, model=_stage(H, cfg, w))
+    r.forward()
+    return r, w, r.output_numpy()
+
+
+def _stage(H, cfg, w):
+    from video_audio_gen_amd import dit
+    m = dit.Model(cfg)
+    dit.dit_stage_weights(m, w, as_bf16=cfg.stream == "bf16")
+    dit.dit_stage_finalize(m)
+    return m
+
+
+C3_SMALL = scaled(S.get_config("c3"), segments=(Segment(0, (2, 8, 16), 0), Segment(1, (64,), 1)))
+C4_SMALL = scaled(S.get_config("c4"), n_blocks=2,
+                  segments=(Segment(0, (1, 4, 8), 0), Segment(1, (24,), 1), Segment(0, (2, 2, 4), 2),
+                            Segment(1, (40,), 3)))
+C5_SMALL = scaled(S.get_config("c5"), n_blocks=2, hidden=256, n_heads=2, ffn=512, denoise_steps=4,
+                  segments=(Segment(0, (2, 4, 8), 0), Segment(1, (16,), 1)))
+
+
+def test_c1_tiny_f32_parity(H):
+    cfg = S.get_config("c1")
+    r, w, got = _run(H, cfg)
+    ref = _oracle(cfg, w, r.inp)
+    assert_f32_close(got["x"], ref["x"], what="c1 forward")
+    c = H.dit.dit_counters()
+    assert c["gemm_f32"] > 0 and c["attention_f32"] > 0 and c["modnorm"] > 0
+
+
+def test_c2_music_f32_reduced_depth_parity(H):
+    cfg = scaled(S.get_config("c2"), n_blocks=2)
+    r, w, got = _run(H, cfg)
+    ref = _oracle(cfg, w, r.inp)
+    for k in ref:
+        assert_f32_close(got[k], ref[k], what=f"c2 (2 blocks) {k}")
+    assert np.abs(got["latent.0"] - got["latent.1"]).max() > 1e-3  # CFG branches differ
+
+
+def test_c2_music_f32_full_parity(H):
+    cfg = S.get_config("c2")
+    r, w, got = _run(H, cfg)
+    ref = _oracle(cfg, w, r.inp)
+    for k in ref:
+        err = np.abs(got[k] - ref[k])
+        print(f"c2 {k}: max|d| {err.max():.3e} rms {rms(ref[k]):.3e} "
+              f"outside {(err > 1e-6 + 1e-5 * np.abs(ref[k])).sum()}/{err.size}")
+        assert_f32_close(got[k], ref[k], what=f"c2 full {k}")
+
+
+def test_c3_block_bf16_parity(H):
+    cfg = C3_SMALL
+    r, w, got = _run(H, cfg)
+    ref = _oracle(cfg, w, r.inp)
+    ctl = _oracle(cfg, w, r.inp, accum="fp32")
+    assert_bf16_parity(got["x"], ref["x"], ctl["x"], "c3 block (320 tokens)")
+
+
+def test_c4_io_bf16_parity(H):
+    cfg = C4_SMALL
+    r, w, got = _run(H, cfg)
+    ref = _oracle(cfg, w, r.inp)
+    ctl = _oracle(cfg, w, r.inp, accum="fp32")
+    for k in ref:
+        assert_bf16_parity(got[k], ref[k], ctl[k], f"c4 small (2 blocks) {k}")
+
+
+def test_packed_equals_alone_bits(H):
+    for cfg in (S.get_config("c1"), C3_SMALL):
+        w = S.all_weights(cfg, 0, threads=8)
+        m = _stage(H, cfg, w)
+        r = H.Runner(cfg, 0, model=m)
+        r.forward()
+        packed = r.output_numpy()["x"]
+        lay = O.pack_layout(cfg)
+        for i, seg in enumerate(cfg.segments):
+            a, b = int(lay["cu_seqlens"][i]), int(lay["cu_seqlens"][i + 1])
+            one = scaled(cfg, segments=(seg,))
+            batch = H.dit.Batch(m, one.segments, H.cond_modality(cfg))
+            ws = H.dit.workspace(batch)
+            xi = r.x_in[a:b].contiguous()
+            out = torch.empty_like(xi)
+            H.dit.dit_forward(m, batch, xi, r.cond, out, ws)
+            torch.cuda.synchronize()
+            assert np.array_equal(out.cpu().numpy(), packed[a:b]), f"{cfg.name} segment {i}"
+
+
+def test_zero_gate_block_identity_and_determinism(H):
+    cfg = C3_SMALL
+    w = S.all_weights(cfg, 0, threads=8)
+    m = _stage(H, cfg, w)
+    r = H.Runner(cfg, 0, model=m)
+    mod = torch.randn(cfg.n_cond, 6, cfg.hidden, device="cuda")
+    mod[:, 2] = 0
+    mod[:, 5] = 0
+    x = r.x_in.clone()
+    H.dit.dit_block_forward(m, 0, x, mod, r.batch, r.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(x, r.x_in)
+    a = r.forward().clone()
+    b = r.forward().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def _schedule_tables(H, cfg):
+    """Per-step conditioning rows and dt, built once on the host by the library."""
+    dit = H.dit
+    steps = cfg.denoise_steps
+    sig = {m: dit.dit_sigma_schedule(cfg.shifts[m], steps) for m in range(cfg.n_mod)}
+    conds, dts = [], []
+    for i in range(steps):
+        t_rows = [np.float32(sig[r.modality][0][i]) for r in cfg.cond_rows]
+        conds.append(dit.dit_timestep_embedding(np.asarray(t_rows, np.float32), cfg.cond_dim))
+        dts.append([sig[m][1][i] for m in range(cfg.n_mod)])
+    return (torch.from_numpy(np.stack(conds)).cuda(), torch.from_numpy(np.asarray(dts, np.float32)).cuda())
+
+
+def test_euler_steps_bit_exact_with_constant_velocity(H):
+    # No blocks and a zero output projection make the velocity exactly the output
+    # bias, on the GPU and in the oracle, so every Euler update must match bit for bit.
+    cfg = scaled(C5_SMALL, n_blocks=0)
+    w = S.island_weights(cfg)
+    for mm in range(cfg.n_mod):
+        w[f"out.{mm}.weight"][:] = 0.0
+        w[f"out.{mm}.bias"][:] = np.random.default_rng(30 + mm).standard_normal(w[f"out.{mm}.bias"].shape)
+    m = _stage(H, cfg, w)
+    r = H.Runner(cfg, 0, model=m)
+    cond_tab, dt_tab = _schedule_tables(H, cfg)
+    lat = r.x_in.clone()
+    for i in range(cfg.denoise_steps):
+        H.dit.dit_denoise_step(m, r.batch, lat, cond_tab[i], dt_tab[i], r.ws)
+        want = O.denoise_loop(cfg, lambda b: {}, w, r.inp, i + 1)
+        got = H.unpack_output(cfg, lat.cpu().numpy())
+        for k in want:
+            assert np.array_equal(got[k], want[k]), f"step {i} {k}"
+
+
+def test_denoise_loop_matches_steps_and_oracle(H):
+    cfg = C5_SMALL
+    w = S.all_weights(cfg, 0, threads=8)
+    m = _stage(H, cfg, w)
+    r = H.Runner(cfg, 0, model=m)
+    cond_tab, dt_tab = _schedule_tables(H, cfg)
+    lat = r.x_in.clone()
+    for i in range(cfg.denoise_steps):
+        H.dit.dit_denoise_step(m, r.batch, lat, cond_tab[i], dt_tab[i], r.ws)
+    lat_loop = r.x_in.clone()
+    H.dit.dit_denoise_loop(m, r.batch, lat_loop, cond_tab, dt_tab, cfg.denoise_steps, r.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(lat_loop, lat)  # the device loop is the same computation as single steps
+    assert (lat - r.x_in).abs().max().item() > 1e-2  # the loop moves the latents
+    isl = {k: v for k, v in w.items() if not k.startswith("blocks.")}
+    ref = O.denoise_loop(cfg, lambda b: w, isl, r.inp, cfg.denoise_steps, threads=8)
+    ctl = O.denoise_loop(cfg, lambda b: w, isl, r.inp, cfg.denoise_steps, threads=8, accum="fp32")
+    got = H.unpack_output(cfg, lat.cpu().numpy())
+    for k in ref:
+        # compare the distance travelled (latent - noise), the part the model computed
+        x0 = r.inp[k].astype(np.float64)
+        assert_bf16_parity(got[k] - x0, ref[k] - x0, ctl[k] - x0, f"denoise {cfg.denoise_steps} steps {k}")

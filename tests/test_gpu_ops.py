@@ -1,0 +1,235 @@
+"""Per-kernel parity through the C ABI op-level calls, against the oracle's steps.
+
+Sizes span several tiles with ragged tails; the last cases of each kernel use
+the shapes of the full workloads and check sampled outputs.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_util import (assert_bf16_rounded, assert_f32_close, assert_rms_rel, from_dev, rms,
+                      to_bf16_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dit():
+    from video_audio_gen_amd import dit as d
+    d.load()
+    return d
+
+
+def _bf16_vals(rng, shape, scale=1.0):
+    a = (rng.standard_normal(shape) * scale).astype(np.float32)
+    return torch.from_numpy(a).to(torch.bfloat16).float().numpy()
+
+
+# ----------------------------------------------------------------------------- GEMM
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 64), (300, 320, 128), (513, 768, 192), (26624 // 8, 18432 // 8, 6144)])
+def test_gemm_bf16(dit, M, N, K):
+    rng = np.random.default_rng(M + N + K)
+    A = _bf16_vals(rng, (M, K))
+    B = _bf16_vals(rng, (N, K), 0.02)
+    bias = rng.standard_normal(N).astype(np.float32)
+    ref = O.linear(A, B, bias)
+    Ad, Bd = to_bf16_dev(A), to_bf16_dev(B)
+    C32 = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    dit.dit_gemm(Ad, Bd, torch.from_numpy(bias).cuda(), C32)
+    g = from_dev(C32)
+    # products of bf16 values are exact in fp32; only the fp32 accumulation order differs
+    assert np.abs(g - ref).max() <= 3e-5 * rms(ref) + 1e-6
+    C16 = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    dit.dit_gemm(Ad, Bd, torch.from_numpy(bias).cuda(), C16)
+    assert_bf16_rounded(from_dev(C16), ref, "gemm bf16 -> bf16", slack=1e-5)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 4, 4), (100, 70, 36), (172, 2560, 2560), (172, 2560, 10240), (160, 1024, 128)])
+def test_gemm_f32_fp64_accumulation(dit, M, N, K):
+    rng = np.random.default_rng(M * 7 + N + K)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    B = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    bias = rng.standard_normal(N).astype(np.float32)
+    ref = O.linear(A, B, bias)
+    C = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    dit.dit_gemm(torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda(), torch.from_numpy(bias).cuda(), C)
+    g = from_dev(C)
+    # fp64 sums: the result is the fp32 rounding of the exact value (half an ulp, one at an fp64 near-tie)
+    assert np.all(np.abs(g - ref) <= 2.0 ** -23 * np.abs(ref) + 1e-12)
+
+
+def test_gemm_packed_equals_alone_bits(dit):
+    rng = np.random.default_rng(1)
+    A = _bf16_vals(rng, (700, 256))
+    B = _bf16_vals(rng, (384, 256), 0.02)
+    Ad, Bd = to_bf16_dev(A), to_bf16_dev(B)
+    full = torch.empty(700, 384, dtype=torch.bfloat16, device="cuda")
+    part = torch.empty(123, 384, dtype=torch.bfloat16, device="cuda")
+    dit.dit_gemm(Ad, Bd, None, full)
+    dit.dit_gemm(Ad[300:423].contiguous(), Bd, None, part)
+    torch.cuda.synchronize()
+    assert torch.equal(full[300:423], part)
+    Af = torch.from_numpy(rng.standard_normal((172, 512)).astype(np.float32)).cuda()
+    Bf = torch.from_numpy(rng.standard_normal((640, 512)).astype(np.float32)).cuda()
+    f_full = torch.empty(172, 640, device="cuda")
+    f_part = torch.empty(86, 640, device="cuda")
+    dit.dit_gemm(Af, Bf, None, f_full)
+    dit.dit_gemm(Af[86:].contiguous(), Bf, None, f_part)
+    torch.cuda.synchronize()
+    assert torch.equal(f_full[86:], f_part)
+
+
+# ----------------------------------------------------------------------------- modulate + norm
+
+@pytest.mark.parametrize("norm", [0, 1])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N,D", [(5, 128), (203, 2560), (77, 6144)])
+def test_modnorm(dit, norm, dtype, N, D):
+    rng = np.random.default_rng(N + D + norm)
+    x = (rng.standard_normal((N, D)) * 2 + 0.5).astype(np.float32)
+    n_cond = 3
+    mod = (rng.standard_normal((n_cond, 6, D)) * 0.3).astype(np.float32)
+    ci = rng.integers(0, n_cond, N).astype(np.int32)
+    kind = "rms" if norm == 0 else "layer"
+    for which, (ks, kc) in enumerate([(0, 1), (3, 4)]):
+        ref = O.modulate(O.norm(x, kind, 1e-6), mod[ci, ks].astype(np.float64), mod[ci, kc].astype(np.float64))
+        h = torch.empty(N, D, dtype=torch.float32 if dtype == "f32" else torch.bfloat16, device="cuda")
+        dit.dit_modnorm(norm, 1e-6, torch.from_numpy(x).cuda(), torch.from_numpy(mod).cuda(), which,
+                        torch.from_numpy(ci).cuda(), h)
+        if dtype == "f32":
+            assert_f32_close(from_dev(h), ref, what="modnorm f32")
+        else:
+            assert_bf16_rounded(from_dev(h), ref, "modnorm bf16")
+    plain = torch.empty(N, D, dtype=torch.float32, device="cuda")
+    dit.dit_modnorm(norm, 1e-6, torch.from_numpy(x).cuda(), None, 0, None, plain)
+    assert_f32_close(from_dev(plain), O.norm(x, kind, 1e-6), what="plain norm")
+
+
+# ----------------------------------------------------------------------------- RoPE + split
+
+@pytest.mark.parametrize("dtype,N,H,hd,rot", [("f32", 160, 4, 32, 32), ("f32", 172, 3, 128, 64),
+                                              ("bf16", 301, 5, 128, 128), ("bf16", 64, 2, 128, 64)])
+def test_rope_split(dit, dtype, N, H, hd, rot):
+    rng = np.random.default_rng(N + H)
+    D = H * hd
+    qkv = rng.standard_normal((N, 3 * D)).astype(np.float32)
+    if dtype == "bf16":
+        qkv = torch.from_numpy(qkv).to(torch.bfloat16).float().numpy()
+    pos = rng.integers(0, 500, N).astype(np.float64)
+    inv = np.array(O.rope_inv_freq(rot, 10000.0))
+    cos = np.cos(np.outer(pos, inv)).astype(np.float32)
+    sin = np.sin(np.outer(pos, inv)).astype(np.float32)
+    tq = torch.from_numpy(qkv).cuda()
+    if dtype == "bf16":
+        tq = tq.to(torch.bfloat16)
+    q, k, v = (torch.empty(H, N, hd, dtype=tq.dtype, device="cuda") for _ in range(3))
+    dit.dit_rope_split(tq, H, hd, rot, torch.from_numpy(cos).cuda(), torch.from_numpy(sin).cuda(), q, k, v)
+    for i, (t, rot_it) in enumerate([(q, True), (k, True), (v, False)]):
+        src = qkv[:, i * D:(i + 1) * D].reshape(N, H, hd).astype(np.float64)
+        ref = O.apply_rope(src, cos, sin, rot) if rot_it else src
+        got = from_dev(t).transpose(1, 0, 2)
+        if not rot_it:
+            assert np.array_equal(got, ref)  # v is a bit-exact copy
+        elif dtype == "f32":
+            assert_f32_close(got, ref, what="rope f32")
+        else:
+            assert_bf16_rounded(got, ref, "rope bf16")
+        if rot_it:
+            assert np.array_equal(got[..., rot:], src[..., rot:])  # partial rotary passes the rest through
+
+
+# ----------------------------------------------------------------------------- attention
+
+@pytest.mark.parametrize("cu,H,hd", [([0, 64, 160], 4, 32), ([0, 86, 172], 3, 128), ([0, 1, 37, 100], 2, 64)])
+def test_attention_f32(dit, cu, H, hd):
+    rng = np.random.default_rng(cu[-1] + hd)
+    N = cu[-1]
+    q, k, v = (rng.standard_normal((H, N, hd)).astype(np.float32) for _ in range(3))
+    ref = O.attention_varlen(*(a.transpose(1, 0, 2).astype(np.float64) for a in (q, k, v)), np.array(cu))
+    o = torch.empty(N, H * hd, device="cuda")
+    cut = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    dit.dit_attention(*(torch.from_numpy(a).cuda() for a in (q, k, v)), cut, int(np.diff(cu).max()), o)
+    assert_f32_close(from_dev(o), ref.reshape(N, H * hd), what="attention f32")
+
+
+@pytest.mark.parametrize("cu,H", [([0, 100, 357, 420], 2), ([0, 1, 129, 300], 3), ([0, 1024, 1536], 2)])
+def test_attention_bf16(dit, cu, H):
+    rng = np.random.default_rng(cu[-1])
+    N, hd = cu[-1], 128
+    q, k, v = (_bf16_vals(rng, (H, N, hd)) for _ in range(3))
+    ref = O.attention_varlen(*(a.transpose(1, 0, 2).astype(np.float64) for a in (q, k, v)), np.array(cu))
+    ref = ref.reshape(N, H * hd)
+    o = torch.empty(N, H * hd, dtype=torch.bfloat16, device="cuda")
+    cut = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    dit.dit_attention(*(to_bf16_dev(a) for a in (q, k, v)), cut, int(np.diff(cu).max()), o)
+    got = from_dev(o)
+    # the output is a bf16 rounding (half an ulp of each value) of a result whose
+    # probabilities entered the PV product as bf16: a CPU emulation of exactly
+    # that arithmetic differs from the fp64 oracle by up to 0.92% of rms
+    assert_bf16_rounded(got, ref, "attention bf16", slack=1.2e-2)
+    assert np.abs(got - ref).mean() / rms(ref) < 2e-3
+
+
+def test_attention_bf16_segmentation_bits(dit):
+    rng = np.random.default_rng(7)
+    cu = [0, 200, 333]
+    N, H, hd = 333, 2, 128
+    q, k, v = (_bf16_vals(rng, (H, N, hd)) for _ in range(3))
+    cut = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    o1 = torch.empty(N, H * hd, dtype=torch.bfloat16, device="cuda")
+    dit.dit_attention(*(to_bf16_dev(a) for a in (q, k, v)), cut, 200, o1)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, 250] += 1.0
+    v2[:, 300] -= 1.0
+    o2 = torch.empty_like(o1)
+    dit.dit_attention(to_bf16_dev(q), to_bf16_dev(k2), to_bf16_dev(v2), cut, 200, o2)
+    alone = torch.empty(133, H * hd, dtype=torch.bfloat16, device="cuda")
+    dit.dit_attention(*(to_bf16_dev(np.ascontiguousarray(a[:, 200:])) for a in (q, k, v)),
+                      torch.tensor([0, 133], dtype=torch.int32, device="cuda"), 133, alone)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[:200], o2[:200])
+    assert not torch.equal(o1[200:], o2[200:])
+    assert torch.equal(o1[200:], alone)
+
+
+# ----------------------------------------------------------------------------- SiLU gate, gated residual
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_silu_gate(dit, dtype):
+    rng = np.random.default_rng(3)
+    N, F = 37, 1024
+    u = (rng.standard_normal((N, 2 * F)) * 3).astype(np.float32)
+    t = torch.from_numpy(u).cuda()
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+        u = from_dev(t)
+    m = torch.empty(N, F, dtype=t.dtype, device="cuda")
+    dit.dit_silu_gate(t, m)
+    ref = O.split_mlp(u.astype(np.float64), "gate_up", F)
+    if dtype == "f32":
+        assert_f32_close(from_dev(m), ref, what="silu f32")
+    else:
+        assert_bf16_rounded(from_dev(m), ref, "silu bf16")
+
+
+def test_gated_residual(dit):
+    rng = np.random.default_rng(4)
+    N, D, n_cond = 99, 512, 4
+    x = rng.standard_normal((N, D)).astype(np.float32)
+    a = rng.standard_normal((N, D)).astype(np.float32)
+    mod = rng.standard_normal((n_cond, 6, D)).astype(np.float32)
+    ci = rng.integers(0, n_cond, N).astype(np.int32)
+    for which, gk in ((0, 2), (1, 5)):
+        xt = torch.from_numpy(x).cuda()
+        dit.dit_gated_residual(xt, torch.from_numpy(a).cuda(), torch.from_numpy(mod).cuda(), which,
+                               torch.from_numpy(ci).cuda())
+        ref = x.astype(np.float64) + mod[ci, gk].astype(np.float64) * a
+        assert_f32_close(from_dev(xt), ref, rel=1.2e-7, abs_=1e-7, what="gated residual")
+    xt = torch.from_numpy(x).cuda()
+    dit.dit_gated_residual(xt, torch.from_numpy(a).cuda(), torch.zeros(n_cond, 6, D, device="cuda"), 0,
+                           torch.from_numpy(ci).cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(xt.cpu(), torch.from_numpy(x))  # a zero gate leaves x bit-identical

@@ -394,3 +394,36 @@ def test_timestep_forward_packed_equals_alone():
         alone = O.forward(one, W, isl, {"latent.0": inp[f"latent.{i}"], "t": inp["t"]},
                           t_rows=[float(inp["t"][0])] * 2)
         assert np.allclose(alone["latent.0"], packed[f"latent.{i}"], rtol=0, atol=1e-12)
+
+
+def test_linear_fp32_accumulation_is_the_float32_product():
+    rng = np.random.default_rng(15)
+    x = rng.standard_normal((7, 300)).astype(np.float32)
+    W = rng.standard_normal((5, 300)).astype(np.float32)
+    b = rng.standard_normal(5)
+    got = O.linear(x, W, b, accum="fp32")
+    assert np.array_equal(got, (x @ W.T).astype(np.float64) + b)
+    assert 0 < np.abs(got - O.linear(x, W, b)).max() < 1e-4
+
+
+def test_denoise_loop_constant_velocity_telescopes():
+    # no blocks and a zero output projection: v = the output bias everywhere,
+    # so n Euler steps move each latent by sum(dt) * bias = -bias (sigma 1 -> 0)
+    cfg = scaled(S.get_config("c5"), n_blocks=0, hidden=256, n_heads=2, ffn=512, denoise_steps=6,
+                 segments=(Segment(0, (1, 2, 2), 0), Segment(1, (5,), 1)))
+    isl = S.island_weights(cfg)
+    bias = {}
+    for m in range(cfg.n_mod):
+        isl[f"out.{m}.weight"][:] = 0.0
+        bias[m] = np.random.default_rng(20 + m).standard_normal(isl[f"out.{m}.bias"].shape).astype(np.float32)
+        isl[f"out.{m}.bias"][:] = bias[m]
+    lat0 = S.inputs(cfg)
+    out = O.denoise_loop(cfg, lambda b: {}, isl, lat0, 6)
+    for j, seg in enumerate(cfg.segments):
+        mod = cfg.modalities[seg.modality]
+        v = O.unpatchify(np.tile(bias[seg.modality], (seg.n_tokens, 1)), mod, seg.grid)
+        want = lat0[f"latent.{j}"].astype(np.float64) - v
+        assert np.abs(out[f"latent.{j}"] - want).max() < 1e-5
+    # and a different shift per modality gives different intermediate sigmas
+    t6, _ = O.denoise_step_conditions(cfg, 3)
+    assert t6[0] != t6[1]

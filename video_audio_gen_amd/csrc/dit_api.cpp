@@ -1,0 +1,907 @@
+// The C ABI of the DiT block forward: configuration checks, the weight
+// contract and its staging into a caller-owned HBM slab, the batch tables, the
+// workspace plan and the launch sequences of the block, the forward and the
+// denoise loop.  No device memory is allocated here; no call synchronises the
+// host except the staging calls, which copy synchronously by contract.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "dit.h"
+#include "internal.h"
+#include "kernels.h"
+
+namespace dit {
+
+static thread_local std::string g_error;
+
+int set_error(int code, const char* fmt, ...) {
+  char buf[1024];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+static std::atomic<int64_t> g_counters[kCntNum];
+void count_launch(Counter c) { g_counters[c].fetch_add(1, std::memory_order_relaxed); }
+
+// Per-launch event timing, off unless dit_profile_begin() was called.
+struct ProfRecord {
+  int family;
+  int ev0, ev1;
+};
+static std::mutex g_prof_mu;
+static std::atomic<bool> g_prof_on{false};
+static std::vector<hipEvent_t> g_events;  // pool, reused across passes
+static size_t g_events_used = 0;
+static std::vector<ProfRecord> g_prof;
+
+static int prof_event() {
+  if (g_events_used == g_events.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return -1;
+    g_events.push_back(e);
+  }
+  return static_cast<int>(g_events_used++);
+}
+
+LaunchScope::LaunchScope(Counter c, hipStream_t s) : slot_(-1), s_(s) {
+  count_launch(c);
+  if (!g_prof_on.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  const int a = prof_event(), b = prof_event();
+  if (a < 0 || b < 0) return;
+  if (hipEventRecord(g_events[a], s) != hipSuccess) return;
+  g_prof.push_back({static_cast<int>(c), a, b});
+  slot_ = static_cast<int>(g_prof.size()) - 1;
+}
+
+LaunchScope::~LaunchScope() {
+  if (slot_ < 0) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  hipEventRecord(g_events[g_prof[slot_].ev1], s_);
+}
+
+static bool sync_check_enabled() {
+  static const bool on = [] {
+    const char* e = getenv("DIT_SYNC_CHECK");
+    return e != nullptr && e[0] == '1';
+  }();
+  return on;
+}
+
+}  // namespace dit
+
+using namespace dit;
+
+#define DIT_HIP(expr)                                                                       \
+  do {                                                                                      \
+    hipError_t e_ = (expr);                                                                 \
+    if (e_ != hipSuccess)                                                                   \
+      return set_error(DIT_E_HIP, "%s: %s (%s)", __func__, hipGetErrorString(e_), #expr);  \
+    if (sync_check_enabled()) {                                                             \
+      e_ = hipDeviceSynchronize();                                                          \
+      if (e_ != hipSuccess)                                                                 \
+        return set_error(DIT_E_HIP, "%s: %s after %s", __func__, hipGetErrorString(e_), #expr); \
+    }                                                                                       \
+  } while (0)
+
+#define DIT_TRY(expr)            \
+  do {                           \
+    int r_ = (expr);             \
+    if (r_ != DIT_OK) return r_; \
+  } while (0)
+
+// ============================================================================ config
+
+static int check_config(const dit_config* c) {
+  if (c == nullptr) return set_error(DIT_E_INVALID, "config is null");
+  if (c->n_blocks < 0 || c->hidden <= 0 || c->n_heads <= 0 || c->head_dim <= 0 || c->ffn <= 0)
+    return set_error(DIT_E_INVALID, "config: non-positive dimension");
+  if (c->hidden != c->n_heads * c->head_dim)
+    return set_error(DIT_E_INVALID, "config: hidden (%d) != n_heads*head_dim (%d)", c->hidden,
+                     c->n_heads * c->head_dim);
+  if (c->norm != DIT_NORM_RMS && c->norm != DIT_NORM_LAYER) return set_error(DIT_E_INVALID, "config: norm");
+  if (!(c->norm_eps > 0.f)) return set_error(DIT_E_INVALID, "config: norm_eps must be > 0");
+  if (c->mlp != DIT_MLP_GATE_UP && c->mlp != DIT_MLP_VALUE_GATE) return set_error(DIT_E_INVALID, "config: mlp");
+  if (c->stream_dtype != DIT_F32 && c->stream_dtype != DIT_BF16)
+    return set_error(DIT_E_INVALID, "config: stream_dtype");
+  if (c->rot_dim <= 0 || c->rot_dim > c->head_dim || c->rot_dim % 2)
+    return set_error(DIT_E_INVALID, "config: rot_dim must be even and in (0, head_dim]");
+  if (!(c->theta > 0.0)) return set_error(DIT_E_INVALID, "config: theta");
+  if (c->cond_dim <= 0) return set_error(DIT_E_INVALID, "config: cond_dim");
+  if (c->n_mod < 1 || c->n_mod > DIT_MAX_MODALITIES) return set_error(DIT_E_INVALID, "config: n_mod");
+  if (c->io != 0 && c->io != 1) return set_error(DIT_E_INVALID, "config: io must be 0 or 1");
+  for (int m = 0; m < c->n_mod; ++m) {
+    const dit_modality& md = c->mod[m];
+    if (md.n_axes != 1 && md.n_axes != 3) return set_error(DIT_E_INVALID, "config: modality %d n_axes", m);
+    int sum = 0;
+    for (int a = 0; a < md.n_axes; ++a) {
+      if (md.axis_dim[a] <= 0 || md.axis_dim[a] % 2)
+        return set_error(DIT_E_INVALID, "config: modality %d axis_dim[%d] must be positive and even", m, a);
+      sum += md.axis_dim[a];
+    }
+    if (sum != c->rot_dim) return set_error(DIT_E_INVALID, "config: modality %d axis dims sum to %d, rot_dim %d", m, sum, c->rot_dim);
+    if (c->io) {
+      if (md.io != DIT_IO_PATCH3D && md.io != DIT_IO_CHANNEL_MAJOR)
+        return set_error(DIT_E_INVALID, "config: modality %d needs an io kind", m);
+      if (md.channels <= 0) return set_error(DIT_E_INVALID, "config: modality %d channels", m);
+      if (md.io == DIT_IO_PATCH3D) {
+        if (md.n_axes != 3) return set_error(DIT_E_INVALID, "config: patch3d modality %d needs 3 axes", m);
+        for (int a = 0; a < 3; ++a)
+          if (md.patch[a] <= 0) return set_error(DIT_E_INVALID, "config: modality %d patch", m);
+      } else if (md.n_axes != 1) {
+        return set_error(DIT_E_INVALID, "config: channel-major modality %d needs 1 axis", m);
+      }
+    } else if (md.io != DIT_IO_NONE) {
+      return set_error(DIT_E_INVALID, "config: modality %d has io but config.io == 0", m);
+    }
+  }
+  const bool bf = c->stream_dtype == DIT_BF16;
+  if (!modnorm_supported(c->hidden)) return set_error(DIT_E_UNSUPPORTED, "hidden %d: need a multiple of 4, <= 8192", c->hidden);
+  if (!rope_split_supported(bf, c->head_dim, c->rot_dim))
+    return set_error(DIT_E_UNSUPPORTED, "head_dim %d / rot_dim %d not supported by the rope kernel", c->head_dim, c->rot_dim);
+  if (!attention_supported(bf, c->head_dim))
+    return set_error(DIT_E_UNSUPPORTED, "head_dim %d not supported by the %s attention kernel", c->head_dim, bf ? "bf16" : "f32");
+  if (bf) {
+    if (c->hidden % 64 || c->ffn % 64) return set_error(DIT_E_UNSUPPORTED, "bf16 stream needs hidden and ffn multiples of 64");
+  } else if (c->ffn % 4) {
+    return set_error(DIT_E_UNSUPPORTED, "ffn must be a multiple of 4");
+  }
+  if (c->cond_dim % 4) return set_error(DIT_E_UNSUPPORTED, "cond_dim must be a multiple of 4");
+  return DIT_OK;
+}
+
+static int token_width(const dit_modality& m) {
+  if (m.io == DIT_IO_PATCH3D) return m.channels * m.patch[0] * m.patch[1] * m.patch[2];
+  if (m.io == DIT_IO_CHANNEL_MAJOR) return m.channels;
+  return 0;
+}
+
+// ============================================================================ model and weight contract
+
+enum SlotKind { kBlockMat = 0, kBias = 1, kIsland = 2 };
+
+struct Slot {
+  std::string name;
+  int ndim;
+  int64_t shape[2];
+  int dtype;       // slot dtype in the slab
+  int kind;
+  bool swap_halves;
+  size_t offset, bytes;
+  bool staged;
+};
+
+struct BlockPtrs {
+  const void* adaln_w[DIT_MAX_MODALITIES];
+  const float* adaln_b[DIT_MAX_MODALITIES];
+  const void *qkv_w, *out_w, *in_w, *mo_w;
+  const float *qkv_b, *out_b, *in_b, *mo_b;
+};
+
+struct dit_model {
+  dit_config cfg;
+  char* slab;
+  size_t slab_bytes;
+  std::vector<Slot> slots;
+  std::unordered_map<std::string, int> index;
+  bool finalized;
+  dit_stage_stats_t stats;
+  std::vector<BlockPtrs> blocks;
+  const float* in_w[DIT_MAX_MODALITIES];
+  const float* in_b[DIT_MAX_MODALITIES];
+  const float* out_w[DIT_MAX_MODALITIES];
+  const float* out_b[DIT_MAX_MODALITIES];
+};
+
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+static void build_contract(const dit_config& c, std::vector<Slot>* slots, size_t* total) {
+  const int64_t D = c.hidden, F = c.ffn, dt = c.cond_dim;
+  const int sd = c.stream_dtype;
+  size_t off = 0;
+  auto add = [&](const std::string& name, int ndim, int64_t s0, int64_t s1, int dtype, int kind, bool swap) {
+    Slot s;
+    s.name = name;
+    s.ndim = ndim;
+    s.shape[0] = s0;
+    s.shape[1] = s1;
+    s.dtype = dtype;
+    s.kind = kind;
+    s.swap_halves = swap;
+    const int64_t n = ndim == 1 ? s0 : s0 * s1;
+    s.bytes = static_cast<size_t>(n) * (dtype == DIT_BF16 ? 2 : 4);
+    s.offset = off;
+    s.staged = false;
+    off = align256(off + s.bytes);
+    slots->push_back(s);
+  };
+  if (c.io) {
+    for (int m = 0; m < c.n_mod; ++m) {
+      const int64_t cw = token_width(c.mod[m]);
+      add("in." + std::to_string(m) + ".weight", 2, D, cw, DIT_F32, kIsland, false);
+      add("in." + std::to_string(m) + ".bias", 1, D, 0, DIT_F32, kBias, false);
+      add("out." + std::to_string(m) + ".weight", 2, cw, D, DIT_F32, kIsland, false);
+      add("out." + std::to_string(m) + ".bias", 1, cw, 0, DIT_F32, kBias, false);
+    }
+  }
+  const bool swap = c.mlp == DIT_MLP_VALUE_GATE;
+  for (int b = 0; b < c.n_blocks; ++b) {
+    const std::string p = "blocks." + std::to_string(b) + ".";
+    for (int m = 0; m < c.n_mod; ++m) {
+      add(p + "adaln." + std::to_string(m) + ".weight", 2, 6 * D, dt, sd, kBlockMat, false);
+      add(p + "adaln." + std::to_string(m) + ".bias", 1, 6 * D, 0, DIT_F32, kBias, false);
+    }
+    add(p + "attn.qkv.weight", 2, 3 * D, D, sd, kBlockMat, false);
+    add(p + "attn.qkv.bias", 1, 3 * D, 0, DIT_F32, kBias, false);
+    add(p + "attn.out.weight", 2, D, D, sd, kBlockMat, false);
+    add(p + "attn.out.bias", 1, D, 0, DIT_F32, kBias, false);
+    add(p + "mlp.in.weight", 2, 2 * F, D, sd, kBlockMat, swap);
+    add(p + "mlp.in.bias", 1, 2 * F, 0, DIT_F32, kBias, swap);
+    add(p + "mlp.out.weight", 2, D, F, sd, kBlockMat, false);
+    add(p + "mlp.out.bias", 1, D, 0, DIT_F32, kBias, false);
+  }
+  *total = off;
+}
+
+extern "C" int dit_weight_bytes(const dit_config* cfg, size_t* bytes) {
+  DIT_TRY(check_config(cfg));
+  if (bytes == nullptr) return set_error(DIT_E_INVALID, "dit_weight_bytes: bytes is null");
+  std::vector<Slot> slots;
+  build_contract(*cfg, &slots, bytes);
+  return DIT_OK;
+}
+
+extern "C" int dit_model_create(const dit_config* cfg, void* slab, size_t slab_bytes, dit_model** out) {
+  DIT_TRY(check_config(cfg));
+  if (out == nullptr) return set_error(DIT_E_INVALID, "dit_model_create: out is null");
+  std::vector<Slot> slots;
+  size_t need;
+  build_contract(*cfg, &slots, &need);
+  if (need > 0 && slab == nullptr) return set_error(DIT_E_INVALID, "dit_model_create: weight slab is null");
+  if (reinterpret_cast<uintptr_t>(slab) % 256) return set_error(DIT_E_INVALID, "dit_model_create: slab must be 256-byte aligned");
+  if (slab_bytes < need)
+    return set_error(DIT_E_WORKSPACE, "dit_model_create: slab of %zu bytes, %zu needed", slab_bytes, need);
+  dit_model* m = new (std::nothrow) dit_model();
+  if (m == nullptr) return set_error(DIT_E_INVALID, "dit_model_create: out of host memory");
+  m->cfg = *cfg;
+  m->slab = static_cast<char*>(slab);
+  m->slab_bytes = slab_bytes;
+  m->slots = std::move(slots);
+  for (size_t i = 0; i < m->slots.size(); ++i) m->index[m->slots[i].name] = static_cast<int>(i);
+  m->finalized = false;
+  std::memset(&m->stats, 0, sizeof m->stats);
+  *out = m;
+  return DIT_OK;
+}
+
+extern "C" void dit_model_destroy(dit_model* m) { delete m; }
+
+static inline uint16_t host_f32_to_bf16(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+extern "C" int dit_stage_weights(dit_model* m, const dit_weight_view* views, int n, dit_stream_t stream) {
+  if (m == nullptr || (n > 0 && views == nullptr)) return set_error(DIT_E_INVALID, "dit_stage_weights: null argument");
+  if (m->finalized) return set_error(DIT_E_STATE, "dit_stage_weights: staging is already finalized");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  std::vector<uint8_t> conv;
+  for (int i = 0; i < n; ++i) {
+    const dit_weight_view& v = views[i];
+    if (v.name == nullptr) return set_error(DIT_E_INVALID, "dit_stage_weights: view %d has no name", i);
+    auto it = m->index.find(v.name);
+    if (it == m->index.end()) return set_error(DIT_E_UNKNOWN_WEIGHT, "unknown weight '%s'", v.name);
+    Slot& sl = m->slots[it->second];
+    if (sl.staged) return set_error(DIT_E_INVALID, "weight '%s' staged twice", v.name);
+    bool shape_ok = v.ndim == sl.ndim;
+    for (int d = 0; shape_ok && d < sl.ndim; ++d) shape_ok = v.shape[d] == sl.shape[d];
+    if (!shape_ok) {
+      return set_error(DIT_E_SHAPE, "weight '%s': shape mismatch (expected [%lld%s%lld])", v.name,
+                       static_cast<long long>(sl.shape[0]), sl.ndim == 2 ? ", " : "",
+                       sl.ndim == 2 ? static_cast<long long>(sl.shape[1]) : 0LL);
+    }
+    if (v.dtype != DIT_F32 && v.dtype != DIT_BF16) return set_error(DIT_E_DTYPE, "weight '%s': dtype %d", v.name, v.dtype);
+    if (v.host == nullptr) return set_error(DIT_E_INVALID, "weight '%s': host pointer is null", v.name);
+    const int64_t count = sl.ndim == 1 ? sl.shape[0] : sl.shape[0] * sl.shape[1];
+    const void* src = v.host;
+    const bool need_conv = v.dtype != sl.dtype || sl.swap_halves;
+    if (need_conv) {
+      conv.resize(sl.bytes);
+      const int64_t rows = sl.shape[0];
+      const int64_t cols = sl.ndim == 1 ? 1 : sl.shape[1];
+      for (int64_t r = 0; r < rows; ++r) {
+        // mlp.in of a [value | gate] model: destination row r takes source row (r + rows/2) % rows.
+        const int64_t sr = sl.swap_halves ? (r + rows / 2) % rows : r;
+        for (int64_t c = 0; c < cols; ++c) {
+          const int64_t di = r * cols + c, si = sr * cols + c;
+          if (sl.dtype == DIT_BF16) {
+            uint16_t b;
+            if (v.dtype == DIT_BF16) b = static_cast<const uint16_t*>(v.host)[si];
+            else b = host_f32_to_bf16(static_cast<const float*>(v.host)[si]);
+            reinterpret_cast<uint16_t*>(conv.data())[di] = b;
+          } else {
+            float f;
+            if (v.dtype == DIT_F32) {
+              f = static_cast<const float*>(v.host)[si];
+            } else {
+              const uint32_t u = static_cast<uint32_t>(static_cast<const uint16_t*>(v.host)[si]) << 16;
+              std::memcpy(&f, &u, 4);
+            }
+            reinterpret_cast<float*>(conv.data())[di] = f;
+          }
+        }
+      }
+      src = conv.data();
+      if (static_cast<int64_t>(conv.size()) > m->stats.host_peak) m->stats.host_peak = static_cast<int64_t>(conv.size());
+      m->stats.converted++;
+    } else {
+      m->stats.direct++;
+    }
+    (void)count;
+    hipError_t e = hipMemcpyAsync(m->slab + sl.offset, src, sl.bytes, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return set_error(DIT_E_HIP, "staging '%s': %s", v.name, hipGetErrorString(e));
+    sl.staged = true;
+    m->stats.tensors++;
+    m->stats.bytes += static_cast<int64_t>(sl.bytes);
+    if (conv.capacity() > 0) std::vector<uint8_t>().swap(conv);  // one tensor's buffer at a time
+  }
+  return DIT_OK;
+}
+
+extern "C" int dit_stage_finalize(dit_model* m) {
+  if (m == nullptr) return set_error(DIT_E_INVALID, "dit_stage_finalize: model is null");
+  if (m->finalized) return set_error(DIT_E_STATE, "dit_stage_finalize: already finalized");
+  for (const Slot& s : m->slots)
+    if (!s.staged) return set_error(DIT_E_MISSING_WEIGHT, "missing weight '%s'", s.name.c_str());
+  const dit_config& c = m->cfg;
+  auto ptr = [&](const std::string& n) -> char* { return m->slab + m->slots[m->index.at(n)].offset; };
+  m->blocks.resize(c.n_blocks);
+  for (int b = 0; b < c.n_blocks; ++b) {
+    const std::string p = "blocks." + std::to_string(b) + ".";
+    BlockPtrs& bp = m->blocks[b];
+    for (int mm = 0; mm < DIT_MAX_MODALITIES; ++mm) {
+      bp.adaln_w[mm] = mm < c.n_mod ? ptr(p + "adaln." + std::to_string(mm) + ".weight") : nullptr;
+      bp.adaln_b[mm] = mm < c.n_mod ? reinterpret_cast<const float*>(ptr(p + "adaln." + std::to_string(mm) + ".bias")) : nullptr;
+    }
+    bp.qkv_w = ptr(p + "attn.qkv.weight");
+    bp.qkv_b = reinterpret_cast<const float*>(ptr(p + "attn.qkv.bias"));
+    bp.out_w = ptr(p + "attn.out.weight");
+    bp.out_b = reinterpret_cast<const float*>(ptr(p + "attn.out.bias"));
+    bp.in_w = ptr(p + "mlp.in.weight");
+    bp.in_b = reinterpret_cast<const float*>(ptr(p + "mlp.in.bias"));
+    bp.mo_w = ptr(p + "mlp.out.weight");
+    bp.mo_b = reinterpret_cast<const float*>(ptr(p + "mlp.out.bias"));
+  }
+  for (int mm = 0; mm < DIT_MAX_MODALITIES; ++mm) {
+    const bool has = c.io && mm < c.n_mod;
+    m->in_w[mm] = has ? reinterpret_cast<const float*>(ptr("in." + std::to_string(mm) + ".weight")) : nullptr;
+    m->in_b[mm] = has ? reinterpret_cast<const float*>(ptr("in." + std::to_string(mm) + ".bias")) : nullptr;
+    m->out_w[mm] = has ? reinterpret_cast<const float*>(ptr("out." + std::to_string(mm) + ".weight")) : nullptr;
+    m->out_b[mm] = has ? reinterpret_cast<const float*>(ptr("out." + std::to_string(mm) + ".bias")) : nullptr;
+  }
+  m->finalized = true;
+  return DIT_OK;
+}
+
+extern "C" int dit_stage_stats(const dit_model* m, dit_stage_stats_t* out) {
+  if (m == nullptr || out == nullptr) return set_error(DIT_E_INVALID, "dit_stage_stats: null argument");
+  *out = m->stats;
+  return DIT_OK;
+}
+
+// ============================================================================ batch
+
+struct dit_batch {
+  const dit_model* model;
+  int N, n_segs, max_seqlen, n_cond;
+  std::vector<dit_segment> segs;
+  std::vector<int32_t> cu;          // host copy of cu_seqlens
+  std::vector<int> cond_mod;        // modality of each modulation row
+  std::vector<int64_t> lat_off;     // float offset of each segment's latent
+  int64_t latent_floats;
+  int max_seg_tokens;
+  const int32_t* cu_dev;
+  const int32_t* cond_dev;
+  const float* cos_dev;
+  const float* sin_dev;
+};
+
+struct TableLayout {
+  size_t cu, cond, cos, sin, total;
+};
+
+static TableLayout table_layout(int N, int n_segs, int half) {
+  TableLayout t;
+  size_t off = 0;
+  t.cu = off;
+  off = align256(off + sizeof(int32_t) * (n_segs + 1));
+  t.cond = off;
+  off = align256(off + sizeof(int32_t) * N);
+  t.cos = off;
+  off = align256(off + sizeof(float) * static_cast<size_t>(N) * half);
+  t.sin = off;
+  off = align256(off + sizeof(float) * static_cast<size_t>(N) * half);
+  t.total = off;
+  return t;
+}
+
+static int64_t segment_latent_floats(const dit_config& c, const dit_segment& s) {
+  const dit_modality& md = c.mod[s.modality];
+  if (md.io == DIT_IO_PATCH3D)
+    return static_cast<int64_t>(md.channels) * s.grid[0] * md.patch[0] * s.grid[1] * md.patch[1] * s.grid[2] * md.patch[2];
+  if (md.io == DIT_IO_CHANNEL_MAJOR) return static_cast<int64_t>(md.channels) * s.grid[0];
+  return 0;
+}
+
+extern "C" int dit_batch_bytes(const dit_model* m, const dit_segment* segs, int n_segs, size_t* bytes) {
+  if (m == nullptr || bytes == nullptr) return set_error(DIT_E_INVALID, "dit_batch_bytes: null argument");
+  std::vector<int32_t> cu(static_cast<size_t>(n_segs > 0 ? n_segs : 0) + 1);
+  int N;
+  DIT_TRY(dit_pack_layout(&m->cfg, segs, n_segs, cu.data(), nullptr, nullptr, &N));
+  *bytes = table_layout(N, n_segs, m->cfg.rot_dim / 2).total;
+  return DIT_OK;
+}
+
+extern "C" int dit_batch_create(const dit_model* m, const dit_segment* segs, int n_segs, int n_cond,
+                                const int* cond_modality, void* tables_dev, size_t tables_bytes,
+                                dit_stream_t stream, dit_batch** out) {
+  if (m == nullptr || out == nullptr || tables_dev == nullptr || cond_modality == nullptr)
+    return set_error(DIT_E_INVALID, "dit_batch_create: null argument");
+  if (n_cond < 1 || n_cond > DIT_MAX_COND) return set_error(DIT_E_INVALID, "dit_batch_create: n_cond=%d", n_cond);
+  const dit_config& c = m->cfg;
+  for (int i = 0; i < n_cond; ++i)
+    if (cond_modality[i] < 0 || cond_modality[i] >= c.n_mod)
+      return set_error(DIT_E_INVALID, "dit_batch_create: cond_modality[%d]=%d", i, cond_modality[i]);
+  std::vector<int32_t> cu(static_cast<size_t>(n_segs > 0 ? n_segs : 0) + 1);
+  int N;
+  DIT_TRY(dit_pack_layout(&c, segs, n_segs, cu.data(), nullptr, nullptr, &N));
+  for (int i = 0; i < n_segs; ++i) {
+    if (segs[i].cond_row >= n_cond)
+      return set_error(DIT_E_INVALID, "dit_batch_create: segment %d uses cond_row %d >= n_cond %d", i, segs[i].cond_row, n_cond);
+    if (c.mod[segs[i].modality].n_axes == 1 && (segs[i].grid[1] != 1 || segs[i].grid[2] != 1))
+      return set_error(DIT_E_INVALID, "dit_batch_create: segment %d is 1-axis but grid[1..2] != 1", i);
+  }
+  const int half = c.rot_dim / 2;
+  TableLayout tl = table_layout(N, n_segs, half);
+  if (tables_bytes < tl.total)
+    return set_error(DIT_E_WORKSPACE, "dit_batch_create: table buffer of %zu bytes, %zu needed", tables_bytes, tl.total);
+  std::vector<uint8_t> host(tl.total, 0);
+  std::vector<int32_t> cu2(n_segs + 1);
+  DIT_TRY(dit_pack_layout(&c, segs, n_segs, cu2.data(), reinterpret_cast<int32_t*>(host.data() + tl.cond), nullptr, &N));
+  std::memcpy(host.data() + tl.cu, cu2.data(), sizeof(int32_t) * (n_segs + 1));
+  DIT_TRY(dit_rope_cache_build(&c, segs, n_segs, reinterpret_cast<float*>(host.data() + tl.cos),
+                               reinterpret_cast<float*>(host.data() + tl.sin)));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(tables_dev, host.data(), tl.total, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return set_error(DIT_E_HIP, "dit_batch_create: %s", hipGetErrorString(e));
+
+  dit_batch* b = new (std::nothrow) dit_batch();
+  if (b == nullptr) return set_error(DIT_E_INVALID, "dit_batch_create: out of host memory");
+  b->model = m;
+  b->N = N;
+  b->n_segs = n_segs;
+  b->n_cond = n_cond;
+  b->segs.assign(segs, segs + n_segs);
+  b->cu = cu2;
+  b->cond_mod.assign(cond_modality, cond_modality + n_cond);
+  b->max_seqlen = 0;
+  b->max_seg_tokens = 0;
+  b->latent_floats = 0;
+  for (int i = 0; i < n_segs; ++i) {
+    const int len = cu2[i + 1] - cu2[i];
+    if (len > b->max_seqlen) b->max_seqlen = len;
+    b->lat_off.push_back(b->latent_floats);
+    b->latent_floats += c.io ? segment_latent_floats(c, segs[i]) : 0;
+  }
+  b->max_seg_tokens = b->max_seqlen;
+  char* base = static_cast<char*>(tables_dev);
+  b->cu_dev = reinterpret_cast<const int32_t*>(base + tl.cu);
+  b->cond_dev = reinterpret_cast<const int32_t*>(base + tl.cond);
+  b->cos_dev = reinterpret_cast<const float*>(base + tl.cos);
+  b->sin_dev = reinterpret_cast<const float*>(base + tl.sin);
+  *out = b;
+  return DIT_OK;
+}
+
+extern "C" void dit_batch_destroy(dit_batch* b) { delete b; }
+
+extern "C" int dit_batch_info(const dit_batch* b, int* n_tokens, int* n_segs, int* max_seqlen, int64_t* latent_floats) {
+  if (b == nullptr) return set_error(DIT_E_INVALID, "dit_batch_info: batch is null");
+  if (n_tokens) *n_tokens = b->N;
+  if (n_segs) *n_segs = b->n_segs;
+  if (max_seqlen) *max_seqlen = b->max_seqlen;
+  if (latent_floats) *latent_floats = b->latent_floats;
+  return DIT_OK;
+}
+
+extern "C" int dit_batch_tables(const dit_batch* b, const int32_t** cu, const int32_t** cond, const float** cos,
+                                const float** sin) {
+  if (b == nullptr) return set_error(DIT_E_INVALID, "dit_batch_tables: batch is null");
+  if (cu) *cu = b->cu_dev;
+  if (cond) *cond = b->cond_dev;
+  if (cos) *cos = b->cos_dev;
+  if (sin) *sin = b->sin_dev;
+  return DIT_OK;
+}
+
+// ============================================================================ workspace plan
+
+struct WsPlan {
+  size_t mod, x, h, big, qkvh, o, a, gemm, tok, vtok, vel, total;
+};
+
+static size_t gemm_ws(const dit_config& c, int M, int N, int K) {
+  return c.stream_dtype == DIT_BF16 ? gemm_bf16_ws_bytes(M, N, K) : gemm_f32_ws_bytes(M, N, K);
+}
+
+static WsPlan plan_ws(const dit_model* m, const dit_batch* b) {
+  const dit_config& c = m->cfg;
+  const size_t N = b->N, D = c.hidden, F = c.ffn;
+  const size_t es = c.stream_dtype == DIT_BF16 ? 2 : 4;
+  WsPlan p;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  p.mod = take(sizeof(float) * c.n_blocks * b->n_cond * 6 * D);
+  p.x = take(c.io ? sizeof(float) * N * D : 0);
+  p.h = take(es * N * D);
+  p.big = take(es * N * (3 * D > 2 * F ? 3 * D : 2 * F));
+  p.qkvh = take(es * N * (3 * D > F ? 3 * D : F));
+  p.o = take(es * N * D);
+  p.a = take(sizeof(float) * N * D);
+  size_t g = 0;
+  auto upd = [&](size_t v) { g = v > g ? v : g; };
+  const int Ni = static_cast<int>(N);
+  upd(gemm_ws(c, Ni, 3 * D, D));
+  upd(gemm_ws(c, Ni, D, D));
+  upd(gemm_ws(c, Ni, 2 * F, D));
+  upd(gemm_ws(c, Ni, D, F));
+  size_t tok = 0;
+  if (c.io) {
+    for (int mm = 0; mm < c.n_mod; ++mm) {
+      const int cw = token_width(c.mod[mm]);
+      upd(gemm_f32_ws_bytes(b->max_seg_tokens, D, cw));
+      upd(gemm_f32_ws_bytes(b->max_seg_tokens, cw, D));
+      const size_t t = sizeof(float) * b->max_seg_tokens * cw;
+      tok = t > tok ? t : tok;
+    }
+  }
+  p.gemm = take(g);
+  p.tok = take(tok);
+  p.vtok = take(tok);
+  p.vel = take(c.io ? sizeof(float) * b->latent_floats : 0);
+  p.total = off;
+  return p;
+}
+
+extern "C" int dit_workspace_bytes(const dit_model* m, const dit_batch* b, size_t* bytes) {
+  if (m == nullptr || b == nullptr || bytes == nullptr) return set_error(DIT_E_INVALID, "dit_workspace_bytes: null argument");
+  if (b->model != m) return set_error(DIT_E_INVALID, "dit_workspace_bytes: batch belongs to another model");
+  *bytes = plan_ws(m, b).total;
+  return DIT_OK;
+}
+
+// ============================================================================ forward
+
+static int check_run(const dit_model* m, const dit_batch* b, void* ws, size_t ws_bytes, WsPlan* plan) {
+  if (m == nullptr || b == nullptr) return set_error(DIT_E_INVALID, "model or batch is null");
+  if (!m->finalized) return set_error(DIT_E_STATE, "weights are not finalized");
+  if (b->model != m) return set_error(DIT_E_INVALID, "batch belongs to another model");
+  *plan = plan_ws(m, b);
+  if (ws_bytes < plan->total)
+    return set_error(DIT_E_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, plan->total);
+  if (plan->total > 0 && ws == nullptr) return set_error(DIT_E_INVALID, "workspace is null");
+  return DIT_OK;
+}
+
+static hipError_t launch_gemm(const dit_config& c, int M, int N, int K, const void* A, const void* W,
+                              const float* bias, void* C, bool c_f32, void* ws, hipStream_t s) {
+  if (c.stream_dtype == DIT_BF16)
+    return gemm_bf16(M, N, K, static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W), bias, C, c_f32, ws, s);
+  return gemm_f32(M, N, K, static_cast<const float*>(A), static_cast<const float*>(W), bias, static_cast<float*>(C), ws, s);
+}
+
+static int run_block(dit_model* m, int blk, float* x, const float* mod, const dit_batch* b, char* ws,
+                     const WsPlan& p, hipStream_t s) {
+  const dit_config& c = m->cfg;
+  const BlockPtrs& w = m->blocks[blk];
+  const int N = b->N, D = c.hidden, F = c.ffn, H = c.n_heads, hd = c.head_dim;
+  const bool bf = c.stream_dtype == DIT_BF16;
+  const size_t es = bf ? 2 : 4;
+  void* h = ws + p.h;
+  void* big = ws + p.big;
+  char* qkvh = ws + p.qkvh;
+  void* o = ws + p.o;
+  float* a = reinterpret_cast<float*>(ws + p.a);
+  void* gws = ws + p.gemm;
+  void* q = qkvh;
+  void* k = qkvh + es * N * D;
+  void* v = qkvh + 2 * es * N * D;
+  // attention sub-layer
+  DIT_HIP(modnorm(bf, c.norm, c.norm_eps, N, D, x, mod, 0, b->cond_dev, h, s));
+  DIT_HIP(launch_gemm(c, N, 3 * D, D, h, w.qkv_w, w.qkv_b, big, false, gws, s));
+  DIT_HIP(rope_split(bf, N, H, hd, c.rot_dim, big, b->cos_dev, b->sin_dev, q, k, v, s));
+  if (bf)
+    DIT_HIP(attention_bf16(N, H, hd, b->n_segs, b->cu_dev, b->max_seqlen, static_cast<const uint16_t*>(q),
+                           static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), s));
+  else
+    DIT_HIP(attention_f32(N, H, hd, b->n_segs, b->cu_dev, b->max_seqlen, static_cast<const float*>(q),
+                          static_cast<const float*>(k), static_cast<const float*>(v), static_cast<float*>(o), s));
+  DIT_HIP(launch_gemm(c, N, D, D, o, w.out_w, w.out_b, a, true, gws, s));
+  DIT_HIP(gated_residual(N, D, x, a, mod, 0, b->cond_dev, s));
+  // MLP sub-layer
+  DIT_HIP(modnorm(bf, c.norm, c.norm_eps, N, D, x, mod, 1, b->cond_dev, h, s));
+  DIT_HIP(launch_gemm(c, N, 2 * F, D, h, w.in_w, w.in_b, big, false, gws, s));
+  DIT_HIP(silu_gate(bf, N, F, big, qkvh, s));
+  DIT_HIP(launch_gemm(c, N, D, F, qkvh, w.mo_w, w.mo_b, a, true, gws, s));
+  DIT_HIP(gated_residual(N, D, x, a, mod, 1, b->cond_dev, s));
+  return DIT_OK;
+}
+
+static int run_modulation(dit_model* m, const dit_batch* b, int block0, int nb, const float* cond, float* mod,
+                          hipStream_t s) {
+  const dit_config& c = m->cfg;
+  std::vector<AdalnBlockPtrs> ptrs(nb);
+  for (int i = 0; i < nb; ++i) {
+    for (int mm = 0; mm < 4; ++mm) {
+      ptrs[i].w[mm] = m->blocks[block0 + i].adaln_w[mm];
+      ptrs[i].bias[mm] = m->blocks[block0 + i].adaln_b[mm];
+    }
+  }
+  DIT_HIP(adaln(c.stream_dtype == DIT_BF16, nb, ptrs.data(), b->n_cond, b->cond_mod.data(), 6 * c.hidden, c.cond_dim,
+                cond, mod, s));
+  return DIT_OK;
+}
+
+extern "C" int dit_modulation(dit_model* m, const dit_batch* b, int block0, int n_blocks, const float* cond_dev,
+                              float* mod_dev, dit_stream_t stream) {
+  if (m == nullptr || b == nullptr || cond_dev == nullptr || mod_dev == nullptr)
+    return set_error(DIT_E_INVALID, "dit_modulation: null argument");
+  if (!m->finalized) return set_error(DIT_E_STATE, "dit_modulation: weights are not finalized");
+  if (block0 < 0 || n_blocks < 0 || block0 + n_blocks > m->cfg.n_blocks)
+    return set_error(DIT_E_INVALID, "dit_modulation: blocks [%d, %d) outside the model", block0, block0 + n_blocks);
+  return run_modulation(m, b, block0, n_blocks, cond_dev, mod_dev, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int dit_block_forward(dit_model* m, int block, float* x_dev, const float* mod_dev, const dit_batch* b,
+                                 void* ws_dev, size_t ws_bytes, dit_stream_t stream) {
+  WsPlan p;
+  DIT_TRY(check_run(m, b, ws_dev, ws_bytes, &p));
+  if (block < 0 || block >= m->cfg.n_blocks) return set_error(DIT_E_INVALID, "dit_block_forward: block %d", block);
+  if (x_dev == nullptr || mod_dev == nullptr) return set_error(DIT_E_INVALID, "dit_block_forward: x or mod is null");
+  return run_block(m, block, x_dev, mod_dev, b, static_cast<char*>(ws_dev), p, reinterpret_cast<hipStream_t>(stream));
+}
+
+static int run_forward(dit_model* m, const dit_batch* b, const float* in, const float* cond, float* out, char* ws,
+                       const WsPlan& p, hipStream_t s) {
+  const dit_config& c = m->cfg;
+  const int N = b->N, D = c.hidden;
+  float* mod = reinterpret_cast<float*>(ws + p.mod);
+  DIT_TRY(run_modulation(m, b, 0, c.n_blocks, cond, mod, s));
+  float* x;
+  if (c.io) {
+    x = reinterpret_cast<float*>(ws + p.x);
+    float* tok = reinterpret_cast<float*>(ws + p.tok);
+    for (int i = 0; i < b->n_segs; ++i) {
+      const dit_segment& sg = b->segs[i];
+      const dit_modality& md = c.mod[sg.modality];
+      const int n = b->cu[i + 1] - b->cu[i];
+      const int cw = token_width(md);
+      DIT_HIP(patch_in(md.io, md.channels, md.patch, sg.grid, in + b->lat_off[i], tok, s));
+      DIT_HIP(gemm_f32(n, D, cw, tok, m->in_w[sg.modality], m->in_b[sg.modality], x + static_cast<size_t>(b->cu[i]) * D,
+                       ws + p.gemm, s));
+    }
+  } else {
+    x = out;
+    if (in != out) DIT_HIP(hipMemcpyAsync(out, in, sizeof(float) * N * D, hipMemcpyDeviceToDevice, s));
+  }
+  for (int blk = 0; blk < c.n_blocks; ++blk) {
+    const float* mb = mod + static_cast<size_t>(blk) * b->n_cond * 6 * D;
+    DIT_TRY(run_block(m, blk, x, mb, b, ws, p, s));
+  }
+  if (!c.io) return DIT_OK;
+  float* y = reinterpret_cast<float*>(ws + p.a);  // final norm, fp32
+  DIT_HIP(modnorm(false, c.norm, c.norm_eps, N, D, x, nullptr, 0, nullptr, y, s));
+  float* vtok = reinterpret_cast<float*>(ws + p.vtok);
+  for (int i = 0; i < b->n_segs; ++i) {
+    const dit_segment& sg = b->segs[i];
+    const dit_modality& md = c.mod[sg.modality];
+    const int n = b->cu[i + 1] - b->cu[i];
+    const int cw = token_width(md);
+    DIT_HIP(gemm_f32(n, cw, D, y + static_cast<size_t>(b->cu[i]) * D, m->out_w[sg.modality], m->out_b[sg.modality], vtok,
+                     ws + p.gemm, s));
+    DIT_HIP(patch_out(md.io, md.channels, md.patch, sg.grid, vtok, out + b->lat_off[i], s));
+  }
+  return DIT_OK;
+}
+
+extern "C" int dit_forward(dit_model* m, const dit_batch* b, const float* in_dev, const float* cond_dev, float* out_dev,
+                           void* ws_dev, size_t ws_bytes, dit_stream_t stream) {
+  WsPlan p;
+  DIT_TRY(check_run(m, b, ws_dev, ws_bytes, &p));
+  if (in_dev == nullptr || cond_dev == nullptr || out_dev == nullptr)
+    return set_error(DIT_E_INVALID, "dit_forward: null input, cond or output");
+  return run_forward(m, b, in_dev, cond_dev, out_dev, static_cast<char*>(ws_dev), p,
+                     reinterpret_cast<hipStream_t>(stream));
+}
+
+static int run_step(dit_model* m, const dit_batch* b, float* lat, const float* cond, const float* dt, char* ws,
+                    const WsPlan& p, hipStream_t s) {
+  float* vel = reinterpret_cast<float*>(ws + p.vel);
+  DIT_TRY(run_forward(m, b, lat, cond, vel, ws, p, s));
+  for (int i = 0; i < b->n_segs; ++i) {
+    const int64_t n = (i + 1 < b->n_segs ? b->lat_off[i + 1] : b->latent_floats) - b->lat_off[i];
+    DIT_HIP(euler(n, lat + b->lat_off[i], vel + b->lat_off[i], dt + b->segs[i].modality, s));
+  }
+  return DIT_OK;
+}
+
+extern "C" int dit_denoise_step(dit_model* m, const dit_batch* b, float* latents_dev, const float* cond_dev,
+                                const float* dt_dev, void* ws_dev, size_t ws_bytes, dit_stream_t stream) {
+  WsPlan p;
+  DIT_TRY(check_run(m, b, ws_dev, ws_bytes, &p));
+  if (!m->cfg.io) return set_error(DIT_E_INVALID, "dit_denoise_step: the model has no latent io");
+  if (latents_dev == nullptr || cond_dev == nullptr || dt_dev == nullptr)
+    return set_error(DIT_E_INVALID, "dit_denoise_step: null argument");
+  return run_step(m, b, latents_dev, cond_dev, dt_dev, static_cast<char*>(ws_dev), p,
+                  reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int dit_denoise_loop(dit_model* m, const dit_batch* b, float* latents_dev, const float* cond_table_dev,
+                                const float* dt_table_dev, int n_steps, void* ws_dev, size_t ws_bytes,
+                                dit_stream_t stream) {
+  WsPlan p;
+  DIT_TRY(check_run(m, b, ws_dev, ws_bytes, &p));
+  if (!m->cfg.io) return set_error(DIT_E_INVALID, "dit_denoise_loop: the model has no latent io");
+  if (latents_dev == nullptr || cond_table_dev == nullptr || dt_table_dev == nullptr || n_steps < 0)
+    return set_error(DIT_E_INVALID, "dit_denoise_loop: bad argument");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t cstride = static_cast<size_t>(b->n_cond) * m->cfg.cond_dim;
+  for (int i = 0; i < n_steps; ++i)
+    DIT_TRY(run_step(m, b, latents_dev, cond_table_dev + i * cstride, dt_table_dev + static_cast<size_t>(i) * m->cfg.n_mod,
+                     static_cast<char*>(ws_dev), p, s));
+  return DIT_OK;
+}
+
+// ============================================================================ op-level calls
+
+extern "C" int dit_gemm_workspace_bytes(int dtype, int M, int N, int K, size_t* bytes) {
+  if (bytes == nullptr || M < 0 || N <= 0 || K <= 0) return set_error(DIT_E_INVALID, "dit_gemm_workspace_bytes: bad argument");
+  *bytes = dtype == DIT_BF16 ? gemm_bf16_ws_bytes(M, N, K) : gemm_f32_ws_bytes(M, N, K);
+  return DIT_OK;
+}
+
+extern "C" int dit_gemm(int dtype, int M, int N, int K, const void* A, const void* B, const float* bias, void* C,
+                        int c_dtype, void* ws, size_t ws_bytes, dit_stream_t stream) {
+  if (M < 0 || N <= 0 || K <= 0) return set_error(DIT_E_INVALID, "dit_gemm: M=%d N=%d K=%d", M, N, K);
+  if (M > 0 && (A == nullptr || B == nullptr || C == nullptr)) return set_error(DIT_E_INVALID, "dit_gemm: null operand");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == DIT_BF16) {
+    if (!gemm_bf16_supported(M, N, K)) return set_error(DIT_E_UNSUPPORTED, "dit_gemm bf16: K=%d must be a multiple of 64", K);
+    if (c_dtype != DIT_F32 && c_dtype != DIT_BF16) return set_error(DIT_E_INVALID, "dit_gemm: c_dtype");
+    DIT_HIP(gemm_bf16(M, N, K, static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), bias, C,
+                      c_dtype == DIT_F32, ws, s));
+    return DIT_OK;
+  }
+  if (dtype != DIT_F32) return set_error(DIT_E_INVALID, "dit_gemm: dtype");
+  if (c_dtype != DIT_F32) return set_error(DIT_E_INVALID, "dit_gemm f32: C must be f32");
+  if (!gemm_f32_supported(M, N, K)) return set_error(DIT_E_UNSUPPORTED, "dit_gemm f32: K=%d must be a multiple of 4", K);
+  const size_t need = gemm_f32_ws_bytes(M, N, K);
+  if (ws_bytes < need) return set_error(DIT_E_WORKSPACE, "dit_gemm: workspace of %zu bytes, %zu needed", ws_bytes, need);
+  if (need > 0 && ws == nullptr) return set_error(DIT_E_INVALID, "dit_gemm: workspace is null");
+  DIT_HIP(gemm_f32(M, N, K, static_cast<const float*>(A), static_cast<const float*>(B), bias, static_cast<float*>(C), ws, s));
+  return DIT_OK;
+}
+
+extern "C" int dit_modnorm(int dtype, int norm, float eps, int N, int D, const float* x, const float* mod, int which,
+                           const int32_t* cond_idx, void* h, dit_stream_t stream) {
+  if (N < 0 || !modnorm_supported(D)) return set_error(DIT_E_INVALID, "dit_modnorm: N=%d D=%d", N, D);
+  if (norm != DIT_NORM_RMS && norm != DIT_NORM_LAYER) return set_error(DIT_E_INVALID, "dit_modnorm: norm");
+  if (which != 0 && which != 1) return set_error(DIT_E_INVALID, "dit_modnorm: which");
+  if (mod != nullptr && cond_idx == nullptr) return set_error(DIT_E_INVALID, "dit_modnorm: cond_idx is null");
+  if (dtype != DIT_F32 && dtype != DIT_BF16) return set_error(DIT_E_INVALID, "dit_modnorm: dtype");
+  DIT_HIP(modnorm(dtype == DIT_BF16, norm, eps, N, D, x, mod, which, cond_idx, h, reinterpret_cast<hipStream_t>(stream)));
+  return DIT_OK;
+}
+
+extern "C" int dit_rope_split(int dtype, int N, int H, int hd, int rot, const void* qkv, const float* cos, const float* sin,
+                              void* q, void* k, void* v, dit_stream_t stream) {
+  const bool bf = dtype == DIT_BF16;
+  if (N < 0 || H <= 0 || !rope_split_supported(bf, hd, rot)) return set_error(DIT_E_INVALID, "dit_rope_split: shape");
+  DIT_HIP(rope_split(bf, N, H, hd, rot, qkv, cos, sin, q, k, v, reinterpret_cast<hipStream_t>(stream)));
+  return DIT_OK;
+}
+
+extern "C" int dit_attention(int dtype, int N, int H, int hd, int n_docs, const int32_t* cu, int max_seqlen, const void* q,
+                             const void* k, const void* v, void* o, dit_stream_t stream) {
+  const bool bf = dtype == DIT_BF16;
+  if (N < 0 || H <= 0 || n_docs < 0 || max_seqlen < 0 || !attention_supported(bf, hd))
+    return set_error(DIT_E_INVALID, "dit_attention: shape");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (bf)
+    DIT_HIP(attention_bf16(N, H, hd, n_docs, cu, max_seqlen, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                           static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), s));
+  else
+    DIT_HIP(attention_f32(N, H, hd, n_docs, cu, max_seqlen, static_cast<const float*>(q), static_cast<const float*>(k),
+                          static_cast<const float*>(v), static_cast<float*>(o), s));
+  return DIT_OK;
+}
+
+extern "C" int dit_silu_gate(int dtype, int N, int F, const void* u, void* m, dit_stream_t stream) {
+  const bool bf = dtype == DIT_BF16;
+  if (N < 0 || F <= 0 || F % (bf ? 8 : 4)) return set_error(DIT_E_INVALID, "dit_silu_gate: F=%d", F);
+  DIT_HIP(silu_gate(bf, N, F, u, m, reinterpret_cast<hipStream_t>(stream)));
+  return DIT_OK;
+}
+
+extern "C" int dit_gated_residual(int N, int D, float* x, const float* a, const float* mod, int which,
+                                  const int32_t* cond_idx, dit_stream_t stream) {
+  if (N < 0 || D <= 0 || D % 4 || (which != 0 && which != 1)) return set_error(DIT_E_INVALID, "dit_gated_residual: shape");
+  DIT_HIP(gated_residual(N, D, x, a, mod, which, cond_idx, reinterpret_cast<hipStream_t>(stream)));
+  return DIT_OK;
+}
+
+// ============================================================================ diagnostics
+
+extern "C" const char* dit_last_error(void) { return g_error.c_str(); }
+
+extern "C" int dit_counters(int64_t* out, int n_max) {
+  if (out == nullptr) return set_error(DIT_E_INVALID, "dit_counters: out is null");
+  for (int i = 0; i < n_max && i < kCntNum; ++i) out[i] = g_counters[i].load();
+  return DIT_OK;
+}
+
+extern "C" void dit_counters_reset(void) {
+  for (int i = 0; i < kCntNum; ++i) g_counters[i].store(0);
+}
+
+extern "C" int dit_profile_begin(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof.clear();
+  g_events_used = 0;
+  g_prof_on.store(true);
+  return DIT_OK;
+}
+
+extern "C" int dit_profile_end(int64_t* counts, double* total_ms, int n_max) {
+  g_prof_on.store(false);
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (counts == nullptr || total_ms == nullptr) return set_error(DIT_E_INVALID, "dit_profile_end: null output");
+  for (int i = 0; i < n_max; ++i) {
+    counts[i] = 0;
+    total_ms[i] = 0.0;
+  }
+  for (const ProfRecord& r : g_prof) {
+    hipError_t e = hipEventSynchronize(g_events[r.ev1]);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, g_events[r.ev0], g_events[r.ev1]);
+    if (e != hipSuccess) return set_error(DIT_E_HIP, "dit_profile_end: %s", hipGetErrorString(e));
+    if (r.family < n_max) {
+      counts[r.family] += 1;
+      total_ms[r.family] += ms;
+    }
+  }
+  g_prof.clear();
+  g_events_used = 0;
+  return DIT_OK;
+}

@@ -1,0 +1,463 @@
+// Bandwidth-bound kernels of the DiT block: AdaLN modulate+norm, RoPE-from-cache
+// with the QKV split, SiLU gate, gated residual, the AdaLN table, patch in/out
+// and the Euler update.  Every kernel reads and writes each byte once with
+// 16-byte (or 8-byte for bf16 quads) coalesced accesses; row reductions stay in
+// one wavefront (64 lanes) with butterfly shuffles, no LDS and no barrier.
+#include "common.h"
+#include "kernels.h"
+
+namespace dit {
+
+// ============================================================================ modulate + norm
+// One wavefront per row, four rows per 256-thread block.  Lane l holds float4
+// chunks l, l+64, ... of the row in registers, so x is read once.
+// Page "port the MiniMax-H3 omni-modal video+audio DiT", section "The
+// device-resident forward (W2b)": RmsNorm reduces in f32, then an indexed AdaLN
+// modulate; page "the 2.4B fp32 DiT onto the device", section "What moved":
+// LayerNorm for the music model.
+
+template <typename TO> struct store4;
+template <> struct store4<float> {
+  static __device__ __forceinline__ void st(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+};
+template <> struct store4<bf16_t> {
+  static __device__ __forceinline__ void st(bf16_t* p, float4 v) {
+    uint2 t;
+    t.x = pack_bf16x2(v.x, v.y);
+    t.y = pack_bf16x2(v.z, v.w);
+    *reinterpret_cast<uint2*>(p) = t;
+  }
+};
+
+// fp32 output (an fp32 stream or the final norm): the row sums run in fp64,
+// so the normalised row is the fp32 rounding of its exact value in practice.
+// bf16 output: fp32 sums (the bf16 rounding dominates).
+template <typename TO> struct norm_acc { typedef float T; };
+template <> struct norm_acc<float> { typedef double T; };
+
+template <typename TO, int NCH>
+__global__ __launch_bounds__(256) void modnorm_kernel(int N, int D, int norm, float eps,
+                                                     const float* __restrict__ x,
+                                                     const float* __restrict__ mod, int shift_k,
+                                                     int scale_k, const int32_t* __restrict__ cond_idx,
+                                                     TO* __restrict__ h) {
+  typedef typename norm_acc<TO>::T A;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= N) return;
+  const int D4 = D >> 2;
+  const float4* xr = reinterpret_cast<const float4*>(x + static_cast<size_t>(row) * D);
+  float4 v[NCH];
+  A s = 0;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = lane + 64 * i;
+    if (c < D4) {
+      v[i] = xr[c];
+      s += (A(v[i].x) + A(v[i].y)) + (A(v[i].z) + A(v[i].w));
+    } else {
+      v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  const A inv_d = A(1) / A(D);
+  A mean = 0;
+  if (norm == 1) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+    mean = s * inv_d;
+  }
+  A ss = 0;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = lane + 64 * i;
+    if (c < D4) {
+      const A a = A(v[i].x) - mean, b = A(v[i].y) - mean, cc = A(v[i].z) - mean, d = A(v[i].w) - mean;
+      ss += (a * a + b * b) + (cc * cc + d * d);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  const A rstd = A(1) / sqrt(ss * inv_d + A(eps));
+  const float4* sh = nullptr;
+  const float4* sc = nullptr;
+  if (mod != nullptr) {
+    const int cr = cond_idx[row];
+    sh = reinterpret_cast<const float4*>(mod + (static_cast<size_t>(cr) * 6 + shift_k) * D);
+    sc = reinterpret_cast<const float4*>(mod + (static_cast<size_t>(cr) * 6 + scale_k) * D);
+  }
+  TO* hr = h + static_cast<size_t>(row) * D;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = lane + 64 * i;
+    if (c < D4) {
+      A y0 = (A(v[i].x) - mean) * rstd, y1 = (A(v[i].y) - mean) * rstd;
+      A y2 = (A(v[i].z) - mean) * rstd, y3 = (A(v[i].w) - mean) * rstd;
+      if (mod != nullptr) {
+        const float4 a = sc[c], b = sh[c];
+        y0 = y0 * (A(1) + A(a.x)) + A(b.x);
+        y1 = y1 * (A(1) + A(a.y)) + A(b.y);
+        y2 = y2 * (A(1) + A(a.z)) + A(b.z);
+        y3 = y3 * (A(1) + A(a.w)) + A(b.w);
+      }
+      store4<TO>::st(hr + 4 * c, make_float4(float(y0), float(y1), float(y2), float(y3)));
+    }
+  }
+}
+
+bool modnorm_supported(int D) { return D > 0 && D % 4 == 0 && D <= 8192; }
+
+template <typename TO>
+static hipError_t modnorm_t(int norm, float eps, int N, int D, const float* x, const float* mod,
+                            int which, const int32_t* ci, TO* h, hipStream_t s) {
+  const int nch = (D / 4 + 63) / 64;
+  const int shift_k = which == 0 ? 0 : 3, scale_k = which == 0 ? 1 : 4;
+  dim3 grid((N + 3) / 4), block(256);
+#define DIT_MN(K)                                                                          \
+  if (nch <= K) {                                                                          \
+    hipLaunchKernelGGL((modnorm_kernel<TO, K>), grid, block, 0, s, N, D, norm, eps, x, mod, \
+                       shift_k, scale_k, ci, h);                                          \
+    return hipGetLastError();                                                              \
+  }
+  DIT_MN(1) DIT_MN(2) DIT_MN(4) DIT_MN(8) DIT_MN(12) DIT_MN(16) DIT_MN(24) DIT_MN(32)
+#undef DIT_MN
+  return hipErrorInvalidValue;
+}
+
+hipError_t modnorm(bool bf16_out, int norm, float eps, int N, int D, const float* x,
+                   const float* mod, int which, const int32_t* cond_idx, void* h, hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  LaunchScope scope_(kCntModnorm, s);
+  if (bf16_out)
+    return modnorm_t<bf16_t>(norm, eps, N, D, x, mod, which, cond_idx, static_cast<bf16_t*>(h), s);
+  return modnorm_t<float>(norm, eps, N, D, x, mod, which, cond_idx, static_cast<float*>(h), s);
+}
+
+// ============================================================================ RoPE + QKV split
+// qkv [N, 3D] token-major with columns [q_all | k_all | v_all] -> q, k, v
+// head-major [H, N, hd].  NeoX rotate_half on the first `rot` dims of each head,
+// cos/sin looked up by token row (page "port the MiniMax-H3 omni-modal
+// video+audio DiT", section "The device-resident forward (W2b)": plain NeoX
+// rotate_half fed by a per-row cos/sin cache; page "the 2.4B fp32 DiT onto the
+// device", section "What moved": partial rotary).  Thread (n, h, j) handles the
+// 16-byte vectors j and rot/2/V + j of the rotated half (or two pass-through
+// vectors), and two vectors of v.  Consecutive threads walk j then h, so a
+// wavefront reads and writes contiguous runs.
+template <typename T>
+__global__ __launch_bounds__(256) void rope_split_kernel(int N, int H, int hd, int rot,
+                                                        const T* __restrict__ qkv,
+                                                        const float* __restrict__ cosb,
+                                                        const float* __restrict__ sinb,
+                                                        T* __restrict__ q, T* __restrict__ k,
+                                                        T* __restrict__ v) {
+  constexpr int V = vec16<T>::N;
+  const int tph = hd / (2 * V);
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t >= static_cast<int64_t>(N) * H * tph) return;
+  const int j = static_cast<int>(t % tph);
+  const int h = static_cast<int>((t / tph) % H);
+  const int n = static_cast<int>(t / (static_cast<int64_t>(tph) * H));
+  const int D = H * hd;
+  const int half = rot / 2;
+  const T* src = qkv + static_cast<size_t>(n) * 3 * D + static_cast<size_t>(h) * hd;
+  const size_t dst_off = (static_cast<size_t>(h) * N + n) * hd;
+  if (j < half / V) {
+    const int i0 = j * V, i1 = half + j * V;
+    float c[V], sn[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      c[e] = cosb[static_cast<size_t>(n) * half + i0 + e];
+      sn[e] = sinb[static_cast<size_t>(n) * half + i0 + e];
+    }
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      const T* s = src + which * D;
+      T* d = (which == 0 ? q : k) + dst_off;
+      float x1[V], x2[V], o1[V], o2[V];
+      vec16<T>::load(s + i0, x1);
+      vec16<T>::load(s + i1, x2);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        o1[e] = x1[e] * c[e] - x2[e] * sn[e];
+        o2[e] = x2[e] * c[e] + x1[e] * sn[e];
+      }
+      vec16<T>::store(d + i0, o1);
+      vec16<T>::store(d + i1, o2);
+    }
+  } else {
+    const int jj = j - half / V;
+    const int i0 = rot + 2 * jj * V, i1 = i0 + V;
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      const T* s = src + which * D;
+      T* d = (which == 0 ? q : k) + dst_off;
+      *reinterpret_cast<uint4*>(d + i0) = *reinterpret_cast<const uint4*>(s + i0);
+      *reinterpret_cast<uint4*>(d + i1) = *reinterpret_cast<const uint4*>(s + i1);
+    }
+  }
+  const T* sv = src + 2 * D;
+  T* dv = v + dst_off;
+  *reinterpret_cast<uint4*>(dv + 2 * j * V) = *reinterpret_cast<const uint4*>(sv + 2 * j * V);
+  *reinterpret_cast<uint4*>(dv + (2 * j + 1) * V) =
+      *reinterpret_cast<const uint4*>(sv + (2 * j + 1) * V);
+}
+
+bool rope_split_supported(bool bf16, int hd, int rot) {
+  const int V = bf16 ? 8 : 4;
+  return hd > 0 && rot > 0 && rot <= hd && rot % 2 == 0 && (rot / 2) % V == 0 && hd % (2 * V) == 0 &&
+         (hd - rot) % (2 * V) == 0;
+}
+
+hipError_t rope_split(bool bf16, int N, int H, int hd, int rot, const void* qkv, const float* cos,
+                      const float* sin, void* q, void* k, void* v, hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  LaunchScope scope_(kCntRopeSplit, s);
+  const int V = bf16 ? 8 : 4;
+  const int64_t total = static_cast<int64_t>(N) * H * (hd / (2 * V));
+  dim3 grid(static_cast<unsigned>((total + 255) / 256)), block(256);
+  if (bf16)
+    hipLaunchKernelGGL(rope_split_kernel<bf16_t>, grid, block, 0, s, N, H, hd, rot,
+                       static_cast<const bf16_t*>(qkv), cos, sin, static_cast<bf16_t*>(q),
+                       static_cast<bf16_t*>(k), static_cast<bf16_t*>(v));
+  else
+    hipLaunchKernelGGL(rope_split_kernel<float>, grid, block, 0, s, N, H, hd, rot,
+                       static_cast<const float*>(qkv), cos, sin, static_cast<float*>(q),
+                       static_cast<float*>(k), static_cast<float*>(v));
+  return hipGetLastError();
+}
+
+// ============================================================================ SiLU gate
+// m[n, j] = silu(u[n, j]) * u[n, F + j]; silu(z) = z / (1 + e^-z).  The music
+// model's [value | gate] projection is half-swapped at stage time, so one
+// kernel serves both (page "the 2.4B fp32 DiT onto the device", section "What
+// moved": SiluAndMul over a stage-time half swap).
+template <typename T>
+__global__ __launch_bounds__(256) void silu_gate_kernel(int N, int F, const T* __restrict__ u,
+                                                       T* __restrict__ m) {
+  constexpr int V = vec16<T>::N;
+  const int fv = F / V;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t >= static_cast<int64_t>(N) * fv) return;
+  const int n = static_cast<int>(t / fv);
+  const int j = static_cast<int>(t % fv) * V;
+  const T* ur = u + static_cast<size_t>(n) * 2 * F;
+  float g[V], up[V], o[V];
+  vec16<T>::load(ur + j, g);
+  vec16<T>::load(ur + F + j, up);
+#pragma unroll
+  for (int e = 0; e < V; ++e) o[e] = g[e] / (1.0f + expf(-g[e])) * up[e];
+  vec16<T>::store(m + static_cast<size_t>(n) * F + j, o);
+}
+
+hipError_t silu_gate(bool bf16, int N, int F, const void* u, void* m, hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  LaunchScope scope_(kCntSiluGate, s);
+  const int V = bf16 ? 8 : 4;
+  if (F % V) return hipErrorInvalidValue;
+  const int64_t total = static_cast<int64_t>(N) * (F / V);
+  dim3 grid(static_cast<unsigned>((total + 255) / 256)), block(256);
+  if (bf16)
+    hipLaunchKernelGGL(silu_gate_kernel<bf16_t>, grid, block, 0, s, N, F,
+                       static_cast<const bf16_t*>(u), static_cast<bf16_t*>(m));
+  else
+    hipLaunchKernelGGL(silu_gate_kernel<float>, grid, block, 0, s, N, F,
+                       static_cast<const float*>(u), static_cast<float*>(m));
+  return hipGetLastError();
+}
+
+// ============================================================================ gated residual
+// x[n, j] += gate[cond_idx[n]][j] * a[n, j] (page "port the MiniMax-H3
+// omni-modal video+audio DiT", section "The device-resident forward (W2b)":
+// Add with an indexed AdaLN gate).
+__global__ __launch_bounds__(256) void gated_residual_kernel(int N, int D, float* __restrict__ x,
+                                                            const float* __restrict__ a,
+                                                            const float* __restrict__ mod, int gate_k,
+                                                            const int32_t* __restrict__ cond_idx) {
+  const int d4 = D / 4;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t >= static_cast<int64_t>(N) * d4) return;
+  const int n = static_cast<int>(t / d4);
+  const int c = static_cast<int>(t % d4);
+  const float4 g = reinterpret_cast<const float4*>(
+      mod + (static_cast<size_t>(cond_idx[n]) * 6 + gate_k) * D)[c];
+  const float4 av = reinterpret_cast<const float4*>(a)[t];
+  float4 xv = reinterpret_cast<float4*>(x)[t];
+  xv.x += g.x * av.x;
+  xv.y += g.y * av.y;
+  xv.z += g.z * av.z;
+  xv.w += g.w * av.w;
+  reinterpret_cast<float4*>(x)[t] = xv;
+}
+
+hipError_t gated_residual(int N, int D, float* x, const float* a, const float* mod, int which,
+                          const int32_t* cond_idx, hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  LaunchScope scope_(kCntGatedResidual, s);
+  const int64_t total = static_cast<int64_t>(N) * (D / 4);
+  dim3 grid(static_cast<unsigned>((total + 255) / 256)), block(256);
+  hipLaunchKernelGGL(gated_residual_kernel, grid, block, 0, s, N, D, x, a, mod, which == 0 ? 2 : 5,
+                     cond_idx);
+  return hipGetLastError();
+}
+
+// ============================================================================ AdaLN table
+// mod[c][j] = W[m(c)][j, :] . e[c, :] + bias[m(c)][j], one wavefront per output
+// column j; sums in fp64 so the table is the correctly rounded fp32 of the dot
+// product in practice.  One launch per block writes that block's rows.
+struct CondMap {
+  int n_cond;
+  int modality[64];
+};
+
+template <typename TW>
+__global__ __launch_bounds__(256) void adaln_kernel(int six_d, int cond_dim, AdalnBlockPtrs p,
+                                                   CondMap cm, const float* __restrict__ e,
+                                                   float* __restrict__ mod) {
+  const int lane = threadIdx.x & 63;
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int m = blockIdx.y;
+  if (j >= six_d || p.w[m] == nullptr) return;
+  const TW* w = static_cast<const TW*>(p.w[m]) + static_cast<size_t>(j) * cond_dim;
+  for (int c = 0; c < cm.n_cond; ++c) {
+    if (cm.modality[c] != m) continue;
+    const float* ec = e + static_cast<size_t>(c) * cond_dim;
+    double acc = 0.0;
+    for (int kk = lane; kk < cond_dim; kk += 64)
+      acc += static_cast<double>(elem<TW>::load(w + kk)) * static_cast<double>(ec[kk]);
+    acc = wave_sum_f64(acc);
+    if (lane == 0) mod[static_cast<size_t>(c) * six_d + j] = static_cast<float>(acc + static_cast<double>(p.bias[m][j]));
+  }
+}
+
+hipError_t adaln(bool w_bf16, int n_blocks, const AdalnBlockPtrs* blocks_host, int n_cond,
+                 const int* cond_modality_host, int six_d, int cond_dim, const float* e,
+                 float* mod, hipStream_t s) {
+  if (n_cond > 64) return hipErrorInvalidValue;
+  CondMap cm;
+  cm.n_cond = n_cond;
+  int n_mod = 0;
+  for (int c = 0; c < n_cond; ++c) {
+    cm.modality[c] = cond_modality_host[c];
+    if (cond_modality_host[c] + 1 > n_mod) n_mod = cond_modality_host[c] + 1;
+  }
+  dim3 grid((six_d + 3) / 4, n_mod), block(256);
+  for (int b = 0; b < n_blocks; ++b) {
+    LaunchScope scope_(kCntAdaln, s);
+    float* out = mod + static_cast<size_t>(b) * n_cond * six_d;
+    if (w_bf16)
+      hipLaunchKernelGGL(adaln_kernel<bf16_t>, grid, block, 0, s, six_d, cond_dim, blocks_host[b], cm,
+                         e, out);
+    else
+      hipLaunchKernelGGL(adaln_kernel<float>, grid, block, 0, s, six_d, cond_dim, blocks_host[b], cm,
+                         e, out);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+// ============================================================================ patch in / out
+// io 1 (patch3d): latent [C, T*pt, H*ph, W*pw] <-> tokens [T*H*W, pt*ph*pw*C],
+// tokens in raster (t, h, w) order, vector order (pt, ph, pw, c) with c
+// fastest (a convolution with kernel == stride is a linear map of the flattened
+// patch; page "port the MiniMax-H3 omni-modal video+audio DiT", update "Encoder
+// complete").  io 2 (channel-major): latent [C, L] <-> tokens [L, C], the
+// frame-major view under which a 1x1 convolution is a GEMM (page "the 2.4B fp32
+// DiT onto the device", section "What moved").  Pure index work: bit-exact.
+struct PatchGeom {
+  int io, C, pt, ph, pw, T, H, W;
+};
+
+__device__ __forceinline__ int64_t patch_latent_index(const PatchGeom& g, int64_t t) {
+  const int cv = g.pt * g.ph * g.pw * g.C;
+  const int64_t tok = t / cv;
+  int e = static_cast<int>(t % cv);
+  if (g.io == 2) return static_cast<int64_t>(e) * g.T + tok;  // T holds L
+  const int c = e % g.C;
+  e /= g.C;
+  const int ipw = e % g.pw;
+  e /= g.pw;
+  const int iph = e % g.ph;
+  const int ipt = e / g.ph;
+  const int w = static_cast<int>(tok % g.W);
+  const int h = static_cast<int>((tok / g.W) % g.H);
+  const int tt = static_cast<int>(tok / (static_cast<int64_t>(g.W) * g.H));
+  const int64_t Tp = static_cast<int64_t>(g.T) * g.pt, Hp = static_cast<int64_t>(g.H) * g.ph,
+                Wp = static_cast<int64_t>(g.W) * g.pw;
+  return ((static_cast<int64_t>(c) * Tp + (tt * g.pt + ipt)) * Hp + (h * g.ph + iph)) * Wp +
+         (w * g.pw + ipw);
+}
+
+__global__ __launch_bounds__(256) void patch_in_kernel(PatchGeom g, int64_t total,
+                                                      const float* __restrict__ latent,
+                                                      float* __restrict__ tokens) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t < total) tokens[t] = latent[patch_latent_index(g, t)];
+}
+__global__ __launch_bounds__(256) void patch_out_kernel(PatchGeom g, int64_t total,
+                                                       const float* __restrict__ tokens,
+                                                       float* __restrict__ latent) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t < total) latent[patch_latent_index(g, t)] = tokens[t];
+}
+
+static PatchGeom make_geom(int io, int C, const int* patch, const int* grid, int64_t* total) {
+  PatchGeom g;
+  g.io = io;
+  g.C = C;
+  if (io == 1) {
+    g.pt = patch[0]; g.ph = patch[1]; g.pw = patch[2];
+    g.T = grid[0]; g.H = grid[1]; g.W = grid[2];
+    *total = static_cast<int64_t>(g.T) * g.H * g.W * g.pt * g.ph * g.pw * C;
+  } else {
+    g.pt = g.ph = g.pw = 1;
+    g.T = grid[0]; g.H = g.W = 1;
+    *total = static_cast<int64_t>(g.T) * C;
+  }
+  return g;
+}
+
+hipError_t patch_in(int io, int C, const int* patch, const int* grid, const float* latent,
+                    float* tokens, hipStream_t s) {
+  int64_t total;
+  PatchGeom g = make_geom(io, C, patch, grid, &total);
+  if (total == 0) return hipSuccess;
+  LaunchScope scope_(kCntPatchIn, s);
+  hipLaunchKernelGGL(patch_in_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0,
+                     s, g, total, latent, tokens);
+  return hipGetLastError();
+}
+
+hipError_t patch_out(int io, int C, const int* patch, const int* grid, const float* tokens,
+                     float* latent, hipStream_t s) {
+  int64_t total;
+  PatchGeom g = make_geom(io, C, patch, grid, &total);
+  if (total == 0) return hipSuccess;
+  LaunchScope scope_(kCntPatchOut, s);
+  hipLaunchKernelGGL(patch_out_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256),
+                     0, s, g, total, tokens, latent);
+  return hipGetLastError();
+}
+
+// ============================================================================ Euler step
+// x += dt * v in fp32 with the product rounded before the sum (no contraction),
+// the euler eta=0 update with rf_v_to_x0 folded in.
+__global__ __launch_bounds__(256) void euler_kernel(int64_t n, float* __restrict__ x,
+                                                   const float* __restrict__ v,
+                                                   const float* __restrict__ dt) {
+#pragma clang fp contract(off)
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) {
+    const float p = dt[0] * v[i];
+    x[i] = x[i] + p;
+  }
+}
+
+hipError_t euler(int64_t n, float* x, const float* v, const float* dt, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  LaunchScope scope_(kCntEuler, s);
+  hipLaunchKernelGGL(euler_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, n,
+                     x, v, dt);
+  return hipGetLastError();
+}
+
+}  // namespace dit

@@ -1,0 +1,145 @@
+// Host-side tables built in fp64 before any kernel runs: packed layout, per-row
+// RoPE cos/sin cache, sinusoidal timestep embedding and the sigma schedule.
+// Compiled with -ffp-contract=off so every product and sum rounds on its own,
+// which makes the tables reproducible bit for bit from their definitions.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "dit.h"
+#include "internal.h"
+
+using dit::set_error;
+
+static int segment_tokens(const dit_config* cfg, const dit_segment& s, int64_t* n) {
+  if (s.modality < 0 || s.modality >= cfg->n_mod) return -1;
+  const int axes = cfg->mod[s.modality].n_axes;
+  int64_t t = 1;
+  for (int a = 0; a < axes; ++a) {
+    if (s.grid[a] <= 0) return -1;
+    t *= s.grid[a];
+  }
+  *n = t;
+  return 0;
+}
+
+// Page "port the MiniMax-H3 omni-modal video+audio DiT", section "Correctness
+// gates": packed layout (ids, tags, cu_seqlens, doc ids) gated exact.
+extern "C" int dit_pack_layout(const dit_config* cfg, const dit_segment* segs, int n_segs,
+                               int32_t* cu_seqlens, int32_t* cond_idx, int32_t* doc_id,
+                               int* n_tokens) {
+  if (cfg == nullptr || segs == nullptr || cu_seqlens == nullptr || n_tokens == nullptr)
+    return set_error(DIT_E_INVALID, "dit_pack_layout: null argument");
+  if (n_segs < 1 || n_segs > DIT_MAX_SEGMENTS)
+    return set_error(DIT_E_INVALID, "dit_pack_layout: n_segs=%d outside [1, %d]", n_segs,
+                     DIT_MAX_SEGMENTS);
+  int64_t total = 0;
+  cu_seqlens[0] = 0;
+  for (int i = 0; i < n_segs; ++i) {
+    int64_t n;
+    if (segment_tokens(cfg, segs[i], &n) != 0)
+      return set_error(DIT_E_INVALID, "dit_pack_layout: segment %d has a bad modality or extent", i);
+    if (segs[i].cond_row < 0 || segs[i].cond_row >= DIT_MAX_COND)
+      return set_error(DIT_E_INVALID, "dit_pack_layout: segment %d cond_row=%d", i, segs[i].cond_row);
+    total += n;
+    if (total >= (int64_t(1) << 31))
+      return set_error(DIT_E_INVALID, "dit_pack_layout: more than 2^31-1 tokens");
+    cu_seqlens[i + 1] = static_cast<int32_t>(total);
+  }
+  for (int i = 0; i < n_segs; ++i) {
+    for (int32_t r = cu_seqlens[i]; r < cu_seqlens[i + 1]; ++r) {
+      if (cond_idx) cond_idx[r] = segs[i].cond_row;
+      if (doc_id) doc_id[r] = i;
+    }
+  }
+  *n_tokens = static_cast<int>(total);
+  return DIT_OK;
+}
+
+// Page "stream the ORIGINAL bf16 DiT to the device", section "What this
+// enables": the cos/sin tables are built on the host before any kernel.  Page
+// "port the MiniMax-H3 omni-modal video+audio DiT", update "video-VAE ViT3D
+// decoder complete": per-axis frequency blocks are concatenated, and the
+// rotate_half pairing (i, i + rot/2) tiles the concatenation twice.
+extern "C" int dit_rope_cache_build(const dit_config* cfg, const dit_segment* segs, int n_segs,
+                                    float* cos_host, float* sin_host) {
+  if (cfg == nullptr || segs == nullptr || cos_host == nullptr || sin_host == nullptr)
+    return set_error(DIT_E_INVALID, "dit_rope_cache_build: null argument");
+  const int half = cfg->rot_dim / 2;
+  // Frequency table per modality: the concatenation over axes of inv_freq_a.
+  std::vector<std::vector<double>> freq(cfg->n_mod);
+  std::vector<std::vector<int>> axis_of(cfg->n_mod);
+  for (int m = 0; m < cfg->n_mod; ++m) {
+    const dit_modality& md = cfg->mod[m];
+    for (int a = 0; a < md.n_axes; ++a) {
+      const int da = md.axis_dim[a];
+      for (int j = 0; j < da / 2; ++j) {
+        const double e = static_cast<double>(2 * j) / static_cast<double>(da);
+        freq[m].push_back(1.0 / std::pow(cfg->theta, e));
+        axis_of[m].push_back(a);
+      }
+    }
+    if (static_cast<int>(freq[m].size()) != half)
+      return set_error(DIT_E_INVALID, "dit_rope_cache_build: modality %d axis dims do not sum to rot_dim", m);
+  }
+  int64_t row = 0;
+  for (int i = 0; i < n_segs; ++i) {
+    const dit_segment& s = segs[i];
+    int64_t n;
+    if (segment_tokens(cfg, s, &n) != 0)
+      return set_error(DIT_E_INVALID, "dit_rope_cache_build: segment %d is malformed", i);
+    const int axes = cfg->mod[s.modality].n_axes;
+    const std::vector<double>& f = freq[s.modality];
+    const std::vector<int>& ax = axis_of[s.modality];
+    for (int64_t t = 0; t < n; ++t, ++row) {
+      int64_t pos[3] = {t, 0, 0};
+      if (axes == 3) {
+        pos[2] = t % s.grid[2];
+        pos[1] = (t / s.grid[2]) % s.grid[1];
+        pos[0] = t / (static_cast<int64_t>(s.grid[2]) * s.grid[1]);
+      }
+      float* cr = cos_host + row * half;
+      float* sr = sin_host + row * half;
+      for (int j = 0; j < half; ++j) {
+        const double ang = static_cast<double>(pos[ax[j]]) * f[j];
+        cr[j] = static_cast<float>(std::cos(ang));
+        sr[j] = static_cast<float>(std::sin(ang));
+      }
+    }
+  }
+  return DIT_OK;
+}
+
+extern "C" int dit_timestep_embedding(const float* t_host, int n, int dim, float* out_host) {
+  if (t_host == nullptr || out_host == nullptr || n < 0 || dim <= 0 || dim % 2)
+    return set_error(DIT_E_INVALID, "dit_timestep_embedding: bad argument (dim must be even)");
+  const int h = dim / 2;
+  for (int i = 0; i < n; ++i) {
+    const double t = static_cast<double>(t_host[i]);
+    for (int j = 0; j < h; ++j) {
+      const double f = std::pow(10000.0, -static_cast<double>(j) / static_cast<double>(h));
+      const double a = t * f;
+      out_host[static_cast<int64_t>(i) * dim + j] = static_cast<float>(std::cos(a));
+      out_host[static_cast<int64_t>(i) * dim + h + j] = static_cast<float>(std::sin(a));
+    }
+  }
+  return DIT_OK;
+}
+
+// Page "port the MiniMax-H3 omni-modal video+audio DiT", update "quantized
+// arms land" item 2: the rectified-flow time-shift sigma schedule (video shift
+// 12, audio shift 3).
+extern "C" int dit_sigma_schedule(double shift, int n_steps, double* sigma_host, float* dt_host) {
+  if (n_steps < 1 || !(shift > 0.0))
+    return set_error(DIT_E_INVALID, "dit_sigma_schedule: n_steps must be >= 1 and shift > 0");
+  std::vector<double> sig(n_steps + 1);
+  for (int i = 0; i <= n_steps; ++i) {
+    const double s = 1.0 - static_cast<double>(i) / static_cast<double>(n_steps);
+    sig[i] = shift * s / (1.0 + (shift - 1.0) * s);
+  }
+  if (sigma_host) std::memcpy(sigma_host, sig.data(), sizeof(double) * (n_steps + 1));
+  if (dt_host)
+    for (int i = 0; i < n_steps; ++i) dt_host[i] = static_cast<float>(sig[i + 1] - sig[i]);
+  return DIT_OK;
+}

@@ -1,0 +1,74 @@
+// Host-side launch helpers of the gfx950 DiT kernels.  Each returns the
+// hipError_t of its launch; shapes are validated by the caller (dit_api.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dit {
+
+enum Counter {
+  kCntGemmBf16 = 0, kCntGemmF32, kCntAttnBf16, kCntAttnF32, kCntModnorm, kCntRopeSplit,
+  kCntSiluGate, kCntGatedResidual, kCntAdaln, kCntPatchIn, kCntPatchOut, kCntEuler,
+  kCntGemmF32Reduce, kCntNum
+};
+void count_launch(Counter c);
+
+// Counts one launch of family `c` and, while profiling is on, records a HIP
+// event pair around it on the launch stream.  Construct it immediately before
+// the kernel launch; it records the end event when it goes out of scope.
+class LaunchScope {
+ public:
+  LaunchScope(Counter c, hipStream_t s);
+  ~LaunchScope();
+ private:
+  int slot_;
+  hipStream_t s_;
+};
+
+// ---- GEMM: C[M,N] = A[M,K] . B[N,K]^T (+ bias)
+size_t gemm_bf16_ws_bytes(int M, int N, int K);
+hipError_t gemm_bf16(int M, int N, int K, const uint16_t* A, const uint16_t* B, const float* bias,
+                     void* C, bool c_f32, void* ws, hipStream_t s);
+size_t gemm_f32_ws_bytes(int M, int N, int K);
+hipError_t gemm_f32(int M, int N, int K, const float* A, const float* B, const float* bias,
+                    float* C, void* ws, hipStream_t s);
+// Which K, N the GEMMs accept (checked by the ABI layer before launching).
+bool gemm_bf16_supported(int M, int N, int K);
+bool gemm_f32_supported(int M, int N, int K);
+
+// ---- attention (q, k, v head-major [H, N, hd]; o [N, H*hd])
+hipError_t attention_bf16(int N, int H, int hd, int n_docs, const int32_t* cu, int max_seqlen,
+                          const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                          hipStream_t s);
+hipError_t attention_f32(int N, int H, int hd, int n_docs, const int32_t* cu, int max_seqlen,
+                         const float* q, const float* k, const float* v, float* o, hipStream_t s);
+bool attention_supported(bool bf16, int hd);
+
+// ---- bandwidth-bound kernels
+hipError_t modnorm(bool bf16_out, int norm, float eps, int N, int D, const float* x,
+                   const float* mod, int which, const int32_t* cond_idx, void* h, hipStream_t s);
+bool modnorm_supported(int D);
+hipError_t rope_split(bool bf16, int N, int H, int hd, int rot, const void* qkv, const float* cos,
+                      const float* sin, void* q, void* k, void* v, hipStream_t s);
+bool rope_split_supported(bool bf16, int hd, int rot);
+hipError_t silu_gate(bool bf16, int N, int F, const void* u, void* m, hipStream_t s);
+hipError_t gated_residual(int N, int D, float* x, const float* a, const float* mod, int which,
+                          const int32_t* cond_idx, hipStream_t s);
+// mod[b][c][j] = W[b][modality(c)][j] . e[c] + bias[b][modality(c)][j]
+struct AdalnBlockPtrs {
+  const void* w[4];      // per modality [6D, d], stream dtype
+  const float* bias[4];  // per modality [6D]
+};
+hipError_t adaln(bool w_bf16, int n_blocks, const AdalnBlockPtrs* blocks_host, int n_cond,
+                 const int* cond_modality_host, int six_d, int cond_dim, const float* e,
+                 float* mod, hipStream_t s);
+// latent segment -> tokens [n, C*pt*ph*pw] (io: 1 patch3d, 2 channel-major)
+hipError_t patch_in(int io, int C, const int* patch, const int* grid, const float* latent,
+                    float* tokens, hipStream_t s);
+hipError_t patch_out(int io, int C, const int* patch, const int* grid, const float* tokens,
+                     float* latent, hipStream_t s);
+hipError_t euler(int64_t n, float* x, const float* v, const float* dt, hipStream_t s);
+
+}  // namespace dit
