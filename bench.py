@@ -41,19 +41,46 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def gemm_shapes(cfg):
-    """(M, N, K) of every GEMM launch of one forward, in launch order."""
+def gemm_shapes(cfg, blocks=True, islands=True):
+    """(M, N, K) of the GEMM launches of one forward, in launch order."""
     N = cfg.n_tokens
     D, F = cfg.hidden, cfg.ffn
     out = []
-    if cfg.io:
+    if cfg.io and islands:
         for s in cfg.segments:
             out.append((s.n_tokens, D, cfg.modalities[s.modality].token_width))
-    for _ in range(cfg.n_blocks):
-        out += [(N, 3 * D, D), (N, D, D), (N, 2 * F, D), (N, D, F)]
-    if cfg.io:
+    if blocks:
+        for _ in range(cfg.n_blocks):
+            out += [(N, 3 * D, D), (N, D, D), (N, 2 * F, D), (N, D, F)]
+    if cfg.io and islands:
         for s in cfg.segments:
             out.append((s.n_tokens, cfg.modalities[s.modality].token_width, D))
+    return out
+
+
+def family_work(cfg):
+    """Algorithmic work of one forward per kernel family: (amount, unit).
+
+    GEMM and attention count flops (2MNK; 4*hd*H*sum L_d^2); the bandwidth-bound
+    kernels count the bytes they must move once (inputs read + outputs written)."""
+    N, D, F, H, hd = cfg.n_tokens, cfg.hidden, cfg.ffn, cfg.n_heads, cfg.head_dim
+    es = 2 if cfg.stream == "bf16" else 4
+    L = cfg.n_blocks
+    w_es = es
+    blocks = sum(2.0 * m * n * k for m, n, k in gemm_shapes(cfg, islands=False))
+    islands = sum(2.0 * m * n * k for m, n, k in gemm_shapes(cfg, blocks=False))
+    out = {
+        # block GEMMs run in the stream dtype; the projections in and out are fp32
+        "gemm_bf16": (blocks if cfg.stream == "bf16" else 0.0, "flop"),
+        "gemm_f32": ((islands if cfg.stream == "bf16" else blocks + islands), "flop"),
+        "attention": (attention_flops(cfg), "flop"),
+        # x read (f32) + h written, twice per block; plus the final fp32 norm with io
+        "modnorm": (L * 2 * N * D * (4 + es) + (N * D * 8 if cfg.io else 0), "byte"),
+        "rope_split": (L * N * (6 * D * es + cfg.rot_dim * 4), "byte"),
+        "silu_gate": (L * N * 3 * F * es, "byte"),
+        "gated_residual": (L * 2 * N * D * 12, "byte"),
+        "adaln": (L * cfg.n_mod * 6 * D * cfg.cond_dim * w_es, "byte"),
+    }
     return out
 
 
@@ -150,10 +177,29 @@ def main(argv=None):
         if n:
             log(f"  {k:16s} launches {n:6d}  total {t:9.3f} ms  avg {t / n * 1e3:9.2f} us  "
                 f"share {t / total_dev * 100:5.1f}%")
+    work = family_work(cfg)
+    kernels = {}
+    for k, (n, t) in prof.items():
+        if not n:
+            continue
+        key = k if k.startswith("gemm") else k.split("_bf16")[0].split("_f32")[0]
+        if key not in work or t <= 0:
+            continue
+        amt, unit = work[key]
+        rate = amt * a.steps / (t * 1e-3)
+        if unit == "byte":
+            kernels[k] = {"GB/s": round(rate / 1e9, 1), "frac_hbm": round(rate / 1e9 / PEAK["hbm_gbs"], 4),
+                          "avg_us": round(t / n * 1e3, 2)}
+        else:
+            peak = PEAK["mfma_f64"] if k == "gemm_f32" else (PEAK["mfma_bf16"] if k.endswith("bf16") else None)
+            kernels[k] = {"TFLOP/s": round(rate / 1e12, 2), "avg_us": round(t / n * 1e3, 2)}
+            if peak:
+                kernels[k]["frac_mfma"] = round(rate / 1e12 / peak, 4)
+        log(f"  {k:16s} {kernels[k]}")
     fam = max(prof.items(), key=lambda kv: kv[1][1])[0]
     n_launch, fam_ms = prof[fam]
     if fam in ("gemm_f32", "gemm_bf16"):
-        flops = sum(2.0 * m * n * k for m, n, k in gemm_shapes(cfg)) * a.steps
+        flops = work[fam][0] * a.steps
         peak_key, peak_note = GEMM_FAMILY_PEAK[fam]
         achieved = flops / (fam_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK[peak_key], "unit": "TFLOP/s",
@@ -195,6 +241,7 @@ def main(argv=None):
                    "device": dev},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "kernels": kernels,
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -1,9 +1,10 @@
 """Seeded synthetic weights and inputs.
 
-Every tensor has its own generator, keyed by (seed, key, FNV-1a-64 of the
-tensor's name), so any one tensor -- one block's weights, one segment's latent --
-can be regenerated alone, in any order, on any machine (numpy's PCG64 and its
-normal sampler are platform independent).  This follows the pages' practice of
+Every tensor has its own generators, keyed by (seed, key, FNV-1a-64 of the
+tensor's name, chunk index) with one PCG64 stream per 4M-value chunk, so any
+one tensor -- one block's weights, one segment's latent -- can be regenerated
+alone, in any order, on any machine, by any number of threads (numpy's PCG64
+and its normal sampler are platform independent).  This follows the pages' practice of
 rebuilding weights on both sides of a check from one keyed generator instead of
 storing them (page "port the MiniMax-H3 omni-modal video+audio DiT", section
 "How this is gated").
@@ -17,6 +18,7 @@ identical numbers; ``bf16_bits`` gives their 16-bit encoding.
 
 from __future__ import annotations
 
+import os
 from concurrent.futures import ThreadPoolExecutor
 from typing import Dict, List, Tuple
 
@@ -67,6 +69,42 @@ def _normal(rng: np.random.Generator, shape, std: float) -> np.ndarray:
     return a
 
 
+CHUNK = 1 << 22  # values per independent stream of a large tensor
+_POOL = None
+
+
+def _pool() -> ThreadPoolExecutor:
+    global _POOL
+    if _POOL is None:
+        _POOL = ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1)))
+    return _POOL
+
+
+def _keyed_normal(seed: int, key: int, name: str, shape, std: float, bf16: bool) -> np.ndarray:
+    """N(0, std^2) float32 values of one tensor.  Value i comes from stream
+    (seed, key, name, i // CHUNK), so the result does not depend on how many
+    threads fill it; chunks are filled in parallel (numpy releases the GIL)."""
+    n = int(np.prod(shape))
+    out = np.empty(n, np.float32)
+
+    def fill(c):
+        lo, hi = c * CHUNK, min(n, (c + 1) * CHUNK)
+        ss = np.random.SeedSequence([int(seed), int(key), fnv1a64(name), c])
+        g = np.random.Generator(np.random.PCG64(ss))
+        g.standard_normal(size=hi - lo, dtype=np.float32, out=out[lo:hi])
+        if std != 1.0:
+            out[lo:hi] *= np.float32(std)
+        if bf16:
+            round_to_bf16(out[lo:hi])
+
+    chunks = (n + CHUNK - 1) // CHUNK
+    if chunks <= 1:
+        fill(0)
+    else:
+        list(_pool().map(fill, range(chunks)))
+    return out.reshape(shape)
+
+
 def block_weight_shapes(cfg: DitConfig) -> List[Tuple[str, Tuple[int, ...]]]:
     """(name suffix, shape) of one block's tensors, nn.Linear layout [out, in]."""
     D, F, dt = cfg.hidden, cfg.ffn, cfg.cond_dim
@@ -97,22 +135,15 @@ def island_weight_shapes(cfg: DitConfig) -> List[Tuple[str, Tuple[int, ...]]]:
 def _make(cfg: DitConfig, name: str, shape, seed: int, stream_bf16: bool) -> np.ndarray:
     if name.endswith(".bias"):
         return np.zeros(shape, np.float32)
-    a = _normal(tensor_rng(seed, 1000 + cfg.model_id, name), shape, WEIGHT_STD)
-    if stream_bf16:
-        round_to_bf16(a)
-    return a
+    return _keyed_normal(seed, 1000 + cfg.model_id, name, shape, WEIGHT_STD, stream_bf16)
 
 
 def block_weights(cfg: DitConfig, b: int, seed: int = 0, threads: int = 1) -> Dict[str, np.ndarray]:
-    """One block's weights, keyed 'blocks.{b}.<suffix>'."""
+    """One block's weights, keyed 'blocks.{b}.<suffix>'.  (``threads`` is
+    accepted for compatibility; large tensors always fill in parallel chunks.)"""
     bf = cfg.stream == "bf16"
     items = [(f"blocks.{b}.{s}", shp) for s, shp in block_weight_shapes(cfg)]
-    if threads > 1:
-        with ThreadPoolExecutor(threads) as ex:
-            arrs = list(ex.map(lambda it: _make(cfg, it[0], it[1], seed, bf), items))
-    else:
-        arrs = [_make(cfg, n, s, seed, bf) for n, s in items]
-    return {n: a for (n, _), a in zip(items, arrs)}
+    return {n: _make(cfg, n, shp, seed, bf) for n, shp in items}
 
 
 def island_weights(cfg: DitConfig, seed: int = 0) -> Dict[str, np.ndarray]:
@@ -151,13 +182,9 @@ def inputs(cfg: DitConfig, seed: int = 0) -> Dict[str, np.ndarray]:
     if cfg.io:
         for i in range(len(cfg.segments)):
             src = 0 if cfg.cfg_replicate_latent else i
-            a = _normal(tensor_rng(seed, k, f"latent.{src}"), segment_latent_shape(cfg, i), 1.0)
-            out[f"latent.{i}"] = a
+            out[f"latent.{i}"] = _keyed_normal(seed, k, f"latent.{src}", segment_latent_shape(cfg, i), 1.0, False)
     else:
-        a = _normal(tensor_rng(seed, k, "x"), (cfg.n_tokens, cfg.hidden), 1.0)
-        if cfg.stream == "bf16":
-            round_to_bf16(a)
-        out["x"] = a
+        out["x"] = _keyed_normal(seed, k, "x", (cfg.n_tokens, cfg.hidden), 1.0, cfg.stream == "bf16")
     if cfg.cond_kind == "timestep":
         if cfg.denoise_steps == 0:
             out["t"] = tensor_rng(seed, k, "t").random(cfg.n_requests, dtype=np.float32)

@@ -797,7 +797,7 @@ extern "C" int dit_gemm(int dtype, int M, int N, int K, const void* A, const voi
   if (M > 0 && (A == nullptr || B == nullptr || C == nullptr)) return set_error(DIT_E_INVALID, "dit_gemm: null operand");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (dtype == DIT_BF16) {
-    if (!gemm_bf16_supported(M, N, K)) return set_error(DIT_E_UNSUPPORTED, "dit_gemm bf16: K=%d must be a multiple of 64", K);
+    if (!gemm_bf16_supported(M, N, K)) return set_error(DIT_E_UNSUPPORTED, "dit_gemm bf16: K=%d must be a multiple of 32", K);
     if (c_dtype != DIT_F32 && c_dtype != DIT_BF16) return set_error(DIT_E_INVALID, "dit_gemm: c_dtype");
     DIT_HIP(gemm_bf16(M, N, K, static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), bias, C,
                       c_dtype == DIT_F32, ws, s));

@@ -4,9 +4,10 @@
 // onto the device, staged once", section "What moved, and onto what".
 //
 // bf16: v_mfma_f32_32x32x16_bf16, fp32 accumulation, 256x256x64 workgroup
-//   tiles, four wavefronts of 128x128, A/B tiles double-buffered in LDS with an
-//   XOR swizzle of the 16-byte chunks so the MFMA operand reads are
-//   bank-conflict free.
+//   tiles, four wavefronts of 128x128; A/B tiles stream HBM -> LDS by direct
+//   buffer loads (double-buffered, 128 KB) into an XOR-swizzled layout so the
+//   MFMA operand reads are bank-conflict free, and the next k-step's operands
+//   are read while the current MFMAs run.
 // f32: exact products and fp64 sums on v_mfma_f64_16x16x4_f64 (fp32 operands
 //   widened on the way in), 64x64x16 tiles and a deterministic split-K whose
 //   partition depends only on (N, K): each partial is reduced in a fixed order
@@ -23,34 +24,59 @@
 namespace dit {
 
 // ============================================================================ bf16 GEMM
+#ifndef DIT_GEMM_BK
+#define DIT_GEMM_BK 64
+#endif
+#ifndef DIT_GEMM_STAGES
+#define DIT_GEMM_STAGES 2
+#endif
 namespace gb {
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int WM = 128, WN = 128;            // per-wave tile
-constexpr int NWAVE = (BM / WM) * (BN / WN);  // 4
+constexpr int BM = 256, BN = 256, BK = DIT_GEMM_BK;
+constexpr int STAGES = DIT_GEMM_STAGES;       // LDS ring: tiles k+1 .. k+STAGES-1 load while k computes
+#ifndef DIT_GEMM_WAVES
+#define DIT_GEMM_WAVES 8
+#endif
+// 8 wavefronts of 128x64 (two per SIMD: one can issue MFMAs while the other
+// waits; measured 42-46% of peak against 37-40% for 4 of 128x128) or 4 of 128x128.
+constexpr int WM = 128, WN = DIT_GEMM_WAVES == 8 ? 64 : 128;  // per-wave tile
+constexpr int NWAVE = (BM / WM) * (BN / WN);
 constexpr int NT = NWAVE * 64;                // 256 threads
-constexpr int TM = WM / 32, TN = WN / 32;     // 32x32 MFMA tiles per wave: 4 x 4
-constexpr int CHUNKS_A = BM * (BK / 8) / NT;  // 16-byte chunks per thread per tile: 8
-constexpr int CHUNKS_B = BN * (BK / 8) / NT;  // 8
+constexpr int TM = WM / 32, TN = WN / 32;     // 32x32 MFMA tiles per wave
+constexpr int CPR = BK / 8;                   // 16-byte chunks per tile row: 4
+constexpr int DMA_PER_WAVE = BM * CPR / 64 / NWAVE;  // buffer_load...lds per operand per wave per stage: 4
 }  // namespace gb
 
-// 16-byte chunk c (0..7) of row r of a BK=64 bf16 tile row lives at physical
-// chunk c ^ ((r >> 1) & 7): the 16 rows read by one 16-lane LDS pass then hit
-// 16 distinct 4-bank groups.
-__device__ __forceinline__ int gb_swz(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
+// Chunk c of row r of a tile row of CPR 16-byte chunks lives at physical chunk
+// c ^ ((r / (16 / CPR)) % CPR): the 16 rows read at one logical chunk by a
+// 16-lane LDS pass then cover all 16 four-bank groups once.
+constexpr int gb_log2(int v) { return v <= 1 ? 0 : 1 + gb_log2(v / 2); }
+__device__ __forceinline__ int gb_swz(int r, int c) {
+  constexpr int sh = gb_log2(16 / gb::CPR);
+  return r * gb::CPR + (c ^ ((r >> sh) & (gb::CPR - 1)));
+}
+static_assert(gb::CPR == 4 || gb::CPR == 8, "tile rows of 4 or 8 16-byte chunks");
 
-__global__ __launch_bounds__(gb::NT, 1) void gemm_bf16_kernel(int M, int N, int K,
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Tiles move HBM -> LDS with buffer_load_dwordx4 ... lds (no VGPR staging, no
+// ds_write): lane l of one instruction writes its 16 bytes at LDS base + 16*l,
+// and a read past the buffer's num_records returns zero, which pads the M and N
+// tails.  A 256x32 tile is 16 such instructions; wave w issues 4w .. 4w+3.
+// Instruction i covers LDS chunks 64i .. 64i+63 = rows 16i .. 16i+15, so lane l
+// fetches row 16i + l/4 at the logical chunk whose swizzled position is l%4.
+__global__ __launch_bounds__(gb::NT) void gemm_bf16_kernel(int M, int N, int K,
                                                               const bf16_t* __restrict__ A,
                                                               const bf16_t* __restrict__ B,
                                                               const float* __restrict__ bias,
                                                               void* __restrict__ Cv, int c_f32,
                                                               int tiles_m, int tiles_n) {
   using namespace gb;
-  __shared__ uint4 smem[2 * (BM + BN) * (BK / 8)];  // 2 stages x (A + B) x 16-byte chunks = 128 KB
+  __shared__ uint4 smem[STAGES * (BM + BN) * CPR];  // STAGES x (A + B): 128 KB at 2 x 64 or 4 x 32
   uint4* As = smem;
-  uint4* Bs = smem + 2 * BM * (BK / 8);
+  uint4* Bs = smem + STAGES * BM * CPR;
 
-  // Tile order: walk M fastest inside a column of tiles so consecutive
-  // workgroups reuse the same weight tile.
+  // Walk M fastest inside a column of tiles so consecutive workgroups share
+  // the weight tile.
   const int bid = blockIdx.x;
   const int tm = bid % tiles_m;
   const int tn = bid / tiles_m;
@@ -60,6 +86,23 @@ __global__ __launch_bounds__(gb::NT, 1) void gemm_bf16_kernel(int M, int N, int 
   const int lane = tid & 63, wave = tid >> 6;
   const int wr = (wave / (BN / WN)) * WM, wc = (wave % (BN / WN)) * WN;
 
+  const int a_rows = M - m0 < BM ? M - m0 : BM;
+  const int b_rows = N - n0 < BN ? N - n0 : BN;
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(A + static_cast<size_t>(m0) * K), 0, a_rows * K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(B + static_cast<size_t>(n0) * K), 0, b_rows * K * 2, 0x00020000);
+  // Byte offset of this lane's chunk for instruction j of its wave: instruction
+  // i covers rows (64/CPR) i .. (64/CPR) i + 64/CPR - 1.
+  uint32_t voff[DMA_PER_WAVE];
+#pragma unroll
+  for (int j = 0; j < DMA_PER_WAVE; ++j) {
+    const int i = wave * DMA_PER_WAVE + j;
+    const int row = (64 / CPR) * i + lane / CPR;
+    const int c = gb_swz(row, lane % CPR) - row * CPR;  // logical chunk stored at position lane % CPR
+    voff[j] = static_cast<uint32_t>(row * K + c * 8) * 2u;
+  }
+
   f32x16_t acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -68,74 +111,84 @@ __global__ __launch_bounds__(gb::NT, 1) void gemm_bf16_kernel(int M, int N, int 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // Prefetch registers: eight 16-byte chunks of A and of B per thread, held in
-  // named variables (an array here is demoted to LDS/scratch by the compiler).
-  static_assert(CHUNKS_A == 8 && CHUNKS_B == 8, "prefetch registers are unrolled for 8 chunks");
-  uint4 ra0, ra1, ra2, ra3, ra4, ra5, ra6, ra7, rb0, rb1, rb2, rb3, rb4, rb5, rb6, rb7;
-#define GB_REP8(X) X(0) X(1) X(2) X(3) X(4) X(5) X(6) X(7)
-#define GB_LD(i)                                                                              \
-  {                                                                                           \
-    const int id = tid + NT * (i), r = id >> 3, c = id & 7;                                   \
-    const int gm = m0 + r, gn = n0 + r;                                                       \
-    ra##i = gm < M ? *reinterpret_cast<const uint4*>(A + static_cast<size_t>(gm) * K + kload + c * 8) \
-                   : make_uint4(0, 0, 0, 0);                                                  \
-    rb##i = gn < N ? *reinterpret_cast<const uint4*>(B + static_cast<size_t>(gn) * K + kload + c * 8) \
-                   : make_uint4(0, 0, 0, 0);                                                  \
-  }
-#define GB_ST(i)                                                                              \
-  {                                                                                           \
-    const int id = tid + NT * (i);                                                            \
-    As[sstage * BM * 8 + gb_swz(id >> 3, id & 7)] = ra##i;                                    \
-    Bs[sstage * BN * 8 + gb_swz(id >> 3, id & 7)] = rb##i;                                    \
-  }
-#define GB_GLOAD(k0)         \
-  {                          \
-    const int kload = (k0);  \
-    GB_REP8(GB_LD)           \
-  }
-#define GB_SSTORE(st)        \
-  {                          \
-    const int sstage = (st); \
-    GB_REP8(GB_ST)           \
+#define GB_DMA(stage, k0)                                                                               \
+  {                                                                                                     \
+    const int soff = (k0) * 2;                                                                          \
+    _Pragma("unroll") for (int j = 0; j < DMA_PER_WAVE; ++j) {                                         \
+      const int i = wave * DMA_PER_WAVE + j;                                                            \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(As + (stage) * BM * CPR + i * 64), 16,  \
+                                               voff[j], soff, 0, 0);                                   \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(Bs + (stage) * BN * CPR + i * 64), 16,  \
+                                               voff[j], soff, 0, 0);                                   \
+    }                                                                                                   \
   }
 
   const int KT = K / BK;
-  GB_GLOAD(0)
-  GB_SSTORE(0)
-  __syncthreads();
-
   const int lr = lane & 31, lg = lane >> 5;
+
+// One BK tile of MFMAs from LDS stage `st`: the operands of k-step s+1 are
+// read while the 16 MFMAs of k-step s run.
+#define GB_COMPUTE(st)                                                                                  \
+  {                                                                                                     \
+    const uint4* a_ = As + (st) * BM * CPR;                                                             \
+    const uint4* b_ = Bs + (st) * BN * CPR;                                                             \
+    bf16x8_t fa[2][TM], fb[2][TN];                                                                      \
+    _Pragma("unroll") for (int i = 0; i < TM; ++i) fa[0][i] =                                          \
+        __builtin_bit_cast(bf16x8_t, a_[gb_swz(wr + i * 32 + lr, lg)]);                                 \
+    _Pragma("unroll") for (int j = 0; j < TN; ++j) fb[0][j] =                                          \
+        __builtin_bit_cast(bf16x8_t, b_[gb_swz(wc + j * 32 + lr, lg)]);                                 \
+    _Pragma("unroll") for (int ks = 0; ks < BK / 16; ++ks) {                                           \
+      const int cur = ks & 1;                                                                           \
+      if (ks + 1 < BK / 16) {                                                                           \
+        const int c_ = (ks + 1) * 2 + lg;                                                               \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i) fa[cur ^ 1][i] =                                \
+            __builtin_bit_cast(bf16x8_t, a_[gb_swz(wr + i * 32 + lr, c_)]);                             \
+        _Pragma("unroll") for (int j = 0; j < TN; ++j) fb[cur ^ 1][j] =                                \
+            __builtin_bit_cast(bf16x8_t, b_[gb_swz(wc + j * 32 + lr, c_)]);                             \
+      }                                                                                                 \
+      _Pragma("unroll") for (int i = 0; i < TM; ++i)                                                   \
+        _Pragma("unroll") for (int j = 0; j < TN; ++j)                                                 \
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0); \
+    }                                                                                                   \
+  }
+
+  // Prologue: tiles 0 .. STAGES-2 in flight.
+#pragma unroll
+  for (int p = 0; p < STAGES - 1; ++p)
+    if (p < KT) GB_DMA(p, p * BK)
+
   for (int kt = 0; kt < KT; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < KT) {
-      GB_GLOAD((kt + 1) * BK)
-    }
-    const uint4* a = As + st * BM * 8;
-    const uint4* b = Bs + st * BN * 8;
+    const int st = kt % STAGES;
+    // Tile kt must have landed: the younger in-flight tiles (2*DMA_PER_WAVE
+    // loads each per wave) may stay outstanding.
+    const int younger = KT - 1 - kt < STAGES - 2 ? KT - 1 - kt : STAGES - 2;
+    constexpr int PER = 2 * DMA_PER_WAVE;
+#define GB_VMCNT(n) (0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+    if (STAGES >= 4 && younger >= 2)
+      __builtin_amdgcn_s_waitcnt(GB_VMCNT(2 * PER < 63 ? 2 * PER : 63));
+    else if (STAGES >= 3 && younger >= 1)
+      __builtin_amdgcn_s_waitcnt(GB_VMCNT(PER));
+    else
+      __builtin_amdgcn_s_waitcnt(GB_VMCNT(0));
+#undef GB_VMCNT
+    __syncthreads();  // every wave's part of tile kt is in LDS; stage (kt-1) is free
+    if (kt + STAGES - 1 < KT) GB_DMA((kt + STAGES - 1) % STAGES, (kt + STAGES - 1) * BK)
+    GB_COMPUTE(st)
+    // Inside the block: the operand reads of k-step 0, then in each k-step the
+    // MFMAs, the first TM+TN of them each followed by one operand read of the
+    // next k-step.
+    __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8_t fa[TM], fb[TN];
-      const int c = ks * 2 + lg;
 #pragma unroll
-      for (int i = 0; i < TM; ++i) fa[i] = __builtin_bit_cast(bf16x8_t, a[gb_swz(wr + i * 32 + lr, c)]);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) fb[j] = __builtin_bit_cast(bf16x8_t, b[gb_swz(wc + j * 32 + lr, c)]);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      for (int t = 0; t < TM * TN; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (ks + 1 < BK / 16 && t < TM + TN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
     }
-    if (kt + 1 < KT) {
-      GB_SSTORE(st ^ 1)
-    }
-    __syncthreads();
   }
-#undef GB_GLOAD
-#undef GB_SSTORE
-#undef GB_LD
-#undef GB_ST
-#undef GB_REP8
+#undef GB_COMPUTE
+#undef GB_DMA
 
   // Epilogue: lane l of a 32x32 tile holds column l%32, rows 8*(e/4) + 4*(l/32) + e%4.
 #pragma unroll
@@ -160,7 +213,10 @@ __global__ __launch_bounds__(gb::NT, 1) void gemm_bf16_kernel(int M, int N, int 
   }
 }
 
-bool gemm_bf16_supported(int M, int N, int K) { return M >= 0 && N > 0 && K > 0 && K % gb::BK == 0; }
+// K a multiple of 32; a 256-row tile of either operand must fit 32-bit buffer offsets.
+bool gemm_bf16_supported(int M, int N, int K) {
+  return M >= 0 && N > 0 && K > 0 && K % gb::BK == 0 && static_cast<int64_t>(gb::BM) * K * 2 < (int64_t(1) << 31);
+}
 size_t gemm_bf16_ws_bytes(int, int, int) { return 0; }
 
 hipError_t gemm_bf16(int M, int N, int K, const uint16_t* A, const uint16_t* B, const float* bias,
