@@ -9,8 +9,6 @@
 namespace dit {
 
 // ============================================================================ modulate + norm
-// One wavefront per row, four rows per 256-thread block.  Lane l holds float4
-// chunks l, l+64, ... of the row in registers, so x is read once.
 // Page "port the MiniMax-H3 omni-modal video+audio DiT", section "The
 // device-resident forward (W2b)": RmsNorm reduces in f32, then an indexed AdaLN
 // modulate; page "the 2.4B fp32 DiT onto the device", section "What moved":
@@ -35,23 +33,47 @@ template <> struct store4<bf16_t> {
 template <typename TO> struct norm_acc { typedef float T; };
 template <> struct norm_acc<float> { typedef double T; };
 
-template <typename TO, int NCH>
+// TPR threads (TPR/64 wavefronts) per row, 256/TPR rows per block; thread t of
+// a row holds float4 chunks t, t+TPR, ... (at most NCH) in registers, so x is
+// read once.  Sums: butterfly inside the wavefront, then across the row's
+// wavefronts through LDS.
+template <typename A, int WPR>
+__device__ __forceinline__ A row_sum(A v, A* red, int wrow, int wsub, int lane) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  if (WPR == 1) return v;
+  __syncthreads();
+  if (lane == 0) red[wrow * WPR + wsub] = v;
+  __syncthreads();
+  A t = 0;
+#pragma unroll
+  for (int i = 0; i < WPR; ++i) t += red[wrow * WPR + i];
+  return t;
+}
+
+template <typename TO, int TPR, int NCH>
 __global__ __launch_bounds__(256) void modnorm_kernel(int N, int D, int norm, float eps,
                                                      const float* __restrict__ x,
                                                      const float* __restrict__ mod, int shift_k,
                                                      int scale_k, const int32_t* __restrict__ cond_idx,
                                                      TO* __restrict__ h) {
   typedef typename norm_acc<TO>::T A;
+  constexpr int WPR = TPR / 64, RPB = 256 / TPR;
+  __shared__ A red[RPB * WPR];
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= N) return;
+  const int wrow = threadIdx.x / TPR;             // row within the block
+  const int wsub = (threadIdx.x % TPR) >> 6;      // wavefront within the row
+  const int t = threadIdx.x % TPR;
+  const int row_raw = blockIdx.x * RPB + wrow;
+  const bool live = row_raw < N;
+  const int row = live ? row_raw : N - 1;         // dead rows keep every barrier reachable
   const int D4 = D >> 2;
   const float4* xr = reinterpret_cast<const float4*>(x + static_cast<size_t>(row) * D);
   float4 v[NCH];
   A s = 0;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    const int c = lane + 64 * i;
+    const int c = t + TPR * i;
     if (c < D4) {
       v[i] = xr[c];
       s += (A(v[i].x) + A(v[i].y)) + (A(v[i].z) + A(v[i].w));
@@ -61,22 +83,18 @@ __global__ __launch_bounds__(256) void modnorm_kernel(int N, int D, int norm, fl
   }
   const A inv_d = A(1) / A(D);
   A mean = 0;
-  if (norm == 1) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
-    mean = s * inv_d;
-  }
+  if (norm == 1) mean = row_sum<A, WPR>(s, red, wrow, wsub, lane) * inv_d;
   A ss = 0;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    const int c = lane + 64 * i;
+    const int c = t + TPR * i;
     if (c < D4) {
       const A a = A(v[i].x) - mean, b = A(v[i].y) - mean, cc = A(v[i].z) - mean, d = A(v[i].w) - mean;
       ss += (a * a + b * b) + (cc * cc + d * d);
     }
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  ss = row_sum<A, WPR>(ss, red, wrow, wsub, lane);
+  if (!live) return;
   const A rstd = A(1) / sqrt(ss * inv_d + A(eps));
   const float4* sh = nullptr;
   const float4* sc = nullptr;
@@ -88,7 +106,7 @@ __global__ __launch_bounds__(256) void modnorm_kernel(int N, int D, int norm, fl
   TO* hr = h + static_cast<size_t>(row) * D;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    const int c = lane + 64 * i;
+    const int c = t + TPR * i;
     if (c < D4) {
       A y0 = (A(v[i].x) - mean) * rstd, y1 = (A(v[i].y) - mean) * rstd;
       A y2 = (A(v[i].z) - mean) * rstd, y3 = (A(v[i].w) - mean) * rstd;
@@ -109,16 +127,21 @@ bool modnorm_supported(int D) { return D > 0 && D % 4 == 0 && D <= 8192; }
 template <typename TO>
 static hipError_t modnorm_t(int norm, float eps, int N, int D, const float* x, const float* mod,
                             int which, const int32_t* ci, TO* h, hipStream_t s) {
-  const int nch = (D / 4 + 63) / 64;
+  const int d4 = D / 4;
   const int shift_k = which == 0 ? 0 : 3, scale_k = which == 0 ? 1 : 4;
-  dim3 grid((N + 3) / 4), block(256);
-#define DIT_MN(K)                                                                          \
-  if (nch <= K) {                                                                          \
-    hipLaunchKernelGGL((modnorm_kernel<TO, K>), grid, block, 0, s, N, D, norm, eps, x, mod, \
-                       shift_k, scale_k, ci, h);                                          \
-    return hipGetLastError();                                                              \
+#define DIT_MN(TPR, K)                                                                                \
+  if ((d4 + TPR - 1) / TPR <= K) {                                                                   \
+    hipLaunchKernelGGL((modnorm_kernel<TO, TPR, K>), dim3((N + 256 / TPR - 1) / (256 / TPR)), dim3(256), \
+                       0, s, N, D, norm, eps, x, mod, shift_k, scale_k, ci, h);                      \
+    return hipGetLastError();                                                                         \
   }
-  DIT_MN(1) DIT_MN(2) DIT_MN(4) DIT_MN(8) DIT_MN(12) DIT_MN(16) DIT_MN(24) DIT_MN(32)
+  if (d4 <= 256) {
+    DIT_MN(64, 1) DIT_MN(64, 2) DIT_MN(64, 4)
+  } else if (d4 <= 1024) {
+    DIT_MN(128, 4) DIT_MN(128, 8)
+  } else {
+    DIT_MN(256, 4) DIT_MN(256, 6) DIT_MN(256, 8)
+  }
 #undef DIT_MN
   return hipErrorInvalidValue;
 }
