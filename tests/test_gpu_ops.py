@@ -173,6 +173,28 @@ def test_attention_bf16(dit, cu, H):
     assert np.abs(got - ref).mean() / rms(ref) < 2e-3
 
 
+@pytest.mark.parametrize("slope", [0.05, 0.4])
+def test_attention_bf16_growing_max(dit, slope):
+    """Scores that keep growing along the keys, so the running row max moves
+    tile after tile (a few, or every, 64-key tile crosses the kernel's lazy
+    max-refresh threshold)."""
+    rng = np.random.default_rng(11)
+    cu = [0, 700, 1300]
+    N, H, hd = cu[-1], 2, 128
+    q, k, v = (rng.standard_normal((H, N, hd)).astype(np.float32) for _ in range(3))
+    q[:, :, 0] = 4.0
+    k[:, :, 0] = slope * np.arange(N, dtype=np.float32)
+    q, k, v = (torch.from_numpy(a).to(torch.bfloat16).float().numpy() for a in (q, k, v))
+    ref = O.attention_varlen(*(a.transpose(1, 0, 2).astype(np.float64) for a in (q, k, v)), np.array(cu))
+    ref = ref.reshape(N, H * hd)
+    o = torch.empty(N, H * hd, dtype=torch.bfloat16, device="cuda")
+    cut = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    dit.dit_attention(*(to_bf16_dev(a) for a in (q, k, v)), cut, 700, o)
+    got = from_dev(o)
+    assert_bf16_rounded(got, ref, "attention bf16 growing max", slack=1.2e-2)
+    assert np.abs(got - ref).mean() / rms(ref) < 2e-3
+
+
 def test_attention_bf16_segmentation_bits(dit):
     rng = np.random.default_rng(7)
     cu = [0, 200, 333]

@@ -16,173 +16,286 @@
 namespace dit {
 
 // ============================================================================ bf16, MFMA
-// Workgroup = one (head, document, 128-query tile); four wavefronts of 32
-// queries.  Scores are computed transposed, S^T = K Q^T, on
-// v_mfma_f32_32x32x16_bf16 so each lane owns one query and 16 of its keys per
-// 32-key block: the row max and row sum stay in the lane plus one partner lane.
-// The probabilities, rounded to bf16, are already in the B-operand layout of
-// the next MFMA, O^T = V^T P^T, given V^T in LDS with the key order inside
-// each 16-key group permuted to match (bits 2 and 3 of the key swapped).
+// Workgroup = one (document, head, 256-query tile); four wavefronts of 64
+// queries, one per SIMD.  Scores are computed transposed, S^T = K Q^T, on
+// v_mfma_f32_32x32x16_bf16, so each lane owns one query (per 32-query block)
+// and 16 of its keys per 32-key block: the row max and row sum stay in the
+// lane plus its partner lane l^32.  Each K or V fragment read from LDS feeds
+// the MFMAs of both 32-query blocks.
+//
+// The probabilities, rounded to bf16, are already the B operand of the next
+// MFMA, O^T = V^T P^T, if the contraction runs over keys in the order the
+// score accumulator holds them (within each 16-key group, keys 4g'..4g'+3 then
+// 8+4g'..8+4g'+3 for lane half g').  V stays key-major in LDS; its transposed
+// fragments come from ds_read_b64_tr_b16, which hands each lane 4 consecutive
+// keys of one dimension.
+//
+// K and V tiles of 64 keys move HBM -> LDS by direct buffer loads, double
+// buffered: while tile t's probabilities are formed, the scores of tile t+1
+// are computed from LDS, and the loads of K(t+2) and V(t+1) are in flight.
+// Reads past the document end return zero and those keys are masked.  The
+// accumulator rescale of the online softmax is skipped (wavefront-uniform
+// branch) for tiles where no row's max grows, which after the first few tiles
+// is most of them.  The max is always exact, so each row's largest probability
+// is 1 and is exact in bf16.
 namespace ab {
-constexpr int HD = 128, QT = 128, KT = 64, NT = 256;
-constexpr int VT_STRIDE = KT + 8;  // bf16 elements per V^T row (144 bytes)
+constexpr int HD = 128;                    // head dim
+constexpr int KT = 64;                     // keys per tile
+#ifndef DIT_ATTN_QB
+#define DIT_ATTN_QB 1
+#endif
+constexpr int QB = DIT_ATTN_QB;            // 32-query blocks per wavefront
+constexpr int QW = 32 * QB;                // queries per wavefront
+constexpr int NW = 8 / QB;                 // wavefronts per workgroup
+constexpr int QT = QW * NW;                // queries per workgroup
+constexpr int NT = NW * 64;
+constexpr int TILE = KT * HD / 8;          // 16-byte chunks of one K or V tile
+constexpr int DMA = TILE / 64 / NW;        // direct loads per wavefront per tile
 }  // namespace ab
 
-__device__ __forceinline__ int ab_kswz(int r, int c) { return r * 16 + (c ^ (r & 15)); }
-__device__ __forceinline__ int ab_vperm(int key) {
-  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+// K rows: chunk c of key r at r*16 + (c ^ (r % 16)), conflict-free for the
+// 16-lane passes of ds_read_b128 that fetch 16 keys at one chunk.
+__device__ __forceinline__ int ab_kpos(int key, int cc) { return key * 16 + (cc ^ (key & 15)); }
+// V rows: the transposing read fetches 4 consecutive keys x 32 dims per 32
+// lanes; XOR-ing the chunk's block-of-4 index with key % 4 spreads the four keys
+// over all 64 banks.
+__device__ __forceinline__ int ab_vswz(int key) { return ((key & 3) << 2) | ((key >> 2) & 3); }
+__device__ __forceinline__ int ab_vpos(int key, int cc) { return key * 16 + (cc ^ ab_vswz(key)); }
+
+typedef __attribute__((address_space(3))) void* ab_lds_t;
+typedef __bf16 ab_bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 ab_bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) ab_bf16x4* ab_lds4_t;
+
+__device__ __forceinline__ uint32_t ab_pack(float lo, float hi) {
+  const ab_bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};  // v_cvt_pk_bf16_f32, RNE
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float ab_pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float ab_pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__global__ __launch_bounds__(ab::NT) void attention_bf16_kernel(int N, int H,
-                                                                   const int32_t* __restrict__ cu,
-                                                                   const bf16_t* __restrict__ q,
-                                                                   const bf16_t* __restrict__ k,
-                                                                   const bf16_t* __restrict__ v,
-                                                                   bf16_t* __restrict__ o,
-                                                                   float scale_log2) {
+__global__ __launch_bounds__(ab::NT, 1) void attention_bf16_kernel(int N, int H, int n_docs, int qtiles,
+                                                                      int work, const int32_t* __restrict__ cu,
+                                                                      const bf16_t* __restrict__ q,
+                                                                      const bf16_t* __restrict__ k,
+                                                                      const bf16_t* __restrict__ v,
+                                                                      bf16_t* __restrict__ o,
+                                                                      float scale_log2) {
   using namespace ab;
-  // One LDS block: K tile (16 KB, swizzled rows of 16 chunks) then V^T (18 KB);
-  // reused whole for the output transpose at the end (4 x 32 x 136 bf16 = 34 KB).
-  __shared__ uint4 smem[(KT * HD + HD * VT_STRIDE) / 8];
-  uint4* Ks = smem;
-  bf16_t* Vt = reinterpret_cast<bf16_t*>(smem + KT * HD / 8);
+  __shared__ uint4 smem[4 * TILE];  // K[2] then V[2]: 64 KB
+  uint4* const Kb = smem;
+  uint4* const Vb = smem + 2 * TILE;
 
-  const int qt = blockIdx.x, h = blockIdx.y, d = blockIdx.z;
+  // Workgroups go to the 8 XCDs round-robin; give each XCD a contiguous run of
+  // (document, head, query tile) items so the workgroups sharing an L2 stream
+  // the same head's keys at the same time.
+  const int per_xcd = gridDim.x / 8;
+  const int w = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (w >= work) return;
+  const int qt = w % qtiles, h = (w / qtiles) % H, d = w / (qtiles * H);
   const int s0 = cu[d], len = cu[d + 1] - s0;
   const int q0 = qt * QT;
   if (q0 >= len) return;
+
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 31, lg = lane >> 5;
+  const size_t base = (static_cast<size_t>(h) * N + s0) * HD;  // this head's document start
 
-  const size_t head_off = static_cast<size_t>(h) * N * HD;
-  const int qi = q0 + wave * 32 + lr;  // this lane's query (document-relative)
-  bf16x8_t qf[HD / 16];
-  {
-    const bool ok = qi < len;
-    const bf16_t* qp = q + head_off + static_cast<size_t>(s0 + (ok ? qi : 0)) * HD;
+  // Q fragments (B operand of S^T): lane holds query lr of block qb, dims
+  // 16c + 8lg .. +7.  Rows past the document end repeat its last row.
+  bf16x8_t qf[QB][HD / 16];
 #pragma unroll
-    for (int c = 0; c < HD / 16; ++c) {
-      const uint4 t = ok ? *reinterpret_cast<const uint4*>(qp + 16 * c + 8 * lg) : make_uint4(0, 0, 0, 0);
-      qf[c] = __builtin_bit_cast(bf16x8_t, t);
-    }
+  for (int qb = 0; qb < QB; ++qb) {
+    int qi = q0 + wave * QW + qb * 32 + lr;
+    qi = qi < len ? qi : len - 1;
+    const bf16_t* qp = q + base + static_cast<size_t>(qi) * HD + 8 * lg;
+#pragma unroll
+    for (int c = 0; c < HD / 16; ++c) qf[qb][c] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qp + 16 * c));
   }
 
-  f32x16_t acc_o[HD / 32];
+  // Direct loads: instruction j of this wavefront fills LDS chunks
+  // (4 wave + j) * 64 + lane = key * 16 + position; the lane fetches the
+  // logical chunk that the swizzle stores at that position.
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(k + base), 0, len * HD * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(v + base), 0, len * HD * 2, 0x00020000);
+  uint32_t vok[DMA], vov[DMA];
 #pragma unroll
-  for (int i = 0; i < HD / 32; ++i)
+  for (int j = 0; j < DMA; ++j) {
+    const int ch = (wave * DMA + j) * 64 + lane, key = ch >> 4, pos = ch & 15;
+    vok[j] = static_cast<uint32_t>(key * HD + (pos ^ (key & 15)) * 8) * 2u;
+    vov[j] = static_cast<uint32_t>(key * HD + (pos ^ ab_vswz(key)) * 8) * 2u;
+  }
+  auto dma_k = [&](int t, int buf) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc_o[i][e] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+    for (int j = 0; j < DMA; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (ab_lds_t)(Kb + buf * TILE + (wave * DMA + j) * 64), 16,
+                                               vok[j] + static_cast<uint32_t>(t * KT * HD * 2), 0, 0, 0);
+  };
+  auto dma_v = [&](int t, int buf) {
+#pragma unroll
+    for (int j = 0; j < DMA; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (ab_lds_t)(Vb + buf * TILE + (wave * DMA + j) * 64), 16,
+                                               vov[j] + static_cast<uint32_t>(t * KT * HD * 2), 0, 0, 0);
+  };
 
-  const int n_kt = (len + KT - 1) / KT;
-  for (int t = 0; t < n_kt; ++t) {
-    const int k0 = t * KT;
-    __syncthreads();  // previous tile fully consumed
-    // K tile: 64 keys x 16 chunks; V tile transposed into V^T.
-#pragma unroll
-    for (int i = 0; i < (KT * HD / 8) / NT; ++i) {
-      const int id = tid + NT * i, r = id >> 4, c = id & 15;
-      const int kk = k0 + r;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (kk < len) {
-        const size_t off = head_off + static_cast<size_t>(s0 + kk) * HD + c * 8;
-        kv = *reinterpret_cast<const uint4*>(k + off);
-        vv = *reinterpret_cast<const uint4*>(v + off);
-      }
-      Ks[ab_kswz(r, c)] = kv;
-      const int pc = ab_vperm(r);
-      const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        Vt[(c * 8 + e) * VT_STRIDE + pc] = static_cast<bf16_t>((e & 1) ? (vw[e >> 1] >> 16) : (vw[e >> 1] & 0xFFFFu));
-    }
-    __syncthreads();
+  // Per-lane LDS offsets (bytes) of the K fragments (key 32kb + lr, chunk
+  // 2c + lg) and of the transposing V reads (4 keys from 16g + 8r + 4(lane/32)
+  // at dims 32i + 16((lane/16)%2) + 4(lane%4)).
+  const int vG = lane >> 4, ve = (lane >> 2) & 3, vc4 = lane & 3;
+  const int vkey0 = 4 * (vG >> 1) + ve;
+  const int vcc = 2 * (vG & 1) + (vc4 >> 1);
 
-    // S^T for keys [k0, k0+64): two 32x32 tiles, K = hd.
-    f32x16_t s[2];
+  f32x16_t acc[QB][HD / 32];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
-#pragma unroll
-      for (int c = 0; c < HD / 16; ++c) {
-        const bf16x8_t ta = __builtin_bit_cast(bf16x8_t, Ks[ab_kswz(kb * 32 + lr, 2 * c + lg)]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta, qf[c], s[kb], 0, 0, 0);
-      }
-    }
-    // Online softmax (base 2, scale folded in).  Lane holds keys
-    // k0 + 32*kb + 8*(e/4) + 4*lg + e%4 of its query.
-    float mt = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * lg + (e & 3);
-        const float x = key < len ? s[kb][e] * scale_log2 : -INFINITY;
-        s[kb][e] = x;
-        mt = fmaxf(mt, x);
-      }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    float ps = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = exp2f(s[kb][e] - m_new);
-        s[kb][e] = p;
-        ps += p;
-      }
-    l_run = l_run * alpha + ps;
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int i = 0; i < HD / 32; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc_o[i][e] *= alpha;
+      for (int e = 0; e < 16; ++e) acc[qb][i][e] = 0.f;
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) m_run[qb] = -INFINITY, l_run[qb] = 0.f;
 
-    // O^T += V^T P^T over four 16-key groups.
+  auto scores = [&](f32x16_t (&s)[QB][2], const uint4* kt) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int kb = g >> 1, base = (g & 1) * 8;
-      const uint4 pw = make_uint4(pack_bf16x2(s[kb][base + 0], s[kb][base + 1]),
-                                  pack_bf16x2(s[kb][base + 2], s[kb][base + 3]),
-                                  pack_bf16x2(s[kb][base + 4], s[kb][base + 5]),
-                                  pack_bf16x2(s[kb][base + 6], s[kb][base + 7]));
-      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int i = 0; i < HD / 32; ++i) {
-        const bf16x8_t tv = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const uint4*>(&Vt[(i * 32 + lr) * VT_STRIDE + g * 16 + 8 * lg]));
-        acc_o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tv, pf, acc_o[i], 0, 0, 0);
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[qb][kb][e] = 0.f;
+#pragma unroll
+    for (int c = 0; c < HD / 16; ++c)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, kt[ab_kpos(kb * 32 + lr, 2 * c + lg)]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][c], s[qb][kb], 0, 0, 0);
+      }
+  };
+
+  // One key tile: probabilities of tile t from its scores s, then the scores
+  // of tile t+1 into sn (independent MFMAs the exp work can hide behind), then
+  // O += V(t)^T P^T.
+  const int n_kt = (len + KT - 1) / KT;
+  auto step = [&](int t, f32x16_t(&s)[QB][2], f32x16_t(&sn)[QB][2]) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wavefront's loads of K(t+1), V(t) are done
+    __syncthreads();                     // ... and everyone's; tile t-1's buffers are free
+    if (t + 2 < n_kt) dma_k(t + 2, t & 1);
+    if (t + 1 < n_kt) dma_v(t + 1, (t + 1) & 1);
+
+    // Keys past the document end (last tile only).  Lane holds keys
+    // 32kb + 8(e/4) + 4lg + e%4 of the tile.
+    const int k0 = t * KT;
+    if (k0 + KT > len) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (k0 + kb * 32 + 8 * (e >> 2) + 4 * lg + (e & 3) >= len) s[qb][kb][e] = -INFINITY;
+    }
+    float mt[QB];
+    bool grow = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float m = s[qb][0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) m = fmaxf(m, s[qb][kb][e]);
+      mt[qb] = ab_pair_max(m);
+      grow |= mt[qb] > m_run[qb];
+    }
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float m_new = fmaxf(m_run[qb], mt[qb]);
+        const float alpha = __builtin_amdgcn_exp2f((m_run[qb] - m_new) * scale_log2);
+        m_run[qb] = m_new;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int i = 0; i < HD / 32; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[qb][i][e] *= alpha;
       }
     }
+    // P = 2^(s c - m c), rounded to bf16 in the B-operand layout.
+    bf16x8_t pf[QB][4];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float mc = m_run[qb] * scale_log2;
+      float ps = 0.f;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][g >> 1][8 * (g & 1) + j], scale_log2, -mc));
+          ps += p[j];
+        }
+        const uint4 pw = make_uint4(ab_pack(p[0], p[1]), ab_pack(p[2], p[3]), ab_pack(p[4], p[5]), ab_pack(p[6], p[7]));
+        pf[qb][g] = __builtin_bit_cast(bf16x8_t, pw);
+      }
+      l_run[qb] += ps;
+    }
+    if (t + 1 < n_kt) scores(sn, Kb + ((t + 1) & 1) * TILE);
+    // O^T += V^T P^T.
+    const char* vt = reinterpret_cast<const char*>(Vb + (t & 1) * TILE);
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int i = 0; i < HD / 32; ++i) {
+        ab_bf16x4 half_[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int key = 16 * g + 8 * r + vkey0;
+          const int off = ab_vpos(key, 4 * i + vcc) * 16 + 8 * (vc4 & 1);
+          half_[r] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ab_lds4_t)(vt + off));
+        }
+        const bf16x8_t vf = __builtin_shufflevector(half_[0], half_[1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) acc[qb][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][g], acc[qb][i], 0, 0, 0);
+      }
+  };
+
+  dma_k(0, 0);
+  if (n_kt > 1) dma_k(1, 1);
+  dma_v(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  f32x16_t sa[QB][2], sb[QB][2];
+  scores(sa, Kb);
+  for (int t = 0; t < n_kt; t += 2) {
+    step(t, sa, sb);
+    if (t + 1 < n_kt) step(t + 1, sb, sa);
   }
 
-  // Normalise and write through LDS so each query row leaves as 16-byte chunks.
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = 1.0f / l_tot;
-  __syncthreads();
-  bf16_t* Os = reinterpret_cast<bf16_t*>(smem) + wave * 32 * (HD + 8);  // 32 rows x 136 per wave
-#pragma unroll
-  for (int i = 0; i < HD / 32; ++i)
-#pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      const int dd = i * 32 + 8 * e4 + 4 * lg;
-      uint2 w;
-      w.x = pack_bf16x2(acc_o[i][4 * e4] * inv, acc_o[i][4 * e4 + 1] * inv);
-      w.y = pack_bf16x2(acc_o[i][4 * e4 + 2] * inv, acc_o[i][4 * e4 + 3] * inv);
-      *reinterpret_cast<uint2*>(&Os[lr * (HD + 8) + dd]) = w;
-    }
-  __syncthreads();
+  // Normalise; lane writes dims 32i + 8(e/4) + 4lg .. +3 of its query as 8 bytes.
   const int D = H * HD;
 #pragma unroll
-  for (int i = 0; i < (32 * HD / 8) / 64; ++i) {
-    const int id = lane + 64 * i, r = id >> 4, c = id & 15;
-    const int qq = q0 + wave * 32 + r;
-    if (qq < len)
-      *reinterpret_cast<uint4*>(o + static_cast<size_t>(s0 + qq) * D + h * HD + c * 8) =
-          *reinterpret_cast<const uint4*>(&Os[r * (HD + 8) + c * 8]);
+  for (int qb = 0; qb < QB; ++qb) {
+    const float inv = 1.0f / ab_pair_sum(l_run[qb]);
+    const int qi = q0 + wave * QW + qb * 32 + lr;
+    if (qi < len) {
+      bf16_t* op = o + static_cast<size_t>(s0 + qi) * D + h * HD + 4 * lg;
+#pragma unroll
+      for (int i = 0; i < HD / 32; ++i)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const uint2 wv = make_uint2(ab_pack(acc[qb][i][4 * e4] * inv, acc[qb][i][4 * e4 + 1] * inv),
+                                      ab_pack(acc[qb][i][4 * e4 + 2] * inv, acc[qb][i][4 * e4 + 3] * inv));
+          *reinterpret_cast<uint2*>(op + i * 32 + 8 * e4) = wv;
+        }
+    }
   }
 }
 
@@ -304,8 +417,12 @@ hipError_t attention_bf16(int N, int H, int hd, int n_docs, const int32_t* cu, i
   if (N == 0 || n_docs == 0 || max_seqlen == 0) return hipSuccess;
   LaunchScope scope_(kCntAttnBf16, s);
   const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(hd));
-  dim3 grid((max_seqlen + ab::QT - 1) / ab::QT, H, n_docs);
-  hipLaunchKernelGGL(attention_bf16_kernel, grid, dim3(ab::NT), 0, s, N, H, cu, q, k, v, o, scale_log2);
+  const int qtiles = (max_seqlen + ab::QT - 1) / ab::QT;
+  const int64_t work = static_cast<int64_t>(qtiles) * H * n_docs;
+  if (work > (int64_t(1) << 30)) return hipErrorInvalidValue;
+  const int blocks = static_cast<int>((work + 7) / 8 * 8);  // a multiple of the XCD count
+  hipLaunchKernelGGL(attention_bf16_kernel, dim3(blocks), dim3(ab::NT), 0, s, N, H, n_docs, qtiles,
+                     static_cast<int>(work), cu, q, k, v, o, scale_log2);
   return hipGetLastError();
 }
 
