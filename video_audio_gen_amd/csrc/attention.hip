@@ -92,11 +92,11 @@ __global__ __launch_bounds__(ab::NT, 1) void attention_bf16_kernel(int N, int H,
   uint4* const Kb = smem;
   uint4* const Vb = smem + 2 * TILE;
 
-  // Workgroups go to the 8 XCDs round-robin; give each XCD a contiguous run of
-  // (document, head, query tile) items so the workgroups sharing an L2 stream
-  // the same head's keys at the same time.
-  const int per_xcd = gridDim.x / 8;
-  const int w = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  // Workgroups go to the 8 XCDs round-robin.  Within each run of 256
+  // consecutive workgroups (one per CU), XCD x takes 32 consecutive
+  // (document, head, query tile) items, so the CUs sharing an L2 stream the
+  // same head's keys at the same time, and every XCD sees every document.
+  const int w = (blockIdx.x / 256) * 256 + (blockIdx.x % 8) * 32 + (blockIdx.x / 8) % 32;
   if (w >= work) return;
   const int qt = w % qtiles, h = (w / qtiles) % H, d = w / (qtiles * H);
   const int s0 = cu[d], len = cu[d + 1] - s0;
@@ -149,9 +149,19 @@ __global__ __launch_bounds__(ab::NT, 1) void attention_bf16_kernel(int N, int H,
   // Per-lane LDS offsets (bytes) of the K fragments (key 32kb + lr, chunk
   // 2c + lg) and of the transposing V reads (4 keys from 16g + 8r + 4(lane/32)
   // at dims 32i + 16((lane/16)%2) + 4(lane%4)).
+  // The V swizzle of key 16g + 8r + vkey0 does not depend on g, so the lane
+  // part of each (r, i) read offset is fixed and g adds a constant.
   const int vG = lane >> 4, ve = (lane >> 2) & 3, vc4 = lane & 3;
   const int vkey0 = 4 * (vG >> 1) + ve;
   const int vcc = 2 * (vG & 1) + (vc4 >> 1);
+  int voff_lane[2][HD / 32];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int i = 0; i < HD / 32; ++i) voff_lane[r][i] = ab_vpos(8 * r + vkey0, 4 * i + vcc) * 16 + 8 * (vc4 & 1);
+  int koff_lane[HD / 16];
+#pragma unroll
+  for (int c = 0; c < HD / 16; ++c) koff_lane[c] = ab_kpos(lr, 2 * c + lg) * 16;
 
   f32x16_t acc[QB][HD / 32];
 #pragma unroll
@@ -175,7 +185,8 @@ __global__ __launch_bounds__(ab::NT, 1) void attention_bf16_kernel(int N, int H,
     for (int c = 0; c < HD / 16; ++c)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, kt[ab_kpos(kb * 32 + lr, 2 * c + lg)]);
+        // key 32kb + lr has the same swizzle as key lr
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(reinterpret_cast<const char*>(kt) + kb * 32 * 256 + koff_lane[c]);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][c], s[qb][kb], 0, 0, 0);
       }
@@ -185,11 +196,11 @@ __global__ __launch_bounds__(ab::NT, 1) void attention_bf16_kernel(int N, int H,
   // of tile t+1 into sn (independent MFMAs the exp work can hide behind), then
   // O += V(t)^T P^T.
   const int n_kt = (len + KT - 1) / KT;
-  auto step = [&](int t, f32x16_t(&s)[QB][2], f32x16_t(&sn)[QB][2]) {
+  auto step = [&](int t, int buf, f32x16_t(&s)[QB][2], f32x16_t(&sn)[QB][2]) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // this wavefront's loads of K(t+1), V(t) are done
     __syncthreads();                     // ... and everyone's; tile t-1's buffers are free
-    if (t + 2 < n_kt) dma_k(t + 2, t & 1);
-    if (t + 1 < n_kt) dma_v(t + 1, (t + 1) & 1);
+    if (t + 2 < n_kt) dma_k(t + 2, buf);
+    if (t + 1 < n_kt) dma_v(t + 1, buf ^ 1);
 
     // Keys past the document end (last tile only).  Lane holds keys
     // 32kb + 8(e/4) + 4lg + e%4 of the tile.
@@ -228,28 +239,34 @@ __global__ __launch_bounds__(ab::NT, 1) void attention_bf16_kernel(int N, int H,
           for (int e = 0; e < 16; ++e) acc[qb][i][e] *= alpha;
       }
     }
-    // P = 2^(s c - m c), rounded to bf16 in the B-operand layout.
+    // P = 2^(s c - m c), rounded to bf16 in the B-operand layout; the row sum
+    // adds the rounded values (v_dot2 with 1.0), so the weights the output is
+    // normalised by are exactly the ones it was summed with.
     bf16x8_t pf[QB][4];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float mc = m_run[qb] * scale_log2;
       float ps = 0.f;
+      const ab_bf16x2 one2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         float p[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][g >> 1][8 * (g & 1) + j], scale_log2, -mc));
-          ps += p[j];
         }
         const uint4 pw = make_uint4(ab_pack(p[0], p[1]), ab_pack(p[2], p[3]), ab_pack(p[4], p[5]), ab_pack(p[6], p[7]));
+        ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(ab_bf16x2, pw.x), one2, ps, false);
+        ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(ab_bf16x2, pw.y), one2, ps, false);
+        ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(ab_bf16x2, pw.z), one2, ps, false);
+        ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(ab_bf16x2, pw.w), one2, ps, false);
         pf[qb][g] = __builtin_bit_cast(bf16x8_t, pw);
       }
       l_run[qb] += ps;
     }
-    if (t + 1 < n_kt) scores(sn, Kb + ((t + 1) & 1) * TILE);
+    if (t + 1 < n_kt) scores(sn, Kb + (buf ^ 1) * TILE);
     // O^T += V^T P^T.
-    const char* vt = reinterpret_cast<const char*>(Vb + (t & 1) * TILE);
+    const char* vt = reinterpret_cast<const char*>(Vb + buf * TILE);
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
@@ -257,9 +274,7 @@ __global__ __launch_bounds__(ab::NT, 1) void attention_bf16_kernel(int N, int H,
         ab_bf16x4 half_[2];
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
-          const int key = 16 * g + 8 * r + vkey0;
-          const int off = ab_vpos(key, 4 * i + vcc) * 16 + 8 * (vc4 & 1);
-          half_[r] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ab_lds4_t)(vt + off));
+          half_[r] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ab_lds4_t)(vt + 16 * g * 256 + voff_lane[r][i]));
         }
         const bf16x8_t vf = __builtin_shufflevector(half_[0], half_[1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
@@ -275,8 +290,8 @@ __global__ __launch_bounds__(ab::NT, 1) void attention_bf16_kernel(int N, int H,
   f32x16_t sa[QB][2], sb[QB][2];
   scores(sa, Kb);
   for (int t = 0; t < n_kt; t += 2) {
-    step(t, sa, sb);
-    if (t + 1 < n_kt) step(t + 1, sb, sa);
+    step(t, 0, sa, sb);
+    if (t + 1 < n_kt) step(t + 1, 1, sb, sa);
   }
 
   // Normalise; lane writes dims 32i + 8(e/4) + 4lg .. +3 of its query as 8 bytes.
@@ -420,7 +435,7 @@ hipError_t attention_bf16(int N, int H, int hd, int n_docs, const int32_t* cu, i
   const int qtiles = (max_seqlen + ab::QT - 1) / ab::QT;
   const int64_t work = static_cast<int64_t>(qtiles) * H * n_docs;
   if (work > (int64_t(1) << 30)) return hipErrorInvalidValue;
-  const int blocks = static_cast<int>((work + 7) / 8 * 8);  // a multiple of the XCD count
+  const int blocks = static_cast<int>((work + 255) / 256 * 256);  // whole runs of 8 XCDs x 32 CUs
   hipLaunchKernelGGL(attention_bf16_kernel, dim3(blocks), dim3(ab::NT), 0, s, N, H, n_docs, qtiles,
                      static_cast<int>(work), cu, q, k, v, o, scale_log2);
   return hipGetLastError();
