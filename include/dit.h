@@ -50,7 +50,7 @@ typedef enum dit_status {
   DIT_E_UNSUPPORTED = 9     /* a shape outside what the kernels handle (message says which) */
 } dit_status;
 
-enum { DIT_F32 = 0, DIT_BF16 = 1 };
+enum { DIT_F32 = 0, DIT_BF16 = 1, DIT_F64 = 2 /* residual stream of an fp32 model only */ };
 enum { DIT_NORM_RMS = 0, DIT_NORM_LAYER = 1 };
 enum { DIT_MLP_GATE_UP = 0, DIT_MLP_VALUE_GATE = 1 };
 enum { DIT_IO_NONE = 0, DIT_IO_PATCH3D = 1, DIT_IO_CHANNEL_MAJOR = 2 };
@@ -216,7 +216,10 @@ int dit_modulation(dit_model* m, const dit_batch* b, int block0, int n_blocks,
                    const float* cond_dev, float* mod_dev, dit_stream_t stream);
 
 /* One block on the packed residual stream x_dev [N, D] float32, in place.
- * mod_dev [n_cond, 6, D] float32 (this block's rows of dit_modulation). */
+ * mod_dev [n_cond, 6, D] float32 (this block's rows of dit_modulation).  An
+ * fp32 model carries its residual stream in float64 inside the library (here:
+ * widened on entry, rounded to float32 once on exit); a bf16 model's is the
+ * float32 x_dev itself. */
 int dit_block_forward(dit_model* m, int block, float* x_dev, const float* mod_dev,
                       const dit_batch* b, void* ws_dev, size_t ws_bytes, dit_stream_t stream);
 
@@ -254,11 +257,12 @@ int dit_gemm_workspace_bytes(int dtype, int M, int N, int K, size_t* bytes);
 int dit_gemm(int dtype, int M, int N, int K, const void* A, const void* B, const float* bias,
              void* C, int c_dtype, void* ws, size_t ws_bytes, dit_stream_t stream);
 
-/* h[N,D] (dtype) = norm(x[N,D] f32) * (1 + mod[c][scale_k]) + mod[c][shift_k],
+/* h[N,D] (dtype) = norm(x[N,D]) * (1 + mod[c][scale_k]) + mod[c][shift_k],
  * c = cond_idx[n]; mod [n_cond, 6, D] f32; which = 0 (msa: shift 0, scale 1) or
- * 1 (mlp: shift 3, scale 4); mod NULL = plain norm.  norm = DIT_NORM_*. */
-int dit_modnorm(int dtype, int norm, float eps, int N, int D, const float* x, const float* mod,
-                int which, const int32_t* cond_idx, void* h, dit_stream_t stream);
+ * 1 (mlp: shift 3, scale 4); mod NULL = plain norm.  norm = DIT_NORM_*.  x is
+ * x_dtype: DIT_F32, or DIT_F64 (the fp32 stream's residual, dtype DIT_F32). */
+int dit_modnorm(int dtype, int norm, float eps, int N, int D, const void* x, int x_dtype,
+                const float* mod, int which, const int32_t* cond_idx, void* h, dit_stream_t stream);
 
 /* qkv [N, 3D] (dtype) -> q, k, v head-major [H, N, hd] (dtype); rotate_half
  * RoPE on the first rot dims of q and k from cos/sin [N, rot/2]; v copied. */
@@ -275,8 +279,10 @@ int dit_attention(int dtype, int N, int H, int hd, int n_docs, const int32_t* cu
 /* m [N, F] (dtype) = silu(u[:, :F]) * u[:, F:]; u [N, 2F] (dtype). */
 int dit_silu_gate(int dtype, int N, int F, const void* u, void* m, dit_stream_t stream);
 
-/* x[N,D] f32 += mod[c][gate_k] * a[N,D] f32, c = cond_idx[n]; which 0 (gate 2) or 1 (gate 5). */
-int dit_gated_residual(int N, int D, float* x, const float* a, const float* mod, int which,
+/* x[N,D] += mod[c][gate_k] * a[N,D] f32, c = cond_idx[n]; which 0 (gate 2) or 1
+ * (gate 5); x is x_dtype DIT_F32 (fused multiply-add) or DIT_F64 (exact product,
+ * one fp64 rounding). */
+int dit_gated_residual(int N, int D, void* x, int x_dtype, const float* a, const float* mod, int which,
                        const int32_t* cond_idx, dit_stream_t stream);
 
 /* ------------------------------------------------------------------ diagnostics */
@@ -284,7 +290,7 @@ int dit_gated_residual(int N, int D, float* x, const float* a, const float* mod,
 const char* dit_last_error(void);
 /* Launch counters per kernel family (index order: gemm_bf16, gemm_f32, attention_bf16,
  * attention_f32, modnorm, rope_split, silu_gate, gated_residual, adaln, patch_in,
- * patch_out, euler, gemm_f32_reduce); n_max entries written; returns DIT_OK. */
+ * patch_out, euler, gemm_f32_reduce, convert); n_max entries written; returns DIT_OK. */
 int dit_counters(int64_t* out, int n_max);
 void dit_counters_reset(void);
 

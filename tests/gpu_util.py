@@ -13,6 +13,8 @@ def to_bf16_dev(a: np.ndarray) -> torch.Tensor:
 
 def from_dev(t: torch.Tensor) -> np.ndarray:
     torch.cuda.synchronize()
+    if t.dtype == torch.float64:
+        return t.cpu().numpy()
     return t.float().cpu().numpy().astype(np.float64)
 
 

@@ -255,3 +255,34 @@ def test_gated_residual(dit):
                            torch.from_numpy(ci).cuda())
     torch.cuda.synchronize()
     assert torch.equal(xt.cpu(), torch.from_numpy(x))  # a zero gate leaves x bit-identical
+
+
+def test_gated_residual_f64(dit):
+    """The fp32 stream's residual in float64: gate * a is exact in fp64, so the
+    update is the fp64 rounding of the exact sum."""
+    rng = np.random.default_rng(5)
+    N, D, n_cond = 77, 2560, 2
+    x = rng.standard_normal((N, D)) * 3.0
+    a = rng.standard_normal((N, D)).astype(np.float32)
+    mod = rng.standard_normal((n_cond, 6, D)).astype(np.float32)
+    ci = rng.integers(0, n_cond, N).astype(np.int32)
+    for which, gk in ((0, 2), (1, 5)):
+        xt = torch.from_numpy(x).cuda()
+        dit.dit_gated_residual(xt, torch.from_numpy(a).cuda(), torch.from_numpy(mod).cuda(), which,
+                               torch.from_numpy(ci).cuda())
+        ref = x + mod[ci, gk].astype(np.float64) * a.astype(np.float64)
+        assert np.array_equal(from_dev(xt), ref)  # numpy's fp64 a*b + x rounds the same way
+
+
+@pytest.mark.parametrize("norm", [0, 1])
+def test_modnorm_f64_residual(dit, norm):
+    rng = np.random.default_rng(6 + norm)
+    N, D, n_cond = 203, 2560, 3
+    x = rng.standard_normal((N, D)) * 2 + 0.5 + rng.standard_normal((N, D)) * 1e-9  # below fp32 resolution
+    mod = (rng.standard_normal((n_cond, 6, D)) * 0.3).astype(np.float32)
+    ci = rng.integers(0, n_cond, N).astype(np.int32)
+    kind = "rms" if norm == 0 else "layer"
+    ref = O.modulate(O.norm(x, kind, 1e-6), mod[ci, 0].astype(np.float64), mod[ci, 1].astype(np.float64))
+    h = torch.empty(N, D, dtype=torch.float32, device="cuda")
+    dit.dit_modnorm(norm, 1e-6, torch.from_numpy(x).cuda(), torch.from_numpy(mod).cuda(), 0, torch.from_numpy(ci).cuda(), h)
+    assert_f32_close(from_dev(h), ref, rel=2.0 ** -23, abs_=1e-12, what="modnorm f64 residual")

@@ -563,7 +563,8 @@ static WsPlan plan_ws(const dit_model* m, const dit_batch* b) {
     return o;
   };
   p.mod = take(sizeof(float) * c.n_blocks * b->n_cond * 6 * D);
-  p.x = take(c.io ? sizeof(float) * N * D : 0);
+  // residual stream: float32 (bf16 stream, with io) or float64 (fp32 stream)
+  p.x = take(c.stream_dtype == DIT_BF16 ? (c.io ? sizeof(float) * N * D : 0) : sizeof(double) * N * D);
   p.h = take(es * N * D);
   p.big = take(es * N * (3 * D > 2 * F ? 3 * D : 2 * F));
   p.qkvh = take(es * N * (3 * D > F ? 3 * D : F));
@@ -621,7 +622,8 @@ static hipError_t launch_gemm(const dit_config& c, int M, int N, int K, const vo
   return gemm_f32(M, N, K, static_cast<const float*>(A), static_cast<const float*>(W), bias, static_cast<float*>(C), ws, s);
 }
 
-static int run_block(dit_model* m, int blk, float* x, const float* mod, const dit_batch* b, char* ws,
+// x: the residual stream, float32 for a bf16 stream, float64 for an fp32 one.
+static int run_block(dit_model* m, int blk, void* x, const float* mod, const dit_batch* b, char* ws,
                      const WsPlan& p, hipStream_t s) {
   const dit_config& c = m->cfg;
   const BlockPtrs& w = m->blocks[blk];
@@ -638,7 +640,8 @@ static int run_block(dit_model* m, int blk, float* x, const float* mod, const di
   void* k = qkvh + es * N * D;
   void* v = qkvh + 2 * es * N * D;
   // attention sub-layer
-  DIT_HIP(modnorm(bf, c.norm, c.norm_eps, N, D, x, mod, 0, b->cond_dev, h, s));
+  const bool x64 = !bf;
+  DIT_HIP(modnorm(bf, c.norm, c.norm_eps, N, D, x64, x, mod, 0, b->cond_dev, h, s));
   DIT_HIP(launch_gemm(c, N, 3 * D, D, h, w.qkv_w, w.qkv_b, big, false, gws, s));
   DIT_HIP(rope_split(bf, N, H, hd, c.rot_dim, big, b->cos_dev, b->sin_dev, q, k, v, s));
   if (bf)
@@ -648,13 +651,13 @@ static int run_block(dit_model* m, int blk, float* x, const float* mod, const di
     DIT_HIP(attention_f32(N, H, hd, b->n_segs, b->cu_dev, b->max_seqlen, static_cast<const float*>(q),
                           static_cast<const float*>(k), static_cast<const float*>(v), static_cast<float*>(o), s));
   DIT_HIP(launch_gemm(c, N, D, D, o, w.out_w, w.out_b, a, true, gws, s));
-  DIT_HIP(gated_residual(N, D, x, a, mod, 0, b->cond_dev, s));
+  DIT_HIP(gated_residual(N, D, x64, x, a, mod, 0, b->cond_dev, s));
   // MLP sub-layer
-  DIT_HIP(modnorm(bf, c.norm, c.norm_eps, N, D, x, mod, 1, b->cond_dev, h, s));
+  DIT_HIP(modnorm(bf, c.norm, c.norm_eps, N, D, x64, x, mod, 1, b->cond_dev, h, s));
   DIT_HIP(launch_gemm(c, N, 2 * F, D, h, w.in_w, w.in_b, big, false, gws, s));
   DIT_HIP(silu_gate(bf, N, F, big, qkvh, s));
   DIT_HIP(launch_gemm(c, N, D, F, qkvh, w.mo_w, w.mo_b, a, true, gws, s));
-  DIT_HIP(gated_residual(N, D, x, a, mod, 1, b->cond_dev, s));
+  DIT_HIP(gated_residual(N, D, x64, x, a, mod, 1, b->cond_dev, s));
   return DIT_OK;
 }
 
@@ -689,7 +692,15 @@ extern "C" int dit_block_forward(dit_model* m, int block, float* x_dev, const fl
   DIT_TRY(check_run(m, b, ws_dev, ws_bytes, &p));
   if (block < 0 || block >= m->cfg.n_blocks) return set_error(DIT_E_INVALID, "dit_block_forward: block %d", block);
   if (x_dev == nullptr || mod_dev == nullptr) return set_error(DIT_E_INVALID, "dit_block_forward: x or mod is null");
-  return run_block(m, block, x_dev, mod_dev, b, static_cast<char*>(ws_dev), p, reinterpret_cast<hipStream_t>(stream));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(ws_dev);
+  if (m->cfg.stream_dtype == DIT_BF16) return run_block(m, block, x_dev, mod_dev, b, ws, p, s);
+  const int64_t n = static_cast<int64_t>(b->N) * m->cfg.hidden;
+  double* x64 = reinterpret_cast<double*>(ws + p.x);
+  DIT_HIP(widen_f32(n, x_dev, x64, s));
+  DIT_TRY(run_block(m, block, x64, mod_dev, b, ws, p, s));
+  DIT_HIP(narrow_f64(n, x64, x_dev, s));
+  return DIT_OK;
 }
 
 static int run_forward(dit_model* m, const dit_batch* b, const float* in, const float* cond, float* out, char* ws,
@@ -698,9 +709,14 @@ static int run_forward(dit_model* m, const dit_batch* b, const float* in, const 
   const int N = b->N, D = c.hidden;
   float* mod = reinterpret_cast<float*>(ws + p.mod);
   DIT_TRY(run_modulation(m, b, 0, c.n_blocks, cond, mod, s));
-  float* x;
+  // The residual stream: float32 for a bf16 stream, float64 for an fp32 one
+  // (entered by exact widening, left rounded once).
+  const bool x64 = c.stream_dtype != DIT_BF16;
+  const int64_t nd = static_cast<int64_t>(N) * D;
+  void* x;
   if (c.io) {
-    x = reinterpret_cast<float*>(ws + p.x);
+    x = ws + p.x;
+    float* xin = x64 ? reinterpret_cast<float*>(ws + p.a) : static_cast<float*>(x);  // in-projection output
     float* tok = reinterpret_cast<float*>(ws + p.tok);
     for (int i = 0; i < b->n_segs; ++i) {
       const dit_segment& sg = b->segs[i];
@@ -708,9 +724,13 @@ static int run_forward(dit_model* m, const dit_batch* b, const float* in, const 
       const int n = b->cu[i + 1] - b->cu[i];
       const int cw = token_width(md);
       DIT_HIP(patch_in(md.io, md.channels, md.patch, sg.grid, in + b->lat_off[i], tok, s));
-      DIT_HIP(gemm_f32(n, D, cw, tok, m->in_w[sg.modality], m->in_b[sg.modality], x + static_cast<size_t>(b->cu[i]) * D,
+      DIT_HIP(gemm_f32(n, D, cw, tok, m->in_w[sg.modality], m->in_b[sg.modality], xin + static_cast<size_t>(b->cu[i]) * D,
                        ws + p.gemm, s));
     }
+    if (x64) DIT_HIP(widen_f32(nd, xin, static_cast<double*>(x), s));
+  } else if (x64) {
+    x = ws + p.x;
+    DIT_HIP(widen_f32(nd, in, static_cast<double*>(x), s));
   } else {
     x = out;
     if (in != out) DIT_HIP(hipMemcpyAsync(out, in, sizeof(float) * N * D, hipMemcpyDeviceToDevice, s));
@@ -719,9 +739,12 @@ static int run_forward(dit_model* m, const dit_batch* b, const float* in, const 
     const float* mb = mod + static_cast<size_t>(blk) * b->n_cond * 6 * D;
     DIT_TRY(run_block(m, blk, x, mb, b, ws, p, s));
   }
-  if (!c.io) return DIT_OK;
+  if (!c.io) {
+    if (x64) DIT_HIP(narrow_f64(nd, static_cast<const double*>(x), out, s));
+    return DIT_OK;
+  }
   float* y = reinterpret_cast<float*>(ws + p.a);  // final norm, fp32
-  DIT_HIP(modnorm(false, c.norm, c.norm_eps, N, D, x, nullptr, 0, nullptr, y, s));
+  DIT_HIP(modnorm(false, c.norm, c.norm_eps, N, D, x64, x, nullptr, 0, nullptr, y, s));
   float* vtok = reinterpret_cast<float*>(ws + p.vtok);
   for (int i = 0; i < b->n_segs; ++i) {
     const dit_segment& sg = b->segs[i];
@@ -813,14 +836,17 @@ extern "C" int dit_gemm(int dtype, int M, int N, int K, const void* A, const voi
   return DIT_OK;
 }
 
-extern "C" int dit_modnorm(int dtype, int norm, float eps, int N, int D, const float* x, const float* mod, int which,
-                           const int32_t* cond_idx, void* h, dit_stream_t stream) {
+extern "C" int dit_modnorm(int dtype, int norm, float eps, int N, int D, const void* x, int x_dtype, const float* mod,
+                           int which, const int32_t* cond_idx, void* h, dit_stream_t stream) {
   if (N < 0 || !modnorm_supported(D)) return set_error(DIT_E_INVALID, "dit_modnorm: N=%d D=%d", N, D);
   if (norm != DIT_NORM_RMS && norm != DIT_NORM_LAYER) return set_error(DIT_E_INVALID, "dit_modnorm: norm");
   if (which != 0 && which != 1) return set_error(DIT_E_INVALID, "dit_modnorm: which");
   if (mod != nullptr && cond_idx == nullptr) return set_error(DIT_E_INVALID, "dit_modnorm: cond_idx is null");
   if (dtype != DIT_F32 && dtype != DIT_BF16) return set_error(DIT_E_INVALID, "dit_modnorm: dtype");
-  DIT_HIP(modnorm(dtype == DIT_BF16, norm, eps, N, D, x, mod, which, cond_idx, h, reinterpret_cast<hipStream_t>(stream)));
+  if (x_dtype != DIT_F32 && !(x_dtype == DIT_F64 && dtype == DIT_F32))
+    return set_error(DIT_E_INVALID, "dit_modnorm: x_dtype %d with output dtype %d", x_dtype, dtype);
+  DIT_HIP(modnorm(dtype == DIT_BF16, norm, eps, N, D, x_dtype == DIT_F64, x, mod, which, cond_idx, h,
+                  reinterpret_cast<hipStream_t>(stream)));
   return DIT_OK;
 }
 
@@ -854,10 +880,11 @@ extern "C" int dit_silu_gate(int dtype, int N, int F, const void* u, void* m, di
   return DIT_OK;
 }
 
-extern "C" int dit_gated_residual(int N, int D, float* x, const float* a, const float* mod, int which,
+extern "C" int dit_gated_residual(int N, int D, void* x, int x_dtype, const float* a, const float* mod, int which,
                                   const int32_t* cond_idx, dit_stream_t stream) {
   if (N < 0 || D <= 0 || D % 4 || (which != 0 && which != 1)) return set_error(DIT_E_INVALID, "dit_gated_residual: shape");
-  DIT_HIP(gated_residual(N, D, x, a, mod, which, cond_idx, reinterpret_cast<hipStream_t>(stream)));
+  if (x_dtype != DIT_F32 && x_dtype != DIT_F64) return set_error(DIT_E_INVALID, "dit_gated_residual: x_dtype %d", x_dtype);
+  DIT_HIP(gated_residual(N, D, x_dtype == DIT_F64, x, a, mod, which, cond_idx, reinterpret_cast<hipStream_t>(stream)));
   return DIT_OK;
 }
 

@@ -29,7 +29,8 @@ template <> struct store4<bf16_t> {
 
 // fp32 output (an fp32 stream or the final norm): the row sums run in fp64,
 // so the normalised row is the fp32 rounding of its exact value in practice.
-// bf16 output: fp32 sums (the bf16 rounding dominates).
+// bf16 output: fp32 sums (the bf16 rounding dominates).  The residual x is
+// float32 (bf16 stream) or float64 (fp32 stream).
 template <typename TO> struct norm_acc { typedef float T; };
 template <> struct norm_acc<float> { typedef double T; };
 
@@ -51,9 +52,26 @@ __device__ __forceinline__ A row_sum(A v, A* red, int wrow, int wsub, int lane) 
   return t;
 }
 
-template <typename TO, int TPR, int NCH>
+// Four consecutive residual values as the accumulation type.
+template <typename TX> struct load4;
+template <> struct load4<float> {
+  template <typename A>
+  static __device__ __forceinline__ void ld(const float* p, A* v) {
+    const float4 t = *reinterpret_cast<const float4*>(p);
+    v[0] = A(t.x); v[1] = A(t.y); v[2] = A(t.z); v[3] = A(t.w);
+  }
+};
+template <> struct load4<double> {
+  template <typename A>
+  static __device__ __forceinline__ void ld(const double* p, A* v) {
+    const double2 t0 = reinterpret_cast<const double2*>(p)[0], t1 = reinterpret_cast<const double2*>(p)[1];
+    v[0] = A(t0.x); v[1] = A(t0.y); v[2] = A(t1.x); v[3] = A(t1.y);
+  }
+};
+
+template <typename TX, typename TO, int TPR, int NCH>
 __global__ __launch_bounds__(256) void modnorm_kernel(int N, int D, int norm, float eps,
-                                                     const float* __restrict__ x,
+                                                     const TX* __restrict__ x,
                                                      const float* __restrict__ mod, int shift_k,
                                                      int scale_k, const int32_t* __restrict__ cond_idx,
                                                      TO* __restrict__ h) {
@@ -68,17 +86,17 @@ __global__ __launch_bounds__(256) void modnorm_kernel(int N, int D, int norm, fl
   const bool live = row_raw < N;
   const int row = live ? row_raw : N - 1;         // dead rows keep every barrier reachable
   const int D4 = D >> 2;
-  const float4* xr = reinterpret_cast<const float4*>(x + static_cast<size_t>(row) * D);
-  float4 v[NCH];
+  const TX* xr = x + static_cast<size_t>(row) * D;
+  A v[NCH][4];
   A s = 0;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int c = t + TPR * i;
     if (c < D4) {
-      v[i] = xr[c];
-      s += (A(v[i].x) + A(v[i].y)) + (A(v[i].z) + A(v[i].w));
+      load4<TX>::ld(xr + 4 * c, v[i]);
+      s += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
     } else {
-      v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      v[i][0] = v[i][1] = v[i][2] = v[i][3] = A(0);
     }
   }
   const A inv_d = A(1) / A(D);
@@ -89,7 +107,7 @@ __global__ __launch_bounds__(256) void modnorm_kernel(int N, int D, int norm, fl
   for (int i = 0; i < NCH; ++i) {
     const int c = t + TPR * i;
     if (c < D4) {
-      const A a = A(v[i].x) - mean, b = A(v[i].y) - mean, cc = A(v[i].z) - mean, d = A(v[i].w) - mean;
+      const A a = v[i][0] - mean, b = v[i][1] - mean, cc = v[i][2] - mean, d = v[i][3] - mean;
       ss += (a * a + b * b) + (cc * cc + d * d);
     }
   }
@@ -108,8 +126,8 @@ __global__ __launch_bounds__(256) void modnorm_kernel(int N, int D, int norm, fl
   for (int i = 0; i < NCH; ++i) {
     const int c = t + TPR * i;
     if (c < D4) {
-      A y0 = (A(v[i].x) - mean) * rstd, y1 = (A(v[i].y) - mean) * rstd;
-      A y2 = (A(v[i].z) - mean) * rstd, y3 = (A(v[i].w) - mean) * rstd;
+      A y0 = (v[i][0] - mean) * rstd, y1 = (v[i][1] - mean) * rstd;
+      A y2 = (v[i][2] - mean) * rstd, y3 = (v[i][3] - mean) * rstd;
       if (mod != nullptr) {
         const float4 a = sc[c], b = sh[c];
         y0 = y0 * (A(1) + A(a.x)) + A(b.x);
@@ -124,14 +142,14 @@ __global__ __launch_bounds__(256) void modnorm_kernel(int N, int D, int norm, fl
 
 bool modnorm_supported(int D) { return D > 0 && D % 4 == 0 && D <= 8192; }
 
-template <typename TO>
-static hipError_t modnorm_t(int norm, float eps, int N, int D, const float* x, const float* mod,
+template <typename TX, typename TO>
+static hipError_t modnorm_t(int norm, float eps, int N, int D, const TX* x, const float* mod,
                             int which, const int32_t* ci, TO* h, hipStream_t s) {
   const int d4 = D / 4;
   const int shift_k = which == 0 ? 0 : 3, scale_k = which == 0 ? 1 : 4;
 #define DIT_MN(TPR, K)                                                                                \
   if ((d4 + TPR - 1) / TPR <= K) {                                                                   \
-    hipLaunchKernelGGL((modnorm_kernel<TO, TPR, K>), dim3((N + 256 / TPR - 1) / (256 / TPR)), dim3(256), \
+    hipLaunchKernelGGL((modnorm_kernel<TX, TO, TPR, K>), dim3((N + 256 / TPR - 1) / (256 / TPR)), dim3(256), \
                        0, s, N, D, norm, eps, x, mod, shift_k, scale_k, ci, h);                      \
     return hipGetLastError();                                                                         \
   }
@@ -146,13 +164,20 @@ static hipError_t modnorm_t(int norm, float eps, int N, int D, const float* x, c
   return hipErrorInvalidValue;
 }
 
-hipError_t modnorm(bool bf16_out, int norm, float eps, int N, int D, const float* x,
+hipError_t modnorm(bool bf16_out, int norm, float eps, int N, int D, bool x_f64, const void* x,
                    const float* mod, int which, const int32_t* cond_idx, void* h, hipStream_t s) {
   if (N == 0) return hipSuccess;
   LaunchScope scope_(kCntModnorm, s);
+  if (x_f64) {
+    if (bf16_out) return hipErrorInvalidValue;  // an fp64 residual belongs to the fp32 stream
+    return modnorm_t<double, float>(norm, eps, N, D, static_cast<const double*>(x), mod, which, cond_idx,
+                                    static_cast<float*>(h), s);
+  }
   if (bf16_out)
-    return modnorm_t<bf16_t>(norm, eps, N, D, x, mod, which, cond_idx, static_cast<bf16_t*>(h), s);
-  return modnorm_t<float>(norm, eps, N, D, x, mod, which, cond_idx, static_cast<float*>(h), s);
+    return modnorm_t<float, bf16_t>(norm, eps, N, D, static_cast<const float*>(x), mod, which, cond_idx,
+                                    static_cast<bf16_t*>(h), s);
+  return modnorm_t<float, float>(norm, eps, N, D, static_cast<const float*>(x), mod, which, cond_idx,
+                                 static_cast<float*>(h), s);
 }
 
 // ============================================================================ RoPE + QKV split
@@ -198,10 +223,12 @@ __global__ __launch_bounds__(256) void rope_split_kernel(int N, int H, int hd, i
       float x1[V], x2[V], o1[V], o2[V];
       vec16<T>::load(s + i0, x1);
       vec16<T>::load(s + i1, x2);
+      // products of floats are exact in fp64: each output is one rounding of
+      // its exact value (fp32 stream); the bf16 rounding dominates otherwise
 #pragma unroll
       for (int e = 0; e < V; ++e) {
-        o1[e] = x1[e] * c[e] - x2[e] * sn[e];
-        o2[e] = x2[e] * c[e] + x1[e] * sn[e];
+        o1[e] = static_cast<float>(double(x1[e]) * double(c[e]) - double(x2[e]) * double(sn[e]));
+        o2[e] = static_cast<float>(double(x2[e]) * double(c[e]) + double(x1[e]) * double(sn[e]));
       }
       vec16<T>::store(d + i0, o1);
       vec16<T>::store(d + i1, o2);
@@ -266,8 +293,16 @@ __global__ __launch_bounds__(256) void silu_gate_kernel(int N, int F, const T* _
   float g[V], up[V], o[V];
   vec16<T>::load(ur + j, g);
   vec16<T>::load(ur + F + j, up);
+  // fp32 stream: evaluated in fp64 and rounded once; bf16: fp32 arithmetic
 #pragma unroll
-  for (int e = 0; e < V; ++e) o[e] = g[e] / (1.0f + expf(-g[e])) * up[e];
+  for (int e = 0; e < V; ++e) {
+    if (sizeof(T) == 4) {
+      const double gd = g[e];
+      o[e] = static_cast<float>(gd / (1.0 + exp(-gd)) * double(up[e]));
+    } else {
+      o[e] = g[e] / (1.0f + expf(-g[e])) * up[e];
+    }
+  }
   vec16<T>::store(m + static_cast<size_t>(n) * F + j, o);
 }
 
@@ -290,8 +325,11 @@ hipError_t silu_gate(bool bf16, int N, int F, const void* u, void* m, hipStream_
 // ============================================================================ gated residual
 // x[n, j] += gate[cond_idx[n]][j] * a[n, j] (page "port the MiniMax-H3
 // omni-modal video+audio DiT", section "The device-resident forward (W2b)":
-// Add with an indexed AdaLN gate).
-__global__ __launch_bounds__(256) void gated_residual_kernel(int N, int D, float* __restrict__ x,
+// Add with an indexed AdaLN gate).  x is float32 (bf16 stream: one fused
+// multiply-add) or float64 (fp32 stream: the product of two floats is exact in
+// fp64, so the update is one fp64 rounding).
+template <typename TX>
+__global__ __launch_bounds__(256) void gated_residual_kernel(int N, int D, TX* __restrict__ x,
                                                             const float* __restrict__ a,
                                                             const float* __restrict__ mod, int gate_k,
                                                             const int32_t* __restrict__ cond_idx) {
@@ -303,22 +341,50 @@ __global__ __launch_bounds__(256) void gated_residual_kernel(int N, int D, float
   const float4 g = reinterpret_cast<const float4*>(
       mod + (static_cast<size_t>(cond_idx[n]) * 6 + gate_k) * D)[c];
   const float4 av = reinterpret_cast<const float4*>(a)[t];
-  float4 xv = reinterpret_cast<float4*>(x)[t];
-  xv.x += g.x * av.x;
-  xv.y += g.y * av.y;
-  xv.z += g.z * av.z;
-  xv.w += g.w * av.w;
-  reinterpret_cast<float4*>(x)[t] = xv;
+  TX* xp = x + 4 * t;
+  xp[0] += TX(g.x) * TX(av.x);
+  xp[1] += TX(g.y) * TX(av.y);
+  xp[2] += TX(g.z) * TX(av.z);
+  xp[3] += TX(g.w) * TX(av.w);
 }
 
-hipError_t gated_residual(int N, int D, float* x, const float* a, const float* mod, int which,
+hipError_t gated_residual(int N, int D, bool x_f64, void* x, const float* a, const float* mod, int which,
                           const int32_t* cond_idx, hipStream_t s) {
   if (N == 0) return hipSuccess;
   LaunchScope scope_(kCntGatedResidual, s);
   const int64_t total = static_cast<int64_t>(N) * (D / 4);
   dim3 grid(static_cast<unsigned>((total + 255) / 256)), block(256);
-  hipLaunchKernelGGL(gated_residual_kernel, grid, block, 0, s, N, D, x, a, mod, which == 0 ? 2 : 5,
-                     cond_idx);
+  if (x_f64)
+    hipLaunchKernelGGL(gated_residual_kernel<double>, grid, block, 0, s, N, D, static_cast<double*>(x), a, mod,
+                       which == 0 ? 2 : 5, cond_idx);
+  else
+    hipLaunchKernelGGL(gated_residual_kernel<float>, grid, block, 0, s, N, D, static_cast<float*>(x), a, mod,
+                       which == 0 ? 2 : 5, cond_idx);
+  return hipGetLastError();
+}
+
+// ============================================================================ residual widen / narrow
+// The fp32 stream carries its residual in float64: tokens enter by exact
+// widening and leave rounded to nearest float32.
+__global__ __launch_bounds__(256) void widen_kernel(int64_t n, const float* __restrict__ src, double* __restrict__ dst) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t < n) dst[t] = static_cast<double>(src[t]);
+}
+__global__ __launch_bounds__(256) void narrow_kernel(int64_t n, const double* __restrict__ src, float* __restrict__ dst) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t < n) dst[t] = static_cast<float>(src[t]);
+}
+
+hipError_t widen_f32(int64_t n, const float* src, double* dst, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  LaunchScope scope_(kCntConvert, s);
+  hipLaunchKernelGGL(widen_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, n, src, dst);
+  return hipGetLastError();
+}
+hipError_t narrow_f64(int64_t n, const double* src, float* dst, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  LaunchScope scope_(kCntConvert, s);
+  hipLaunchKernelGGL(narrow_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, n, src, dst);
   return hipGetLastError();
 }
 

@@ -4,16 +4,18 @@
 // onto the device, staged once", section "What moved, and onto what".
 //
 // bf16: v_mfma_f32_32x32x16_bf16, fp32 accumulation, 256x256x64 workgroup
-//   tiles, four wavefronts of 128x128; A/B tiles stream HBM -> LDS by direct
+//   tiles, eight wavefronts of 128x64; A/B tiles stream HBM -> LDS by direct
 //   buffer loads (double-buffered, 128 KB) into an XOR-swizzled layout so the
 //   MFMA operand reads are bank-conflict free, and the next k-step's operands
 //   are read while the current MFMAs run.
 // f32: exact products and fp64 sums on v_mfma_f64_16x16x4_f64 (fp32 operands
 //   widened on the way in), 64x64x16 tiles and a deterministic split-K whose
 //   partition depends only on (N, K): each partial is reduced in a fixed order
-//   and rounded to fp32 once.  fp32 accumulation over K = 2560..10240 breaks
-//   the fp32 parity bound of rel 1e-5 / abs 1e-6 on ~9% of the music model's
-//   outputs, so the f32 path accumulates in fp64.
+//   and rounded to fp32 once.  The fp32 parity bound (rel 1e-5 / abs 1e-6)
+//   after the music model's 24 blocks leaves room for about one rounding per
+//   stored value: fp32 accumulation, and even six-term bf16 splitting of the
+//   operands with fp64 sums of each MFMA (whose 16-product sums truncate),
+//   break it; correctly rounded GEMMs keep it.
 //
 // In both, the value of C[i][j] depends only on row i of A, row j of B and K --
 // never on M or on where row i sits in a tile -- so a document computed alone
@@ -230,27 +232,59 @@ hipError_t gemm_bf16(int M, int N, int K, const uint16_t* A, const uint16_t* B, 
 }
 
 // ============================================================================ f32 GEMM, fp64 accumulation
+// Exact products (fp32 operands widened to fp64) and fp64 sums on
+// v_mfma_f64_16x16x4_f64, one rounding to fp32 at the end: the result is the
+// correctly rounded value of the dot product except at fp64 near-ties.
+// Within a 16-wide K chunk the MFMAs run k-step-outer, so consecutive MFMAs of
+// a wavefront write different accumulators.  Split-K partials are fp64,
+// reduced in a fixed order.
+// Tile shape: 2 x 2 wavefronts of 32 x 32 (2 x 2 MFMA tiles), 64 x 64 x 16
+// workgroup tiles, ~1024 workgroups per GEMM.  Measured on the music model's
+// shapes, 48x64 and 48x32 wavefront tiles with 96- and 192-row workgroups, and
+// 512..2048 workgroups, all land within 10%: v_mfma_f64_16x16x4_f64 alone
+// sustains ~43 TFLOP/s on gfx950 (55% of the 78.6 TFLOP/s the datasheet
+// gives), and this kernel runs at 42-44 on the large shapes.
+#ifndef DIT_GF_WAVES_M
+#define DIT_GF_WAVES_M 2
+#endif
+#ifndef DIT_GF_WAVES_N
+#define DIT_GF_WAVES_N 2
+#endif
+#ifndef DIT_GF_TI
+#define DIT_GF_TI 2
+#endif
+#ifndef DIT_GF_TJ
+#define DIT_GF_TJ 2
+#endif
+#ifndef DIT_GF_TARGET
+#define DIT_GF_TARGET 1024
+#endif
 namespace gf {
-constexpr int BM = 64, BN = 64, BK = 16, PAD = 20;  // LDS rows padded to 20 floats
-constexpr int NT = 256;
+constexpr int TI = DIT_GF_TI, TJ = DIT_GF_TJ;          // 16x16 MFMA tiles per wave
+constexpr int WM = 16 * TI, WN = 16 * TJ;              // per-wave tile
+constexpr int BM = DIT_GF_WAVES_M * WM, BN = DIT_GF_WAVES_N * WN, BK = 16;
+constexpr int PAD = 20;                                // LDS rows padded to 20 floats: conflict-free float4 reads
+constexpr int NT = 64 * DIT_GF_WAVES_M * DIT_GF_WAVES_N;
+constexpr int A_LD = (BM * 4 + NT - 1) / NT, B_LD = (BN * 4 + NT - 1) / NT;  // float4 loads per thread
 }  // namespace gf
 
-// Split count from (N, K) only, so a row's result never depends on M.
+// Split count from (N, K) only, so a row's result never depends on M: about
+// DIT_GF_TARGET workgroups when the rows fit one tile, each split >= 256 of K.
 static int gf_splits(int N, int K) {
   const int tiles_n = (N + gf::BN - 1) / gf::BN;
   const int chunks = (K + gf::BK - 1) / gf::BK;
-  int s = (1536 + tiles_n - 1) / tiles_n;
+  int s = (DIT_GF_TARGET + tiles_n - 1) / tiles_n;
   int cap = chunks / 16;
   if (cap < 1) cap = 1;
   if (s > cap) s = cap;
-  if (s < 1) s = 1;
-  return s;
+  if (s > 64) s = 64;
+  return s < 1 ? 1 : s;
 }
 
 // MFMA 16x16x4 f64: lane l supplies A[l%16][k = l/16] and B[k = l/16][l%16];
 // the result lane l holds D[4*i + l/16][l%16], i = 0..3.  Over four
-// consecutive MFMAs, lane group g = l/16 feeds k = 4g + j (j = MFMA index), so
-// each lane reads one float4 per row per 16-wide K chunk.
+// consecutive k-steps, lane group g = l/16 feeds k = 4g + j (j = step), so each
+// lane reads one float4 per row per 16-wide K chunk.
 __global__ __launch_bounds__(gf::NT) void gemm_f32_kernel(int M, int N, int K,
                                                          const float* __restrict__ A,
                                                          const float* __restrict__ B,
@@ -266,82 +300,94 @@ __global__ __launch_bounds__(gf::NT) void gemm_f32_kernel(int M, int N, int K,
   const int m0 = tm * BM, n0 = tn * BN;
   const int chunks = (K + BK - 1) / BK;
   const int c_begin = sp * chunks_per_split;
-  int c_end = c_begin + chunks_per_split;
-  if (c_end > chunks) c_end = chunks;
+  const int c_end = c_begin + chunks_per_split < chunks ? c_begin + chunks_per_split : chunks;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wr = (wave >> 1) * 32, wc = (wave & 1) * 32;
-  const int lrow = tid >> 2, lcol = (tid & 3) * 4;  // loader: one float4 of A and of B
+  const int wr = (wave / DIT_GF_WAVES_N) * WM, wc = (wave % DIT_GF_WAVES_N) * WN;
 
-  f64x4_t acc[2][2];
+  f64x4_t acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+    for (int j = 0; j < TJ; ++j) acc[i][j] = f64x4_t{0.0, 0.0, 0.0, 0.0};
 
-  float4 ra, rb;
-#define GF_GLOAD(ch)                                                                                    \
-  {                                                                                                     \
-    const int k = (ch) * BK + lcol;                                                                     \
-    const int gm = m0 + lrow, gn = n0 + lrow;                                                           \
-    ra = (gm < M && k < K) ? *reinterpret_cast<const float4*>(A + static_cast<size_t>(gm) * K + k)  \
-                           : make_float4(0.f, 0.f, 0.f, 0.f);                                       \
-    rb = (gn < N && k < K) ? *reinterpret_cast<const float4*>(B + static_cast<size_t>(gn) * K + k)  \
-                           : make_float4(0.f, 0.f, 0.f, 0.f);                                       \
-  }
-#define GF_SSTORE(st)                                          \
-  {                                                            \
-    *reinterpret_cast<float4*>(&As[st][lrow][lcol]) = ra;      \
-    *reinterpret_cast<float4*>(&Bs[st][lrow][lcol]) = rb;      \
-  }
+  // Loader: float4 q of this thread is row (tid + NT q) / 4, k 4 ((tid + NT q) % 4).
+  float4 ra[A_LD], rb[B_LD];
+  auto gload = [&](int ch) {
+#pragma unroll
+    for (int q = 0; q < A_LD; ++q) {
+      const int id = tid + NT * q, r = id >> 2, k = ch * BK + 4 * (id & 3);
+      const int gm = m0 + r;
+      ra[q] = (r < BM && gm < M && k < K) ? *reinterpret_cast<const float4*>(A + static_cast<size_t>(gm) * K + k)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int q = 0; q < B_LD; ++q) {
+      const int id = tid + NT * q, r = id >> 2, k = ch * BK + 4 * (id & 3);
+      const int gn = n0 + r;
+      rb[q] = (r < BN && gn < N && k < K) ? *reinterpret_cast<const float4*>(B + static_cast<size_t>(gn) * K + k)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto sstore = [&](int st) {
+#pragma unroll
+    for (int q = 0; q < A_LD; ++q) {
+      const int id = tid + NT * q;
+      if ((id >> 2) < BM) *reinterpret_cast<float4*>(&As[st][id >> 2][4 * (id & 3)]) = ra[q];
+    }
+#pragma unroll
+    for (int q = 0; q < B_LD; ++q) {
+      const int id = tid + NT * q;
+      if ((id >> 2) < BN) *reinterpret_cast<float4*>(&Bs[st][id >> 2][4 * (id & 3)]) = rb[q];
+    }
+  };
 
   if (c_begin < c_end) {
-    GF_GLOAD(c_begin)
-    GF_SSTORE(0)
+    gload(c_begin);
+    sstore(0);
   }
   __syncthreads();
   const int r16 = lane & 15, g = lane >> 4;
   for (int ch = c_begin; ch < c_end; ++ch) {
     const int st = (ch - c_begin) & 1;
-    if (ch + 1 < c_end) GF_GLOAD(ch + 1)
-    float4 fa[2], fb[2];
+    if (ch + 1 < c_end) gload(ch + 1);
+    float4 fa[TI], fb[TJ];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) fa[i] = *reinterpret_cast<const float4*>(&As[st][wr + i * 16 + r16][4 * g]);
+    for (int i = 0; i < TI; ++i) fa[i] = *reinterpret_cast<const float4*>(&As[st][wr + i * 16 + r16][4 * g]);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) fb[j] = *reinterpret_cast<const float4*>(&Bs[st][wc + j * 16 + r16][4 * g]);
+    for (int j = 0; j < TJ; ++j) fb[j] = *reinterpret_cast<const float4*>(&Bs[st][wc + j * 16 + r16][4 * g]);
+    const float* fa_ = reinterpret_cast<const float*>(fa);
+    const float* fb_ = reinterpret_cast<const float*>(fb);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)fa[i].x, (double)fb[j].x, acc[i][j], 0, 0, 0);
-        acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)fa[i].y, (double)fb[j].y, acc[i][j], 0, 0, 0);
-        acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)fa[i].z, (double)fb[j].z, acc[i][j], 0, 0, 0);
-        acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)fa[i].w, (double)fb[j].w, acc[i][j], 0, 0, 0);
+      for (int i = 0; i < TI; ++i) {
+        const double av = static_cast<double>(fa_[4 * i + kk]);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, static_cast<double>(fb_[4 * j + kk]), acc[i][j], 0, 0, 0);
       }
-    if (ch + 1 < c_end) GF_SSTORE(st ^ 1)
+    if (ch + 1 < c_end) sstore(st ^ 1);
     __syncthreads();
   }
-#undef GF_GLOAD
-#undef GF_SSTORE
 
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < TJ; ++j) {
+    const int gn = n0 + wc + j * 16 + r16;
+    if (gn >= N) continue;
+    const double bv = (splits == 1 && bias != nullptr) ? static_cast<double>(bias[gn]) : 0.0;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int gn = n0 + wc + j * 16 + r16;
-      if (gn >= N) continue;
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int gm = m0 + wr + i * 16 + 4 * e + g;
         if (gm >= M) continue;
-        if (splits == 1) {
-          const double v = acc[i][j][e] + (bias != nullptr ? static_cast<double>(bias[gn]) : 0.0);
-          C[static_cast<size_t>(gm) * N + gn] = static_cast<float>(v);
-        } else {
+        if (splits == 1)
+          C[static_cast<size_t>(gm) * N + gn] = static_cast<float>(acc[i][j][e] + bv);
+        else
           part[(static_cast<size_t>(sp) * M + gm) * N + gn] = acc[i][j][e];
-        }
       }
-    }
+  }
 }
 
 // Fixed-order reduction of the split-K partials, bias added in fp64, one rounding.

@@ -11,7 +11,7 @@ namespace dit {
 enum Counter {
   kCntGemmBf16 = 0, kCntGemmF32, kCntAttnBf16, kCntAttnF32, kCntModnorm, kCntRopeSplit,
   kCntSiluGate, kCntGatedResidual, kCntAdaln, kCntPatchIn, kCntPatchOut, kCntEuler,
-  kCntGemmF32Reduce, kCntNum
+  kCntGemmF32Reduce, kCntConvert, kCntNum
 };
 void count_launch(Counter c);
 
@@ -47,15 +47,18 @@ hipError_t attention_f32(int N, int H, int hd, int n_docs, const int32_t* cu, in
 bool attention_supported(bool bf16, int hd);
 
 // ---- bandwidth-bound kernels
-hipError_t modnorm(bool bf16_out, int norm, float eps, int N, int D, const float* x,
+// x is float32, or float64 when x_f64 (the fp32 stream's residual; output then float32)
+hipError_t modnorm(bool bf16_out, int norm, float eps, int N, int D, bool x_f64, const void* x,
                    const float* mod, int which, const int32_t* cond_idx, void* h, hipStream_t s);
 bool modnorm_supported(int D);
 hipError_t rope_split(bool bf16, int N, int H, int hd, int rot, const void* qkv, const float* cos,
                       const float* sin, void* q, void* k, void* v, hipStream_t s);
 bool rope_split_supported(bool bf16, int hd, int rot);
 hipError_t silu_gate(bool bf16, int N, int F, const void* u, void* m, hipStream_t s);
-hipError_t gated_residual(int N, int D, float* x, const float* a, const float* mod, int which,
+hipError_t gated_residual(int N, int D, bool x_f64, void* x, const float* a, const float* mod, int which,
                           const int32_t* cond_idx, hipStream_t s);
+hipError_t widen_f32(int64_t n, const float* src, double* dst, hipStream_t s);
+hipError_t narrow_f64(int64_t n, const double* src, float* dst, hipStream_t s);
 // mod[b][c][j] = W[b][modality(c)][j] . e[c] + bias[b][modality(c)][j]
 struct AdalnBlockPtrs {
   const void* w[4];      // per modality [6D, d], stream dtype

@@ -24,14 +24,14 @@ LIB_PATH = os.path.join(HERE, "libdit.so")
 DIT_OK = 0
 STATUS = {0: "DIT_OK", 1: "DIT_E_INVALID", 2: "DIT_E_STATE", 3: "DIT_E_UNKNOWN_WEIGHT", 4: "DIT_E_SHAPE",
           5: "DIT_E_DTYPE", 6: "DIT_E_MISSING_WEIGHT", 7: "DIT_E_WORKSPACE", 8: "DIT_E_HIP", 9: "DIT_E_UNSUPPORTED"}
-DIT_F32, DIT_BF16 = 0, 1
+DIT_F32, DIT_BF16, DIT_F64 = 0, 1, 2
 DIT_NORM_RMS, DIT_NORM_LAYER = 0, 1
 DIT_MLP_GATE_UP, DIT_MLP_VALUE_GATE = 0, 1
 DIT_IO_NONE, DIT_IO_PATCH3D, DIT_IO_CHANNEL_MAJOR = 0, 1, 2
 MAX_MOD = 4
 COUNTER_NAMES = ["gemm_bf16", "gemm_f32", "attention_bf16", "attention_f32", "modnorm", "rope_split",
                  "silu_gate", "gated_residual", "adaln", "patch_in", "patch_out", "euler",
-                 "gemm_f32_reduce"]
+                 "gemm_f32_reduce", "convert"]
 
 
 class DitError(RuntimeError):
@@ -93,11 +93,11 @@ _SIGS = {
     "dit_denoise_loop": [_P, _P, _P, _P, _P, _I, _P, _SZ, _P],
     "dit_gemm_workspace_bytes": [_I, _I, _I, _I, ctypes.POINTER(_SZ)],
     "dit_gemm": [_I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _SZ, _P],
-    "dit_modnorm": [_I, _I, ctypes.c_float, _I, _I, _P, _P, _I, _P, _P, _P],
+    "dit_modnorm": [_I, _I, ctypes.c_float, _I, _I, _P, _I, _P, _I, _P, _P, _P],
     "dit_rope_split": [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P],
     "dit_attention": [_I, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P],
     "dit_silu_gate": [_I, _I, _I, _P, _P, _P],
-    "dit_gated_residual": [_I, _I, _P, _P, _P, _I, _P, _P],
+    "dit_gated_residual": [_I, _I, _P, _I, _P, _P, _I, _P, _P],
     "dit_counters": [ctypes.POINTER(ctypes.c_int64), _I],
     "dit_profile_begin": [],
     "dit_profile_end": [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double), _I],
@@ -386,6 +386,8 @@ def dit_denoise_loop(model: Model, batch: Batch, latents, cond_table, dt_table, 
 def _dt(t) -> int:
     if t.dtype in (torch.float32,):
         return DIT_F32
+    if t.dtype == torch.float64:
+        return DIT_F64
     if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
         return DIT_BF16
     raise TypeError(t.dtype)
@@ -406,7 +408,7 @@ def dit_gemm(A, B, bias, C, stream=None):
 
 def dit_modnorm(norm: int, eps: float, x, mod, which: int, cond_idx, h, stream=None):
     N, D = x.shape
-    _check(load().dit_modnorm(_dt(h), norm, eps, N, D, _ptr(x), _ptr(mod), which, _ptr(cond_idx), _ptr(h),
+    _check(load().dit_modnorm(_dt(h), norm, eps, N, D, _ptr(x), _dt(x), _ptr(mod), which, _ptr(cond_idx), _ptr(h),
                               _stream(stream)))
 
 
@@ -429,7 +431,8 @@ def dit_silu_gate(u, m, stream=None):
 
 def dit_gated_residual(x, a, mod, which: int, cond_idx, stream=None):
     N, D = x.shape
-    _check(load().dit_gated_residual(N, D, _ptr(x), _ptr(a), _ptr(mod), which, _ptr(cond_idx), _stream(stream)))
+    _check(load().dit_gated_residual(N, D, _ptr(x), _dt(x), _ptr(a), _ptr(mod), which, _ptr(cond_idx),
+                                     _stream(stream)))
 
 
 def dit_counters() -> Dict[str, int]:
