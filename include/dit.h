@@ -167,7 +167,10 @@ void dit_model_destroy(dit_model* m);
  * stream is rounded to nearest-even on the host through one tensor-sized
  * buffer); biases and the projections in and out stay float32 ("fp32 islands",
  * page "port the MiniMax-H3 omni-modal video+audio DiT", update "quantized arms
- * land").  For DIT_MLP_VALUE_GATE the two row halves of mlp.in are swapped so
+ * land").  The fp32 GEMM weights (an fp32 stream's four block matrices and the
+ * projections) are staged as the five int8 slices plus per-row exponents the
+ * fp32 GEMM consumes (dit_gemm), cut on the host; the AdaLN weights stay as
+ * given.  For DIT_MLP_VALUE_GATE the two row halves of mlp.in are swapped so
  * the kernel computes silu(first) * second (page "the 2.4B fp32 DiT onto the
  * device, staged once", section "What moved").  Copies are synchronous on
  * `stream`.  Errors: DIT_E_UNKNOWN_WEIGHT, DIT_E_SHAPE, DIT_E_DTYPE (named),
@@ -250,9 +253,12 @@ int dit_denoise_loop(dit_model* m, const dit_batch* b, float* latents_dev,
  * timing.  dtype arguments are DIT_F32 or DIT_BF16 (bf16 = uint16 bits). */
 
 /* C[M,N] = A[M,K] . B[N,K]^T + bias[N] (bias may be NULL).  bf16: A, B bf16,
- * fp32 accumulation, C in c_dtype.  f32: A, B float32, products exact and sums
- * in fp64, C float32 (rounded once).  ws is split-K scratch
- * (dit_gemm_workspace_bytes). */
+ * fp32 accumulation, C in c_dtype.  f32: A, B float32 (K a multiple of 4),
+ * each row scaled by a power of two and cut into five 7-bit integer slices,
+ * the slice products summed exactly on the int8 matrix cores (pairs whose
+ * weight is below 2^-32 of the product dropped), combined in fp64 and
+ * rounded once to float32 C.  ws holds B's and A's slices and split-K
+ * partials (dit_gemm_workspace_bytes). */
 int dit_gemm_workspace_bytes(int dtype, int M, int N, int K, size_t* bytes);
 int dit_gemm(int dtype, int M, int N, int K, const void* A, const void* B, const float* bias,
              void* C, int c_dtype, void* ws, size_t ws_bytes, dit_stream_t stream);

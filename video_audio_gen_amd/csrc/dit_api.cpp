@@ -172,6 +172,8 @@ static int token_width(const dit_modality& m) {
 // ============================================================================ model and weight contract
 
 enum SlotKind { kBlockMat = 0, kBias = 1, kIsland = 2 };
+// Slot dtype of an fp32 GEMM weight: stored as its int8 slices (gemm_f32).
+constexpr int kSlicedF32 = 16;
 
 struct Slot {
   std::string name;
@@ -200,9 +202,9 @@ struct dit_model {
   bool finalized;
   dit_stage_stats_t stats;
   std::vector<BlockPtrs> blocks;
-  const float* in_w[DIT_MAX_MODALITIES];
+  const void* in_w[DIT_MAX_MODALITIES];   // int8 slices
   const float* in_b[DIT_MAX_MODALITIES];
-  const float* out_w[DIT_MAX_MODALITIES];
+  const void* out_w[DIT_MAX_MODALITIES];  // int8 slices
   const float* out_b[DIT_MAX_MODALITIES];
 };
 
@@ -222,7 +224,8 @@ static void build_contract(const dit_config& c, std::vector<Slot>* slots, size_t
     s.kind = kind;
     s.swap_halves = swap;
     const int64_t n = ndim == 1 ? s0 : s0 * s1;
-    s.bytes = static_cast<size_t>(n) * (dtype == DIT_BF16 ? 2 : 4);
+    s.bytes = dtype == kSlicedF32 ? gemm_f32_slices_bytes(static_cast<int>(s0), static_cast<int>(s1))
+                                  : static_cast<size_t>(n) * (dtype == DIT_BF16 ? 2 : 4);
     s.offset = off;
     s.staged = false;
     off = align256(off + s.bytes);
@@ -231,26 +234,27 @@ static void build_contract(const dit_config& c, std::vector<Slot>* slots, size_t
   if (c.io) {
     for (int m = 0; m < c.n_mod; ++m) {
       const int64_t cw = token_width(c.mod[m]);
-      add("in." + std::to_string(m) + ".weight", 2, D, cw, DIT_F32, kIsland, false);
+      add("in." + std::to_string(m) + ".weight", 2, D, cw, kSlicedF32, kIsland, false);
       add("in." + std::to_string(m) + ".bias", 1, D, 0, DIT_F32, kBias, false);
-      add("out." + std::to_string(m) + ".weight", 2, cw, D, DIT_F32, kIsland, false);
+      add("out." + std::to_string(m) + ".weight", 2, cw, D, kSlicedF32, kIsland, false);
       add("out." + std::to_string(m) + ".bias", 1, cw, 0, DIT_F32, kBias, false);
     }
   }
   const bool swap = c.mlp == DIT_MLP_VALUE_GATE;
+  const int gd = sd == DIT_BF16 ? DIT_BF16 : kSlicedF32;  // dtype of the GEMM weights
   for (int b = 0; b < c.n_blocks; ++b) {
     const std::string p = "blocks." + std::to_string(b) + ".";
     for (int m = 0; m < c.n_mod; ++m) {
       add(p + "adaln." + std::to_string(m) + ".weight", 2, 6 * D, dt, sd, kBlockMat, false);
       add(p + "adaln." + std::to_string(m) + ".bias", 1, 6 * D, 0, DIT_F32, kBias, false);
     }
-    add(p + "attn.qkv.weight", 2, 3 * D, D, sd, kBlockMat, false);
+    add(p + "attn.qkv.weight", 2, 3 * D, D, gd, kBlockMat, false);
     add(p + "attn.qkv.bias", 1, 3 * D, 0, DIT_F32, kBias, false);
-    add(p + "attn.out.weight", 2, D, D, sd, kBlockMat, false);
+    add(p + "attn.out.weight", 2, D, D, gd, kBlockMat, false);
     add(p + "attn.out.bias", 1, D, 0, DIT_F32, kBias, false);
-    add(p + "mlp.in.weight", 2, 2 * F, D, sd, kBlockMat, swap);
+    add(p + "mlp.in.weight", 2, 2 * F, D, gd, kBlockMat, swap);
     add(p + "mlp.in.bias", 1, 2 * F, 0, DIT_F32, kBias, swap);
-    add(p + "mlp.out.weight", 2, D, F, sd, kBlockMat, false);
+    add(p + "mlp.out.weight", 2, D, F, gd, kBlockMat, false);
     add(p + "mlp.out.bias", 1, D, 0, DIT_F32, kBias, false);
   }
   *total = off;
@@ -300,7 +304,7 @@ extern "C" int dit_stage_weights(dit_model* m, const dit_weight_view* views, int
   if (m == nullptr || (n > 0 && views == nullptr)) return set_error(DIT_E_INVALID, "dit_stage_weights: null argument");
   if (m->finalized) return set_error(DIT_E_STATE, "dit_stage_weights: staging is already finalized");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  std::vector<uint8_t> conv;
+  std::vector<uint8_t> conv, sliced_buf;
   for (int i = 0; i < n; ++i) {
     const dit_weight_view& v = views[i];
     if (v.name == nullptr) return set_error(DIT_E_INVALID, "dit_stage_weights: view %d has no name", i);
@@ -319,9 +323,12 @@ extern "C" int dit_stage_weights(dit_model* m, const dit_weight_view* views, int
     if (v.host == nullptr) return set_error(DIT_E_INVALID, "weight '%s': host pointer is null", v.name);
     const int64_t count = sl.ndim == 1 ? sl.shape[0] : sl.shape[0] * sl.shape[1];
     const void* src = v.host;
+    const bool sliced = sl.dtype == kSlicedF32;
     const bool need_conv = v.dtype != sl.dtype || sl.swap_halves;
     if (need_conv) {
-      conv.resize(sl.bytes);
+      // rows gathered (and widened or rounded) into the slot dtype; a sliced
+      // slot gathers float32 rows first and slices them below
+      conv.resize(sliced ? sizeof(float) * count : sl.bytes);
       const int64_t rows = sl.shape[0];
       const int64_t cols = sl.ndim == 1 ? 1 : sl.shape[1];
       for (int64_t r = 0; r < rows; ++r) {
@@ -329,7 +336,7 @@ extern "C" int dit_stage_weights(dit_model* m, const dit_weight_view* views, int
         const int64_t sr = sl.swap_halves ? (r + rows / 2) % rows : r;
         for (int64_t c = 0; c < cols; ++c) {
           const int64_t di = r * cols + c, si = sr * cols + c;
-          if (sl.dtype == DIT_BF16) {
+          if (sl.dtype == DIT_BF16 && !sliced) {
             uint16_t b;
             if (v.dtype == DIT_BF16) b = static_cast<const uint16_t*>(v.host)[si];
             else b = host_f32_to_bf16(static_cast<const float*>(v.host)[si]);
@@ -347,7 +354,14 @@ extern "C" int dit_stage_weights(dit_model* m, const dit_weight_view* views, int
         }
       }
       src = conv.data();
-      if (static_cast<int64_t>(conv.size()) > m->stats.host_peak) m->stats.host_peak = static_cast<int64_t>(conv.size());
+      if (sliced) {
+        sliced_buf.resize(sl.bytes);
+        host_slice_rows(sl.shape[0], sl.shape[1], (sl.shape[1] + 31) / 32 * 32, reinterpret_cast<const float*>(conv.data()),
+                        reinterpret_cast<int8_t*>(sliced_buf.data()));
+        src = sliced_buf.data();
+      }
+      const int64_t held = static_cast<int64_t>(conv.size() + sliced_buf.size());
+      if (held > m->stats.host_peak) m->stats.host_peak = held;
       m->stats.converted++;
     } else {
       m->stats.direct++;
@@ -360,6 +374,7 @@ extern "C" int dit_stage_weights(dit_model* m, const dit_weight_view* views, int
     m->stats.tensors++;
     m->stats.bytes += static_cast<int64_t>(sl.bytes);
     if (conv.capacity() > 0) std::vector<uint8_t>().swap(conv);  // one tensor's buffer at a time
+    if (sliced_buf.capacity() > 0) std::vector<uint8_t>().swap(sliced_buf);
   }
   return DIT_OK;
 }
@@ -390,9 +405,9 @@ extern "C" int dit_stage_finalize(dit_model* m) {
   }
   for (int mm = 0; mm < DIT_MAX_MODALITIES; ++mm) {
     const bool has = c.io && mm < c.n_mod;
-    m->in_w[mm] = has ? reinterpret_cast<const float*>(ptr("in." + std::to_string(mm) + ".weight")) : nullptr;
+    m->in_w[mm] = has ? ptr("in." + std::to_string(mm) + ".weight") : nullptr;
     m->in_b[mm] = has ? reinterpret_cast<const float*>(ptr("in." + std::to_string(mm) + ".bias")) : nullptr;
-    m->out_w[mm] = has ? reinterpret_cast<const float*>(ptr("out." + std::to_string(mm) + ".weight")) : nullptr;
+    m->out_w[mm] = has ? ptr("out." + std::to_string(mm) + ".weight") : nullptr;
     m->out_b[mm] = has ? reinterpret_cast<const float*>(ptr("out." + std::to_string(mm) + ".bias")) : nullptr;
   }
   m->finalized = true;
@@ -619,7 +634,7 @@ static hipError_t launch_gemm(const dit_config& c, int M, int N, int K, const vo
                               const float* bias, void* C, bool c_f32, void* ws, hipStream_t s) {
   if (c.stream_dtype == DIT_BF16)
     return gemm_bf16(M, N, K, static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W), bias, C, c_f32, ws, s);
-  return gemm_f32(M, N, K, static_cast<const float*>(A), static_cast<const float*>(W), bias, static_cast<float*>(C), ws, s);
+  return gemm_f32(M, N, K, static_cast<const float*>(A), W, bias, static_cast<float*>(C), ws, s);
 }
 
 // x: the residual stream, float32 for a bf16 stream, float64 for an fp32 one.
@@ -810,7 +825,8 @@ extern "C" int dit_denoise_loop(dit_model* m, const dit_batch* b, float* latents
 
 extern "C" int dit_gemm_workspace_bytes(int dtype, int M, int N, int K, size_t* bytes) {
   if (bytes == nullptr || M < 0 || N <= 0 || K <= 0) return set_error(DIT_E_INVALID, "dit_gemm_workspace_bytes: bad argument");
-  *bytes = dtype == DIT_BF16 ? gemm_bf16_ws_bytes(M, N, K) : gemm_f32_ws_bytes(M, N, K);
+  // f32: the slices of B, then the GEMM's own scratch (slices of A, split-K partials)
+  *bytes = dtype == DIT_BF16 ? gemm_bf16_ws_bytes(M, N, K) : gemm_f32_slices_bytes(N, K) + gemm_f32_ws_bytes(M, N, K);
   return DIT_OK;
 }
 
@@ -828,11 +844,15 @@ extern "C" int dit_gemm(int dtype, int M, int N, int K, const void* A, const voi
   }
   if (dtype != DIT_F32) return set_error(DIT_E_INVALID, "dit_gemm: dtype");
   if (c_dtype != DIT_F32) return set_error(DIT_E_INVALID, "dit_gemm f32: C must be f32");
-  if (!gemm_f32_supported(M, N, K)) return set_error(DIT_E_UNSUPPORTED, "dit_gemm f32: K=%d must be a multiple of 4", K);
-  const size_t need = gemm_f32_ws_bytes(M, N, K);
+  if (!gemm_f32_supported(M, N, K))
+    return set_error(DIT_E_UNSUPPORTED, "dit_gemm f32: K=%d must be a multiple of 4 (and slices within 2 GB)", K);
+  const size_t bsl = gemm_f32_slices_bytes(N, K);
+  const size_t need = bsl + gemm_f32_ws_bytes(M, N, K);
   if (ws_bytes < need) return set_error(DIT_E_WORKSPACE, "dit_gemm: workspace of %zu bytes, %zu needed", ws_bytes, need);
-  if (need > 0 && ws == nullptr) return set_error(DIT_E_INVALID, "dit_gemm: workspace is null");
-  DIT_HIP(gemm_f32(M, N, K, static_cast<const float*>(A), static_cast<const float*>(B), bias, static_cast<float*>(C), ws, s));
+  if (ws == nullptr) return set_error(DIT_E_INVALID, "dit_gemm: workspace is null");
+  if (M == 0) return DIT_OK;
+  DIT_HIP(slice_rows(N, K, static_cast<const float*>(B), ws, s));
+  DIT_HIP(gemm_f32(M, N, K, static_cast<const float*>(A), ws, bias, static_cast<float*>(C), static_cast<char*>(ws) + bsl, s));
   return DIT_OK;
 }
 

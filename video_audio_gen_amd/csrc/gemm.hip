@@ -231,163 +231,240 @@ hipError_t gemm_bf16(int M, int N, int K, const uint16_t* A, const uint16_t* B, 
   return hipGetLastError();
 }
 
-// ============================================================================ f32 GEMM, fp64 accumulation
-// Exact products (fp32 operands widened to fp64) and fp64 sums on
-// v_mfma_f64_16x16x4_f64, one rounding to fp32 at the end: the result is the
-// correctly rounded value of the dot product except at fp64 near-ties.
-// Within a 16-wide K chunk the MFMAs run k-step-outer, so consecutive MFMAs of
-// a wavefront write different accumulators.  Split-K partials are fp64,
-// reduced in a fixed order.
-// Tile shape: 2 x 2 wavefronts of 32 x 32 (2 x 2 MFMA tiles), 64 x 64 x 16
-// workgroup tiles, ~1024 workgroups per GEMM.  Measured on the music model's
-// shapes, 48x64 and 48x32 wavefront tiles with 96- and 192-row workgroups, and
-// 512..2048 workgroups, all land within 10%: v_mfma_f64_16x16x4_f64 alone
-// sustains ~43 TFLOP/s on gfx950 (55% of the 78.6 TFLOP/s the datasheet
-// gives), and this kernel runs at 42-44 on the large shapes.
-#ifndef DIT_GF_WAVES_M
-#define DIT_GF_WAVES_M 2
-#endif
-#ifndef DIT_GF_WAVES_N
-#define DIT_GF_WAVES_N 2
-#endif
-#ifndef DIT_GF_TI
-#define DIT_GF_TI 2
-#endif
-#ifndef DIT_GF_TJ
-#define DIT_GF_TJ 2
-#endif
-#ifndef DIT_GF_TARGET
-#define DIT_GF_TARGET 1024
-#endif
-namespace gf {
-constexpr int TI = DIT_GF_TI, TJ = DIT_GF_TJ;          // 16x16 MFMA tiles per wave
-constexpr int WM = 16 * TI, WN = 16 * TJ;              // per-wave tile
-constexpr int BM = DIT_GF_WAVES_M * WM, BN = DIT_GF_WAVES_N * WN, BK = 16;
-constexpr int PAD = 20;                                // LDS rows padded to 20 floats: conflict-free float4 reads
-constexpr int NT = 64 * DIT_GF_WAVES_M * DIT_GF_WAVES_N;
-constexpr int A_LD = (BM * 4 + NT - 1) / NT, B_LD = (BN * 4 + NT - 1) / NT;  // float4 loads per thread
-}  // namespace gf
+// ============================================================================ f32 GEMM, int8 slices
+// Error-free splitting onto the integer matrix cores (the Ozaki scheme on
+// int8 units).  Each row x of A (and of B) is scaled by the power of two 2^-e
+// that brings it inside (-1, 1), and the scaled row is cut into S = 5 signed
+// 7-bit integer slices: x 2^-e = sum_s a_s 2^-7s + r with a_s in [-127, 127] and
+// |r| < 2^-35.  The product of two rows is then
+//   2^(e_i + f_j) sum_{s,t} 2^-7(s+t) (a_s . b_t)
+// where every a_s . b_t is an exact int32 dot product on
+// v_mfma_i32_32x32x32_i8.  Slice pairs with s + t <= S + 1 are kept (15 of
+// 25); the rest, with r, weigh below 2^-32 of the scaled product per term, so
+// the sum before its one rounding to fp32 is within ~0.02 fp32 ulps (rms, of
+// the output's rms) of the exact dot product, against 0.24 for the rounding
+// itself.  Pairs with equal s + t share one int32 accumulator (5 of them):
+// 5 pairs x 127^2 x K stays below 2^31 for K <= 26630, and splits never exceed
+// 16384 of K.  The integer sums are exact, so the result does not depend on
+// summation order; split-K partials are combined in fp64 in a fixed order.
+//
+// Workgroup tile 192 x 64 (a few hundred rows of activations are covered by
+// one or two tiles, so each weight slice is read once per row tile), K step
+// 32, twelve wavefronts of 32 x 32 (three per SIMD); slices of A and B stream
+// HBM -> LDS by direct buffer loads into a three-stage ring (120 KB).
+namespace go {
+constexpr int S = 5;                      // slices per operand
+constexpr int BM = 192, BN = 64, BK = 32, NW = 12, NT = 64 * NW, STAGES = 3;
+constexpr int APLANE = BM * BK / 16;      // 16-byte chunks of one A slice tile: 384
+constexpr int BPLANE = BN * BK / 16;      // ... of one B slice tile: 128
+constexpr int AOPER = S * APLANE, BOPER = S * BPLANE;
+constexpr int STAGE = AOPER + BOPER;      // 2560 chunks = 40 KB
+constexpr int NDMA = STAGE / 64;          // 1 KB direct loads per stage: 40
+constexpr int AQ = AOPER / 64;            // the first 30 of them fill A
+constexpr int DMA_MAX = (NDMA + NW - 1) / NW;  // per wave: 4 (waves 0-3) or 3
+constexpr int KSPLIT_MAX = 16384;
+}  // namespace go
 
-// Split count from (N, K) only, so a row's result never depends on M: about
-// DIT_GF_TARGET workgroups when the rows fit one tile, each split >= 256 of K.
-static int gf_splits(int N, int K) {
-  const int tiles_n = (N + gf::BN - 1) / gf::BN;
-  const int chunks = (K + gf::BK - 1) / gf::BK;
-  int s = (DIT_GF_TARGET + tiles_n - 1) / tiles_n;
-  int cap = chunks / 16;
-  if (cap < 1) cap = 1;
-  if (s > cap) s = cap;
-  if (s > 64) s = 64;
-  return s < 1 ? 1 : s;
+// Padded K of the slice planes (a multiple of the K step; pad slices are zero).
+static inline int go_kp(int K) { return (K + go::BK - 1) / go::BK * go::BK; }
+
+// Chunk c (0/1) of row r of a slice tile sits at r*2 + (c ^ ((r / 8) % 2)):
+// the 16 rows a 16-lane ds_read_b128 pass reads cover all 64 banks.
+__device__ __forceinline__ int go_swz(int r, int c) { return r * 2 + (c ^ ((r >> 3) & 1)); }
+
+// ---------------------------------------------------------------- slicing
+// One workgroup per row: e = exponent of max|x| (max|x| < 2^e), then five
+// truncating 7-bit digits of x 2^-e.  Every step is exact in fp32.
+__global__ __launch_bounds__(256) void slice_rows_kernel(int R, int K, int Kp, const float* __restrict__ X,
+                                                        int8_t* __restrict__ P, int32_t* __restrict__ E) {
+  __shared__ float red[4];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const float* x = X + static_cast<size_t>(row) * K;
+  float mx = 0.f;
+  for (int k = 4 * tid; k < K; k += 4 * 256) {
+    const float4 v = *reinterpret_cast<const float4*>(x + k);
+    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  }
+  mx = wave_max(mx);
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  int e = 0;
+  if (mx > 0.f) frexpf(mx, &e);  // mx = m 2^e, m in [0.5, 1)
+  if (tid == 0) E[row] = e;
+  const size_t plane = static_cast<size_t>(R) * Kp;
+  for (int k = 4 * tid; k < Kp; k += 4 * 256) {
+    float4 v = k < K ? *reinterpret_cast<const float4*>(x + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+    float f[4] = {ldexpf(v.x, -e), ldexpf(v.y, -e), ldexpf(v.z, -e), ldexpf(v.w, -e)};
+#pragma unroll
+    for (int sl = 0; sl < go::S; ++sl) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f[j] *= 128.f;
+        const float d = truncf(f[j]);
+        f[j] -= d;
+        w |= (static_cast<uint32_t>(static_cast<int>(d)) & 0xFFu) << (8 * j);
+      }
+      *reinterpret_cast<uint32_t*>(P + sl * plane + static_cast<size_t>(row) * Kp + k) = w;
+    }
+  }
 }
 
-// MFMA 16x16x4 f64: lane l supplies A[l%16][k = l/16] and B[k = l/16][l%16];
-// the result lane l holds D[4*i + l/16][l%16], i = 0..3.  Over four
-// consecutive k-steps, lane group g = l/16 feeds k = 4g + j (j = step), so each
-// lane reads one float4 per row per 16-wide K chunk.
-__global__ __launch_bounds__(gf::NT) void gemm_f32_kernel(int M, int N, int K,
-                                                         const float* __restrict__ A,
-                                                         const float* __restrict__ B,
-                                                         const float* __restrict__ bias,
-                                                         float* __restrict__ C,
-                                                         double* __restrict__ part, int splits,
-                                                         int chunks_per_split, int tiles_m) {
-  using namespace gf;
-  __shared__ float As[2][BM][PAD];
-  __shared__ float Bs[2][BN][PAD];
-  const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
-  const int sp = blockIdx.y;
+// ---------------------------------------------------------------- GEMM
+
+__global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
+                                                         const int8_t* __restrict__ Ap, const int32_t* __restrict__ Ae,
+                                                         const int8_t* __restrict__ Bp, const int32_t* __restrict__ Be,
+                                                         const float* __restrict__ bias, float* __restrict__ C,
+                                                         double* __restrict__ part, int splits, int steps_per_split,
+                                                         int tiles_m, int tiles_n) {
+  using namespace go;
+  __shared__ uint4 smem[STAGES * STAGE];  // 120 KB
+  // Workgroups go to the 8 XCDs round-robin; each run of 256 gives XCD x the
+  // 32 consecutive items 32x .. 32x+31 of (row tile fastest, N tile, split),
+  // so the row tiles sharing a weight tile share an L2.
+  const int w = (blockIdx.x / 256) * 256 + (blockIdx.x % 8) * 32 + (blockIdx.x / 8) % 32;
+  if (w >= tiles_m * tiles_n * splits) return;
+  const int tm = w % tiles_m, tn = (w / tiles_m) % tiles_n;
+  const int sp = w / (tiles_m * tiles_n);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int chunks = (K + BK - 1) / BK;
-  const int c_begin = sp * chunks_per_split;
-  const int c_end = c_begin + chunks_per_split < chunks ? c_begin + chunks_per_split : chunks;
+  const int ksteps = Kp / BK;
+  const int t_begin = sp * steps_per_split;
+  const int t_end = t_begin + steps_per_split < ksteps ? t_begin + steps_per_split : ksteps;
+  const int nsteps = t_end > t_begin ? t_end - t_begin : 0;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wr = (wave / DIT_GF_WAVES_N) * WM, wc = (wave % DIT_GF_WAVES_N) * WN;
+  const int lr = lane & 31, lg = lane >> 5;
+  const int wr = (wave % 6) * 32, wc = (wave / 6) * 32;
 
-  f64x4_t acc[TI][TJ];
+  // Direct loads: instruction q = wave + 12 j fills 1 KB = 32 rows of one
+  // slice plane: q < 30 row block q%6 of A plane q/6, else row block (q-30)%2
+  // of B plane (q-30)/2; lane l fetches row 32 (block) + l/2 at the logical
+  // chunk the swizzle stores at position l%2.  Rows past M or N get an offset
+  // past the buffer, which reads as zero.
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(Ap), 0, static_cast<uint32_t>(S * static_cast<int64_t>(M) * Kp), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(Bp), 0, static_cast<uint32_t>(S * static_cast<int64_t>(N) * Kp), 0x00020000);
+  const int ndma = wave < NDMA - NW * (DMA_MAX - 1) ? DMA_MAX : DMA_MAX - 1;
+  uint32_t voff[DMA_MAX];
 #pragma unroll
-  for (int i = 0; i < TI; ++i)
+  for (int j = 0; j < DMA_MAX; ++j) {
+    const int q = wave + NW * j;
+    const bool a_op = q < AQ;
+    const int plane = a_op ? q / 6 : (q - AQ) / 2;
+    const int r = 32 * (a_op ? q % 6 : (q - AQ) % 2) + (lane >> 1);
+    const int c = (lane & 1) ^ ((r >> 3) & 1);
+    const int grow = (a_op ? m0 : n0) + r;
+    const int rows = a_op ? M : N;
+    voff[j] = (q < NDMA && grow < rows) ? static_cast<uint32_t>((static_cast<int64_t>(plane) * rows + grow) * Kp + 16 * c)
+                                        : 0xFFFFFFF0u;
+  }
+  auto dma = [&](int t, int st) {
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) acc[i][j] = f64x4_t{0.0, 0.0, 0.0, 0.0};
-
-  // Loader: float4 q of this thread is row (tid + NT q) / 4, k 4 ((tid + NT q) % 4).
-  float4 ra[A_LD], rb[B_LD];
-  auto gload = [&](int ch) {
-#pragma unroll
-    for (int q = 0; q < A_LD; ++q) {
-      const int id = tid + NT * q, r = id >> 2, k = ch * BK + 4 * (id & 3);
-      const int gm = m0 + r;
-      ra[q] = (r < BM && gm < M && k < K) ? *reinterpret_cast<const float4*>(A + static_cast<size_t>(gm) * K + k)
-                                : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-#pragma unroll
-    for (int q = 0; q < B_LD; ++q) {
-      const int id = tid + NT * q, r = id >> 2, k = ch * BK + 4 * (id & 3);
-      const int gn = n0 + r;
-      rb[q] = (r < BN && gn < N && k < K) ? *reinterpret_cast<const float4*>(B + static_cast<size_t>(gn) * K + k)
-                                : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < DMA_MAX; ++j) {
+      const int q = wave + NW * j;
+      if (j < ndma) {
+        const uint32_t off = voff[j] == 0xFFFFFFF0u ? voff[j] : voff[j] + static_cast<uint32_t>(t * BK);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(q < AQ ? ra : rb, (lds_ptr_t)(smem + st * STAGE + q * 64), 16, off, 0,
+                                                 0, 0);
+      }
     }
   };
-  auto sstore = [&](int st) {
-#pragma unroll
-    for (int q = 0; q < A_LD; ++q) {
-      const int id = tid + NT * q;
-      if ((id >> 2) < BM) *reinterpret_cast<float4*>(&As[st][id >> 2][4 * (id & 3)]) = ra[q];
-    }
-#pragma unroll
-    for (int q = 0; q < B_LD; ++q) {
-      const int id = tid + NT * q;
-      if ((id >> 2) < BN) *reinterpret_cast<float4*>(&Bs[st][id >> 2][4 * (id & 3)]) = rb[q];
-    }
-  };
 
-  if (c_begin < c_end) {
-    gload(c_begin);
-    sstore(0);
-  }
-  __syncthreads();
-  const int r16 = lane & 15, g = lane >> 4;
-  for (int ch = c_begin; ch < c_end; ++ch) {
-    const int st = (ch - c_begin) & 1;
-    if (ch + 1 < c_end) gload(ch + 1);
-    float4 fa[TI], fb[TJ];
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  typedef int v16i __attribute__((ext_vector_type(16)));
+  v16i acc[S];
 #pragma unroll
-    for (int i = 0; i < TI; ++i) fa[i] = *reinterpret_cast<const float4*>(&As[st][wr + i * 16 + r16][4 * g]);
+  for (int d = 0; d < S; ++d)
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) fb[j] = *reinterpret_cast<const float4*>(&Bs[st][wc + j * 16 + r16][4 * g]);
-    const float* fa_ = reinterpret_cast<const float*>(fa);
-    const float* fb_ = reinterpret_cast<const float*>(fb);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int i = 0; i < TI; ++i) {
-        const double av = static_cast<double>(fa_[4 * i + kk]);
-#pragma unroll
-        for (int j = 0; j < TJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, static_cast<double>(fb_[4 * j + kk]), acc[i][j], 0, 0, 0);
-      }
-    if (ch + 1 < c_end) sstore(st ^ 1);
-    __syncthreads();
-  }
+    for (int e = 0; e < 16; ++e) acc[d][e] = 0;
 
 #pragma unroll
-  for (int j = 0; j < TJ; ++j) {
-    const int gn = n0 + wc + j * 16 + r16;
-    if (gn >= N) continue;
-    const double bv = (splits == 1 && bias != nullptr) ? static_cast<double>(bias[gn]) : 0.0;
+  for (int p = 0; p < STAGES - 1; ++p)
+    if (p < nsteps) dma(t_begin + p, p);
+  for (int i = 0; i < nsteps; ++i) {
+    const int st = i % STAGES;
+    // step i landed: the younger in-flight step (this wave's 3 or 4 loads) may stay outstanding
+    if (i + 1 < nsteps) {
+      if (ndma == DMA_MAX) __builtin_amdgcn_s_waitcnt(0x0F70 | DMA_MAX);
+      else __builtin_amdgcn_s_waitcnt(0x0F70 | (DMA_MAX - 1));
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+    __syncthreads();  // every wave's share of step i is in LDS; stage (i-1) is free
+    if (i + STAGES - 1 < nsteps) dma(t_begin + i + STAGES - 1, (i + STAGES - 1) % STAGES);
+    const uint4* sa = smem + st * STAGE;
+    const uint4* sb = sa + AOPER;
+    v4i fa[S], fb[S];
 #pragma unroll
-    for (int i = 0; i < TI; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int gm = m0 + wr + i * 16 + 4 * e + g;
-        if (gm >= M) continue;
-        if (splits == 1)
-          C[static_cast<size_t>(gm) * N + gn] = static_cast<float>(acc[i][j][e] + bv);
-        else
-          part[(static_cast<size_t>(sp) * M + gm) * N + gn] = acc[i][j][e];
-      }
+    for (int p = 0; p < S; ++p) {
+      fa[p] = __builtin_bit_cast(v4i, sa[p * APLANE + go_swz(wr + lr, lg)]);
+      fb[p] = __builtin_bit_cast(v4i, sb[p * BPLANE + go_swz(wc + lr, lg)]);
+    }
+    // pair (s, t) accumulates in acc[s + t]; the order keeps two MFMAs on one
+    // accumulator at least two instructions apart (levels 4 3 2 4 3 2 4 3 2 4 3 1 4 0 1)
+#define GO_MFMA(s_, t_) acc[(s_) + (t_)] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[s_], fb[t_], acc[(s_) + (t_)], 0, 0, 0);
+    GO_MFMA(4, 0) GO_MFMA(3, 0) GO_MFMA(2, 0) GO_MFMA(3, 1) GO_MFMA(2, 1) GO_MFMA(1, 1) GO_MFMA(2, 2)
+    GO_MFMA(1, 2) GO_MFMA(0, 2) GO_MFMA(1, 3) GO_MFMA(0, 3) GO_MFMA(1, 0) GO_MFMA(0, 4) GO_MFMA(0, 0)
+    GO_MFMA(0, 1)
+#undef GO_MFMA
   }
+
+  // Lane holds column wc + lr, rows wr + 8 (e/4) + 4 lg + e%4 of each level.
+  const int gn = n0 + wc + lr;
+  if (gn >= N) return;
+  const int fe = Be[gn];
+  const double bv = (splits == 1 && bias != nullptr) ? static_cast<double>(bias[gn]) : 0.0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int gm = m0 + wr + 8 * (e >> 2) + 4 * lg + (e & 3);
+    if (gm >= M) continue;
+    // sum_d acc_d 2^-7(d+2): each term exact in fp64, five terms
+    double v = 0.0;
+#pragma unroll
+    for (int d = S - 1; d >= 0; --d) v += ldexp(static_cast<double>(acc[d][e]), -7 * (d + 2));
+    v = ldexp(v, Ae[gm] + fe);
+    if (splits == 1)
+      C[static_cast<size_t>(gm) * N + gn] = static_cast<float>(v + bv);
+    else
+      part[(static_cast<size_t>(sp) * M + gm) * N + gn] = v;
+  }
+}
+
+// Split count from (N, K) and the device alone, so a row's result never
+// depends on M.  One workgroup fits a CU (120 KB of LDS), so for a single row
+// tile the launch runs in ceil(tiles_n * s / CUs) rounds of ceil(steps / s) K
+// steps each; s minimises that product plus a small charge per split for its
+// partial (written and re-read), with splits of >= 8 steps and <= 16384 of K.
+static int go_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus = n;
+  }
+  return cus;
+}
+static int go_splits(int N, int K) {
+  const int tiles_n = (N + go::BN - 1) / go::BN;
+  const int steps = go_kp(K) / go::BK;
+  const int cus = go_cus();
+  int lo = (steps * go::BK + go::KSPLIT_MAX - 1) / go::KSPLIT_MAX;  // int32 headroom
+  int hi = steps / 8;
+  if (hi > 64) hi = 64;
+  if (hi < lo) hi = lo;
+  if (lo < 1) lo = 1;
+  int best = lo;
+  double best_cost = 1e30;
+  for (int sp = lo; sp <= hi; ++sp) {
+    const int rounds = (tiles_n * sp + cus - 1) / cus;
+    const double cost = static_cast<double>(rounds) * ((steps + sp - 1) / sp) + 0.5 * sp;
+    if (cost < best_cost) best_cost = cost, best = sp;
+  }
+  return best;
 }
 
 // Fixed-order reduction of the split-K partials, bias added in fp64, one rounding.
@@ -404,32 +481,62 @@ __global__ __launch_bounds__(256) void gemm_f32_reduce_kernel(int M, int N, int 
   C[t] = static_cast<float>(v);
 }
 
-bool gemm_f32_supported(int M, int N, int K) { return M >= 0 && N > 0 && K > 0 && K % 4 == 0; }
-
-size_t gemm_f32_ws_bytes(int M, int N, int K) {
-  const int s = gf_splits(N, K);
-  return s > 1 ? static_cast<size_t>(s) * M * N * sizeof(double) : 0;
+// K a multiple of 4; every slice buffer must fit 32-bit buffer offsets.
+bool gemm_f32_supported(int M, int N, int K) {
+  const int64_t kp = go_kp(K);
+  return M >= 0 && N > 0 && K > 0 && K % 4 == 0 && go::S * kp * (M > N ? M : N) < (int64_t(1) << 31) - 256;
 }
 
-hipError_t gemm_f32(int M, int N, int K, const float* A, const float* B, const float* bias,
-                    float* C, void* ws, hipStream_t s) {
+static size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+size_t gemm_f32_slices_bytes(int R, int K) {
+  return al256(static_cast<size_t>(go::S) * R * go_kp(K)) + al256(sizeof(int32_t) * R);
+}
+size_t gemm_f32_ws_bytes(int M, int N, int K) {
+  const int s = go_splits(N, K);
+  return gemm_f32_slices_bytes(M, K) + (s > 1 ? al256(static_cast<size_t>(s) * M * N * sizeof(double)) : 0);
+}
+
+hipError_t slice_rows(int R, int K, const float* X, void* slices, hipStream_t s) {
+  if (R == 0) return hipSuccess;
+  const int kp = go_kp(K);
+  int8_t* P = static_cast<int8_t*>(slices);
+  int32_t* E = reinterpret_cast<int32_t*>(P + al256(static_cast<size_t>(go::S) * R * kp));
+  LaunchScope scope_(kCntConvert, s);
+  hipLaunchKernelGGL(slice_rows_kernel, dim3(R), dim3(256), 0, s, R, K, kp, X, P, E);
+  return hipGetLastError();
+}
+
+hipError_t gemm_f32(int M, int N, int K, const float* A, const void* Bs, const float* bias, float* C,
+                    void* ws, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  const int splits = gf_splits(N, K);
-  const int chunks = (K + gf::BK - 1) / gf::BK;
-  const int cps = (chunks + splits - 1) / splits;
-  const int tiles_m = (M + gf::BM - 1) / gf::BM, tiles_n = (N + gf::BN - 1) / gf::BN;
+  const int kp = go_kp(K);
+  char* w = static_cast<char*>(ws);
+  hipError_t e = slice_rows(M, K, A, w, s);
+  if (e != hipSuccess) return e;
+  const int8_t* Ap = reinterpret_cast<const int8_t*>(w);
+  const int32_t* Ae = reinterpret_cast<const int32_t*>(w + al256(static_cast<size_t>(go::S) * M * kp));
+  const int8_t* Bp = static_cast<const int8_t*>(Bs);
+  const int32_t* Be = reinterpret_cast<const int32_t*>(Bp + al256(static_cast<size_t>(go::S) * N * kp));
+  double* part = reinterpret_cast<double*>(w + gemm_f32_slices_bytes(M, K));
+  const int splits = go_splits(N, K);
+  const int steps = kp / go::BK;
+  const int sps = (steps + splits - 1) / splits;
+  const int tiles_m = (M + go::BM - 1) / go::BM, tiles_n = (N + go::BN - 1) / go::BN;
+  const int64_t work = static_cast<int64_t>(tiles_m) * tiles_n * splits;
+  if (work >= (int64_t(1) << 31) - 256) return hipErrorInvalidValue;
+  const unsigned blocks = static_cast<unsigned>((work + 255) / 256 * 256);
   {
     LaunchScope scope_(kCntGemmF32, s);
-    hipLaunchKernelGGL(gemm_f32_kernel, dim3(tiles_m * tiles_n, splits), dim3(gf::NT), 0, s, M, N, K,
-                       A, B, bias, C, static_cast<double*>(ws), splits, cps, tiles_m);
+    hipLaunchKernelGGL(gemm_f32_kernel, dim3(blocks), dim3(go::NT), 0, s, M, N, kp, Ap, Ae, Bp, Be, bias, C, part,
+                       splits, sps, tiles_m, tiles_n);
   }
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   const int64_t MN = static_cast<int64_t>(M) * N;
   {
     LaunchScope scope_(kCntGemmF32Reduce, s);
     hipLaunchKernelGGL(gemm_f32_reduce_kernel, dim3(static_cast<unsigned>((MN + 255) / 256)), dim3(256),
-                       0, s, M, N, splits, static_cast<const double*>(ws), bias, C);
+                       0, s, M, N, splits, part, bias, C);
   }
   return hipGetLastError();
 }

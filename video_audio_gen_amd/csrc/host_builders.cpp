@@ -143,3 +143,32 @@ extern "C" int dit_sigma_schedule(double shift, int n_steps, double* sigma_host,
     for (int i = 0; i < n_steps; ++i) dt_host[i] = static_cast<float>(sig[i + 1] - sig[i]);
   return DIT_OK;
 }
+
+// ---------------------------------------------------------------- int8 slices of fp32 weights
+// The staging-time twin of the device slicing (slice_rows): per row, e with
+// max|x| < 2^e (frexp), then five truncating 7-bit digits of x 2^-e; planes
+// [5][R][Kp] int8 (zero past K), then R int32 exponents 256 bytes further
+// aligned.  All steps are exact in fp32, so both sides produce the same bytes.
+namespace dit {
+void host_slice_rows(int64_t R, int64_t K, int64_t Kp, const float* X, int8_t* out) {
+  const size_t plane = static_cast<size_t>(R) * Kp;
+  int32_t* E = reinterpret_cast<int32_t*>(out + ((5 * plane + 255) & ~size_t(255)));
+  for (int64_t r = 0; r < R; ++r) {
+    const float* x = X + r * K;
+    float mx = 0.f;
+    for (int64_t k = 0; k < K; ++k) mx = std::fmax(mx, std::fabs(x[k]));
+    int e = 0;
+    if (mx > 0.f) std::frexp(mx, &e);
+    E[r] = e;
+    for (int64_t k = 0; k < Kp; ++k) {
+      float f = k < K ? std::ldexp(x[k], -e) : 0.f;
+      for (int s = 0; s < 5; ++s) {
+        f *= 128.f;
+        const float d = std::trunc(f);
+        f -= d;
+        out[s * plane + static_cast<size_t>(r) * Kp + k] = static_cast<int8_t>(static_cast<int>(d));
+      }
+    }
+  }
+}
+}  // namespace dit

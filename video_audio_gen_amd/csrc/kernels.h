@@ -31,8 +31,13 @@ class LaunchScope {
 size_t gemm_bf16_ws_bytes(int M, int N, int K);
 hipError_t gemm_bf16(int M, int N, int K, const uint16_t* A, const uint16_t* B, const float* bias,
                      void* C, bool c_f32, void* ws, hipStream_t s);
+// f32: B is given as its int8 slices (slice_rows layout: 5 planes [5][N][Kp]
+// int8, Kp = K rounded up to 32, then N int32 exponents, each part 256-byte
+// aligned); A is sliced into ws on the way.
+size_t gemm_f32_slices_bytes(int R, int K);
+hipError_t slice_rows(int R, int K, const float* X, void* slices, hipStream_t s);
 size_t gemm_f32_ws_bytes(int M, int N, int K);
-hipError_t gemm_f32(int M, int N, int K, const float* A, const float* B, const float* bias,
+hipError_t gemm_f32(int M, int N, int K, const float* A, const void* B_slices, const float* bias,
                     float* C, void* ws, hipStream_t s);
 // Which K, N the GEMMs accept (checked by the ABI layer before launching).
 bool gemm_bf16_supported(int M, int N, int K);
