@@ -265,6 +265,20 @@ constexpr int DMA_MAX = (NDMA + NW - 1) / NW;  // per wave: 4 (waves 0-3) or 3
 constexpr int KSPLIT_MAX = 16384;
 }  // namespace go
 
+// s_waitcnt vmcnt(n) for a run-time n (larger n waits for the n = 7 case).
+__device__ __forceinline__ void go_wait_vm(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+  }
+}
+
 // Padded K of the slice planes (a multiple of the K step; pad slices are zero).
 static inline int go_kp(int K) { return (K + go::BK - 1) / go::BK * go::BK; }
 
@@ -274,7 +288,9 @@ __device__ __forceinline__ int go_swz(int r, int c) { return r * 2 + (c ^ ((r >>
 
 // ---------------------------------------------------------------- slicing
 // One workgroup per row: e = exponent of max|x| (max|x| < 2^e), then five
-// truncating 7-bit digits of x 2^-e.  Every step is exact in fp32.
+// truncating 7-bit digits of x 2^-e.  Every step is exact in fp32.  Planes are
+// stored K-step-major, [plane][K / 32][row][32 bytes], so the 32 rows of one K
+// step that a direct load fetches are 1 KB of consecutive bytes.
 __global__ __launch_bounds__(256) void slice_rows_kernel(int R, int K, int Kp, const float* __restrict__ X,
                                                         int8_t* __restrict__ P, int32_t* __restrict__ E) {
   __shared__ float red[4];
@@ -306,7 +322,8 @@ __global__ __launch_bounds__(256) void slice_rows_kernel(int R, int K, int Kp, c
         f[j] -= d;
         w |= (static_cast<uint32_t>(static_cast<int>(d)) & 0xFFu) << (8 * j);
       }
-      *reinterpret_cast<uint32_t*>(P + sl * plane + static_cast<size_t>(row) * Kp + k) = w;
+      // layout [plane][K step][row][32 bytes]
+      *reinterpret_cast<uint32_t*>(P + sl * plane + (static_cast<size_t>(k / go::BK) * R + row) * go::BK + (k % go::BK)) = w;
     }
   }
 }
@@ -358,15 +375,18 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
     const int c = (lane & 1) ^ ((r >> 3) & 1);
     const int grow = (a_op ? m0 : n0) + r;
     const int rows = a_op ? M : N;
-    voff[j] = (q < NDMA && grow < rows) ? static_cast<uint32_t>((static_cast<int64_t>(plane) * rows + grow) * Kp + 16 * c)
-                                        : 0xFFFFFFF0u;
+    // slice layout [plane][K step][row][32 bytes]: one instruction reads 1 KB in a row
+    voff[j] = (q < NDMA && grow < rows)
+                  ? static_cast<uint32_t>((static_cast<int64_t>(plane) * (Kp / BK) * rows + grow) * BK + 16 * c)
+                  : 0xFFFFFFF0u;
   }
+  const uint32_t a_step = static_cast<uint32_t>(M) * BK, b_step = static_cast<uint32_t>(N) * BK;  // bytes per K step
   auto dma = [&](int t, int st) {
 #pragma unroll
     for (int j = 0; j < DMA_MAX; ++j) {
       const int q = wave + NW * j;
       if (j < ndma) {
-        const uint32_t off = voff[j] == 0xFFFFFFF0u ? voff[j] : voff[j] + static_cast<uint32_t>(t * BK);
+        const uint32_t off = voff[j] == 0xFFFFFFF0u ? voff[j] : voff[j] + static_cast<uint32_t>(t) * (q < AQ ? a_step : b_step);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(q < AQ ? ra : rb, (lds_ptr_t)(smem + st * STAGE + q * 64), 16, off, 0,
                                                  0, 0);
       }
@@ -381,18 +401,15 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[d][e] = 0;
 
+  static_assert(STAGES == 3, "the wait counts below assume two copies in flight");
 #pragma unroll
   for (int p = 0; p < STAGES - 1; ++p)
     if (p < nsteps) dma(t_begin + p, p);
   for (int i = 0; i < nsteps; ++i) {
     const int st = i % STAGES;
-    // step i landed: the younger in-flight step (this wave's 3 or 4 loads) may stay outstanding
-    if (i + 1 < nsteps) {
-      if (ndma == DMA_MAX) __builtin_amdgcn_s_waitcnt(0x0F70 | DMA_MAX);
-      else __builtin_amdgcn_s_waitcnt(0x0F70 | (DMA_MAX - 1));
-    } else {
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-    }
+    // Step i's copy landed once only the next step's copy (this wave's 3 or 4
+    // loads) is outstanding: loads complete in issue order.
+    go_wait_vm(i + 1 < nsteps ? ndma : 0);
     __syncthreads();  // every wave's share of step i is in LDS; stage (i-1) is free
     if (i + STAGES - 1 < nsteps) dma(t_begin + i + STAGES - 1, (i + STAGES - 1) % STAGES);
     const uint4* sa = smem + st * STAGE;

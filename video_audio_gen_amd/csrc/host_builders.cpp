@@ -146,9 +146,10 @@ extern "C" int dit_sigma_schedule(double shift, int n_steps, double* sigma_host,
 
 // ---------------------------------------------------------------- int8 slices of fp32 weights
 // The staging-time twin of the device slicing (slice_rows): per row, e with
-// max|x| < 2^e (frexp), then five truncating 7-bit digits of x 2^-e; planes
-// [5][R][Kp] int8 (zero past K), then R int32 exponents 256 bytes further
-// aligned.  All steps are exact in fp32, so both sides produce the same bytes.
+// max|x| < 2^e (frexp), then five truncating 7-bit digits of x 2^-e; five
+// planes of [Kp/32][R][32] int8 (zero past K), then R int32 exponents 256
+// bytes further aligned.  All steps are exact in fp32, so both sides produce
+// the same bytes.
 namespace dit {
 void host_slice_rows(int64_t R, int64_t K, int64_t Kp, const float* X, int8_t* out) {
   const size_t plane = static_cast<size_t>(R) * Kp;
@@ -166,7 +167,7 @@ void host_slice_rows(int64_t R, int64_t K, int64_t Kp, const float* X, int8_t* o
         f *= 128.f;
         const float d = std::trunc(f);
         f -= d;
-        out[s * plane + static_cast<size_t>(r) * Kp + k] = static_cast<int8_t>(static_cast<int>(d));
+        out[s * plane + (static_cast<size_t>(k / 32) * R + r) * 32 + (k % 32)] = static_cast<int8_t>(static_cast<int>(d));
       }
     }
   }

@@ -31,9 +31,9 @@ class LaunchScope {
 size_t gemm_bf16_ws_bytes(int M, int N, int K);
 hipError_t gemm_bf16(int M, int N, int K, const uint16_t* A, const uint16_t* B, const float* bias,
                      void* C, bool c_f32, void* ws, hipStream_t s);
-// f32: B is given as its int8 slices (slice_rows layout: 5 planes [5][N][Kp]
-// int8, Kp = K rounded up to 32, then N int32 exponents, each part 256-byte
-// aligned); A is sliced into ws on the way.
+// f32: B is given as its int8 slices (slice_rows layout: 5 planes of
+// [Kp/32][N][32] int8, Kp = K rounded up to 32, then N int32 exponents, each
+// part 256-byte aligned); A is sliced into ws on the way.
 size_t gemm_f32_slices_bytes(int R, int K);
 hipError_t slice_rows(int R, int K, const float* X, void* slices, hipStream_t s);
 size_t gemm_f32_ws_bytes(int M, int N, int K);
