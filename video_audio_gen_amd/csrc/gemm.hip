@@ -265,6 +265,11 @@ constexpr int DMA_MAX = (NDMA + NW - 1) / NW;  // per wave: 4 (waves 0-3) or 3
 constexpr int KSPLIT_MAX = 16384;
 }  // namespace go
 
+// Workgroup barrier without the memory fence of __syncthreads(): LDS written
+// by direct loads is covered by the explicit vmcnt waits before it, and the
+// "memory" clobber keeps the compiler from moving LDS reads across it.
+__device__ __forceinline__ void go_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 // s_waitcnt vmcnt(n) for a run-time n (larger n waits for the n = 7 case).
 __device__ __forceinline__ void go_wait_vm(int n) {
   switch (n) {
@@ -351,7 +356,8 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
   const int t_end = t_begin + steps_per_split < ksteps ? t_begin + steps_per_split : ksteps;
   const int nsteps = t_end > t_begin ? t_end - t_begin : 0;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches and buffer descriptors
   const int lr = lane & 31, lg = lane >> 5;
   const int wr = (wave % 6) * 32, wc = (wave / 6) * 32;
 
@@ -410,7 +416,10 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
     // Step i's copy landed once only the next step's copy (this wave's 3 or 4
     // loads) is outstanding: loads complete in issue order.
     go_wait_vm(i + 1 < nsteps ? ndma : 0);
-    __syncthreads();  // every wave's share of step i is in LDS; stage (i-1) is free
+    // Every wave's share of step i is in LDS and stage (i-1) is free.  A bare
+    // s_barrier: __syncthreads() would also wait for the copy just issued
+    // for step i+1 (vmcnt(0)), which serialises the ring.
+    go_barrier();
     if (i + STAGES - 1 < nsteps) dma(t_begin + i + STAGES - 1, (i + STAGES - 1) % STAGES);
     const uint4* sa = smem + st * STAGE;
     const uint4* sb = sa + AOPER;
