@@ -315,15 +315,20 @@ __global__ __launch_bounds__(ab::NT, 1) void attention_bf16_kernel(int N, int H,
 }
 
 // ============================================================================ f32 stream
-// Workgroup = one (head, document, 16-query tile); each wavefront owns 4
-// queries and walks them one at a time: lane j scores key j of the 64-key tile,
-// the wavefront reduces max and sum, and lane d accumulates output dims d,
-// d + 64 with the probabilities broadcast by readlane.  Scores, softmax and
-// the weighted sum run in fp64 and the output is rounded once to fp32: the
-// fp32 stream is held to rel 1e-5 / abs 1e-6, which fp32 sums over 24 blocks
-// do not meet.
+// Scores, softmax and the weighted sum in fp64 with one rounding of the output
+// to fp32: the fp32 stream is held to rel 1e-5 / abs 1e-6 after 24 blocks,
+// which fp32 dot products over the head dim do not meet.  The products run on
+// v_mfma_f64_16x16x4_f64 (fp32 operands are exact in fp64).
+//
+// Workgroup = one (document, head, 64-query tile); four wavefronts of 16
+// queries; 64-key K/V tiles in LDS (fp32, rows padded so the operand reads
+// are bank-conflict free).  Scores are formed transposed, S^T = K Q^T: lane l
+// then holds 4 keys (4i + l/16 of a 16-key block) of query l%16, which is
+// exactly the B operand layout of O^T += V^T P^T, so the probabilities never
+// leave registers; the row max and sum reduce over i in the lane and over the
+// four lanes l%16 + 16g.
 namespace af {
-constexpr int QT = 16, QW = 4, KT = 64, NT = 256;
+constexpr int QW = 16, NW = 4, QT = QW * NW, KT = 64, NT = NW * 64;
 }
 
 template <int HD>
@@ -333,92 +338,118 @@ __global__ __launch_bounds__(af::NT) void attention_f32_kernel(int N, int H, con
                                                               const float* __restrict__ v,
                                                               float* __restrict__ o, double scale) {
   using namespace af;
-  constexpr int KS = HD + 1;
+  constexpr int KS = HD + 4;    // Q/K row stride (floats): 16 rows x 4 columns hit 64 distinct banks
+  constexpr int VS = HD + 16;   // V row stride: 4 rows x 16 columns hit 64 distinct banks
+  constexpr int NDB = HD / 16;  // 16-dim output blocks
+  __shared__ float Qs[QT * KS];
   __shared__ float Ks[KT * KS];
-  __shared__ float Vs[KT * HD];
-  __shared__ float Qs[QT * HD];
+  __shared__ float Vs[KT * VS];
   const int qt = blockIdx.x, h = blockIdx.y, d = blockIdx.z;
   const int s0 = cu[d], len = cu[d + 1] - s0;
   const int q0 = qt * QT;
   if (q0 >= len) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const size_t head_off = static_cast<size_t>(h) * N * HD;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  const size_t base = (static_cast<size_t>(h) * N + s0) * HD;
+  constexpr int F4 = HD / 4;  // float4 per row
 
-  for (int i = tid; i < QT * HD; i += NT) {
-    const int r = i / HD, c = i % HD;
-    Qs[i] = (q0 + r < len) ? q[head_off + static_cast<size_t>(s0 + q0 + r) * HD + c] : 0.f;
+  for (int i = tid; i < QT * F4; i += NT) {
+    const int r = i / F4, c = i % F4;
+    const float4 t = q0 + r < len ? *reinterpret_cast<const float4*>(q + base + static_cast<size_t>(q0 + r) * HD + 4 * c)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float4*>(&Qs[r * KS + 4 * c]) = t;
   }
+  __syncthreads();
+  // Q^T operand: lane holds Q[query wave*16 + r16][dim 4 ks + g]
+  double qf[HD / 4];
+#pragma unroll
+  for (int ks = 0; ks < HD / 4; ++ks) qf[ks] = static_cast<double>(Qs[(wave * QW + r16) * KS + 4 * ks + g]);
+  const bool active = q0 + wave * QW < len;  // this wavefront has a query in the document
 
-  constexpr int DPL = (HD + 63) / 64;  // output dims per lane
-  double acc[QW][DPL];
-  double m_run[QW], l_run[QW];
+  f64x4_t acc[NDB];
 #pragma unroll
-  for (int qq = 0; qq < QW; ++qq) {
-    m_run[qq] = -INFINITY;
-    l_run[qq] = 0.0;
-#pragma unroll
-    for (int u = 0; u < DPL; ++u) acc[qq][u] = 0.0;
-  }
+  for (int b = 0; b < NDB; ++b) acc[b] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+  double m_run = -INFINITY, l_run = 0.0;
 
   const int n_kt = (len + KT - 1) / KT;
   for (int t = 0; t < n_kt; ++t) {
     const int k0 = t * KT;
-    __syncthreads();
-    for (int i = tid; i < KT * HD; i += NT) {
-      const int r = i / HD, c = i % HD;
-      const bool ok = k0 + r < len;
-      const size_t off = head_off + static_cast<size_t>(s0 + k0 + r) * HD + c;
-      Ks[r * KS + c] = ok ? k[off] : 0.f;
-      Vs[r * HD + c] = ok ? v[off] : 0.f;
+    __syncthreads();  // previous tile consumed
+    for (int i = tid; i < KT * F4; i += NT) {
+      const int r = i / F4, c = i % F4;
+      float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
+      if (k0 + r < len) {
+        const size_t off = base + static_cast<size_t>(k0 + r) * HD + 4 * c;
+        kv = *reinterpret_cast<const float4*>(k + off);
+        vv = *reinterpret_cast<const float4*>(v + off);
+      }
+      *reinterpret_cast<float4*>(&Ks[r * KS + 4 * c]) = kv;
+      *reinterpret_cast<float4*>(&Vs[r * VS + 4 * c]) = vv;
     }
     __syncthreads();
-    const bool key_ok = k0 + lane < len;
+    if (!active) continue;
+    const int nkb = (len - k0) >= KT ? KT / 16 : (len - k0 + 15) / 16;  // 16-key blocks holding keys
+    // S^T blocks: lane holds keys kb*16 + 4i + g of query r16
+    f64x4_t sblk[KT / 16];
+    double mt = -INFINITY;
 #pragma unroll
-    for (int qq = 0; qq < QW; ++qq) {
-      const float* qr = Qs + (wave * QW + qq) * HD;
-      double sc = 0.0;
-#pragma unroll 8
-      for (int c = 0; c < HD; ++c) sc += double(qr[c]) * double(Ks[lane * KS + c]);
-      sc = key_ok ? sc * scale : -INFINITY;
-      double mt = sc;
+    for (int kb = 0; kb < KT / 16; ++kb) {
+      sblk[kb] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+      if (kb < nkb) {
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) mt = fmax(mt, __shfl_xor(mt, off, 64));
-      const double m_new = fmax(m_run[qq], mt);
-      const double alpha = exp(m_run[qq] - m_new);
-      const double p = key_ok ? exp(sc - m_new) : 0.0;
-      double ps = p;
+        for (int ks = 0; ks < HD / 4; ++ks)
+          sblk[kb] = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(Ks[(kb * 16 + r16) * KS + 4 * ks + g]),
+                                                         qf[ks], sblk[kb], 0, 0, 0);
+      }
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) ps += __shfl_xor(ps, off, 64);
-      l_run[qq] = l_run[qq] * alpha + ps;
-      m_run[qq] = m_new;
-#pragma unroll
-      for (int u = 0; u < DPL; ++u) acc[qq][u] *= alpha;
-      const int64_t pbits = __double_as_longlong(p);
-      const int plo = static_cast<int>(pbits & 0xFFFFFFFF), phi = static_cast<int>(pbits >> 32);
-      for (int j = 0; j < KT; ++j) {
-        const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(plo, j));
-        const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(phi, j));
-        const double pj = __longlong_as_double(static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo));
-#pragma unroll
-        for (int u = 0; u < DPL; ++u) {
-          const int dd = lane + 64 * u;
-          if (dd < HD) acc[qq][u] += pj * double(Vs[j * HD + dd]);
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int key = k0 + kb * 16 + 4 * i + g;
+        const double sc = (kb < nkb && key < len) ? sblk[kb][i] * scale : -INFINITY;
+        sblk[kb][i] = sc;
+        mt = fmax(mt, sc);
       }
     }
-  }
-  const int D = H * HD;
+    mt = fmax(mt, __shfl_xor(mt, 16, 64));
+    mt = fmax(mt, __shfl_xor(mt, 32, 64));
+    const double m_new = fmax(m_run, mt);
+    const double alpha = exp(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
 #pragma unroll
-  for (int qq = 0; qq < QW; ++qq) {
-    const int qi = q0 + wave * QW + qq;
-    if (qi >= len) continue;
-    const double inv = 1.0 / l_run[qq];
+    for (int b = 0; b < NDB; ++b)
 #pragma unroll
-    for (int u = 0; u < DPL; ++u) {
-      const int dd = lane + 64 * u;
-      if (dd < HD) o[static_cast<size_t>(s0 + qi) * D + h * HD + dd] = static_cast<float>(acc[qq][u] * inv);
+      for (int i = 0; i < 4; ++i) acc[b][i] *= alpha;
+#pragma unroll
+    for (int kb = 0; kb < KT / 16; ++kb) {
+      if (kb >= nkb) break;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const double p = exp(sblk[kb][i] - m_new);  // exp(-inf) = 0 for masked keys
+        sblk[kb][i] = p;
+        l_run += p;
+      }
+      // O^T += V^T P^T over this block's keys 4ks + g: B operand = p of slot ks
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int b = 0; b < NDB; ++b)
+          acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(
+              static_cast<double>(Vs[(kb * 16 + 4 * ks + g) * VS + b * 16 + r16]), sblk[kb][ks], acc[b], 0, 0, 0);
     }
   }
+  if (!active) return;
+  double l_tot = l_run + __shfl_xor(l_run, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  const double inv = 1.0 / l_tot;
+  const int qi = q0 + wave * QW + r16;
+  if (qi >= len) return;
+  // lane holds O^T[dim b*16 + 4i + g][query r16]
+  float* op = o + static_cast<size_t>(s0 + qi) * H * HD + static_cast<size_t>(h) * HD;
+#pragma unroll
+  for (int b = 0; b < NDB; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) op[b * 16 + 4 * i + g] = static_cast<float>(acc[b][i] * inv);
 }
 
 bool attention_supported(bool bf16, int hd) {
@@ -447,6 +478,7 @@ hipError_t attention_f32(int N, int H, int hd, int n_docs, const int32_t* cu, in
   LaunchScope scope_(kCntAttnF32, s);
   const double scale = 1.0 / sqrt(static_cast<double>(hd));
   dim3 grid((max_seqlen + af::QT - 1) / af::QT, H, n_docs);
+  if (grid.y > 65535 || grid.z > 65535) return hipErrorInvalidValue;
   switch (hd) {
     case 32: hipLaunchKernelGGL(attention_f32_kernel<32>, grid, dim3(af::NT), 0, s, N, H, cu, q, k, v, o, scale); break;
     case 64: hipLaunchKernelGGL(attention_f32_kernel<64>, grid, dim3(af::NT), 0, s, N, H, cu, q, k, v, o, scale); break;
