@@ -320,15 +320,16 @@ __global__ __launch_bounds__(ab::NT, 1) void attention_bf16_kernel(int N, int H,
 // which fp32 dot products over the head dim do not meet.  The products run on
 // v_mfma_f64_16x16x4_f64 (fp32 operands are exact in fp64).
 //
-// Workgroup = one (document, head, 64-query tile); four wavefronts of 16
-// queries; 64-key K/V tiles in LDS (fp32, rows padded so the operand reads
-// are bank-conflict free).  Scores are formed transposed, S^T = K Q^T: lane l
-// then holds 4 keys (4i + l/16 of a 16-key block) of query l%16, which is
-// exactly the B operand layout of O^T += V^T P^T, so the probabilities never
-// leave registers; the row max and sum reduce over i in the lane and over the
-// four lanes l%16 + 16g.
+// Workgroup = one (document, head, 16-query tile); its four wavefronts split
+// every 64-key K/V tile (fp32 in LDS, rows padded so the operand reads are
+// bank-conflict free) into 16-key blocks, one each, and keep their own online
+// softmax; the four partial results are merged through LDS at the end.
+// Scores are formed transposed, S^T = K Q^T: lane l then holds 4 keys
+// (4i + l/16 of the block) of query l%16, which is exactly the B operand
+// layout of O^T += V^T P^T, so the probabilities never leave registers; the
+// row max and sum reduce over i in the lane and over the lanes l%16 + 16g.
 namespace af {
-constexpr int QW = 16, NW = 4, QT = QW * NW, KT = 64, NT = NW * 64;
+constexpr int QT = 16, NW = 4, KT = 16 * NW, NT = NW * 64;
 }
 
 template <int HD>
@@ -341,9 +342,13 @@ __global__ __launch_bounds__(af::NT) void attention_f32_kernel(int N, int H, con
   constexpr int KS = HD + 4;    // Q/K row stride (floats): 16 rows x 4 columns hit 64 distinct banks
   constexpr int VS = HD + 16;   // V row stride: 4 rows x 16 columns hit 64 distinct banks
   constexpr int NDB = HD / 16;  // 16-dim output blocks
+  constexpr int F4 = HD / 4;    // float4 per row
+  constexpr int KV_FLOATS = KT * (KS + VS);
+  static_assert(KV_FLOATS >= NW * QT * (HD + 2) * 2, "the merge reuses the K/V tile space");
   __shared__ float Qs[QT * KS];
-  __shared__ float Ks[KT * KS];
-  __shared__ float Vs[KT * VS];
+  __shared__ __align__(16) float KVs[KV_FLOATS];
+  float* Ks = KVs;
+  float* Vs = KVs + KT * KS;
   const int qt = blockIdx.x, h = blockIdx.y, d = blockIdx.z;
   const int s0 = cu[d], len = cu[d + 1] - s0;
   const int q0 = qt * QT;
@@ -352,7 +357,6 @@ __global__ __launch_bounds__(af::NT) void attention_f32_kernel(int N, int H, con
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;
   const size_t base = (static_cast<size_t>(h) * N + s0) * HD;
-  constexpr int F4 = HD / 4;  // float4 per row
 
   for (int i = tid; i < QT * F4; i += NT) {
     const int r = i / F4, c = i % F4;
@@ -361,11 +365,10 @@ __global__ __launch_bounds__(af::NT) void attention_f32_kernel(int N, int H, con
     *reinterpret_cast<float4*>(&Qs[r * KS + 4 * c]) = t;
   }
   __syncthreads();
-  // Q^T operand: lane holds Q[query wave*16 + r16][dim 4 ks + g]
+  // Q^T operand: lane holds Q[query r16][dim 4 ks + g]
   double qf[HD / 4];
 #pragma unroll
-  for (int ks = 0; ks < HD / 4; ++ks) qf[ks] = static_cast<double>(Qs[(wave * QW + r16) * KS + 4 * ks + g]);
-  const bool active = q0 + wave * QW < len;  // this wavefront has a query in the document
+  for (int ks = 0; ks < HD / 4; ++ks) qf[ks] = static_cast<double>(Qs[r16 * KS + 4 * ks + g]);
 
   f64x4_t acc[NDB];
 #pragma unroll
@@ -388,27 +391,20 @@ __global__ __launch_bounds__(af::NT) void attention_f32_kernel(int N, int H, con
       *reinterpret_cast<float4*>(&Vs[r * VS + 4 * c]) = vv;
     }
     __syncthreads();
-    if (!active) continue;
-    const int nkb = (len - k0) >= KT ? KT / 16 : (len - k0 + 15) / 16;  // 16-key blocks holding keys
-    // S^T blocks: lane holds keys kb*16 + 4i + g of query r16
-    f64x4_t sblk[KT / 16];
+    const int kb0 = wave * 16;  // this wavefront's key block
+    if (k0 + kb0 >= len) continue;
+    // S^T block: lane holds keys kb0 + 4i + g of query r16
+    f64x4_t sb = f64x4_t{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int ks = 0; ks < HD / 4; ++ks)
+      sb = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(Ks[(kb0 + r16) * KS + 4 * ks + g]), qf[ks], sb, 0,
+                                                0, 0);
     double mt = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < KT / 16; ++kb) {
-      sblk[kb] = f64x4_t{0.0, 0.0, 0.0, 0.0};
-      if (kb < nkb) {
-#pragma unroll
-        for (int ks = 0; ks < HD / 4; ++ks)
-          sblk[kb] = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(Ks[(kb * 16 + r16) * KS + 4 * ks + g]),
-                                                         qf[ks], sblk[kb], 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = k0 + kb * 16 + 4 * i + g;
-        const double sc = (kb < nkb && key < len) ? sblk[kb][i] * scale : -INFINITY;
-        sblk[kb][i] = sc;
-        mt = fmax(mt, sc);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const double sc = k0 + kb0 + 4 * i + g < len ? sb[i] * scale : -INFINITY;
+      sb[i] = sc;
+      mt = fmax(mt, sc);
     }
     mt = fmax(mt, __shfl_xor(mt, 16, 64));
     mt = fmax(mt, __shfl_xor(mt, 32, 64));
@@ -421,35 +417,54 @@ __global__ __launch_bounds__(af::NT) void attention_f32_kernel(int N, int H, con
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[b][i] *= alpha;
 #pragma unroll
-    for (int kb = 0; kb < KT / 16; ++kb) {
-      if (kb >= nkb) break;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const double p = exp(sblk[kb][i] - m_new);  // exp(-inf) = 0 for masked keys
-        sblk[kb][i] = p;
-        l_run += p;
-      }
-      // O^T += V^T P^T over this block's keys 4ks + g: B operand = p of slot ks
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int b = 0; b < NDB; ++b)
-          acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(
-              static_cast<double>(Vs[(kb * 16 + 4 * ks + g) * VS + b * 16 + r16]), sblk[kb][ks], acc[b], 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      const double p = exp(sb[i] - m_new);  // exp(-inf) = 0 for keys past the end
+      sb[i] = p;
+      l_run += p;
     }
+    // O^T += V^T P^T over the block's keys 4ks + g: B operand = p of slot ks
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int b = 0; b < NDB; ++b)
+        acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(Vs[(kb0 + 4 * ks + g) * VS + b * 16 + r16]),
+                                                      sb[ks], acc[b], 0, 0, 0);
   }
-  if (!active) return;
-  double l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  const double inv = 1.0 / l_tot;
-  const int qi = q0 + wave * QW + r16;
-  if (qi >= len) return;
-  // lane holds O^T[dim b*16 + 4i + g][query r16]
-  float* op = o + static_cast<size_t>(s0 + qi) * H * HD + static_cast<size_t>(h) * HD;
+
+  // Merge the four wavefronts: m, l per query and O^T per (dim, query) go to
+  // LDS; then thread t writes outputs (query, dim) = t + 256 j, dims fastest.
+  double l_w = l_run + __shfl_xor(l_run, 16, 64);
+  l_w += __shfl_xor(l_w, 32, 64);
+  __syncthreads();  // K/V space free
+  double* mw = reinterpret_cast<double*>(KVs);       // [NW][QT]
+  double* lw = mw + NW * QT;                          // [NW][QT]
+  double* ow = lw + NW * QT;                          // [NW][HD][QT]
+  if (g == 0) {
+    mw[wave * QT + r16] = m_run;
+    lw[wave * QT + r16] = l_w;
+  }
 #pragma unroll
   for (int b = 0; b < NDB; ++b)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) op[b * 16 + 4 * i + g] = static_cast<float>(acc[b][i] * inv);
+    for (int i = 0; i < 4; ++i) ow[(wave * HD + b * 16 + 4 * i + g) * QT + r16] = acc[b][i];
+  __syncthreads();
+  for (int idx = tid; idx < QT * HD; idx += NT) {
+    const int qq = idx / HD, dim = idx % HD;
+    if (q0 + qq >= len) continue;
+    double m = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) m = fmax(m, mw[w * QT + qq]);
+    double num = 0.0, den = 0.0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const double mwq = mw[w * QT + qq];
+      if (mwq == -INFINITY) continue;  // a wavefront that saw no key of the document
+      const double f = exp(mwq - m);
+      num += f * ow[(w * HD + dim) * QT + qq];
+      den += f * lw[w * QT + qq];
+    }
+    o[static_cast<size_t>(s0 + q0 + qq) * H * HD + static_cast<size_t>(h) * HD + dim] = static_cast<float>(num / den);
+  }
 }
 
 bool attention_supported(bool bf16, int hd) {
