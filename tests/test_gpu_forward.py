@@ -192,3 +192,25 @@ def test_denoise_loop_matches_steps_and_oracle(H):
         # compare the distance travelled (latent - noise), the part the model computed
         x0 = r.inp[k].astype(np.float64)
         assert_bf16_parity(got[k] - x0, ref[k] - x0, ctl[k] - x0, f"denoise {cfg.denoise_steps} steps {k}")
+
+
+@pytest.mark.parametrize("name", ["c1", "c2_2blocks"])
+def test_graph_replay_matches_eager(H, name):
+    """One forward captured as a HIP graph and replayed three times, with eager
+    forwards and synchronisations between the replays: every replay equals the
+    eager output bit for bit (the forward launches no memset or allocation)."""
+    cfg = S.get_config("c1") if name == "c1" else scaled(S.get_config("c2"), n_blocks=2)
+    r, w, _ = _run(H, cfg)
+    eager = r.forward().clone()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        r.forward()
+    for _ in range(3):
+        r.out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(r.out, eager)
+        again = r.forward().clone()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(again, eager)
