@@ -44,6 +44,35 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def _source_digest(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+KERNEL_SOURCE = {"gemm_f32": "video_audio_gen_amd/csrc/gemm.hip", "gemm_bf16": "video_audio_gen_amd/csrc/gemm.hip",
+                 "attention_bf16": "video_audio_gen_amd/csrc/attention.hip"}
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain
+    copy's reading), or None when there is none or the kernel's source has
+    changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    src = KERNEL_SOURCE.get(kernel)
+    if src is None or not os.path.exists(path):
+        return None
+    rec = None
+    with open(path) as f:
+        for ln in f:
+            if ln.startswith("traffic_json: "):
+                rec = json.loads(ln[len("traffic_json: "):])
+    if rec is None or rec.get("source_sha256_16") != _source_digest(os.path.join(ROOT, src)):
+        return None
+    return rec.get("bytes_per_launch")
+
+
 def gemm_shapes(cfg, blocks=True, islands=True):
     """(M, N, K) of the GEMM launches of one forward, in launch order."""
     N = cfg.n_tokens
@@ -131,6 +160,9 @@ def main(argv=None):
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-blocks", type=int, default=4)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device-to-device five times (the known-size kernel that scales "
+                         "the FETCH_SIZE / WRITE_SIZE counters), then exit")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch every kernel from the host instead of replaying one captured HIP graph")
     a = ap.parse_args(argv)
@@ -141,6 +173,16 @@ def main(argv=None):
 
     import numpy as np
     import torch
+
+    if a.copy_calibration:
+        n = a.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {a.copy_calibration} MiB x 5")
+        return 0
 
     import synthetic as S
     from video_audio_gen_amd import dit, harness
@@ -236,6 +278,7 @@ def main(argv=None):
     else:
         roof = {"bound": "unknown", "achieved": None, "peak": None, "unit": None, "frac": None,
                 "traffic": None, "kernel": fam}
+    roof["traffic"] = measured_traffic(fam, cfg.name)
 
     cpu = None
     if not a.no_cpu_baseline:
