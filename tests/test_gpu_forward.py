@@ -214,3 +214,22 @@ def test_graph_replay_matches_eager(H, name):
         again = r.forward().clone()  # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(again, eager)
+
+
+def test_c3_full_size_sampled_parity(H):
+    """The single 6144-wide bf16 block at its full size (24,576 video + 2,048
+    audio tokens) against stored oracle values at 4,096 seeded positions
+    (tests/golden/make_samples.py runs the oracle and its fp32-accumulation
+    control arm on the CPU; nothing there comes from the GPU)."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "c3_block_bf16_samples.json")
+    gold = json.load(open(path))
+    cfg = S.get_config("c3")
+    assert gold["config"] == cfg.name
+    r, w, got = _run(H, cfg)
+    t = gold["tensors"]["x"]
+    assert list(got["x"].shape) == t["shape"]
+    idx = np.array(t["index"])
+    g = got["x"].reshape(-1)[idx]
+    assert_bf16_parity(g, np.array(t["value"]), np.array(t["control_value"]), "c3 full size (sampled)")
