@@ -60,6 +60,13 @@ static_assert(gb::CPR == 4 || gb::CPR == 8, "tile rows of 4 or 8 16-byte chunks"
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// Workgroup barrier without the memory fence of __syncthreads(): LDS written
+// by direct loads is covered by explicit vmcnt waits before it (the fence
+// would add vmcnt(0), i.e. also wait for the copies just issued for later
+// tiles), and the "memory" clobber keeps the compiler from moving LDS reads
+// across it.
+__device__ __forceinline__ void go_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 // Tiles move HBM -> LDS with buffer_load_dwordx4 ... lds (no VGPR staging, no
 // ds_write): lane l of one instruction writes its 16 bytes at LDS base + 16*l,
 // and a read past the buffer's num_records returns zero, which pads the M and N
@@ -85,7 +92,8 @@ __global__ __launch_bounds__(gb::NT) void gemm_bf16_kernel(int M, int N, int K,
   const int m0 = tm * BM, n0 = tn * BN;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = (wave / (BN / WN)) * WM, wc = (wave % (BN / WN)) * WN;
 
   const int a_rows = M - m0 < BM ? M - m0 : BM;
@@ -173,7 +181,7 @@ __global__ __launch_bounds__(gb::NT) void gemm_bf16_kernel(int M, int N, int K,
     else
       __builtin_amdgcn_s_waitcnt(GB_VMCNT(0));
 #undef GB_VMCNT
-    __syncthreads();  // every wave's part of tile kt is in LDS; stage (kt-1) is free
+    go_barrier();  // every wave's part of tile kt is in LDS; stage (kt-1) is free
     if (kt + STAGES - 1 < KT) GB_DMA((kt + STAGES - 1) % STAGES, (kt + STAGES - 1) * BK)
     GB_COMPUTE(st)
     // Inside the block: the operand reads of k-step 0, then in each k-step the
@@ -265,10 +273,6 @@ constexpr int DMA_MAX = (NDMA + NW - 1) / NW;  // per wave: 4 (waves 0-3) or 3
 constexpr int KSPLIT_MAX = 16384;
 }  // namespace go
 
-// Workgroup barrier without the memory fence of __syncthreads(): LDS written
-// by direct loads is covered by the explicit vmcnt waits before it, and the
-// "memory" clobber keeps the compiler from moving LDS reads across it.
-__device__ __forceinline__ void go_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // s_waitcnt vmcnt(n) for a run-time n (larger n waits for the n = 7 case).
 __device__ __forceinline__ void go_wait_vm(int n) {
