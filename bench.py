@@ -90,11 +90,14 @@ def gemm_shapes(cfg, blocks=True, islands=True):
     return out
 
 
-def family_work(cfg):
+def family_work(cfg, splits=None):
     """Algorithmic work of one forward per kernel family: (amount, unit).
 
     GEMM and attention count flops (2MNK; 4*hd*H*sum L_d^2); the bandwidth-bound
-    kernels count the bytes they must move once (inputs read + outputs written)."""
+    kernels count the bytes they must move once (inputs read + outputs written).
+    In the fp32 stream a GEMM result reaches the row kernel after it as
+    `splits(n, k)` fp64 split-K partials, which that kernel must read; int8
+    slices are 5 bytes per value."""
     N, D, F, H, hd = cfg.n_tokens, cfg.hidden, cfg.ffn, cfg.n_heads, cfg.head_dim
     es = 2 if cfg.stream == "bf16" else 4
     L = cfg.n_blocks
@@ -113,6 +116,25 @@ def family_work(cfg):
         "gated_residual": (L * 2 * N * D * 12, "byte"),
         "adaln": (L * cfg.n_mod * 6 * D * cfg.cond_dim * w_es, "byte"),
     }
+    if cfg.stream == "f32" and splits is not None:
+        s_qkv, s_o, s_in, s_out = splits(3 * D, D), splits(D, D), splits(2 * F, D), splits(D, F)
+        nd = N * D
+        # rope_part: partials of q|k|v in, q, k, v out, cos/sin rows
+        out["rope_split"] = (L * (s_qkv * 3 * nd * 8 + 3 * nd * 4 + N * cfg.rot_dim * 4), "byte")
+        # residual (fp64) read + written, partials in, slices out; the prologue
+        # reads x and slices it; with io the last one stores the fp32 norm instead
+        rn = L * ((s_o + s_out) * nd * 8 + 2 * 16 * nd + 2 * 5 * nd) + (8 * nd + 5 * nd if L else 0)
+        out["resid_norm_slice"] = (rn, "byte")
+        out["silu_slice"] = (L * (s_in * 2 * N * F * 8 + 5 * N * F), "byte")
+        # slice_rows of each attention output (fp32 in, slices out); the residual
+        # widened on entry and, without io, narrowed on exit; with io the slices
+        # of the in-projection's tokens and of the final norm
+        conv = L * 9 * nd + 12 * nd
+        if cfg.io:
+            conv += 9 * nd + sum(9 * sg.n_tokens * cfg.modalities[sg.modality].token_width for sg in cfg.segments)
+        else:
+            conv += 12 * nd
+        out["convert"] = (conv, "byte")
     return out
 
 
@@ -241,7 +263,7 @@ def main(argv=None):
         if n:
             log(f"  {k:16s} launches {n:6d}  total {t:9.3f} ms  avg {t / n * 1e3:9.2f} us  "
                 f"share {t / total_dev * 100:5.1f}%")
-    work = family_work(cfg)
+    work = family_work(cfg, dit.dit_gemm_splits if cfg.stream == "f32" else None)
     kernels = {}
     for k, (n, t) in prof.items():
         if not n:

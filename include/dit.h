@@ -260,6 +260,11 @@ int dit_denoise_loop(dit_model* m, const dit_batch* b, float* latents_dev,
  * rounded once to float32 C.  ws holds B's and A's slices and split-K
  * partials (dit_gemm_workspace_bytes). */
 int dit_gemm_workspace_bytes(int dtype, int M, int N, int K, size_t* bytes);
+/* Split-K count of the fp32 GEMM for an [N, K] weight on the current device:
+ * the number of fp64 partials [splits][M][N] that the block's fp32 GEMMs hand
+ * to the row kernel after them (chosen from N, K and the compute-unit count
+ * only, so a row's result never depends on M).  dtype must be DIT_F32. */
+int dit_gemm_splits(int dtype, int N, int K, int* splits);
 int dit_gemm(int dtype, int M, int N, int K, const void* A, const void* B, const float* bias,
              void* C, int c_dtype, void* ws, size_t ws_bytes, dit_stream_t stream);
 
@@ -296,7 +301,7 @@ int dit_gated_residual(int N, int D, void* x, int x_dtype, const float* a, const
 const char* dit_last_error(void);
 /* Launch counters per kernel family (index order: gemm_bf16, gemm_f32, attention_bf16,
  * attention_f32, modnorm, rope_split, silu_gate, gated_residual, adaln, patch_in,
- * patch_out, euler, gemm_f32_reduce, convert); n_max entries written; returns DIT_OK. */
+ * patch_out, euler, gemm_f32_reduce, convert, resid_norm_slice, silu_slice); n_max entries written; returns DIT_OK. */
 int dit_counters(int64_t* out, int n_max);
 void dit_counters_reset(void);
 

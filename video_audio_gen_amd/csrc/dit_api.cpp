@@ -70,7 +70,8 @@ LaunchScope::LaunchScope(Counter c, hipStream_t s) : slot_(-1), s_(s) {
 LaunchScope::~LaunchScope() {
   if (slot_ < 0) return;
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  hipEventRecord(g_events[g_prof[slot_].ev1], s_);
+  // a failed record leaves the end event unrecorded: dit_profile_end reports it
+  (void)hipEventRecord(g_events[g_prof[slot_].ev1], s_);
 }
 
 static bool sync_check_enabled() {
@@ -156,8 +157,8 @@ static int check_config(const dit_config* c) {
     return set_error(DIT_E_UNSUPPORTED, "head_dim %d not supported by the %s attention kernel", c->head_dim, bf ? "bf16" : "f32");
   if (bf) {
     if (c->hidden % 64 || c->ffn % 64) return set_error(DIT_E_UNSUPPORTED, "bf16 stream needs hidden and ffn multiples of 64");
-  } else if (c->ffn % 4) {
-    return set_error(DIT_E_UNSUPPORTED, "ffn must be a multiple of 4");
+  } else if (!fused_f32_supported(c->hidden, c->ffn)) {
+    return set_error(DIT_E_UNSUPPORTED, "fp32 stream needs ffn a multiple of 4 and <= 32768");
   }
   if (c->cond_dim % 4) return set_error(DIT_E_UNSUPPORTED, "cond_dim must be a multiple of 4");
   return DIT_OK;
@@ -559,7 +560,7 @@ extern "C" int dit_batch_tables(const dit_batch* b, const int32_t** cu, const in
 // ============================================================================ workspace plan
 
 struct WsPlan {
-  size_t mod, x, h, big, qkvh, o, a, gemm, tok, vtok, vel, total;
+  size_t mod, x, h, big, qkvh, o, a, sl, gemm, tok, vtok, vel, total;
 };
 
 static size_t gemm_ws(const dit_config& c, int M, int N, int K) {
@@ -580,18 +581,29 @@ static WsPlan plan_ws(const dit_model* m, const dit_batch* b) {
   p.mod = take(sizeof(float) * c.n_blocks * b->n_cond * 6 * D);
   // residual stream: float32 (bf16 stream, with io) or float64 (fp32 stream)
   p.x = take(c.stream_dtype == DIT_BF16 ? (c.io ? sizeof(float) * N * D : 0) : sizeof(double) * N * D);
-  p.h = take(es * N * D);
-  p.big = take(es * N * (3 * D > 2 * F ? 3 * D : 2 * F));
+  const bool bf = c.stream_dtype == DIT_BF16;
+  p.h = take(bf ? es * N * D : 0);
+  p.big = take(bf ? es * N * (3 * D > 2 * F ? 3 * D : 2 * F) : 0);
   p.qkvh = take(es * N * (3 * D > F ? 3 * D : F));
   p.o = take(es * N * D);
   p.a = take(sizeof(float) * N * D);
+  const int Ni = static_cast<int>(N);
+  const bool f32 = !bf;
+  // fp32 stream: the int8 slices of the next GEMM's input (K = D or F)
+  p.sl = take(f32 ? gemm_f32_slices_bytes(Ni, static_cast<int>(D > F ? D : F)) : 0);
   size_t g = 0;
   auto upd = [&](size_t v) { g = v > g ? v : g; };
-  const int Ni = static_cast<int>(N);
-  upd(gemm_ws(c, Ni, 3 * D, D));
-  upd(gemm_ws(c, Ni, D, D));
-  upd(gemm_ws(c, Ni, 2 * F, D));
-  upd(gemm_ws(c, Ni, D, F));
+  if (f32) {  // fp64 split-K partials of the block GEMMs
+    upd(gemm_f32_part_bytes(Ni, 3 * D, D));
+    upd(gemm_f32_part_bytes(Ni, D, D));
+    upd(gemm_f32_part_bytes(Ni, 2 * F, D));
+    upd(gemm_f32_part_bytes(Ni, D, F));
+  } else {
+    upd(gemm_ws(c, Ni, 3 * D, D));
+    upd(gemm_ws(c, Ni, D, D));
+    upd(gemm_ws(c, Ni, 2 * F, D));
+    upd(gemm_ws(c, Ni, D, F));
+  }
   size_t tok = 0;
   if (c.io) {
     for (int mm = 0; mm < c.n_mod; ++mm) {
@@ -630,49 +642,78 @@ static int check_run(const dit_model* m, const dit_batch* b, void* ws, size_t ws
   return DIT_OK;
 }
 
-static hipError_t launch_gemm(const dit_config& c, int M, int N, int K, const void* A, const void* W,
-                              const float* bias, void* C, bool c_f32, void* ws, hipStream_t s) {
-  if (c.stream_dtype == DIT_BF16)
-    return gemm_bf16(M, N, K, static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W), bias, C, c_f32, ws, s);
-  return gemm_f32(M, N, K, static_cast<const float*>(A), W, bias, static_cast<float*>(C), ws, s);
-}
-
-// x: the residual stream, float32 for a bf16 stream, float64 for an fp32 one.
-static int run_block(dit_model* m, int blk, void* x, const float* mod, const dit_batch* b, char* ws,
-                     const WsPlan& p, hipStream_t s) {
+// bf16 stream: x is the float32 residual.
+static int run_block_bf16(dit_model* m, int blk, float* x, const float* mod, const dit_batch* b, char* ws,
+                          const WsPlan& p, hipStream_t s) {
   const dit_config& c = m->cfg;
   const BlockPtrs& w = m->blocks[blk];
   const int N = b->N, D = c.hidden, F = c.ffn, H = c.n_heads, hd = c.head_dim;
-  const bool bf = c.stream_dtype == DIT_BF16;
-  const size_t es = bf ? 2 : 4;
-  void* h = ws + p.h;
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws + p.h);
   void* big = ws + p.big;
-  char* qkvh = ws + p.qkvh;
-  void* o = ws + p.o;
+  uint16_t* qkvh = reinterpret_cast<uint16_t*>(ws + p.qkvh);
+  uint16_t* o = reinterpret_cast<uint16_t*>(ws + p.o);
   float* a = reinterpret_cast<float*>(ws + p.a);
   void* gws = ws + p.gemm;
-  void* q = qkvh;
-  void* k = qkvh + es * N * D;
-  void* v = qkvh + 2 * es * N * D;
+  uint16_t* q = qkvh;
+  uint16_t* k = qkvh + static_cast<size_t>(N) * D;
+  uint16_t* v = qkvh + 2 * static_cast<size_t>(N) * D;
+  auto gemm = [&](int n, int kk, const void* A, const void* W, const float* bias, void* C, bool c_f32) {
+    return gemm_bf16(N, n, kk, static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W), bias, C, c_f32, gws, s);
+  };
   // attention sub-layer
-  const bool x64 = !bf;
-  DIT_HIP(modnorm(bf, c.norm, c.norm_eps, N, D, x64, x, mod, 0, b->cond_dev, h, s));
-  DIT_HIP(launch_gemm(c, N, 3 * D, D, h, w.qkv_w, w.qkv_b, big, false, gws, s));
-  DIT_HIP(rope_split(bf, N, H, hd, c.rot_dim, big, b->cos_dev, b->sin_dev, q, k, v, s));
-  if (bf)
-    DIT_HIP(attention_bf16(N, H, hd, b->n_segs, b->cu_dev, b->max_seqlen, static_cast<const uint16_t*>(q),
-                           static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), s));
-  else
-    DIT_HIP(attention_f32(N, H, hd, b->n_segs, b->cu_dev, b->max_seqlen, static_cast<const float*>(q),
-                          static_cast<const float*>(k), static_cast<const float*>(v), static_cast<float*>(o), s));
-  DIT_HIP(launch_gemm(c, N, D, D, o, w.out_w, w.out_b, a, true, gws, s));
-  DIT_HIP(gated_residual(N, D, x64, x, a, mod, 0, b->cond_dev, s));
+  DIT_HIP(modnorm(true, c.norm, c.norm_eps, N, D, false, x, mod, 0, b->cond_dev, h, s));
+  DIT_HIP(gemm(3 * D, D, h, w.qkv_w, w.qkv_b, big, false));
+  DIT_HIP(rope_split(true, N, H, hd, c.rot_dim, big, b->cos_dev, b->sin_dev, q, k, v, s));
+  DIT_HIP(attention_bf16(N, H, hd, b->n_segs, b->cu_dev, b->max_seqlen, q, k, v, o, s));
+  DIT_HIP(gemm(D, D, o, w.out_w, w.out_b, a, true));
+  DIT_HIP(gated_residual(N, D, false, x, a, mod, 0, b->cond_dev, s));
   // MLP sub-layer
-  DIT_HIP(modnorm(bf, c.norm, c.norm_eps, N, D, x64, x, mod, 1, b->cond_dev, h, s));
-  DIT_HIP(launch_gemm(c, N, 2 * F, D, h, w.in_w, w.in_b, big, false, gws, s));
-  DIT_HIP(silu_gate(bf, N, F, big, qkvh, s));
-  DIT_HIP(launch_gemm(c, N, D, F, qkvh, w.mo_w, w.mo_b, a, true, gws, s));
-  DIT_HIP(gated_residual(N, D, x64, x, a, mod, 1, b->cond_dev, s));
+  DIT_HIP(modnorm(true, c.norm, c.norm_eps, N, D, false, x, mod, 1, b->cond_dev, h, s));
+  DIT_HIP(gemm(2 * F, D, h, w.in_w, w.in_b, big, false));
+  DIT_HIP(silu_gate(true, N, F, big, qkvh, s));
+  DIT_HIP(gemm(D, F, qkvh, w.mo_w, w.mo_b, a, true));
+  DIT_HIP(gated_residual(N, D, false, x, a, mod, 1, b->cond_dev, s));
+  return DIT_OK;
+}
+
+// fp32 stream, x the float64 residual.  Each GEMM reads its input as int8
+// slices and leaves fp64 split-K partials that the next row kernel sums:
+//   (slices of the attention norm, made by the previous block or f32_prologue)
+//   QKV GEMM -> rope_part -> attention -> slice_rows -> O GEMM ->
+//   resid_norm_slice (gate MSA, MLP norm) -> in GEMM -> silu_slice -> out GEMM ->
+//   resid_norm_slice (gate MLP, then next_mod's attention norm sliced, or
+//   the plain final norm into y, or nothing)
+static int f32_prologue(const dit_model* m, double* x, const float* mod, const dit_batch* b, char* ws,
+                        const WsPlan& p, hipStream_t s) {
+  const dit_config& c = m->cfg;
+  DIT_HIP(resid_norm_slice(b->N, c.hidden, 0, nullptr, nullptr, nullptr, 0, mod, 0, c.norm, c.norm_eps, b->cond_dev, x,
+                           ws + p.sl, nullptr, s));
+  return DIT_OK;
+}
+
+static int run_block_f32(dit_model* m, int blk, double* x, const float* mod, const float* next_mod, float* y,
+                         const dit_batch* b, char* ws, const WsPlan& p, hipStream_t s) {
+  const dit_config& c = m->cfg;
+  const BlockPtrs& w = m->blocks[blk];
+  const int N = b->N, D = c.hidden, F = c.ffn, H = c.n_heads, hd = c.head_dim;
+  void* sl = ws + p.sl;
+  double* part = reinterpret_cast<double*>(ws + p.gemm);
+  float* q = reinterpret_cast<float*>(ws + p.qkvh);
+  float* k = q + static_cast<size_t>(N) * D;
+  float* v = k + static_cast<size_t>(N) * D;
+  float* o = reinterpret_cast<float*>(ws + p.o);
+  DIT_HIP(gemm_f32_sliced(N, 3 * D, D, sl, w.qkv_w, part, s));
+  DIT_HIP(rope_part(N, H, hd, c.rot_dim, gemm_f32_splits(3 * D, D), part, w.qkv_b, b->cos_dev, b->sin_dev, q, k, v, s));
+  DIT_HIP(attention_f32(N, H, hd, b->n_segs, b->cu_dev, b->max_seqlen, q, k, v, o, s));
+  DIT_HIP(slice_rows(N, D, o, sl, s));
+  DIT_HIP(gemm_f32_sliced(N, D, D, sl, w.out_w, part, s));
+  DIT_HIP(resid_norm_slice(N, D, gemm_f32_splits(D, D), part, w.out_b, mod, 0, mod, 1, c.norm, c.norm_eps, b->cond_dev, x,
+                           sl, nullptr, s));
+  DIT_HIP(gemm_f32_sliced(N, 2 * F, D, sl, w.in_w, part, s));
+  DIT_HIP(silu_slice(N, F, gemm_f32_splits(2 * F, D), part, w.in_b, sl, s));
+  DIT_HIP(gemm_f32_sliced(N, D, F, sl, w.mo_w, part, s));
+  DIT_HIP(resid_norm_slice(N, D, gemm_f32_splits(D, F), part, w.mo_b, mod, 1, next_mod, 0, c.norm, c.norm_eps,
+                           b->cond_dev, x, next_mod != nullptr ? sl : nullptr, y, s));
   return DIT_OK;
 }
 
@@ -709,11 +750,12 @@ extern "C" int dit_block_forward(dit_model* m, int block, float* x_dev, const fl
   if (x_dev == nullptr || mod_dev == nullptr) return set_error(DIT_E_INVALID, "dit_block_forward: x or mod is null");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(ws_dev);
-  if (m->cfg.stream_dtype == DIT_BF16) return run_block(m, block, x_dev, mod_dev, b, ws, p, s);
+  if (m->cfg.stream_dtype == DIT_BF16) return run_block_bf16(m, block, x_dev, mod_dev, b, ws, p, s);
   const int64_t n = static_cast<int64_t>(b->N) * m->cfg.hidden;
   double* x64 = reinterpret_cast<double*>(ws + p.x);
   DIT_HIP(widen_f32(n, x_dev, x64, s));
-  DIT_TRY(run_block(m, block, x64, mod_dev, b, ws, p, s));
+  DIT_TRY(f32_prologue(m, x64, mod_dev, b, ws, p, s));
+  DIT_TRY(run_block_f32(m, block, x64, mod_dev, nullptr, nullptr, b, ws, p, s));
   DIT_HIP(narrow_f64(n, x64, x_dev, s));
   return DIT_OK;
 }
@@ -750,16 +792,25 @@ static int run_forward(dit_model* m, const dit_batch* b, const float* in, const 
     x = out;
     if (in != out) DIT_HIP(hipMemcpyAsync(out, in, sizeof(float) * N * D, hipMemcpyDeviceToDevice, s));
   }
-  for (int blk = 0; blk < c.n_blocks; ++blk) {
-    const float* mb = mod + static_cast<size_t>(blk) * b->n_cond * 6 * D;
-    DIT_TRY(run_block(m, blk, x, mb, b, ws, p, s));
+  const size_t mod_stride = static_cast<size_t>(b->n_cond) * 6 * D;
+  float* y = reinterpret_cast<float*>(ws + p.a);  // final norm, fp32
+  const int L = c.n_blocks;
+  if (x64) {
+    // the last block's closing kernel also writes the final norm (with io)
+    double* xd = static_cast<double*>(x);
+    if (L > 0) DIT_TRY(f32_prologue(m, xd, mod, b, ws, p, s));
+    for (int blk = 0; blk < L; ++blk)
+      DIT_TRY(run_block_f32(m, blk, xd, mod + blk * mod_stride, blk + 1 < L ? mod + (blk + 1) * mod_stride : nullptr,
+                            blk + 1 == L && c.io ? y : nullptr, b, ws, p, s));
+  } else {
+    for (int blk = 0; blk < L; ++blk)
+      DIT_TRY(run_block_bf16(m, blk, static_cast<float*>(x), mod + blk * mod_stride, b, ws, p, s));
   }
   if (!c.io) {
     if (x64) DIT_HIP(narrow_f64(nd, static_cast<const double*>(x), out, s));
     return DIT_OK;
   }
-  float* y = reinterpret_cast<float*>(ws + p.a);  // final norm, fp32
-  DIT_HIP(modnorm(false, c.norm, c.norm_eps, N, D, x64, x, nullptr, 0, nullptr, y, s));
+  if (!x64 || L == 0) DIT_HIP(modnorm(false, c.norm, c.norm_eps, N, D, x64, x, nullptr, 0, nullptr, y, s));
   float* vtok = reinterpret_cast<float*>(ws + p.vtok);
   for (int i = 0; i < b->n_segs; ++i) {
     const dit_segment& sg = b->segs[i];
@@ -822,6 +873,12 @@ extern "C" int dit_denoise_loop(dit_model* m, const dit_batch* b, float* latents
 }
 
 // ============================================================================ op-level calls
+
+extern "C" int dit_gemm_splits(int dtype, int N, int K, int* splits) {
+  if (splits == nullptr || dtype != DIT_F32 || N <= 0 || K <= 0) return set_error(DIT_E_INVALID, "dit_gemm_splits: bad argument");
+  *splits = gemm_f32_splits(N, K);
+  return DIT_OK;
+}
 
 extern "C" int dit_gemm_workspace_bytes(int dtype, int M, int N, int K, size_t* bytes) {
   if (bytes == nullptr || M < 0 || N <= 0 || K <= 0) return set_error(DIT_E_INVALID, "dit_gemm_workspace_bytes: bad argument");

@@ -1,0 +1,358 @@
+// Row kernels that join the fp32 stream's GEMMs.  An fp32 GEMM of the block
+// leaves fp64 split-K partials; the kernel after it sums them in split order,
+// adds the bias and rounds once to fp32 (the value a stand-alone reduction
+// would store), applies its own operation and, where the next GEMM reads the
+// result, cuts that GEMM's int8 slices directly (slices.h).  A block then runs
+// 11 launches instead of 17, and the fp32 GEMM outputs, the modulated norms
+// and the SiLU product never make a round trip through HBM as fp32.
+//
+//   resid_norm_slice  x += gate * a (fp64 residual), then the AdaLN-modulated
+//                     norm of the next sub-layer, sliced; or the plain final
+//                     norm as fp32; or the residual update alone
+//   rope_part         RoPE + QKV split of the QKV projection
+//   silu_slice        SiLU gate of the MLP input projection, sliced
+//
+// Pages: "port the MiniMax-H3 omni-modal video+audio DiT", section "The
+// device-resident forward (W2b)" (indexed AdaLN modulate, NeoX rotate_half
+// from a per-row cos/sin cache, gated Add); "the 2.4B fp32 DiT onto the
+// device", section "What moved" (LayerNorm, partial rotary, SiluAndMul).
+#include "common.h"
+#include "kernels.h"
+#include "slices.h"
+
+namespace dit {
+
+// Columns col..col+3 of row `row` of a GEMM result [M, ncol] held as S fp64
+// split-K partials [S][M][ncol]: summed in split order from zero, bias added
+// last, rounded once.  Groups of four splits are loaded before they are added
+// so their latencies overlap.
+__device__ __forceinline__ void sum_parts4(const double* __restrict__ part, int S, size_t MN, size_t off,
+                                           const float* __restrict__ bias, int col, float* out) {
+  double v0 = 0.0, v1 = 0.0, v2 = 0.0, v3 = 0.0;
+  const double* p = part + off;
+  int s = 0;
+  for (; s + 4 <= S; s += 4) {
+    double2 a[4], b[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      a[u] = reinterpret_cast<const double2*>(p + (s + u) * MN)[0];
+      b[u] = reinterpret_cast<const double2*>(p + (s + u) * MN)[1];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      v0 += a[u].x; v1 += a[u].y; v2 += b[u].x; v3 += b[u].y;
+    }
+  }
+  for (; s < S; ++s) {
+    const double2 a = reinterpret_cast<const double2*>(p + s * MN)[0];
+    const double2 b = reinterpret_cast<const double2*>(p + s * MN)[1];
+    v0 += a.x; v1 += a.y; v2 += b.x; v3 += b.y;
+  }
+  if (bias != nullptr) {
+    const float4 bb = *reinterpret_cast<const float4*>(bias + col);
+    v0 += static_cast<double>(bb.x); v1 += static_cast<double>(bb.y);
+    v2 += static_cast<double>(bb.z); v3 += static_cast<double>(bb.w);
+  }
+  out[0] = static_cast<float>(v0); out[1] = static_cast<float>(v1);
+  out[2] = static_cast<float>(v2); out[3] = static_cast<float>(v3);
+}
+
+template <int NT>
+__device__ __forceinline__ double block_sum(double v, double* red) {
+  v = wave_sum_f64(v);
+  if (NT == 64) return v;
+  __syncthreads();  // red may still be read by the previous reduction
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) t += red[i];
+  return t;
+}
+
+template <int NT>
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  if (NT == 64) return v;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) t = fmaxf(t, red[i]);
+  return t;
+}
+
+// Row max of the four-float chunks a thread holds, then the row's exponent
+// and its slices; chunks between the row's width and the 32-padded width are
+// written as zero slices.
+template <int NT, int NCH>
+__device__ __forceinline__ void slice_row(float (*y)[4], int C4, int row, int R, int K, float* redf, int8_t* sl) {
+  const int t = threadIdx.x;
+  float mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i)
+    if (t + NT * i < C4)
+      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(y[i][0]), fabsf(y[i][1])), fmaxf(fabsf(y[i][2]), fabsf(y[i][3]))));
+  mx = block_max<NT>(mx, redf);
+  const int e = slice_exponent(mx);
+  const int Kp = slice_kp(K);
+  if (t == 0) reinterpret_cast<int32_t*>(sl + slice_exp_offset(R, K))[row] = e;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = t + NT * i;
+    if (c < C4) slice_store4(y[i], e, row, 4 * c, R, Kp, sl);
+  }
+  const float z[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int c = C4 + t; c < Kp / 4; c += NT) slice_store4(z, e, row, 4 * c, R, Kp, sl);
+}
+
+// ============================================================================ residual + norm + slices
+// One workgroup per token row.  With `part`: a = the GEMM result (partials +
+// bias), x += gate[cond(row)] * a in fp64 (the product of two floats is exact,
+// so the update rounds once).  Then, unless both sl and y are null, the row's
+// norm in fp64 (LayerNorm when norm == 1, else RmsNorm), modulated by
+// (1 + scale) and shift from nmod when nmod is non-null, rounded to fp32 and
+// either sliced into sl (rows N, K = D) or stored to y.
+template <int NT, int NCH>
+__global__ __launch_bounds__(NT) void resid_norm_slice_kernel(
+    int N, int D, int S, const double* __restrict__ part, const float* __restrict__ bias,
+    const float* __restrict__ gmod, int gate_k, const float* __restrict__ nmod, int shift_k, int scale_k,
+    int norm, float eps, const int32_t* __restrict__ cond_idx, double* __restrict__ x, int8_t* __restrict__ sl,
+    float* __restrict__ y) {
+  __shared__ double red[NT / 64];
+  __shared__ float redf[NT / 64];
+  const int row = blockIdx.x, t = threadIdx.x;
+  const int D4 = D >> 2;
+  const int cr = cond_idx != nullptr ? cond_idx[row] : 0;
+  double* xr = x + static_cast<size_t>(row) * D;
+  double v[NCH][4];
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = t + NT * i;
+    if (c < D4) {
+      const double2 x0 = reinterpret_cast<const double2*>(xr + 4 * c)[0];
+      const double2 x1 = reinterpret_cast<const double2*>(xr + 4 * c)[1];
+      v[i][0] = x0.x; v[i][1] = x0.y; v[i][2] = x1.x; v[i][3] = x1.y;
+      if (part != nullptr) {
+        float a[4];
+        sum_parts4(part, S, static_cast<size_t>(N) * D, static_cast<size_t>(row) * D + 4 * c, bias, 4 * c, a);
+        const float4 g = reinterpret_cast<const float4*>(gmod + (static_cast<size_t>(cr) * 6 + gate_k) * D)[c];
+        v[i][0] += static_cast<double>(g.x) * static_cast<double>(a[0]);
+        v[i][1] += static_cast<double>(g.y) * static_cast<double>(a[1]);
+        v[i][2] += static_cast<double>(g.z) * static_cast<double>(a[2]);
+        v[i][3] += static_cast<double>(g.w) * static_cast<double>(a[3]);
+        reinterpret_cast<double2*>(xr + 4 * c)[0] = make_double2(v[i][0], v[i][1]);
+        reinterpret_cast<double2*>(xr + 4 * c)[1] = make_double2(v[i][2], v[i][3]);
+      }
+      s += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
+    } else {
+      v[i][0] = v[i][1] = v[i][2] = v[i][3] = 0.0;
+    }
+  }
+  if (sl == nullptr && y == nullptr) return;
+  const double inv_d = 1.0 / static_cast<double>(D);
+  const double mean = norm == 1 ? block_sum<NT>(s, red) * inv_d : 0.0;
+  double ss = 0.0;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    if (t + NT * i < D4) {
+      const double a = v[i][0] - mean, b = v[i][1] - mean, c = v[i][2] - mean, d = v[i][3] - mean;
+      ss += (a * a + b * b) + (c * c + d * d);
+    }
+  }
+  ss = block_sum<NT>(ss, red);
+  const double rstd = 1.0 / sqrt(ss * inv_d + static_cast<double>(eps));
+  const float4* sh = nullptr;
+  const float4* sc = nullptr;
+  if (nmod != nullptr) {
+    sh = reinterpret_cast<const float4*>(nmod + (static_cast<size_t>(cr) * 6 + shift_k) * D);
+    sc = reinterpret_cast<const float4*>(nmod + (static_cast<size_t>(cr) * 6 + scale_k) * D);
+  }
+  float yv[NCH][4];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = t + NT * i;
+    if (c < D4) {
+      double z[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) z[e] = (v[i][e] - mean) * rstd;
+      if (nmod != nullptr) {
+        const float4 a = sc[c], b = sh[c];
+        z[0] = z[0] * (1.0 + static_cast<double>(a.x)) + static_cast<double>(b.x);
+        z[1] = z[1] * (1.0 + static_cast<double>(a.y)) + static_cast<double>(b.y);
+        z[2] = z[2] * (1.0 + static_cast<double>(a.z)) + static_cast<double>(b.z);
+        z[3] = z[3] * (1.0 + static_cast<double>(a.w)) + static_cast<double>(b.w);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) yv[i][e] = static_cast<float>(z[e]);
+    } else {
+      yv[i][0] = yv[i][1] = yv[i][2] = yv[i][3] = 0.f;
+    }
+  }
+  if (y != nullptr) {
+    float* yr = y + static_cast<size_t>(row) * D;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = t + NT * i;
+      if (c < D4) reinterpret_cast<float4*>(yr)[c] = make_float4(yv[i][0], yv[i][1], yv[i][2], yv[i][3]);
+    }
+    return;
+  }
+  slice_row<NT, NCH>(yv, D4, row, N, D, redf, sl);
+}
+
+// ============================================================================ SiLU gate + slices
+// One workgroup per token row of the [gate | up] projection (2F columns):
+// m = silu(g) * u evaluated in fp64 and rounded once, then sliced (rows N,
+// K = F).
+template <int NT, int NCH>
+__global__ __launch_bounds__(NT) void silu_slice_kernel(int N, int F, int S, const double* __restrict__ part,
+                                                       const float* __restrict__ bias, int8_t* __restrict__ sl) {
+  __shared__ float redf[NT / 64];
+  const int row = blockIdx.x, t = threadIdx.x;
+  const int F4 = F >> 2;
+  const size_t MN = static_cast<size_t>(N) * 2 * F;
+  const size_t base = static_cast<size_t>(row) * 2 * F;
+  float m[NCH][4];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = t + NT * i;
+    if (c < F4) {
+      float g[4], u[4];
+      sum_parts4(part, S, MN, base + 4 * c, bias, 4 * c, g);
+      sum_parts4(part, S, MN, base + F + 4 * c, bias, F + 4 * c, u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double gd = g[e];
+        m[i][e] = static_cast<float>(gd / (1.0 + exp(-gd)) * static_cast<double>(u[e]));
+      }
+    } else {
+      m[i][0] = m[i][1] = m[i][2] = m[i][3] = 0.f;
+    }
+  }
+  slice_row<NT, NCH>(m, F4, row, N, F, redf, sl);
+}
+
+// ============================================================================ RoPE + QKV split
+// The QKV projection [N, 3D] (columns q | k | v, head h at h*hd) from its
+// partials to head-major q, k, v [H, N, hd]; NeoX rotate_half on the first
+// `rot` dims of q and k with cos/sin by token row, evaluated in fp64 (each
+// output is one rounding of its exact value).  Thread (n, h, j): vector pair j
+// of the rotated half (or two pass-through vectors) of q and k, two vectors of
+// v.
+__global__ __launch_bounds__(256) void rope_part_kernel(int N, int H, int hd, int rot, int S,
+                                                       const double* __restrict__ part,
+                                                       const float* __restrict__ bias,
+                                                       const float* __restrict__ cosb,
+                                                       const float* __restrict__ sinb, float* __restrict__ q,
+                                                       float* __restrict__ k, float* __restrict__ v) {
+  const int tph = hd / 8;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t >= static_cast<int64_t>(N) * H * tph) return;
+  const int j = static_cast<int>(t % tph);
+  const int h = static_cast<int>((t / tph) % H);
+  const int n = static_cast<int>(t / (static_cast<int64_t>(tph) * H));
+  const int D = H * hd;
+  const int half = rot / 2;
+  const size_t MN = static_cast<size_t>(N) * 3 * D;
+  const size_t row = static_cast<size_t>(n) * 3 * D;
+  const size_t dst_off = (static_cast<size_t>(h) * N + n) * hd;
+  auto col = [&](int which, int i) { return which * D + h * hd + i; };
+  if (j < half / 4) {
+    const int i0 = j * 4, i1 = half + j * 4;
+    float c[4], sn[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      c[e] = cosb[static_cast<size_t>(n) * half + i0 + e];
+      sn[e] = sinb[static_cast<size_t>(n) * half + i0 + e];
+    }
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      float x1[4], x2[4], o1[4], o2[4];
+      sum_parts4(part, S, MN, row + col(which, i0), bias, col(which, i0), x1);
+      sum_parts4(part, S, MN, row + col(which, i1), bias, col(which, i1), x2);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o1[e] = static_cast<float>(double(x1[e]) * double(c[e]) - double(x2[e]) * double(sn[e]));
+        o2[e] = static_cast<float>(double(x2[e]) * double(c[e]) + double(x1[e]) * double(sn[e]));
+      }
+      float* d = (which == 0 ? q : k) + dst_off;
+      vec16<float>::store(d + i0, o1);
+      vec16<float>::store(d + i1, o2);
+    }
+  } else {
+    const int i0 = rot + 2 * (j - half / 4) * 4, i1 = i0 + 4;
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      float x1[4], x2[4];
+      sum_parts4(part, S, MN, row + col(which, i0), bias, col(which, i0), x1);
+      sum_parts4(part, S, MN, row + col(which, i1), bias, col(which, i1), x2);
+      float* d = (which == 0 ? q : k) + dst_off;
+      vec16<float>::store(d + i0, x1);
+      vec16<float>::store(d + i1, x2);
+    }
+  }
+  float v1[4], v2[4];
+  sum_parts4(part, S, MN, row + col(2, 8 * j), bias, col(2, 8 * j), v1);
+  sum_parts4(part, S, MN, row + col(2, 8 * j + 4), bias, col(2, 8 * j + 4), v2);
+  vec16<float>::store(v + dst_off + 8 * j, v1);
+  vec16<float>::store(v + dst_off + 8 * j + 4, v2);
+}
+
+// ============================================================================ host side
+// Row kernels: NT threads per row, NCH four-float chunks per thread.
+#define DIT_ROW_LAUNCH(KERNEL, C4, ...)                                                              \
+  do {                                                                                               \
+    const int nt_ = (C4) <= 1024 ? 256 : ((C4) <= 2048 ? 512 : 1024);                                \
+    const int nch_ = ((C4) + nt_ - 1) / nt_;                                                         \
+    if (nt_ == 256 && nch_ <= 1) hipLaunchKernelGGL((KERNEL<256, 1>), dim3(N), dim3(256), 0, s, __VA_ARGS__); \
+    else if (nt_ == 256 && nch_ <= 2) hipLaunchKernelGGL((KERNEL<256, 2>), dim3(N), dim3(256), 0, s, __VA_ARGS__); \
+    else if (nt_ == 256) hipLaunchKernelGGL((KERNEL<256, 4>), dim3(N), dim3(256), 0, s, __VA_ARGS__); \
+    else if (nt_ == 512) hipLaunchKernelGGL((KERNEL<512, 4>), dim3(N), dim3(512), 0, s, __VA_ARGS__); \
+    else if (nch_ <= 4) hipLaunchKernelGGL((KERNEL<1024, 4>), dim3(N), dim3(1024), 0, s, __VA_ARGS__); \
+    else if (nch_ <= 8) hipLaunchKernelGGL((KERNEL<1024, 8>), dim3(N), dim3(1024), 0, s, __VA_ARGS__); \
+    else return hipErrorInvalidValue;                                                                \
+  } while (0)
+
+bool fused_f32_supported(int D, int F) {
+  return D > 0 && F > 0 && D % 4 == 0 && F % 4 == 0 && D / 4 <= 8192 && F / 4 <= 8192;
+}
+
+hipError_t resid_norm_slice(int N, int D, int S, const double* part, const float* bias, const float* gmod, int gate_which,
+                            const float* nmod, int norm_which, int norm, float eps, const int32_t* cond_idx, double* x,
+                            void* slices, float* y, hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  if (D % 4 || D / 4 > 8192 || (slices != nullptr && y != nullptr)) return hipErrorInvalidValue;
+  LaunchScope scope_(kCntResidNormSlice, s);
+  const int gate_k = gate_which == 0 ? 2 : 5;
+  const int shift_k = norm_which == 0 ? 0 : 3, scale_k = norm_which == 0 ? 1 : 4;
+  const int D4 = D / 4;
+  DIT_ROW_LAUNCH(resid_norm_slice_kernel, D4, N, D, S, part, bias, gmod, gate_k, nmod, shift_k, scale_k, norm, eps,
+                 cond_idx, x, static_cast<int8_t*>(slices), y);
+  return hipGetLastError();
+}
+
+hipError_t silu_slice(int N, int F, int S, const double* part, const float* bias, void* slices, hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  if (F % 4 || F / 4 > 8192) return hipErrorInvalidValue;
+  LaunchScope scope_(kCntSiluSlice, s);
+  const int F4 = F / 4;
+  DIT_ROW_LAUNCH(silu_slice_kernel, F4, N, F, S, part, bias, static_cast<int8_t*>(slices));
+  return hipGetLastError();
+}
+#undef DIT_ROW_LAUNCH
+
+hipError_t rope_part(int N, int H, int hd, int rot, int S, const double* part, const float* bias, const float* cos,
+                     const float* sin, float* q, float* k, float* v, hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  if (!rope_split_supported(false, hd, rot)) return hipErrorInvalidValue;
+  LaunchScope scope_(kCntRopeSplit, s);
+  const int64_t total = static_cast<int64_t>(N) * H * (hd / 8);
+  hipLaunchKernelGGL(rope_part_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s, N, H, hd,
+                     rot, S, part, bias, cos, sin, q, k, v);
+  return hipGetLastError();
+}
+
+}  // namespace dit

@@ -22,6 +22,7 @@
 // and the same document inside a packed batch give bit-identical results.
 #include "common.h"
 #include "kernels.h"
+#include "slices.h"
 
 namespace dit {
 
@@ -296,10 +297,7 @@ static inline int go_kp(int K) { return (K + go::BK - 1) / go::BK * go::BK; }
 __device__ __forceinline__ int go_swz(int r, int c) { return r * 2 + (c ^ ((r >> 3) & 1)); }
 
 // ---------------------------------------------------------------- slicing
-// One workgroup per row: e = exponent of max|x| (max|x| < 2^e), then five
-// truncating 7-bit digits of x 2^-e.  Every step is exact in fp32.  Planes are
-// stored K-step-major, [plane][K / 32][row][32 bytes], so the 32 rows of one K
-// step that a direct load fetches are 1 KB of consecutive bytes.
+// One workgroup per row: the row's max, then its slices (slices.h).
 __global__ __launch_bounds__(256) void slice_rows_kernel(int R, int K, int Kp, const float* __restrict__ X,
                                                         int8_t* __restrict__ P, int32_t* __restrict__ E) {
   __shared__ float red[4];
@@ -314,26 +312,12 @@ __global__ __launch_bounds__(256) void slice_rows_kernel(int R, int K, int Kp, c
   if ((tid & 63) == 0) red[tid >> 6] = mx;
   __syncthreads();
   mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  int e = 0;
-  if (mx > 0.f) frexpf(mx, &e);  // mx = m 2^e, m in [0.5, 1)
+  const int e = slice_exponent(mx);
   if (tid == 0) E[row] = e;
-  const size_t plane = static_cast<size_t>(R) * Kp;
   for (int k = 4 * tid; k < Kp; k += 4 * 256) {
-    float4 v = k < K ? *reinterpret_cast<const float4*>(x + k) : make_float4(0.f, 0.f, 0.f, 0.f);
-    float f[4] = {ldexpf(v.x, -e), ldexpf(v.y, -e), ldexpf(v.z, -e), ldexpf(v.w, -e)};
-#pragma unroll
-    for (int sl = 0; sl < go::S; ++sl) {
-      uint32_t w = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f[j] *= 128.f;
-        const float d = truncf(f[j]);
-        f[j] -= d;
-        w |= (static_cast<uint32_t>(static_cast<int>(d)) & 0xFFu) << (8 * j);
-      }
-      // layout [plane][K step][row][32 bytes]
-      *reinterpret_cast<uint32_t*>(P + sl * plane + (static_cast<size_t>(k / go::BK) * R + row) * go::BK + (k % go::BK)) = w;
-    }
+    const float4 v = k < K ? *reinterpret_cast<const float4*>(x + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float f[4] = {v.x, v.y, v.z, v.w};
+    slice_store4(f, e, row, k, R, Kp, P);
   }
 }
 
@@ -446,7 +430,9 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
   const int gn = n0 + wc + lr;
   if (gn >= N) return;
   const int fe = Be[gn];
-  const double bv = (splits == 1 && bias != nullptr) ? static_cast<double>(bias[gn]) : 0.0;
+  // C null: fp64 partials for a consumer that sums them itself (any split count)
+  const bool direct = splits == 1 && C != nullptr;
+  const double bv = (direct && bias != nullptr) ? static_cast<double>(bias[gn]) : 0.0;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     const int gm = m0 + wr + 8 * (e >> 2) + 4 * lg + (e & 3);
@@ -456,7 +442,7 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
 #pragma unroll
     for (int d = S - 1; d >= 0; --d) v += ldexp(static_cast<double>(acc[d][e]), -7 * (d + 2));
     v = ldexp(v, Ae[gm] + fe);
-    if (splits == 1)
+    if (direct)
       C[static_cast<size_t>(gm) * N + gn] = static_cast<float>(v + bv);
     else
       part[(static_cast<size_t>(sp) * M + gm) * N + gn] = v;
@@ -536,6 +522,36 @@ hipError_t slice_rows(int R, int K, const float* X, void* slices, hipStream_t s)
   return hipGetLastError();
 }
 
+int gemm_f32_splits(int N, int K) { return go_splits(N, K); }
+size_t gemm_f32_part_bytes(int M, int N, int K) {
+  return al256(static_cast<size_t>(go_splits(N, K)) * M * N * sizeof(double));
+}
+
+static hipError_t launch_gemm_f32(int M, int N, int kp, const int8_t* Ap, const int32_t* Ae, const int8_t* Bp,
+                                  const int32_t* Be, const float* bias, float* C, double* part, int splits,
+                                  hipStream_t s) {
+  const int steps = kp / go::BK;
+  const int sps = (steps + splits - 1) / splits;
+  const int tiles_m = (M + go::BM - 1) / go::BM, tiles_n = (N + go::BN - 1) / go::BN;
+  const int64_t work = static_cast<int64_t>(tiles_m) * tiles_n * splits;
+  if (work >= (int64_t(1) << 31) - 256) return hipErrorInvalidValue;
+  const unsigned blocks = static_cast<unsigned>((work + 255) / 256 * 256);
+  LaunchScope scope_(kCntGemmF32, s);
+  hipLaunchKernelGGL(gemm_f32_kernel, dim3(blocks), dim3(go::NT), 0, s, M, N, kp, Ap, Ae, Bp, Be, bias, C, part,
+                     splits, sps, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+hipError_t gemm_f32_sliced(int M, int N, int K, const void* As, const void* Bs, double* part, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  const int kp = go_kp(K);
+  const int8_t* Ap = static_cast<const int8_t*>(As);
+  const int32_t* Ae = reinterpret_cast<const int32_t*>(Ap + al256(static_cast<size_t>(go::S) * M * kp));
+  const int8_t* Bp = static_cast<const int8_t*>(Bs);
+  const int32_t* Be = reinterpret_cast<const int32_t*>(Bp + al256(static_cast<size_t>(go::S) * N * kp));
+  return launch_gemm_f32(M, N, kp, Ap, Ae, Bp, Be, nullptr, nullptr, part, go_splits(N, K), s);
+}
+
 hipError_t gemm_f32(int M, int N, int K, const float* A, const void* Bs, const float* bias, float* C,
                     void* ws, hipStream_t s) {
   if (M == 0) return hipSuccess;
@@ -549,18 +565,7 @@ hipError_t gemm_f32(int M, int N, int K, const float* A, const void* Bs, const f
   const int32_t* Be = reinterpret_cast<const int32_t*>(Bp + al256(static_cast<size_t>(go::S) * N * kp));
   double* part = reinterpret_cast<double*>(w + gemm_f32_slices_bytes(M, K));
   const int splits = go_splits(N, K);
-  const int steps = kp / go::BK;
-  const int sps = (steps + splits - 1) / splits;
-  const int tiles_m = (M + go::BM - 1) / go::BM, tiles_n = (N + go::BN - 1) / go::BN;
-  const int64_t work = static_cast<int64_t>(tiles_m) * tiles_n * splits;
-  if (work >= (int64_t(1) << 31) - 256) return hipErrorInvalidValue;
-  const unsigned blocks = static_cast<unsigned>((work + 255) / 256 * 256);
-  {
-    LaunchScope scope_(kCntGemmF32, s);
-    hipLaunchKernelGGL(gemm_f32_kernel, dim3(blocks), dim3(go::NT), 0, s, M, N, kp, Ap, Ae, Bp, Be, bias, C, part,
-                       splits, sps, tiles_m, tiles_n);
-  }
-  e = hipGetLastError();
+  e = launch_gemm_f32(M, N, kp, Ap, Ae, Bp, Be, bias, C, part, splits, s);
   if (e != hipSuccess || splits == 1) return e;
   const int64_t MN = static_cast<int64_t>(M) * N;
   {

@@ -11,7 +11,7 @@ namespace dit {
 enum Counter {
   kCntGemmBf16 = 0, kCntGemmF32, kCntAttnBf16, kCntAttnF32, kCntModnorm, kCntRopeSplit,
   kCntSiluGate, kCntGatedResidual, kCntAdaln, kCntPatchIn, kCntPatchOut, kCntEuler,
-  kCntGemmF32Reduce, kCntConvert, kCntNum
+  kCntGemmF32Reduce, kCntConvert, kCntResidNormSlice, kCntSiluSlice, kCntNum
 };
 void count_launch(Counter c);
 
@@ -39,6 +39,13 @@ hipError_t slice_rows(int R, int K, const float* X, void* slices, hipStream_t s)
 size_t gemm_f32_ws_bytes(int M, int N, int K);
 hipError_t gemm_f32(int M, int N, int K, const float* A, const void* B_slices, const float* bias,
                     float* C, void* ws, hipStream_t s);
+// A also given as slices; the product goes to fp64 split-K partials
+// part[splits][M][N] (splits = gemm_f32_splits(N, K), no bias) that the
+// consumer sums in split order.
+int gemm_f32_splits(int N, int K);
+size_t gemm_f32_part_bytes(int M, int N, int K);
+hipError_t gemm_f32_sliced(int M, int N, int K, const void* A_slices, const void* B_slices, double* part,
+                           hipStream_t s);
 // Which K, N the GEMMs accept (checked by the ABI layer before launching).
 bool gemm_bf16_supported(int M, int N, int K);
 bool gemm_f32_supported(int M, int N, int K);
@@ -62,6 +69,18 @@ bool rope_split_supported(bool bf16, int hd, int rot);
 hipError_t silu_gate(bool bf16, int N, int F, const void* u, void* m, hipStream_t s);
 hipError_t gated_residual(int N, int D, bool x_f64, void* x, const float* a, const float* mod, int which,
                           const int32_t* cond_idx, hipStream_t s);
+// ---- fused row kernels of the fp32 stream (fused_f32.hip); part: fp64 split-K
+// partials [S][N][cols] of the preceding gemm_f32_sliced, bias added after them.
+// resid_norm_slice: with part, x += gate(gmod, which) * a; then the norm of x,
+// modulated from nmod (which) unless nmod is null, sliced into `slices` (rows
+// N, K = D) or stored to y, or neither when both are null.
+bool fused_f32_supported(int D, int F);
+hipError_t resid_norm_slice(int N, int D, int S, const double* part, const float* bias, const float* gmod, int gate_which,
+                            const float* nmod, int norm_which, int norm, float eps, const int32_t* cond_idx, double* x,
+                            void* slices, float* y, hipStream_t s);
+hipError_t silu_slice(int N, int F, int S, const double* part, const float* bias, void* slices, hipStream_t s);
+hipError_t rope_part(int N, int H, int hd, int rot, int S, const double* part, const float* bias, const float* cos,
+                     const float* sin, float* q, float* k, float* v, hipStream_t s);
 hipError_t widen_f32(int64_t n, const float* src, double* dst, hipStream_t s);
 hipError_t narrow_f64(int64_t n, const double* src, float* dst, hipStream_t s);
 // mod[b][c][j] = W[b][modality(c)][j] . e[c] + bias[b][modality(c)][j]

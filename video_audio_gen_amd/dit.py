@@ -31,7 +31,7 @@ DIT_IO_NONE, DIT_IO_PATCH3D, DIT_IO_CHANNEL_MAJOR = 0, 1, 2
 MAX_MOD = 4
 COUNTER_NAMES = ["gemm_bf16", "gemm_f32", "attention_bf16", "attention_f32", "modnorm", "rope_split",
                  "silu_gate", "gated_residual", "adaln", "patch_in", "patch_out", "euler",
-                 "gemm_f32_reduce", "convert"]
+                 "gemm_f32_reduce", "convert", "resid_norm_slice", "silu_slice"]
 
 
 class DitError(RuntimeError):
@@ -92,6 +92,7 @@ _SIGS = {
     "dit_denoise_step": [_P, _P, _P, _P, _P, _P, _SZ, _P],
     "dit_denoise_loop": [_P, _P, _P, _P, _P, _I, _P, _SZ, _P],
     "dit_gemm_workspace_bytes": [_I, _I, _I, _I, ctypes.POINTER(_SZ)],
+    "dit_gemm_splits": [_I, _I, _I, ctypes.POINTER(_I)],
     "dit_gemm": [_I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _SZ, _P],
     "dit_modnorm": [_I, _I, ctypes.c_float, _I, _I, _P, _I, _P, _I, _P, _P, _P],
     "dit_rope_split": [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P],
@@ -404,6 +405,13 @@ def dit_gemm(A, B, bias, C, stream=None):
     _check(load().dit_gemm(dt, M, N, K, _ptr(A), _ptr(B), _ptr(bias), _ptr(C), _dt(C), _ptr(ws), int(ws_bytes.value),
                            _stream(stream)))
     return ws
+
+
+def dit_gemm_splits(N: int, K: int) -> int:
+    """Split-K count of the fp32 GEMM for an [N, K] weight on the current device."""
+    s = ctypes.c_int()
+    _check(load().dit_gemm_splits(DIT_F32, N, K, ctypes.byref(s)))
+    return int(s.value)
 
 
 def dit_modnorm(norm: int, eps: float, x, mod, which: int, cond_idx, h, stream=None):
