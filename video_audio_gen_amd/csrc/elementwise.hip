@@ -397,30 +397,53 @@ struct CondMap {
   int modality[64];
 };
 
+// Four consecutive weights as floats.
+template <typename TW> struct wload4;
+template <> struct wload4<float> {
+  static __device__ __forceinline__ float4 ld(const float* p) { return *reinterpret_cast<const float4*>(p); }
+};
+template <> struct wload4<bf16_t> {
+  static __device__ __forceinline__ float4 ld(const bf16_t* p) {
+    const uint2 t = *reinterpret_cast<const uint2*>(p);
+    return make_float4(__uint_as_float(t.x << 16), __uint_as_float(t.x & 0xFFFF0000u), __uint_as_float(t.y << 16),
+                       __uint_as_float(t.y & 0xFFFF0000u));
+  }
+};
+
+// blockIdx.z: the block (weights at p + z * stride bytes, output rows at
+// mod + z * n_cond * six_d); each lane reads four consecutive weights.
 template <typename TW>
-__global__ __launch_bounds__(256) void adaln_kernel(int six_d, int cond_dim, AdalnBlockPtrs p,
-                                                   CondMap cm, const float* __restrict__ e,
+__global__ __launch_bounds__(256) void adaln_kernel(int six_d, int cond_dim, AdalnBlockPtrs p, int64_t w_stride,
+                                                   int64_t b_stride, CondMap cm, const float* __restrict__ e,
                                                    float* __restrict__ mod) {
   const int lane = threadIdx.x & 63;
   const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int m = blockIdx.y;
   if (j >= six_d || p.w[m] == nullptr) return;
-  const TW* w = static_cast<const TW*>(p.w[m]) + static_cast<size_t>(j) * cond_dim;
+  const TW* w = reinterpret_cast<const TW*>(static_cast<const char*>(p.w[m]) + blockIdx.z * w_stride) +
+                static_cast<size_t>(j) * cond_dim;
+  const float* bias = reinterpret_cast<const float*>(reinterpret_cast<const char*>(p.bias[m]) + blockIdx.z * b_stride);
+  float* out = mod + static_cast<size_t>(blockIdx.z) * cm.n_cond * six_d;
   for (int c = 0; c < cm.n_cond; ++c) {
     if (cm.modality[c] != m) continue;
     const float* ec = e + static_cast<size_t>(c) * cond_dim;
     double acc = 0.0;
-    for (int kk = lane; kk < cond_dim; kk += 64)
-      acc += static_cast<double>(elem<TW>::load(w + kk)) * static_cast<double>(ec[kk]);
+    for (int kk = 4 * lane; kk < cond_dim; kk += 256) {
+      const float4 wv = wload4<TW>::ld(w + kk);
+      const float4 ev = *reinterpret_cast<const float4*>(ec + kk);
+      acc += static_cast<double>(wv.x) * static_cast<double>(ev.x) + static_cast<double>(wv.y) * static_cast<double>(ev.y) +
+             static_cast<double>(wv.z) * static_cast<double>(ev.z) + static_cast<double>(wv.w) * static_cast<double>(ev.w);
+    }
     acc = wave_sum_f64(acc);
-    if (lane == 0) mod[static_cast<size_t>(c) * six_d + j] = static_cast<float>(acc + static_cast<double>(p.bias[m][j]));
+    if (lane == 0) out[static_cast<size_t>(c) * six_d + j] = static_cast<float>(acc + static_cast<double>(bias[j]));
   }
 }
 
 hipError_t adaln(bool w_bf16, int n_blocks, const AdalnBlockPtrs* blocks_host, int n_cond,
                  const int* cond_modality_host, int six_d, int cond_dim, const float* e,
                  float* mod, hipStream_t s) {
-  if (n_cond > 64) return hipErrorInvalidValue;
+  if (n_cond > 64 || cond_dim % 4) return hipErrorInvalidValue;
+  if (n_blocks == 0) return hipSuccess;
   CondMap cm;
   cm.n_cond = n_cond;
   int n_mod = 0;
@@ -428,16 +451,32 @@ hipError_t adaln(bool w_bf16, int n_blocks, const AdalnBlockPtrs* blocks_host, i
     cm.modality[c] = cond_modality_host[c];
     if (cond_modality_host[c] + 1 > n_mod) n_mod = cond_modality_host[c] + 1;
   }
-  dim3 grid((six_d + 3) / 4, n_mod), block(256);
-  for (int b = 0; b < n_blocks; ++b) {
+  // One launch for all blocks when their weights sit at one stride from
+  // block to block (the staged slab's layout), else one launch per block.
+  auto byte = [](const void* q) { return static_cast<int64_t>(reinterpret_cast<intptr_t>(q)); };
+  int64_t ws = 0, bs = 0;
+  bool uniform = false;
+  for (int mm = 0; mm < n_mod && n_blocks > 1; ++mm) {
+    if (blocks_host[0].w[mm] == nullptr) continue;
+    if (!uniform) {
+      ws = byte(blocks_host[1].w[mm]) - byte(blocks_host[0].w[mm]);
+      bs = byte(blocks_host[1].bias[mm]) - byte(blocks_host[0].bias[mm]);
+      uniform = true;
+    }
+    for (int b = 1; b < n_blocks; ++b)
+      if (byte(blocks_host[b].w[mm]) - byte(blocks_host[0].w[mm]) != b * ws ||
+          byte(blocks_host[b].bias[mm]) - byte(blocks_host[0].bias[mm]) != b * bs)
+        uniform = false, mm = n_mod, b = n_blocks;  // stop: per-block launches
+  }
+  const int launches = uniform ? 1 : n_blocks;
+  for (int b = 0; b < launches; ++b) {
+    dim3 grid((six_d + 3) / 4, n_mod, uniform ? n_blocks : 1), block(256);
     LaunchScope scope_(kCntAdaln, s);
     float* out = mod + static_cast<size_t>(b) * n_cond * six_d;
     if (w_bf16)
-      hipLaunchKernelGGL(adaln_kernel<bf16_t>, grid, block, 0, s, six_d, cond_dim, blocks_host[b], cm,
-                         e, out);
+      hipLaunchKernelGGL(adaln_kernel<bf16_t>, grid, block, 0, s, six_d, cond_dim, blocks_host[b], ws, bs, cm, e, out);
     else
-      hipLaunchKernelGGL(adaln_kernel<float>, grid, block, 0, s, six_d, cond_dim, blocks_host[b], cm,
-                         e, out);
+      hipLaunchKernelGGL(adaln_kernel<float>, grid, block, 0, s, six_d, cond_dim, blocks_host[b], ws, bs, cm, e, out);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

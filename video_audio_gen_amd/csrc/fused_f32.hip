@@ -24,77 +24,84 @@ namespace dit {
 
 // Columns col..col+3 of row `row` of a GEMM result [M, ncol] held as S fp64
 // split-K partials [S][M][ncol]: summed in split order from zero, bias added
-// last, rounded once.  Groups of four splits are loaded before they are added
-// so their latencies overlap.
+// last, rounded once.  Up to eight splits are loaded before any is added, so
+// their latencies overlap.
+template <int NS>
+__device__ __forceinline__ void add_parts4(const double* __restrict__ p, size_t MN, double* v) {
+  double2 a[NS], b[NS];
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    a[u] = reinterpret_cast<const double2*>(p + u * MN)[0];
+    b[u] = reinterpret_cast<const double2*>(p + u * MN)[1];
+  }
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    v[0] += a[u].x; v[1] += a[u].y; v[2] += b[u].x; v[3] += b[u].y;
+  }
+}
+
 __device__ __forceinline__ void sum_parts4(const double* __restrict__ part, int S, size_t MN, size_t off,
                                            const float* __restrict__ bias, int col, float* out) {
-  double v0 = 0.0, v1 = 0.0, v2 = 0.0, v3 = 0.0;
+  double v[4] = {0.0, 0.0, 0.0, 0.0};
   const double* p = part + off;
   int s = 0;
-  for (; s + 4 <= S; s += 4) {
-    double2 a[4], b[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      a[u] = reinterpret_cast<const double2*>(p + (s + u) * MN)[0];
-      b[u] = reinterpret_cast<const double2*>(p + (s + u) * MN)[1];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      v0 += a[u].x; v1 += a[u].y; v2 += b[u].x; v3 += b[u].y;
-    }
-  }
-  for (; s < S; ++s) {
-    const double2 a = reinterpret_cast<const double2*>(p + s * MN)[0];
-    const double2 b = reinterpret_cast<const double2*>(p + s * MN)[1];
-    v0 += a.x; v1 += a.y; v2 += b.x; v3 += b.y;
+  for (; s + 8 <= S; s += 8) add_parts4<8>(p + s * MN, MN, v);
+  switch (S - s) {  // uniform
+    case 1: add_parts4<1>(p + s * MN, MN, v); break;
+    case 2: add_parts4<2>(p + s * MN, MN, v); break;
+    case 3: add_parts4<3>(p + s * MN, MN, v); break;
+    case 4: add_parts4<4>(p + s * MN, MN, v); break;
+    case 5: add_parts4<5>(p + s * MN, MN, v); break;
+    case 6: add_parts4<6>(p + s * MN, MN, v); break;
+    case 7: add_parts4<7>(p + s * MN, MN, v); break;
+    default: break;
   }
   if (bias != nullptr) {
     const float4 bb = *reinterpret_cast<const float4*>(bias + col);
-    v0 += static_cast<double>(bb.x); v1 += static_cast<double>(bb.y);
-    v2 += static_cast<double>(bb.z); v3 += static_cast<double>(bb.w);
+    v[0] += static_cast<double>(bb.x); v[1] += static_cast<double>(bb.y);
+    v[2] += static_cast<double>(bb.z); v[3] += static_cast<double>(bb.w);
   }
-  out[0] = static_cast<float>(v0); out[1] = static_cast<float>(v1);
-  out[2] = static_cast<float>(v2); out[3] = static_cast<float>(v3);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) out[e] = static_cast<float>(v[e]);
 }
 
-template <int NT>
+// Row reductions over the workgroup (blockDim.x a multiple of 64, <= 1024).
 __device__ __forceinline__ double block_sum(double v, double* red) {
   v = wave_sum_f64(v);
-  if (NT == 64) return v;
+  const int nw = blockDim.x >> 6;
+  if (nw == 1) return v;
   __syncthreads();  // red may still be read by the previous reduction
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   double t = 0.0;
-#pragma unroll
-  for (int i = 0; i < NT / 64; ++i) t += red[i];
+  for (int i = 0; i < nw; ++i) t += red[i];
   return t;
 }
 
-template <int NT>
 __device__ __forceinline__ float block_max(float v, float* red) {
   v = wave_max(v);
-  if (NT == 64) return v;
+  const int nw = blockDim.x >> 6;
+  if (nw == 1) return v;
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   float t = 0.f;
-#pragma unroll
-  for (int i = 0; i < NT / 64; ++i) t = fmaxf(t, red[i]);
+  for (int i = 0; i < nw; ++i) t = fmaxf(t, red[i]);
   return t;
 }
 
 // Row max of the four-float chunks a thread holds, then the row's exponent
 // and its slices; chunks between the row's width and the 32-padded width are
 // written as zero slices.
-template <int NT, int NCH>
+template <int NCH>
 __device__ __forceinline__ void slice_row(float (*y)[4], int C4, int row, int R, int K, float* redf, int8_t* sl) {
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, NT = blockDim.x;
   float mx = 0.f;
 #pragma unroll
   for (int i = 0; i < NCH; ++i)
     if (t + NT * i < C4)
       mx = fmaxf(mx, fmaxf(fmaxf(fabsf(y[i][0]), fabsf(y[i][1])), fmaxf(fabsf(y[i][2]), fabsf(y[i][3]))));
-  mx = block_max<NT>(mx, redf);
+  mx = block_max(mx, redf);
   const int e = slice_exponent(mx);
   const int Kp = slice_kp(K);
   if (t == 0) reinterpret_cast<int32_t*>(sl + slice_exp_offset(R, K))[row] = e;
@@ -114,15 +121,15 @@ __device__ __forceinline__ void slice_row(float (*y)[4], int C4, int row, int R,
 // norm in fp64 (LayerNorm when norm == 1, else RmsNorm), modulated by
 // (1 + scale) and shift from nmod when nmod is non-null, rounded to fp32 and
 // either sliced into sl (rows N, K = D) or stored to y.
-template <int NT, int NCH>
-__global__ __launch_bounds__(NT) void resid_norm_slice_kernel(
+template <int NCH>
+__global__ __launch_bounds__(1024) void resid_norm_slice_kernel(
     int N, int D, int S, const double* __restrict__ part, const float* __restrict__ bias,
     const float* __restrict__ gmod, int gate_k, const float* __restrict__ nmod, int shift_k, int scale_k,
     int norm, float eps, const int32_t* __restrict__ cond_idx, double* __restrict__ x, int8_t* __restrict__ sl,
     float* __restrict__ y) {
-  __shared__ double red[NT / 64];
-  __shared__ float redf[NT / 64];
-  const int row = blockIdx.x, t = threadIdx.x;
+  __shared__ double red[16];
+  __shared__ float redf[16];
+  const int row = blockIdx.x, t = threadIdx.x, NT = blockDim.x;
   const int D4 = D >> 2;
   const int cr = cond_idx != nullptr ? cond_idx[row] : 0;
   double* xr = x + static_cast<size_t>(row) * D;
@@ -153,7 +160,7 @@ __global__ __launch_bounds__(NT) void resid_norm_slice_kernel(
   }
   if (sl == nullptr && y == nullptr) return;
   const double inv_d = 1.0 / static_cast<double>(D);
-  const double mean = norm == 1 ? block_sum<NT>(s, red) * inv_d : 0.0;
+  const double mean = norm == 1 ? block_sum(s, red) * inv_d : 0.0;
   double ss = 0.0;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
@@ -162,7 +169,7 @@ __global__ __launch_bounds__(NT) void resid_norm_slice_kernel(
       ss += (a * a + b * b) + (c * c + d * d);
     }
   }
-  ss = block_sum<NT>(ss, red);
+  ss = block_sum(ss, red);
   const double rstd = 1.0 / sqrt(ss * inv_d + static_cast<double>(eps));
   const float4* sh = nullptr;
   const float4* sc = nullptr;
@@ -200,18 +207,18 @@ __global__ __launch_bounds__(NT) void resid_norm_slice_kernel(
     }
     return;
   }
-  slice_row<NT, NCH>(yv, D4, row, N, D, redf, sl);
+  slice_row<NCH>(yv, D4, row, N, D, redf, sl);
 }
 
 // ============================================================================ SiLU gate + slices
 // One workgroup per token row of the [gate | up] projection (2F columns):
 // m = silu(g) * u evaluated in fp64 and rounded once, then sliced (rows N,
 // K = F).
-template <int NT, int NCH>
-__global__ __launch_bounds__(NT) void silu_slice_kernel(int N, int F, int S, const double* __restrict__ part,
+template <int NCH>
+__global__ __launch_bounds__(1024) void silu_slice_kernel(int N, int F, int S, const double* __restrict__ part,
                                                        const float* __restrict__ bias, int8_t* __restrict__ sl) {
-  __shared__ float redf[NT / 64];
-  const int row = blockIdx.x, t = threadIdx.x;
+  __shared__ float redf[16];
+  const int row = blockIdx.x, t = threadIdx.x, NT = blockDim.x;
   const int F4 = F >> 2;
   const size_t MN = static_cast<size_t>(N) * 2 * F;
   const size_t base = static_cast<size_t>(row) * 2 * F;
@@ -232,16 +239,16 @@ __global__ __launch_bounds__(NT) void silu_slice_kernel(int N, int F, int S, con
       m[i][0] = m[i][1] = m[i][2] = m[i][3] = 0.f;
     }
   }
-  slice_row<NT, NCH>(m, F4, row, N, F, redf, sl);
+  slice_row<NCH>(m, F4, row, N, F, redf, sl);
 }
 
 // ============================================================================ RoPE + QKV split
 // The QKV projection [N, 3D] (columns q | k | v, head h at h*hd) from its
 // partials to head-major q, k, v [H, N, hd]; NeoX rotate_half on the first
 // `rot` dims of q and k with cos/sin by token row, evaluated in fp64 (each
-// output is one rounding of its exact value).  Thread (n, h, j): vector pair j
-// of the rotated half (or two pass-through vectors) of q and k, two vectors of
-// v.
+// output is one rounding of its exact value).  Thread (n, h, which, j), j
+// fastest: for q and k, vector pair j of the rotated half (columns 4j and
+// rot/2 + 4j) or two pass-through vectors; for v, columns 8j .. 8j+7.
 __global__ __launch_bounds__(256) void rope_part_kernel(int N, int H, int hd, int rot, int S,
                                                        const double* __restrict__ part,
                                                        const float* __restrict__ bias,
@@ -250,70 +257,62 @@ __global__ __launch_bounds__(256) void rope_part_kernel(int N, int H, int hd, in
                                                        float* __restrict__ k, float* __restrict__ v) {
   const int tph = hd / 8;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (t >= static_cast<int64_t>(N) * H * tph) return;
+  if (t >= static_cast<int64_t>(N) * H * 3 * tph) return;
   const int j = static_cast<int>(t % tph);
-  const int h = static_cast<int>((t / tph) % H);
-  const int n = static_cast<int>(t / (static_cast<int64_t>(tph) * H));
+  const int which = static_cast<int>((t / tph) % 3);
+  const int h = static_cast<int>((t / (3 * tph)) % H);
+  const int n = static_cast<int>(t / (static_cast<int64_t>(3 * tph) * H));
   const int D = H * hd;
   const int half = rot / 2;
   const size_t MN = static_cast<size_t>(N) * 3 * D;
-  const size_t row = static_cast<size_t>(n) * 3 * D;
-  const size_t dst_off = (static_cast<size_t>(h) * N + n) * hd;
-  auto col = [&](int which, int i) { return which * D + h * hd + i; };
-  if (j < half / 4) {
+  const int col0 = which * D + h * hd;
+  const size_t src = static_cast<size_t>(n) * 3 * D + col0;
+  float* d = (which == 0 ? q : which == 1 ? k : v) + (static_cast<size_t>(h) * N + n) * hd;
+  if (which < 2 && j < half / 4) {
     const int i0 = j * 4, i1 = half + j * 4;
-    float c[4], sn[4];
+    const float4 c = *reinterpret_cast<const float4*>(cosb + static_cast<size_t>(n) * half + i0);
+    const float4 sn = *reinterpret_cast<const float4*>(sinb + static_cast<size_t>(n) * half + i0);
+    const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
+    float x1[4], x2[4], o1[4], o2[4];
+    sum_parts4(part, S, MN, src + i0, bias, col0 + i0, x1);
+    sum_parts4(part, S, MN, src + i1, bias, col0 + i1, x2);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      c[e] = cosb[static_cast<size_t>(n) * half + i0 + e];
-      sn[e] = sinb[static_cast<size_t>(n) * half + i0 + e];
+      o1[e] = static_cast<float>(double(x1[e]) * double(cc[e]) - double(x2[e]) * double(ss[e]));
+      o2[e] = static_cast<float>(double(x2[e]) * double(cc[e]) + double(x1[e]) * double(ss[e]));
     }
-#pragma unroll
-    for (int which = 0; which < 2; ++which) {
-      float x1[4], x2[4], o1[4], o2[4];
-      sum_parts4(part, S, MN, row + col(which, i0), bias, col(which, i0), x1);
-      sum_parts4(part, S, MN, row + col(which, i1), bias, col(which, i1), x2);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        o1[e] = static_cast<float>(double(x1[e]) * double(c[e]) - double(x2[e]) * double(sn[e]));
-        o2[e] = static_cast<float>(double(x2[e]) * double(c[e]) + double(x1[e]) * double(sn[e]));
-      }
-      float* d = (which == 0 ? q : k) + dst_off;
-      vec16<float>::store(d + i0, o1);
-      vec16<float>::store(d + i1, o2);
-    }
+    vec16<float>::store(d + i0, o1);
+    vec16<float>::store(d + i1, o2);
   } else {
-    const int i0 = rot + 2 * (j - half / 4) * 4, i1 = i0 + 4;
-#pragma unroll
-    for (int which = 0; which < 2; ++which) {
-      float x1[4], x2[4];
-      sum_parts4(part, S, MN, row + col(which, i0), bias, col(which, i0), x1);
-      sum_parts4(part, S, MN, row + col(which, i1), bias, col(which, i1), x2);
-      float* d = (which == 0 ? q : k) + dst_off;
-      vec16<float>::store(d + i0, x1);
-      vec16<float>::store(d + i1, x2);
-    }
+    // v, or the pass-through dims of q and k: two vectors copied
+    const int i0 = which == 2 ? 8 * j : rot + 8 * (j - half / 4);
+    float x1[4], x2[4];
+    sum_parts4(part, S, MN, src + i0, bias, col0 + i0, x1);
+    sum_parts4(part, S, MN, src + i0 + 4, bias, col0 + i0 + 4, x2);
+    vec16<float>::store(d + i0, x1);
+    vec16<float>::store(d + i0 + 4, x2);
   }
-  float v1[4], v2[4];
-  sum_parts4(part, S, MN, row + col(2, 8 * j), bias, col(2, 8 * j), v1);
-  sum_parts4(part, S, MN, row + col(2, 8 * j + 4), bias, col(2, 8 * j + 4), v2);
-  vec16<float>::store(v + dst_off + 8 * j, v1);
-  vec16<float>::store(v + dst_off + 8 * j + 4, v2);
 }
 
 // ============================================================================ host side
-// Row kernels: NT threads per row, NCH four-float chunks per thread.
-#define DIT_ROW_LAUNCH(KERNEL, C4, ...)                                                              \
-  do {                                                                                               \
-    const int nt_ = (C4) <= 1024 ? 256 : ((C4) <= 2048 ? 512 : 1024);                                \
-    const int nch_ = ((C4) + nt_ - 1) / nt_;                                                         \
-    if (nt_ == 256 && nch_ <= 1) hipLaunchKernelGGL((KERNEL<256, 1>), dim3(N), dim3(256), 0, s, __VA_ARGS__); \
-    else if (nt_ == 256 && nch_ <= 2) hipLaunchKernelGGL((KERNEL<256, 2>), dim3(N), dim3(256), 0, s, __VA_ARGS__); \
-    else if (nt_ == 256) hipLaunchKernelGGL((KERNEL<256, 4>), dim3(N), dim3(256), 0, s, __VA_ARGS__); \
-    else if (nt_ == 512) hipLaunchKernelGGL((KERNEL<512, 4>), dim3(N), dim3(512), 0, s, __VA_ARGS__); \
-    else if (nch_ <= 4) hipLaunchKernelGGL((KERNEL<1024, 4>), dim3(N), dim3(1024), 0, s, __VA_ARGS__); \
-    else if (nch_ <= 8) hipLaunchKernelGGL((KERNEL<1024, 8>), dim3(N), dim3(1024), 0, s, __VA_ARGS__); \
-    else return hipErrorInvalidValue;                                                                \
+// Row kernels: one workgroup per row, NCH four-float chunks per thread with
+// NCH the least of 1, 2, 3, 4, 6, 8 that keeps the workgroup within 1024
+// threads, and as many wavefronts as the row then needs: every load of a row
+// is issued at once, by as many wavefronts as possible.
+#define DIT_ROW_LAUNCH(KERNEL, C4, ...)                                                               \
+  do {                                                                                                \
+    const int c4_ = (C4);                                                                             \
+    const int nch_ = c4_ <= 1024 ? 1 : c4_ <= 2048 ? 2 : c4_ <= 3072 ? 3 : c4_ <= 4096 ? 4             \
+                     : c4_ <= 6144 ? 6 : 8;                                                           \
+    const int nt_ = ((c4_ + nch_ - 1) / nch_ + 63) / 64 * 64;                                         \
+    switch (nch_) {                                                                                   \
+      case 1: hipLaunchKernelGGL((KERNEL<1>), dim3(N), dim3(nt_), 0, s, __VA_ARGS__); break;         \
+      case 2: hipLaunchKernelGGL((KERNEL<2>), dim3(N), dim3(nt_), 0, s, __VA_ARGS__); break;         \
+      case 3: hipLaunchKernelGGL((KERNEL<3>), dim3(N), dim3(nt_), 0, s, __VA_ARGS__); break;         \
+      case 4: hipLaunchKernelGGL((KERNEL<4>), dim3(N), dim3(nt_), 0, s, __VA_ARGS__); break;         \
+      case 6: hipLaunchKernelGGL((KERNEL<6>), dim3(N), dim3(nt_), 0, s, __VA_ARGS__); break;         \
+      default: hipLaunchKernelGGL((KERNEL<8>), dim3(N), dim3(nt_), 0, s, __VA_ARGS__); break;        \
+    }                                                                                                 \
   } while (0)
 
 bool fused_f32_supported(int D, int F) {
@@ -349,7 +348,7 @@ hipError_t rope_part(int N, int H, int hd, int rot, int S, const double* part, c
   if (N == 0) return hipSuccess;
   if (!rope_split_supported(false, hd, rot)) return hipErrorInvalidValue;
   LaunchScope scope_(kCntRopeSplit, s);
-  const int64_t total = static_cast<int64_t>(N) * H * (hd / 8);
+  const int64_t total = static_cast<int64_t>(N) * H * 3 * (hd / 8);
   hipLaunchKernelGGL(rope_part_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s, N, H, hd,
                      rot, S, part, bias, cos, sin, q, k, v);
   return hipGetLastError();

@@ -452,8 +452,11 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
 // Split count from (N, K) and the device alone, so a row's result never
 // depends on M.  One workgroup fits a CU (120 KB of LDS), so for a single row
 // tile the launch runs in ceil(tiles_n * s / CUs) rounds of ceil(steps / s) K
-// steps each; s minimises that product plus a small charge per split for its
-// partial (written and re-read), with splits of >= 8 steps and <= 16384 of K.
+// steps each.  Measured on MI355X: a K step takes ~1.1 us, a round adds ~5
+// steps of fixed cost (first copies in flight, epilogue), and each split adds
+// an fp64 partial of the row tile that is written and read back once (192 N
+// 16 bytes at ~4.5 TB/s, i.e. N / 1600 steps).  s minimises the sum, with
+// splits of >= 8 steps and <= 16384 of K.
 static int go_cus() {
   static int cus = 0;
   if (cus == 0) {
@@ -473,11 +476,12 @@ static int go_splits(int N, int K) {
   if (hi > 64) hi = 64;
   if (hi < lo) hi = lo;
   if (lo < 1) lo = 1;
+  const double part_steps = N / 1600.0;
   int best = lo;
   double best_cost = 1e30;
   for (int sp = lo; sp <= hi; ++sp) {
     const int rounds = (tiles_n * sp + cus - 1) / cus;
-    const double cost = static_cast<double>(rounds) * ((steps + sp - 1) / sp) + 0.5 * sp;
+    const double cost = static_cast<double>(rounds) * ((steps + sp - 1) / sp + 5) + part_steps * sp;
     if (cost < best_cost) best_cost = cost, best = sp;
   }
   return best;
