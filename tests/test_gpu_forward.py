@@ -63,6 +63,22 @@ def test_c1_tiny_f32_parity(H):
     assert c["resid_norm_slice"] > 0 and c["silu_slice"] > 0
 
 
+# fp32 stream at widths that reach the fused row kernels' rarer paths: an ffn
+# that is not a multiple of 32 (zero slices pad the MLP-out GEMM's K), more
+# than eight split-K partials (MLP out: 96 x 8200 takes 32 splits), LayerNorm
+# and the swapped [value | gate] projection.
+C1_RAGGED = scaled(S.get_config("c1"), hidden=96, n_heads=3, ffn=8200, norm="layer", mlp="value_gate",
+                   segments=(Segment(0, (3, 3, 4), 0), Segment(0, (2, 5, 5), 0)))
+
+
+def test_f32_ragged_ffn_many_splits_parity(H):
+    cfg = C1_RAGGED
+    assert H.dit.dit_gemm_splits(cfg.hidden, cfg.ffn) > 8
+    r, w, got = _run(H, cfg)
+    ref = _oracle(cfg, w, r.inp)
+    assert_f32_close(got["x"], ref["x"], what="ragged fp32 forward")
+
+
 def test_c2_music_f32_reduced_depth_parity(H):
     cfg = scaled(S.get_config("c2"), n_blocks=2)
     r, w, got = _run(H, cfg)

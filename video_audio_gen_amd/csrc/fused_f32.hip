@@ -40,21 +40,30 @@ __device__ __forceinline__ void add_parts4(const double* __restrict__ p, size_t 
   }
 }
 
+// SF > 0: the split count is the compile-time SF (no branch, so a thread's
+// loads for all its columns can be in flight together); SF = 0: S at run time.
+template <int SF>
 __device__ __forceinline__ void sum_parts4(const double* __restrict__ part, int S, size_t MN, size_t off,
                                            const float* __restrict__ bias, int col, float* out) {
   double v[4] = {0.0, 0.0, 0.0, 0.0};
   const double* p = part + off;
-  int s = 0;
-  for (; s + 8 <= S; s += 8) add_parts4<8>(p + s * MN, MN, v);
-  switch (S - s) {  // uniform
-    case 1: add_parts4<1>(p + s * MN, MN, v); break;
-    case 2: add_parts4<2>(p + s * MN, MN, v); break;
-    case 3: add_parts4<3>(p + s * MN, MN, v); break;
-    case 4: add_parts4<4>(p + s * MN, MN, v); break;
-    case 5: add_parts4<5>(p + s * MN, MN, v); break;
-    case 6: add_parts4<6>(p + s * MN, MN, v); break;
-    case 7: add_parts4<7>(p + s * MN, MN, v); break;
-    default: break;
+  if constexpr (SF > 0) {
+#pragma unroll
+    for (int s = 0; s + 8 <= SF; s += 8) add_parts4<8>(p + s * MN, MN, v);
+    if constexpr (SF % 8 > 0) add_parts4<SF % 8>(p + (SF / 8 * 8) * MN, MN, v);
+  } else {
+    int s = 0;
+    for (; s + 8 <= S; s += 8) add_parts4<8>(p + s * MN, MN, v);
+    switch (S - s) {  // uniform
+      case 1: add_parts4<1>(p + s * MN, MN, v); break;
+      case 2: add_parts4<2>(p + s * MN, MN, v); break;
+      case 3: add_parts4<3>(p + s * MN, MN, v); break;
+      case 4: add_parts4<4>(p + s * MN, MN, v); break;
+      case 5: add_parts4<5>(p + s * MN, MN, v); break;
+      case 6: add_parts4<6>(p + s * MN, MN, v); break;
+      case 7: add_parts4<7>(p + s * MN, MN, v); break;
+      default: break;
+    }
   }
   if (bias != nullptr) {
     const float4 bb = *reinterpret_cast<const float4*>(bias + col);
@@ -121,7 +130,7 @@ __device__ __forceinline__ void slice_row(float (*y)[4], int C4, int row, int R,
 // norm in fp64 (LayerNorm when norm == 1, else RmsNorm), modulated by
 // (1 + scale) and shift from nmod when nmod is non-null, rounded to fp32 and
 // either sliced into sl (rows N, K = D) or stored to y.
-template <int NCH>
+template <int NCH, int SF>
 __global__ __launch_bounds__(1024) void resid_norm_slice_kernel(
     int N, int D, int S, const double* __restrict__ part, const float* __restrict__ bias,
     const float* __restrict__ gmod, int gate_k, const float* __restrict__ nmod, int shift_k, int scale_k,
@@ -144,7 +153,7 @@ __global__ __launch_bounds__(1024) void resid_norm_slice_kernel(
       v[i][0] = x0.x; v[i][1] = x0.y; v[i][2] = x1.x; v[i][3] = x1.y;
       if (part != nullptr) {
         float a[4];
-        sum_parts4(part, S, static_cast<size_t>(N) * D, static_cast<size_t>(row) * D + 4 * c, bias, 4 * c, a);
+        sum_parts4<SF>(part, S, static_cast<size_t>(N) * D, static_cast<size_t>(row) * D + 4 * c, bias, 4 * c, a);
         const float4 g = reinterpret_cast<const float4*>(gmod + (static_cast<size_t>(cr) * 6 + gate_k) * D)[c];
         v[i][0] += static_cast<double>(g.x) * static_cast<double>(a[0]);
         v[i][1] += static_cast<double>(g.y) * static_cast<double>(a[1]);
@@ -214,7 +223,7 @@ __global__ __launch_bounds__(1024) void resid_norm_slice_kernel(
 // One workgroup per token row of the [gate | up] projection (2F columns):
 // m = silu(g) * u evaluated in fp64 and rounded once, then sliced (rows N,
 // K = F).
-template <int NCH>
+template <int NCH, int SF>
 __global__ __launch_bounds__(1024) void silu_slice_kernel(int N, int F, int S, const double* __restrict__ part,
                                                        const float* __restrict__ bias, int8_t* __restrict__ sl) {
   __shared__ float redf[16];
@@ -228,8 +237,8 @@ __global__ __launch_bounds__(1024) void silu_slice_kernel(int N, int F, int S, c
     const int c = t + NT * i;
     if (c < F4) {
       float g[4], u[4];
-      sum_parts4(part, S, MN, base + 4 * c, bias, 4 * c, g);
-      sum_parts4(part, S, MN, base + F + 4 * c, bias, F + 4 * c, u);
+      sum_parts4<SF>(part, S, MN, base + 4 * c, bias, 4 * c, g);
+      sum_parts4<SF>(part, S, MN, base + F + 4 * c, bias, F + 4 * c, u);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const double gd = g[e];
@@ -249,6 +258,7 @@ __global__ __launch_bounds__(1024) void silu_slice_kernel(int N, int F, int S, c
 // output is one rounding of its exact value).  Thread (n, h, which, j), j
 // fastest: for q and k, vector pair j of the rotated half (columns 4j and
 // rot/2 + 4j) or two pass-through vectors; for v, columns 8j .. 8j+7.
+template <int SF>
 __global__ __launch_bounds__(256) void rope_part_kernel(int N, int H, int hd, int rot, int S,
                                                        const double* __restrict__ part,
                                                        const float* __restrict__ bias,
@@ -274,8 +284,8 @@ __global__ __launch_bounds__(256) void rope_part_kernel(int N, int H, int hd, in
     const float4 sn = *reinterpret_cast<const float4*>(sinb + static_cast<size_t>(n) * half + i0);
     const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
     float x1[4], x2[4], o1[4], o2[4];
-    sum_parts4(part, S, MN, src + i0, bias, col0 + i0, x1);
-    sum_parts4(part, S, MN, src + i1, bias, col0 + i1, x2);
+    sum_parts4<SF>(part, S, MN, src + i0, bias, col0 + i0, x1);
+    sum_parts4<SF>(part, S, MN, src + i1, bias, col0 + i1, x2);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       o1[e] = static_cast<float>(double(x1[e]) * double(cc[e]) - double(x2[e]) * double(ss[e]));
@@ -287,8 +297,8 @@ __global__ __launch_bounds__(256) void rope_part_kernel(int N, int H, int hd, in
     // v, or the pass-through dims of q and k: two vectors copied
     const int i0 = which == 2 ? 8 * j : rot + 8 * (j - half / 4);
     float x1[4], x2[4];
-    sum_parts4(part, S, MN, src + i0, bias, col0 + i0, x1);
-    sum_parts4(part, S, MN, src + i0 + 4, bias, col0 + i0 + 4, x2);
+    sum_parts4<SF>(part, S, MN, src + i0, bias, col0 + i0, x1);
+    sum_parts4<SF>(part, S, MN, src + i0 + 4, bias, col0 + i0 + 4, x2);
     vec16<float>::store(d + i0, x1);
     vec16<float>::store(d + i0 + 4, x2);
   }
@@ -299,37 +309,68 @@ __global__ __launch_bounds__(256) void rope_part_kernel(int N, int H, int hd, in
 // NCH the least of 1, 2, 3, 4, 6, 8 that keeps the workgroup within 1024
 // threads, and as many wavefronts as the row then needs: every load of a row
 // is issued at once, by as many wavefronts as possible.
-#define DIT_ROW_LAUNCH(KERNEL, C4, ...)                                                               \
-  do {                                                                                                \
-    const int c4_ = (C4);                                                                             \
-    const int nch_ = c4_ <= 1024 ? 1 : c4_ <= 2048 ? 2 : c4_ <= 3072 ? 3 : c4_ <= 4096 ? 4             \
-                     : c4_ <= 6144 ? 6 : 8;                                                           \
-    const int nt_ = ((c4_ + nch_ - 1) / nch_ + 63) / 64 * 64;                                         \
-    switch (nch_) {                                                                                   \
-      case 1: hipLaunchKernelGGL((KERNEL<1>), dim3(N), dim3(nt_), 0, s, __VA_ARGS__); break;         \
-      case 2: hipLaunchKernelGGL((KERNEL<2>), dim3(N), dim3(nt_), 0, s, __VA_ARGS__); break;         \
-      case 3: hipLaunchKernelGGL((KERNEL<3>), dim3(N), dim3(nt_), 0, s, __VA_ARGS__); break;         \
-      case 4: hipLaunchKernelGGL((KERNEL<4>), dim3(N), dim3(nt_), 0, s, __VA_ARGS__); break;         \
-      case 6: hipLaunchKernelGGL((KERNEL<6>), dim3(N), dim3(nt_), 0, s, __VA_ARGS__); break;         \
-      default: hipLaunchKernelGGL((KERNEL<8>), dim3(N), dim3(nt_), 0, s, __VA_ARGS__); break;        \
-    }                                                                                                 \
-  } while (0)
+// One workgroup per row, NCH four-float chunks per thread with NCH the least
+// of 1, 2, 3, 4, 6, 8 that keeps the workgroup within 1024 threads, and as
+// many wavefronts as the row then needs.  Split counts 1, 2, 4, 6 and 8 are
+// compile-time template arguments (every load of a thread in flight at once);
+// other counts are read at run time.
+static void row_shape(int c4, int* nch, int* nt) {
+  *nch = c4 <= 1024 ? 1 : c4 <= 2048 ? 2 : c4 <= 3072 ? 3 : c4 <= 4096 ? 4 : c4 <= 6144 ? 6 : 8;
+  *nt = ((c4 + *nch - 1) / *nch + 63) / 64 * 64;
+}
+
+#define DIT_SF_CASES(LAUNCH)                                   \
+  switch (S) {                                                 \
+    case 1: LAUNCH(1); break;                                  \
+    case 2: LAUNCH(2); break;                                  \
+    case 4: LAUNCH(4); break;                                  \
+    case 6: LAUNCH(6); break;                                  \
+    case 8: LAUNCH(8); break;                                  \
+    default: LAUNCH(0); break;                                 \
+  }
+
+template <int NCH>
+static void launch_rns(int nt, int N, int D, int S, const double* part, const float* bias, const float* gmod,
+                       int gate_k, const float* nmod, int shift_k, int scale_k, int norm, float eps,
+                       const int32_t* ci, double* x, int8_t* sl, float* y, hipStream_t s) {
+#define DIT_L(SF_)                                                                                     \
+  hipLaunchKernelGGL((resid_norm_slice_kernel<NCH, SF_>), dim3(N), dim3(nt), 0, s, N, D, S, part, bias, gmod, \
+                     gate_k, nmod, shift_k, scale_k, norm, eps, ci, x, sl, y)
+  DIT_SF_CASES(DIT_L)
+#undef DIT_L
+}
+
+template <int NCH>
+static void launch_silu(int nt, int N, int F, int S, const double* part, const float* bias, int8_t* sl,
+                        hipStream_t s) {
+#define DIT_L(SF_) hipLaunchKernelGGL((silu_slice_kernel<NCH, SF_>), dim3(N), dim3(nt), 0, s, N, F, S, part, bias, sl)
+  DIT_SF_CASES(DIT_L)
+#undef DIT_L
+}
 
 bool fused_f32_supported(int D, int F) {
-  return D > 0 && F > 0 && D % 4 == 0 && F % 4 == 0 && D / 4 <= 8192 && F / 4 <= 8192;
+  return D > 0 && F > 0 && D % 4 == 0 && F % 4 == 0 && D <= 8192 && F / 4 <= 8192;
 }
 
 hipError_t resid_norm_slice(int N, int D, int S, const double* part, const float* bias, const float* gmod, int gate_which,
                             const float* nmod, int norm_which, int norm, float eps, const int32_t* cond_idx, double* x,
                             void* slices, float* y, hipStream_t s) {
   if (N == 0) return hipSuccess;
-  if (D % 4 || D / 4 > 8192 || (slices != nullptr && y != nullptr)) return hipErrorInvalidValue;
+  // D <= 8192: at most two chunks per thread (the fp64 row stays in registers)
+  if (D % 4 || D > 8192 || (slices != nullptr && y != nullptr)) return hipErrorInvalidValue;
   LaunchScope scope_(kCntResidNormSlice, s);
   const int gate_k = gate_which == 0 ? 2 : 5;
   const int shift_k = norm_which == 0 ? 0 : 3, scale_k = norm_which == 0 ? 1 : 4;
-  const int D4 = D / 4;
-  DIT_ROW_LAUNCH(resid_norm_slice_kernel, D4, N, D, S, part, bias, gmod, gate_k, nmod, shift_k, scale_k, norm, eps,
-                 cond_idx, x, static_cast<int8_t*>(slices), y);
+  int nch, nt;
+  row_shape(D / 4, &nch, &nt);
+  int8_t* sl = static_cast<int8_t*>(slices);
+#define DIT_R(NCH_)                                                                                          \
+  launch_rns<NCH_>(nt, N, D, S, part, bias, gmod, gate_k, nmod, shift_k, scale_k, norm, eps, cond_idx, x, sl, y, s)
+  if (nch == 1)
+    DIT_R(1);
+  else
+    DIT_R(2);
+#undef DIT_R
   return hipGetLastError();
 }
 
@@ -337,11 +378,19 @@ hipError_t silu_slice(int N, int F, int S, const double* part, const float* bias
   if (N == 0) return hipSuccess;
   if (F % 4 || F / 4 > 8192) return hipErrorInvalidValue;
   LaunchScope scope_(kCntSiluSlice, s);
-  const int F4 = F / 4;
-  DIT_ROW_LAUNCH(silu_slice_kernel, F4, N, F, S, part, bias, static_cast<int8_t*>(slices));
+  int nch, nt;
+  row_shape(F / 4, &nch, &nt);
+  int8_t* sl = static_cast<int8_t*>(slices);
+  switch (nch) {
+    case 1: launch_silu<1>(nt, N, F, S, part, bias, sl, s); break;
+    case 2: launch_silu<2>(nt, N, F, S, part, bias, sl, s); break;
+    case 3: launch_silu<3>(nt, N, F, S, part, bias, sl, s); break;
+    case 4: launch_silu<4>(nt, N, F, S, part, bias, sl, s); break;
+    case 6: launch_silu<6>(nt, N, F, S, part, bias, sl, s); break;
+    default: launch_silu<8>(nt, N, F, S, part, bias, sl, s); break;
+  }
   return hipGetLastError();
 }
-#undef DIT_ROW_LAUNCH
 
 hipError_t rope_part(int N, int H, int hd, int rot, int S, const double* part, const float* bias, const float* cos,
                      const float* sin, float* q, float* k, float* v, hipStream_t s) {
@@ -349,9 +398,13 @@ hipError_t rope_part(int N, int H, int hd, int rot, int S, const double* part, c
   if (!rope_split_supported(false, hd, rot)) return hipErrorInvalidValue;
   LaunchScope scope_(kCntRopeSplit, s);
   const int64_t total = static_cast<int64_t>(N) * H * 3 * (hd / 8);
-  hipLaunchKernelGGL(rope_part_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s, N, H, hd,
-                     rot, S, part, bias, cos, sin, q, k, v);
+  const dim3 grid(static_cast<unsigned>((total + 255) / 256));
+#define DIT_L(SF_) \
+  hipLaunchKernelGGL((rope_part_kernel<SF_>), grid, dim3(256), 0, s, N, H, hd, rot, S, part, bias, cos, sin, q, k, v)
+  DIT_SF_CASES(DIT_L)
+#undef DIT_L
   return hipGetLastError();
 }
+#undef DIT_SF_CASES
 
 }  // namespace dit
