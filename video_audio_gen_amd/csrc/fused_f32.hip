@@ -23,9 +23,9 @@
 namespace dit {
 
 // Columns col..col+3 of row `row` of a GEMM result [M, ncol] held as S fp64
-// split-K partials [S][M][ncol]: summed in split order from zero, bias added
-// last, rounded once.  Up to eight splits are loaded before any is added, so
-// their latencies overlap.
+// split-K partials [S][M][ncol]: summed in split order from zero, bias (never
+// null here) added last, rounded once.  Up to eight splits are loaded before
+// any is added, so their latencies overlap.
 template <int NS>
 __device__ __forceinline__ void add_parts4(const double* __restrict__ p, size_t MN, double* v) {
   double2 a[NS], b[NS];
@@ -45,6 +45,8 @@ __device__ __forceinline__ void add_parts4(const double* __restrict__ p, size_t 
 template <int SF>
 __device__ __forceinline__ void sum_parts4(const double* __restrict__ part, int S, size_t MN, size_t off,
                                            const float* __restrict__ bias, int col, float* out) {
+  // the bias first, so its load is in flight with the partials'
+  const float4 bb = *reinterpret_cast<const float4*>(bias + col);
   double v[4] = {0.0, 0.0, 0.0, 0.0};
   const double* p = part + off;
   if constexpr (SF > 0) {
@@ -65,13 +67,18 @@ __device__ __forceinline__ void sum_parts4(const double* __restrict__ part, int 
       default: break;
     }
   }
-  if (bias != nullptr) {
-    const float4 bb = *reinterpret_cast<const float4*>(bias + col);
-    v[0] += static_cast<double>(bb.x); v[1] += static_cast<double>(bb.y);
-    v[2] += static_cast<double>(bb.z); v[3] += static_cast<double>(bb.w);
-  }
+  v[0] += static_cast<double>(bb.x); v[1] += static_cast<double>(bb.y);
+  v[2] += static_cast<double>(bb.z); v[3] += static_cast<double>(bb.w);
 #pragma unroll
   for (int e = 0; e < 4; ++e) out[e] = static_cast<float>(v[e]);
+}
+
+// Workgroup barrier for LDS only: waits for this wave's LDS operations, not
+// for its global stores (__syncthreads() would also wait for the residual
+// row just stored).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
 }
 
 // Row reductions over the workgroup (blockDim.x a multiple of 64, <= 1024).
@@ -79,9 +86,9 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
   v = wave_sum_f64(v);
   const int nw = blockDim.x >> 6;
   if (nw == 1) return v;
-  __syncthreads();  // red may still be read by the previous reduction
+  lds_barrier();  // red may still be read by the previous reduction
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
+  lds_barrier();
   double t = 0.0;
   for (int i = 0; i < nw; ++i) t += red[i];
   return t;
@@ -91,9 +98,9 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   v = wave_max(v);
   const int nw = blockDim.x >> 6;
   if (nw == 1) return v;
-  __syncthreads();
+  lds_barrier();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
+  lds_barrier();
   float t = 0.f;
   for (int i = 0; i < nw; ++i) t = fmaxf(t, red[i]);
   return t;
@@ -144,27 +151,35 @@ __global__ __launch_bounds__(1024) void resid_norm_slice_kernel(
   double* xr = x + static_cast<size_t>(row) * D;
   double v[NCH][4];
   double s = 0.0;
+  // Every load is issued without a branch (a thread past the row's end reads
+  // its last chunk and drops it), so all of them are in flight at once.
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int c = t + NT * i;
-    if (c < D4) {
-      const double2 x0 = reinterpret_cast<const double2*>(xr + 4 * c)[0];
-      const double2 x1 = reinterpret_cast<const double2*>(xr + 4 * c)[1];
-      v[i][0] = x0.x; v[i][1] = x0.y; v[i][2] = x1.x; v[i][3] = x1.y;
-      if (part != nullptr) {
-        float a[4];
-        sum_parts4<SF>(part, S, static_cast<size_t>(N) * D, static_cast<size_t>(row) * D + 4 * c, bias, 4 * c, a);
-        const float4 g = reinterpret_cast<const float4*>(gmod + (static_cast<size_t>(cr) * 6 + gate_k) * D)[c];
-        v[i][0] += static_cast<double>(g.x) * static_cast<double>(a[0]);
-        v[i][1] += static_cast<double>(g.y) * static_cast<double>(a[1]);
-        v[i][2] += static_cast<double>(g.z) * static_cast<double>(a[2]);
-        v[i][3] += static_cast<double>(g.w) * static_cast<double>(a[3]);
+    const int cc = c < D4 ? c : D4 - 1;
+    const double2 x0 = reinterpret_cast<const double2*>(xr + 4 * cc)[0];
+    const double2 x1 = reinterpret_cast<const double2*>(xr + 4 * cc)[1];
+    v[i][0] = x0.x; v[i][1] = x0.y; v[i][2] = x1.x; v[i][3] = x1.y;
+    if (part != nullptr) {  // uniform
+      const float4 g = reinterpret_cast<const float4*>(gmod + (static_cast<size_t>(cr) * 6 + gate_k) * D)[cc];
+      float a[4];
+      sum_parts4<SF>(part, S, static_cast<size_t>(N) * D, static_cast<size_t>(row) * D + 4 * cc, bias, 4 * cc, a);
+      v[i][0] += static_cast<double>(g.x) * static_cast<double>(a[0]);
+      v[i][1] += static_cast<double>(g.y) * static_cast<double>(a[1]);
+      v[i][2] += static_cast<double>(g.z) * static_cast<double>(a[2]);
+      v[i][3] += static_cast<double>(g.w) * static_cast<double>(a[3]);
+    }
+    if (c >= D4) v[i][0] = v[i][1] = v[i][2] = v[i][3] = 0.0;
+    s += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
+  }
+  if (part != nullptr) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = t + NT * i;
+      if (c < D4) {
         reinterpret_cast<double2*>(xr + 4 * c)[0] = make_double2(v[i][0], v[i][1]);
         reinterpret_cast<double2*>(xr + 4 * c)[1] = make_double2(v[i][2], v[i][3]);
       }
-      s += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
-    } else {
-      v[i][0] = v[i][1] = v[i][2] = v[i][3] = 0.0;
     }
   }
   if (sl == nullptr && y == nullptr) return;
@@ -235,17 +250,14 @@ __global__ __launch_bounds__(1024) void silu_slice_kernel(int N, int F, int S, c
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int c = t + NT * i;
-    if (c < F4) {
-      float g[4], u[4];
-      sum_parts4<SF>(part, S, MN, base + 4 * c, bias, 4 * c, g);
-      sum_parts4<SF>(part, S, MN, base + F + 4 * c, bias, F + 4 * c, u);
+    const int cc = c < F4 ? c : F4 - 1;  // branch-free loads, as in resid_norm_slice
+    float g[4], u[4];
+    sum_parts4<SF>(part, S, MN, base + 4 * cc, bias, 4 * cc, g);
+    sum_parts4<SF>(part, S, MN, base + F + 4 * cc, bias, F + 4 * cc, u);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const double gd = g[e];
-        m[i][e] = static_cast<float>(gd / (1.0 + exp(-gd)) * static_cast<double>(u[e]));
-      }
-    } else {
-      m[i][0] = m[i][1] = m[i][2] = m[i][3] = 0.f;
+    for (int e = 0; e < 4; ++e) {
+      const double gd = g[e];
+      m[i][e] = c < F4 ? static_cast<float>(gd / (1.0 + exp(-gd)) * static_cast<double>(u[e])) : 0.f;
     }
   }
   slice_row<NCH>(m, F4, row, N, F, redf, sl);
@@ -357,7 +369,8 @@ hipError_t resid_norm_slice(int N, int D, int S, const double* part, const float
                             void* slices, float* y, hipStream_t s) {
   if (N == 0) return hipSuccess;
   // D <= 8192: at most two chunks per thread (the fp64 row stays in registers)
-  if (D % 4 || D > 8192 || (slices != nullptr && y != nullptr)) return hipErrorInvalidValue;
+  if (D % 4 || D > 8192 || (slices != nullptr && y != nullptr) || (part != nullptr && bias == nullptr))
+    return hipErrorInvalidValue;
   LaunchScope scope_(kCntResidNormSlice, s);
   const int gate_k = gate_which == 0 ? 2 : 5;
   const int shift_k = norm_which == 0 ? 0 : 3, scale_k = norm_which == 0 ? 1 : 4;
@@ -376,7 +389,7 @@ hipError_t resid_norm_slice(int N, int D, int S, const double* part, const float
 
 hipError_t silu_slice(int N, int F, int S, const double* part, const float* bias, void* slices, hipStream_t s) {
   if (N == 0) return hipSuccess;
-  if (F % 4 || F / 4 > 8192) return hipErrorInvalidValue;
+  if (F % 4 || F / 4 > 8192 || bias == nullptr) return hipErrorInvalidValue;
   LaunchScope scope_(kCntSiluSlice, s);
   int nch, nt;
   row_shape(F / 4, &nch, &nt);
@@ -395,7 +408,7 @@ hipError_t silu_slice(int N, int F, int S, const double* part, const float* bias
 hipError_t rope_part(int N, int H, int hd, int rot, int S, const double* part, const float* bias, const float* cos,
                      const float* sin, float* q, float* k, float* v, hipStream_t s) {
   if (N == 0) return hipSuccess;
-  if (!rope_split_supported(false, hd, rot)) return hipErrorInvalidValue;
+  if (!rope_split_supported(false, hd, rot) || bias == nullptr) return hipErrorInvalidValue;
   LaunchScope scope_(kCntRopeSplit, s);
   const int64_t total = static_cast<int64_t>(N) * H * 3 * (hd / 8);
   const dim3 grid(static_cast<unsigned>((total + 255) / 256));

@@ -70,7 +70,8 @@ hipError_t silu_gate(bool bf16, int N, int F, const void* u, void* m, hipStream_
 hipError_t gated_residual(int N, int D, bool x_f64, void* x, const float* a, const float* mod, int which,
                           const int32_t* cond_idx, hipStream_t s);
 // ---- fused row kernels of the fp32 stream (fused_f32.hip); part: fp64 split-K
-// partials [S][N][cols] of the preceding gemm_f32_sliced, bias added after them.
+// partials [S][N][cols] of the preceding gemm_f32_sliced, bias (required with
+// part) added after them.
 // resid_norm_slice: with part, x += gate(gmod, which) * a; then the norm of x,
 // modulated from nmod (which) unless nmod is null, sliced into `slices` (rows
 // N, K = D) or stored to y, or neither when both are null.
