@@ -112,7 +112,9 @@ def test_config_validation(dit):
     lib = dit.load()
     bad = [scaled(S.get_config("c1"), hidden=130), scaled(S.get_config("c1"), rot_dim=40),
            scaled(S.get_config("c3"), head_dim=64, n_heads=96),  # bf16 attention is head_dim 128 only
-           scaled(S.get_config("c1"), norm_eps=0.0)]
+           scaled(S.get_config("c1"), norm_eps=0.0),
+           scaled(S.get_config("c1"), ffn=40000),  # the fp32 stream's SiLU row kernel: ffn <= 32768
+           scaled(S.get_config("c1"), ffn=514)]    # ffn a multiple of 4
     for cfg in bad:
         c = dit.make_config(cfg)
         n = ctypes.c_size_t()
@@ -138,3 +140,13 @@ def test_forward_requires_finalized_model(dit):
     rc = lib.dit_block_forward(None, 0, 1, 1, None, None, 0, None)
     assert rc == 1
     lib.dit_model_destroy(h)
+
+
+def test_gemm_splits_query(dit):
+    lib = dit.load()
+    n = ctypes.c_int()
+    # fp32 GEMM split count: a positive count for valid shapes, errors otherwise
+    assert lib.dit_gemm_splits(dit.DIT_F32, 2560, 10240, ctypes.byref(n)) == 0 and n.value >= 1
+    assert lib.dit_gemm_splits(dit.DIT_BF16, 2560, 10240, ctypes.byref(n)) == 1
+    assert lib.dit_gemm_splits(dit.DIT_F32, 0, 10240, ctypes.byref(n)) == 1
+    assert lib.dit_gemm_splits(dit.DIT_F32, 2560, 10240, None) == 1
