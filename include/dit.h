@@ -222,7 +222,10 @@ int dit_modulation(dit_model* m, const dit_batch* b, int block0, int n_blocks,
  * mod_dev [n_cond, 6, D] float32 (this block's rows of dit_modulation).  An
  * fp32 model carries its residual stream in float64 inside the library (here:
  * widened on entry, rounded to float32 once on exit); a bf16 model's is the
- * float32 x_dev itself. */
+ * float32 x_dev itself.  In an fp32 model every GEMM result is still rounded
+ * once to float32 before it is used, as dit_gemm returns it: the kernel after
+ * each GEMM sums its fp64 split-K partials in split order and adds the bias
+ * (the fused kernels change where that happens, not the values). */
 int dit_block_forward(dit_model* m, int block, float* x_dev, const float* mod_dev,
                       const dit_batch* b, void* ws_dev, size_t ws_bytes, dit_stream_t stream);
 
