@@ -47,8 +47,10 @@ def test_gemm_bf16(dit, M, N, K):
     assert_bf16_rounded(from_dev(C16), ref, "gemm bf16 -> bf16", slack=1e-5)
 
 
+# (172, 20480, 2560): the music model's MLP-in projection; (60, 6144, 16384):
+# a long K with several splits.
 @pytest.mark.parametrize("M,N,K", [(1, 4, 4), (100, 70, 36), (172, 2560, 2560), (172, 2560, 10240), (160, 1024, 128),
-                                   (400, 300, 96), (70, 130, 20000)])
+                                   (400, 300, 96), (70, 130, 20000), (172, 20480, 2560), (60, 6144, 16384)])
 def test_gemm_f32_int8_slices(dit, M, N, K):
     rng = np.random.default_rng(M * 7 + N + K)
     A = rng.standard_normal((M, K)).astype(np.float32)
@@ -90,6 +92,15 @@ def test_gemm_packed_equals_alone_bits(dit):
     dit.dit_gemm(Af[86:].contiguous(), Bf, None, f_part)
     torch.cuda.synchronize()
     assert torch.equal(f_full[86:], f_part)
+    # a wide fp32 GEMM (N 20480, K 2560): two row tiles against one
+    As = torch.from_numpy(rng.standard_normal((300, 2560)).astype(np.float32)).cuda()
+    Bs = torch.from_numpy((rng.standard_normal((20480, 2560)) * 0.02).astype(np.float32)).cuda()
+    s_full = torch.empty(300, 20480, device="cuda")
+    s_part = torch.empty(86, 20480, device="cuda")
+    dit.dit_gemm(As, Bs, None, s_full)
+    dit.dit_gemm(As[150:236].contiguous(), Bs, None, s_part)
+    torch.cuda.synchronize()
+    assert torch.equal(s_full[150:236], s_part)
 
 
 # ----------------------------------------------------------------------------- modulate + norm
