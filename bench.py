@@ -143,8 +143,10 @@ def attention_flops(cfg):
     return per_block * cfg.n_blocks
 
 
-def cpu_baseline(cfg, weights_fn, islands, inp, sample_blocks: int, log=log):
-    """Time the oracle on `sample_blocks` blocks of this workload and scale to a forward."""
+def cpu_baseline(cfg, weights_fn, islands, inp, sample_blocks: int, log=log, min_seconds: float = 10.0):
+    """Time the oracle's block forward on this workload's tokens, cycling over the
+    weights of `sample_blocks` blocks until at least `min_seconds` of CPU work
+    (at least one pass), and scale the per-block time to a forward."""
     import numpy as np
     import oracle as O
     try:
@@ -162,16 +164,21 @@ def cpu_baseline(cfg, weights_fn, islands, inp, sample_blocks: int, log=log):
     x = np.random.default_rng(0).standard_normal((cfg.n_tokens, cfg.hidden))
     ws = [weights_fn(b) for b in range(sample_blocks)]
     t0 = time.perf_counter()
-    for b in range(sample_blocks):
+    run = 0
+    while True:
+        b = run % sample_blocks
         mod = O.adaln_table(cfg, ws[b], b, emb, mode)
         x = O.block_forward(cfg, x, mod, ws[b], b, lay, cos, sin, mode, threads=min(cores, 16))
-    dt = time.perf_counter() - t0
-    per_forward = dt / sample_blocks * cfg.n_blocks
-    log(f"cpu oracle: {sample_blocks} blocks in {dt:.2f}s -> {per_forward:.2f}s per forward")
+        run += 1
+        dt = time.perf_counter() - t0
+        if run >= sample_blocks and dt >= min_seconds:
+            break
+    per_forward = dt / run * cfg.n_blocks
+    log(f"cpu oracle: {run} block forwards in {dt:.2f}s -> {per_forward:.2f}s per forward")
     return {"value": cfg.n_tokens / per_forward, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{sample_blocks} of {cfg.n_blocks} blocks ({mode}, numpy/OpenBLAS), "
-                      f"{dt:.2f}s, scaled x{cfg.n_blocks / sample_blocks:.1f} to one forward "
-                      f"({per_forward:.1f}s)"}
+            "sample": f"{run} block forwards over the weights of {sample_blocks} of {cfg.n_blocks} blocks "
+                      f"({mode}, numpy/OpenBLAS, {cfg.n_tokens} tokens), {dt:.1f}s, scaled to one "
+                      f"{cfg.n_blocks}-block forward ({per_forward:.1f}s)"}
 
 
 def main(argv=None):
