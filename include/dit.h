@@ -263,10 +263,12 @@ int dit_denoise_loop(dit_model* m, const dit_batch* b, float* latents_dev,
  * rounded once to float32 C.  ws holds B's and A's slices and split-K
  * partials (dit_gemm_workspace_bytes). */
 int dit_gemm_workspace_bytes(int dtype, int M, int N, int K, size_t* bytes);
-/* Split-K count of the fp32 GEMM for an [N, K] weight on the current device:
- * the number of fp64 partials [splits][M][N] that the block's fp32 GEMMs hand
- * to the row kernel after them (chosen from N, K and the compute-unit count
- * only, so a row's result never depends on M).  dtype must be DIT_F32. */
+/* Split-K slots of the fp32 GEMM for an [N, K] weight on the current device:
+ * the fp64 partials [splits][M][N] that the block's fp32 GEMMs hand to the
+ * row kernel after them (the most any column has: the first columns can take
+ * fewer splits than the last, to even out the last round of workgroups).
+ * Chosen from N, K and the compute-unit count only, so a row's result never
+ * depends on M.  dtype must be DIT_F32. */
 int dit_gemm_splits(int dtype, int N, int K, int* splits);
 int dit_gemm(int dtype, int M, int N, int K, const void* A, const void* B, const float* bias,
              void* C, int c_dtype, void* ws, size_t ws_bytes, dit_stream_t stream);

@@ -113,7 +113,7 @@ def test_config_validation(dit):
     bad = [scaled(S.get_config("c1"), hidden=130), scaled(S.get_config("c1"), rot_dim=40),
            scaled(S.get_config("c3"), head_dim=64, n_heads=96),  # bf16 attention is head_dim 128 only
            scaled(S.get_config("c1"), norm_eps=0.0),
-           scaled(S.get_config("c1"), ffn=40000),  # the fp32 stream's SiLU row kernel: ffn <= 32768
+           scaled(S.get_config("c1"), ffn=24580),  # the fp32 stream's SiLU row kernel: ffn <= 24576
            scaled(S.get_config("c1"), ffn=514)]    # ffn a multiple of 4
     for cfg in bad:
         c = dit.make_config(cfg)

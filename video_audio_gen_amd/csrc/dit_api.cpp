@@ -158,7 +158,7 @@ static int check_config(const dit_config* c) {
   if (bf) {
     if (c->hidden % 64 || c->ffn % 64) return set_error(DIT_E_UNSUPPORTED, "bf16 stream needs hidden and ffn multiples of 64");
   } else if (!fused_f32_supported(c->hidden, c->ffn)) {
-    return set_error(DIT_E_UNSUPPORTED, "fp32 stream needs ffn a multiple of 4 and <= 32768");
+    return set_error(DIT_E_UNSUPPORTED, "fp32 stream needs ffn a multiple of 4 and <= 24576");
   }
   if (c->cond_dim % 4) return set_error(DIT_E_UNSUPPORTED, "cond_dim must be a multiple of 4");
   return DIT_OK;
@@ -686,7 +686,7 @@ static int run_block_bf16(dit_model* m, int blk, float* x, const float* mod, con
 static int f32_prologue(const dit_model* m, double* x, const float* mod, const dit_batch* b, char* ws,
                         const WsPlan& p, hipStream_t s) {
   const dit_config& c = m->cfg;
-  DIT_HIP(resid_norm_slice(b->N, c.hidden, 0, nullptr, nullptr, nullptr, 0, mod, 0, c.norm, c.norm_eps, b->cond_dev, x,
+  DIT_HIP(resid_norm_slice(b->N, c.hidden, F32Splits{0, 0, c.hidden}, nullptr, nullptr, nullptr, 0, mod, 0, c.norm, c.norm_eps, b->cond_dev, x,
                            ws + p.sl, nullptr, s));
   return DIT_OK;
 }
@@ -703,16 +703,16 @@ static int run_block_f32(dit_model* m, int blk, double* x, const float* mod, con
   float* v = k + static_cast<size_t>(N) * D;
   float* o = reinterpret_cast<float*>(ws + p.o);
   DIT_HIP(gemm_f32_sliced(N, 3 * D, D, sl, w.qkv_w, part, s));
-  DIT_HIP(rope_part(N, H, hd, c.rot_dim, gemm_f32_splits(3 * D, D), part, w.qkv_b, b->cos_dev, b->sin_dev, q, k, v, s));
+  DIT_HIP(rope_part(N, H, hd, c.rot_dim, gemm_f32_split_groups(3 * D, D), part, w.qkv_b, b->cos_dev, b->sin_dev, q, k, v, s));
   DIT_HIP(attention_f32(N, H, hd, b->n_segs, b->cu_dev, b->max_seqlen, q, k, v, o, s));
   DIT_HIP(slice_rows(N, D, o, sl, s));
   DIT_HIP(gemm_f32_sliced(N, D, D, sl, w.out_w, part, s));
-  DIT_HIP(resid_norm_slice(N, D, gemm_f32_splits(D, D), part, w.out_b, mod, 0, mod, 1, c.norm, c.norm_eps, b->cond_dev, x,
+  DIT_HIP(resid_norm_slice(N, D, gemm_f32_split_groups(D, D), part, w.out_b, mod, 0, mod, 1, c.norm, c.norm_eps, b->cond_dev, x,
                            sl, nullptr, s));
   DIT_HIP(gemm_f32_sliced(N, 2 * F, D, sl, w.in_w, part, s));
-  DIT_HIP(silu_slice(N, F, gemm_f32_splits(2 * F, D), part, w.in_b, sl, s));
+  DIT_HIP(silu_slice(N, F, gemm_f32_split_groups(2 * F, D), part, w.in_b, sl, s));
   DIT_HIP(gemm_f32_sliced(N, D, F, sl, w.mo_w, part, s));
-  DIT_HIP(resid_norm_slice(N, D, gemm_f32_splits(D, F), part, w.mo_b, mod, 1, next_mod, 0, c.norm, c.norm_eps,
+  DIT_HIP(resid_norm_slice(N, D, gemm_f32_split_groups(D, F), part, w.mo_b, mod, 1, next_mod, 0, c.norm, c.norm_eps,
                            b->cond_dev, x, next_mod != nullptr ? sl : nullptr, y, s));
   return DIT_OK;
 }

@@ -73,6 +73,17 @@ __device__ __forceinline__ void sum_parts4(const double* __restrict__ part, int 
   for (int e = 0; e < 4; ++e) out[e] = static_cast<float>(v[e]);
 }
 
+// Columns below cb carry s_lo partials, the others s_hi (the GEMM's split
+// groups); SF is the compile-time form of s_lo.
+template <int SF>
+__device__ __forceinline__ void sum_parts4g(const double* __restrict__ part, int s_lo, int s_hi, int cb, size_t MN,
+                                            size_t off, const float* __restrict__ bias, int col, float* out) {
+  if (col < cb)
+    sum_parts4<SF>(part, s_lo, MN, off, bias, col, out);
+  else
+    sum_parts4<0>(part, s_hi, MN, off, bias, col, out);
+}
+
 // Workgroup barrier for LDS only: waits for this wave's LDS operations, not
 // for its global stores (__syncthreads() would also wait for the residual
 // row just stored).
@@ -139,7 +150,7 @@ __device__ __forceinline__ void slice_row(float (*y)[4], int C4, int row, int R,
 // either sliced into sl (rows N, K = D) or stored to y.
 template <int NCH, int SF>
 __global__ __launch_bounds__(1024) void resid_norm_slice_kernel(
-    int N, int D, int S, const double* __restrict__ part, const float* __restrict__ bias,
+    int N, int D, int S, int S_hi, int cb, const double* __restrict__ part, const float* __restrict__ bias,
     const float* __restrict__ gmod, int gate_k, const float* __restrict__ nmod, int shift_k, int scale_k,
     int norm, float eps, const int32_t* __restrict__ cond_idx, double* __restrict__ x, int8_t* __restrict__ sl,
     float* __restrict__ y) {
@@ -163,7 +174,8 @@ __global__ __launch_bounds__(1024) void resid_norm_slice_kernel(
     if (part != nullptr) {  // uniform
       const float4 g = reinterpret_cast<const float4*>(gmod + (static_cast<size_t>(cr) * 6 + gate_k) * D)[cc];
       float a[4];
-      sum_parts4<SF>(part, S, static_cast<size_t>(N) * D, static_cast<size_t>(row) * D + 4 * cc, bias, 4 * cc, a);
+      sum_parts4g<SF>(part, S, S_hi, cb, static_cast<size_t>(N) * D, static_cast<size_t>(row) * D + 4 * cc, bias, 4 * cc,
+                      a);
       v[i][0] += static_cast<double>(g.x) * static_cast<double>(a[0]);
       v[i][1] += static_cast<double>(g.y) * static_cast<double>(a[1]);
       v[i][2] += static_cast<double>(g.z) * static_cast<double>(a[2]);
@@ -239,7 +251,8 @@ __global__ __launch_bounds__(1024) void resid_norm_slice_kernel(
 // m = silu(g) * u evaluated in fp64 and rounded once, then sliced (rows N,
 // K = F).
 template <int NCH, int SF>
-__global__ __launch_bounds__(1024) void silu_slice_kernel(int N, int F, int S, const double* __restrict__ part,
+__global__ __launch_bounds__(1024) void silu_slice_kernel(int N, int F, int S, int S_hi, int cb,
+                                                        const double* __restrict__ part,
                                                        const float* __restrict__ bias, int8_t* __restrict__ sl) {
   __shared__ float redf[16];
   const int row = blockIdx.x, t = threadIdx.x, NT = blockDim.x;
@@ -252,8 +265,8 @@ __global__ __launch_bounds__(1024) void silu_slice_kernel(int N, int F, int S, c
     const int c = t + NT * i;
     const int cc = c < F4 ? c : F4 - 1;  // branch-free loads, as in resid_norm_slice
     float g[4], u[4];
-    sum_parts4<SF>(part, S, MN, base + 4 * cc, bias, 4 * cc, g);
-    sum_parts4<SF>(part, S, MN, base + F + 4 * cc, bias, F + 4 * cc, u);
+    sum_parts4g<SF>(part, S, S_hi, cb, MN, base + 4 * cc, bias, 4 * cc, g);
+    sum_parts4g<SF>(part, S, S_hi, cb, MN, base + F + 4 * cc, bias, F + 4 * cc, u);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const double gd = g[e];
@@ -271,7 +284,7 @@ __global__ __launch_bounds__(1024) void silu_slice_kernel(int N, int F, int S, c
 // fastest: for q and k, vector pair j of the rotated half (columns 4j and
 // rot/2 + 4j) or two pass-through vectors; for v, columns 8j .. 8j+7.
 template <int SF>
-__global__ __launch_bounds__(256) void rope_part_kernel(int N, int H, int hd, int rot, int S,
+__global__ __launch_bounds__(256) void rope_part_kernel(int N, int H, int hd, int rot, int S, int S_hi, int cb,
                                                        const double* __restrict__ part,
                                                        const float* __restrict__ bias,
                                                        const float* __restrict__ cosb,
@@ -296,8 +309,8 @@ __global__ __launch_bounds__(256) void rope_part_kernel(int N, int H, int hd, in
     const float4 sn = *reinterpret_cast<const float4*>(sinb + static_cast<size_t>(n) * half + i0);
     const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
     float x1[4], x2[4], o1[4], o2[4];
-    sum_parts4<SF>(part, S, MN, src + i0, bias, col0 + i0, x1);
-    sum_parts4<SF>(part, S, MN, src + i1, bias, col0 + i1, x2);
+    sum_parts4g<SF>(part, S, S_hi, cb, MN, src + i0, bias, col0 + i0, x1);
+    sum_parts4g<SF>(part, S, S_hi, cb, MN, src + i1, bias, col0 + i1, x2);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       o1[e] = static_cast<float>(double(x1[e]) * double(cc[e]) - double(x2[e]) * double(ss[e]));
@@ -309,8 +322,8 @@ __global__ __launch_bounds__(256) void rope_part_kernel(int N, int H, int hd, in
     // v, or the pass-through dims of q and k: two vectors copied
     const int i0 = which == 2 ? 8 * j : rot + 8 * (j - half / 4);
     float x1[4], x2[4];
-    sum_parts4<SF>(part, S, MN, src + i0, bias, col0 + i0, x1);
-    sum_parts4<SF>(part, S, MN, src + i0 + 4, bias, col0 + i0 + 4, x2);
+    sum_parts4g<SF>(part, S, S_hi, cb, MN, src + i0, bias, col0 + i0, x1);
+    sum_parts4g<SF>(part, S, S_hi, cb, MN, src + i0 + 4, bias, col0 + i0 + 4, x2);
     vec16<float>::store(d + i0, x1);
     vec16<float>::store(d + i0 + 4, x2);
   }
@@ -342,29 +355,30 @@ static void row_shape(int c4, int* nch, int* nt) {
   }
 
 template <int NCH>
-static void launch_rns(int nt, int N, int D, int S, const double* part, const float* bias, const float* gmod,
+static void launch_rns(int nt, int N, int D, int S, int S_hi, int cb, const double* part, const float* bias, const float* gmod,
                        int gate_k, const float* nmod, int shift_k, int scale_k, int norm, float eps,
                        const int32_t* ci, double* x, int8_t* sl, float* y, hipStream_t s) {
 #define DIT_L(SF_)                                                                                     \
-  hipLaunchKernelGGL((resid_norm_slice_kernel<NCH, SF_>), dim3(N), dim3(nt), 0, s, N, D, S, part, bias, gmod, \
+  hipLaunchKernelGGL((resid_norm_slice_kernel<NCH, SF_>), dim3(N), dim3(nt), 0, s, N, D, S, S_hi, cb, part, bias, gmod, \
                      gate_k, nmod, shift_k, scale_k, norm, eps, ci, x, sl, y)
   DIT_SF_CASES(DIT_L)
 #undef DIT_L
 }
 
 template <int NCH>
-static void launch_silu(int nt, int N, int F, int S, const double* part, const float* bias, int8_t* sl,
-                        hipStream_t s) {
-#define DIT_L(SF_) hipLaunchKernelGGL((silu_slice_kernel<NCH, SF_>), dim3(N), dim3(nt), 0, s, N, F, S, part, bias, sl)
+static void launch_silu(int nt, int N, int F, int S, int S_hi, int cb, const double* part, const float* bias,
+                        int8_t* sl, hipStream_t s) {
+#define DIT_L(SF_) \
+  hipLaunchKernelGGL((silu_slice_kernel<NCH, SF_>), dim3(N), dim3(nt), 0, s, N, F, S, S_hi, cb, part, bias, sl)
   DIT_SF_CASES(DIT_L)
 #undef DIT_L
 }
 
 bool fused_f32_supported(int D, int F) {
-  return D > 0 && F > 0 && D % 4 == 0 && F % 4 == 0 && D <= 8192 && F / 4 <= 8192;
+  return D > 0 && F > 0 && D % 4 == 0 && F % 4 == 0 && D <= 8192 && F <= 24576;
 }
 
-hipError_t resid_norm_slice(int N, int D, int S, const double* part, const float* bias, const float* gmod, int gate_which,
+hipError_t resid_norm_slice(int N, int D, F32Splits sg, const double* part, const float* bias, const float* gmod, int gate_which,
                             const float* nmod, int norm_which, int norm, float eps, const int32_t* cond_idx, double* x,
                             void* slices, float* y, hipStream_t s) {
   if (N == 0) return hipSuccess;
@@ -377,8 +391,9 @@ hipError_t resid_norm_slice(int N, int D, int S, const double* part, const float
   int nch, nt;
   row_shape(D / 4, &nch, &nt);
   int8_t* sl = static_cast<int8_t*>(slices);
+  const int S = sg.s_lo;
 #define DIT_R(NCH_)                                                                                          \
-  launch_rns<NCH_>(nt, N, D, S, part, bias, gmod, gate_k, nmod, shift_k, scale_k, norm, eps, cond_idx, x, sl, y, s)
+  launch_rns<NCH_>(nt, N, D, S, sg.s_hi, sg.col_split, part, bias, gmod, gate_k, nmod, shift_k, scale_k, norm, eps, cond_idx, x, sl, y, s)
   if (nch == 1)
     DIT_R(1);
   else
@@ -387,25 +402,25 @@ hipError_t resid_norm_slice(int N, int D, int S, const double* part, const float
   return hipGetLastError();
 }
 
-hipError_t silu_slice(int N, int F, int S, const double* part, const float* bias, void* slices, hipStream_t s) {
+hipError_t silu_slice(int N, int F, F32Splits sg, const double* part, const float* bias, void* slices, hipStream_t s) {
   if (N == 0) return hipSuccess;
-  if (F % 4 || F / 4 > 8192 || bias == nullptr) return hipErrorInvalidValue;
+  // F <= 24576: at most six chunks per thread
+  if (F % 4 || F > 24576 || bias == nullptr) return hipErrorInvalidValue;
   LaunchScope scope_(kCntSiluSlice, s);
   int nch, nt;
   row_shape(F / 4, &nch, &nt);
   int8_t* sl = static_cast<int8_t*>(slices);
   switch (nch) {
-    case 1: launch_silu<1>(nt, N, F, S, part, bias, sl, s); break;
-    case 2: launch_silu<2>(nt, N, F, S, part, bias, sl, s); break;
-    case 3: launch_silu<3>(nt, N, F, S, part, bias, sl, s); break;
-    case 4: launch_silu<4>(nt, N, F, S, part, bias, sl, s); break;
-    case 6: launch_silu<6>(nt, N, F, S, part, bias, sl, s); break;
-    default: launch_silu<8>(nt, N, F, S, part, bias, sl, s); break;
+    case 1: launch_silu<1>(nt, N, F, sg.s_lo, sg.s_hi, sg.col_split, part, bias, sl, s); break;
+    case 2: launch_silu<2>(nt, N, F, sg.s_lo, sg.s_hi, sg.col_split, part, bias, sl, s); break;
+    case 3: launch_silu<3>(nt, N, F, sg.s_lo, sg.s_hi, sg.col_split, part, bias, sl, s); break;
+    case 4: launch_silu<4>(nt, N, F, sg.s_lo, sg.s_hi, sg.col_split, part, bias, sl, s); break;
+    default: launch_silu<6>(nt, N, F, sg.s_lo, sg.s_hi, sg.col_split, part, bias, sl, s); break;
   }
   return hipGetLastError();
 }
 
-hipError_t rope_part(int N, int H, int hd, int rot, int S, const double* part, const float* bias, const float* cos,
+hipError_t rope_part(int N, int H, int hd, int rot, F32Splits sg, const double* part, const float* bias, const float* cos,
                      const float* sin, float* q, float* k, float* v, hipStream_t s) {
   if (N == 0) return hipSuccess;
   if (!rope_split_supported(false, hd, rot) || bias == nullptr) return hipErrorInvalidValue;
@@ -413,7 +428,9 @@ hipError_t rope_part(int N, int H, int hd, int rot, int S, const double* part, c
   const int64_t total = static_cast<int64_t>(N) * H * 3 * (hd / 8);
   const dim3 grid(static_cast<unsigned>((total + 255) / 256));
 #define DIT_L(SF_) \
-  hipLaunchKernelGGL((rope_part_kernel<SF_>), grid, dim3(256), 0, s, N, H, hd, rot, S, part, bias, cos, sin, q, k, v)
+  hipLaunchKernelGGL((rope_part_kernel<SF_>), grid, dim3(256), 0, s, N, H, hd, rot, S, sg.s_hi, sg.col_split, part, \
+                     bias, cos, sin, q, k, v)
+  const int S = sg.s_lo;
   DIT_SF_CASES(DIT_L)
 #undef DIT_L
   return hipGetLastError();

@@ -327,17 +327,23 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
                                                          const int8_t* __restrict__ Ap, const int32_t* __restrict__ Ae,
                                                          const int8_t* __restrict__ Bp, const int32_t* __restrict__ Be,
                                                          const float* __restrict__ bias, float* __restrict__ C,
-                                                         double* __restrict__ part, int splits, int steps_per_split,
-                                                         int tiles_m, int tiles_n) {
+                                                         double* __restrict__ part, int s1, int s2, int n1, int sps1,
+                                                         int sps2, int tiles_m, int tiles_n) {
   using namespace go;
   __shared__ uint4 smem[STAGES * STAGE];  // 120 KB
-  // Workgroups go to the 8 XCDs round-robin; each run of 256 gives XCD x the
-  // 32 consecutive items 32x .. 32x+31 of (row tile fastest, N tile, split),
-  // so the row tiles sharing a weight tile share an L2.
+  // Work items: N tiles 0 .. n1-1 in s1 splits of sps1 K steps, then the other
+  // N tiles in s2 splits of sps2 (the longer items first).  Workgroups go to
+  // the 8 XCDs round-robin; each run of 256 gives XCD x the 32 consecutive
+  // items 32x .. 32x+31 (row tile fastest, then N tile, then split), so the
+  // row tiles sharing a weight tile share an L2.
   const int w = (blockIdx.x / 256) * 256 + (blockIdx.x % 8) * 32 + (blockIdx.x / 8) % 32;
-  if (w >= tiles_m * tiles_n * splits) return;
-  const int tm = w % tiles_m, tn = (w / tiles_m) % tiles_n;
-  const int sp = w / (tiles_m * tiles_n);
+  const int items1 = n1 * s1, items2 = (tiles_n - n1) * s2;
+  if (w >= tiles_m * (items1 + items2)) return;
+  const int tm = w % tiles_m, it = w / tiles_m;
+  const bool first = it < items1;
+  const int tn = first ? it % n1 : n1 + (it - items1) % (tiles_n - n1);
+  const int sp = first ? it / n1 : (it - items1) / (tiles_n - n1);
+  const int steps_per_split = first ? sps1 : sps2;
   const int m0 = tm * BM, n0 = tn * BN;
   const int ksteps = Kp / BK;
   const int t_begin = sp * steps_per_split;
@@ -431,7 +437,7 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
   if (gn >= N) return;
   const int fe = Be[gn];
   // C null: fp64 partials for a consumer that sums them itself (any split count)
-  const bool direct = splits == 1 && C != nullptr;
+  const bool direct = s1 == 1 && s2 == 1 && C != nullptr;
   const double bv = (direct && bias != nullptr) ? static_cast<double>(bias[gn]) : 0.0;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
@@ -449,14 +455,16 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
   }
 }
 
-// Split count from (N, K) and the device alone, so a row's result never
-// depends on M.  One workgroup fits a CU (120 KB of LDS), so for a single row
-// tile the launch runs in ceil(tiles_n * s / CUs) rounds of ceil(steps / s) K
-// steps each.  Measured on MI355X: a K step takes ~1.1 us, a round adds ~5
-// steps of fixed cost (first copies in flight, epilogue), and each split adds
-// an fp64 partial of the row tile that is written and read back once (192 N
-// 16 bytes at ~4.5 TB/s, i.e. N / 1600 steps).  s minimises the sum, with
-// splits of >= 8 steps and <= 16384 of K.
+// Split plan from (N, K) and the device alone, so a row's result never
+// depends on M.  One workgroup fits a CU (120 KB of LDS).  Measured on MI355X:
+// a K step takes ~1.1 us, a round of workgroups adds ~5 steps of fixed cost
+// (first copies in flight, epilogue), and each split adds an fp64 partial of
+// the row tile that is written and read back once (192 N 16 bytes at
+// ~4.5 TB/s, i.e. N / 1600 steps per slot).  Plans: every N tile in s splits
+// (ceil(tiles_n s / CUs) rounds of ceil(steps / s) steps), or the first n1
+// tiles in s1 splits filling k whole rounds and the rest in s2 = 2..4 s1
+// splits after them, which evens out a last, partial round.  Splits have
+// >= 8 steps and <= 16384 of K; the cheapest plan wins.
 static int go_cus() {
   static int cus = 0;
   if (cus == 0) {
@@ -467,7 +475,10 @@ static int go_cus() {
   }
   return cus;
 }
-static int go_splits(int N, int K) {
+struct GoSplit {
+  int s1, s2, n1;  // N tiles [0, n1) in s1 splits, the rest in s2
+};
+static GoSplit go_split(int N, int K) {
   const int tiles_n = (N + go::BN - 1) / go::BN;
   const int steps = go_kp(K) / go::BK;
   const int cus = go_cus();
@@ -477,18 +488,34 @@ static int go_splits(int N, int K) {
   if (hi < lo) hi = lo;
   if (lo < 1) lo = 1;
   const double part_steps = N / 1600.0;
-  int best = lo;
+  GoSplit best{lo, lo, tiles_n};
   double best_cost = 1e30;
   for (int sp = lo; sp <= hi; ++sp) {
     const int rounds = (tiles_n * sp + cus - 1) / cus;
     const double cost = static_cast<double>(rounds) * ((steps + sp - 1) / sp + 5) + part_steps * sp;
-    if (cost < best_cost) best_cost = cost, best = sp;
+    if (cost < best_cost) best_cost = cost, best = GoSplit{sp, sp, tiles_n};
+  }
+  for (int a = lo; a <= hi; ++a) {
+    for (int k = 1; k <= 2; ++k) {
+      if (cus * k % a) continue;
+      const int n1 = cus * k / a;  // k whole rounds of s1 = a splits
+      if (n1 <= 0 || n1 >= tiles_n) continue;
+      for (int m = 2; m <= 4; ++m) {
+        const int b = a * m;
+        if (b > hi) break;
+        const int r = tiles_n - n1;
+        const int rounds2 = (r * b + cus - 1) / cus;
+        const double cost = k * ((steps + a - 1) / a + 5.0) + rounds2 * ((steps + b - 1) / b + 5.0) +
+                            part_steps * (static_cast<double>(n1) * a + static_cast<double>(r) * b) / tiles_n;
+        if (cost < best_cost) best_cost = cost, best = GoSplit{a, b, n1};
+      }
+    }
   }
   return best;
 }
 
 // Fixed-order reduction of the split-K partials, bias added in fp64, one rounding.
-__global__ __launch_bounds__(256) void gemm_f32_reduce_kernel(int M, int N, int splits,
+__global__ __launch_bounds__(256) void gemm_f32_reduce_kernel(int M, int N, int s1, int s2, int cb,
                                                              const double* __restrict__ part,
                                                              const float* __restrict__ bias,
                                                              float* __restrict__ C) {
@@ -496,6 +523,7 @@ __global__ __launch_bounds__(256) void gemm_f32_reduce_kernel(int M, int N, int 
   const int64_t MN = static_cast<int64_t>(M) * N;
   if (t >= MN) return;
   double v = 0.0;
+  const int splits = t % N < cb ? s1 : s2;  // partials of this column
   for (int s = 0; s < splits; ++s) v += part[s * MN + t];
   if (bias != nullptr) v += static_cast<double>(bias[t % N]);
   C[t] = static_cast<float>(v);
@@ -511,8 +539,9 @@ static size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 size_t gemm_f32_slices_bytes(int R, int K) {
   return al256(static_cast<size_t>(go::S) * R * go_kp(K)) + al256(sizeof(int32_t) * R);
 }
+static int go_slots(const GoSplit& g) { return g.s1 > g.s2 ? g.s1 : g.s2; }
 size_t gemm_f32_ws_bytes(int M, int N, int K) {
-  const int s = go_splits(N, K);
+  const int s = go_slots(go_split(N, K));
   return gemm_f32_slices_bytes(M, K) + (s > 1 ? al256(static_cast<size_t>(s) * M * N * sizeof(double)) : 0);
 }
 
@@ -526,23 +555,28 @@ hipError_t slice_rows(int R, int K, const float* X, void* slices, hipStream_t s)
   return hipGetLastError();
 }
 
-int gemm_f32_splits(int N, int K) { return go_splits(N, K); }
+int gemm_f32_splits(int N, int K) { return go_slots(go_split(N, K)); }
+F32Splits gemm_f32_split_groups(int N, int K) {
+  const GoSplit g = go_split(N, K);
+  return F32Splits{g.s1, g.s2, g.n1 * go::BN < N ? g.n1 * go::BN : N};
+}
 size_t gemm_f32_part_bytes(int M, int N, int K) {
-  return al256(static_cast<size_t>(go_splits(N, K)) * M * N * sizeof(double));
+  return al256(static_cast<size_t>(gemm_f32_splits(N, K)) * M * N * sizeof(double));
 }
 
 static hipError_t launch_gemm_f32(int M, int N, int kp, const int8_t* Ap, const int32_t* Ae, const int8_t* Bp,
-                                  const int32_t* Be, const float* bias, float* C, double* part, int splits,
+                                  const int32_t* Be, const float* bias, float* C, double* part, const GoSplit& g,
                                   hipStream_t s) {
   const int steps = kp / go::BK;
-  const int sps = (steps + splits - 1) / splits;
+  const int sps1 = (steps + g.s1 - 1) / g.s1, sps2 = (steps + g.s2 - 1) / g.s2;
   const int tiles_m = (M + go::BM - 1) / go::BM, tiles_n = (N + go::BN - 1) / go::BN;
-  const int64_t work = static_cast<int64_t>(tiles_m) * tiles_n * splits;
+  const int64_t work = static_cast<int64_t>(tiles_m) * (static_cast<int64_t>(g.n1) * g.s1 +
+                                                        static_cast<int64_t>(tiles_n - g.n1) * g.s2);
   if (work >= (int64_t(1) << 31) - 256) return hipErrorInvalidValue;
   const unsigned blocks = static_cast<unsigned>((work + 255) / 256 * 256);
   LaunchScope scope_(kCntGemmF32, s);
   hipLaunchKernelGGL(gemm_f32_kernel, dim3(blocks), dim3(go::NT), 0, s, M, N, kp, Ap, Ae, Bp, Be, bias, C, part,
-                     splits, sps, tiles_m, tiles_n);
+                     g.s1, g.s2, g.n1, sps1, sps2, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -553,7 +587,7 @@ hipError_t gemm_f32_sliced(int M, int N, int K, const void* As, const void* Bs, 
   const int32_t* Ae = reinterpret_cast<const int32_t*>(Ap + al256(static_cast<size_t>(go::S) * M * kp));
   const int8_t* Bp = static_cast<const int8_t*>(Bs);
   const int32_t* Be = reinterpret_cast<const int32_t*>(Bp + al256(static_cast<size_t>(go::S) * N * kp));
-  return launch_gemm_f32(M, N, kp, Ap, Ae, Bp, Be, nullptr, nullptr, part, go_splits(N, K), s);
+  return launch_gemm_f32(M, N, kp, Ap, Ae, Bp, Be, nullptr, nullptr, part, go_split(N, K), s);
 }
 
 hipError_t gemm_f32(int M, int N, int K, const float* A, const void* Bs, const float* bias, float* C,
@@ -568,14 +602,15 @@ hipError_t gemm_f32(int M, int N, int K, const float* A, const void* Bs, const f
   const int8_t* Bp = static_cast<const int8_t*>(Bs);
   const int32_t* Be = reinterpret_cast<const int32_t*>(Bp + al256(static_cast<size_t>(go::S) * N * kp));
   double* part = reinterpret_cast<double*>(w + gemm_f32_slices_bytes(M, K));
-  const int splits = go_splits(N, K);
-  e = launch_gemm_f32(M, N, kp, Ap, Ae, Bp, Be, bias, C, part, splits, s);
-  if (e != hipSuccess || splits == 1) return e;
+  const GoSplit g = go_split(N, K);
+  e = launch_gemm_f32(M, N, kp, Ap, Ae, Bp, Be, bias, C, part, g, s);
+  if (e != hipSuccess || (g.s1 == 1 && g.s2 == 1)) return e;  // one split writes C itself
   const int64_t MN = static_cast<int64_t>(M) * N;
+  const int cb = g.n1 * go::BN < N ? g.n1 * go::BN : N;
   {
     LaunchScope scope_(kCntGemmF32Reduce, s);
     hipLaunchKernelGGL(gemm_f32_reduce_kernel, dim3(static_cast<unsigned>((MN + 255) / 256)), dim3(256),
-                       0, s, M, N, splits, part, bias, C);
+                       0, s, M, N, g.s1, g.s2, cb, part, bias, C);
   }
   return hipGetLastError();
 }

@@ -40,9 +40,14 @@ size_t gemm_f32_ws_bytes(int M, int N, int K);
 hipError_t gemm_f32(int M, int N, int K, const float* A, const void* B_slices, const float* bias,
                     float* C, void* ws, hipStream_t s);
 // A also given as slices; the product goes to fp64 split-K partials
-// part[splits][M][N] (splits = gemm_f32_splits(N, K), no bias) that the
-// consumer sums in split order.
+// part[slot][M][N] (no bias) that the consumer sums in split order: columns
+// below col_split have s_lo partials, the others s_hi; gemm_f32_splits is the
+// layout's slot count, max(s_lo, s_hi).
+struct F32Splits {
+  int s_lo, s_hi, col_split;
+};
 int gemm_f32_splits(int N, int K);
+F32Splits gemm_f32_split_groups(int N, int K);
 size_t gemm_f32_part_bytes(int M, int N, int K);
 hipError_t gemm_f32_sliced(int M, int N, int K, const void* A_slices, const void* B_slices, double* part,
                            hipStream_t s);
@@ -76,11 +81,11 @@ hipError_t gated_residual(int N, int D, bool x_f64, void* x, const float* a, con
 // modulated from nmod (which) unless nmod is null, sliced into `slices` (rows
 // N, K = D) or stored to y, or neither when both are null.
 bool fused_f32_supported(int D, int F);
-hipError_t resid_norm_slice(int N, int D, int S, const double* part, const float* bias, const float* gmod, int gate_which,
+hipError_t resid_norm_slice(int N, int D, F32Splits sg, const double* part, const float* bias, const float* gmod, int gate_which,
                             const float* nmod, int norm_which, int norm, float eps, const int32_t* cond_idx, double* x,
                             void* slices, float* y, hipStream_t s);
-hipError_t silu_slice(int N, int F, int S, const double* part, const float* bias, void* slices, hipStream_t s);
-hipError_t rope_part(int N, int H, int hd, int rot, int S, const double* part, const float* bias, const float* cos,
+hipError_t silu_slice(int N, int F, F32Splits sg, const double* part, const float* bias, void* slices, hipStream_t s);
+hipError_t rope_part(int N, int H, int hd, int rot, F32Splits sg, const double* part, const float* bias, const float* cos,
                      const float* sin, float* q, float* k, float* v, hipStream_t s);
 hipError_t widen_f32(int64_t n, const float* src, double* dst, hipStream_t s);
 hipError_t narrow_f64(int64_t n, const double* src, float* dst, hipStream_t s);
