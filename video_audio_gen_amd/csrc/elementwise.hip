@@ -411,31 +411,45 @@ template <> struct wload4<bf16_t> {
 };
 
 // blockIdx.z: the block (weights at p + z * stride bytes, output rows at
-// mod + z * n_cond * six_d); each lane reads four consecutive weights.
+// mod + z * n_cond * six_d).  Each wavefront computes ADA_JW consecutive
+// outputs; each lane reads four consecutive weights of each of their rows.
+constexpr int ADA_JW = 4;
 template <typename TW>
 __global__ __launch_bounds__(256) void adaln_kernel(int six_d, int cond_dim, AdalnBlockPtrs p, int64_t w_stride,
                                                    int64_t b_stride, CondMap cm, const float* __restrict__ e,
                                                    float* __restrict__ mod) {
   const int lane = threadIdx.x & 63;
-  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int j0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * ADA_JW;
   const int m = blockIdx.y;
-  if (j >= six_d || p.w[m] == nullptr) return;
+  if (j0 >= six_d || p.w[m] == nullptr) return;
   const TW* w = reinterpret_cast<const TW*>(static_cast<const char*>(p.w[m]) + blockIdx.z * w_stride) +
-                static_cast<size_t>(j) * cond_dim;
+                static_cast<size_t>(j0) * cond_dim;
   const float* bias = reinterpret_cast<const float*>(reinterpret_cast<const char*>(p.bias[m]) + blockIdx.z * b_stride);
   float* out = mod + static_cast<size_t>(blockIdx.z) * cm.n_cond * six_d;
+  const int nj = six_d - j0 < ADA_JW ? six_d - j0 : ADA_JW;
   for (int c = 0; c < cm.n_cond; ++c) {
     if (cm.modality[c] != m) continue;
     const float* ec = e + static_cast<size_t>(c) * cond_dim;
-    double acc = 0.0;
+    double acc[ADA_JW] = {0.0, 0.0, 0.0, 0.0};
     for (int kk = 4 * lane; kk < cond_dim; kk += 256) {
-      const float4 wv = wload4<TW>::ld(w + kk);
       const float4 ev = *reinterpret_cast<const float4*>(ec + kk);
-      acc += static_cast<double>(wv.x) * static_cast<double>(ev.x) + static_cast<double>(wv.y) * static_cast<double>(ev.y) +
-             static_cast<double>(wv.z) * static_cast<double>(ev.z) + static_cast<double>(wv.w) * static_cast<double>(ev.w);
+#pragma unroll
+      for (int r = 0; r < ADA_JW; ++r) {
+        if (r < nj) {
+          const float4 wv = wload4<TW>::ld(w + static_cast<size_t>(r) * cond_dim + kk);
+          acc[r] += static_cast<double>(wv.x) * static_cast<double>(ev.x) +
+                    static_cast<double>(wv.y) * static_cast<double>(ev.y) +
+                    static_cast<double>(wv.z) * static_cast<double>(ev.z) +
+                    static_cast<double>(wv.w) * static_cast<double>(ev.w);
+        }
+      }
     }
-    acc = wave_sum_f64(acc);
-    if (lane == 0) out[static_cast<size_t>(c) * six_d + j] = static_cast<float>(acc + static_cast<double>(bias[j]));
+#pragma unroll
+    for (int r = 0; r < ADA_JW; ++r) {
+      const double t = wave_sum_f64(acc[r]);
+      if (lane == 0 && r < nj)
+        out[static_cast<size_t>(c) * six_d + j0 + r] = static_cast<float>(t + static_cast<double>(bias[j0 + r]));
+    }
   }
 }
 
@@ -470,7 +484,7 @@ hipError_t adaln(bool w_bf16, int n_blocks, const AdalnBlockPtrs* blocks_host, i
   }
   const int launches = uniform ? 1 : n_blocks;
   for (int b = 0; b < launches; ++b) {
-    dim3 grid((six_d + 3) / 4, n_mod, uniform ? n_blocks : 1), block(256);
+    dim3 grid((six_d + 4 * ADA_JW - 1) / (4 * ADA_JW), n_mod, uniform ? n_blocks : 1), block(256);
     LaunchScope scope_(kCntAdaln, s);
     float* out = mod + static_cast<size_t>(b) * n_cond * six_d;
     if (w_bf16)
