@@ -283,3 +283,23 @@ def test_c4_full_size_packed_equals_alone_and_deterministic(H):
         torch.cuda.synchronize()
         assert torch.equal(out, packed[offs[i]:offs[i + 1]]), f"document {i} alone differs from the packed forward"
         del ws
+
+
+def test_c5_full_size_denoise_loop_equals_steps(H):
+    """The 50-step denoise configuration at its full size (64 blocks, 18,432
+    tokens): the device loop over the first three steps equals three single
+    steps bit for bit, the latents stay finite and move."""
+    cfg = S.get_config("c5")
+    m = H.stage_model(cfg, 0, threads=16)
+    r = H.Runner(cfg, 0, model=m)
+    cond_tab, dt_tab = _schedule_tables(H, cfg)
+    n = 3
+    lat = r.x_in.clone()
+    for i in range(n):
+        H.dit.dit_denoise_step(m, r.batch, lat, cond_tab[i], dt_tab[i], r.ws)
+    lat_loop = r.x_in.clone()
+    H.dit.dit_denoise_loop(m, r.batch, lat_loop, cond_tab, dt_tab, n, r.ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(lat).all()
+    assert torch.equal(lat_loop, lat)
+    assert (lat - r.x_in).abs().max().item() > 1e-3
