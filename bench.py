@@ -196,8 +196,8 @@ def main(argv=None):
                     help="launch every kernel from the host instead of replaying one captured HIP graph")
     a = ap.parse_args(argv)
     if a.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported by this build "
-              "(the path runs on a single device)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (the path runs on a single device; "
+              "multi-GPU sharding is designed, not built)", file=sys.stderr)
         return 2
 
     import numpy as np
