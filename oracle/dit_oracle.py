@@ -25,7 +25,10 @@ steps and their sources:
     bf16 DiT to the device", section "What this enables";
   * rectified-flow time-shift sigma schedule, euler eta=0 with rf_v_to_x0 --
     page "port the MiniMax-H3 omni-modal video+audio DiT", update "quantized
-    arms land" item 2 and milestone "the whole t2va path composes end to end".
+    arms land" item 2 and milestone "the whole t2va path composes end to end";
+  * the music model's loop of DiT forwards over two classifier-free-guidance
+    branches per step -- page "the 2.4B fp32 DiT onto the device, staged
+    once", opening paragraph (steps x 2 CFG branches x windows).
 
 Where the pages leave a step open, the plainest reading is taken; each reading
 is named in the docstring of the function that takes it.
@@ -56,7 +59,8 @@ __all__ = [
     "timestep_embedding", "cond_embeddings", "norm", "modulate", "linear", "apply_rope",
     "attention_varlen", "attention_dense_masked", "silu", "adaln_table", "block_forward",
     "patchify", "unpatchify", "forward", "sigma_schedule", "sigma_dt", "euler_step",
-    "denoise_step_conditions", "denoise_loop", "split_mlp",
+    "denoise_step_conditions", "denoise_loop", "split_mlp", "cfg_pairs", "cfg_combine",
+    "cfg_denoise_loop",
 ]
 
 
@@ -581,3 +585,63 @@ def denoise_step_conditions(cfg, step: int):
         sig = sigma_schedule(cfg.shifts[r.modality], cfg.denoise_steps)
         t_rows.append(float(np.float32(sig[step])))
     return t_rows, dts
+
+
+# ----------------------------------------------------------------------------- CFG denoise loop
+
+def cfg_pairs(cfg) -> int:
+    """Number P of guidance pairs in a packed batch of 2P segments.
+
+    Reading taken (the pages give the branch count, not the packing): the
+    first P segments are the conditional branches, segment j + P is the
+    unconditional branch of segment j, with the same modality and grid, and
+    both branches of a pair see the same latent.
+    """
+    n = len(cfg.segments)
+    if n % 2:
+        raise ValueError("a guided batch holds an even number of segments")
+    P = n // 2
+    for j in range(P):
+        a, b = cfg.segments[j], cfg.segments[j + P]
+        if a.modality != b.modality or tuple(a.grid) != tuple(b.grid):
+            raise ValueError(f"segments {j} and {j + P} do not pair")
+    return P
+
+
+def cfg_combine(v_cond: np.ndarray, v_uncond: np.ndarray, w: float) -> np.ndarray:
+    """Classifier-free guidance v = v_u + w (v_c - v_u), float32 operations in
+    that order, each rounded (no contraction).
+
+    Reading taken (the pages name the two branches but print no formula): the
+    standard guidance form in which w = 0 is the unconditional velocity and
+    w = 1 the conditional one.
+    """
+    vc = np.asarray(v_cond, np.float32)
+    vu = np.asarray(v_uncond, np.float32)
+    d = (vc - vu).astype(np.float32)
+    return (vu + (np.float32(w) * d).astype(np.float32)).astype(np.float32)
+
+
+def cfg_denoise_loop(cfg, weights, islands, latents: Dict[str, np.ndarray], cond_steps: np.ndarray,
+                     dts: np.ndarray, w: float, n_steps: int, mode: Optional[str] = None,
+                     threads: int = 1, accum: str = "fp64") -> Dict[str, np.ndarray]:
+    """n_steps guided Euler steps of a vector-conditioned model.
+
+    ``latents`` holds the P shared latents ('latent.{j}', j < P).  Step i runs
+    one forward over all 2P segments -- segment j and j + P both read latent
+    j, each with its own conditioning row taken from ``cond_steps[i]``
+    ([n_sources, cond_dim]; the per-step rows carry whatever the sampler folds
+    into them, the timestep included) -- combines each pair with
+    ``cfg_combine`` and moves latent j by ``dts[i][modality]`` times the
+    guided velocity (``euler_step``).
+    """
+    P = cfg_pairs(cfg)
+    lat = {f"latent.{j}": np.asarray(latents[f"latent.{j}"], np.float32) for j in range(P)}
+    for i in range(n_steps):
+        inp = {f"latent.{j}": lat[f"latent.{j % P}"] for j in range(2 * P)}
+        inp["cond"] = np.asarray(cond_steps[i])
+        v = forward(cfg, weights, islands, inp, mode, threads=threads, accum=accum)
+        for j in range(P):
+            g = cfg_combine(v[f"latent.{j}"].astype(np.float32), v[f"latent.{j + P}"].astype(np.float32), w)
+            lat[f"latent.{j}"] = euler_step(lat[f"latent.{j}"], g, np.float32(dts[i][cfg.segments[j].modality]))
+    return lat

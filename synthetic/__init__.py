@@ -17,6 +17,7 @@ from .gen import (  # noqa: F401
     island_weights,
     all_weights,
     inputs,
+    cond_steps,
     round_to_bf16,
     bf16_bits,
 )

@@ -87,7 +87,7 @@ class DitConfig:
     io: bool                     # True: latents in, velocities out; False: tokens in, tokens out
     denoise_steps: int = 0
     shifts: Tuple[float, ...] = field(default_factory=tuple)
-    cfg_replicate_latent: bool = False  # CFG branches see one latent, replicated per branch
+    cfg_replicate_latent: bool = False  # segment j + P reads the latent of segment j (P = half the segments)
 
     @property
     def n_tokens(self) -> int:
@@ -125,7 +125,8 @@ C2 = DitConfig(
     stream="f32", cond_kind="vector", cond_dim=256,
     modalities=(Modality("music", "channel_major", 128, (1, 1, 1), (64,)),),
     segments=(Segment(0, (86,), 0), Segment(0, (86,), 1)),
-    cond_rows=(CondRow(0, 0), CondRow(0, 1)), n_requests=2, io=True, cfg_replicate_latent=True)
+    cond_rows=(CondRow(0, 0), CondRow(0, 1)), n_requests=2, io=True, cfg_replicate_latent=True,
+    denoise_steps=30, shifts=(1.0,))
 
 C3 = DitConfig(
     name="c3_block_bf16", key_id=3, model_id=3, n_blocks=1, **_WIDE,

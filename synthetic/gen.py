@@ -181,7 +181,7 @@ def inputs(cfg: DitConfig, seed: int = 0) -> Dict[str, np.ndarray]:
     k = cfg.key_id
     if cfg.io:
         for i in range(len(cfg.segments)):
-            src = 0 if cfg.cfg_replicate_latent else i
+            src = i % (len(cfg.segments) // 2) if cfg.cfg_replicate_latent else i
             out[f"latent.{i}"] = _keyed_normal(seed, k, f"latent.{src}", segment_latent_shape(cfg, i), 1.0, False)
     else:
         out["x"] = _keyed_normal(seed, k, "x", (cfg.n_tokens, cfg.hidden), 1.0, cfg.stream == "bf16")
@@ -191,4 +191,16 @@ def inputs(cfg: DitConfig, seed: int = 0) -> Dict[str, np.ndarray]:
     else:
         n_src = 1 + max(r.source for r in cfg.cond_rows)
         out["cond"] = _normal(tensor_rng(seed, k, "cond"), (n_src, cfg.cond_dim), 1.0)
+    return out
+
+
+def cond_steps(cfg: DitConfig, n_steps: int, seed: int = 0) -> np.ndarray:
+    """Per-step conditioning vectors of a vector-conditioned denoise loop,
+    [n_steps, n_sources, cond_dim] float32, N(0, 1); step 0 equals
+    ``inputs(cfg)['cond']``."""
+    n_src = 1 + max(r.source for r in cfg.cond_rows)
+    out = np.empty((n_steps, n_src, cfg.cond_dim), np.float32)
+    for i in range(n_steps):
+        name = "cond" if i == 0 else f"cond.step{i}"
+        out[i] = _normal(tensor_rng(seed, cfg.key_id, name), (n_src, cfg.cond_dim), 1.0)
     return out

@@ -427,3 +427,100 @@ def test_denoise_loop_constant_velocity_telescopes():
     # and a different shift per modality gives different intermediate sigmas
     t6, _ = O.denoise_step_conditions(cfg, 3)
     assert t6[0] != t6[1]
+
+
+# ----------------------------------------------------------------------------- guided (CFG) loop
+
+def test_cfg_combine_hand_values():
+    vc = np.array([3.0, -1.0, 0.5, 2.0], np.float32)
+    vu = np.array([1.0, 1.0, 0.5, -2.0], np.float32)
+    # v_u + w (v_c - v_u) at w = 2: 1 + 4, 1 - 4, 0.5 + 0, -2 + 8
+    assert np.array_equal(O.cfg_combine(vc, vu, 2.0), np.array([5.0, -3.0, 0.5, 6.0], np.float32))
+    r = np.random.default_rng(40)
+    a, b = r.standard_normal(500).astype(np.float32), r.standard_normal(500).astype(np.float32)
+    assert np.array_equal(O.cfg_combine(a, b, 0.0), b)  # w = 0: the unconditional branch exactly
+    assert O.cfg_combine(a, b, 3.0).dtype == np.float32
+    # float32 steps: each of the three operations rounds once
+    d = (a - b).astype(np.float32)
+    exact = b.astype(np.float64) + 3.0 * (a.astype(np.float64) - b.astype(np.float64))
+    got = O.cfg_combine(a, b, 3.0).astype(np.float64)
+    assert np.abs(got - exact).max() <= 4 * np.finfo(np.float32).eps * (np.abs(exact) + 3 * np.abs(d)).max()
+
+
+def test_cfg_pairs_layout():
+    c2 = S.get_config("c2")
+    assert O.cfg_pairs(c2) == 1
+    four = scaled(c2, segments=(Segment(0, (8,), 0), Segment(0, (12,), 0), Segment(0, (8,), 1),
+                                Segment(0, (12,), 1)))
+    assert O.cfg_pairs(four) == 2
+    with pytest.raises(ValueError):
+        O.cfg_pairs(scaled(c2, segments=four.segments[:3]))
+    with pytest.raises(ValueError):  # segment j pairs with j + P, not j + 1
+        O.cfg_pairs(scaled(c2, segments=(Segment(0, (8,), 0), Segment(0, (8,), 1), Segment(0, (12,), 0),
+                                         Segment(0, (12,), 1))))
+
+
+_CFG_TINY = scaled(S.get_config("c2"), n_blocks=1, hidden=256, n_heads=2, ffn=512, denoise_steps=3,
+                   segments=(Segment(0, (8,), 0), Segment(0, (12,), 0), Segment(0, (8,), 1),
+                             Segment(0, (12,), 1)))
+
+
+def _cfg_setup(cfg):
+    isl = S.island_weights(cfg)
+    bw = S.block_weights(cfg, 0)
+    inp = S.inputs(cfg)
+    P = len(cfg.segments) // 2
+    lat = {f"latent.{j}": inp[f"latent.{j}"] for j in range(P)}
+    conds = S.cond_steps(cfg, cfg.denoise_steps)
+    dt = O.sigma_dt(O.sigma_schedule(cfg.shifts[0], cfg.denoise_steps))
+    dts = dt[:, None]
+    return isl, (lambda b: bw), lat, conds, dts
+
+
+def _alone_loop(cfg, j, source, W, isl, lat, conds, dts, n):
+    """Segment j on its own with conditioning source ``source``: a plain Euler
+    loop on the unguided velocity."""
+    seg = cfg.segments[j]
+    one = scaled(cfg, segments=(Segment(seg.modality, seg.grid, 0),), cond_rows=(CondRow(seg.modality, 0),),
+                 cfg_replicate_latent=False)
+    x = lat[f"latent.{j}"]
+    for i in range(n):
+        v = O.forward(one, W, isl, {"latent.0": x, "cond": conds[i][source:source + 1]})["latent.0"]
+        x = O.euler_step(x, v.astype(np.float32), dts[i][seg.modality])
+    return x
+
+
+def test_cfg_loop_reduces_to_each_branch():
+    cfg = _CFG_TINY
+    isl, W, lat, conds, dts = _cfg_setup(cfg)
+    n = cfg.denoise_steps
+    g0 = O.cfg_denoise_loop(cfg, W, isl, lat, conds, dts, 0.0, n)
+    g1 = O.cfg_denoise_loop(cfg, W, isl, lat, conds, dts, 1.0, n)
+    for j in range(2):
+        unc = _alone_loop(cfg, j, 1, W, isl, lat, conds, dts, n)
+        con = _alone_loop(cfg, j, 0, W, isl, lat, conds, dts, n)
+        assert np.abs(con - unc).max() > 1e-3  # the two branches do differ
+        # w = 0: the unconditional branch, up to the packed-vs-alone fp64 rounding order
+        assert np.abs(g0[f"latent.{j}"] - unc).max() < 1e-6
+        # w = 1: the conditional branch, up to three float32 roundings per step
+        assert np.abs(g1[f"latent.{j}"] - con).max() < 1e-5
+
+
+def test_cfg_loop_identical_branches_ignore_guidance():
+    cfg = _CFG_TINY
+    isl, W, lat, conds, dts = _cfg_setup(cfg)
+    conds = conds.copy()
+    conds[:, 1] = conds[:, 0]
+    g = O.cfg_denoise_loop(cfg, W, isl, lat, conds, dts, 7.5, 2)
+    for j in range(2):
+        plain = _alone_loop(cfg, j, 0, W, isl, lat, conds, dts, 2)
+        assert np.abs(g[f"latent.{j}"] - plain).max() < 1e-5
+
+
+def test_cfg_step_is_affine_in_guidance():
+    cfg = _CFG_TINY
+    isl, W, lat, conds, dts = _cfg_setup(cfg)
+    x = [O.cfg_denoise_loop(cfg, W, isl, lat, conds, dts, w, 1)["latent.1"].astype(np.float64) for w in (0.0, 1.0, 2.0)]
+    step = x[1] - x[0]
+    assert np.abs(step).max() > 1e-4
+    assert np.abs((x[2] - x[1]) - step).max() < 1e-5 * np.abs(x[0]).max()

@@ -62,6 +62,19 @@ def cond_rows(cfg, inp: Dict[str, np.ndarray], t_rows=None) -> np.ndarray:
     return np.stack([inp["cond"][r.source] for r in cfg.cond_rows]).astype(np.float32)
 
 
+def cond_step_rows(cfg, cond_steps: np.ndarray) -> np.ndarray:
+    """[n_steps, n_cond, cond_dim] rows of a vector-conditioned loop from the
+    per-step conditioning vectors [n_steps, n_sources, cond_dim]."""
+    return np.stack([cond_rows(cfg, {"cond": c}) for c in cond_steps]).astype(np.float32)
+
+
+def dt_table(cfg, n_steps: Optional[int] = None) -> np.ndarray:
+    """[n_steps, n_mod] float32 step sizes from the library's sigma schedule."""
+    n = cfg.denoise_steps if n_steps is None else n_steps
+    sig = [dit.dit_sigma_schedule(cfg.shifts[m], cfg.denoise_steps)[1] for m in range(cfg.n_mod)]
+    return np.asarray([[sig[m][i] for m in range(cfg.n_mod)] for i in range(n)], np.float32)
+
+
 def pack_input(cfg, inp: Dict[str, np.ndarray]) -> np.ndarray:
     """The forward's input buffer: tokens [N, D] or all segment latents end to end."""
     if not cfg.io:
@@ -96,7 +109,7 @@ class Runner:
         self.out = torch.empty_like(self.x_in) if not cfg.io else torch.empty(
             self.batch.latent_floats, dtype=torch.float32, device="cuda")
         self.cond = None
-        if cfg.denoise_steps == 0:
+        if cfg.denoise_steps == 0 or cfg.cond_kind == "vector":
             self.cond = torch.from_numpy(cond_rows(cfg, self.inp)).cuda()
 
     def forward(self, x_in=None, cond=None, out=None):
