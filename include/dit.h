@@ -251,6 +251,23 @@ int dit_denoise_loop(dit_model* m, const dit_batch* b, float* latents_dev,
                      const float* cond_table_dev, const float* dt_table_dev, int n_steps,
                      void* ws_dev, size_t ws_bytes, dit_stream_t stream);
 
+/* Guided (classifier-free guidance) denoise loop of a vector-conditioned
+ * model, as the music generator runs its DiT (page "the 2.4B fp32 DiT onto
+ * the device, staged once", What moved: the conditional and unconditional
+ * branches of every step).  The batch holds 2P segments: segment j + P is the
+ * unconditional branch of segment j, with the same modality and grid.
+ * latents_dev holds the P shared latents, segment after segment (the first
+ * half of the batch's latent layout), float32, updated in place.  Step i runs
+ * one forward over all 2P segments, both branches of pair j reading latent j,
+ * with modulation rows cond_table_dev + i*n_cond*cond_dim, then moves latent j
+ * by dt * (v_u + w (v_c - v_u)), dt = dt_table_dev[i*n_mod + modality], each
+ * operation rounded to float32 (w = 0: unconditional; w = 1: conditional).
+ * Asynchronous on `stream`; no host round trip.  DIT_E_INVALID when the
+ * segments do not pair, w is not finite or the model has no io. */
+int dit_cfg_denoise_loop(dit_model* m, const dit_batch* b, float* latents_dev,
+                         const float* cond_table_dev, const float* dt_table_dev, float w,
+                         int n_steps, void* ws_dev, size_t ws_bytes, dit_stream_t stream);
+
 /* ------------------------------------------------------------------ op-level calls
  * The kernels the block is made of, exposed for per-op parity checks and
  * timing.  dtype arguments are DIT_F32 or DIT_BF16 (bf16 = uint16 bits). */

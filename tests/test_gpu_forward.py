@@ -303,3 +303,140 @@ def test_c5_full_size_denoise_loop_equals_steps(H):
     assert torch.isfinite(lat).all()
     assert torch.equal(lat_loop, lat)
     assert (lat - r.x_in).abs().max().item() > 1e-3
+
+
+# ----------------------------------------------------------------------------- guided (CFG) loop
+
+CFG_SMALL = scaled(S.get_config("c2"), n_blocks=2, hidden=256, n_heads=2, ffn=512, denoise_steps=30,
+                   segments=(Segment(0, (86,), 0), Segment(0, (40,), 0), Segment(0, (86,), 1),
+                             Segment(0, (40,), 1)))
+
+
+def _cfg_tables(H, cfg, n):
+    conds = S.cond_steps(cfg, n)
+    cond_tab = torch.from_numpy(H.cond_step_rows(cfg, conds)).cuda()
+    dts = H.dt_table(cfg, n)
+    return conds, cond_tab, dts, torch.from_numpy(dts).cuda()
+
+
+def _cfg_oracle_steps(cfg, w_model, lat, conds, dts, w, n):
+    """The oracle's guided loop, step by step, keeping each step's two branch
+    velocities for the error bound; checked equal to oracle.cfg_denoise_loop."""
+    P = len(cfg.segments) // 2
+    isl = {k: v for k, v in w_model.items() if not k.startswith("blocks.")}
+    x = {k: np.asarray(v, np.float32) for k, v in lat.items()}
+    vels = []
+    for i in range(n):
+        inp = {f"latent.{j}": x[f"latent.{j % P}"] for j in range(2 * P)}
+        inp["cond"] = conds[i]
+        v = O.forward(cfg, lambda b: w_model, isl, inp, threads=8)
+        vels.append(v)
+        for j in range(P):
+            g = O.cfg_combine(v[f"latent.{j}"].astype(np.float32), v[f"latent.{j + P}"].astype(np.float32), w)
+            x[f"latent.{j}"] = O.euler_step(x[f"latent.{j}"], g, np.float32(dts[i][0]))
+    ref = O.cfg_denoise_loop(cfg, lambda b: w_model, isl, lat, conds, dts, w, n, threads=8)
+    for k in ref:
+        assert np.array_equal(ref[k], x[k])
+    return x, vels
+
+
+def _cfg_bound(cfg, vels, dts, w, x_ref):
+    """Per element: each forward is inside |d| <= 1e-6 + 1e-5 |v|; the guided
+    velocity (1 - w) v_u + w v_c carries |1 - w| and |w| of those; each step
+    moves the latent by |dt| of that.  Doubled for the latent fed back into the
+    later steps, plus one float32 rounding of the latent per step."""
+    P = len(cfg.segments) // 2
+    tol = {f"latent.{j}": np.zeros_like(x_ref[f"latent.{j}"], np.float64) for j in range(P)}
+    for i, v in enumerate(vels):
+        for j in range(P):
+            vc = np.abs(v[f"latent.{j}"].astype(np.float64))
+            vu = np.abs(v[f"latent.{j + P}"].astype(np.float64))
+            tol[f"latent.{j}"] += abs(float(dts[i][0])) * (abs(1 - w) * (1e-6 + 1e-5 * vu) + abs(w) * (1e-6 + 1e-5 * vc))
+    return {k: 2 * t + len(vels) * 2.0 ** -23 * np.abs(x_ref[k]) for k, t in tol.items()}
+
+
+def test_cfg_loop_is_forward_then_guided_euler_bits(H):
+    """One guided step equals dit_forward on the latents copied into both
+    branches followed by the guidance combine and the Euler update done on
+    the host in float32 (bit for bit); n steps of the loop equal n one-step
+    calls; w = 1 equals the plain Euler step on the conditional velocity."""
+    cfg = CFG_SMALL
+    w_model = S.all_weights(cfg, 0, threads=8)
+    m = _stage(H, cfg, w_model)
+    r = H.Runner(cfg, 0, model=m)
+    n = 3
+    conds, cond_tab, dts, dt_tab = _cfg_tables(H, cfg, n)
+    P = 2
+    half = sum(int(np.prod(r.inp[f"latent.{j}"].shape)) for j in range(P))
+    assert torch.equal(r.x_in[:half], r.x_in[half:])  # the batch's two halves hold one latent
+    w = 3.5
+    lat = r.x_in[:half].clone()
+    H.dit.dit_cfg_denoise_loop(m, r.batch, lat, cond_tab[0], dt_tab[0], w, 1, r.ws)
+    # the same step composed from the forward and host float32 arithmetic
+    v = r.forward(x_in=r.x_in, cond=cond_tab[0]).cpu().numpy()
+    vc, vu = v[:half], v[half:]
+    d = (vc - vu).astype(np.float32)
+    g = (vu + (np.float32(w) * d).astype(np.float32)).astype(np.float32)
+    x0 = r.x_in[:half].cpu().numpy()
+    want = (x0 + (np.float32(dts[0][0]) * g).astype(np.float32)).astype(np.float32)
+    got = lat.cpu().numpy()
+    assert np.array_equal(got, want)
+    assert np.abs(got - x0).max() > 1e-3
+    # n steps in one call == n one-step calls
+    lat_loop = r.x_in[:half].clone()
+    H.dit.dit_cfg_denoise_loop(m, r.batch, lat_loop, cond_tab, dt_tab, w, n, r.ws)
+    lat_steps = r.x_in[:half].clone()
+    for i in range(n):
+        H.dit.dit_cfg_denoise_loop(m, r.batch, lat_steps, cond_tab[i], dt_tab[i], w, 1, r.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(lat_loop, lat_steps)
+    # w = 1: the guided velocity is vu + fl(vc - vu), the conditional velocity
+    # up to that one rounding
+    lat1 = r.x_in[:half].clone()
+    H.dit.dit_cfg_denoise_loop(m, r.batch, lat1, cond_tab[0], dt_tab[0], 1.0, 1, r.ws)
+    g1 = (vu + (vc - vu).astype(np.float32)).astype(np.float32)
+    want1 = (x0 + (np.float32(dts[0][0]) * g1).astype(np.float32)).astype(np.float32)
+    assert np.array_equal(lat1.cpu().numpy(), want1)
+
+
+def test_cfg_loop_rejects_unpaired_batch(H):
+    cfg = scaled(CFG_SMALL, segments=(Segment(0, (86,), 0), Segment(0, (40,), 0), Segment(0, (40,), 1),
+                                      Segment(0, (86,), 1)))
+    w_model = S.all_weights(cfg, 0, threads=8)
+    r = H.Runner(cfg, 0, model=_stage(H, cfg, w_model))
+    _, cond_tab, _, dt_tab = _cfg_tables(H, cfg, 1)
+    lat = r.x_in[:(86 + 40) * 128].clone()
+    with pytest.raises(H.dit.DitError, match="do not pair"):
+        H.dit.dit_cfg_denoise_loop(r.model, r.batch, lat, cond_tab, dt_tab, 2.0, 1, r.ws)
+    with pytest.raises(H.dit.DitError, match="not finite"):
+        H.dit.dit_cfg_denoise_loop(r.model, r.batch, lat, cond_tab, dt_tab, float("nan"), 1, r.ws)
+
+
+@pytest.mark.parametrize("name", ["small_4seg", "c2_2blocks"])
+def test_cfg_loop_oracle_parity(H, name):
+    """Guided loop against the oracle's: the distance each latent travels
+    inside the fp32 bound of every forward, carried through the guidance."""
+    if name == "small_4seg":
+        cfg, n, w = CFG_SMALL, 3, 3.5
+    else:
+        cfg, n, w = scaled(S.get_config("c2"), n_blocks=2), 2, 5.0
+    w_model = S.all_weights(cfg, 0, threads=8)
+    r = H.Runner(cfg, 0, model=_stage(H, cfg, w_model))
+    conds, cond_tab, dts, dt_tab = _cfg_tables(H, cfg, n)
+    P = len(cfg.segments) // 2
+    lat_in = {f"latent.{j}": r.inp[f"latent.{j}"] for j in range(P)}
+    half = sum(int(np.prod(v.shape)) for v in lat_in.values())
+    lat = r.x_in[:half].clone()
+    H.dit.dit_cfg_denoise_loop(r.model, r.batch, lat, cond_tab, dt_tab, w, n, r.ws)
+    torch.cuda.synchronize()
+    got = H.unpack_output(cfg, np.concatenate([lat.cpu().numpy(), lat.cpu().numpy()]))
+    x_ref, vels = _cfg_oracle_steps(cfg, w_model, lat_in, conds, dts, w, n)
+    tol = _cfg_bound(cfg, vels, dts, w, x_ref)
+    for k in x_ref:
+        x0 = lat_in[k].astype(np.float64)
+        dg = got[k].astype(np.float64) - x0
+        dr = x_ref[k].astype(np.float64) - x0
+        assert np.abs(dr).max() > 1e-3
+        ratio = np.abs(dg - dr) / tol[k]
+        print(f"cfg {name} {k}: max|d| {np.abs(dg - dr).max():.3e} worst err/bound {ratio.max():.3f}")
+        assert (ratio <= 1).all(), f"{k}: {(ratio > 1).sum()} outside the bound, worst {ratio.max():.3f}"

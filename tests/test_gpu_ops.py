@@ -129,6 +129,38 @@ def test_modnorm(dit, norm, dtype, N, D):
     assert_f32_close(from_dev(plain), O.norm(x, kind, 1e-6), what="plain norm")
 
 
+@pytest.mark.parametrize("D,N", [(6144, 4103), (2560, 8195)])
+@pytest.mark.parametrize("runs", ["random", "contiguous"])
+def test_modnorm_many_rows(dit, D, N, runs):
+    """Enough rows for the several-rows-per-workgroup launch, with a ragged
+    last workgroup: parity with the oracle, and every row bit-identical to the
+    same row normalised in a short call (one row per workgroup)."""
+    rng = np.random.default_rng(D + N)
+    x = (rng.standard_normal((N, D)) * 2 + 0.5).astype(np.float32)
+    n_cond = 3
+    mod = (rng.standard_normal((n_cond, 6, D)) * 0.3).astype(np.float32)
+    if runs == "random":
+        ci = rng.integers(0, n_cond, N).astype(np.int32)
+    else:  # runs of odd lengths, the way packed segments lie
+        bounds = np.sort(rng.choice(np.arange(1, N), 9, replace=False))
+        ci = np.zeros(N, np.int32)
+        for i, b in enumerate(bounds):
+            ci[b:] = (i + 1) % n_cond
+    xd, md, cd = torch.from_numpy(x).cuda(), torch.from_numpy(mod).cuda(), torch.from_numpy(ci).cuda()
+    for norm in (0, 1):
+        kind = "rms" if norm == 0 else "layer"
+        ref = O.modulate(O.norm(x, kind, 1e-6), mod[ci, 3].astype(np.float64), mod[ci, 4].astype(np.float64))
+        h = torch.empty(N, D, dtype=torch.bfloat16, device="cuda")
+        dit.dit_modnorm(norm, 1e-6, xd, md, 1, cd, h)
+        got = from_dev(h)
+        assert_bf16_rounded(got, ref, "modnorm bf16 many rows")
+        lo = N - 300
+        hs = torch.empty(300, D, dtype=torch.bfloat16, device="cuda")
+        dit.dit_modnorm(norm, 1e-6, xd[lo:].contiguous(), md, 1, cd[lo:].contiguous(), hs)
+        torch.cuda.synchronize()
+        assert torch.equal(hs, h[lo:])
+
+
 # ----------------------------------------------------------------------------- RoPE + split
 
 @pytest.mark.parametrize("dtype,N,H,hd,rot", [("f32", 160, 4, 32, 32), ("f32", 172, 3, 128, 64),

@@ -13,6 +13,7 @@
 #include <mutex>
 #include <string>
 #include <unordered_map>
+#include <cmath>
 #include <vector>
 
 #include "dit.h"
@@ -869,6 +870,56 @@ extern "C" int dit_denoise_loop(dit_model* m, const dit_batch* b, float* latents
   for (int i = 0; i < n_steps; ++i)
     DIT_TRY(run_step(m, b, latents_dev, cond_table_dev + i * cstride, dt_table_dev + static_cast<size_t>(i) * m->cfg.n_mod,
                      static_cast<char*>(ws_dev), p, s));
+  return DIT_OK;
+}
+
+// Guided loop: the batch holds 2P segments, segment j + P the unconditional
+// branch of segment j on the same latent.  Each step copies the P latents
+// into both halves of the velocity buffer, runs the forward in place there
+// (the forward reads its whole input before it writes its output), then moves
+// latent j by dt times the guided velocity of pair j.
+static int check_cfg_pairs(const dit_batch* b, int* P) {
+  if (b->n_segs % 2) return set_error(DIT_E_INVALID, "guided loop: %d segments, an even count is needed", b->n_segs);
+  const int h = b->n_segs / 2;
+  for (int j = 0; j < h; ++j) {
+    const dit_segment& a = b->segs[j];
+    const dit_segment& u = b->segs[j + h];
+    if (a.modality != u.modality || a.grid[0] != u.grid[0] || a.grid[1] != u.grid[1] || a.grid[2] != u.grid[2])
+      return set_error(DIT_E_INVALID, "guided loop: segments %d and %d do not pair (modality or grid differ)", j, j + h);
+    if (b->lat_off[j + h] - b->lat_off[h] != b->lat_off[j])
+      return set_error(DIT_E_INVALID, "guided loop: latent layout of segment %d does not mirror segment %d", j + h, j);
+  }
+  *P = h;
+  return DIT_OK;
+}
+
+extern "C" int dit_cfg_denoise_loop(dit_model* m, const dit_batch* b, float* latents_dev, const float* cond_table_dev,
+                                    const float* dt_table_dev, float w, int n_steps, void* ws_dev, size_t ws_bytes,
+                                    dit_stream_t stream) {
+  WsPlan p;
+  DIT_TRY(check_run(m, b, ws_dev, ws_bytes, &p));
+  if (!m->cfg.io) return set_error(DIT_E_INVALID, "dit_cfg_denoise_loop: the model has no latent io");
+  if (latents_dev == nullptr || cond_table_dev == nullptr || dt_table_dev == nullptr || n_steps < 0)
+    return set_error(DIT_E_INVALID, "dit_cfg_denoise_loop: bad argument");
+  if (!std::isfinite(w)) return set_error(DIT_E_INVALID, "dit_cfg_denoise_loop: guidance weight is not finite");
+  int P = 0;
+  DIT_TRY(check_cfg_pairs(b, &P));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(ws_dev);
+  float* vel = reinterpret_cast<float*>(ws + p.vel);
+  const int64_t half = b->lat_off[P];  // floats of the P shared latents
+  const size_t cstride = static_cast<size_t>(b->n_cond) * m->cfg.cond_dim;
+  for (int i = 0; i < n_steps; ++i) {
+    DIT_HIP(hipMemcpyAsync(vel, latents_dev, sizeof(float) * half, hipMemcpyDeviceToDevice, s));
+    DIT_HIP(hipMemcpyAsync(vel + half, latents_dev, sizeof(float) * half, hipMemcpyDeviceToDevice, s));
+    DIT_TRY(run_forward(m, b, vel, cond_table_dev + i * cstride, vel, ws, p, s));
+    const float* dt = dt_table_dev + static_cast<size_t>(i) * m->cfg.n_mod;
+    for (int j = 0; j < P; ++j) {
+      const int64_t n = (j + 1 < P ? b->lat_off[j + 1] : half) - b->lat_off[j];
+      DIT_HIP(cfg_euler(n, latents_dev + b->lat_off[j], vel + b->lat_off[j], vel + half + b->lat_off[j], w,
+                        dt + b->segs[j].modality, s));
+    }
+  }
   return DIT_OK;
 }
 

@@ -69,7 +69,12 @@ template <> struct load4<double> {
   }
 };
 
-template <typename TX, typename TO, int TPR, int NCH>
+// ROWS consecutive rows per workgroup, one after the other: the next row's x
+// is in flight while the current row reduces, and the shift/scale rows stay in
+// registers while consecutive rows share their modulation row (a packed
+// segment is contiguous), so they come from L2 once per workgroup instead of
+// once per row.  Every row's arithmetic is the same as with ROWS = 1.
+template <typename TX, typename TO, int TPR, int NCH, int ROWS>
 __global__ __launch_bounds__(256) void modnorm_kernel(int N, int D, int norm, float eps,
                                                      const TX* __restrict__ x,
                                                      const float* __restrict__ mod, int shift_k,
@@ -77,65 +82,92 @@ __global__ __launch_bounds__(256) void modnorm_kernel(int N, int D, int norm, fl
                                                      TO* __restrict__ h) {
   typedef typename norm_acc<TO>::T A;
   constexpr int WPR = TPR / 64, RPB = 256 / TPR;
-  __shared__ A red[RPB * WPR];
+  __shared__ A red[2][RPB * WPR];
   const int lane = threadIdx.x & 63;
   const int wrow = threadIdx.x / TPR;             // row within the block
   const int wsub = (threadIdx.x % TPR) >> 6;      // wavefront within the row
   const int t = threadIdx.x % TPR;
-  const int row_raw = blockIdx.x * RPB + wrow;
-  const bool live = row_raw < N;
-  const int row = live ? row_raw : N - 1;         // dead rows keep every barrier reachable
   const int D4 = D >> 2;
-  const TX* xr = x + static_cast<size_t>(row) * D;
-  A v[NCH][4];
-  A s = 0;
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int c = t + TPR * i;
-    if (c < D4) {
-      load4<TX>::ld(xr + 4 * c, v[i]);
-      s += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
-    } else {
-      v[i][0] = v[i][1] = v[i][2] = v[i][3] = A(0);
-    }
-  }
   const A inv_d = A(1) / A(D);
-  A mean = 0;
-  if (norm == 1) mean = row_sum<A, WPR>(s, red, wrow, wsub, lane) * inv_d;
-  A ss = 0;
+  A v[2][NCH][4];
+  float4 shv[NCH], scv[NCH];
+  int cur_cond = -1;
+  auto row_of = [&](int it) {
+    const int r = (blockIdx.x * ROWS + it) * RPB + wrow;
+    return r < N ? r : N - 1;                      // dead rows keep every barrier reachable
+  };
+  auto load_row = [&](int r, A (*dst)[4]) {
+    const TX* xr = x + static_cast<size_t>(r) * D;
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int c = t + TPR * i;
-    if (c < D4) {
-      const A a = v[i][0] - mean, b = v[i][1] - mean, cc = v[i][2] - mean, d = v[i][3] - mean;
-      ss += (a * a + b * b) + (cc * cc + d * d);
-    }
-  }
-  ss = row_sum<A, WPR>(ss, red, wrow, wsub, lane);
-  if (!live) return;
-  const A rstd = A(1) / sqrt(ss * inv_d + A(eps));
-  const float4* sh = nullptr;
-  const float4* sc = nullptr;
-  if (mod != nullptr) {
-    const int cr = cond_idx[row];
-    sh = reinterpret_cast<const float4*>(mod + (static_cast<size_t>(cr) * 6 + shift_k) * D);
-    sc = reinterpret_cast<const float4*>(mod + (static_cast<size_t>(cr) * 6 + scale_k) * D);
-  }
-  TO* hr = h + static_cast<size_t>(row) * D;
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int c = t + TPR * i;
-    if (c < D4) {
-      A y0 = (v[i][0] - mean) * rstd, y1 = (v[i][1] - mean) * rstd;
-      A y2 = (v[i][2] - mean) * rstd, y3 = (v[i][3] - mean) * rstd;
-      if (mod != nullptr) {
-        const float4 a = sc[c], b = sh[c];
-        y0 = y0 * (A(1) + A(a.x)) + A(b.x);
-        y1 = y1 * (A(1) + A(a.y)) + A(b.y);
-        y2 = y2 * (A(1) + A(a.z)) + A(b.z);
-        y3 = y3 * (A(1) + A(a.w)) + A(b.w);
+    for (int i = 0; i < NCH; ++i) {
+      const int c = t + TPR * i;
+      if (c < D4) {
+        load4<TX>::ld(xr + 4 * c, dst[i]);
+      } else {
+        dst[i][0] = dst[i][1] = dst[i][2] = dst[i][3] = A(0);
       }
-      store4<TO>::st(hr + 4 * c, make_float4(float(y0), float(y1), float(y2), float(y3)));
+    }
+  };
+  load_row(row_of(0), v[0]);
+#pragma unroll
+  for (int it = 0; it < ROWS; ++it) {
+    const int row_raw = (blockIdx.x * ROWS + it) * RPB + wrow;
+    if ((blockIdx.x * ROWS + it) * RPB >= N) break;  // uniform: no live row left in the block
+    const bool live = row_raw < N;
+    const int row = live ? row_raw : N - 1;
+    A (*vc)[4] = v[it & 1];
+    if (it + 1 < ROWS) load_row(row_of(it + 1), v[(it + 1) & 1]);
+    if (mod != nullptr) {
+      const int cr = cond_idx[row];
+      if (cr != cur_cond) {
+        cur_cond = cr;
+        const float4* sh = reinterpret_cast<const float4*>(mod + (static_cast<size_t>(cr) * 6 + shift_k) * D);
+        const float4* sc = reinterpret_cast<const float4*>(mod + (static_cast<size_t>(cr) * 6 + scale_k) * D);
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          const int c = t + TPR * i;
+          if (c < D4) {
+            shv[i] = sh[c];
+            scv[i] = sc[c];
+          }
+        }
+      }
+    }
+    A s = 0;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+      if (t + TPR * i < D4) s += (vc[i][0] + vc[i][1]) + (vc[i][2] + vc[i][3]);
+    A mean = 0;
+    if (norm == 1) mean = row_sum<A, WPR>(s, red[0], wrow, wsub, lane) * inv_d;
+    A ss = 0;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = t + TPR * i;
+      if (c < D4) {
+        const A a = vc[i][0] - mean, b = vc[i][1] - mean, cc = vc[i][2] - mean, d = vc[i][3] - mean;
+        ss += (a * a + b * b) + (cc * cc + d * d);
+      }
+    }
+    ss = row_sum<A, WPR>(ss, red[1], wrow, wsub, lane);
+    if (live) {
+      const A rstd = A(1) / sqrt(ss * inv_d + A(eps));
+      TO* hr = h + static_cast<size_t>(row) * D;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int c = t + TPR * i;
+        if (c < D4) {
+          A y0 = (vc[i][0] - mean) * rstd, y1 = (vc[i][1] - mean) * rstd;
+          A y2 = (vc[i][2] - mean) * rstd, y3 = (vc[i][3] - mean) * rstd;
+          if (mod != nullptr) {
+            const float4 a = scv[i], b = shv[i];
+            y0 = y0 * (A(1) + A(a.x)) + A(b.x);
+            y1 = y1 * (A(1) + A(a.y)) + A(b.y);
+            y2 = y2 * (A(1) + A(a.z)) + A(b.z);
+            y3 = y3 * (A(1) + A(a.w)) + A(b.w);
+          }
+          store4<TO>::st(hr + 4 * c, make_float4(float(y0), float(y1), float(y2), float(y3)));
+        }
+      }
     }
   }
 }
@@ -147,10 +179,19 @@ static hipError_t modnorm_t(int norm, float eps, int N, int D, const TX* x, cons
                             int which, const int32_t* ci, TO* h, hipStream_t s) {
   const int d4 = D / 4;
   const int shift_k = which == 0 ? 0 : 3, scale_k = which == 0 ? 1 : 4;
+  // several rows per workgroup once there are enough rows to fill the chip
+  constexpr int R = sizeof(TX) == 4 ? 4 : 1;
 #define DIT_MN(TPR, K)                                                                                \
   if ((d4 + TPR - 1) / TPR <= K) {                                                                   \
-    hipLaunchKernelGGL((modnorm_kernel<TX, TO, TPR, K>), dim3((N + 256 / TPR - 1) / (256 / TPR)), dim3(256), \
-                       0, s, N, D, norm, eps, x, mod, shift_k, scale_k, ci, h);                      \
+    constexpr int RPB = 256 / TPR;                                                                    \
+    if (N >= 4096 * RPB) {                                                                            \
+      const int nb = (N + RPB * R - 1) / (RPB * R);                                                   \
+      hipLaunchKernelGGL((modnorm_kernel<TX, TO, TPR, K, R>), dim3(nb), dim3(256), 0, s, N, D, norm, eps, \
+                         x, mod, shift_k, scale_k, ci, h);                                            \
+    } else {                                                                                          \
+      hipLaunchKernelGGL((modnorm_kernel<TX, TO, TPR, K, 1>), dim3((N + RPB - 1) / RPB), dim3(256), 0, s, \
+                         N, D, norm, eps, x, mod, shift_k, scale_k, ci, h);                           \
+    }                                                                                                 \
     return hipGetLastError();                                                                         \
   }
   if (d4 <= 256) {
@@ -599,6 +640,33 @@ hipError_t euler(int64_t n, float* x, const float* v, const float* dt, hipStream
   LaunchScope scope_(kCntEuler, s);
   hipLaunchKernelGGL(euler_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, n,
                      x, v, dt);
+  return hipGetLastError();
+}
+
+// ============================================================================ guided Euler step
+// Classifier-free guidance then the Euler update, each operation rounded to
+// fp32 in turn (no contraction): g = vu + w (vc - vu); x += dt g.
+__global__ __launch_bounds__(256) void cfg_euler_kernel(int64_t n, float* __restrict__ x,
+                                                       const float* __restrict__ vc,
+                                                       const float* __restrict__ vu, float w,
+                                                       const float* __restrict__ dt) {
+#pragma clang fp contract(off)
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) {
+    const float u = vu[i];
+    const float d = vc[i] - u;
+    const float g = u + w * d;
+    const float p = dt[0] * g;
+    x[i] = x[i] + p;
+  }
+}
+
+hipError_t cfg_euler(int64_t n, float* x, const float* vc, const float* vu, float w, const float* dt,
+                     hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  LaunchScope scope_(kCntCfgEuler, s);
+  hipLaunchKernelGGL(cfg_euler_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
+                     n, x, vc, vu, w, dt);
   return hipGetLastError();
 }
 

@@ -11,7 +11,7 @@ namespace dit {
 enum Counter {
   kCntGemmBf16 = 0, kCntGemmF32, kCntAttnBf16, kCntAttnF32, kCntModnorm, kCntRopeSplit,
   kCntSiluGate, kCntGatedResidual, kCntAdaln, kCntPatchIn, kCntPatchOut, kCntEuler,
-  kCntGemmF32Reduce, kCntConvert, kCntResidNormSlice, kCntSiluSlice, kCntNum
+  kCntGemmF32Reduce, kCntConvert, kCntResidNormSlice, kCntSiluSlice, kCntCfgEuler, kCntNum
 };
 void count_launch(Counter c);
 
@@ -103,5 +103,8 @@ hipError_t patch_in(int io, int C, const int* patch, const int* grid, const floa
 hipError_t patch_out(int io, int C, const int* patch, const int* grid, const float* tokens,
                      float* latent, hipStream_t s);
 hipError_t euler(int64_t n, float* x, const float* v, const float* dt, hipStream_t s);
+// x += dt * (vu + w * (vc - vu)), each operation rounded to fp32
+hipError_t cfg_euler(int64_t n, float* x, const float* vc, const float* vu, float w, const float* dt,
+                     hipStream_t s);
 
 }  // namespace dit

@@ -31,7 +31,7 @@ DIT_IO_NONE, DIT_IO_PATCH3D, DIT_IO_CHANNEL_MAJOR = 0, 1, 2
 MAX_MOD = 4
 COUNTER_NAMES = ["gemm_bf16", "gemm_f32", "attention_bf16", "attention_f32", "modnorm", "rope_split",
                  "silu_gate", "gated_residual", "adaln", "patch_in", "patch_out", "euler",
-                 "gemm_f32_reduce", "convert", "resid_norm_slice", "silu_slice"]
+                 "gemm_f32_reduce", "convert", "resid_norm_slice", "silu_slice", "cfg_euler"]
 
 
 class DitError(RuntimeError):
@@ -91,6 +91,7 @@ _SIGS = {
     "dit_forward": [_P, _P, _P, _P, _P, _P, _SZ, _P],
     "dit_denoise_step": [_P, _P, _P, _P, _P, _P, _SZ, _P],
     "dit_denoise_loop": [_P, _P, _P, _P, _P, _I, _P, _SZ, _P],
+    "dit_cfg_denoise_loop": [_P, _P, _P, _P, _P, ctypes.c_float, _I, _P, _SZ, _P],
     "dit_gemm_workspace_bytes": [_I, _I, _I, _I, ctypes.POINTER(_SZ)],
     "dit_gemm_splits": [_I, _I, _I, ctypes.POINTER(_I)],
     "dit_gemm": [_I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _SZ, _P],
@@ -380,6 +381,12 @@ def dit_denoise_step(model: Model, batch: Batch, latents, cond, dt, ws, stream=N
 def dit_denoise_loop(model: Model, batch: Batch, latents, cond_table, dt_table, n_steps: int, ws, stream=None):
     _check(load().dit_denoise_loop(model.handle, batch.handle, _ptr(latents), _ptr(cond_table), _ptr(dt_table),
                                    n_steps, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def dit_cfg_denoise_loop(model: Model, batch: Batch, latents, cond_table, dt_table, w: float, n_steps: int, ws,
+                         stream=None):
+    _check(load().dit_cfg_denoise_loop(model.handle, batch.handle, _ptr(latents), _ptr(cond_table), _ptr(dt_table),
+                                       float(w), n_steps, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 # ----------------------------------------------------------------------------- op-level calls
