@@ -440,3 +440,58 @@ def test_cfg_loop_oracle_parity(H, name):
         ratio = np.abs(dg - dr) / tol[k]
         print(f"cfg {name} {k}: max|d| {np.abs(dg - dr).max():.3e} worst err/bound {ratio.max():.3f}")
         assert (ratio <= 1).all(), f"{k}: {(ratio > 1).sum()} outside the bound, worst {ratio.max():.3f}"
+
+
+# ----------------------------------------------------------------------------- fused epilogues
+
+@pytest.mark.parametrize("name", ["c3_small", "ragged"])
+def test_bf16_block_equals_separate_kernels_bits(H, name):
+    """The bf16 block applies the SiLU gate inside the MLP-in GEMM's epilogue
+    (its weight staged in [32 gate | 32 up] row groups); it equals the same
+    block built from the op-level calls -- a GEMM that stores u on the plain
+    [gate | up] weight, then the separate SiLU-gate kernel -- bit for bit,
+    at a ragged width too (ffn 704: 5.5 column tiles of 256)."""
+    cfg = C3_SMALL if name == "c3_small" else scaled(
+        C3_SMALL, hidden=256, n_heads=2, ffn=704,
+        segments=(Segment(0, (1, 5, 7), 0), Segment(1, (45,), 1), Segment(0, (2, 3, 9), 0)))
+    w = S.all_weights(cfg, 0, threads=8)
+    m = _stage(H, cfg, w)
+    r = H.Runner(cfg, 0, model=m)
+    dit = H.dit
+    N, D, F, nh, hd = cfg.n_tokens, cfg.hidden, cfg.ffn, cfg.n_heads, cfg.head_dim
+    mod = torch.empty(1, r.batch.n_cond, 6, D, device="cuda")
+    dit.dit_modulation(m, r.batch, 0, 1, r.cond, mod)
+    x_blk = r.x_in.clone()
+    dit.dit_block_forward(m, 0, x_blk, mod[0], r.batch, r.ws)
+
+    lay = dit.dit_pack_layout(cfg)
+    cos, sin = dit.dit_rope_cache_build(cfg)
+    cu = torch.from_numpy(lay["cu_seqlens"]).cuda()
+    ci = torch.from_numpy(lay["cond_idx"]).cuda()
+    cos, sin = torch.from_numpy(cos).cuda(), torch.from_numpy(sin).cuda()
+    bw = lambda k: torch.from_numpy(w[f"blocks.0.{k}"]).cuda()
+    wb = lambda k: bw(k).to(torch.bfloat16).contiguous()
+    mod0 = mod[0].contiguous()
+    norm = 0 if cfg.norm == "rms" else 1
+    x = r.x_in.clone()
+    h = torch.empty(N, D, dtype=torch.bfloat16, device="cuda")
+    dit.dit_modnorm(norm, cfg.norm_eps, x, mod0, 0, ci, h)
+    qkv = torch.empty(N, 3 * D, dtype=torch.bfloat16, device="cuda")
+    dit.dit_gemm(h, wb("attn.qkv.weight"), bw("attn.qkv.bias"), qkv)
+    q, k, v = (torch.empty(nh, N, hd, dtype=torch.bfloat16, device="cuda") for _ in range(3))
+    dit.dit_rope_split(qkv, nh, hd, cfg.rot_dim, cos, sin, q, k, v)
+    o = torch.empty(N, D, dtype=torch.bfloat16, device="cuda")
+    dit.dit_attention(q, k, v, cu, r.batch.max_seqlen, o)
+    a = torch.empty(N, D, dtype=torch.float32, device="cuda")
+    dit.dit_gemm(o, wb("attn.out.weight"), bw("attn.out.bias"), a)
+    dit.dit_gated_residual(x, a, mod0, 0, ci)
+    dit.dit_modnorm(norm, cfg.norm_eps, x, mod0, 1, ci, h)
+    u = torch.empty(N, 2 * F, dtype=torch.bfloat16, device="cuda")
+    dit.dit_gemm(h, wb("mlp.in.weight"), bw("mlp.in.bias"), u)
+    mm = torch.empty(N, F, dtype=torch.bfloat16, device="cuda")
+    dit.dit_silu_gate(u, mm)
+    dit.dit_gemm(mm, wb("mlp.out.weight"), bw("mlp.out.bias"), a)
+    dit.dit_gated_residual(x, a, mod0, 1, ci)
+    torch.cuda.synchronize()
+    assert (x - r.x_in).abs().max().item() > 1e-3
+    assert torch.equal(x_blk, x)

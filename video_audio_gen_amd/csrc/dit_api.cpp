@@ -183,7 +183,7 @@ struct Slot {
   int64_t shape[2];
   int dtype;       // slot dtype in the slab
   int kind;
-  bool swap_halves;
+  int row_order;   // kRowsSwapHalves | kRowsPairs32, applied at stage time
   size_t offset, bytes;
   bool staged;
 };
@@ -212,11 +212,27 @@ struct dit_model {
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Stage-time row orders of the MLP-in weight and bias (2F rows):
+//   kRowsSwapHalves: a [value | gate] model is stored [gate | up];
+//   kRowsPairs32 (bf16 stream): groups of 64 rows [32 gate | 32 up] of the same
+//     32 features, so the GEMM that produces them can apply the SiLU gate in
+//     its epilogue (a wave holds both halves of a group).
+enum RowOrder { kRowsSwapHalves = 1, kRowsPairs32 = 2 };
+
+static int64_t staged_source_row(int64_t r, int64_t rows, int order) {
+  int64_t q = r;  // row in [gate | up] order
+  if (order & kRowsPairs32) {
+    const int64_t g = r / 64, w = r % 64;
+    q = (w < 32 ? 0 : rows / 2) + g * 32 + (w % 32);
+  }
+  return (order & kRowsSwapHalves) ? (q + rows / 2) % rows : q;
+}
+
 static void build_contract(const dit_config& c, std::vector<Slot>* slots, size_t* total) {
   const int64_t D = c.hidden, F = c.ffn, dt = c.cond_dim;
   const int sd = c.stream_dtype;
   size_t off = 0;
-  auto add = [&](const std::string& name, int ndim, int64_t s0, int64_t s1, int dtype, int kind, bool swap) {
+  auto add = [&](const std::string& name, int ndim, int64_t s0, int64_t s1, int dtype, int kind, int order) {
     Slot s;
     s.name = name;
     s.ndim = ndim;
@@ -224,7 +240,7 @@ static void build_contract(const dit_config& c, std::vector<Slot>* slots, size_t
     s.shape[1] = s1;
     s.dtype = dtype;
     s.kind = kind;
-    s.swap_halves = swap;
+    s.row_order = order;
     const int64_t n = ndim == 1 ? s0 : s0 * s1;
     s.bytes = dtype == kSlicedF32 ? gemm_f32_slices_bytes(static_cast<int>(s0), static_cast<int>(s1))
                                   : static_cast<size_t>(n) * (dtype == DIT_BF16 ? 2 : 4);
@@ -242,7 +258,7 @@ static void build_contract(const dit_config& c, std::vector<Slot>* slots, size_t
       add("out." + std::to_string(m) + ".bias", 1, cw, 0, DIT_F32, kBias, false);
     }
   }
-  const bool swap = c.mlp == DIT_MLP_VALUE_GATE;
+  const int in_order = (c.mlp == DIT_MLP_VALUE_GATE ? kRowsSwapHalves : 0) | (sd == DIT_BF16 ? kRowsPairs32 : 0);
   const int gd = sd == DIT_BF16 ? DIT_BF16 : kSlicedF32;  // dtype of the GEMM weights
   for (int b = 0; b < c.n_blocks; ++b) {
     const std::string p = "blocks." + std::to_string(b) + ".";
@@ -254,8 +270,8 @@ static void build_contract(const dit_config& c, std::vector<Slot>* slots, size_t
     add(p + "attn.qkv.bias", 1, 3 * D, 0, DIT_F32, kBias, false);
     add(p + "attn.out.weight", 2, D, D, gd, kBlockMat, false);
     add(p + "attn.out.bias", 1, D, 0, DIT_F32, kBias, false);
-    add(p + "mlp.in.weight", 2, 2 * F, D, gd, kBlockMat, swap);
-    add(p + "mlp.in.bias", 1, 2 * F, 0, DIT_F32, kBias, swap);
+    add(p + "mlp.in.weight", 2, 2 * F, D, gd, kBlockMat, in_order);
+    add(p + "mlp.in.bias", 1, 2 * F, 0, DIT_F32, kBias, in_order);
     add(p + "mlp.out.weight", 2, D, F, gd, kBlockMat, false);
     add(p + "mlp.out.bias", 1, D, 0, DIT_F32, kBias, false);
   }
@@ -326,7 +342,7 @@ extern "C" int dit_stage_weights(dit_model* m, const dit_weight_view* views, int
     const int64_t count = sl.ndim == 1 ? sl.shape[0] : sl.shape[0] * sl.shape[1];
     const void* src = v.host;
     const bool sliced = sl.dtype == kSlicedF32;
-    const bool need_conv = v.dtype != sl.dtype || sl.swap_halves;
+    const bool need_conv = v.dtype != sl.dtype || sl.row_order != 0;
     if (need_conv) {
       // rows gathered (and widened or rounded) into the slot dtype; a sliced
       // slot gathers float32 rows first and slices them below
@@ -334,8 +350,7 @@ extern "C" int dit_stage_weights(dit_model* m, const dit_weight_view* views, int
       const int64_t rows = sl.shape[0];
       const int64_t cols = sl.ndim == 1 ? 1 : sl.shape[1];
       for (int64_t r = 0; r < rows; ++r) {
-        // mlp.in of a [value | gate] model: destination row r takes source row (r + rows/2) % rows.
-        const int64_t sr = sl.swap_halves ? (r + rows / 2) % rows : r;
+        const int64_t sr = staged_source_row(r, rows, sl.row_order);
         for (int64_t c = 0; c < cols; ++c) {
           const int64_t di = r * cols + c, si = sr * cols + c;
           if (sl.dtype == DIT_BF16 && !sliced) {
@@ -584,7 +599,7 @@ static WsPlan plan_ws(const dit_model* m, const dit_batch* b) {
   p.x = take(c.stream_dtype == DIT_BF16 ? (c.io ? sizeof(float) * N * D : 0) : sizeof(double) * N * D);
   const bool bf = c.stream_dtype == DIT_BF16;
   p.h = take(bf ? es * N * D : 0);
-  p.big = take(bf ? es * N * (3 * D > 2 * F ? 3 * D : 2 * F) : 0);
+  p.big = take(bf ? es * N * 3 * D : 0);  // the QKV GEMM's output (MLP-in's is consumed in its epilogue)
   p.qkvh = take(es * N * (3 * D > F ? 3 * D : F));
   p.o = take(es * N * D);
   p.a = take(sizeof(float) * N * D);
@@ -653,26 +668,30 @@ static int run_block_bf16(dit_model* m, int blk, float* x, const float* mod, con
   void* big = ws + p.big;
   uint16_t* qkvh = reinterpret_cast<uint16_t*>(ws + p.qkvh);
   uint16_t* o = reinterpret_cast<uint16_t*>(ws + p.o);
-  float* a = reinterpret_cast<float*>(ws + p.a);
-  void* gws = ws + p.gemm;
   uint16_t* q = qkvh;
   uint16_t* k = qkvh + static_cast<size_t>(N) * D;
   uint16_t* v = qkvh + 2 * static_cast<size_t>(N) * D;
-  auto gemm = [&](int n, int kk, const void* A, const void* W, const float* bias, void* C, bool c_f32) {
-    return gemm_bf16(N, n, kk, static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W), bias, C, c_f32, gws, s);
+  auto gemm = [&](int n, int kk, const void* A, const void* W, const float* bias, void* C, const GemmEpilogue& ep) {
+    return gemm_bf16(N, n, kk, static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W), bias, C, ep, s);
   };
+  // The SiLU gate runs in the MLP-in GEMM's epilogue (the weight is staged in
+  // [32 gate | 32 up] row groups), which writes m = silu(g) * u and never u:
+  // every value is the one the separate kernel produces from a stored u.
+  float* a = reinterpret_cast<float*>(ws + p.a);
+  const GemmEpilogue to_bf16{kEpiBf16};
+  const GemmEpilogue to_f32{kEpiF32};
+  const GemmEpilogue silu{kEpiSiluGate};
   // attention sub-layer
   DIT_HIP(modnorm(true, c.norm, c.norm_eps, N, D, false, x, mod, 0, b->cond_dev, h, s));
-  DIT_HIP(gemm(3 * D, D, h, w.qkv_w, w.qkv_b, big, false));
+  DIT_HIP(gemm(3 * D, D, h, w.qkv_w, w.qkv_b, big, to_bf16));
   DIT_HIP(rope_split(true, N, H, hd, c.rot_dim, big, b->cos_dev, b->sin_dev, q, k, v, s));
   DIT_HIP(attention_bf16(N, H, hd, b->n_segs, b->cu_dev, b->max_seqlen, q, k, v, o, s));
-  DIT_HIP(gemm(D, D, o, w.out_w, w.out_b, a, true));
+  DIT_HIP(gemm(D, D, o, w.out_w, w.out_b, a, to_f32));
   DIT_HIP(gated_residual(N, D, false, x, a, mod, 0, b->cond_dev, s));
   // MLP sub-layer
   DIT_HIP(modnorm(true, c.norm, c.norm_eps, N, D, false, x, mod, 1, b->cond_dev, h, s));
-  DIT_HIP(gemm(2 * F, D, h, w.in_w, w.in_b, big, false));
-  DIT_HIP(silu_gate(true, N, F, big, qkvh, s));
-  DIT_HIP(gemm(D, F, qkvh, w.mo_w, w.mo_b, a, true));
+  DIT_HIP(gemm(2 * F, D, h, w.in_w, w.in_b, qkvh, silu));
+  DIT_HIP(gemm(D, F, qkvh, w.mo_w, w.mo_b, a, to_f32));
   DIT_HIP(gated_residual(N, D, false, x, a, mod, 1, b->cond_dev, s));
   return DIT_OK;
 }
@@ -946,8 +965,8 @@ extern "C" int dit_gemm(int dtype, int M, int N, int K, const void* A, const voi
   if (dtype == DIT_BF16) {
     if (!gemm_bf16_supported(M, N, K)) return set_error(DIT_E_UNSUPPORTED, "dit_gemm bf16: K=%d must be a multiple of 32", K);
     if (c_dtype != DIT_F32 && c_dtype != DIT_BF16) return set_error(DIT_E_INVALID, "dit_gemm: c_dtype");
-    DIT_HIP(gemm_bf16(M, N, K, static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), bias, C,
-                      c_dtype == DIT_F32, ws, s));
+    const GemmEpilogue ep{c_dtype == DIT_F32 ? kEpiF32 : kEpiBf16};
+    DIT_HIP(gemm_bf16(M, N, K, static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), bias, C, ep, s));
     return DIT_OK;
   }
   if (dtype != DIT_F32) return set_error(DIT_E_INVALID, "dit_gemm: dtype");

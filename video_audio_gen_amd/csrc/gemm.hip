@@ -58,6 +58,7 @@ __device__ __forceinline__ int gb_swz(int r, int c) {
   return r * gb::CPR + (c ^ ((r >> sh) & (gb::CPR - 1)));
 }
 static_assert(gb::CPR == 4 || gb::CPR == 8, "tile rows of 4 or 8 16-byte chunks");
+static_assert(gb::WN == 64 && gb::BN % 64 == 0, "the SiLU-gate epilogue pairs a wave's two 32-column tiles");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(gb::NT) void gemm_bf16_kernel(int M, int N, int K,
                                                               const bf16_t* __restrict__ A,
                                                               const bf16_t* __restrict__ B,
                                                               const float* __restrict__ bias,
-                                                              void* __restrict__ Cv, int c_f32,
+                                                              void* __restrict__ Cv, GemmEpilogue ep,
                                                               int tiles_m, int tiles_n) {
   using namespace gb;
   __shared__ uint4 smem[STAGES * (BM + BN) * CPR];  // STAGES x (A + B): 128 KB at 2 x 64 or 4 x 32
@@ -202,6 +203,33 @@ __global__ __launch_bounds__(gb::NT) void gemm_bf16_kernel(int M, int N, int K,
 #undef GB_DMA
 
   // Epilogue: lane l of a 32x32 tile holds column l%32, rows 8*(e/4) + 4*(l/32) + e%4.
+  if (ep.mode == kEpiSiluGate) {
+    // Columns come in 64-wide groups [32 gate | 32 up] of the same 32 MLP
+    // features (the staged row order), so a wave's two 32-column tiles hold
+    // the gate and the up value of one output: both rounded to bf16 as a
+    // stored u would be, then silu(g) * up in fp32, rounded to bf16.
+    const int gn = n0 + wc + lr;  // gate column; its up column is gn + 32
+    if (gn < N) {
+      const int F = N >> 1;
+      const int f = ((n0 + wc) >> 1) + lr;
+      const float bg = bias != nullptr ? bias[gn] : 0.f;
+      const float bu = bias != nullptr ? bias[gn + 32] : 0.f;
+      bf16_t* Mo = static_cast<bf16_t*>(Cv);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int gm = m0 + wr + i * 32 + 8 * (e >> 2) + 4 * lg + (e & 3);
+          if (gm < M) {
+            const float g = bf16_to_f32(f32_to_bf16(acc[i][0][e] + bg));
+            const float u = bf16_to_f32(f32_to_bf16(acc[i][1][e] + bu));
+            Mo[static_cast<size_t>(gm) * F + f] = f32_to_bf16(g / (1.0f + expf(-g)) * u);
+          }
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int gn = n0 + wc + j * 32 + lr;
@@ -214,10 +242,12 @@ __global__ __launch_bounds__(gb::NT) void gemm_bf16_kernel(int M, int N, int K,
         const int gm = m0 + wr + i * 32 + 8 * (e >> 2) + 4 * lg + (e & 3);
         if (gm < M) {
           const float v = acc[i][j][e] + bv;
-          if (c_f32)
-            static_cast<float*>(Cv)[static_cast<size_t>(gm) * N + gn] = v;
-          else
-            static_cast<bf16_t*>(Cv)[static_cast<size_t>(gm) * N + gn] = f32_to_bf16(v);
+          const size_t o = static_cast<size_t>(gm) * N + gn;
+          if (ep.mode == kEpiF32) {
+            static_cast<float*>(Cv)[o] = v;
+          } else {
+            static_cast<bf16_t*>(Cv)[o] = f32_to_bf16(v);
+          }
         }
       }
     }
@@ -231,12 +261,13 @@ bool gemm_bf16_supported(int M, int N, int K) {
 size_t gemm_bf16_ws_bytes(int, int, int) { return 0; }
 
 hipError_t gemm_bf16(int M, int N, int K, const uint16_t* A, const uint16_t* B, const float* bias,
-                     void* C, bool c_f32, void*, hipStream_t s) {
+                     void* C, const GemmEpilogue& ep, hipStream_t s) {
   if (M == 0) return hipSuccess;
+  if (ep.mode == kEpiSiluGate && N % 64 != 0) return hipErrorInvalidValue;
   LaunchScope scope_(kCntGemmBf16, s);
   const int tiles_m = (M + gb::BM - 1) / gb::BM, tiles_n = (N + gb::BN - 1) / gb::BN;
   hipLaunchKernelGGL(gemm_bf16_kernel, dim3(tiles_m * tiles_n), dim3(gb::NT), 0, s, M, N, K, A, B,
-                     bias, C, c_f32 ? 1 : 0, tiles_m, tiles_n);
+                     bias, C, ep, tiles_m, tiles_n);
   return hipGetLastError();
 }
 

@@ -29,8 +29,17 @@ class LaunchScope {
 
 // ---- GEMM: C[M,N] = A[M,K] . B[N,K]^T (+ bias)
 size_t gemm_bf16_ws_bytes(int M, int N, int K);
+// What the bf16 GEMM does with v = A.B^T + bias:
+//   kEpiBf16 / kEpiF32: store C[M,N] as bf16 / fp32;
+//   kEpiSiluGate: B's rows come in 64-row groups [32 gate | 32 up] of the same
+//     32 features; C is m[M, N/2] bf16, m = silu(bf16(g)) * bf16(u) in fp32, rounded
+//     to bf16 (N a multiple of 64).
+enum GemmEpiMode { kEpiBf16 = 0, kEpiF32 = 1, kEpiSiluGate = 2 };
+struct GemmEpilogue {
+  int mode;
+};
 hipError_t gemm_bf16(int M, int N, int K, const uint16_t* A, const uint16_t* B, const float* bias,
-                     void* C, bool c_f32, void* ws, hipStream_t s);
+                     void* C, const GemmEpilogue& ep, hipStream_t s);
 // f32: B is given as its int8 slices (slice_rows layout: 5 planes of
 // [Kp/32][N][32] int8, Kp = K rounded up to 32, then N int32 exponents, each
 // part 256-byte aligned); A is sliced into ws on the way.
