@@ -157,7 +157,9 @@ def cpu_baseline(cfg, weights_fn, islands, inp, sample_blocks: int, log=log, min
     mode = "bf16" if cfg.stream == "bf16" else "fp64"
     lay = O.pack_layout(cfg)
     cos, sin = O.rope_cache(cfg)
-    if cfg.cond_kind == "timestep":
+    if cfg.cond_kind == "timestep" and "t" not in inp:
+        emb = O.cond_embeddings(cfg, O.denoise_step_conditions(cfg, 0)[0])
+    elif cfg.cond_kind == "timestep":
         emb = O.cond_embeddings(cfg, [float(inp["t"][r.source]) for r in cfg.cond_rows])
     else:
         emb = O.cond_embeddings(cfg, None, inp["cond"])
@@ -225,6 +227,34 @@ def main(argv=None):
     r = harness.Runner(cfg, model=model)
     torch.cuda.synchronize()
 
+    # A timestep-conditioned denoise configuration times Euler steps of its
+    # schedule (dit_denoise_loop: forward + update per step, latents resident);
+    # every other configuration times forwards.
+    loop = cfg.denoise_steps > 0 and cfg.cond_kind == "timestep"
+    if loop:
+        sched = [dit.dit_sigma_schedule(cfg.shifts[m], cfg.denoise_steps) for m in range(cfg.n_mod)]
+        conds, dts = [], []
+        for i in range(cfg.denoise_steps):
+            t_rows = np.asarray([sched[rw.modality][0][i] for rw in cfg.cond_rows], np.float32)
+            conds.append(dit.dit_timestep_embedding(t_rows, cfg.cond_dim))
+            dts.append([sched[m][1][i] for m in range(cfg.n_mod)])
+        cond_tab = torch.from_numpy(np.stack(conds)).cuda()
+        dt_tab = torch.from_numpy(np.asarray(dts, np.float32)).cuda()
+        lat = r.x_in.clone()
+        state = {"i": 0}
+
+        def run_steps(k):
+            """k consecutive steps of the schedule; back to the initial noise at step 0."""
+            while k > 0:
+                i = state["i"]
+                if i == 0:
+                    lat.copy_(r.x_in)
+                n = min(k, cfg.denoise_steps - i)
+                dit.dit_denoise_loop(model, r.batch, lat, cond_tab[i:], dt_tab[i:], n, r.ws)
+                state["i"] = (i + n) % cfg.denoise_steps
+                k -= n
+        r.forward = lambda: run_steps(1)
+
     for _ in range(a.warmup):
         r.forward()
     torch.cuda.synchronize()
@@ -233,7 +263,7 @@ def main(argv=None):
     # replay without host round trips); its output is checked against the eager
     # forward before timing.
     step = r.forward
-    if not a.no_graph:
+    if not a.no_graph and not loop:
         eager = r.forward().clone()
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
@@ -252,18 +282,25 @@ def main(argv=None):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
-    for _ in range(a.steps):
-        step()
+    if loop:
+        run_steps(a.steps)
+    else:
+        for _ in range(a.steps):
+            step()
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = start.elapsed_time(stop) / a.steps
-    log(f"timed {a.steps} forwards: {ms:.3f} ms per forward (host wall {wall * 1e3 / a.steps:.3f} ms)")
+    log(f"timed {a.steps} {'denoise steps' if loop else 'forwards'}: {ms:.3f} ms per "
+        f"{'step' if loop else 'forward'} (host wall {wall * 1e3 / a.steps:.3f} ms)")
 
     # per-kernel device time: HIP events recorded around every launch on its stream
     dit.dit_profile_begin()
-    for _ in range(a.steps):
-        r.forward()
+    if loop:
+        run_steps(a.steps)
+    else:
+        for _ in range(a.steps):
+            r.forward()
     prof = dit.dit_profile_end()
     total_dev = sum(v[1] for v in prof.values())
     for k, (n, t) in sorted(prof.items(), key=lambda kv: -kv[1][1]):
@@ -337,6 +374,12 @@ def main(argv=None):
         "cpu_baseline": cpu,
         "kernels": kernels,
     }
+    if loop:
+        line["config"]["denoise_steps"] = cfg.denoise_steps
+        line["config"]["timed"] = f"{a.steps} Euler steps of the {cfg.denoise_steps}-step schedule (forward + update each)"
+        line["loop_s"] = round(ms * cfg.denoise_steps / 1e3, 3)
+        line["loop_s_kind"] = "measured" if a.steps == cfg.denoise_steps else \
+            f"{cfg.denoise_steps} x the measured per-step time"
     print(json.dumps(line), flush=True)
     return 0
 
