@@ -335,6 +335,9 @@ def main(argv=None):
         roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK[peak_key], "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK[peak_key], 4), "traffic": None, "kernel": fam,
                 "launches": n_launch, "avg_launch_us": round(fam_ms / n_launch * 1e3, 2), "peak_kind": peak_note}
+        if fam == "gemm_f32":
+            # the same rate against the published fp32 MFMA peak (the unit an fp32 GEMM would otherwise use)
+            roof["frac_of_fp32_mfma_peak"] = round(achieved / PEAK["mfma_f32"], 4)
     elif fam == "attention_bf16":
         flops = attention_flops(cfg) * a.steps
         achieved = flops / (fam_ms * 1e-3) / 1e12
