@@ -69,19 +69,21 @@ template <> struct load4<double> {
   }
 };
 
-// ROWS consecutive rows per workgroup, one after the other: the next row's x
-// is in flight while the current row reduces, and the shift/scale rows stay in
-// registers while consecutive rows share their modulation row (a packed
-// segment is contiguous), so they come from L2 once per workgroup instead of
-// once per row.  Every row's arithmetic is the same as with ROWS = 1.
-template <typename TX, typename TO, int TPR, int NCH, int ROWS>
-__global__ __launch_bounds__(256) void modnorm_kernel(int N, int D, int norm, float eps,
+// TPR threads per row (TPR/64 wavefronts; 256/TPR rows per workgroup below
+// 256 threads, one above).  ROWS consecutive rows per workgroup, one after
+// the other: the row PF ahead is in flight while the current row reduces, and
+// the shift/scale rows stay in registers while consecutive rows share their
+// modulation row (a packed segment is contiguous), so they come from L2 once
+// per workgroup instead of once per row.  Every row's arithmetic is the same
+// as with ROWS = 1.
+template <typename TX, typename TO, int TPR, int NCH, int ROWS, int PF = 1>
+__global__ __launch_bounds__(TPR > 256 ? TPR : 256) void modnorm_kernel(int N, int D, int norm, float eps,
                                                      const TX* __restrict__ x,
                                                      const float* __restrict__ mod, int shift_k,
                                                      int scale_k, const int32_t* __restrict__ cond_idx,
                                                      TO* __restrict__ h) {
   typedef typename norm_acc<TO>::T A;
-  constexpr int WPR = TPR / 64, RPB = 256 / TPR;
+  constexpr int WPR = TPR / 64, RPB = (TPR > 256 ? TPR : 256) / TPR;
   __shared__ A red[2][RPB * WPR];
   const int lane = threadIdx.x & 63;
   const int wrow = threadIdx.x / TPR;             // row within the block
@@ -89,7 +91,7 @@ __global__ __launch_bounds__(256) void modnorm_kernel(int N, int D, int norm, fl
   const int t = threadIdx.x % TPR;
   const int D4 = D >> 2;
   const A inv_d = A(1) / A(D);
-  A v[2][NCH][4];
+  A v[PF + 1][NCH][4];
   float4 shv[NCH], scv[NCH];
   int cur_cond = -1;
   auto row_of = [&](int it) {
@@ -108,15 +110,16 @@ __global__ __launch_bounds__(256) void modnorm_kernel(int N, int D, int norm, fl
       }
     }
   };
-  load_row(row_of(0), v[0]);
+#pragma unroll
+  for (int p = 0; p < PF && p < ROWS; ++p) load_row(row_of(p), v[p]);
 #pragma unroll
   for (int it = 0; it < ROWS; ++it) {
     const int row_raw = (blockIdx.x * ROWS + it) * RPB + wrow;
     if ((blockIdx.x * ROWS + it) * RPB >= N) break;  // uniform: no live row left in the block
     const bool live = row_raw < N;
     const int row = live ? row_raw : N - 1;
-    A (*vc)[4] = v[it & 1];
-    if (it + 1 < ROWS) load_row(row_of(it + 1), v[(it + 1) & 1]);
+    A (*vc)[4] = v[it % (PF + 1)];
+    if (it + PF < ROWS) load_row(row_of(it + PF), v[(it + PF) % (PF + 1)]);
     if (mod != nullptr) {
       const int cr = cond_idx[row];
       if (cr != cur_cond) {
@@ -179,17 +182,17 @@ static hipError_t modnorm_t(int norm, float eps, int N, int D, const TX* x, cons
                             int which, const int32_t* ci, TO* h, hipStream_t s) {
   const int d4 = D / 4;
   const int shift_k = which == 0 ? 0 : 3, scale_k = which == 0 ? 1 : 4;
-  // several rows per workgroup once there are enough rows to fill the chip
-  constexpr int R = sizeof(TX) == 4 ? 4 : 1;
+  // two rows per workgroup once there are enough rows to fill the chip
+  constexpr int R = sizeof(TX) == 4 ? 2 : 1;
 #define DIT_MN(TPR, K)                                                                                \
   if ((d4 + TPR - 1) / TPR <= K) {                                                                   \
-    constexpr int RPB = 256 / TPR;                                                                    \
+    constexpr int NTH = TPR > 256 ? TPR : 256, RPB = NTH / TPR;                                       \
     if (N >= 4096 * RPB) {                                                                            \
       const int nb = (N + RPB * R - 1) / (RPB * R);                                                   \
-      hipLaunchKernelGGL((modnorm_kernel<TX, TO, TPR, K, R>), dim3(nb), dim3(256), 0, s, N, D, norm, eps, \
+      hipLaunchKernelGGL((modnorm_kernel<TX, TO, TPR, K, R>), dim3(nb), dim3(NTH), 0, s, N, D, norm, eps, \
                          x, mod, shift_k, scale_k, ci, h);                                            \
     } else {                                                                                          \
-      hipLaunchKernelGGL((modnorm_kernel<TX, TO, TPR, K, 1>), dim3((N + RPB - 1) / RPB), dim3(256), 0, s, \
+      hipLaunchKernelGGL((modnorm_kernel<TX, TO, TPR, K, 1>), dim3((N + RPB - 1) / RPB), dim3(NTH), 0, s, \
                          N, D, norm, eps, x, mod, shift_k, scale_k, ci, h);                           \
     }                                                                                                 \
     return hipGetLastError();                                                                         \
@@ -199,7 +202,11 @@ static hipError_t modnorm_t(int norm, float eps, int N, int D, const TX* x, cons
   } else if (d4 <= 1024) {
     DIT_MN(128, 4) DIT_MN(128, 8)
   } else {
-    DIT_MN(256, 4) DIT_MN(256, 6) DIT_MN(256, 8)
+    // wide rows: 512 threads per row up to 6144 (fewer registers per thread,
+    // more waves in flight: 6144-wide rows 65 -> 69 % of HBM against 256).
+    // The thread count depends on D only, so a row's sums run in the same
+    // order whatever N is (a document alone equals it packed, bit for bit).
+    DIT_MN(512, 3) DIT_MN(256, 8)
   }
 #undef DIT_MN
   return hipErrorInvalidValue;
