@@ -344,7 +344,7 @@ __global__ __launch_bounds__(af::NT) void attention_f32_kernel(int N, int H, con
   constexpr int NDB = HD / 16;  // 16-dim output blocks
   constexpr int F4 = HD / 4;    // float4 per row
   constexpr int KV_FLOATS = KT * (KS + VS);
-  static_assert(KV_FLOATS >= NW * QT * (HD + 2) * 2, "the merge reuses the K/V tile space");
+  static_assert(KV_FLOATS >= (NW * QT * (HD + 3) + QT) * 2, "the merge reuses the K/V tile space");
   __shared__ float Qs[QT * KS];
   __shared__ __align__(16) float KVs[KV_FLOATS];
   float* Ks = KVs;
@@ -358,12 +358,40 @@ __global__ __launch_bounds__(af::NT) void attention_f32_kernel(int N, int H, con
   const int r16 = lane & 15, g = lane >> 4;
   const size_t base = (static_cast<size_t>(h) * N + s0) * HD;
 
+  // K/V tiles pass through registers: the loads of tile t+1 are issued before
+  // tile t's MFMAs and land in LDS after them.  Thread tid holds the float4s
+  // tid + NT j of the tile (row r = i / F4, column chunk i % F4).
+  constexpr int PT = KT * F4 / NT;  // float4 per thread per operand
+  static_assert(KT * F4 % NT == 0, "whole float4s per thread");
+  float4 kreg[PT], vreg[PT];
+  auto load_kv = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const int i = tid + NT * j, r = i / F4, c = i % F4;
+      kreg[j] = vreg[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (k0 + r < len) {
+        const size_t off = base + static_cast<size_t>(k0 + r) * HD + 4 * c;
+        kreg[j] = *reinterpret_cast<const float4*>(k + off);
+        vreg[j] = *reinterpret_cast<const float4*>(v + off);
+      }
+    }
+  };
+  auto store_kv = [&]() {
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const int i = tid + NT * j, r = i / F4, c = i % F4;
+      *reinterpret_cast<float4*>(&Ks[r * KS + 4 * c]) = kreg[j];
+      *reinterpret_cast<float4*>(&Vs[r * VS + 4 * c]) = vreg[j];
+    }
+  };
+  load_kv(0);
   for (int i = tid; i < QT * F4; i += NT) {
     const int r = i / F4, c = i % F4;
     const float4 t = q0 + r < len ? *reinterpret_cast<const float4*>(q + base + static_cast<size_t>(q0 + r) * HD + 4 * c)
                                   : make_float4(0.f, 0.f, 0.f, 0.f);
     *reinterpret_cast<float4*>(&Qs[r * KS + 4 * c]) = t;
   }
+  store_kv();
   __syncthreads();
   // Q^T operand: lane holds Q[query r16][dim 4 ks + g]
   double qf[HD / 4];
@@ -378,19 +406,12 @@ __global__ __launch_bounds__(af::NT) void attention_f32_kernel(int N, int H, con
   const int n_kt = (len + KT - 1) / KT;
   for (int t = 0; t < n_kt; ++t) {
     const int k0 = t * KT;
-    __syncthreads();  // previous tile consumed
-    for (int i = tid; i < KT * F4; i += NT) {
-      const int r = i / F4, c = i % F4;
-      float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
-      if (k0 + r < len) {
-        const size_t off = base + static_cast<size_t>(k0 + r) * HD + 4 * c;
-        kv = *reinterpret_cast<const float4*>(k + off);
-        vv = *reinterpret_cast<const float4*>(v + off);
-      }
-      *reinterpret_cast<float4*>(&Ks[r * KS + 4 * c]) = kv;
-      *reinterpret_cast<float4*>(&Vs[r * VS + 4 * c]) = vv;
+    if (t > 0) {
+      __syncthreads();  // previous tile consumed
+      store_kv();
+      __syncthreads();
     }
-    __syncthreads();
+    if (t + 1 < n_kt) load_kv(k0 + KT);
     const int kb0 = wave * 16;  // this wavefront's key block
     if (k0 + kb0 >= len) continue;
     // S^T block: lane holds keys kb0 + 4i + g of query r16
@@ -448,22 +469,36 @@ __global__ __launch_bounds__(af::NT) void attention_f32_kernel(int N, int H, con
 #pragma unroll
     for (int i = 0; i < 4; ++i) ow[(wave * HD + b * 16 + 4 * i + g) * QT + r16] = acc[b][i];
   __syncthreads();
-  for (int idx = tid; idx < QT * HD; idx += NT) {
-    const int qq = idx / HD, dim = idx % HD;
-    if (q0 + qq >= len) continue;
+  // Per query: each wavefront's factor exp(m_w - m) (0 for a wavefront that saw
+  // no key of the document) and the merged denominator, once per query.
+  double* fw = ow + NW * HD * QT;  // [NW][QT]
+  double* dw = fw + NW * QT;       // [QT]
+  if (tid < QT) {
+    const int qq = tid;
     double m = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) m = fmax(m, mw[w * QT + qq]);
-    double num = 0.0, den = 0.0;
+    double den = 0.0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       const double mwq = mw[w * QT + qq];
-      if (mwq == -INFINITY) continue;  // a wavefront that saw no key of the document
-      const double f = exp(mwq - m);
-      num += f * ow[(w * HD + dim) * QT + qq];
-      den += f * lw[w * QT + qq];
+      const double f = mwq == -INFINITY ? 0.0 : exp(mwq - m);
+      fw[w * QT + qq] = f;
+      if (mwq != -INFINITY) den += f * lw[w * QT + qq];
     }
-    o[static_cast<size_t>(s0 + q0 + qq) * H * HD + static_cast<size_t>(h) * HD + dim] = static_cast<float>(num / den);
+    dw[qq] = den;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < QT * HD; idx += NT) {
+    const int qq = idx / HD, dim = idx % HD;
+    if (q0 + qq >= len) continue;
+    double num = 0.0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      if (mw[w * QT + qq] == -INFINITY) continue;
+      num += fw[w * QT + qq] * ow[(w * HD + dim) * QT + qq];
+    }
+    o[static_cast<size_t>(s0 + q0 + qq) * H * HD + static_cast<size_t>(h) * HD + dim] = static_cast<float>(num / dw[qq]);
   }
 }
 
