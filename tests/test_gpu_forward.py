@@ -495,3 +495,32 @@ def test_bf16_block_equals_separate_kernels_bits(H, name):
     torch.cuda.synchronize()
     assert (x - r.x_in).abs().max().item() > 1e-3
     assert torch.equal(x_blk, x)
+
+
+def test_cfg_loop_graph_replay_matches_eager(H):
+    """Three guided steps captured as one HIP graph (two device copies, the
+    forward's kernels and the guided Euler kernel per step) replay equal to
+    the eager loop bit for bit, three times, with eager loops between."""
+    cfg = CFG_SMALL
+    w_model = S.all_weights(cfg, 0, threads=8)
+    r = H.Runner(cfg, 0, model=_stage(H, cfg, w_model))
+    n = 3
+    _, cond_tab, _, dt_tab = _cfg_tables(H, cfg, n)
+    half = r.x_in.numel() // 2
+    lat = r.x_in[:half].clone()
+    H.dit.dit_cfg_denoise_loop(r.model, r.batch, lat, cond_tab, dt_tab, 3.5, n, r.ws)
+    torch.cuda.synchronize()
+    eager = lat.clone()
+    g_lat = r.x_in[:half].clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        H.dit.dit_cfg_denoise_loop(r.model, r.batch, g_lat, cond_tab, dt_tab, 3.5, n, r.ws)
+    for _ in range(3):
+        g_lat.copy_(r.x_in[:half])
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(g_lat, eager)
+        again = r.x_in[:half].clone()
+        H.dit.dit_cfg_denoise_loop(r.model, r.batch, again, cond_tab, dt_tab, 3.5, n, r.ws)
+        torch.cuda.synchronize()
+        assert torch.equal(again, eager)
