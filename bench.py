@@ -294,6 +294,32 @@ def main(argv=None):
     log(f"timed {a.steps} {'denoise steps' if loop else 'forwards'}: {ms:.3f} ms per "
         f"{'step' if loop else 'forward'} (host wall {wall * 1e3 / a.steps:.3f} ms)")
 
+    # The pages' protocol beside it: loops of R = 1 and R = 3 forwards, each
+    # between two events, five of each; median / min / max per forward and the
+    # slope over R (the intercept is a loop's fixed cost).
+    timing = None
+    if not loop:
+        per = {1: [], 3: []}
+        for _ in range(5):
+            for R in (1, 3):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record()
+                for _ in range(R):
+                    step()
+                e1.record()
+                torch.cuda.synchronize()
+                per[R].append(e0.elapsed_time(e1))
+        med = {R: float(np.median(v)) for R, v in per.items()}
+        slope = (med[3] - med[1]) / 2
+        timing = {"loops": 5,
+                  "r1_ms": {"median": round(med[1], 4), "min": round(min(per[1]), 4), "max": round(max(per[1]), 4)},
+                  "r3_ms_per_forward": {"median": round(med[3] / 3, 4), "min": round(min(per[3]) / 3, 4),
+                                        "max": round(max(per[3]) / 3, 4)},
+                  "slope_ms_per_forward": round(slope, 4), "intercept_ms": round(med[1] - slope, 4)}
+        log(f"R=1 median {med[1]:.3f} ms, R=3 median {med[3] / 3:.3f} ms per forward, slope {slope:.3f} ms, "
+            f"intercept {med[1] - slope:.3f} ms")
+
     # per-kernel device time: HIP events recorded around every launch on its stream
     dit.dit_profile_begin()
     if loop:
@@ -375,6 +401,7 @@ def main(argv=None):
                    "device": dev, "launch": "hip_graph" if step is not r.forward else "eager"},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "timing": timing,
         "kernels": kernels,
     }
     if loop:
