@@ -444,7 +444,43 @@ def test_cfg_loop_oracle_parity(H, name):
 
 # ----------------------------------------------------------------------------- fused epilogues
 
-@pytest.mark.parametrize("name", ["c3_small", "ragged"])
+def _with_biases(w, seed=7, scale=0.1):
+    """The weights with every bias (block GEMMs, AdaLN, projections) drawn
+    N(0, scale^2) instead of zero, so the bias paths carry values."""
+    rng = np.random.default_rng(seed)
+    out = dict(w)
+    for k, v in w.items():
+        if k.endswith(".bias"):
+            out[k] = (rng.standard_normal(v.shape) * scale).astype(np.float32)
+    return out
+
+
+@pytest.mark.parametrize("name", ["c1_ragged_value_gate", "c3_small", "c4_small_io"])
+def test_nonzero_biases_parity(H, name):
+    """Every bias non-zero: oracle parity (fp32 bound, or the bf16 bound with
+    its control arm), and the output moves against the zero-bias forward, so
+    no bias path is dead -- including the MLP-in bias staged half-swapped
+    ([value | gate] models) or in [32 gate | 32 up] groups (bf16 models)."""
+    cfg = {"c1_ragged_value_gate": C1_RAGGED, "c3_small": C3_SMALL, "c4_small_io": C4_SMALL}[name]
+    w0 = S.all_weights(cfg, 0, threads=8)
+    w = _with_biases(w0)
+    r = H.Runner(cfg, 0, model=_stage(H, cfg, w))
+    r.forward()
+    got = r.output_numpy()
+    r0 = H.Runner(cfg, 0, model=_stage(H, cfg, w0))
+    r0.forward()
+    got0 = r0.output_numpy()
+    ref = _oracle(cfg, w, r.inp)
+    for k in ref:
+        assert np.abs(got[k] - got0[k]).max() > 1e-3
+        if cfg.stream == "f32":
+            assert_f32_close(got[k], ref[k], what=f"{name} {k} with biases")
+        else:
+            ctl = _oracle(cfg, w, r.inp, accum="fp32")
+            assert_bf16_parity(got[k], ref[k], ctl[k], f"{name} {k} with biases")
+
+
+@pytest.mark.parametrize("name", ["c3_small", "ragged", "ragged_biases"])
 def test_bf16_block_equals_separate_kernels_bits(H, name):
     """The bf16 block applies the SiLU gate inside the MLP-in GEMM's epilogue
     (its weight staged in [32 gate | 32 up] row groups); it equals the same
@@ -455,6 +491,8 @@ def test_bf16_block_equals_separate_kernels_bits(H, name):
         C3_SMALL, hidden=256, n_heads=2, ffn=704,
         segments=(Segment(0, (1, 5, 7), 0), Segment(1, (45,), 1), Segment(0, (2, 3, 9), 0)))
     w = S.all_weights(cfg, 0, threads=8)
+    if name == "ragged_biases":
+        w = _with_biases(w)
     m = _stage(H, cfg, w)
     r = H.Runner(cfg, 0, model=m)
     dit = H.dit
