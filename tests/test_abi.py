@@ -129,6 +129,8 @@ def test_layout_rejects_malformed_segments(dit):
     assert e.value.status == "DIT_E_INVALID"
     with pytest.raises(dit.DitError):
         dit.dit_pack_layout(cfg, [Segment(3, (4, 4, 4), 0)])  # no modality 3
+    with pytest.raises(dit.DitError, match="cond_row"):
+        dit.dit_pack_layout(cfg, [Segment(0, (4, 4, 4), -1)])  # modulation row out of range
 
 
 def test_forward_requires_finalized_model(dit):
