@@ -562,3 +562,28 @@ def test_cfg_loop_graph_replay_matches_eager(H):
         H.dit.dit_cfg_denoise_loop(r.model, r.batch, again, cond_tab, dt_tab, 3.5, n, r.ws)
         torch.cuda.synchronize()
         assert torch.equal(again, eager)
+
+
+@pytest.mark.parametrize("name", ["c2_2blocks", "c4_small"])
+def test_adaln_table_correctly_rounded(H, name):
+    """dit_modulation against the oracle's table on the same float32
+    conditioning rows: fp64 dot products rounded once, so at most one ulp
+    apart (sums in another order) and almost every value identical; with
+    random biases so the bias term is live."""
+    cfg = scaled(S.get_config("c2"), n_blocks=2) if name == "c2_2blocks" else C4_SMALL
+    w = _with_biases(S.all_weights(cfg, 0, threads=8))
+    m = _stage(H, cfg, w)
+    r = H.Runner(cfg, 0, model=m)
+    L, D = cfg.n_blocks, cfg.hidden
+    mod = torch.empty(L, r.batch.n_cond, 6, D, device="cuda")
+    H.dit.dit_modulation(m, r.batch, 0, L, r.cond, mod)
+    got = mod.cpu().numpy()
+    emb = r.cond.cpu().numpy().astype(np.float64)
+    same = total = 0
+    for b in range(L):
+        ref = O.adaln_table(cfg, w, b, emb, "fp64").astype(np.float32)
+        ulp = np.spacing(np.abs(ref)).astype(np.float64)
+        assert (np.abs(got[b].astype(np.float64) - ref) <= ulp).all(), f"block {b}: beyond one ulp"
+        same += int((got[b] == ref).sum())
+        total += ref.size
+    assert same >= 0.999 * total, f"{total - same} of {total} values differ by one ulp"

@@ -437,9 +437,8 @@ hipError_t narrow_f64(int64_t n, const double* src, float* dst, hipStream_t s) {
 }
 
 // ============================================================================ AdaLN table
-// mod[c][j] = W[m(c)][j, :] . e[c, :] + bias[m(c)][j], one wavefront per output
-// column j; sums in fp64 so the table is the correctly rounded fp32 of the dot
-// product in practice.  One launch per block writes that block's rows.
+// mod[c][j] = W[m(c)][j, :] . e[c, :] + bias[m(c)][j]; sums in fp64 so the
+// table is the correctly rounded fp32 of the dot product in practice.
 struct CondMap {
   int n_cond;
   int modality[64];
@@ -459,45 +458,58 @@ template <> struct wload4<bf16_t> {
 };
 
 // blockIdx.z: the block (weights at p + z * stride bytes, output rows at
-// mod + z * n_cond * six_d).  Each wavefront computes ADA_JW consecutive
-// outputs; each lane reads four consecutive weights of each of their rows.
-constexpr int ADA_JW = 4;
+// mod + z * n_cond * six_d).  Eight lanes per output row, eight rows per
+// wavefront, 32 per workgroup: lane k of a row reads four consecutive weights
+// at k, k + 8, ... (in float4 steps), so the eight lanes of a row read 128
+// contiguous bytes per step, and the row's sum closes in three shuffle steps.
+constexpr int ADA_LPR = 8, ADA_ROWS = 256 / ADA_LPR, ADA_U = 8;
 template <typename TW>
 __global__ __launch_bounds__(256) void adaln_kernel(int six_d, int cond_dim, AdalnBlockPtrs p, int64_t w_stride,
                                                    int64_t b_stride, CondMap cm, const float* __restrict__ e,
                                                    float* __restrict__ mod) {
-  const int lane = threadIdx.x & 63;
-  const int j0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * ADA_JW;
+  const int kp = threadIdx.x % ADA_LPR;
+  const int j_raw = blockIdx.x * ADA_ROWS + threadIdx.x / ADA_LPR;
   const int m = blockIdx.y;
-  if (j0 >= six_d || p.w[m] == nullptr) return;
+  if (p.w[m] == nullptr) return;
+  const bool live = j_raw < six_d;
+  const int j = live ? j_raw : six_d - 1;  // dead rows still take part in the shuffles
   const TW* w = reinterpret_cast<const TW*>(static_cast<const char*>(p.w[m]) + blockIdx.z * w_stride) +
-                static_cast<size_t>(j0) * cond_dim;
+                static_cast<size_t>(j) * cond_dim;
   const float* bias = reinterpret_cast<const float*>(reinterpret_cast<const char*>(p.bias[m]) + blockIdx.z * b_stride);
   float* out = mod + static_cast<size_t>(blockIdx.z) * cm.n_cond * six_d;
-  const int nj = six_d - j0 < ADA_JW ? six_d - j0 : ADA_JW;
+  auto dot4 = [](float4 wv, float4 ev) {
+    return static_cast<double>(wv.x) * static_cast<double>(ev.x) + static_cast<double>(wv.y) * static_cast<double>(ev.y) +
+           static_cast<double>(wv.z) * static_cast<double>(ev.z) + static_cast<double>(wv.w) * static_cast<double>(ev.w);
+  };
+  // Up to ADA_U float4 per lane (cond_dim <= 4 * 8 * ADA_U): the row's weights
+  // are loaded once, all in flight together, and reused for every
+  // conditioning row; longer rows stream per conditioning row.
+  const bool in_regs = cond_dim <= 4 * ADA_LPR * ADA_U;
+  float4 wr[ADA_U];
+  if (in_regs) {
+#pragma unroll
+    for (int u = 0; u < ADA_U; ++u) {
+      const int kk = 4 * kp + 4 * ADA_LPR * u;
+      wr[u] = kk < cond_dim ? wload4<TW>::ld(w + kk) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
   for (int c = 0; c < cm.n_cond; ++c) {
     if (cm.modality[c] != m) continue;
     const float* ec = e + static_cast<size_t>(c) * cond_dim;
-    double acc[ADA_JW] = {0.0, 0.0, 0.0, 0.0};
-    for (int kk = 4 * lane; kk < cond_dim; kk += 256) {
-      const float4 ev = *reinterpret_cast<const float4*>(ec + kk);
+    double acc = 0.0;
+    if (in_regs) {
 #pragma unroll
-      for (int r = 0; r < ADA_JW; ++r) {
-        if (r < nj) {
-          const float4 wv = wload4<TW>::ld(w + static_cast<size_t>(r) * cond_dim + kk);
-          acc[r] += static_cast<double>(wv.x) * static_cast<double>(ev.x) +
-                    static_cast<double>(wv.y) * static_cast<double>(ev.y) +
-                    static_cast<double>(wv.z) * static_cast<double>(ev.z) +
-                    static_cast<double>(wv.w) * static_cast<double>(ev.w);
-        }
+      for (int u = 0; u < ADA_U; ++u) {
+        const int kk = 4 * kp + 4 * ADA_LPR * u;
+        if (kk < cond_dim) acc += dot4(wr[u], *reinterpret_cast<const float4*>(ec + kk));
       }
+    } else {
+      for (int kk = 4 * kp; kk < cond_dim; kk += 4 * ADA_LPR)
+        acc += dot4(wload4<TW>::ld(w + kk), *reinterpret_cast<const float4*>(ec + kk));
     }
 #pragma unroll
-    for (int r = 0; r < ADA_JW; ++r) {
-      const double t = wave_sum_f64(acc[r]);
-      if (lane == 0 && r < nj)
-        out[static_cast<size_t>(c) * six_d + j0 + r] = static_cast<float>(t + static_cast<double>(bias[j0 + r]));
-    }
+    for (int o = ADA_LPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if (kp == 0 && live) out[static_cast<size_t>(c) * six_d + j] = static_cast<float>(acc + static_cast<double>(bias[j]));
   }
 }
 
@@ -532,7 +544,7 @@ hipError_t adaln(bool w_bf16, int n_blocks, const AdalnBlockPtrs* blocks_host, i
   }
   const int launches = uniform ? 1 : n_blocks;
   for (int b = 0; b < launches; ++b) {
-    dim3 grid((six_d + 4 * ADA_JW - 1) / (4 * ADA_JW), n_mod, uniform ? n_blocks : 1), block(256);
+    dim3 grid((six_d + ADA_ROWS - 1) / ADA_ROWS, n_mod, uniform ? n_blocks : 1), block(256);
     LaunchScope scope_(kCntAdaln, s);
     float* out = mod + static_cast<size_t>(b) * n_cond * six_d;
     if (w_bf16)
