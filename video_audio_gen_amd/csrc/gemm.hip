@@ -86,11 +86,21 @@ __global__ __launch_bounds__(gb::NT) void gemm_bf16_kernel(int M, int N, int K,
   uint4* As = smem;
   uint4* Bs = smem + STAGES * BM * CPR;
 
-  // Walk M fastest inside a column of tiles so consecutive workgroups share
-  // the weight tile.
   const int bid = blockIdx.x;
-  const int tm = bid % tiles_m;
-  const int tn = bid / tiles_m;
+  // Tile order: bands of 4 tile rows, walked column by column with the rows
+  // fastest, so a band's four A tiles are reused across every column of B.
+  // Workgroups go to the 8 XCDs round-robin; in each run of 256 (one per
+  // CU), XCD x takes 32 consecutive tiles of that order (eight columns of one
+  // band), so the CUs sharing an L2 share their A and B tiles.  The grid is
+  // padded to whole runs; the padding exits here.
+  const int t = (bid / 256) * 256 + (bid % 8) * 32 + (bid / 8) % 32;
+  if (t >= tiles_m * tiles_n) return;
+  constexpr int G = 4;
+  const int band = t / (G * tiles_n);
+  const int gr = tiles_m - band * G < G ? tiles_m - band * G : G;  // rows in this band
+  const int rr = t - band * G * tiles_n;
+  const int tm = band * G + rr % gr;
+  const int tn = rr / gr;
   const int m0 = tm * BM, n0 = tn * BN;
 
   const int tid = threadIdx.x;
@@ -266,7 +276,8 @@ hipError_t gemm_bf16(int M, int N, int K, const uint16_t* A, const uint16_t* B, 
   if (ep.mode == kEpiSiluGate && N % 64 != 0) return hipErrorInvalidValue;
   LaunchScope scope_(kCntGemmBf16, s);
   const int tiles_m = (M + gb::BM - 1) / gb::BM, tiles_n = (N + gb::BN - 1) / gb::BN;
-  hipLaunchKernelGGL(gemm_bf16_kernel, dim3(tiles_m * tiles_n), dim3(gb::NT), 0, s, M, N, K, A, B,
+  const int nblk = (tiles_m * tiles_n + 255) / 256 * 256;  // whole runs of 8 XCDs x 32 CUs
+  hipLaunchKernelGGL(gemm_bf16_kernel, dim3(nblk), dim3(gb::NT), 0, s, M, N, K, A, B,
                      bias, C, ep, tiles_m, tiles_n);
   return hipGetLastError();
 }
