@@ -80,27 +80,35 @@ __global__ __launch_bounds__(gb::NT) void gemm_bf16_kernel(int M, int N, int K,
                                                               const bf16_t* __restrict__ B,
                                                               const float* __restrict__ bias,
                                                               void* __restrict__ Cv, GemmEpilogue ep,
-                                                              int tiles_m, int tiles_n) {
+                                                              int tiles_m, int tiles_n, int banded) {
   using namespace gb;
   __shared__ uint4 smem[STAGES * (BM + BN) * CPR];  // STAGES x (A + B): 128 KB at 2 x 64 or 4 x 32
   uint4* As = smem;
   uint4* Bs = smem + STAGES * BM * CPR;
 
   const int bid = blockIdx.x;
-  // Tile order: bands of 4 tile rows, walked column by column with the rows
-  // fastest, so a band's four A tiles are reused across every column of B.
-  // Workgroups go to the 8 XCDs round-robin; in each run of 256 (one per
-  // CU), XCD x takes 32 consecutive tiles of that order (eight columns of one
-  // band), so the CUs sharing an L2 share their A and B tiles.  The grid is
-  // padded to whole runs; the padding exits here.
-  const int t = (bid / 256) * 256 + (bid % 8) * 32 + (bid / 8) % 32;
-  if (t >= tiles_m * tiles_n) return;
-  constexpr int G = 4;
-  const int band = t / (G * tiles_n);
-  const int gr = tiles_m - band * G < G ? tiles_m - band * G : G;  // rows in this band
-  const int rr = t - band * G * tiles_n;
-  const int tm = band * G + rr % gr;
-  const int tn = rr / gr;
+  int tm, tn;
+  if (banded) {
+    // Bands of 4 tile rows, walked column by column with the rows fastest, so
+    // a band's four A tiles are reused across every column of B.  Workgroups
+    // go to the 8 XCDs round-robin; in each run of 128, XCD x takes 16
+    // consecutive tiles of that order (four columns of one band), so the CUs
+    // sharing an L2 share their A and B tiles.  The grid is padded to whole
+    // runs; the padding exits here.
+    constexpr int XG = 16, G = 4;
+    const int t = (bid / (8 * XG)) * (8 * XG) + (bid % 8) * XG + (bid / 8) % XG;
+    if (t >= tiles_m * tiles_n) return;
+    const int band = t / (G * tiles_n);
+    const int gr = tiles_m - band * G < G ? tiles_m - band * G : G;  // rows in this band
+    const int rr = t - band * G * tiles_n;
+    tm = band * G + rr % gr;
+    tn = rr / gr;
+  } else {
+    // Column-major: M fastest inside a column of tiles, so consecutive
+    // workgroups share the weight tile while A streams from the last-level cache.
+    tm = bid % tiles_m;
+    tn = bid / tiles_m;
+  }
   const int m0 = tm * BM, n0 = tn * BN;
 
   const int tid = threadIdx.x;
@@ -276,9 +284,16 @@ hipError_t gemm_bf16(int M, int N, int K, const uint16_t* A, const uint16_t* B, 
   if (ep.mode == kEpiSiluGate && N % 64 != 0) return hipErrorInvalidValue;
   LaunchScope scope_(kCntGemmBf16, s);
   const int tiles_m = (M + gb::BM - 1) / gb::BM, tiles_n = (N + gb::BN - 1) / gb::BN;
-  const int nblk = (tiles_m * tiles_n + 255) / 256 * 256;  // whole runs of 8 XCDs x 32 CUs
+  // Tile order from the shapes (measured on the 6144-wide block's GEMMs at
+  // 18,432 and 26,624 rows): banded when B has few column tiles, or when A
+  // outgrows the 256 MB last-level cache (column-major order then re-streams
+  // it from HBM for every few columns) and B is not too wide; column-major
+  // otherwise.
+  const double a_bytes = 2.0 * M * K;
+  const int banded = tiles_n <= 32 || (a_bytes > 256.0 * (1 << 20) && tiles_n <= 96);
+  const int nblk = banded ? (tiles_m * tiles_n + 127) / 128 * 128 : tiles_m * tiles_n;
   hipLaunchKernelGGL(gemm_bf16_kernel, dim3(nblk), dim3(gb::NT), 0, s, M, N, K, A, B,
-                     bias, C, ep, tiles_m, tiles_n);
+                     bias, C, ep, tiles_m, tiles_n, banded);
   return hipGetLastError();
 }
 
