@@ -29,7 +29,8 @@ def _bf16_vals(rng, shape, scale=1.0):
 
 # ----------------------------------------------------------------------------- GEMM
 
-@pytest.mark.parametrize("M,N,K", [(1, 64, 64), (300, 320, 128), (513, 768, 192), (26624 // 8, 18432 // 8, 6144)])
+@pytest.mark.parametrize("M,N,K", [(1, 64, 64), (300, 320, 128), (513, 768, 192), (26624 // 8, 18432 // 8, 6144),
+                                   (65, 97, 64)])
 def test_gemm_bf16(dit, M, N, K):
     rng = np.random.default_rng(M + N + K)
     A = _bf16_vals(rng, (M, K))
@@ -50,7 +51,8 @@ def test_gemm_bf16(dit, M, N, K):
 # (172, 20480, 2560): the music model's MLP-in projection; (60, 6144, 16384):
 # a long K with several splits.
 @pytest.mark.parametrize("M,N,K", [(1, 4, 4), (100, 70, 36), (172, 2560, 2560), (172, 2560, 10240), (160, 1024, 128),
-                                   (400, 300, 96), (70, 130, 20000), (172, 20480, 2560), (60, 6144, 16384)])
+                                   (400, 300, 96), (70, 130, 20000), (172, 20480, 2560), (60, 6144, 16384),
+                                   (37, 33, 64), (173, 97, 2560)])
 def test_gemm_f32_int8_slices(dit, M, N, K):
     rng = np.random.default_rng(M * 7 + N + K)
     A = rng.standard_normal((M, K)).astype(np.float32)

@@ -536,10 +536,47 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
 
   // Lane holds column wc + lr, rows wr + 8 (e/4) + 4 lg + e%4 of each level.
   const int gn = n0 + wc + lr;
-  if (gn >= N) return;
-  const int fe = Be[gn];
   // C null: fp64 partials for a consumer that sums them itself (any split count)
   const bool direct = s1 == 1 && s2 == 1 && C != nullptr;
+  if ((N & 1) == 0 && (reinterpret_cast<uintptr_t>(C) & 7) == 0) {
+    // Rows e and e+1 are adjacent: lanes 2c and 2c+1 swap one value, and each
+    // stores two adjacent columns of its row (16-byte partials, 8-byte C).
+    const bool odd = lr & 1;
+    const int gnc = gn < N ? gn : N - 1;
+    const int fe = Be[gnc];
+    const double bv = (direct && bias != nullptr) ? static_cast<double>(bias[gnc]) : 0.0;
+    const double bv_pair = __shfl_xor(bv, 1, 64);  // the partner column's bias
+    const int col = odd ? gn - 1 : gn;
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      const int gm = m0 + wr + 8 * (e >> 2) + 4 * lg + (e & 3);
+      double v[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = gm + h < M ? gm + h : M - 1;
+        // sum_d acc_d 2^-7(d+2): each term exact in fp64, five terms
+        double x = 0.0;
+#pragma unroll
+        for (int d = S - 1; d >= 0; --d) x += ldexp(static_cast<double>(acc[d][e + h]), -7 * (d + 2));
+        v[h] = ldexp(x, Ae[r] + fe);
+      }
+      const double recv = __shfl_xor(odd ? v[0] : v[1], 1, 64);
+      const int row = odd ? gm + 1 : gm;
+      if (row < M && col < N) {
+        const double lo = odd ? recv : v[0], hi = odd ? v[1] : recv;
+        if (direct) {
+          const double b_lo = odd ? bv_pair : bv, b_hi = odd ? bv : bv_pair;  // columns col, col + 1
+          *reinterpret_cast<float2*>(C + static_cast<size_t>(row) * N + col) =
+              make_float2(static_cast<float>(lo + b_lo), static_cast<float>(hi + b_hi));
+        } else {
+          *reinterpret_cast<double2*>(part + (static_cast<size_t>(sp) * M + row) * N + col) = make_double2(lo, hi);
+        }
+      }
+    }
+    return;
+  }
+  if (gn >= N) return;
+  const int fe = Be[gn];
   const double bv = (direct && bias != nullptr) ? static_cast<double>(bias[gn]) : 0.0;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
