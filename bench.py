@@ -109,11 +109,18 @@ def family_work(cfg, splits=None):
         "gemm_bf16": (blocks if cfg.stream == "bf16" else 0.0, "flop"),
         "gemm_f32": ((islands if cfg.stream == "bf16" else blocks + islands), "flop"),
         "attention": (attention_flops(cfg), "flop"),
-        # x read (f32) + h written, twice per block; plus the final fp32 norm with io
-        "modnorm": (L * 2 * N * D * (4 + es) + (N * D * 8 if cfg.io else 0), "byte"),
+        # x read (f32) + h written: the first block's attention norm (every
+        # later norm runs fused with the gated residual before it), plus the
+        # final fp32 norm with io
+        "modnorm": ((N * D * (4 + es) if L else 0) + (N * D * 8 if cfg.io else 0), "byte"),
+        # gated residual + the next norm: x and a read, x and h written; per
+        # block the MLP's norm, and every block but the last the next block's
+        # attention norm
+        "resid_modnorm": ((2 * L - 1) * N * D * (12 + es) if L else 0, "byte"),
         "rope_split": (L * N * (6 * D * es + cfg.rot_dim * 4), "byte"),
         "silu_gate": (L * N * 3 * F * es, "byte"),
-        "gated_residual": (L * 2 * N * D * 12, "byte"),
+        # the last block's closing gated residual (the others are fused)
+        "gated_residual": (N * D * 12 if L else 0, "byte"),
         "adaln": (L * cfg.n_mod * 6 * D * cfg.cond_dim * w_es, "byte"),
     }
     if cfg.stream == "f32" and splits is not None:

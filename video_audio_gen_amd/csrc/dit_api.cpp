@@ -658,9 +658,12 @@ static int check_run(const dit_model* m, const dit_batch* b, void* ws, size_t ws
   return DIT_OK;
 }
 
-// bf16 stream: x is the float32 residual.
-static int run_block_bf16(dit_model* m, int blk, float* x, const float* mod, const dit_batch* b, char* ws,
-                          const WsPlan& p, hipStream_t s) {
+// bf16 stream: x is the float32 residual.  h_ready: h already holds this
+// block's attention norm (the block before closed with it).  next_mod: the
+// next block's modulation rows; the MLP's gated residual then runs fused with
+// that block's attention norm, else alone.
+static int run_block_bf16(dit_model* m, int blk, float* x, const float* mod, const float* next_mod, bool h_ready,
+                          const dit_batch* b, char* ws, const WsPlan& p, hipStream_t s) {
   const dit_config& c = m->cfg;
   const BlockPtrs& w = m->blocks[blk];
   const int N = b->N, D = c.hidden, F = c.ffn, H = c.n_heads, hd = c.head_dim;
@@ -682,17 +685,19 @@ static int run_block_bf16(dit_model* m, int blk, float* x, const float* mod, con
   const GemmEpilogue to_f32{kEpiF32};
   const GemmEpilogue silu{kEpiSiluGate};
   // attention sub-layer
-  DIT_HIP(modnorm(true, c.norm, c.norm_eps, N, D, false, x, mod, 0, b->cond_dev, h, s));
+  if (!h_ready) DIT_HIP(modnorm(true, c.norm, c.norm_eps, N, D, false, x, mod, 0, b->cond_dev, h, s));
   DIT_HIP(gemm(3 * D, D, h, w.qkv_w, w.qkv_b, big, to_bf16));
   DIT_HIP(rope_split(true, N, H, hd, c.rot_dim, big, b->cos_dev, b->sin_dev, q, k, v, s));
   DIT_HIP(attention_bf16(N, H, hd, b->n_segs, b->cu_dev, b->max_seqlen, q, k, v, o, s));
   DIT_HIP(gemm(D, D, o, w.out_w, w.out_b, a, to_f32));
-  DIT_HIP(gated_residual(N, D, false, x, a, mod, 0, b->cond_dev, s));
-  // MLP sub-layer
-  DIT_HIP(modnorm(true, c.norm, c.norm_eps, N, D, false, x, mod, 1, b->cond_dev, h, s));
+  // MLP sub-layer: the attention's gated residual and the MLP norm in one pass
+  DIT_HIP(resid_modnorm(c.norm, c.norm_eps, N, D, x, a, mod, 0, mod, 1, b->cond_dev, h, s));
   DIT_HIP(gemm(2 * F, D, h, w.in_w, w.in_b, qkvh, silu));
   DIT_HIP(gemm(D, F, qkvh, w.mo_w, w.mo_b, a, to_f32));
-  DIT_HIP(gated_residual(N, D, false, x, a, mod, 1, b->cond_dev, s));
+  if (next_mod != nullptr)
+    DIT_HIP(resid_modnorm(c.norm, c.norm_eps, N, D, x, a, mod, 1, next_mod, 0, b->cond_dev, h, s));
+  else
+    DIT_HIP(gated_residual(N, D, false, x, a, mod, 1, b->cond_dev, s));
   return DIT_OK;
 }
 
@@ -770,7 +775,7 @@ extern "C" int dit_block_forward(dit_model* m, int block, float* x_dev, const fl
   if (x_dev == nullptr || mod_dev == nullptr) return set_error(DIT_E_INVALID, "dit_block_forward: x or mod is null");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(ws_dev);
-  if (m->cfg.stream_dtype == DIT_BF16) return run_block_bf16(m, block, x_dev, mod_dev, b, ws, p, s);
+  if (m->cfg.stream_dtype == DIT_BF16) return run_block_bf16(m, block, x_dev, mod_dev, nullptr, false, b, ws, p, s);
   const int64_t n = static_cast<int64_t>(b->N) * m->cfg.hidden;
   double* x64 = reinterpret_cast<double*>(ws + p.x);
   DIT_HIP(widen_f32(n, x_dev, x64, s));
@@ -824,7 +829,8 @@ static int run_forward(dit_model* m, const dit_batch* b, const float* in, const 
                             blk + 1 == L && c.io ? y : nullptr, b, ws, p, s));
   } else {
     for (int blk = 0; blk < L; ++blk)
-      DIT_TRY(run_block_bf16(m, blk, static_cast<float*>(x), mod + blk * mod_stride, b, ws, p, s));
+      DIT_TRY(run_block_bf16(m, blk, static_cast<float*>(x), mod + blk * mod_stride,
+                             blk + 1 < L ? mod + (blk + 1) * mod_stride : nullptr, blk > 0, b, ws, p, s));
   }
   if (!c.io) {
     if (x64) DIT_HIP(narrow_f64(nd, static_cast<const double*>(x), out, s));

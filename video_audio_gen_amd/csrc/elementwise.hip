@@ -76,12 +76,17 @@ template <> struct load4<double> {
 // modulation row (a packed segment is contiguous), so they come from L2 once
 // per workgroup instead of once per row.  Every row's arithmetic is the same
 // as with ROWS = 1.
-template <typename TX, typename TO, int TPR, int NCH, int ROWS, int PF = 1>
+//
+// RES (bf16 stream): the gated residual of the sub-layer before runs first,
+// x = fma(gate[c], a, x) per element -- the value the separate gated-residual
+// kernel stores -- x is written back and the row normalised from it.
+template <typename TX, typename TO, int TPR, int NCH, int ROWS, int PF = 1, bool RES = false>
 __global__ __launch_bounds__(TPR > 256 ? TPR : 256) void modnorm_kernel(int N, int D, int norm, float eps,
                                                      const TX* __restrict__ x,
                                                      const float* __restrict__ mod, int shift_k,
                                                      int scale_k, const int32_t* __restrict__ cond_idx,
-                                                     TO* __restrict__ h) {
+                                                     TO* __restrict__ h, float* xw, const float* __restrict__ a,
+                                                     const float* __restrict__ gmod, int gate_k) {
   typedef typename norm_acc<TO>::T A;
   constexpr int WPR = TPR / 64, RPB = (TPR > 256 ? TPR : 256) / TPR;
   __shared__ A red[2][RPB * WPR];
@@ -94,19 +99,48 @@ __global__ __launch_bounds__(TPR > 256 ? TPR : 256) void modnorm_kernel(int N, i
   A v[PF + 1][NCH][4];
   float4 shv[NCH], scv[NCH];
   int cur_cond = -1;
-  auto row_of = [&](int it) {
-    const int r = (blockIdx.x * ROWS + it) * RPB + wrow;
-    return r < N ? r : N - 1;                      // dead rows keep every barrier reachable
-  };
-  auto load_row = [&](int r, A (*dst)[4]) {
-    const TX* xr = x + static_cast<size_t>(r) * D;
+  auto row_of = [&](int it) { return (blockIdx.x * ROWS + it) * RPB + wrow; };
+  // A dead row (past N) reads row N-1 so every barrier stays reachable, and
+  // stores nothing.
+  auto load_row = [&](int r_raw, A (*dst)[4]) {
+    const bool row_live = r_raw < N;
+    const int r = row_live ? r_raw : N - 1;
+    if constexpr (RES) {
+      float* xr = xw + static_cast<size_t>(r) * D;
+      const float* ar = a + static_cast<size_t>(r) * D;
+      const float* gr = gmod + (static_cast<size_t>(cond_idx[r]) * 6 + gate_k) * D;
+      float4 xv[NCH], av[NCH], gv[NCH];
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = t + TPR * i;
-      if (c < D4) {
-        load4<TX>::ld(xr + 4 * c, dst[i]);
-      } else {
-        dst[i][0] = dst[i][1] = dst[i][2] = dst[i][3] = A(0);
+      for (int i = 0; i < NCH; ++i) {
+        const int c = t + TPR * i;
+        if (c < D4) {
+          xv[i] = reinterpret_cast<const float4*>(xr)[c];
+          av[i] = reinterpret_cast<const float4*>(ar)[c];
+          gv[i] = reinterpret_cast<const float4*>(gr)[c];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int c = t + TPR * i;
+        if (c < D4) {
+          const float4 y = make_float4(__builtin_fmaf(gv[i].x, av[i].x, xv[i].x), __builtin_fmaf(gv[i].y, av[i].y, xv[i].y),
+                                       __builtin_fmaf(gv[i].z, av[i].z, xv[i].z), __builtin_fmaf(gv[i].w, av[i].w, xv[i].w));
+          if (row_live) reinterpret_cast<float4*>(xr)[c] = y;
+          dst[i][0] = A(y.x); dst[i][1] = A(y.y); dst[i][2] = A(y.z); dst[i][3] = A(y.w);
+        } else {
+          dst[i][0] = dst[i][1] = dst[i][2] = dst[i][3] = A(0);
+        }
+      }
+    } else {
+      const TX* xr = x + static_cast<size_t>(r) * D;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int c = t + TPR * i;
+        if (c < D4) {
+          load4<TX>::ld(xr + 4 * c, dst[i]);
+        } else {
+          dst[i][0] = dst[i][1] = dst[i][2] = dst[i][3] = A(0);
+        }
       }
     }
   };
@@ -177,9 +211,10 @@ __global__ __launch_bounds__(TPR > 256 ? TPR : 256) void modnorm_kernel(int N, i
 
 bool modnorm_supported(int D) { return D > 0 && D % 4 == 0 && D <= 8192; }
 
-template <typename TX, typename TO>
+template <typename TX, typename TO, bool RES = false>
 static hipError_t modnorm_t(int norm, float eps, int N, int D, const TX* x, const float* mod,
-                            int which, const int32_t* ci, TO* h, hipStream_t s) {
+                            int which, const int32_t* ci, TO* h, hipStream_t s, float* xw = nullptr,
+                            const float* a = nullptr, const float* gmod = nullptr, int gate_k = 0) {
   const int d4 = D / 4;
   const int shift_k = which == 0 ? 0 : 3, scale_k = which == 0 ? 1 : 4;
   // two rows per workgroup once there are enough rows to fill the chip
@@ -189,11 +224,11 @@ static hipError_t modnorm_t(int norm, float eps, int N, int D, const TX* x, cons
     constexpr int NTH = TPR > 256 ? TPR : 256, RPB = NTH / TPR;                                       \
     if (N >= 4096 * RPB) {                                                                            \
       const int nb = (N + RPB * R - 1) / (RPB * R);                                                   \
-      hipLaunchKernelGGL((modnorm_kernel<TX, TO, TPR, K, R>), dim3(nb), dim3(NTH), 0, s, N, D, norm, eps, \
-                         x, mod, shift_k, scale_k, ci, h);                                            \
+      hipLaunchKernelGGL((modnorm_kernel<TX, TO, TPR, K, R, 1, RES>), dim3(nb), dim3(NTH), 0, s, N, D, norm, \
+                         eps, x, mod, shift_k, scale_k, ci, h, xw, a, gmod, gate_k);                        \
     } else {                                                                                          \
-      hipLaunchKernelGGL((modnorm_kernel<TX, TO, TPR, K, 1>), dim3((N + RPB - 1) / RPB), dim3(NTH), 0, s, \
-                         N, D, norm, eps, x, mod, shift_k, scale_k, ci, h);                           \
+      hipLaunchKernelGGL((modnorm_kernel<TX, TO, TPR, K, 1, 1, RES>), dim3((N + RPB - 1) / RPB), dim3(NTH), 0, \
+                         s, N, D, norm, eps, x, mod, shift_k, scale_k, ci, h, xw, a, gmod, gate_k);         \
     }                                                                                                 \
     return hipGetLastError();                                                                         \
   }
@@ -226,6 +261,18 @@ hipError_t modnorm(bool bf16_out, int norm, float eps, int N, int D, bool x_f64,
                                     static_cast<bf16_t*>(h), s);
   return modnorm_t<float, float>(norm, eps, N, D, static_cast<const float*>(x), mod, which, cond_idx,
                                  static_cast<float*>(h), s);
+}
+
+// Gated residual of the sub-layer before (gmod's gate_which row: 0 gate_msa,
+// 1 gate_mlp) then modulate + norm of the next one (nmod's norm_which rows),
+// one pass over x.
+hipError_t resid_modnorm(int norm, float eps, int N, int D, float* x, const float* a, const float* gmod,
+                         int gate_which, const float* nmod, int norm_which, const int32_t* cond_idx, bf16_t* h,
+                         hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  LaunchScope scope_(kCntResidModnorm, s);
+  return modnorm_t<float, bf16_t, true>(norm, eps, N, D, x, nmod, norm_which, cond_idx, h, s, x, a, gmod,
+                                        gate_which == 0 ? 2 : 5);
 }
 
 // ============================================================================ RoPE + QKV split
@@ -390,10 +437,12 @@ __global__ __launch_bounds__(256) void gated_residual_kernel(int N, int D, TX* _
       mod + (static_cast<size_t>(cond_idx[n]) * 6 + gate_k) * D)[c];
   const float4 av = reinterpret_cast<const float4*>(a)[t];
   TX* xp = x + 4 * t;
-  xp[0] += TX(g.x) * TX(av.x);
-  xp[1] += TX(g.y) * TX(av.y);
-  xp[2] += TX(g.z) * TX(av.z);
-  xp[3] += TX(g.w) * TX(av.w);
+  // one rounding per element: fma (for a float64 x the product of two floats
+  // is exact, so this is x + g a rounded once either way)
+  xp[0] = fma(TX(g.x), TX(av.x), xp[0]);
+  xp[1] = fma(TX(g.y), TX(av.y), xp[1]);
+  xp[2] = fma(TX(g.z), TX(av.z), xp[2]);
+  xp[3] = fma(TX(g.w), TX(av.w), xp[3]);
 }
 
 hipError_t gated_residual(int N, int D, bool x_f64, void* x, const float* a, const float* mod, int which,

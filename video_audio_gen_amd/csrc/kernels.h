@@ -11,7 +11,7 @@ namespace dit {
 enum Counter {
   kCntGemmBf16 = 0, kCntGemmF32, kCntAttnBf16, kCntAttnF32, kCntModnorm, kCntRopeSplit,
   kCntSiluGate, kCntGatedResidual, kCntAdaln, kCntPatchIn, kCntPatchOut, kCntEuler,
-  kCntGemmF32Reduce, kCntConvert, kCntResidNormSlice, kCntSiluSlice, kCntCfgEuler, kCntNum
+  kCntGemmF32Reduce, kCntConvert, kCntResidNormSlice, kCntSiluSlice, kCntCfgEuler, kCntResidModnorm, kCntNum
 };
 void count_launch(Counter c);
 
@@ -81,6 +81,12 @@ hipError_t rope_split(bool bf16, int N, int H, int hd, int rot, const void* qkv,
                       const float* sin, void* q, void* k, void* v, hipStream_t s);
 bool rope_split_supported(bool bf16, int hd, int rot);
 hipError_t silu_gate(bool bf16, int N, int F, const void* u, void* m, hipStream_t s);
+// bf16 stream: x = fma(gate[c], a, x) with gmod's gate (gate_which: 0 gate_msa,
+// 1 gate_mlp), as gated_residual stores it, then h = modnorm(x) with nmod's
+// shift/scale (norm_which), in one pass.
+hipError_t resid_modnorm(int norm, float eps, int N, int D, float* x, const float* a, const float* gmod,
+                         int gate_which, const float* nmod, int norm_which, const int32_t* cond_idx, uint16_t* h,
+                         hipStream_t s);
 hipError_t gated_residual(int N, int D, bool x_f64, void* x, const float* a, const float* mod, int which,
                           const int32_t* cond_idx, hipStream_t s);
 // ---- fused row kernels of the fp32 stream (fused_f32.hip); part: fp64 split-K

@@ -31,7 +31,8 @@ DIT_IO_NONE, DIT_IO_PATCH3D, DIT_IO_CHANNEL_MAJOR = 0, 1, 2
 MAX_MOD = 4
 COUNTER_NAMES = ["gemm_bf16", "gemm_f32", "attention_bf16", "attention_f32", "modnorm", "rope_split",
                  "silu_gate", "gated_residual", "adaln", "patch_in", "patch_out", "euler",
-                 "gemm_f32_reduce", "convert", "resid_norm_slice", "silu_slice", "cfg_euler"]
+                 "gemm_f32_reduce", "convert", "resid_norm_slice", "silu_slice", "cfg_euler",
+                 "resid_modnorm"]
 
 
 class DitError(RuntimeError):
