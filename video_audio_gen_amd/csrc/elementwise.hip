@@ -271,8 +271,9 @@ hipError_t resid_modnorm(int norm, float eps, int N, int D, float* x, const floa
                          hipStream_t s) {
   if (N == 0) return hipSuccess;
   LaunchScope scope_(kCntResidModnorm, s);
-  return modnorm_t<float, bf16_t, true>(norm, eps, N, D, x, nmod, norm_which, cond_idx, h, s, x, a, gmod,
-                                        gate_which == 0 ? 2 : 5);
+  // x is read and written through xw only (the read-only pointer stays null)
+  return modnorm_t<float, bf16_t, true>(norm, eps, N, D, static_cast<const float*>(nullptr), nmod, norm_which,
+                                        cond_idx, h, s, x, a, gmod, gate_which == 0 ? 2 : 5);
 }
 
 // ============================================================================ RoPE + QKV split
