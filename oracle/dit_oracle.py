@@ -41,9 +41,14 @@ Precision modes:
              the time embedding and the projections in and out stay fp32.
 
 Pins: tests/test_oracle_pins.py checks every function here against closed
-forms, invariants and brute force.  The whole random-weight forward is pinned
-only through its parts ("parity unpinned" beyond them): the pages' printed
-accuracy figures belong to a model and inputs that are not available.
+forms, invariants and brute force; tests/test_oracle_wiring_pins.py pins the
+wiring between them -- q and k roles and the RoPE target (scores through the
+relative position), the in/out projections and the final norm (closed form of
+an islands-only forward), every bf16 storage point (a block rounded by hand)
+and the timestep of each denoise step (hand fractions).  Each of those pins
+was run against an oracle carrying the mutation it names.  The random-weight
+forward as a whole has no printed value to meet: the pages' accuracy figures
+belong to a model and inputs that are not available.
 """
 
 from __future__ import annotations
