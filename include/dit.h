@@ -116,12 +116,24 @@ int dit_rope_cache_build(const dit_config* cfg, const dit_segment* segs, int n_s
                          float* cos_host, float* sin_host);
 
 /* Sinusoidal timestep embedding: out[i, j] = cos(t_i f_j), out[i, dim/2 + j] =
- * sin(t_i f_j), f_j = 10000^(-j/(dim/2)), fp64 math, float32 out [n, dim]. */
+ * sin(t_i f_j), f_j = 10000^(-j/(dim/2)), fp64 math, float32 out [n, dim].
+ * The time embedder is one of the fp32 islands of the bf16 stream (page "port
+ * the MiniMax-H3 omni-modal video+audio DiT", update "quantized arms land",
+ * item 1); the pages print no formula, so this is the standard DiT form,
+ * t in [0, 1] unscaled.  t_host [n] float32, out_host [n, dim] caller-owned;
+ * DIT_E_INVALID for n < 0, a dim that is not positive and even, or a null
+ * pointer. */
 int dit_timestep_embedding(const float* t_host, int n, int dim, float* out_host);
 
-/* Time-shifted rectified-flow sigmas: s_i = 1 - i/n_steps,
+/* Time-shifted rectified-flow sigmas (page "port the MiniMax-H3 omni-modal
+ * video+audio DiT", update "quantized arms land", item 2: the time-shift
+ * sigma schedule; milestone "the whole t2va path composes end to end": shift
+ * 12 for video, 3 for audio): s_i = 1 - i/n_steps,
  * sigma_i = shift s_i / (1 + (shift - 1) s_i), i = 0..n_steps (fp64), and
- * dt_i = float32(sigma_{i+1} - sigma_i), i < n_steps.  Either output may be NULL. */
+ * dt_i = float32(sigma_{i+1} - sigma_i), i < n_steps.  Either output may be
+ * NULL; sigma_host holds n_steps + 1 doubles, dt_host n_steps floats, both
+ * caller-owned.  DIT_E_INVALID for n_steps < 1 or a shift that is not
+ * positive and finite. */
 int dit_sigma_schedule(double shift, int n_steps, double* sigma_host, float* dt_host);
 
 /* ------------------------------------------------------------------ model and staging */
@@ -144,11 +156,21 @@ typedef struct dit_stage_stats_t {
   int64_t host_peak;    /* largest host conversion buffer held at once (one tensor) */
 } dit_stage_stats_t;
 
-/* Bytes of the weight slab for this config (256-byte aligned views). */
+/* Bytes of the weight slab for this config (256-byte aligned views), from
+ * the config alone, before any weight is read or any memory allocated (page
+ * "stream the ORIGINAL bf16 DiT to the device, one tensor at a time", section
+ * "What this enables": the manifest first, so the geometry is known before a
+ * byte is allocated).  Validates cfg: DIT_E_INVALID names the first field
+ * outside what the kernels handle. */
 int dit_weight_bytes(const dit_config* cfg, size_t* bytes);
 
-/* Validate cfg and bind a caller-owned device slab of at least dit_weight_bytes.
- * The handle is library-owned (free with dit_model_destroy); the slab is not. */
+/* Validate cfg and bind a caller-owned device slab of at least dit_weight_bytes
+ * that the weights are staged into once and read by every later forward (page
+ * "the 2.4B fp32 DiT onto the device, staged once", section "Speed": one
+ * staging outside the timed loop).  The handle is library-owned (free with
+ * dit_model_destroy); the slab is not, and must outlive the handle.  No
+ * device call is made.  DIT_E_INVALID for a bad cfg or a slab smaller than
+ * dit_weight_bytes. */
 int dit_model_create(const dit_config* cfg, void* weight_slab_dev, size_t slab_bytes,
                      dit_model** out);
 void dit_model_destroy(dit_model* m);
@@ -177,8 +199,16 @@ void dit_model_destroy(dit_model* m);
  * DIT_E_STATE after finalize, DIT_E_INVALID for a repeat. */
 int dit_stage_weights(dit_model* m, const dit_weight_view* views, int n, dit_stream_t stream);
 
-/* Close staging.  DIT_E_MISSING_WEIGHT names the first tensor never staged. */
+/* Close staging.  DIT_E_MISSING_WEIGHT names the first tensor never staged,
+ * instead of a forward reading an unwritten slot as zeros (page "port the
+ * MiniMax-H3 omni-modal video+audio DiT", update "GGUF arm complete": missing
+ * tensors fail by name).  Forward calls need a finalized model (DIT_E_STATE). */
 int dit_stage_finalize(dit_model* m);
+/* Counters of what staging did -- tensors, device bytes, tensors copied
+ * directly and converted on the host, the largest host conversion buffer --
+ * so the bound of one tensor of host memory is observable (page "stream the
+ * ORIGINAL bf16 DiT to the device, one tensor at a time", sections "What this
+ * enables" and "Gates I ran").  out caller-owned; DIT_E_INVALID on null. */
 int dit_stage_stats(const dit_model* m, dit_stage_stats_t* out);
 
 /* ------------------------------------------------------------------ batch */
@@ -186,31 +216,47 @@ int dit_stage_stats(const dit_model* m, dit_stage_stats_t* out);
 typedef struct dit_batch dit_batch;
 
 /* Device bytes of the batch tables (cu_seqlens, cond_idx, cos, sin, segment
- * table) for these segments. */
+ * table) for these segments: the packed layout of page "port the MiniMax-H3
+ * omni-modal video+audio DiT", section "Correctness gates" (cu_seqlens, doc
+ * ids), and the per-row rope cache of its section "The device-resident
+ * forward (W2b)".  DIT_E_INVALID as dit_pack_layout. */
 int dit_batch_bytes(const dit_model* m, const dit_segment* segs, int n_segs, size_t* bytes);
 
-/* Build the batch on the host (layout, rope cache) and copy it into the
- * caller's device buffer `tables_dev` (synchronous on `stream`).  n_cond rows of
- * modulation; cond_modality[c] selects the AdaLN linear of row c.  The handle
- * is library-owned; free with dit_batch_destroy.  The buffer must outlive it. */
+/* Build the batch on the host (layout, rope cache; page "stream the ORIGINAL
+ * bf16 DiT to the device", section "What this enables": cos/sin built on the
+ * host before any kernel) and copy it into the caller's device buffer
+ * `tables_dev` (synchronous on `stream`).  n_cond rows of modulation;
+ * cond_modality[c] selects the AdaLN linear of row c (page "port the
+ * MiniMax-H3 omni-modal video+audio DiT", section "The device-resident forward
+ * (W2b)": indexed AdaLN modulates).  The handle is library-owned; free with
+ * dit_batch_destroy.  The buffer must outlive it.  DIT_E_INVALID for a bad
+ * segment or modulation row, DIT_E_WORKSPACE for a short buffer,
+ * DIT_E_UNSUPPORTED when a GEMM of a forward over this batch would exceed the
+ * kernels' 32-bit buffer offsets (checked before any device call). */
 int dit_batch_create(const dit_model* m, const dit_segment* segs, int n_segs, int n_cond,
                      const int* cond_modality, void* tables_dev, size_t tables_bytes,
                      dit_stream_t stream, dit_batch** out);
 void dit_batch_destroy(dit_batch* b);
 /* N, number of segments, longest segment; latent floats of the whole batch
- * (sum over segments of C*T*pt*H*ph*W*pw or C*L; 0 without io). */
+ * (sum over segments of C*T*pt*H*ph*W*pw or C*L; 0 without io).  Any output
+ * pointer may be NULL. */
 int dit_batch_info(const dit_batch* b, int* n_tokens, int* n_segs, int* max_seqlen,
                    int64_t* latent_floats);
 /* Device pointers into the batch tables (for callers driving the op-level calls). */
 int dit_batch_tables(const dit_batch* b, const int32_t** cu_seqlens_dev,
                      const int32_t** cond_idx_dev, const float** cos_dev, const float** sin_dev);
 
-/* Workspace bytes that dit_block_forward / dit_forward / dit_denoise_step need. */
+/* Workspace bytes that dit_block_forward / dit_forward / dit_denoise_step need:
+ * every activation of the forward lives in this caller-owned device buffer,
+ * so nothing round-trips through the host (page "port the MiniMax-H3
+ * omni-modal video+audio DiT", section "The device-resident forward (W2b)"). */
 int dit_workspace_bytes(const dit_model* m, const dit_batch* b, size_t* bytes);
 
 /* ------------------------------------------------------------------ forward */
 
-/* AdaLN table of blocks [block0, block0 + n_blocks): mod[b][c][k][D] =
+/* AdaLN table (page "port the MiniMax-H3 omni-modal video+audio DiT",
+ * section "The device-resident forward (W2b)": two indexed AdaLN modulates, one
+ * linear per modality) of blocks [block0, block0 + n_blocks): mod[b][c][k][D] =
  * (W_ada[b][cond_modality[c]] . cond[c] + bias)[k*D + j], k = shift_msa,
  * scale_msa, gate_msa, shift_mlp, scale_mlp, gate_mlp.  cond_dev [n_cond,
  * cond_dim] float32 (an embedded timestep or a conditioning vector); mod_dev
@@ -218,7 +264,12 @@ int dit_workspace_bytes(const dit_model* m, const dit_batch* b, size_t* bytes);
 int dit_modulation(dit_model* m, const dit_batch* b, int block0, int n_blocks,
                    const float* cond_dev, float* mod_dev, dit_stream_t stream);
 
-/* One block on the packed residual stream x_dev [N, D] float32, in place.
+/* One block on the packed residual stream x_dev [N, D] float32, in place
+ * (page "port the MiniMax-H3 omni-modal video+audio DiT", section "The
+ * device-resident forward (W2b)"; page "the 2.4B fp32 DiT onto the device,
+ * staged once", section "What moved, and onto what").  DIT_E_STATE before
+ * finalize, DIT_E_WORKSPACE for a short workspace, DIT_E_INVALID for a block
+ * index out of range, DIT_E_HIP for a launch failure.
  * mod_dev [n_cond, 6, D] float32 (this block's rows of dit_modulation).  An
  * fp32 model carries its residual stream in float64 inside the library (here:
  * widened on entry, rounded to float32 once on exit); a bf16 model's is the
@@ -229,7 +280,12 @@ int dit_modulation(dit_model* m, const dit_batch* b, int block0, int n_blocks,
 int dit_block_forward(dit_model* m, int block, float* x_dev, const float* mod_dev,
                       const dit_batch* b, void* ws_dev, size_t ws_bytes, dit_stream_t stream);
 
-/* The whole forward.  With io: in_dev holds every segment's latent, segment
+/* The whole forward (page "port the MiniMax-H3 omni-modal video+audio DiT",
+ * section "The device-resident forward (W2b)" and update "quantized arms
+ * land": fp32 patch projections and output heads around the block stream;
+ * page "the 2.4B fp32 DiT onto the device, staged once", section "What moved":
+ * 1x1 convolutions as GEMMs on the frame-major activation), asynchronous on
+ * `stream`; errors as dit_block_forward.  With io: in_dev holds every segment's latent, segment
  * after segment ([C, T*pt, H*ph, W*pw] or [C, L], float32); out_dev receives
  * the velocities in the same layout.  Without io: in_dev is tokens [N, D]
  * float32 and out_dev the tokens after the last block.  cond_dev as in
@@ -245,8 +301,12 @@ int dit_forward(dit_model* m, const dit_batch* b, const float* in_dev, const flo
 int dit_denoise_step(dit_model* m, const dit_batch* b, float* latents_dev, const float* cond_dev,
                      const float* dt_dev, void* ws_dev, size_t ws_bytes, dit_stream_t stream);
 
-/* n_steps consecutive steps with no host round trip: step i reads
- * cond_table_dev + i*n_cond*cond_dim and dt_table_dev + i*n_mod. */
+/* n_steps consecutive steps with no host round trip (page "port the
+ * MiniMax-H3 omni-modal video+audio DiT", section "The device-resident forward
+ * (W2b)": the 50-step denoise loop above the block stack stays on the
+ * device): step i reads cond_table_dev + i*n_cond*cond_dim and
+ * dt_table_dev + i*n_mod (tables built once, e.g. from dit_sigma_schedule and
+ * dit_timestep_embedding).  Errors as dit_denoise_step. */
 int dit_denoise_loop(dit_model* m, const dit_batch* b, float* latents_dev,
                      const float* cond_table_dev, const float* dt_table_dev, int n_steps,
                      void* ws_dev, size_t ws_bytes, dit_stream_t stream);
@@ -270,7 +330,15 @@ int dit_cfg_denoise_loop(dit_model* m, const dit_batch* b, float* latents_dev,
 
 /* ------------------------------------------------------------------ op-level calls
  * The kernels the block is made of, exposed for per-op parity checks and
- * timing.  dtype arguments are DIT_F32 or DIT_BF16 (bf16 = uint16 bits). */
+ * timing: the shared ops the pages compose the block from (page "port the
+ * MiniMax-H3 omni-modal video+audio DiT", section "The device-resident forward
+ * (W2b)": MatmulBT, RmsNorm, QkvSplit, RopeFromCache, SiluAndMul, Add,
+ * DFlashBlockAttention; page "the 2.4B fp32 DiT onto the device", section
+ * "What moved": LayerNorm, partial rotary).  dtype arguments are DIT_F32 or
+ * DIT_BF16 (bf16 = uint16 bits).  Every pointer is a device pointer the caller
+ * owns; calls are asynchronous on `stream`; DIT_E_INVALID for a bad argument,
+ * DIT_E_UNSUPPORTED for a shape the kernel does not handle, DIT_E_WORKSPACE
+ * for a short workspace. */
 
 /* C[M,N] = A[M,K] . B[N,K]^T + bias[N] (bias may be NULL).  bf16: A, B bf16,
  * fp32 accumulation, C in c_dtype.  f32: A, B float32 (K a multiple of 4),
@@ -318,8 +386,14 @@ int dit_silu_gate(int dtype, int N, int F, const void* u, void* m, dit_stream_t 
 int dit_gated_residual(int N, int D, void* x, int x_dtype, const float* a, const float* mod, int which,
                        const int32_t* cond_idx, dit_stream_t stream);
 
-/* ------------------------------------------------------------------ diagnostics */
+/* ------------------------------------------------------------------ diagnostics
+ * A failure fails the call, never the process (page "port the MiniMax-H3
+ * omni-modal video+audio DiT", section "Serving": a failing runner fails the
+ * job, not the process); counters make a launch path observable (page "stream
+ * the ORIGINAL bf16 DiT to the device", section "What this enables"). */
 
+/* The calling thread's message of its last failed call (library-owned, valid
+ * until that thread's next call). */
 const char* dit_last_error(void);
 /* Launch counters per kernel family (index order: gemm_bf16, gemm_f32, attention_bf16,
  * attention_f32, modnorm, rope_split, silu_gate, gated_residual, adaln, patch_in,
@@ -327,7 +401,9 @@ const char* dit_last_error(void);
 int dit_counters(int64_t* out, int n_max);
 void dit_counters_reset(void);
 
-/* Per-kernel timing.  Between dit_profile_begin and dit_profile_end every
+/* Per-kernel timing, for the device-side timing protocol of page "the 2.4B
+ * fp32 DiT onto the device, staged once", section "Speed" (only the forward
+ * loop timed).  Between dit_profile_begin and dit_profile_end every
  * launch records a HIP event pair around itself on its own stream (a few
  * microseconds of host time per launch).  dit_profile_end waits for those
  * events and writes, per kernel family (index order as dit_counters), the

@@ -152,3 +152,35 @@ def test_gemm_splits_query(dit):
     assert lib.dit_gemm_splits(dit.DIT_BF16, 2560, 10240, ctypes.byref(n)) == 1
     assert lib.dit_gemm_splits(dit.DIT_F32, 0, 10240, ctypes.byref(n)) == 1
     assert lib.dit_gemm_splits(dit.DIT_F32, 2560, 10240, None) == 1
+
+
+def test_nonfinite_fp32_gemm_weight_is_rejected_by_name(dit):
+    # an fp32 GEMM weight is cut into int8 slices on the host; a NaN or an Inf
+    # has no slicing and must fail the call (before any device copy), not
+    # stage as finite digits
+    cfg = S.get_config("c1")
+    lib = dit.load()
+    for bad in (np.nan, np.inf, -np.inf):
+        h, _ = _fake_model(dit, cfg)
+        w = np.zeros((384, 128), np.float32)
+        w[77, 5] = bad
+        assert _stage_one(dit, h, "blocks.0.attn.qkv.weight", w) == 1
+        msg = lib.dit_last_error()
+        assert b"blocks.0.attn.qkv.weight" in msg and b"row 77" in msg, msg
+        lib.dit_model_destroy(h)
+
+
+def test_batch_beyond_the_gemm_offsets_is_rejected_before_any_device_call(dit):
+    # the music model's fp32 GEMMs address 5 bytes of slices per element of an
+    # [N, 10240] operand in 32 bits: N = 50,000 tokens is beyond them
+    cfg = S.get_config("c2")
+    h, _ = _fake_model(dit, cfg)
+    lib = dit.load()
+    segs = dit.make_segments([Segment(0, (50000,), 0)])
+    cond_mod = (ctypes.c_int * 1)(0)
+    out = ctypes.c_void_p()
+    fake_tables = 1 << 41  # never dereferenced: the check comes before the copy
+    rc = lib.dit_batch_create(h, segs, 1, 1, cond_mod, fake_tables, 1 << 40, None, ctypes.byref(out))
+    assert rc == 9, lib.dit_last_error()
+    assert b"32-bit" in lib.dit_last_error()
+    lib.dit_model_destroy(h)

@@ -117,6 +117,24 @@ def test_c4_io_bf16_parity(H):
         assert_bf16_parity(got[k], ref[k], ctl[k], f"c4 small (2 blocks) {k}")
 
 
+def test_nonfinite_input_stays_visible_and_inside_its_document(H):
+    """A NaN in one token of the fp32 tiny model's first document: every
+    output of that document is NaN (attention mixes the document's rows, and
+    the int8-sliced GEMMs carry a non-finite row as NaN rather than as finite
+    digits), while the second document's outputs equal the clean forward's
+    bit for bit (no term crosses a document boundary)."""
+    cfg = S.get_config("c1")
+    r, w, clean = _run(H, cfg)
+    x = r.x_in.clone()
+    x[5, 3] = float("nan")
+    out = torch.empty_like(x)
+    r.forward(x_in=x, out=out)
+    got = r.output_numpy(out)["x"]
+    n0 = cfg.segments[0].n_tokens
+    assert np.isnan(got[:n0]).all()
+    assert np.array_equal(got[n0:], clean["x"][n0:])
+
+
 def test_packed_equals_alone_bits(H):
     for cfg in (S.get_config("c1"), C3_SMALL):
         w = S.all_weights(cfg, 0, threads=8)

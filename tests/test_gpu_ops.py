@@ -75,6 +75,57 @@ def test_gemm_f32_int8_slices(dit, M, N, K):
     assert np.sqrt(np.mean(err ** 2)) <= 2.0 ** -24 * rms(ref)
 
 
+@pytest.mark.parametrize("outlier_log2", [10, 14])
+def test_gemm_f32_outlier_channels(dit, outlier_log2):
+    """Rows whose range is dominated by one channel 2^10 or 2^14 above the rest.
+    Each row is scaled by its max, so an element 2^k below the max keeps 35 - k
+    bits of its five 7-bit slices: the rigorous bound (dropped slice pairs and
+    remainders below K 2^-30 max|A_i| max|B_j|) still holds, but at k = 14 it
+    is ~2^-16 of the typical product, beyond a correct fp32 rounding of an
+    output whose terms are mostly the small elements.  The test checks the
+    rigorous bound and reports the error against a correct rounding."""
+    M, N, K = 172, 640, 2560
+    rng = np.random.default_rng(50 + outlier_log2)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    A[:, 7] *= np.float32(2.0 ** outlier_log2)
+    B = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    ref = O.linear(A, B, np.zeros(N))
+    C = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    dit.dit_gemm(torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda(), None, C)
+    g = from_dev(C)
+    err = np.abs(g - ref)
+    amax = np.abs(A).max(axis=1).astype(np.float64)
+    bmax = np.abs(B).max(axis=1).astype(np.float64)
+    bound = 2.0 ** -24 * np.abs(ref) * 1.0001 + K * 2.0 ** -30 * np.outer(amax, bmax)
+    assert np.all(err <= bound)
+    ulp_rms = np.sqrt(np.mean(err ** 2)) / (2.0 ** -24 * rms(ref))
+    print(f"outlier 2^{outlier_log2}: rms error {ulp_rms:.3f} half-ulps of the output rms, "
+          f"max err/bound {(err / bound).max():.3f}")
+
+
+@pytest.mark.parametrize("M,N,K", [(37, 33, 64), (172, 2560, 2560), (172, 2560, 10240)])
+def test_gemm_f32_nonfinite_rows_come_out_nan(dit, M, N, K):
+    """A row of A holding a NaN, +Inf or -Inf has no int8 slicing: its output
+    row must be NaN (never finite digits), on the direct and the split-K paths,
+    and every other row keeps its value."""
+    rng = np.random.default_rng(M + K)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    B = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    bias = rng.standard_normal(N).astype(np.float32)
+    bad = {3: np.nan, 7: np.inf, 9: -np.inf}
+    for r, v in bad.items():
+        A[r, (r * 13) % K] = v
+    C = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    dit.dit_gemm(torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda(), torch.from_numpy(bias).cuda(), C)
+    g = from_dev(C)
+    good = [r for r in range(M) if r not in bad]
+    for r in bad:
+        assert np.isnan(g[r]).all(), f"row {r} not NaN"
+    ref = O.linear(A[good], B, bias)
+    assert np.isfinite(g[good]).all()
+    assert_f32_close(g[good], ref, rel=2e-6, abs_=1e-6, what="finite rows beside non-finite ones")
+
+
 def test_gemm_packed_equals_alone_bits(dit):
     rng = np.random.default_rng(1)
     A = _bf16_vals(rng, (700, 256))

@@ -16,12 +16,11 @@
 namespace dit {
 
 // ============================================================================ bf16, MFMA
-// Workgroup = one (document, head, 256-query tile); four wavefronts of 64
-// queries, one per SIMD.  Scores are computed transposed, S^T = K Q^T, on
+// Workgroup = one (document, head, 256-query tile); eight wavefronts of 32
+// queries, two per SIMD.  Scores are computed transposed, S^T = K Q^T, on
 // v_mfma_f32_32x32x16_bf16, so each lane owns one query (per 32-query block)
 // and 16 of its keys per 32-key block: the row max and row sum stay in the
-// lane plus its partner lane l^32.  Each K or V fragment read from LDS feeds
-// the MFMAs of both 32-query blocks.
+// lane plus its partner lane l^32.
 //
 // The probabilities, rounded to bf16, are already the B operand of the next
 // MFMA, O^T = V^T P^T, if the contraction runs over keys in the order the

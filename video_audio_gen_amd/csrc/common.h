@@ -82,9 +82,12 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
+// max that keeps a NaN from either side (fmaxf drops it), so a row max over
+// |x| reports a non-finite row as NaN or Inf
+__device__ __forceinline__ float nan_max(float a, float b) { return (a > b || a != a) ? a : b; }
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  for (int o = 32; o >= 1; o >>= 1) v = nan_max(v, __shfl_xor(v, o, 64));
   return v;
 }
 

@@ -373,8 +373,12 @@ extern "C" int dit_stage_weights(dit_model* m, const dit_weight_view* views, int
       src = conv.data();
       if (sliced) {
         sliced_buf.resize(sl.bytes);
-        host_slice_rows(sl.shape[0], sl.shape[1], (sl.shape[1] + 31) / 32 * 32, reinterpret_cast<const float*>(conv.data()),
-                        reinterpret_cast<int8_t*>(sliced_buf.data()));
+        const int64_t bad = host_slice_rows(sl.shape[0], sl.shape[1], (sl.shape[1] + 31) / 32 * 32,
+                                            reinterpret_cast<const float*>(conv.data()),
+                                            reinterpret_cast<int8_t*>(sliced_buf.data()));
+        if (bad >= 0)
+          return set_error(DIT_E_INVALID, "weight '%s': row %lld holds a NaN or an Inf (fp32 GEMM weights must be finite)",
+                           v.name, static_cast<long long>(bad));
         src = sliced_buf.data();
       }
       const int64_t held = static_cast<int64_t>(conv.size() + sliced_buf.size());
@@ -490,6 +494,29 @@ extern "C" int dit_batch_bytes(const dit_model* m, const dit_segment* segs, int 
   return DIT_OK;
 }
 
+// Every GEMM a forward over this batch launches must fit the kernels' 32-bit
+// buffer offsets (the fp32 GEMM addresses 5 bytes of slices per element of an
+// operand, the bf16 GEMM one 256-row tile of an operand at a time).
+static int check_gemm_shapes(const dit_config& c, int N, int max_seg_tokens) {
+  const int D = c.hidden, F = c.ffn;
+  const int shapes[4][2] = {{3 * D, D}, {D, D}, {2 * F, D}, {D, F}};
+  for (const auto& sh : shapes) {
+    const bool ok = c.stream_dtype == DIT_BF16 ? gemm_bf16_supported(N, sh[0], sh[1]) : gemm_f32_supported(N, sh[0], sh[1]);
+    if (!ok)
+      return set_error(DIT_E_UNSUPPORTED, "%s GEMM [%d x %d] x [%d x %d]^T of a %d-token batch is beyond the kernel's 32-bit offsets",
+                       c.stream_dtype == DIT_BF16 ? "bf16" : "fp32", N, sh[1], sh[0], sh[1], N);
+  }
+  if (c.io) {
+    for (int mm = 0; mm < c.n_mod; ++mm) {
+      const int cw = token_width(c.mod[mm]);
+      if (!gemm_f32_supported(max_seg_tokens, D, cw) || !gemm_f32_supported(max_seg_tokens, cw, D))
+        return set_error(DIT_E_UNSUPPORTED, "a %d-token segment is beyond the fp32 projection GEMM's 32-bit offsets",
+                         max_seg_tokens);
+    }
+  }
+  return DIT_OK;
+}
+
 extern "C" int dit_batch_create(const dit_model* m, const dit_segment* segs, int n_segs, int n_cond,
                                 const int* cond_modality, void* tables_dev, size_t tables_bytes,
                                 dit_stream_t stream, dit_batch** out) {
@@ -509,6 +536,9 @@ extern "C" int dit_batch_create(const dit_model* m, const dit_segment* segs, int
     if (c.mod[segs[i].modality].n_axes == 1 && (segs[i].grid[1] != 1 || segs[i].grid[2] != 1))
       return set_error(DIT_E_INVALID, "dit_batch_create: segment %d is 1-axis but grid[1..2] != 1", i);
   }
+  int max_seg = 0;
+  for (int i = 0; i < n_segs; ++i) max_seg = cu[i + 1] - cu[i] > max_seg ? cu[i + 1] - cu[i] : max_seg;
+  DIT_TRY(check_gemm_shapes(c, N, max_seg));
   const int half = c.rot_dim / 2;
   TableLayout tl = table_layout(N, n_segs, half);
   if (tables_bytes < tl.total)
@@ -651,6 +681,7 @@ static int check_run(const dit_model* m, const dit_batch* b, void* ws, size_t ws
   if (m == nullptr || b == nullptr) return set_error(DIT_E_INVALID, "model or batch is null");
   if (!m->finalized) return set_error(DIT_E_STATE, "weights are not finalized");
   if (b->model != m) return set_error(DIT_E_INVALID, "batch belongs to another model");
+  DIT_TRY(check_gemm_shapes(m->cfg, b->N, b->max_seg_tokens));
   *plan = plan_ws(m, b);
   if (ws_bytes < plan->total)
     return set_error(DIT_E_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, plan->total);
@@ -969,7 +1000,7 @@ extern "C" int dit_gemm(int dtype, int M, int N, int K, const void* A, const voi
   if (M > 0 && (A == nullptr || B == nullptr || C == nullptr)) return set_error(DIT_E_INVALID, "dit_gemm: null operand");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (dtype == DIT_BF16) {
-    if (!gemm_bf16_supported(M, N, K)) return set_error(DIT_E_UNSUPPORTED, "dit_gemm bf16: K=%d must be a multiple of 32", K);
+    if (!gemm_bf16_supported(M, N, K)) return set_error(DIT_E_UNSUPPORTED, "dit_gemm bf16: K=%d must be a multiple of 64", K);
     if (c_dtype != DIT_F32 && c_dtype != DIT_BF16) return set_error(DIT_E_INVALID, "dit_gemm: c_dtype");
     const GemmEpilogue ep{c_dtype == DIT_F32 ? kEpiF32 : kEpiBf16};
     DIT_HIP(gemm_bf16(M, N, K, static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), bias, C, ep, s));

@@ -1,8 +1,10 @@
 // Bandwidth-bound kernels of the DiT block: AdaLN modulate+norm, RoPE-from-cache
 // with the QKV split, SiLU gate, gated residual, the AdaLN table, patch in/out
 // and the Euler update.  Every kernel reads and writes each byte once with
-// 16-byte (or 8-byte for bf16 quads) coalesced accesses; row reductions stay in
-// one wavefront (64 lanes) with butterfly shuffles, no LDS and no barrier.
+// 16-byte (or 8-byte for bf16 quads) coalesced accesses.  Row reductions run
+// as wavefront butterfly shuffles; where a row spans several wavefronts (the
+// norms at width 6144: 64-512 threads per row) the partial sums meet in LDS
+// behind a workgroup barrier.
 #include "common.h"
 #include "kernels.h"
 

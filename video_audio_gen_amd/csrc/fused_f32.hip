@@ -113,7 +113,7 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   lds_barrier();
   float t = 0.f;
-  for (int i = 0; i < nw; ++i) t = fmaxf(t, red[i]);
+  for (int i = 0; i < nw; ++i) t = nan_max(t, red[i]);
   return t;
 }
 
@@ -127,7 +127,7 @@ __device__ __forceinline__ void slice_row(float (*y)[4], int C4, int row, int R,
 #pragma unroll
   for (int i = 0; i < NCH; ++i)
     if (t + NT * i < C4)
-      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(y[i][0]), fabsf(y[i][1])), fmaxf(fabsf(y[i][2]), fabsf(y[i][3]))));
+      mx = nan_max(mx, nan_max(nan_max(fabsf(y[i][0]), fabsf(y[i][1])), nan_max(fabsf(y[i][2]), fabsf(y[i][3]))));
   mx = block_max(mx, redf);
   const int e = slice_exponent(mx);
   const int Kp = slice_kp(K);

@@ -8,18 +8,19 @@
 //   buffer loads (double-buffered, 128 KB) into an XOR-swizzled layout so the
 //   MFMA operand reads are bank-conflict free, and the next k-step's operands
 //   are read while the current MFMAs run.
-// f32: exact products and fp64 sums on v_mfma_f64_16x16x4_f64 (fp32 operands
-//   widened on the way in), 64x64x16 tiles and a deterministic split-K whose
-//   partition depends only on (N, K): each partial is reduced in a fixed order
-//   and rounded to fp32 once.  The fp32 parity bound (rel 1e-5 / abs 1e-6)
-//   after the music model's 24 blocks leaves room for about one rounding per
-//   stored value: fp32 accumulation, and even six-term bf16 splitting of the
-//   operands with fp64 sums of each MFMA (whose 16-product sums truncate),
-//   break it; correctly rounded GEMMs keep it.
+// f32: each row of A and B scaled by a power of two and cut into five 7-bit
+//   integer slices; the slice products run exactly on v_mfma_i32_32x32x32_i8
+//   and are combined in fp64, rounded to fp32 once (details below).  The fp32
+//   parity bound (rel 1e-5 / abs 1e-6) after the music model's 24 blocks
+//   leaves room for about one rounding per stored value: fp32 accumulation,
+//   and even six-term bf16 splitting of the operands with fp32 MFMA sums
+//   (whose 16-product sums truncate), break it; nearly correctly rounded
+//   GEMMs keep it.
 //
-// In both, the value of C[i][j] depends only on row i of A, row j of B and K --
-// never on M or on where row i sits in a tile -- so a document computed alone
-// and the same document inside a packed batch give bit-identical results.
+// In both, the value of C[i][j] depends only on row i of A, row j of B, K and
+// the device's compute-unit count (the fp32 GEMM's split-K plan) -- never on M
+// or on where row i sits in a tile -- so a document computed alone and the
+// same document inside a packed batch give bit-identical results.
 #include "common.h"
 #include "kernels.h"
 #include "slices.h"
@@ -317,7 +318,7 @@ __global__ __launch_bounds__(gb::NT) void gemm_bf16_kernel(int M, int N, int K,
   }
 }
 
-// K a multiple of 32; a 256-row tile of either operand must fit 32-bit buffer offsets.
+// K a multiple of the 64-wide K tile; a 256-row tile of either operand must fit 32-bit buffer offsets.
 bool gemm_bf16_supported(int M, int N, int K) {
   return M >= 0 && N > 0 && K > 0 && K % gb::BK == 0 && static_cast<int64_t>(gb::BM) * K * 2 < (int64_t(1) << 31);
 }
@@ -356,8 +357,11 @@ hipError_t gemm_bf16(int M, int N, int K, const uint16_t* A, const uint16_t* B, 
 // the output's rms) of the exact dot product, against 0.24 for the rounding
 // itself.  Pairs with equal s + t share one int32 accumulator (5 of them):
 // 5 pairs x 127^2 x K stays below 2^31 for K <= 26630, and splits never exceed
-// 16384 of K.  The integer sums are exact, so the result does not depend on
-// summation order; split-K partials are combined in fp64 in a fixed order.
+// 16384 of K.  The integer sums are exact; each partial's five levels are
+// combined in fp64 (one rounding), and the split-K partials are summed in a
+// fixed order.  The split plan depends on (N, K) and the compute-unit count,
+// so results are bit-reproducible on devices with the same number of CUs (a
+// device with another count may round a different set of partials).
 //
 // Workgroup tile 192 x 64 (a few hundred rows of activations are covered by
 // one or two tiles, so each weight slice is read once per row tile), K step
@@ -408,12 +412,12 @@ __global__ __launch_bounds__(256) void slice_rows_kernel(int R, int K, int Kp, c
   float mx = 0.f;
   for (int k = 4 * tid; k < K; k += 4 * 256) {
     const float4 v = *reinterpret_cast<const float4*>(x + k);
-    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    mx = nan_max(mx, nan_max(nan_max(fabsf(v.x), fabsf(v.y)), nan_max(fabsf(v.z), fabsf(v.w))));
   }
   mx = wave_max(mx);
   if ((tid & 63) == 0) red[tid >> 6] = mx;
   __syncthreads();
-  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  mx = nan_max(nan_max(red[0], red[1]), nan_max(red[2], red[3]));
   const int e = slice_exponent(mx);
   if (tid == 0) E[row] = e;
   for (int k = 4 * tid; k < Kp; k += 4 * 256) {
@@ -544,6 +548,7 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
     const bool odd = lr & 1;
     const int gnc = gn < N ? gn : N - 1;
     const int fe = Be[gnc];
+    const bool bad_col = fe == kSliceNonFinite;
     const double bv = (direct && bias != nullptr) ? static_cast<double>(bias[gnc]) : 0.0;
     const double bv_pair = __shfl_xor(bv, 1, 64);  // the partner column's bias
     const int col = odd ? gn - 1 : gn;
@@ -558,7 +563,8 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
         double x = 0.0;
 #pragma unroll
         for (int d = S - 1; d >= 0; --d) x += ldexp(static_cast<double>(acc[d][e + h]), -7 * (d + 2));
-        v[h] = ldexp(x, Ae[r] + fe);
+        const int ae = Ae[r];
+        v[h] = (bad_col || ae == kSliceNonFinite) ? __builtin_nan("") : ldexp(x, ae + fe);
       }
       const double recv = __shfl_xor(odd ? v[0] : v[1], 1, 64);
       const int row = odd ? gm + 1 : gm;
@@ -586,7 +592,8 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
     double v = 0.0;
 #pragma unroll
     for (int d = S - 1; d >= 0; --d) v += ldexp(static_cast<double>(acc[d][e]), -7 * (d + 2));
-    v = ldexp(v, Ae[gm] + fe);
+    const int ae = Ae[gm];
+    v = (fe == kSliceNonFinite || ae == kSliceNonFinite) ? __builtin_nan("") : ldexp(v, ae + fe);
     if (direct)
       C[static_cast<size_t>(gm) * N + gn] = static_cast<float>(v + bv);
     else

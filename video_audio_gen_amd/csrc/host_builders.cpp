@@ -131,8 +131,8 @@ extern "C" int dit_timestep_embedding(const float* t_host, int n, int dim, float
 // arms land" item 2: the rectified-flow time-shift sigma schedule (video shift
 // 12, audio shift 3).
 extern "C" int dit_sigma_schedule(double shift, int n_steps, double* sigma_host, float* dt_host) {
-  if (n_steps < 1 || !(shift > 0.0))
-    return set_error(DIT_E_INVALID, "dit_sigma_schedule: n_steps must be >= 1 and shift > 0");
+  if (n_steps < 1 || !(shift > 0.0 && std::isfinite(shift)))
+    return set_error(DIT_E_INVALID, "dit_sigma_schedule: n_steps must be >= 1 and shift positive and finite");
   std::vector<double> sig(n_steps + 1);
   for (int i = 0; i <= n_steps; ++i) {
     const double s = 1.0 - static_cast<double>(i) / static_cast<double>(n_steps);
@@ -149,15 +149,19 @@ extern "C" int dit_sigma_schedule(double shift, int n_steps, double* sigma_host,
 // max|x| < 2^e (frexp), then five truncating 7-bit digits of x 2^-e; five
 // planes of [Kp/32][R][32] int8 (zero past K), then R int32 exponents 256
 // bytes further aligned.  All steps are exact in fp32, so both sides produce
-// the same bytes.
+// the same bytes.  A weight row holding a NaN or an Inf has no slicing (the
+// device marks such activation rows instead): the first one is returned.
 namespace dit {
-void host_slice_rows(int64_t R, int64_t K, int64_t Kp, const float* X, int8_t* out) {
+int64_t host_slice_rows(int64_t R, int64_t K, int64_t Kp, const float* X, int8_t* out) {
   const size_t plane = static_cast<size_t>(R) * Kp;
   int32_t* E = reinterpret_cast<int32_t*>(out + ((5 * plane + 255) & ~size_t(255)));
   for (int64_t r = 0; r < R; ++r) {
     const float* x = X + r * K;
     float mx = 0.f;
-    for (int64_t k = 0; k < K; ++k) mx = std::fmax(mx, std::fabs(x[k]));
+    for (int64_t k = 0; k < K; ++k) {
+      if (!std::isfinite(x[k])) return r;
+      mx = std::fmax(mx, std::fabs(x[k]));
+    }
     int e = 0;
     if (mx > 0.f) std::frexp(mx, &e);
     E[r] = e;
@@ -171,5 +175,6 @@ void host_slice_rows(int64_t R, int64_t K, int64_t Kp, const float* X, int8_t* o
       }
     }
   }
+  return -1;
 }
 }  // namespace dit

@@ -9,5 +9,7 @@ namespace dit {
 // Record a thread-local error message and return `code`.
 int set_error(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 // int8 slices of an fp32 weight matrix [R, K] for the f32 GEMM (host_builders.cpp).
-void host_slice_rows(int64_t R, int64_t K, int64_t Kp, const float* X, int8_t* out);
+// Returns -1, or the first row holding a NaN or an Inf (the output is then
+// incomplete and must not be used).
+int64_t host_slice_rows(int64_t R, int64_t K, int64_t Kp, const float* X, int8_t* out);
 }  // namespace dit
