@@ -358,6 +358,23 @@ int dit_gemm_splits(int dtype, int N, int K, int* splits);
 int dit_gemm(int dtype, int M, int N, int K, const void* A, const void* B, const float* bias,
              void* C, int c_dtype, void* ws, size_t ws_bytes, dit_stream_t stream);
 
+/* The fp32 dit_gemm for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same kernels, same split plan and bit-identical C as
+ * dit_gemm(DIT_F32, ...); the scratch (int8 slices of A and B, fp64 split-K
+ * partials) lives in a device array built into the library, of
+ * dit_gemm_f32_noalloc_limit() bytes (64 MiB) on each device it runs on, held
+ * until the process ends.  No allocation, no host synchronisation.  A, B, bias
+ * (may be NULL) and C are device pointers the caller owns, C[M,N] float32.
+ * Every call on one device shares that device's array: calls that overlap on
+ * a device (other streams, or other host threads without ordering) race.
+ * DIT_E_WORKSPACE when the shapes need more scratch than the array holds
+ * (dit_gemm_workspace_bytes(DIT_F32, ...) gives the need), DIT_E_INVALID /
+ * DIT_E_UNSUPPORTED as dit_gemm; nothing is launched then. */
+size_t dit_gemm_f32_noalloc_limit(void);
+int dit_gemm_f32_noalloc(int M, int N, int K, const float* A, const float* B, const float* bias, float* C,
+                         dit_stream_t stream);
+
 /* h[N,D] (dtype) = norm(x[N,D]) * (1 + mod[c][scale_k]) + mod[c][shift_k],
  * c = cond_idx[n]; mod [n_cond, 6, D] f32; which = 0 (msa: shift 0, scale 1) or
  * 1 (mlp: shift 3, scale 4); mod NULL = plain norm.  norm = DIT_NORM_*.  x is

@@ -26,7 +26,7 @@ def dit():
 
 def test_exports_every_declared_symbol(dit):
     hdr = open(os.path.join(ROOT, "include", "dit.h")).read()
-    names = set(re.findall(r"^\s*(?:int|void|const char\*)\s+(dit_\w+)\s*\(", hdr, re.M))
+    names = set(re.findall(r"^\s*(?:int|void|size_t|const char\*)\s+(dit_\w+)\s*\(", hdr, re.M))
     assert len(names) >= 30
     lib = dit.load()
     missing = [n for n in sorted(names) if not hasattr(lib, n)]

@@ -96,6 +96,7 @@ _SIGS = {
     "dit_gemm_workspace_bytes": [_I, _I, _I, _I, ctypes.POINTER(_SZ)],
     "dit_gemm_splits": [_I, _I, _I, ctypes.POINTER(_I)],
     "dit_gemm": [_I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _SZ, _P],
+    "dit_gemm_f32_noalloc": [_I, _I, _I, _P, _P, _P, _P, _P],
     "dit_modnorm": [_I, _I, ctypes.c_float, _I, _I, _P, _I, _P, _I, _P, _P, _P],
     "dit_rope_split": [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P],
     "dit_attention": [_I, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P],
@@ -128,6 +129,8 @@ def load() -> ctypes.CDLL:
         f.restype = None
     lib.dit_last_error.argtypes = []
     lib.dit_last_error.restype = ctypes.c_char_p
+    lib.dit_gemm_f32_noalloc_limit.argtypes = []
+    lib.dit_gemm_f32_noalloc_limit.restype = ctypes.c_size_t
     _lib = lib
     return lib
 
@@ -413,6 +416,17 @@ def dit_gemm(A, B, bias, C, stream=None):
     _check(load().dit_gemm(dt, M, N, K, _ptr(A), _ptr(B), _ptr(bias), _ptr(C), _dt(C), _ptr(ws), int(ws_bytes.value),
                            _stream(stream)))
     return ws
+
+
+def dit_gemm_f32_noalloc(A, B, bias, C, stream=None):
+    """fp32 C[M,N] = A[M,K] . B[N,K]^T + bias with the library's built-in scratch (no workspace)."""
+    M, K = A.shape
+    N = B.shape[0]
+    _check(load().dit_gemm_f32_noalloc(M, N, K, _ptr(A), _ptr(B), _ptr(bias), _ptr(C), _stream(stream)))
+
+
+def dit_gemm_f32_noalloc_limit() -> int:
+    return int(load().dit_gemm_f32_noalloc_limit())
 
 
 def dit_gemm_splits(N: int, K: int) -> int:
