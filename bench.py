@@ -15,6 +15,11 @@ seconds per forward); `roofline` reports the kernel family that takes the most
 device time, from per-launch HIP events recorded on the launch stream during a
 second pass of K forwards; `cpu_baseline` times the CPU oracle on a bounded
 sample (a few blocks) of the same workload and scales it to a whole forward.
+
+`--extra c4` (the default) then frees the headline model and times the 64-block
+bf16 DiT (18,432 tokens in four documents, weights staged once) in a timed
+region of its own, reported under `extra.c4` with its own roofline: a second
+measured configuration, not part of the headline value.
 """
 
 from __future__ import annotations
@@ -190,42 +195,15 @@ def cpu_baseline(cfg, weights_fn, islands, inp, sample_blocks: int, log=log, min
                       f"{cfg.n_blocks}-block forward ({per_forward:.1f}s)"}
 
 
-def main(argv=None):
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c2")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-blocks", type=int, default=4)
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="only copy MIB MiB device-to-device five times (the known-size kernel that scales "
-                         "the FETCH_SIZE / WRITE_SIZE counters), then exit")
-    ap.add_argument("--no-graph", action="store_true",
-                    help="launch every kernel from the host instead of replaying one captured HIP graph")
-    a = ap.parse_args(argv)
-    if a.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (the path runs on a single device; "
-              "multi-GPU sharding is designed, not built)", file=sys.stderr)
-        return 2
-
+def measure(cfg, steps, warmup, no_graph=False, protocol_loops=5):
+    """Stage `cfg`'s weights, time `steps` forwards (or denoise steps) after
+    `warmup`, then a per-kernel pass; returns the measurements and the runner."""
     import numpy as np
     import torch
 
-    if a.copy_calibration:
-        n = a.copy_calibration * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"copied {a.copy_calibration} MiB x 5")
-        return 0
-
-    import synthetic as S
+    import synthetic as S  # noqa: F401
     from video_audio_gen_amd import dit, harness
 
-    cfg = S.get_config(a.workload)
     dev = torch.cuda.get_device_name(0)
     log(f"workload {cfg.name}: {cfg.n_blocks} blocks, hidden {cfg.hidden}, {cfg.n_tokens} tokens on {dev}")
     t0 = time.time()
@@ -262,15 +240,15 @@ def main(argv=None):
                 k -= n
         r.forward = lambda: run_steps(1)
 
-    for _ in range(a.warmup):
+    for _ in range(warmup):
         r.forward()
     torch.cuda.synchronize()
-    log(f"warmup {a.warmup} done")
+    log(f"warmup {warmup} done")
     # One forward captured as a HIP graph (the ~500 launches of the music model
     # replay without host round trips); its output is checked against the eager
     # forward before timing.
     step = r.forward
-    if not a.no_graph and not loop:
+    if not no_graph and not loop:
         eager = r.forward().clone()
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
@@ -290,24 +268,24 @@ def main(argv=None):
     t0 = time.perf_counter()
     start.record()
     if loop:
-        run_steps(a.steps)
+        run_steps(steps)
     else:
-        for _ in range(a.steps):
+        for _ in range(steps):
             step()
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = start.elapsed_time(stop) / a.steps
-    log(f"timed {a.steps} {'denoise steps' if loop else 'forwards'}: {ms:.3f} ms per "
-        f"{'step' if loop else 'forward'} (host wall {wall * 1e3 / a.steps:.3f} ms)")
+    ms = start.elapsed_time(stop) / steps
+    log(f"timed {steps} {'denoise steps' if loop else 'forwards'}: {ms:.3f} ms per "
+        f"{'step' if loop else 'forward'} (host wall {wall * 1e3 / steps:.3f} ms)")
 
     # The pages' protocol beside it: loops of R = 1 and R = 3 forwards, each
     # between two events, five of each; median / min / max per forward and the
     # slope over R (the intercept is a loop's fixed cost).
     timing = None
-    if not loop:
+    if not loop and protocol_loops > 0:
         per = {1: [], 3: []}
-        for _ in range(5):
+        for _ in range(protocol_loops):
             for R in (1, 3):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 torch.cuda.synchronize()
@@ -319,7 +297,7 @@ def main(argv=None):
                 per[R].append(e0.elapsed_time(e1))
         med = {R: float(np.median(v)) for R, v in per.items()}
         slope = (med[3] - med[1]) / 2
-        timing = {"loops": 5,
+        timing = {"loops": protocol_loops,
                   "r1_ms": {"median": round(med[1], 4), "min": round(min(per[1]), 4), "max": round(max(per[1]), 4)},
                   "r3_ms_per_forward": {"median": round(med[3] / 3, 4), "min": round(min(per[3]) / 3, 4),
                                         "max": round(max(per[3]) / 3, 4)},
@@ -330,9 +308,9 @@ def main(argv=None):
     # per-kernel device time: HIP events recorded around every launch on its stream
     dit.dit_profile_begin()
     if loop:
-        run_steps(a.steps)
+        run_steps(steps)
     else:
-        for _ in range(a.steps):
+        for _ in range(steps):
             r.forward()
     prof = dit.dit_profile_end()
     total_dev = sum(v[1] for v in prof.values())
@@ -349,7 +327,7 @@ def main(argv=None):
         if key not in work or t <= 0:
             continue
         amt, unit = work[key]
-        rate = amt * a.steps / (t * 1e-3)
+        rate = amt * steps / (t * 1e-3)
         if unit == "byte":
             kernels[k] = {"GB/s": round(rate / 1e9, 1), "frac_hbm": round(rate / 1e9 / PEAK["hbm_gbs"], 4),
                           "avg_us": round(t / n * 1e3, 2)}
@@ -362,7 +340,7 @@ def main(argv=None):
     fam = max(prof.items(), key=lambda kv: kv[1][1])[0]
     n_launch, fam_ms = prof[fam]
     if fam in ("gemm_f32", "gemm_bf16"):
-        flops = work[fam][0] * a.steps
+        flops = work[fam][0] * steps
         peak_key, peak_note = GEMM_FAMILY_PEAK[fam]
         achieved = flops / (fam_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK[peak_key], "unit": "TFLOP/s",
@@ -372,7 +350,7 @@ def main(argv=None):
             # the same rate against the published fp32 MFMA peak (the unit an fp32 GEMM would otherwise use)
             roof["frac_of_fp32_mfma_peak"] = round(achieved / PEAK["mfma_f32"], 4)
     elif fam == "attention_bf16":
-        flops = attention_flops(cfg) * a.steps
+        flops = attention_flops(cfg) * steps
         achieved = flops / (fam_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK["mfma_bf16"], "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK["mfma_bf16"], 4), "traffic": None, "kernel": fam,
@@ -381,6 +359,55 @@ def main(argv=None):
         roof = {"bound": "unknown", "achieved": None, "peak": None, "unit": None, "frac": None,
                 "traffic": None, "kernel": fam}
     roof["traffic"] = measured_traffic(fam, cfg.name)
+
+    return {"ms": ms, "timing": timing, "kernels": kernels, "roofline": roof, "loop": loop,
+            "launch": "hip_graph" if step is not r.forward else "eager", "dev": dev, "runner": r,
+            "model": model}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-blocks", type=int, default=4)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device-to-device five times (the known-size kernel that scales "
+                         "the FETCH_SIZE / WRITE_SIZE counters), then exit")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch every kernel from the host instead of replaying one captured HIP graph")
+    ap.add_argument("--extra", default="c4",
+                    help="comma-separated workloads timed after the headline one, each in its own timed "
+                         "region, reported under their own keys ('none' for none)")
+    ap.add_argument("--extra-steps", type=int, default=5)
+    ap.add_argument("--extra-warmup", type=int, default=1)
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (the path runs on a single device; "
+              "multi-GPU sharding is designed, not built)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    if a.copy_calibration:
+        n = a.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {a.copy_calibration} MiB x 5")
+        return 0
+
+    import synthetic as S
+
+    cfg = S.get_config(a.workload)
+    res = measure(cfg, a.steps, a.warmup, a.no_graph)
+    r, ms, loop, dev = res["runner"], res["ms"], res["loop"], res["dev"]
+    timing, kernels, roof = res["timing"], res["kernels"], res["roofline"]
 
     cpu = None
     if not a.no_cpu_baseline:
@@ -405,12 +432,33 @@ def main(argv=None):
         "config": {"workload": cfg.name, "n_blocks": cfg.n_blocks, "hidden": cfg.hidden,
                    "heads": cfg.n_heads, "head_dim": cfg.head_dim, "ffn": cfg.ffn,
                    "tokens": tokens, "documents": [s.n_tokens for s in cfg.segments],
-                   "device": dev, "launch": "hip_graph" if step is not r.forward else "eager"},
+                   "device": dev, "launch": res["launch"]},
         "roofline": roof,
         "cpu_baseline": cpu,
         "timing": timing,
         "kernels": kernels,
     }
+    # further workloads after the headline one (the headline model is freed first)
+    extras = [w for w in a.extra.split(",") if w and w != "none" and S.get_config(w).name != cfg.name]
+    if extras:
+        del r, res
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        line["extra"] = {}
+        for w in extras:
+            ecfg = S.get_config(w)
+            e = measure(ecfg, a.extra_steps, a.extra_warmup, a.no_graph, protocol_loops=0)
+            line["extra"][w] = {
+                "workload": ecfg.name, "dtype": "f32" if ecfg.stream == "f32" else "bf16",
+                "ms_per_forward" if not e["loop"] else "ms_per_step": round(e["ms"], 4),
+                "tokens_per_s": round(ecfg.n_tokens / (e["ms"] * 1e-3), 2),
+                "steps": a.extra_steps, "warmup": a.extra_warmup, "launch": e["launch"],
+                "n_blocks": ecfg.n_blocks, "tokens": ecfg.n_tokens,
+                "documents": [sg.n_tokens for sg in ecfg.segments],
+                "roofline": e["roofline"], "kernels": e["kernels"]}
+            del e
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
     if loop:
         line["config"]["denoise_steps"] = cfg.denoise_steps
         line["config"]["timed"] = f"{a.steps} Euler steps of the {cfg.denoise_steps}-step schedule (forward + update each)"

@@ -76,8 +76,10 @@ def assert_bf16_parity(got, ref, ctl, what=""):
     g_max, c_max = float(d.max() / r), float(dc.max() / r)
     max_bound = max(BF16_BOUND, CONTROL_FACTOR * c_max)
     rms_bound = max(BF16_BOUND, CONTROL_FACTOR * c_rms)
-    print(f"{what}: max|d|/rms {g_max:.3e} (control {c_max:.3e}, bound {max_bound:.3e})  "
-          f"rms(d)/rms {g_rms:.3e} (control {c_rms:.3e}, bound {rms_bound:.3e})")
+    print(f"{what}: max|d|/rms {g_max:.3e} (control {c_max:.3e}, bound {max_bound:.3e}, "
+          f"{'inside' if g_max <= BF16_BOUND else 'outside'} the 3e-3 target)  "
+          f"rms(d)/rms {g_rms:.3e} (control {c_rms:.3e}, bound {rms_bound:.3e})  "
+          f"GPU/control {g_max / max(c_max, 1e-30):.2f} (max) {g_rms / max(c_rms, 1e-30):.2f} (rms)")
     assert g_max <= max_bound, f"{what}: max|d|/rms = {g_max:.3e} > {max_bound:.3e}"
     assert g_rms <= rms_bound, f"{what}: rms(d)/rms = {g_rms:.3e} > {rms_bound:.3e}"
     return g_max, g_rms
