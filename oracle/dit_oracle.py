@@ -38,7 +38,9 @@ Precision modes:
   'bf16'  -- float64 math with round-to-nearest-even to bf16 at the storage
              points of a bf16 block stream with fp32 islands (listed in
              ``block_forward``).  The residual stream, the modulation table,
-             the time embedding and the projections in and out stay fp32.
+             the time embedding and the projections in and out stay fp32;
+  'mxfp8' -- as 'bf16', with the four block GEMMs' operands re-quantized to
+             MXFP8 (``quantize_mx8``) and dequantized before the product.
 
 Pins: tests/test_oracle_pins.py checks every function here against closed
 forms, invariants and brute force; tests/test_oracle_wiring_pins.py pins the
@@ -65,7 +67,8 @@ __all__ = [
     "attention_varlen", "attention_dense_masked", "silu", "adaln_table", "block_forward",
     "patchify", "unpatchify", "forward", "sigma_schedule", "sigma_dt", "euler_step",
     "denoise_step_conditions", "denoise_loop", "split_mlp", "cfg_pairs", "cfg_combine",
-    "cfg_denoise_loop",
+    "cfg_denoise_loop", "e4m3_value", "e8m0_value", "e4m3_encode", "e4m3_encode_array", "quantize_mx8", "dequantize_mx8",
+    "linear_mx8",
 ]
 
 
@@ -91,12 +94,135 @@ def round_f32(x: np.ndarray) -> np.ndarray:
 
 def _store(x: np.ndarray, mode: str) -> np.ndarray:
     """A bf16 storage point of the block stream (identity in 'fp64' mode)."""
-    return round_bf16(x) if mode == "bf16" else x
+    return round_bf16(x) if mode in ("bf16", "mxfp8") else x
 
 
 def _store_f32(x: np.ndarray, mode: str) -> np.ndarray:
     """An fp32 storage point of a bf16 stream (identity in 'fp64' mode)."""
-    return round_f32(x) if mode == "bf16" else x
+    return round_f32(x) if mode in ("bf16", "mxfp8") else x
+
+
+# ----------------------------------------------------------------------------- MX block scaling (fp8)
+#
+# The low-precision GEMM path.  The pages' speed path is NVFP4 (FP4 values,
+# one E4M3 scale per group of 16 along K plus an fp32 global scale; page "port
+# the MiniMax-H3 omni-modal video+audio DiT", update "NVFP4 arm grounded" and
+# "Not yet built -- honestly recorded").  The matrix cores of this GPU take
+# the OCP microscaling (MX) formats instead: 32 consecutive K values share one
+# power-of-two scale (E8M0), the values are OCP FP8 E4M3.  Reading taken: both
+# operands of the four block GEMMs of a bf16 stream are re-quantized to MXFP8
+# from their bf16 values (weights at staging, activations before each GEMM);
+# the scale of a block is the smallest power of two 2^s with max|v| <= 448 2^s
+# (so no value of the block saturates: the OCP rule 2^(floor(log2 max|v|) - 8)
+# would clamp the block maximum by up to 1/8 whenever its leading digits
+# exceed 1.75), each value divided by it is rounded to nearest-even E4M3;
+# s is clamped to [-127, 127]; an all-zero block takes the smallest scale
+# 2^-127 and a block holding a NaN or an Inf the NaN scale (byte 255).
+
+E4M3_MAX = 448.0
+MX_BLOCK = 32
+
+
+def e4m3_value(code: int) -> float:
+    """Value of an OCP FP8 E4M3 byte: sign, 4 exponent bits (bias 7), 3
+    mantissa bits; exponent 0 is subnormal (m 2^-9); S.1111.111 is NaN."""
+    code = int(code) & 0xFF
+    sgn = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 15, code & 7
+    if e == 15 and m == 7:
+        return float("nan")
+    if e == 0:
+        return sgn * m * 2.0 ** -9
+    return sgn * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def e8m0_value(byte: int) -> float:
+    """Value of an E8M0 scale byte: 2^(byte - 127); 255 is NaN."""
+    byte = int(byte) & 0xFF
+    return float("nan") if byte == 255 else 2.0 ** (byte - 127)
+
+
+def _half_even(x: float) -> int:
+    """Nearest integer to x >= 0, ties to even."""
+    f = math.floor(x)
+    r = x - f
+    if r > 0.5 or (r == 0.5 and f % 2 == 1):
+        f += 1
+    return int(f)
+
+
+def e4m3_encode(y: float) -> int:
+    """Round y to nearest-even OCP E4M3, clamped to +-448 (the sign of y kept, -0 included)."""
+    sgn = 0x80 if math.copysign(1.0, y) < 0 else 0
+    a = abs(y)
+    if a >= E4M3_MAX:
+        return sgn | 0x7E
+    if a < 2.0 ** -6:                       # subnormal range: steps of 2^-9 (8 steps reach 2^-6, code 0x08)
+        return sgn | _half_even(a * 2.0 ** 9)
+    e = math.frexp(a)[1] - 1                # a = mant 2^e, mant in [1, 2)
+    q = _half_even((a / 2.0 ** e - 1.0) * 8.0)
+    if q == 8:
+        e, q = e + 1, 0
+    return sgn | ((e + 7) << 3) | q
+
+
+def e4m3_encode_array(y: np.ndarray) -> np.ndarray:
+    """``e4m3_encode`` over an array (the same steps, vectorized: np.rint
+    rounds half to even)."""
+    y = np.asarray(y, np.float64)
+    sgn = np.where(np.signbit(y), 0x80, 0).astype(np.int64)
+    a = np.abs(y)
+    sub = a < 2.0 ** -6
+    e = np.frexp(np.where(sub, 1.0, a))[1] - 1
+    q = np.rint((np.where(sub, 1.0, a) / np.exp2(e.astype(np.float64)) - 1.0) * 8.0).astype(np.int64)
+    carry = q == 8
+    e = np.where(carry, e + 1, e)
+    q = np.where(carry, 0, q)
+    mag = np.where(sub, np.rint(a * 2.0 ** 9).astype(np.int64), ((e + 7) << 3) | q)
+    mag = np.where(a >= E4M3_MAX, 0x7E, mag)
+    return (sgn | mag).astype(np.uint8)
+
+
+def quantize_mx8(v: np.ndarray):
+    """MXFP8 quantization of the rows of v [R, K] (K a multiple of 32):
+    returns (codes uint8 [R, K], scales uint8 [R, K/32])."""
+    v = np.asarray(v, np.float64)
+    R, K = v.shape
+    assert K % MX_BLOCK == 0
+    blk = v.reshape(R, K // MX_BLOCK, MX_BLOCK)
+    finite = np.isfinite(blk).all(axis=2)
+    amax = np.where(finite, np.abs(np.where(np.isfinite(blk), blk, 0.0)).max(axis=2), 0.0)
+    e = np.frexp(amax)[1] - 1                                        # amax = m 2^e, m in [1, 2)
+    over = amax / np.exp2(e.astype(np.float64)) > E4M3_MAX / 256.0     # m > 1.75: 2^(e-8) would clamp
+    shared = np.clip(e - 8 + over, -127, 127)
+    scales = np.where(amax > 0, shared + 127, 0)
+    scales = np.where(finite, scales, 255).astype(np.uint8)
+    X = np.exp2(np.where(amax > 0, shared, 0).astype(np.float64))[..., None]
+    codes = e4m3_encode_array(np.where(finite[..., None], blk, 0.0) / X)
+    # an all-zero block keeps each zero's sign; a non-finite block has zero codes
+    codes = np.where(finite[..., None], codes, 0).astype(np.uint8)
+    return codes.reshape(R, K), scales
+
+
+_E4M3_TABLE = None
+
+
+def dequantize_mx8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Values of MXFP8 rows: E4M3 value times its block's E8M0 scale."""
+    global _E4M3_TABLE
+    if _E4M3_TABLE is None:
+        _E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], np.float64)
+    vals = _E4M3_TABLE[np.asarray(codes, np.uint8)]
+    sc = np.array([e8m0_value(b) for b in range(256)], np.float64)[np.asarray(scales, np.uint8)]
+    return vals * np.repeat(sc, MX_BLOCK, axis=-1)
+
+
+def linear_mx8(x: np.ndarray, W: np.ndarray, b: np.ndarray, accum: str = "fp64") -> np.ndarray:
+    """y = Q(x) Q(W)^T + b: both operands quantized to MXFP8 along K and
+    dequantized, then the plain product (the scaled matrix cores' definition)."""
+    xq = dequantize_mx8(*quantize_mx8(x))
+    wq = dequantize_mx8(*quantize_mx8(W))
+    return linear(xq, wq, b, accum)
 
 
 # ----------------------------------------------------------------------------- layout
@@ -404,8 +530,10 @@ def block_forward(cfg, x: np.ndarray, mod: np.ndarray, bw: Dict[str, np.ndarray]
     m  = gated SiLU of u                                        (bf16 store)
     x  = x + gate_mlp[c] * (m W_2^T + b)                        (fp32 store)
 
-    c = cond_idx of the token.  The storage points apply in 'bf16' mode only;
-    ``accum`` selects the GEMM accumulation (see ``linear``).
+    c = cond_idx of the token.  The storage points apply in 'bf16' and
+    'mxfp8' mode; in 'mxfp8' mode the four GEMMs run on MXFP8 re-quantized
+    operands (``linear_mx8``).  ``accum`` selects the GEMM accumulation (see
+    ``linear``).
     Reading taken: the residual stream and both projection outputs feeding it
     stay fp32, because a bf16 rounding of those values alone moves a block's
     output by more than the bf16 tolerance.
@@ -416,7 +544,8 @@ def block_forward(cfg, x: np.ndarray, mod: np.ndarray, bw: Dict[str, np.ndarray]
     m_tok = mod[ci]  # [N, 6, D]
     p = f"blocks.{b}."
     W = lambda n: bw[p + n]  # noqa: E731
-    lin = lambda a, w, bias: linear(a, w, bias, accum)  # noqa: E731
+    gemm = linear_mx8 if mode == "mxfp8" else linear
+    lin = lambda a, w, bias: gemm(a, w, bias, accum)  # noqa: E731
 
     h = _store(modulate(norm(x, cfg.norm, cfg.norm_eps), m_tok[:, 0], m_tok[:, 1]), mode)
     qkv = _store(lin(h, W("attn.qkv.weight"), W("attn.qkv.bias")), mode)
@@ -495,7 +624,8 @@ def forward(cfg, weights: Callable[[int], Dict[str, np.ndarray]], islands: Dict[
     only the fp32 output heads) -> gather -> fp32 out-projection -> unpatchify.
     Without: tokens in, tokens out.  Returns {'latent.{i}' or 'x': array}.
     """
-    mode = mode or ("bf16" if cfg.stream == "bf16" else "fp64")
+    mode = mode or ("fp64" if cfg.stream != "bf16" else ("mxfp8" if getattr(cfg, "gemm", "stream") == "mxfp8"
+                                                         else "bf16"))
     layout = pack_layout(cfg)
     cos, sin = rope_cache(cfg)
     cu = layout["cu_seqlens"]
