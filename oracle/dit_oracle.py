@@ -68,7 +68,7 @@ __all__ = [
     "patchify", "unpatchify", "forward", "sigma_schedule", "sigma_dt", "euler_step",
     "denoise_step_conditions", "denoise_loop", "split_mlp", "cfg_pairs", "cfg_combine",
     "cfg_denoise_loop", "e4m3_value", "e8m0_value", "e4m3_encode", "e4m3_encode_array", "quantize_mx8", "dequantize_mx8",
-    "linear_mx8",
+    "linear_mx8", "centered_rope_cache", "rms_affine", "vit_block_forward",
 ]
 
 
@@ -567,6 +567,87 @@ def block_forward(cfg, x: np.ndarray, mod: np.ndarray, bw: Dict[str, np.ndarray]
     if trace is not None:
         trace.update(h2=h2, u=u, m=mm, a2=a2, x_out=x)
     return x
+
+
+# ----------------------------------------------------------------------------- ViT-style block variant
+#
+# The video VAE's decoder block (page "port the MiniMax-H3 omni-modal
+# video+audio DiT", updates "video-VAE decoder block ported" and "video-VAE
+# ViT3D decoder complete"), fp32 throughout:
+#   h += scale1 * Attention(RMSNorm(h)),  h += scale2 * GatedSiLU_FF(RMSNorm(h))
+# with affine RMSNorms, learned per-channel residual scales, a per-head RMS norm
+# of q and k without affine weights, a fused qkv projection laid out per head
+# ([head0 q | head0 k | head0 v | head1 q | ...]) and a 3-axis rotary
+# embedding on length-normalized token coordinates.
+
+def centered_rope_cache(grid, axis_dims, theta: float):
+    """cos/sin [T*H*W, sum(axis_dims)/2] of a (t, h, w) token grid, raster order.
+
+    Per axis a of extent n_a, token index i has the coordinate
+    c = (2i + 1)/n_a - 1 (the centre of cell i of [-1, 1) split in n_a), and
+    the angle of frequency j is (2 pi c) f_aj with f_aj = 1/theta^(2j/d_a),
+    j < d_a/2; the axes' blocks are concatenated (t, h, w) and paired with
+    rotate_half as in the integer-grid cache.  fp64, scalar libm, rounded to
+    float32.  (Readings taken: the axes share the rotary width equally -- the
+    caller passes d_a -- and the frequency spacing is the standard one.)
+    """
+    n_tok = 1
+    for g in grid:
+        n_tok *= g
+    half = sum(axis_dims) // 2
+    cos = np.empty((n_tok, half), np.float32)
+    sin = np.empty((n_tok, half), np.float32)
+    freqs = [rope_inv_freq(d, theta) for d in axis_dims]
+    two_pi = 2.0 * math.pi
+    row = 0
+    for t in range(grid[0]):
+        for h in range(grid[1]):
+            for w in range(grid[2]):
+                idx = (t, h, w)
+                col = 0
+                for a in range(3):
+                    c = (2.0 * idx[a] + 1.0) / grid[a] - 1.0
+                    for f in freqs[a]:
+                        ang = (two_pi * c) * f
+                        cos[row, col] = math.cos(ang)
+                        sin[row, col] = math.sin(ang)
+                        col += 1
+                row += 1
+    return cos, sin
+
+
+def rms_affine(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm with a per-channel weight: x / sqrt(mean(x^2) + eps) * g."""
+    return norm(x, "rms", eps) * np.asarray(g, np.float64)
+
+
+def vit_block_forward(x: np.ndarray, w: Dict[str, np.ndarray], n_heads: int, rot: int, eps: float,
+                      cu_seqlens: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
+    """One ViT-style decoder block on x [N, D] in fp64.
+
+    w: 'norm1.weight' [D], 'attn.qkv.weight' [3D, D] + bias (rows per head:
+    [q | k | v] of head 0, then head 1, ...), 'attn.out.weight' [D, D] + bias,
+    'scale1' [D], 'norm2.weight' [D], 'ff.w1.weight' [2F, D] + bias ([gate |
+    up], reading taken for the gated SiLU), 'ff.w2.weight' [D, F] + bias,
+    'scale2' [D].  The q/k norm is an RMS norm over each head's dims with the
+    block's eps and no weight; RoPE acts on the first ``rot`` dims of q and k.
+    """
+    N, D = x.shape
+    hd = D // n_heads
+    h = rms_affine(x, w["norm1.weight"], eps)
+    qkv = linear(h, w["attn.qkv.weight"], w["attn.qkv.bias"]).reshape(N, n_heads, 3, hd)
+    q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+    q = norm(q, "rms", eps)
+    k = norm(k, "rms", eps)
+    q = apply_rope(q, cos, sin, rot)
+    k = apply_rope(k, cos, sin, rot)
+    o = attention_varlen(q, k, v, cu_seqlens).reshape(N, D)
+    x = x + np.asarray(w["scale1"], np.float64) * linear(o, w["attn.out.weight"], w["attn.out.bias"])
+    h2 = rms_affine(x, w["norm2.weight"], eps)
+    u = linear(h2, w["ff.w1.weight"], w["ff.w1.bias"])
+    F = u.shape[1] // 2
+    m = silu(u[:, :F]) * u[:, F:]
+    return x + np.asarray(w["scale2"], np.float64) * linear(m, w["ff.w2.weight"], w["ff.w2.bias"])
 
 
 # ----------------------------------------------------------------------------- patch islands
