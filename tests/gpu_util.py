@@ -62,18 +62,32 @@ def assert_rms_rel(got, ref, bound, what=""):
 # -- the oracle against itself with fp32 instead of fp64 GEMM accumulation,
 # same bf16 storage points -- already breaks it (single-ulp bf16 rounding flips
 # at large elements: max|d|/rms = 1.7e-2 on one 6144-wide block), the bound
-# that applies is 3x the control arm's own drift, in max and in rms.
+# that applies is 2x the control arm's own drift, in max and in rms: the GPU's
+# one rounding beyond the control's is the attention's bf16 probabilities, and
+# its measured drift is 1.0-1.95x the control's on every bf16 test (1 to 64
+# blocks, 320 to 26,624 tokens).
 BF16_BOUND = 3e-3
-CONTROL_FACTOR = 3.0
+CONTROL_FACTOR = 2.0
 
 
 def assert_bf16_parity(got, ref, ctl, what=""):
-    got, ref, ctl = (np.asarray(a, np.float64) for a in (got, ref, ctl))
+    ref, ctl = (np.asarray(a, np.float64) for a in (ref, ctl))
+    r = rms(ref)
+    dc = np.abs(ctl - ref)
+    return assert_bf16_parity_stats(got, ref, float(dc.max() / r), float(np.sqrt(np.mean(dc * dc)) / r), what)
+
+
+def assert_bf16_parity_stats(got, ref, c_max, c_rms, what=""):
+    """The bf16 criterion with the control arm's drift given as its statistics
+    (max|ctl - ref|/rms(ref) and rms(ctl - ref)/rms(ref)), as the stored
+    full-size goldens carry it."""
+    got, ref = (np.asarray(a, np.float64) for a in (got, ref))
+    assert got.shape == ref.shape, (got.shape, ref.shape)
     assert np.isfinite(got).all(), f"{what}: non-finite output"
     r = rms(ref)
-    d, dc = np.abs(got - ref), np.abs(ctl - ref)
-    g_rms, c_rms = float(np.sqrt(np.mean(d * d)) / r), float(np.sqrt(np.mean(dc * dc)) / r)
-    g_max, c_max = float(d.max() / r), float(dc.max() / r)
+    d = np.abs(got - ref)
+    g_rms = float(np.sqrt(np.mean(d * d)) / r)
+    g_max = float(d.max() / r)
     max_bound = max(BF16_BOUND, CONTROL_FACTOR * c_max)
     rms_bound = max(BF16_BOUND, CONTROL_FACTOR * c_rms)
     print(f"{what}: max|d|/rms {g_max:.3e} (control {c_max:.3e}, bound {max_bound:.3e}, "
