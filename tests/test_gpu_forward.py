@@ -10,7 +10,7 @@ import torch
 
 import oracle as O
 import synthetic as S
-from gpu_util import assert_bf16_parity, assert_f32_close, rms
+from gpu_util import assert_bf16_parity, assert_bf16_parity_stats, assert_f32_close, rms
 from synthetic.configs import CondRow, Segment, scaled
 
 pytestmark = pytest.mark.gpu
@@ -252,35 +252,90 @@ def test_graph_replay_matches_eager(H, name):
         assert torch.equal(again, eager)
 
 
-def test_c3_full_size_sampled_parity(H):
-    """The single 6144-wide bf16 block at its full size (24,576 video + 2,048
-    audio tokens) against stored oracle values at 4,096 seeded positions
-    (tests/golden/make_samples.py runs the oracle and its fp32-accumulation
-    control arm on the CPU; nothing there comes from the GPU)."""
+def _golden(name):
+    """A stored oracle output (tests/golden/make_samples.py runs only the CPU
+    oracle and its fp32-accumulation control arm; nothing comes from the GPU)."""
     import json
     import os
-    path = os.path.join(os.path.dirname(__file__), "golden", "c3_block_bf16_samples.json")
-    gold = json.load(open(path))
-    cfg = S.get_config("c3")
-    assert gold["config"] == cfg.name
+    import sys
+    here = os.path.join(os.path.dirname(__file__), "golden")
+    if here not in sys.path:
+        sys.path.insert(0, here)
+    import make_samples
+    meta = json.load(open(os.path.join(here, f"{name}.json")))
+    arrays = np.load(os.path.join(here, f"{name}.npz"))
+    cfg = make_samples.GOLDENS[name]["cfg"]
+    assert meta["config"] == cfg.name and meta["n_tokens"] == cfg.n_tokens and meta["n_blocks"] == cfg.n_blocks
+    return cfg, meta, arrays
+
+
+def _check_golden(got, meta, arrays, what):
+    for k, t in meta["tensors"].items():
+        assert_bf16_parity_stats(got[k], arrays[k], t["control_max_rel"], t["control_rms_rel"], f"{what} {k}")
+
+
+def test_c3_full_size_rows_parity(H):
+    """The single 6144-wide bf16 block at its full size (24,576 video + 2,048
+    audio tokens): complete output rows at both ends of each document, on
+    either side of the 256-query attention tiles and the 256-row GEMM tiles,
+    and at seeded interior rows, against the stored oracle rows."""
+    cfg, meta, arrays = _golden("c3_block_bf16_rows")
     r, w, got = _run(H, cfg)
-    t = gold["tensors"]["x"]
-    assert list(got["x"].shape) == t["shape"]
-    idx = np.array(t["index"])
-    g = got["x"].reshape(-1)[idx]
-    assert_bf16_parity(g, np.array(t["value"]), np.array(t["control_value"]), "c3 full size (sampled)")
+    rows = meta["rows"]
+    _check_golden({"x": got["x"][rows]}, meta, arrays, "c3 full size (rows)")
 
 
-def test_c4_full_size_packed_equals_alone_and_deterministic(H):
+@pytest.fixture(scope="module")
+def model64(H):
+    """The 64-block bf16 DiT's weights, staged once for every test that runs it
+    (the benchmark's batch, the denoise configuration, the full-depth golden)."""
+    m = H.stage_model(S.get_config("c4"), 0, threads=16)
+    yield m
+    del m
+    torch.cuda.empty_cache()
+
+
+def test_c4_full_depth_parity(H, model64):
+    """The 64-block model at its full width and depth on four small documents
+    of both modalities (with the in/out projections), against the oracle's
+    whole output latents."""
+    cfg, meta, arrays = _golden("c4_full_depth_small_tokens")
+    r = H.Runner(cfg, 0, model=model64)
+    r.forward()
+    _check_golden(r.output_numpy(), meta, arrays, "c4 64 blocks, 112 tokens")
+    del r
+
+
+@pytest.mark.parametrize("name", ["c4_full_tokens_2blocks", "c5_full_tokens_2blocks_step0"])
+def test_full_token_layouts_parity(H, name):
+    """The benchmark's packed layouts at 18,432 tokens -- two requests of
+    8,192 video + 1,024 audio tokens in four documents, and one request of
+    16,384 + 2,048 at the first denoise step (timesteps sigma(0)) -- through
+    the first two blocks of the 64-block model's weights, whole output
+    latents against the oracle's."""
+    cfg, meta, arrays = _golden(name)
+    w = {}
+    m = H.stage_model(cfg, 0, threads=16)
+    r = H.Runner(cfg, 0, model=m)
+    cond = r.cond
+    if meta["t_rows"] is not None:
+        cond = torch.from_numpy(H.cond_rows(cfg, r.inp, meta["t_rows"])).cuda()
+    r.forward(cond=cond)
+    _check_golden(r.output_numpy(), meta, arrays, f"{name}")
+    del r, m, w
+    torch.cuda.empty_cache()
+
+
+def test_c4_full_size_packed_equals_alone_and_deterministic(H, model64):
     """The 64-block bf16 DiT at its benchmark size (18,432 tokens in four
-    documents), where no oracle forward fits: properties that hold at any size.
-    Each document's velocities from the packed forward equal, bit for bit, a
-    forward of that document alone (every GEMM row, attention document and
-    modulation row is independent of the rest of the batch); a repeated
-    forward is bit-identical; every output is finite."""
+    documents): properties that hold at any size.  Each document's velocities
+    from the packed forward equal, bit for bit, a forward of that document
+    alone (every GEMM row, attention document and modulation row is
+    independent of the rest of the batch); a repeated forward is
+    bit-identical; every output is finite."""
     import synthetic.gen as G
     cfg = S.get_config("c4")
-    m = H.stage_model(cfg, 0, threads=16)
+    m = model64
     r = H.Runner(cfg, 0, model=m)
     r.forward()
     torch.cuda.synchronize()
@@ -303,12 +358,12 @@ def test_c4_full_size_packed_equals_alone_and_deterministic(H):
         del ws
 
 
-def test_c5_full_size_denoise_loop_equals_steps(H):
+def test_c5_full_size_denoise_loop_equals_steps(H, model64):
     """The 50-step denoise configuration at its full size (64 blocks, 18,432
     tokens): the device loop over the first three steps equals three single
     steps bit for bit, the latents stay finite and move."""
     cfg = S.get_config("c5")
-    m = H.stage_model(cfg, 0, threads=16)
+    m = model64
     r = H.Runner(cfg, 0, model=m)
     cond_tab, dt_tab = _schedule_tables(H, cfg)
     n = 3
