@@ -50,10 +50,26 @@ typedef enum dit_status {
   DIT_E_UNSUPPORTED = 9     /* a shape outside what the kernels handle (message says which) */
 } dit_status;
 
-enum { DIT_F32 = 0, DIT_BF16 = 1, DIT_F64 = 2 /* residual stream of an fp32 model only */ };
+enum { DIT_F32 = 0, DIT_BF16 = 1, DIT_F64 = 2 /* residual stream of an fp32 model only */,
+       DIT_MXFP8 = 3 /* OCP E4M3 values with one E8M0 scale per 32 along K (dit_gemm, dit_quantize_mx8) */ };
+/* Format of the four block GEMMs of a bf16-stream model: the stream dtype, or
+ * MXFP8 re-quantized operands (weights at staging, activations before each
+ * GEMM) on the scaled fp8 matrix cores. */
+enum { DIT_GEMM_STREAM = 0, DIT_GEMM_MXFP8 = 1 };
 enum { DIT_NORM_RMS = 0, DIT_NORM_LAYER = 1 };
 enum { DIT_MLP_GATE_UP = 0, DIT_MLP_VALUE_GATE = 1 };
 enum { DIT_IO_NONE = 0, DIT_IO_PATCH3D = 1, DIT_IO_CHANNEL_MAJOR = 2 };
+/* Row layout of the fused qkv projection: [q_all | k_all | v_all] (the DiT's),
+ * or per head [q | k | v of head 0 | q | k | v of head 1 | ...] (the video VAE
+ * decoder's ViT; page "port the MiniMax-H3 omni-modal video+audio DiT", update
+ * "video-VAE decoder block ported": same size, a wrong reading raises no
+ * error).  A per-head weight is reordered at stage time. */
+enum { DIT_QKV_CONCAT = 0, DIT_QKV_PER_HEAD = 1 };
+/* Position grid of a modality's rotary angles: integer positions from 0, or
+ * per axis the centre of cell i of [-1, 1) split in n, (2i + 1)/n - 1, scaled
+ * by 2 pi (the ViT decoder's ND rotary embedding; same page, update "video-VAE
+ * ViT3D decoder complete"). */
+enum { DIT_ROPE_INTEGER = 0, DIT_ROPE_CENTERED = 1 };
 
 #define DIT_MAX_MODALITIES 4
 #define DIT_MAX_SEGMENTS 64
@@ -66,6 +82,7 @@ typedef struct dit_modality {
   int patch[3];    /* (pt, ph, pw) for DIT_IO_PATCH3D, else (1,1,1) */
   int n_axes;      /* 1 or 3 position axes */
   int axis_dim[3]; /* rotary sub-dimension per axis; sums to rot_dim; each even */
+  int rope_grid;   /* DIT_ROPE_* */
 } dit_modality;
 
 /* Model shape.  All fields are read at dit_model_create and copied. */
@@ -82,6 +99,13 @@ typedef struct dit_config {
   int n_mod;         /* modalities (one AdaLN linear and one projection pair each) */
   int io;            /* 1: latents in / velocities out through fp32 projections; 0: tokens in/out */
   dit_modality mod[DIT_MAX_MODALITIES];
+  int gemm_format;   /* DIT_GEMM_*: DIT_GEMM_MXFP8 needs a bf16 stream and hidden, ffn multiples of 128
+                        (the low-precision arm; page "port the MiniMax-H3 omni-modal video+audio DiT",
+                        update "NVFP4 arm grounded": the pages' is NVFP4, this GPU's matrix cores take MX) */
+  int qkv_layout;    /* DIT_QKV_* */
+  int qk_norm;       /* 1: q and k RMS-normalised over each head (eps norm_eps, no weight) before RoPE,
+                        as the ViT decoder block (same page, update "video-VAE decoder block ported");
+                        fp32 stream only */
 } dit_config;
 
 /* One document of a packed batch: a contiguous run of tokens of one modality
@@ -341,7 +365,9 @@ int dit_cfg_denoise_loop(dit_model* m, const dit_batch* b, float* latents_dev,
  * for a short workspace. */
 
 /* C[M,N] = A[M,K] . B[N,K]^T + bias[N] (bias may be NULL).  bf16: A, B bf16,
- * fp32 accumulation, C in c_dtype.  f32: A, B float32 (K a multiple of 4),
+ * fp32 accumulation, C in c_dtype.  DIT_MXFP8: A, B given as bf16, both
+ * re-quantized as dit_quantize_mx8 into ws, then multiplied on the scaled fp8
+ * matrix cores (K a multiple of 128), C in c_dtype.  f32: A, B float32 (K a multiple of 4),
  * each row scaled by a power of two and cut into five 7-bit integer slices,
  * the slice products summed exactly on the int8 matrix cores (pairs whose
  * weight is below 2^-32 of the product dropped), combined in fp64 and
@@ -374,6 +400,18 @@ int dit_gemm(int dtype, int M, int N, int K, const void* A, const void* B, const
 size_t dit_gemm_f32_noalloc_limit(void);
 int dit_gemm_f32_noalloc(int M, int N, int K, const float* A, const float* B, const float* bias, float* C,
                          dit_stream_t stream);
+
+/* MXFP8 re-quantization of bf16 rows x [R, K] (K a multiple of 32): codes
+ * [R, K] OCP E4M3 bytes, scales [R, K/32] E8M0 bytes.  Per 32 consecutive
+ * values the scale is the smallest power of two 2^s with max|v| <= 448 2^s
+ * (byte s + 127, s clamped to [-127, 127]), each value v 2^-s rounded to
+ * nearest-even E4M3 with its sign; an all-zero block takes byte 0, a block
+ * holding a NaN or an Inf byte 255 (NaN) and zero codes.  The pages' low-
+ * precision arm is NVFP4 (page "port the MiniMax-H3 omni-modal video+audio
+ * DiT", update "NVFP4 arm grounded": FP4 values, an E4M3 scale per 16 and an
+ * fp32 global scale); this GPU's matrix cores take MX block scales.  x and
+ * codes 16-byte aligned; device pointers; asynchronous. */
+int dit_quantize_mx8(int R, int K, const void* x, void* codes, void* scales, dit_stream_t stream);
 
 /* h[N,D] (dtype) = norm(x[N,D]) * (1 + mod[c][scale_k]) + mod[c][shift_k],
  * c = cond_idx[n]; mod [n_cond, 6, D] f32; which = 0 (msa: shift 0, scale 1) or

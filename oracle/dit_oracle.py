@@ -298,9 +298,11 @@ def rope_cache(cfg):
     cos = np.empty((n, half), np.float32)
     sin = np.empty((n, half), np.float32)
     freqs = [[rope_inv_freq(d, cfg.theta) for d in m.rope_axes] for m in cfg.modalities]
+    two_pi = 2.0 * math.pi
     row = 0
     for s in cfg.segments:
         fr = freqs[s.modality]
+        centered = getattr(cfg.modalities[s.modality], "rope_grid", "integer") == "centered"
         assert len(fr) == len(s.grid), "segment grid must have one extent per rope axis"
         assert sum(len(f) for f in fr) == half
         for _ in range(s.n_tokens):
@@ -309,7 +311,10 @@ def rope_cache(cfg):
             for a, fa in enumerate(fr):
                 pa = float(p[a])
                 for f in fa:
-                    ang = pa * f
+                    if centered:  # the ND rotary embedding's coordinates (``centered_rope_cache``)
+                        ang = (two_pi * ((2.0 * pa + 1.0) / s.grid[a] - 1.0)) * f
+                    else:
+                        ang = pa * f
                     cos[row, col] = math.cos(ang)
                     sin[row, col] = math.sin(ang)
                     col += 1
@@ -408,7 +413,29 @@ def linear(x: np.ndarray, W: np.ndarray, b: np.ndarray, accum: str = "fp64") -> 
     if accum == "fp32":
         y = np.asarray(x, np.float32) @ np.asarray(W, np.float32).T
         return y.astype(np.float64) + np.asarray(b, np.float64)
+    if accum == "mx_step":
+        return _linear_step_grid(x, W, b)
     return np.asarray(x, np.float64) @ np.asarray(W, np.float64).T + np.asarray(b, np.float64)
+
+
+def _linear_step_grid(x: np.ndarray, W: np.ndarray, b: np.ndarray, step: int = 64, bits: int = 16) -> np.ndarray:
+    """Control-arm accumulation for the MXFP8 mode only: K in steps of 64; each
+    step's products summed exactly, then rounded to the grid 2^(floor(log2 M) -
+    bits), M the step's sum of |products|; the steps accumulated in float32.
+    This is a second valid accumulation of the same exact products at the
+    precision class of a matrix core that adds a step's 64 products on an
+    aligned fixed-point grid (the op-level GPU test bounds the scaled fp8
+    instruction's error by 2^-14 of that magnitude sum)."""
+    x = np.asarray(x, np.float64)
+    W = np.asarray(W, np.float64)
+    acc = np.zeros((x.shape[0], W.shape[0]), np.float32)
+    for k0 in range(0, x.shape[1], step):
+        xs, ws = x[:, k0:k0 + step], W[:, k0:k0 + step]
+        p = xs @ ws.T
+        mag = np.abs(xs) @ np.abs(ws).T
+        q = np.exp2(np.frexp(np.where(mag > 0, mag, 1.0))[1] - 1.0 - bits)
+        acc = (acc + (np.rint(p / q) * q).astype(np.float32)).astype(np.float32)
+    return acc.astype(np.float64) + np.asarray(b, np.float64)
 
 
 def apply_rope(x: np.ndarray, cos: np.ndarray, sin: np.ndarray, rot: int) -> np.ndarray:

@@ -20,7 +20,7 @@ Shapes follow the workloads the pages describe:
     video tokens and 1-axis RoPE on audio tokens, at three batch shapes.
 """
 
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 from typing import Tuple
 
 
@@ -31,6 +31,7 @@ class Modality:
     channels: int                # latent channels C (0 when io == 'none')
     patch: Tuple[int, int, int]  # (pt, ph, pw) for 'patch3d'
     rope_axes: Tuple[int, ...]   # rotary sub-dimension per position axis; sums to rot_dim
+    rope_grid: str = "integer"   # 'integer' positions | 'centered' cell centres of [-1, 1) times 2 pi
 
     @property
     def token_width(self) -> int:
@@ -88,6 +89,9 @@ class DitConfig:
     denoise_steps: int = 0
     shifts: Tuple[float, ...] = field(default_factory=tuple)
     cfg_replicate_latent: bool = False  # segment j + P reads the latent of segment j (P = half the segments)
+    gemm: str = "stream"         # 'stream' | 'mxfp8': format of the four block GEMMs of a bf16 stream
+    qkv_layout: str = "concat"   # 'concat' [q_all | k_all | v_all] | 'per_head' [q k v of head 0 | ...]
+    qk_norm: bool = False        # per-head RMS norm of q and k (no weight) before RoPE
 
     @property
     def n_tokens(self) -> int:
@@ -148,8 +152,22 @@ C5 = DitConfig(
     cond_rows=(CondRow(0, 0), CondRow(1, 0)), n_requests=1, io=True,
     denoise_steps=50, shifts=(12.0, 3.0))
 
-CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5)}
-_SHORT = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5}
+# The 64-block model with its four block GEMMs on MXFP8 operands (the low-precision arm).
+C3_MX = replace(C3, name="c3_block_mxfp8", gemm="mxfp8")
+C4_MX = replace(C4, name="c4_full_mxfp8", gemm="mxfp8")
+
+# The video VAE decoder's ViT block at the pages' width (32 heads x 64, rotary
+# on 0.75 of each head split over 3 axes, theta 100, fp32): per-head qkv rows,
+# per-head q/k norm, centred coordinates.  The MLP width is a reading (4x).
+VIT = DitConfig(
+    name="vit3d_block_f32", key_id=6, model_id=6, n_blocks=1, hidden=2048, n_heads=32, head_dim=64, ffn=8192,
+    norm="rms", norm_eps=1e-6, mlp="gate_up", rot_dim=48, theta=100.0, stream="f32", cond_kind="vector",
+    cond_dim=4, modalities=(Modality("video", "none", 0, (1, 1, 1), (16, 16, 16), "centered"),),
+    segments=(Segment(0, (2, 8, 12), 0), Segment(0, (1, 4, 6), 0)),
+    cond_rows=(CondRow(0, 0),), n_requests=1, io=False, qkv_layout="per_head", qk_norm=True)
+
+CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5, C3_MX, C4_MX, VIT)}
+_SHORT = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5, "c3_mxfp8": C3_MX, "c4_mxfp8": C4_MX, "vit": VIT}
 
 
 def get_config(name: str) -> DitConfig:

@@ -184,3 +184,30 @@ def test_batch_beyond_the_gemm_offsets_is_rejected_before_any_device_call(dit):
     assert rc == 9, lib.dit_last_error()
     assert b"32-bit" in lib.dit_last_error()
     lib.dit_model_destroy(h)
+
+
+def test_centered_rope_cache_bit_exact(dit):
+    # the ViT decoder's centred 3-axis coordinates: the library's table equals
+    # the oracle's, and a single segment equals the stand-alone definition
+    cfg = S.get_config("vit")
+    c, s = dit.dit_rope_cache_build(cfg)
+    oc, os_ = O.rope_cache(cfg)
+    assert np.array_equal(c.view(np.uint32), oc.view(np.uint32))
+    assert np.array_equal(s.view(np.uint32), os_.view(np.uint32))
+    g = cfg.segments[0].grid
+    cc, ss = O.centered_rope_cache(g, cfg.modalities[0].rope_axes, cfg.theta)
+    n = cfg.segments[0].n_tokens
+    assert np.array_equal(cc.view(np.uint32), c[:n].view(np.uint32))
+    assert np.array_equal(ss.view(np.uint32), s[:n].view(np.uint32))
+
+
+def test_vit_config_validation(dit):
+    lib = dit.load()
+    good = S.get_config("vit")
+    c = dit.make_config(good)
+    n = ctypes.c_size_t()
+    assert lib.dit_weight_bytes(ctypes.byref(c), ctypes.byref(n)) == 0
+    for bad in (scaled(good, stream="bf16"),          # the q/k norm runs in the fp32 stream only
+                scaled(good, head_dim=48, n_heads=32, hidden=1536, rot_dim=48)):  # head lanes not a power of two
+        c = dit.make_config(bad)
+        assert lib.dit_weight_bytes(ctypes.byref(c), ctypes.byref(n)) != 0

@@ -27,7 +27,7 @@ def checker(tmp_path_factory):
         pytest.skip("g++ not available")
     exe = str(tmp_path_factory.mktemp("asan") / "host_builders_check")
     cmd = ["g++", "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-ffp-contract=off",
-           "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-pthread",
            f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
            os.path.join(CSRC, "host_builders.cpp"), os.path.join(ROOT, "tests", "host_check", "host_builders_check.cpp"),
            "-o", exe]

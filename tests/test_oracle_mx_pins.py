@@ -155,3 +155,20 @@ def test_zero_gate_block_identity_holds_in_mxfp8_mode(mode):
     b = O.block_forward(cfg, x, mod, w, 0, lay, cos, sin, "mxfp8")
     rel = np.abs(a - b).max() / np.sqrt(np.mean(a * a))
     assert 1e-3 < rel < 0.2   # the fp8 operands move the block, by the size of their rounding
+
+
+def test_mx_step_control_accumulation():
+    """The MXFP8 mode's control arm: exact on small-integer products, within
+    half a grid step (2^-17 of the step's magnitude sum) per 64-product step
+    plus the fp32 accumulation, and different from the exact product."""
+    rng = np.random.default_rng(9)
+    xi = rng.integers(-3, 4, (6, 256)).astype(np.float64)
+    wi = rng.integers(-3, 4, (5, 256)).astype(np.float64)
+    assert np.array_equal(O.linear(xi, wi, np.zeros(5), accum="mx_step"), xi @ wi.T)
+    x = rng.standard_normal((6, 256))
+    w = rng.standard_normal((5, 256))
+    got = O.linear(x, w, np.zeros(5), accum="mx_step")
+    exact = x @ w.T
+    mag = sum(np.abs(x[:, k:k + 64]) @ np.abs(w[:, k:k + 64]).T for k in range(0, 256, 64))
+    assert np.all(np.abs(got - exact) <= 2.0 ** -17 * mag + 4 * 2.0 ** -24 * mag)
+    assert np.abs(got - exact).max() > 0

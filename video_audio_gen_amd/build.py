@@ -25,7 +25,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdit.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["gemm.hip", "attention.hip", "elementwise.hip", "fused_f32.hip", "noalloc.hip"]
+HIP_SOURCES = ["gemm.hip", "attention.hip", "elementwise.hip", "fused_f32.hip", "noalloc.hip", "mx8.hip"]
 HOST_HIP_SOURCES = ["dit_api.cpp"]   # host code using the HIP runtime API
 HOST_SOURCES = ["host_builders.cpp"]  # plain C++, no HIP
 
@@ -58,7 +58,7 @@ def build(clean: bool = False, verbose: bool = False) -> str:
     for s in HOST_SOURCES:
         o = os.path.join(BUILD, s + ".o")
         jobs.append(["g++", "-O2", "-fPIC", "-std=c++17", "-ffp-contract=off", f"-I{INCLUDE}", f"-I{CSRC}",
-                     "-Wall", "-c", os.path.join(CSRC, s), "-o", o])
+                     "-Wall", "-pthread", "-c", os.path.join(CSRC, s), "-o", o])
     with ThreadPoolExecutor(min(8, len(jobs))) as ex:
         outs = list(ex.map(_run, jobs))
     if verbose:
@@ -67,7 +67,7 @@ def build(clean: bool = False, verbose: bool = False) -> str:
                 print(o)
     objs = [os.path.join(BUILD, s + ".o") for s in HIP_SOURCES + HOST_HIP_SOURCES + HOST_SOURCES]
     tmp = LIB + ".tmp"
-    _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs])
+    _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs, "-pthread"])
     os.replace(tmp, LIB)
     return LIB
 

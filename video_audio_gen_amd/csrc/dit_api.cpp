@@ -162,6 +162,19 @@ static int check_config(const dit_config* c) {
     return set_error(DIT_E_UNSUPPORTED, "fp32 stream needs ffn a multiple of 4 and <= 24576");
   }
   if (c->cond_dim % 4) return set_error(DIT_E_UNSUPPORTED, "cond_dim must be a multiple of 4");
+  if (c->qkv_layout != DIT_QKV_CONCAT && c->qkv_layout != DIT_QKV_PER_HEAD)
+    return set_error(DIT_E_INVALID, "config: qkv_layout %d", c->qkv_layout);
+  if (c->qk_norm != 0 && c->qk_norm != 1) return set_error(DIT_E_INVALID, "config: qk_norm %d", c->qk_norm);
+  if (c->qk_norm && bf) return set_error(DIT_E_UNSUPPORTED, "the q/k norm runs in the fp32 stream only");
+  if (c->qk_norm && c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128)
+    return set_error(DIT_E_UNSUPPORTED, "the q/k norm needs head_dim 32, 64 or 128");
+  for (int m = 0; m < c->n_mod; ++m)
+    if (c->mod[m].rope_grid != DIT_ROPE_INTEGER && c->mod[m].rope_grid != DIT_ROPE_CENTERED)
+      return set_error(DIT_E_INVALID, "config: modality %d rope_grid %d", m, c->mod[m].rope_grid);
+  if (c->gemm_format != DIT_GEMM_STREAM && c->gemm_format != DIT_GEMM_MXFP8)
+    return set_error(DIT_E_INVALID, "config: gemm_format %d", c->gemm_format);
+  if (c->gemm_format == DIT_GEMM_MXFP8 && (!bf || c->hidden % 128 || c->ffn % 128))
+    return set_error(DIT_E_UNSUPPORTED, "MXFP8 GEMMs need a bf16 stream and hidden, ffn multiples of 128");
   return DIT_OK;
 }
 
@@ -176,6 +189,13 @@ static int token_width(const dit_modality& m) {
 enum SlotKind { kBlockMat = 0, kBias = 1, kIsland = 2 };
 // Slot dtype of an fp32 GEMM weight: stored as its int8 slices (gemm_f32).
 constexpr int kSlicedF32 = 16;
+// Slot dtype of an MXFP8 GEMM weight [R, K]: E4M3 codes [R, K], then (256-byte
+// aligned) E8M0 scales [R, K/32].
+constexpr int kMx8 = 17;
+static size_t mx8_bytes(int64_t R, int64_t K) { return ((static_cast<size_t>(R * K) + 255) & ~size_t(255)) + R * K / 32; }
+static const uint8_t* mx8_scales(const void* w, int64_t R, int64_t K) {
+  return static_cast<const uint8_t*>(w) + ((static_cast<size_t>(R * K) + 255) & ~size_t(255));
+}
 
 struct Slot {
   std::string name;
@@ -193,6 +213,7 @@ struct BlockPtrs {
   const float* adaln_b[DIT_MAX_MODALITIES];
   const void *qkv_w, *out_w, *in_w, *mo_w;
   const float *qkv_b, *out_b, *in_b, *mo_b;
+  const uint8_t *qkv_s, *out_s, *in_s, *mo_s;  // MXFP8 weights: their E8M0 scales (else null)
 };
 
 struct dit_model {
@@ -217,9 +238,16 @@ static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 //   kRowsPairs32 (bf16 stream): groups of 64 rows [32 gate | 32 up] of the same
 //     32 features, so the GEMM that produces them can apply the SiLU gate in
 //     its epilogue (a wave holds both halves of a group).
-enum RowOrder { kRowsSwapHalves = 1, kRowsPairs32 = 2 };
+//   kRowsPerHead (qkv weight and bias, 3D rows): the source is laid out per
+//     head [q | k | v of head 0 | ...] (head_dim rows each), stored [q_all |
+//     k_all | v_all].
+enum RowOrder { kRowsSwapHalves = 1, kRowsPairs32 = 2, kRowsPerHead = 4 };
 
-static int64_t staged_source_row(int64_t r, int64_t rows, int order) {
+static int64_t staged_source_row(int64_t r, int64_t rows, int order, int64_t hd) {
+  if (order & kRowsPerHead) {
+    const int64_t D = rows / 3, part = r / D, hh = (r % D) / hd, d = r % hd;
+    return hh * 3 * hd + part * hd + d;
+  }
   int64_t q = r;  // row in [gate | up] order
   if (order & kRowsPairs32) {
     const int64_t g = r / 64, w = r % 64;
@@ -243,6 +271,7 @@ static void build_contract(const dit_config& c, std::vector<Slot>* slots, size_t
     s.row_order = order;
     const int64_t n = ndim == 1 ? s0 : s0 * s1;
     s.bytes = dtype == kSlicedF32 ? gemm_f32_slices_bytes(static_cast<int>(s0), static_cast<int>(s1))
+              : dtype == kMx8     ? mx8_bytes(s0, s1)
                                   : static_cast<size_t>(n) * (dtype == DIT_BF16 ? 2 : 4);
     s.offset = off;
     s.staged = false;
@@ -259,15 +288,17 @@ static void build_contract(const dit_config& c, std::vector<Slot>* slots, size_t
     }
   }
   const int in_order = (c.mlp == DIT_MLP_VALUE_GATE ? kRowsSwapHalves : 0) | (sd == DIT_BF16 ? kRowsPairs32 : 0);
-  const int gd = sd == DIT_BF16 ? DIT_BF16 : kSlicedF32;  // dtype of the GEMM weights
+  // dtype of the GEMM weights
+  const int gd = sd == DIT_BF16 ? (c.gemm_format == DIT_GEMM_MXFP8 ? kMx8 : DIT_BF16) : kSlicedF32;
   for (int b = 0; b < c.n_blocks; ++b) {
     const std::string p = "blocks." + std::to_string(b) + ".";
     for (int m = 0; m < c.n_mod; ++m) {
       add(p + "adaln." + std::to_string(m) + ".weight", 2, 6 * D, dt, sd, kBlockMat, false);
       add(p + "adaln." + std::to_string(m) + ".bias", 1, 6 * D, 0, DIT_F32, kBias, false);
     }
-    add(p + "attn.qkv.weight", 2, 3 * D, D, gd, kBlockMat, false);
-    add(p + "attn.qkv.bias", 1, 3 * D, 0, DIT_F32, kBias, false);
+    const int qkv_order = c.qkv_layout == DIT_QKV_PER_HEAD ? kRowsPerHead : 0;
+    add(p + "attn.qkv.weight", 2, 3 * D, D, gd, kBlockMat, qkv_order);
+    add(p + "attn.qkv.bias", 1, 3 * D, 0, DIT_F32, kBias, qkv_order);
     add(p + "attn.out.weight", 2, D, D, gd, kBlockMat, false);
     add(p + "attn.out.bias", 1, D, 0, DIT_F32, kBias, false);
     add(p + "mlp.in.weight", 2, 2 * F, D, gd, kBlockMat, in_order);
@@ -342,18 +373,19 @@ extern "C" int dit_stage_weights(dit_model* m, const dit_weight_view* views, int
     const int64_t count = sl.ndim == 1 ? sl.shape[0] : sl.shape[0] * sl.shape[1];
     const void* src = v.host;
     const bool sliced = sl.dtype == kSlicedF32;
+    const bool mx = sl.dtype == kMx8;
     const bool need_conv = v.dtype != sl.dtype || sl.row_order != 0;
     if (need_conv) {
       // rows gathered (and widened or rounded) into the slot dtype; a sliced
       // slot gathers float32 rows first and slices them below
-      conv.resize(sliced ? sizeof(float) * count : sl.bytes);
+      conv.resize(sliced || mx ? sizeof(float) * count : sl.bytes);
       const int64_t rows = sl.shape[0];
       const int64_t cols = sl.ndim == 1 ? 1 : sl.shape[1];
       for (int64_t r = 0; r < rows; ++r) {
-        const int64_t sr = staged_source_row(r, rows, sl.row_order);
+        const int64_t sr = staged_source_row(r, rows, sl.row_order, m->cfg.head_dim);
         for (int64_t c = 0; c < cols; ++c) {
           const int64_t di = r * cols + c, si = sr * cols + c;
-          if (sl.dtype == DIT_BF16 && !sliced) {
+          if (sl.dtype == DIT_BF16) {
             uint16_t b;
             if (v.dtype == DIT_BF16) b = static_cast<const uint16_t*>(v.host)[si];
             else b = host_f32_to_bf16(static_cast<const float*>(v.host)[si]);
@@ -371,6 +403,17 @@ extern "C" int dit_stage_weights(dit_model* m, const dit_weight_view* views, int
         }
       }
       src = conv.data();
+      if (mx) {
+        // an MXFP8 weight is re-quantized from the (bf16) values as given
+        sliced_buf.resize(sl.bytes);
+        uint8_t* codes = reinterpret_cast<uint8_t*>(sliced_buf.data());
+        const int64_t bad = host_quantize_mx8(sl.shape[0], sl.shape[1], reinterpret_cast<const float*>(conv.data()), codes,
+                                              codes + (mx8_scales(codes, sl.shape[0], sl.shape[1]) - codes));
+        if (bad >= 0)
+          return set_error(DIT_E_INVALID, "weight '%s': row %lld holds a NaN or an Inf (MXFP8 GEMM weights must be finite)",
+                           v.name, static_cast<long long>(bad));
+        src = sliced_buf.data();
+      }
       if (sliced) {
         sliced_buf.resize(sl.bytes);
         const int64_t bad = host_slice_rows(sl.shape[0], sl.shape[1], (sl.shape[1] + 31) / 32 * 32,
@@ -423,6 +466,12 @@ extern "C" int dit_stage_finalize(dit_model* m) {
     bp.in_b = reinterpret_cast<const float*>(ptr(p + "mlp.in.bias"));
     bp.mo_w = ptr(p + "mlp.out.weight");
     bp.mo_b = reinterpret_cast<const float*>(ptr(p + "mlp.out.bias"));
+    const bool mx = c.gemm_format == DIT_GEMM_MXFP8;
+    const int64_t D = c.hidden, F = c.ffn;
+    bp.qkv_s = mx ? mx8_scales(bp.qkv_w, 3 * D, D) : nullptr;
+    bp.out_s = mx ? mx8_scales(bp.out_w, D, D) : nullptr;
+    bp.in_s = mx ? mx8_scales(bp.in_w, 2 * F, D) : nullptr;
+    bp.mo_s = mx ? mx8_scales(bp.mo_w, D, F) : nullptr;
   }
   for (int mm = 0; mm < DIT_MAX_MODALITIES; ++mm) {
     const bool has = c.io && mm < c.n_mod;
@@ -501,7 +550,10 @@ static int check_gemm_shapes(const dit_config& c, int N, int max_seg_tokens) {
   const int D = c.hidden, F = c.ffn;
   const int shapes[4][2] = {{3 * D, D}, {D, D}, {2 * F, D}, {D, F}};
   for (const auto& sh : shapes) {
-    const bool ok = c.stream_dtype == DIT_BF16 ? gemm_bf16_supported(N, sh[0], sh[1]) : gemm_f32_supported(N, sh[0], sh[1]);
+    const bool ok = c.stream_dtype == DIT_BF16
+                        ? (c.gemm_format == DIT_GEMM_MXFP8 ? gemm_mx8_supported(N, sh[0], sh[1])
+                                                           : gemm_bf16_supported(N, sh[0], sh[1]))
+                        : gemm_f32_supported(N, sh[0], sh[1]);
     if (!ok)
       return set_error(DIT_E_UNSUPPORTED, "%s GEMM [%d x %d] x [%d x %d]^T of a %d-token batch is beyond the kernel's 32-bit offsets",
                        c.stream_dtype == DIT_BF16 ? "bf16" : "fp32", N, sh[1], sh[0], sh[1], N);
@@ -606,7 +658,7 @@ extern "C" int dit_batch_tables(const dit_batch* b, const int32_t** cu, const in
 // ============================================================================ workspace plan
 
 struct WsPlan {
-  size_t mod, x, h, big, qkvh, o, a, sl, gemm, tok, vtok, vel, total;
+  size_t mod, x, h, big, qkvh, o, a, sl, gemm, tok, vtok, vel, q8, q8s, total;
 };
 
 static size_t gemm_ws(const dit_config& c, int M, int N, int K) {
@@ -664,6 +716,10 @@ static WsPlan plan_ws(const dit_model* m, const dit_batch* b) {
   p.tok = take(tok);
   p.vtok = take(tok);
   p.vel = take(c.io ? sizeof(float) * b->latent_floats : 0);
+  // MXFP8 GEMMs: the re-quantized input of the current GEMM (K = D or F)
+  const bool mx = c.gemm_format == DIT_GEMM_MXFP8;
+  p.q8 = take(mx ? N * (D > F ? D : F) : 0);
+  p.q8s = take(mx ? N * (D > F ? D : F) / 32 : 0);
   p.total = off;
   return p;
 }
@@ -705,7 +761,18 @@ static int run_block_bf16(dit_model* m, int blk, float* x, const float* mod, con
   uint16_t* q = qkvh;
   uint16_t* k = qkvh + static_cast<size_t>(N) * D;
   uint16_t* v = qkvh + 2 * static_cast<size_t>(N) * D;
-  auto gemm = [&](int n, int kk, const void* A, const void* W, const float* bias, void* C, const GemmEpilogue& ep) {
+  // MXFP8 model: each GEMM's bf16 input is re-quantized (E4M3 + E8M0 per 32)
+  // into the workspace, then multiplied on the scaled fp8 matrix cores
+  const bool mx = c.gemm_format == DIT_GEMM_MXFP8;
+  uint8_t* q8 = reinterpret_cast<uint8_t*>(ws + p.q8);
+  uint8_t* q8s = reinterpret_cast<uint8_t*>(ws + p.q8s);
+  auto gemm = [&](int n, int kk, const void* A, const void* W, const uint8_t* Wsc, const float* bias, void* C,
+                  const GemmEpilogue& ep) -> hipError_t {
+    if (mx) {
+      const hipError_t e = quantize_mx8(N, kk, static_cast<const uint16_t*>(A), q8, q8s, s);
+      if (e != hipSuccess) return e;
+      return gemm_mx8(N, n, kk, q8, q8s, static_cast<const uint8_t*>(W), Wsc, bias, C, ep, s);
+    }
     return gemm_bf16(N, n, kk, static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W), bias, C, ep, s);
   };
   // The SiLU gate runs in the MLP-in GEMM's epilogue (the weight is staged in
@@ -717,14 +784,14 @@ static int run_block_bf16(dit_model* m, int blk, float* x, const float* mod, con
   const GemmEpilogue silu{kEpiSiluGate};
   // attention sub-layer
   if (!h_ready) DIT_HIP(modnorm(true, c.norm, c.norm_eps, N, D, false, x, mod, 0, b->cond_dev, h, s));
-  DIT_HIP(gemm(3 * D, D, h, w.qkv_w, w.qkv_b, big, to_bf16));
+  DIT_HIP(gemm(3 * D, D, h, w.qkv_w, w.qkv_s, w.qkv_b, big, to_bf16));
   DIT_HIP(rope_split(true, N, H, hd, c.rot_dim, big, b->cos_dev, b->sin_dev, q, k, v, s));
   DIT_HIP(attention_bf16(N, H, hd, b->n_segs, b->cu_dev, b->max_seqlen, q, k, v, o, s));
-  DIT_HIP(gemm(D, D, o, w.out_w, w.out_b, a, to_f32));
+  DIT_HIP(gemm(D, D, o, w.out_w, w.out_s, w.out_b, a, to_f32));
   // MLP sub-layer: the attention's gated residual and the MLP norm in one pass
   DIT_HIP(resid_modnorm(c.norm, c.norm_eps, N, D, x, a, mod, 0, mod, 1, b->cond_dev, h, s));
-  DIT_HIP(gemm(2 * F, D, h, w.in_w, w.in_b, qkvh, silu));
-  DIT_HIP(gemm(D, F, qkvh, w.mo_w, w.mo_b, a, to_f32));
+  DIT_HIP(gemm(2 * F, D, h, w.in_w, w.in_s, w.in_b, qkvh, silu));
+  DIT_HIP(gemm(D, F, qkvh, w.mo_w, w.mo_s, w.mo_b, a, to_f32));
   if (next_mod != nullptr)
     DIT_HIP(resid_modnorm(c.norm, c.norm_eps, N, D, x, a, mod, 1, next_mod, 0, b->cond_dev, h, s));
   else
@@ -759,7 +826,8 @@ static int run_block_f32(dit_model* m, int blk, double* x, const float* mod, con
   float* v = k + static_cast<size_t>(N) * D;
   float* o = reinterpret_cast<float*>(ws + p.o);
   DIT_HIP(gemm_f32_sliced(N, 3 * D, D, sl, w.qkv_w, part, s));
-  DIT_HIP(rope_part(N, H, hd, c.rot_dim, gemm_f32_split_groups(3 * D, D), part, w.qkv_b, b->cos_dev, b->sin_dev, q, k, v, s));
+  DIT_HIP(rope_part(N, H, hd, c.rot_dim, gemm_f32_split_groups(3 * D, D), part, w.qkv_b, b->cos_dev, b->sin_dev, q, k, v,
+                    c.qk_norm, c.norm_eps, s));
   DIT_HIP(attention_f32(N, H, hd, b->n_segs, b->cu_dev, b->max_seqlen, q, k, v, o, s));
   DIT_HIP(slice_rows(N, D, o, sl, s));
   DIT_HIP(gemm_f32_sliced(N, D, D, sl, w.out_w, part, s));
@@ -989,8 +1057,11 @@ extern "C" int dit_gemm_splits(int dtype, int N, int K, int* splits) {
 
 extern "C" int dit_gemm_workspace_bytes(int dtype, int M, int N, int K, size_t* bytes) {
   if (bytes == nullptr || M < 0 || N <= 0 || K <= 0) return set_error(DIT_E_INVALID, "dit_gemm_workspace_bytes: bad argument");
-  // f32: the slices of B, then the GEMM's own scratch (slices of A, split-K partials)
-  *bytes = dtype == DIT_BF16 ? gemm_bf16_ws_bytes(M, N, K) : gemm_f32_slices_bytes(N, K) + gemm_f32_ws_bytes(M, N, K);
+  // f32: the slices of B, then the GEMM's own scratch (slices of A, split-K partials);
+  // MXFP8: both operands re-quantized (codes, then scales)
+  *bytes = dtype == DIT_BF16    ? gemm_bf16_ws_bytes(M, N, K)
+           : dtype == DIT_MXFP8 ? (K % 32 ? 0 : mx8_bytes(M, K) + 256 + mx8_bytes(N, K))
+                                : gemm_f32_slices_bytes(N, K) + gemm_f32_ws_bytes(M, N, K);
   return DIT_OK;
 }
 
@@ -1006,6 +1077,24 @@ extern "C" int dit_gemm(int dtype, int M, int N, int K, const void* A, const voi
     DIT_HIP(gemm_bf16(M, N, K, static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), bias, C, ep, s));
     return DIT_OK;
   }
+  if (dtype == DIT_MXFP8) {
+    // A [M,K] and B [N,K] bf16, re-quantized to MXFP8 into ws, then the scaled fp8 GEMM
+    if (!gemm_mx8_supported(M, N, K)) return set_error(DIT_E_UNSUPPORTED, "dit_gemm mxfp8: K=%d must be a multiple of 128", K);
+    if (c_dtype != DIT_F32 && c_dtype != DIT_BF16) return set_error(DIT_E_INVALID, "dit_gemm: c_dtype");
+    const size_t need = mx8_bytes(M, K) + 256 + mx8_bytes(N, K);
+    if (ws_bytes < need) return set_error(DIT_E_WORKSPACE, "dit_gemm: workspace of %zu bytes, %zu needed", ws_bytes, need);
+    if (ws == nullptr) return set_error(DIT_E_INVALID, "dit_gemm: workspace is null");
+    if (M == 0) return DIT_OK;
+    uint8_t* qa = static_cast<uint8_t*>(ws);
+    uint8_t* qb = qa + align256(mx8_bytes(M, K));
+    const uint8_t* sa = mx8_scales(qa, M, K);
+    const uint8_t* sb = mx8_scales(qb, N, K);
+    DIT_HIP(quantize_mx8(M, K, static_cast<const uint16_t*>(A), qa, const_cast<uint8_t*>(sa), s));
+    DIT_HIP(quantize_mx8(N, K, static_cast<const uint16_t*>(B), qb, const_cast<uint8_t*>(sb), s));
+    const GemmEpilogue ep{c_dtype == DIT_F32 ? kEpiF32 : kEpiBf16};
+    DIT_HIP(gemm_mx8(M, N, K, qa, sa, qb, sb, bias, C, ep, s));
+    return DIT_OK;
+  }
   if (dtype != DIT_F32) return set_error(DIT_E_INVALID, "dit_gemm: dtype");
   if (c_dtype != DIT_F32) return set_error(DIT_E_INVALID, "dit_gemm f32: C must be f32");
   if (!gemm_f32_supported(M, N, K))
@@ -1017,6 +1106,17 @@ extern "C" int dit_gemm(int dtype, int M, int N, int K, const void* A, const voi
   if (M == 0) return DIT_OK;
   DIT_HIP(slice_rows(N, K, static_cast<const float*>(B), ws, s));
   DIT_HIP(gemm_f32(M, N, K, static_cast<const float*>(A), ws, bias, static_cast<float*>(C), static_cast<char*>(ws) + bsl, s));
+  return DIT_OK;
+}
+
+extern "C" int dit_quantize_mx8(int R, int K, const void* x, void* codes, void* scales, dit_stream_t stream) {
+  if (R < 0 || K <= 0 || K % 32) return set_error(DIT_E_INVALID, "dit_quantize_mx8: R=%d K=%d (K a multiple of 32)", R, K);
+  if (R > 0 && (x == nullptr || codes == nullptr || scales == nullptr))
+    return set_error(DIT_E_INVALID, "dit_quantize_mx8: null pointer");
+  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(codes)) & 15)
+    return set_error(DIT_E_INVALID, "dit_quantize_mx8: x and codes must be 16-byte aligned");
+  DIT_HIP(quantize_mx8(R, K, static_cast<const uint16_t*>(x), static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales),
+                       reinterpret_cast<hipStream_t>(stream)));
   return DIT_OK;
 }
 

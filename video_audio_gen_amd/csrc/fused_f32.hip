@@ -284,14 +284,23 @@ __global__ __launch_bounds__(1024) void silu_slice_kernel(int N, int F, int S, i
 // fastest: for q and k, vector pair j of the rotated half (columns 4j and
 // rot/2 + 4j) or two pass-through vectors; for v, columns 8j .. 8j+7.
 template <int SF>
+// qk_norm: q and k are first divided by the RMS of their head's hd values
+// (sqrt(mean + eps), fp64; page "port the MiniMax-H3 omni-modal video+audio
+// DiT", update "video-VAE decoder block ported": per-head RMS q/k norm without
+// weight).  A head's hd/8 threads are consecutive lanes of one wavefront and
+// reduce by butterfly shuffles; RoPE preserves the RMS, so norm-then-rotate
+// equals rotate-then-norm.
 __global__ __launch_bounds__(256) void rope_part_kernel(int N, int H, int hd, int rot, int S, int S_hi, int cb,
                                                        const double* __restrict__ part,
                                                        const float* __restrict__ bias,
                                                        const float* __restrict__ cosb,
                                                        const float* __restrict__ sinb, float* __restrict__ q,
-                                                       float* __restrict__ k, float* __restrict__ v) {
+                                                       float* __restrict__ k, float* __restrict__ v, int qk_norm,
+                                                       float eps) {
   const int tph = hd / 8;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  // whole heads are in or out of range (the total is a multiple of tph), so
+  // the shuffles below never read an exited lane of the thread's head
   if (t >= static_cast<int64_t>(N) * H * 3 * tph) return;
   const int j = static_cast<int>(t % tph);
   const int which = static_cast<int>((t / tph) % 3);
@@ -303,29 +312,46 @@ __global__ __launch_bounds__(256) void rope_part_kernel(int N, int H, int hd, in
   const int col0 = which * D + h * hd;
   const size_t src = static_cast<size_t>(n) * 3 * D + col0;
   float* d = (which == 0 ? q : which == 1 ? k : v) + (static_cast<size_t>(h) * N + n) * hd;
-  if (which < 2 && j < half / 4) {
-    const int i0 = j * 4, i1 = half + j * 4;
+  const bool rotary = which < 2 && j < half / 4;
+  // this thread's 8 values: dims i0..i0+3 and i1..i1+3 (a rotary pair), or
+  // i0..i0+7 (v, or q/k dims past rot)
+  const int i0 = rotary ? j * 4 : (which == 2 ? 8 * j : rot + 8 * (j - half / 4));
+  const int i1 = rotary ? half + j * 4 : i0 + 4;
+  float x1[4], x2[4];
+  sum_parts4g<SF>(part, S, S_hi, cb, MN, src + i0, bias, col0 + i0, x1);
+  sum_parts4g<SF>(part, S, S_hi, cb, MN, src + i1, bias, col0 + i1, x2);
+  double sc = 1.0;
+  if (qk_norm) {  // uniform
+    double ss = 0.0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss += double(x1[e]) * double(x1[e]) + double(x2[e]) * double(x2[e]);
+    for (int o = 1; o < tph; o <<= 1) ss += __shfl_xor(ss, o, 64);
+    if (which < 2) sc = 1.0 / sqrt(ss / hd + static_cast<double>(eps));
+  }
+  if (rotary) {
     const float4 c = *reinterpret_cast<const float4*>(cosb + static_cast<size_t>(n) * half + i0);
     const float4 sn = *reinterpret_cast<const float4*>(sinb + static_cast<size_t>(n) * half + i0);
-    const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
-    float x1[4], x2[4], o1[4], o2[4];
-    sum_parts4g<SF>(part, S, S_hi, cb, MN, src + i0, bias, col0 + i0, x1);
-    sum_parts4g<SF>(part, S, S_hi, cb, MN, src + i1, bias, col0 + i1, x2);
+    const float cc[4] = {c.x, c.y, c.z, c.w}, ssn[4] = {sn.x, sn.y, sn.z, sn.w};
+    float o1[4], o2[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      o1[e] = static_cast<float>(double(x1[e]) * double(cc[e]) - double(x2[e]) * double(ss[e]));
-      o2[e] = static_cast<float>(double(x2[e]) * double(cc[e]) + double(x1[e]) * double(ss[e]));
+      const double a = double(x1[e]) * sc, b = double(x2[e]) * sc;
+      o1[e] = static_cast<float>(a * double(cc[e]) - b * double(ssn[e]));
+      o2[e] = static_cast<float>(b * double(cc[e]) + a * double(ssn[e]));
     }
     vec16<float>::store(d + i0, o1);
     vec16<float>::store(d + i1, o2);
   } else {
-    // v, or the pass-through dims of q and k: two vectors copied
-    const int i0 = which == 2 ? 8 * j : rot + 8 * (j - half / 4);
-    float x1[4], x2[4];
-    sum_parts4g<SF>(part, S, S_hi, cb, MN, src + i0, bias, col0 + i0, x1);
-    sum_parts4g<SF>(part, S, S_hi, cb, MN, src + i0 + 4, bias, col0 + i0 + 4, x2);
+    // v, or the pass-through dims of q and k: copied (normalised for q, k)
+    if (sc != 1.0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x1[e] = static_cast<float>(double(x1[e]) * sc);
+        x2[e] = static_cast<float>(double(x2[e]) * sc);
+      }
+    }
     vec16<float>::store(d + i0, x1);
-    vec16<float>::store(d + i0 + 4, x2);
+    vec16<float>::store(d + i1, x2);
   }
 }
 
@@ -421,15 +447,16 @@ hipError_t silu_slice(int N, int F, F32Splits sg, const double* part, const floa
 }
 
 hipError_t rope_part(int N, int H, int hd, int rot, F32Splits sg, const double* part, const float* bias, const float* cos,
-                     const float* sin, float* q, float* k, float* v, hipStream_t s) {
+                     const float* sin, float* q, float* k, float* v, int qk_norm, float eps, hipStream_t s) {
   if (N == 0) return hipSuccess;
   if (!rope_split_supported(false, hd, rot) || bias == nullptr) return hipErrorInvalidValue;
+  if (qk_norm && (hd / 8) & (hd / 8 - 1)) return hipErrorInvalidValue;  // a head's lanes: a power of two
   LaunchScope scope_(kCntRopeSplit, s);
   const int64_t total = static_cast<int64_t>(N) * H * 3 * (hd / 8);
   const dim3 grid(static_cast<unsigned>((total + 255) / 256));
 #define DIT_L(SF_) \
   hipLaunchKernelGGL((rope_part_kernel<SF_>), grid, dim3(256), 0, s, N, H, hd, rot, S, sg.s_hi, sg.col_split, part, \
-                     bias, cos, sin, q, k, v)
+                     bias, cos, sin, q, k, v, qk_norm, eps)
   const int S = sg.s_lo;
   DIT_SF_CASES(DIT_L)
 #undef DIT_L

@@ -76,13 +76,24 @@ __device__ __forceinline__ void go_barrier() { asm volatile("s_barrier" ::: "mem
 // tails.  A 256x32 tile is 16 such instructions; wave w issues 4w .. 4w+3.
 // Instruction i covers LDS chunks 64i .. 64i+63 = rows 16i .. 16i+15, so lane l
 // fetches row 16i + l/4 at the logical chunk whose swizzled position is l%4.
-__global__ __launch_bounds__(gb::NT) void gemm_bf16_kernel(int M, int N, int K,
-                                                              const bf16_t* __restrict__ A,
-                                                              const bf16_t* __restrict__ B,
-                                                              const float* __restrict__ bias,
-                                                              void* __restrict__ Cv, GemmEpilogue ep,
-                                                              int tiles_m, int tiles_n, int banded) {
+//
+// MX (MXFP8) instantiation: A and B are OCP E4M3 bytes with one E8M0 scale per
+// 32 consecutive K values (Asc [M][K/32], Bsc [N][K/32]); a 128-byte tile row
+// is 128 K values, two k-steps of v_mfma_scale_f32_32x32x64_f8f6f4.  In that
+// instruction lane (r, g) (row r = lane % 32, g = lane / 32) supplies bytes
+// 0-15 from the step's first 32-value block and bytes 16-31 from its second
+// (any assignment inside a block works if A and B share it: lane g takes
+// values 16g .. 16g+15 of each block), and the scale of block g of row r.
+// Each lane loads its rows' four scales of a tile as one dword, a tile ahead.
+template <bool MX>
+__device__ __forceinline__ void gemm_tile_body(int M, int N, int K, const void* __restrict__ Av,
+                                               const void* __restrict__ Bv, const uint8_t* __restrict__ Asc,
+                                               const uint8_t* __restrict__ Bsc, const float* __restrict__ bias,
+                                               void* __restrict__ Cv, GemmEpilogue ep, int tiles_m, int tiles_n,
+                                               int banded) {
   using namespace gb;
+  // bytes of one operand row; a tile row is always BK * 2 = 128 bytes
+  const int rowb = MX ? K : 2 * K;
   __shared__ uint4 smem[STAGES * (BM + BN) * CPR];  // STAGES x (A + B): 128 KB at 2 x 64 or 4 x 32
   uint4* As = smem;
   uint4* Bs = smem + STAGES * BM * CPR;
@@ -119,10 +130,12 @@ __global__ __launch_bounds__(gb::NT) void gemm_bf16_kernel(int M, int N, int K,
 
   const int a_rows = M - m0 < BM ? M - m0 : BM;
   const int b_rows = N - n0 < BN ? N - n0 : BN;
+  const char* A = static_cast<const char*>(Av);
+  const char* B = static_cast<const char*>(Bv);
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16_t*>(A + static_cast<size_t>(m0) * K), 0, a_rows * K * 2, 0x00020000);
+      const_cast<char*>(A + static_cast<size_t>(m0) * rowb), 0, a_rows * rowb, 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16_t*>(B + static_cast<size_t>(n0) * K), 0, b_rows * K * 2, 0x00020000);
+      const_cast<char*>(B + static_cast<size_t>(n0) * rowb), 0, b_rows * rowb, 0x00020000);
   // Byte offset of this lane's chunk for instruction j of its wave: instruction
   // i covers rows (64/CPR) i .. (64/CPR) i + 64/CPR - 1.
   uint32_t voff[DMA_PER_WAVE];
@@ -131,7 +144,7 @@ __global__ __launch_bounds__(gb::NT) void gemm_bf16_kernel(int M, int N, int K,
     const int i = wave * DMA_PER_WAVE + j;
     const int row = (64 / CPR) * i + lane / CPR;
     const int c = gb_swz(row, lane % CPR) - row * CPR;  // logical chunk stored at position lane % CPR
-    voff[j] = static_cast<uint32_t>(row * K + c * 8) * 2u;
+    voff[j] = static_cast<uint32_t>(row * rowb + c * 16);
   }
 
   f32x16_t acc[TM][TN];
@@ -142,9 +155,9 @@ __global__ __launch_bounds__(gb::NT) void gemm_bf16_kernel(int M, int N, int K,
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-#define GB_DMA(stage, k0)                                                                               \
+#define GB_DMA(stage, kt_)                                                                              \
   {                                                                                                     \
-    const int soff = (k0) * 2;                                                                          \
+    const int soff = (kt_) * (BK * 2);                                                                  \
     _Pragma("unroll") for (int j = 0; j < DMA_PER_WAVE; ++j) {                                         \
       const int i = wave * DMA_PER_WAVE + j;                                                            \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(As + (stage) * BM * CPR + i * 64), 16,  \
@@ -154,8 +167,27 @@ __global__ __launch_bounds__(gb::NT) void gemm_bf16_kernel(int M, int N, int K,
     }                                                                                                   \
   }
 
-  const int KT = K / BK;
+  const int KT = MX ? K / (2 * BK) : K / BK;
   const int lr = lane & 31, lg = lane >> 5;
+  // MX: this lane's rows' scale dwords (4 blocks = one tile), a tile ahead
+  uint32_t sa[TM], sb[TN], nsa[TM], nsb[TN];
+  const int kb = K / 32;  // scale bytes per row
+  auto load_scales = [&](int kt_) {
+    if constexpr (MX) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        int r = m0 + wr + i * 32 + lr;
+        r = r < M ? r : M - 1;
+        nsa[i] = *reinterpret_cast<const uint32_t*>(Asc + static_cast<size_t>(r) * kb + 4 * kt_);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        int r = n0 + wc + j * 32 + lr;
+        r = r < N ? r : N - 1;
+        nsb[j] = *reinterpret_cast<const uint32_t*>(Bsc + static_cast<size_t>(r) * kb + 4 * kt_);
+      }
+    }
+  };
 
 // One BK tile of MFMAs from LDS stage `st`: the operands of k-step s+1 are
 // read while the 16 MFMAs of k-step s run.
@@ -183,10 +215,43 @@ __global__ __launch_bounds__(gb::NT) void gemm_bf16_kernel(int M, int N, int K,
     }                                                                                                   \
   }
 
+// MX: one tile is two k-steps of 64; a lane's 32-byte operand is logical
+// chunks 4s + g and 4s + 2 + g of its row (bytes 16g.. of each 32-value block).
+// Byte 2s + g of the scale dword is this lane's block of step s.
+typedef int mx_v4i __attribute__((ext_vector_type(4)));
+typedef int mx_v8i __attribute__((ext_vector_type(8)));
+#define GB_MX_OPER(base, row, s_)                                                                       \
+  __builtin_shufflevector(__builtin_bit_cast(mx_v4i, (base)[gb_swz((row), 4 * (s_) + lg)]),            \
+                          __builtin_bit_cast(mx_v4i, (base)[gb_swz((row), 4 * (s_) + 2 + lg)]), 0, 1, 2,  \
+                          3, 4, 5, 6, 7)
+#define GB_MX_MFMA(s_)                                                                                  \
+  _Pragma("unroll") for (int i = 0; i < TM; ++i)                                                       \
+    _Pragma("unroll") for (int j = 0; j < TN; ++j)                                                     \
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                                     \
+          xa[s_][i], xb[s_][j], acc[i][j], 0, 0, 0,                                                    \
+          static_cast<int>((sa[i] >> (8 * (2 * (s_) + lg))) & 0xFFu), 0,                               \
+          static_cast<int>((sb[j] >> (8 * (2 * (s_) + lg))) & 0xFFu));
+#define GB_COMPUTE_MX(st)                                                                               \
+  {                                                                                                     \
+    const uint4* a_ = As + (st) * BM * CPR;                                                             \
+    const uint4* b_ = Bs + (st) * BN * CPR;                                                             \
+    mx_v8i xa[2][TM], xb[2][TN];                                                                        \
+    _Pragma("unroll") for (int i = 0; i < TM; ++i) xa[0][i] = GB_MX_OPER(a_, wr + i * 32 + lr, 0);     \
+    _Pragma("unroll") for (int j = 0; j < TN; ++j) xb[0][j] = GB_MX_OPER(b_, wc + j * 32 + lr, 0);     \
+    _Pragma("unroll") for (int i = 0; i < TM; ++i) xa[1][i] = GB_MX_OPER(a_, wr + i * 32 + lr, 1);     \
+    _Pragma("unroll") for (int j = 0; j < TN; ++j) xb[1][j] = GB_MX_OPER(b_, wc + j * 32 + lr, 1);     \
+    GB_MX_MFMA(0)                                                                                       \
+    GB_MX_MFMA(1)                                                                                       \
+  }
+
   // Prologue: tiles 0 .. STAGES-2 in flight.
 #pragma unroll
   for (int p = 0; p < STAGES - 1; ++p)
-    if (p < KT) GB_DMA(p, p * BK)
+    if (p < KT) GB_DMA(p, p)
+  if constexpr (MX) {
+    static_assert(STAGES == 2, "the MX scale prefetch assumes two stages");
+    if (KT > 0) load_scales(0);
+  }
 
   for (int kt = 0; kt < KT; ++kt) {
     const int st = kt % STAGES;
@@ -203,7 +268,27 @@ __global__ __launch_bounds__(gb::NT) void gemm_bf16_kernel(int M, int N, int K,
       __builtin_amdgcn_s_waitcnt(GB_VMCNT(0));
 #undef GB_VMCNT
     go_barrier();  // every wave's part of tile kt is in LDS; stage (kt-1) is free
-    if (kt + STAGES - 1 < KT) GB_DMA((kt + STAGES - 1) % STAGES, (kt + STAGES - 1) * BK)
+    if (kt + STAGES - 1 < KT) GB_DMA((kt + STAGES - 1) % STAGES, kt + STAGES - 1)
+    if constexpr (MX) {
+      // tile kt's scales landed with the vmcnt(0) above; fetch tile kt+1's
+#pragma unroll
+      for (int i = 0; i < TM; ++i) sa[i] = nsa[i];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) sb[j] = nsb[j];
+      if (kt + 1 < KT) load_scales(kt + 1);
+      GB_COMPUTE_MX(st)
+      // Step 0's twelve operand reads, then step 0's MFMAs each followed by
+      // two reads of step 1's operands, then step 1's MFMAs.
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TM + TN), 0);
+#pragma unroll
+      for (int t = 0; t < TM * TN; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (t < TM + TN) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+#pragma unroll
+      for (int t = 0; t < TM * TN; ++t) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      continue;
+    }
     GB_COMPUTE(st)
     // Inside the block: the operand reads of k-step 0, then in each k-step the
     // MFMAs, the first TM+TN of them each followed by one operand read of the
@@ -219,6 +304,9 @@ __global__ __launch_bounds__(gb::NT) void gemm_bf16_kernel(int M, int N, int K,
     }
   }
 #undef GB_COMPUTE
+#undef GB_COMPUTE_MX
+#undef GB_MX_MFMA
+#undef GB_MX_OPER
 #undef GB_DMA
 
   // Epilogue: lane l of a 32x32 tile holds column l%32, rows 8*(e/4) + 4*(l/32) + e%4.
@@ -318,6 +406,23 @@ __global__ __launch_bounds__(gb::NT) void gemm_bf16_kernel(int M, int N, int K,
   }
 }
 
+__global__ __launch_bounds__(gb::NT) void gemm_bf16_kernel(int M, int N, int K, const bf16_t* __restrict__ A,
+                                                              const bf16_t* __restrict__ B,
+                                                              const float* __restrict__ bias,
+                                                              void* __restrict__ Cv, GemmEpilogue ep, int tiles_m,
+                                                              int tiles_n, int banded) {
+  gemm_tile_body<false>(M, N, K, A, B, nullptr, nullptr, bias, Cv, ep, tiles_m, tiles_n, banded);
+}
+
+__global__ __launch_bounds__(gb::NT) void gemm_mx8_kernel(int M, int N, int K, const uint8_t* __restrict__ A,
+                                                             const uint8_t* __restrict__ Asc,
+                                                             const uint8_t* __restrict__ B,
+                                                             const uint8_t* __restrict__ Bsc,
+                                                             const float* __restrict__ bias, void* __restrict__ Cv,
+                                                             GemmEpilogue ep, int tiles_m, int tiles_n, int banded) {
+  gemm_tile_body<true>(M, N, K, A, B, Asc, Bsc, bias, Cv, ep, tiles_m, tiles_n, banded);
+}
+
 // K a multiple of the 64-wide K tile; a 256-row tile of either operand must fit 32-bit buffer offsets.
 bool gemm_bf16_supported(int M, int N, int K) {
   return M >= 0 && N > 0 && K > 0 && K % gb::BK == 0 && static_cast<int64_t>(gb::BM) * K * 2 < (int64_t(1) << 31);
@@ -340,6 +445,25 @@ hipError_t gemm_bf16(int M, int N, int K, const uint16_t* A, const uint16_t* B, 
   const int nblk = banded ? (tiles_m * tiles_n + 127) / 128 * 128 : tiles_m * tiles_n;
   hipLaunchKernelGGL(gemm_bf16_kernel, dim3(nblk), dim3(gb::NT), 0, s, M, N, K, A, B,
                      bias, C, ep, tiles_m, tiles_n, banded);
+  return hipGetLastError();
+}
+
+bool gemm_mx8_supported(int M, int N, int K) {
+  return M >= 0 && N > 0 && K > 0 && K % (2 * gb::BK) == 0 && static_cast<int64_t>(gb::BM) * K < (int64_t(1) << 31);
+}
+
+hipError_t gemm_mx8(int M, int N, int K, const uint8_t* A, const uint8_t* Asc, const uint8_t* B, const uint8_t* Bsc,
+                    const float* bias, void* C, const GemmEpilogue& ep, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (ep.mode == kEpiSiluGate && N % 64 != 0) return hipErrorInvalidValue;
+  LaunchScope scope_(kCntGemmMx8, s);
+  const int tiles_m = (M + gb::BM - 1) / gb::BM, tiles_n = (N + gb::BN - 1) / gb::BN;
+  // tile order as the bf16 GEMM's, with A's bytes at one per value
+  const double a_bytes = 1.0 * M * K;
+  const int banded = tiles_n <= 32 || (a_bytes > 256.0 * (1 << 20) && tiles_n <= 96);
+  const int nblk = banded ? (tiles_m * tiles_n + 127) / 128 * 128 : tiles_m * tiles_n;
+  hipLaunchKernelGGL(gemm_mx8_kernel, dim3(nblk), dim3(gb::NT), 0, s, M, N, K, A, Asc, B, Bsc, bias, C, ep, tiles_m,
+                     tiles_n, banded);
   return hipGetLastError();
 }
 

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <thread>
 #include <vector>
 
 #include "dit.h"
@@ -61,7 +62,9 @@ extern "C" int dit_pack_layout(const dit_config* cfg, const dit_segment* segs, i
 // enables": the cos/sin tables are built on the host before any kernel.  Page
 // "port the MiniMax-H3 omni-modal video+audio DiT", update "video-VAE ViT3D
 // decoder complete": per-axis frequency blocks are concatenated, and the
-// rotate_half pairing (i, i + rot/2) tiles the concatenation twice.
+// rotate_half pairing (i, i + rot/2) tiles the concatenation twice; a
+// DIT_ROPE_CENTERED modality takes its angles from cell centres of [-1, 1)
+// scaled by 2 pi (the same update's length-normalized token ids).
 extern "C" int dit_rope_cache_build(const dit_config* cfg, const dit_segment* segs, int n_segs,
                                     float* cos_host, float* sin_host) {
   if (cfg == nullptr || segs == nullptr || cos_host == nullptr || sin_host == nullptr)
@@ -101,8 +104,16 @@ extern "C" int dit_rope_cache_build(const dit_config* cfg, const dit_segment* se
       }
       float* cr = cos_host + row * half;
       float* sr = sin_host + row * half;
+      const bool centered = cfg->mod[s.modality].rope_grid == DIT_ROPE_CENTERED;
       for (int j = 0; j < half; ++j) {
-        const double ang = static_cast<double>(pos[ax[j]]) * f[j];
+        double ang;
+        if (centered) {
+          // the centre of cell pos of [-1, 1) split in the axis' extent, times 2 pi
+          const double c = (2.0 * static_cast<double>(pos[ax[j]]) + 1.0) / static_cast<double>(s.grid[ax[j]]) - 1.0;
+          ang = (2.0 * M_PI * c) * f[j];
+        } else {
+          ang = static_cast<double>(pos[ax[j]]) * f[j];
+        }
         cr[j] = static_cast<float>(std::cos(ang));
         sr[j] = static_cast<float>(std::sin(ang));
       }
@@ -177,4 +188,75 @@ int64_t host_slice_rows(int64_t R, int64_t K, int64_t Kp, const float* X, int8_t
   }
   return -1;
 }
+
+// ---------------------------------------------------------------- MXFP8 weights
+// The staging-time twin of the device quantizer (mx8.hip): per 32 consecutive
+// K values, the smallest power-of-two scale 2^s with max|v| <= 448 2^s (E8M0
+// byte s + 127; byte 0 for an all-zero block), then each v 2^-s rounded to
+// nearest-even E4M3 (sign kept).  Every step is exact in float, so both sides
+// produce the same bytes.
+static uint8_t host_e4m3(float y) {
+  const uint8_t sgn = std::signbit(y) ? 0x80 : 0;
+  const float a = std::fabs(y);
+  if (a >= 448.0f) return sgn | 0x7E;
+  if (a < 0.015625f) return sgn | static_cast<uint8_t>(std::nearbyint(a * 512.0f));
+  uint32_t ua;
+  std::memcpy(&ua, &a, 4);
+  int e = static_cast<int>(ua >> 23) - 127;
+  uint32_t keep = (ua >> 20) & 7u;
+  const uint32_t rem = ua & 0xFFFFFu;
+  if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) ++keep;
+  if (keep == 8u) {
+    keep = 0;
+    ++e;
+  }
+  return sgn | static_cast<uint8_t>((static_cast<uint32_t>(e + 7) << 3) | keep);
+}
+
+static int64_t quantize_mx8_rows(int64_t r0, int64_t r1, int64_t K, const float* X, uint8_t* codes, uint8_t* scales) {
+  const int64_t kb = K / 32;
+  for (int64_t r = r0; r < r1; ++r) {
+    for (int64_t b = 0; b < kb; ++b) {
+      const float* v = X + r * K + b * 32;
+      float amax = 0.0f;
+      for (int i = 0; i < 32; ++i) {
+        if (!std::isfinite(v[i])) return r;
+        amax = std::fmax(amax, std::fabs(v[i]));
+      }
+      int s = 0;
+      uint8_t byte = 0;
+      if (amax > 0.0f) {
+        int ef;
+        const float f = std::frexp(amax, &ef);
+        s = ef - 1 - 8 + (f > 0.875f ? 1 : 0);
+        s = s < -127 ? -127 : (s > 127 ? 127 : s);
+        byte = static_cast<uint8_t>(s + 127);
+      }
+      scales[r * kb + b] = byte;
+      for (int i = 0; i < 32; ++i) codes[r * K + b * 32 + i] = host_e4m3(std::ldexp(v[i], -s));
+    }
+  }
+  return -1;
+}
+
+// Rows in parallel over the host's cores (each row is independent; the
+// result does not depend on the split).
+int64_t host_quantize_mx8(int64_t R, int64_t K, const float* X, uint8_t* codes, uint8_t* scales) {
+  unsigned nt = std::thread::hardware_concurrency();
+  nt = nt == 0 ? 1 : (nt > 16 ? 16 : nt);
+  if (R * K < (int64_t(1) << 22) || nt == 1) return quantize_mx8_rows(0, R, K, X, codes, scales);
+  std::vector<int64_t> bad(nt, -1);
+  std::vector<std::thread> pool;
+  const int64_t per = (R + nt - 1) / nt;
+  for (unsigned t = 0; t < nt; ++t) {
+    const int64_t r0 = per * t, r1 = r0 + per < R ? r0 + per : R;
+    if (r0 >= r1) break;
+    pool.emplace_back([=, &bad] { bad[t] = quantize_mx8_rows(r0, r1, K, X, codes, scales); });
+  }
+  for (auto& th : pool) th.join();
+  for (int64_t b : bad)
+    if (b >= 0) return b;  // threads cover rows in order: the first one found is the smallest
+  return -1;
+}
+
 }  // namespace dit

@@ -12,4 +12,8 @@ int set_error(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3
 // Returns -1, or the first row holding a NaN or an Inf (the output is then
 // incomplete and must not be used).
 int64_t host_slice_rows(int64_t R, int64_t K, int64_t Kp, const float* X, int8_t* out);
+// MXFP8 codes [R, K] and E8M0 scales [R, K/32] of a weight matrix (K a
+// multiple of 32), the same arithmetic as the device quantizer; returns -1, or
+// the first row holding a NaN or an Inf (output then incomplete).
+int64_t host_quantize_mx8(int64_t R, int64_t K, const float* X, uint8_t* codes, uint8_t* scales);
 }  // namespace dit

@@ -11,7 +11,8 @@ namespace dit {
 enum Counter {
   kCntGemmBf16 = 0, kCntGemmF32, kCntAttnBf16, kCntAttnF32, kCntModnorm, kCntRopeSplit,
   kCntSiluGate, kCntGatedResidual, kCntAdaln, kCntPatchIn, kCntPatchOut, kCntEuler,
-  kCntGemmF32Reduce, kCntConvert, kCntResidNormSlice, kCntSiluSlice, kCntCfgEuler, kCntResidModnorm, kCntNum
+  kCntGemmF32Reduce, kCntConvert, kCntResidNormSlice, kCntSiluSlice, kCntCfgEuler, kCntResidModnorm,
+  kCntGemmMx8, kCntQuantMx8, kCntNum
 };
 void count_launch(Counter c);
 
@@ -40,6 +41,13 @@ struct GemmEpilogue {
 };
 hipError_t gemm_bf16(int M, int N, int K, const uint16_t* A, const uint16_t* B, const float* bias,
                      void* C, const GemmEpilogue& ep, hipStream_t s);
+// MXFP8: A [M,K] and B [N,K] as E4M3 bytes, each with E8M0 scales [rows][K/32]
+// (quantize_mx8); K a multiple of 128; epilogues as gemm_bf16.
+hipError_t gemm_mx8(int M, int N, int K, const uint8_t* A, const uint8_t* Asc, const uint8_t* B, const uint8_t* Bsc,
+                    const float* bias, void* C, const GemmEpilogue& ep, hipStream_t s);
+bool gemm_mx8_supported(int M, int N, int K);
+// bf16 rows [R, K] (K a multiple of 32) -> E4M3 codes [R, K] + E8M0 scales [R, K/32]
+hipError_t quantize_mx8(int R, int K, const uint16_t* x, uint8_t* codes, uint8_t* scales, hipStream_t s);
 // f32: B is given as its int8 slices (slice_rows layout: 5 planes of
 // [Kp/32][N][32] int8, Kp = K rounded up to 32, then N int32 exponents, each
 // part 256-byte aligned); A is sliced into ws on the way.
@@ -100,8 +108,9 @@ hipError_t resid_norm_slice(int N, int D, F32Splits sg, const double* part, cons
                             const float* nmod, int norm_which, int norm, float eps, const int32_t* cond_idx, double* x,
                             void* slices, float* y, hipStream_t s);
 hipError_t silu_slice(int N, int F, F32Splits sg, const double* part, const float* bias, void* slices, hipStream_t s);
+// qk_norm: q and k RMS-normalised over each head (eps, no weight) before the rotation
 hipError_t rope_part(int N, int H, int hd, int rot, F32Splits sg, const double* part, const float* bias, const float* cos,
-                     const float* sin, float* q, float* k, float* v, hipStream_t s);
+                     const float* sin, float* q, float* k, float* v, int qk_norm, float eps, hipStream_t s);
 hipError_t widen_f32(int64_t n, const float* src, double* dst, hipStream_t s);
 hipError_t narrow_f64(int64_t n, const double* src, float* dst, hipStream_t s);
 // mod[b][c][j] = W[b][modality(c)][j] . e[c] + bias[b][modality(c)][j]

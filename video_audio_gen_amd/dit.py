@@ -24,7 +24,8 @@ LIB_PATH = os.path.join(HERE, "libdit.so")
 DIT_OK = 0
 STATUS = {0: "DIT_OK", 1: "DIT_E_INVALID", 2: "DIT_E_STATE", 3: "DIT_E_UNKNOWN_WEIGHT", 4: "DIT_E_SHAPE",
           5: "DIT_E_DTYPE", 6: "DIT_E_MISSING_WEIGHT", 7: "DIT_E_WORKSPACE", 8: "DIT_E_HIP", 9: "DIT_E_UNSUPPORTED"}
-DIT_F32, DIT_BF16, DIT_F64 = 0, 1, 2
+DIT_F32, DIT_BF16, DIT_F64, DIT_MXFP8 = 0, 1, 2, 3
+DIT_GEMM_STREAM, DIT_GEMM_MXFP8 = 0, 1
 DIT_NORM_RMS, DIT_NORM_LAYER = 0, 1
 DIT_MLP_GATE_UP, DIT_MLP_VALUE_GATE = 0, 1
 DIT_IO_NONE, DIT_IO_PATCH3D, DIT_IO_CHANNEL_MAJOR = 0, 1, 2
@@ -32,7 +33,7 @@ MAX_MOD = 4
 COUNTER_NAMES = ["gemm_bf16", "gemm_f32", "attention_bf16", "attention_f32", "modnorm", "rope_split",
                  "silu_gate", "gated_residual", "adaln", "patch_in", "patch_out", "euler",
                  "gemm_f32_reduce", "convert", "resid_norm_slice", "silu_slice", "cfg_euler",
-                 "resid_modnorm"]
+                 "resid_modnorm", "gemm_mx8", "quantize_mx8"]
 
 
 class DitError(RuntimeError):
@@ -44,7 +45,7 @@ class DitError(RuntimeError):
 
 class dit_modality(ctypes.Structure):
     _fields_ = [("io", ctypes.c_int), ("channels", ctypes.c_int), ("patch", ctypes.c_int * 3),
-                ("n_axes", ctypes.c_int), ("axis_dim", ctypes.c_int * 3)]
+                ("n_axes", ctypes.c_int), ("axis_dim", ctypes.c_int * 3), ("rope_grid", ctypes.c_int)]
 
 
 class dit_config(ctypes.Structure):
@@ -52,7 +53,8 @@ class dit_config(ctypes.Structure):
                 ("head_dim", ctypes.c_int), ("ffn", ctypes.c_int), ("norm", ctypes.c_int),
                 ("norm_eps", ctypes.c_float), ("mlp", ctypes.c_int), ("rot_dim", ctypes.c_int),
                 ("theta", ctypes.c_double), ("stream_dtype", ctypes.c_int), ("cond_dim", ctypes.c_int),
-                ("n_mod", ctypes.c_int), ("io", ctypes.c_int), ("mod", dit_modality * MAX_MOD)]
+                ("n_mod", ctypes.c_int), ("io", ctypes.c_int), ("mod", dit_modality * MAX_MOD),
+                ("gemm_format", ctypes.c_int), ("qkv_layout", ctypes.c_int), ("qk_norm", ctypes.c_int)]
 
 
 class dit_segment(ctypes.Structure):
@@ -97,6 +99,7 @@ _SIGS = {
     "dit_gemm_splits": [_I, _I, _I, ctypes.POINTER(_I)],
     "dit_gemm": [_I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _SZ, _P],
     "dit_gemm_f32_noalloc": [_I, _I, _I, _P, _P, _P, _P, _P],
+    "dit_quantize_mx8": [_I, _I, _P, _P, _P, _P],
     "dit_modnorm": [_I, _I, ctypes.c_float, _I, _I, _P, _I, _P, _I, _P, _P, _P],
     "dit_rope_split": [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P],
     "dit_attention": [_I, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P],
@@ -174,6 +177,9 @@ def make_config(spec) -> dit_config:
     c.cond_dim = spec.cond_dim
     c.n_mod = len(spec.modalities)
     c.io = 1 if spec.io else 0
+    c.gemm_format = DIT_GEMM_MXFP8 if getattr(spec, "gemm", "stream") == "mxfp8" else DIT_GEMM_STREAM
+    c.qkv_layout = 1 if getattr(spec, "qkv_layout", "concat") == "per_head" else 0
+    c.qk_norm = 1 if getattr(spec, "qk_norm", False) else 0
     for i, m in enumerate(spec.modalities):
         md = c.mod[i]
         md.io = {"none": DIT_IO_NONE, "patch3d": DIT_IO_PATCH3D, "channel_major": DIT_IO_CHANNEL_MAJOR}[m.io]
@@ -181,6 +187,7 @@ def make_config(spec) -> dit_config:
         for a in range(3):
             md.patch[a] = m.patch[a]
         md.n_axes = len(m.rope_axes)
+        md.rope_grid = 1 if getattr(m, "rope_grid", "integer") == "centered" else 0
         for a in range(md.n_axes):
             md.axis_dim[a] = m.rope_axes[a]
     return c
@@ -405,11 +412,17 @@ def _dt(t) -> int:
     raise TypeError(t.dtype)
 
 
-def dit_gemm(A, B, bias, C, stream=None):
-    """C[M,N] = A[M,K] . B[N,K]^T + bias."""
+def dit_quantize_mx8(x, codes, scales, stream=None):
+    """bf16 rows x [R, K] -> E4M3 codes [R, K] (uint8) and E8M0 scales [R, K/32] (uint8)."""
+    R, K = x.shape
+    _check(load().dit_quantize_mx8(R, K, _ptr(x), _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def dit_gemm(A, B, bias, C, stream=None, mxfp8=False):
+    """C[M,N] = A[M,K] . B[N,K]^T + bias (mxfp8: bf16 A, B re-quantized to MXFP8 first)."""
     M, K = A.shape
     N = B.shape[0]
-    dt = _dt(A)
+    dt = DIT_MXFP8 if mxfp8 else _dt(A)
     ws_bytes = ctypes.c_size_t()
     _check(load().dit_gemm_workspace_bytes(dt, M, N, K, ctypes.byref(ws_bytes)))
     ws = torch.empty(max(int(ws_bytes.value), 1), dtype=torch.uint8, device=A.device)
