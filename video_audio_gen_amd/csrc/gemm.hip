@@ -84,7 +84,8 @@ __device__ __forceinline__ void go_barrier() { asm volatile("s_barrier" ::: "mem
 // 0-15 from the step's first 32-value block and bytes 16-31 from its second
 // (any assignment inside a block works if A and B share it: lane g takes
 // values 16g .. 16g+15 of each block), and the scale of block g of row r.
-// Each lane loads its rows' four scales of a tile as one dword, a tile ahead.
+// The four scales of a row in a tile are one dword, staged through LDS with
+// the tile (one direct dword load per wave).
 template <bool MX>
 __device__ __forceinline__ void gemm_tile_body(int M, int N, int K, const void* __restrict__ Av,
                                                const void* __restrict__ Bv, const uint8_t* __restrict__ Asc,
@@ -94,9 +95,13 @@ __device__ __forceinline__ void gemm_tile_body(int M, int N, int K, const void* 
   using namespace gb;
   // bytes of one operand row; a tile row is always BK * 2 = 128 bytes
   const int rowb = MX ? K : 2 * K;
-  __shared__ uint4 smem[STAGES * (BM + BN) * CPR];  // STAGES x (A + B): 128 KB at 2 x 64 or 4 x 32
+  // STAGES x (A + B): 128 KB at 2 x 64 or 4 x 32; MX adds each stage's scale
+  // dwords of the A and B rows (STAGES x 2 KB)
+  constexpr int SC_CHUNKS = MX ? STAGES * (BM + BN) / 4 : 0;
+  __shared__ uint4 smem[STAGES * (BM + BN) * CPR + SC_CHUNKS];
   uint4* As = smem;
   uint4* Bs = smem + STAGES * BM * CPR;
+  uint32_t* Ss = reinterpret_cast<uint32_t*>(smem + STAGES * (BM + BN) * CPR);  // [stage][A rows | B rows]
 
   const int bid = blockIdx.x;
   int tm, tn;
@@ -155,6 +160,9 @@ __device__ __forceinline__ void gemm_tile_body(int M, int N, int K, const void* 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
+// MX: wave w also copies the scale dwords of tile kt_ of 64 rows -- A rows
+// 64w.. for w < 4, B rows 64(w-4).. otherwise -- to Ss[stage][row] (lane l's
+// dword lands at the instruction's LDS base + 4l).
 #define GB_DMA(stage, kt_)                                                                              \
   {                                                                                                     \
     const int soff = (kt_) * (BK * 2);                                                                  \
@@ -165,29 +173,27 @@ __device__ __forceinline__ void gemm_tile_body(int M, int N, int K, const void* 
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(Bs + (stage) * BN * CPR + i * 64), 16,  \
                                                voff[j], soff, 0, 0);                                   \
     }                                                                                                   \
+    if constexpr (MX)                                                                                   \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wave < 4 ? rsa : rsb,                                   \
+                                               (lds_ptr_t)(Ss + (stage) * (BM + BN) + 64 * wave), 4,   \
+                                               s_voff, 4 * (kt_), 0, 0);                               \
   }
 
   const int KT = MX ? K / (2 * BK) : K / BK;
   const int lr = lane & 31, lg = lane >> 5;
-  // MX: this lane's rows' scale dwords (4 blocks = one tile), a tile ahead
-  uint32_t sa[TM], sb[TN], nsa[TM], nsb[TN];
+  // MX: scale rows [M][K/32] bytes; a tile's four scales of a row are one
+  // dword.  Rows past M or N read as zero (their outputs are not stored).
   const int kb = K / 32;  // scale bytes per row
-  auto load_scales = [&](int kt_) {
-    if constexpr (MX) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        int r = m0 + wr + i * 32 + lr;
-        r = r < M ? r : M - 1;
-        nsa[i] = *reinterpret_cast<const uint32_t*>(Asc + static_cast<size_t>(r) * kb + 4 * kt_);
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        int r = n0 + wc + j * 32 + lr;
-        r = r < N ? r : N - 1;
-        nsb[j] = *reinterpret_cast<const uint32_t*>(Bsc + static_cast<size_t>(r) * kb + 4 * kt_);
-      }
-    }
-  };
+  __amdgpu_buffer_rsrc_t rsa = ra, rsb = rb;
+  uint32_t s_voff = 0;
+  if constexpr (MX) {
+    rsa = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(Asc + static_cast<size_t>(m0) * kb), 0, a_rows * kb,
+                                            0x00020000);
+    rsb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(Bsc + static_cast<size_t>(n0) * kb), 0, b_rows * kb,
+                                            0x00020000);
+    s_voff = static_cast<uint32_t>((64 * (wave & 3) + lane) * kb);
+  }
+  uint32_t sa[TM], sb[TN];
 
 // One BK tile of MFMAs from LDS stage `st`: the operands of k-step s+1 are
 // read while the 16 MFMAs of k-step s run.
@@ -248,10 +254,6 @@ typedef int mx_v8i __attribute__((ext_vector_type(8)));
 #pragma unroll
   for (int p = 0; p < STAGES - 1; ++p)
     if (p < KT) GB_DMA(p, p)
-  if constexpr (MX) {
-    static_assert(STAGES == 2, "the MX scale prefetch assumes two stages");
-    if (KT > 0) load_scales(0);
-  }
 
   for (int kt = 0; kt < KT; ++kt) {
     const int st = kt % STAGES;
@@ -270,16 +272,16 @@ typedef int mx_v8i __attribute__((ext_vector_type(8)));
     go_barrier();  // every wave's part of tile kt is in LDS; stage (kt-1) is free
     if (kt + STAGES - 1 < KT) GB_DMA((kt + STAGES - 1) % STAGES, kt + STAGES - 1)
     if constexpr (MX) {
-      // tile kt's scales landed with the vmcnt(0) above; fetch tile kt+1's
+      // tile kt's scale dwords: staged with its operands
+      const uint32_t* ss = Ss + st * (BM + BN);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) sa[i] = nsa[i];
+      for (int i = 0; i < TM; ++i) sa[i] = ss[wr + i * 32 + lr];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) sb[j] = nsb[j];
-      if (kt + 1 < KT) load_scales(kt + 1);
+      for (int j = 0; j < TN; ++j) sb[j] = ss[BM + wc + j * 32 + lr];
       GB_COMPUTE_MX(st)
-      // Step 0's twelve operand reads, then step 0's MFMAs each followed by
-      // two reads of step 1's operands, then step 1's MFMAs.
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TM + TN), 0);
+      // The scale and step 0's operand reads, then step 0's MFMAs each
+      // followed by two reads of step 1's operands, then step 1's MFMAs.
+      __builtin_amdgcn_sched_group_barrier(0x100, TM + TN + 2 * (TM + TN), 0);
 #pragma unroll
       for (int t = 0; t < TM * TN; ++t) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
