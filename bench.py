@@ -16,10 +16,11 @@ device time, from per-launch HIP events recorded on the launch stream during a
 second pass of K forwards; `cpu_baseline` times the CPU oracle on a bounded
 sample (a few blocks) of the same workload and scales it to a whole forward.
 
-`--extra c4` (the default) then frees the headline model and times the 64-block
-bf16 DiT (18,432 tokens in four documents, weights staged once) in a timed
-region of its own, reported under `extra.c4` with its own roofline: a second
-measured configuration, not part of the headline value.
+`--extra c4,c4_mxfp8` (the default) then frees the headline model and times the
+64-block bf16 DiT (18,432 tokens in four documents, weights staged once), and
+the same model with its block GEMMs on MXFP8 operands, each in a timed region
+of its own, reported under `extra.<name>` with its own roofline: further
+measured configurations, not part of the headline value.
 """
 
 from __future__ import annotations
@@ -36,12 +37,14 @@ if ROOT not in sys.path:
 
 METRIC = "ms per DiT forward + tokens/s at 1 GPU; % of MFMA / HBM peak"
 # MI355X published peaks.
-PEAK = {"mfma_f64": 78.6, "mfma_bf16": 2500.0, "mfma_f32": 157.3, "mfma_i8": 5000.0, "hbm_gbs": 8000.0,
+PEAK = {"mfma_f64": 78.6, "mfma_bf16": 2500.0, "mfma_f32": 157.3, "mfma_i8": 5000.0, "mfma_fp8": 5000.0,
+        "hbm_gbs": 8000.0,
         # the fp32 GEMM runs each fp32 product as 15 exact int8 slice products:
         # its ceiling in fp32 flop/s is the int8 MFMA peak / 15
         "mfma_i8_slices": 5000.0 / 15}
 GEMM_FAMILY_PEAK = {"gemm_f32": ("mfma_i8_slices", "int8 MFMA 5.0 POP/s / 15 slice products per fp32 product"),
                     "gemm_bf16": ("mfma_bf16", "bf16 MFMA"),
+                    "gemm_mx8": ("mfma_fp8", "fp8 MFMA (MXFP8 operands)"),
                     "attention_bf16": ("mfma_bf16", "bf16 MFMA")}
 
 
@@ -55,7 +58,8 @@ def _source_digest(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-KERNEL_SOURCE = {"gemm_f32": "video_audio_gen_amd/csrc/gemm.hip", "gemm_bf16": "video_audio_gen_amd/csrc/gemm.hip",
+KERNEL_SOURCE = {"gemm_f32": "video_audio_gen_amd/csrc/gemm_slices.hip", "gemm_bf16": "video_audio_gen_amd/csrc/gemm.hip",
+                 "gemm_mx8": "video_audio_gen_amd/csrc/gemm.hip",
                  "attention_bf16": "video_audio_gen_amd/csrc/attention.hip"}
 
 
@@ -111,7 +115,10 @@ def family_work(cfg, splits=None):
     islands = sum(2.0 * m * n * k for m, n, k in gemm_shapes(cfg, blocks=False))
     out = {
         # block GEMMs run in the stream dtype; the projections in and out are fp32
-        "gemm_bf16": (blocks if cfg.stream == "bf16" else 0.0, "flop"),
+        "gemm_bf16": (blocks if cfg.stream == "bf16" and cfg.gemm != "mxfp8" else 0.0, "flop"),
+        "gemm_mx8": (blocks if cfg.gemm == "mxfp8" else 0.0, "flop"),
+        # MXFP8: each GEMM input re-quantized (bf16 read, E4M3 + one scale byte per 32 written)
+        "quantize_mx8": ((L * N * (3 * D + F) * (2 + 1 + 1 / 32)) if cfg.gemm == "mxfp8" else 0.0, "byte"),
         "gemm_f32": ((islands if cfg.stream == "bf16" else blocks + islands), "flop"),
         "attention": (attention_flops(cfg), "flop"),
         # x read (f32) + h written: the first block's attention norm (every
@@ -332,14 +339,15 @@ def measure(cfg, steps, warmup, no_graph=False, protocol_loops=5):
             kernels[k] = {"GB/s": round(rate / 1e9, 1), "frac_hbm": round(rate / 1e9 / PEAK["hbm_gbs"], 4),
                           "avg_us": round(t / n * 1e3, 2)}
         else:
-            peak = PEAK["mfma_i8_slices"] if k == "gemm_f32" else (PEAK["mfma_bf16"] if k.endswith("bf16") else None)
+            peak = (PEAK["mfma_i8_slices"] if k == "gemm_f32" else PEAK["mfma_fp8"] if k == "gemm_mx8"
+                    else PEAK["mfma_bf16"] if k.endswith("bf16") else None)
             kernels[k] = {"TFLOP/s": round(rate / 1e12, 2), "avg_us": round(t / n * 1e3, 2)}
             if peak:
                 kernels[k]["frac_mfma"] = round(rate / 1e12 / peak, 4)
         log(f"  {k:16s} {kernels[k]}")
     fam = max(prof.items(), key=lambda kv: kv[1][1])[0]
     n_launch, fam_ms = prof[fam]
-    if fam in ("gemm_f32", "gemm_bf16"):
+    if fam in ("gemm_f32", "gemm_bf16", "gemm_mx8"):
         flops = work[fam][0] * steps
         peak_key, peak_note = GEMM_FAMILY_PEAK[fam]
         achieved = flops / (fam_ms * 1e-3) / 1e12
@@ -378,7 +386,7 @@ def main(argv=None):
                          "the FETCH_SIZE / WRITE_SIZE counters), then exit")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch every kernel from the host instead of replaying one captured HIP graph")
-    ap.add_argument("--extra", default="c4",
+    ap.add_argument("--extra", default="c4,c4_mxfp8",
                     help="comma-separated workloads timed after the headline one, each in its own timed "
                          "region, reported under their own keys ('none' for none)")
     ap.add_argument("--extra-steps", type=int, default=5)

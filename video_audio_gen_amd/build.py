@@ -25,7 +25,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdit.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["gemm.hip", "attention.hip", "elementwise.hip", "fused_f32.hip", "noalloc.hip", "mx8.hip"]
+HIP_SOURCES = ["gemm.hip", "gemm_slices.hip", "attention.hip", "elementwise.hip", "fused_f32.hip", "noalloc.hip",
+               "mx8.hip"]
 HOST_HIP_SOURCES = ["dit_api.cpp"]   # host code using the HIP runtime API
 HOST_SOURCES = ["host_builders.cpp"]  # plain C++, no HIP
 

@@ -91,4 +91,13 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Workgroup barrier without the memory fence of __syncthreads(): LDS written
+// by direct loads is covered by explicit vmcnt waits before it (the fence
+// would add vmcnt(0), i.e. also wait for the copies just issued for later
+// tiles), and the "memory" clobber keeps the compiler from moving LDS reads
+// across it.
+__device__ __forceinline__ void go_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 }  // namespace dit
