@@ -13,8 +13,9 @@ once", section "Speed").
 Prints one JSON line.  `value` is tokens per second (tokens of the batch /
 seconds per forward); `roofline` reports the kernel family that takes the most
 device time, from per-launch HIP events recorded on the launch stream during a
-second pass of K forwards; `cpu_baseline` times the CPU oracle on a bounded
-sample (a few blocks) of the same workload and scales it to a whole forward.
+second pass of K forwards; `cpu_baseline` times the CPU oracle: for an fp32
+workload one whole forward on one host thread (as the pages time theirs), for
+a bf16 one a bounded sample of blocks on all host threads, scaled to a forward.
 
 `--extra c4,c4_mxfp8` (the default) then frees the headline model and times the
 64-block bf16 DiT (18,432 tokens in four documents, weights staged once), and
@@ -202,6 +203,32 @@ def cpu_baseline(cfg, weights_fn, islands, inp, sample_blocks: int, log=log, min
                       f"{cfg.n_blocks}-block forward ({per_forward:.1f}s)"}
 
 
+def cpu_whole_forward(cfg, inp, log=log):
+    """Time one whole forward of the oracle (every block, the projections in
+    and out) on one host thread, the way the pages time their host reference
+    (page "the 2.4B fp32 DiT onto the device, staged once", section "Speed":
+    a single-threaded CPU forward).  The block weights are generated before the
+    clock starts."""
+    import numpy as np
+    import oracle as O
+    import synthetic as S
+    from threadpoolctl import threadpool_limits
+
+    t0 = time.perf_counter()
+    ws = [S.block_weights(cfg, b, threads=8) for b in range(cfg.n_blocks)]
+    isl = S.island_weights(cfg) if cfg.io else None
+    log(f"cpu oracle: generated {cfg.n_blocks} blocks of weights in {time.perf_counter() - t0:.1f}s")
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        out = O.forward(cfg, lambda b: ws[b], isl, inp, threads=1)
+        dt = time.perf_counter() - t0
+    assert all(np.isfinite(v).all() for v in out.values())
+    log(f"cpu oracle: one whole {cfg.n_blocks}-block forward on one thread in {dt:.2f}s")
+    return {"value": cfg.n_tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"one whole {cfg.n_blocks}-block forward with the in/out projections (fp64 numpy, "
+                      f"one thread, {cfg.n_tokens} tokens): {dt:.2f}s"}
+
+
 def measure(cfg, steps, warmup, no_graph=False, protocol_loops=5):
     """Stage `cfg`'s weights, time `steps` forwards (or denoise steps) after
     `warmup`, then a per-kernel pass; returns the measurements and the runner."""
@@ -381,6 +408,9 @@ def main(argv=None):
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-blocks", type=int, default=4)
+    ap.add_argument("--cpu-sampled", action="store_true",
+                    help="time the oracle on a few blocks with all host threads and scale to a forward "
+                         "(the default for an fp32 workload is one whole forward on one thread)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device five times (the known-size kernel that scales "
                          "the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -420,8 +450,11 @@ def main(argv=None):
     cpu = None
     if not a.no_cpu_baseline:
         import oracle  # noqa: F401
-        cpu = cpu_baseline(cfg, lambda b: S.block_weights(cfg, b, threads=8), None, r.inp,
-                           min(a.cpu_sample_blocks, cfg.n_blocks))
+        if cfg.stream == "f32" and not a.cpu_sampled:
+            cpu = cpu_whole_forward(cfg, r.inp)
+        else:
+            cpu = cpu_baseline(cfg, lambda b: S.block_weights(cfg, b, threads=8), None, r.inp,
+                               min(a.cpu_sample_blocks, cfg.n_blocks))
 
     tokens = cfg.n_tokens
     line = {
@@ -457,7 +490,7 @@ def main(argv=None):
             ecfg = S.get_config(w)
             e = measure(ecfg, a.extra_steps, a.extra_warmup, a.no_graph, protocol_loops=0)
             line["extra"][w] = {
-                "workload": ecfg.name, "dtype": "f32" if ecfg.stream == "f32" else "bf16",
+                "workload": ecfg.name, "dtype": "f32" if ecfg.stream == "f32" else ("mxfp8" if ecfg.gemm == "mxfp8" else "bf16"),
                 "ms_per_forward" if not e["loop"] else "ms_per_step": round(e["ms"], 4),
                 "tokens_per_s": round(ecfg.n_tokens / (e["ms"] * 1e-3), 2),
                 "steps": a.extra_steps, "warmup": a.extra_warmup, "launch": e["launch"],
