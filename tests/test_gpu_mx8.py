@@ -61,6 +61,29 @@ def test_quantize_mx8_bit_exact(dit, R, K):
     assert np.array_equal(codes.cpu().numpy(), codes_o)
 
 
+def test_quantize_mx8_every_bf16_value(dit):
+    """Every bf16 bit pattern (NaNs and infinities included) through the device
+    quantizer, bit for bit against the oracle: in blocks of 32 consecutive
+    patterns (each block's values share a binade, so they land on the upper
+    E4M3 codes), in blocks shifted by 16 patterns (straddling binades), and in
+    a seeded shuffle (mixed magnitudes: the small values of a block fall into
+    the E4M3 subnormals and to signed zeros).  The device encodes with the
+    hardware fp8 conversion; this pins it to the nearest-even definition."""
+    pats = np.arange(65536, dtype=np.uint32) << 16
+    with np.errstate(invalid="ignore"):
+        vals = pats.view(np.float32).astype(np.float64)
+    rng = np.random.default_rng(7)
+    x = np.concatenate([vals, np.roll(vals, 16), vals[rng.permutation(65536)]]).reshape(-1, 128)
+    codes_o, scales_o = O.quantize_mx8(x)
+    xd = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).cuda()
+    codes = torch.empty(x.shape, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(x.shape[0], x.shape[1] // 32, dtype=torch.uint8, device="cuda")
+    dit.dit_quantize_mx8(xd, codes, scales)
+    torch.cuda.synchronize()
+    assert np.array_equal(scales.cpu().numpy(), scales_o)
+    assert np.array_equal(codes.cpu().numpy(), codes_o)
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 64, 128), (300, 320, 256), (513, 768, 384), (65, 97, 128),
                                    (26624 // 8, 18432 // 8, 6144), (200, 6144, 16384)])
 def test_gemm_mx8(dit, M, N, K):

@@ -12,6 +12,7 @@
 // output projection reads).
 #include "common.h"
 #include "kernels.h"
+#include "mx8.h"
 
 namespace dit {
 
@@ -85,7 +86,8 @@ __global__ __launch_bounds__(ab::NT, 1) void attention_bf16_kernel(int N, int H,
                                                                       const bf16_t* __restrict__ k,
                                                                       const bf16_t* __restrict__ v,
                                                                       bf16_t* __restrict__ o,
-                                                                      float scale_log2) {
+                                                                      float scale_log2, uint8_t* __restrict__ o8,
+                                                                      uint8_t* __restrict__ o8s) {
   using namespace ab;
   __shared__ uint4 smem[4 * TILE];  // K[2] then V[2]: 64 KB
   uint4* const Kb = smem;
@@ -299,7 +301,32 @@ __global__ __launch_bounds__(ab::NT, 1) void attention_bf16_kernel(int N, int H,
   for (int qb = 0; qb < QB; ++qb) {
     const float inv = 1.0f / ab_pair_sum(l_run[qb]);
     const int qi = q0 + wave * QW + qb * 32 + lr;
-    if (qi < len) {
+    if (qi < len && o8 != nullptr) {
+      // MXFP8 output (codes [N][D], scales [N][D/32]): the bf16 values a
+      // stored o would hold, quantized per 32 dims; the lane holds 16 of the
+      // block's values and its partner lane l^32 the other 16.
+      uint8_t* op = o8 + static_cast<size_t>(s0 + qi) * D + h * HD + 4 * lg;
+#pragma unroll
+      for (int i = 0; i < HD / 32; ++i) {
+        float f[16];
+        float am = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          f[e] = static_cast<float>(static_cast<__bf16>(acc[qb][i][e] * inv));  // as ab_pack rounds
+          am = nan_max(am, fabsf(f[e]));
+        }
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(am), __float_as_uint(am), false, false);
+        am = nan_max(__uint_as_float(r[0]), __uint_as_float(r[1]));
+        int div;
+        const uint32_t sb = mx_scale(am, &div);
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          *reinterpret_cast<uint32_t*>(op + i * 32 + 8 * e4) =
+              mx_code4(f[4 * e4], f[4 * e4 + 1], f[4 * e4 + 2], f[4 * e4 + 3], sb, div);
+        }
+        if (lg == 0) o8s[static_cast<size_t>(s0 + qi) * (D / 32) + (h * HD) / 32 + i] = static_cast<uint8_t>(sb);
+      }
+    } else if (qi < len) {
       bf16_t* op = o + static_cast<size_t>(s0 + qi) * D + h * HD + 4 * lg;
 #pragma unroll
       for (int i = 0; i < HD / 32; ++i)
@@ -508,7 +535,7 @@ bool attention_supported(bool bf16, int hd) {
 
 hipError_t attention_bf16(int N, int H, int hd, int n_docs, const int32_t* cu, int max_seqlen,
                           const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
-                          hipStream_t s) {
+                          hipStream_t s, uint8_t* o8, uint8_t* o8s) {
   if (N == 0 || n_docs == 0 || max_seqlen == 0) return hipSuccess;
   LaunchScope scope_(kCntAttnBf16, s);
   const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(hd));
@@ -517,7 +544,7 @@ hipError_t attention_bf16(int N, int H, int hd, int n_docs, const int32_t* cu, i
   if (work > (int64_t(1) << 30)) return hipErrorInvalidValue;
   const int blocks = static_cast<int>((work + 255) / 256 * 256);  // whole runs of 8 XCDs x 32 CUs
   hipLaunchKernelGGL(attention_bf16_kernel, dim3(blocks), dim3(ab::NT), 0, s, N, H, n_docs, qtiles,
-                     static_cast<int>(work), cu, q, k, v, o, scale_log2);
+                     static_cast<int>(work), cu, q, k, v, o, scale_log2, o8, o8s);
   return hipGetLastError();
 }
 

@@ -680,10 +680,11 @@ static WsPlan plan_ws(const dit_model* m, const dit_batch* b) {
   // residual stream: float32 (bf16 stream, with io) or float64 (fp32 stream)
   p.x = take(c.stream_dtype == DIT_BF16 ? (c.io ? sizeof(float) * N * D : 0) : sizeof(double) * N * D);
   const bool bf = c.stream_dtype == DIT_BF16;
-  p.h = take(bf ? es * N * D : 0);
+  const bool mx = c.gemm_format == DIT_GEMM_MXFP8;  // h and o then live in q8 (MXFP8) only
+  p.h = take(bf && !mx ? es * N * D : 0);
   p.big = take(bf ? es * N * 3 * D : 0);  // the QKV GEMM's output (MLP-in's is consumed in its epilogue)
   p.qkvh = take(es * N * (3 * D > F ? 3 * D : F));
-  p.o = take(es * N * D);
+  p.o = take(mx ? 0 : es * N * D);
   p.a = take(sizeof(float) * N * D);
   const int Ni = static_cast<int>(N);
   const bool f32 = !bf;
@@ -716,8 +717,7 @@ static WsPlan plan_ws(const dit_model* m, const dit_batch* b) {
   p.tok = take(tok);
   p.vtok = take(tok);
   p.vel = take(c.io ? sizeof(float) * b->latent_floats : 0);
-  // MXFP8 GEMMs: the re-quantized input of the current GEMM (K = D or F)
-  const bool mx = c.gemm_format == DIT_GEMM_MXFP8;
+  // MXFP8 GEMMs: the input of the current GEMM in MXFP8 (h, o, h2: K = D; m: K = F)
   p.q8 = take(mx ? N * (D > F ? D : F) : 0);
   p.q8s = take(mx ? N * (D > F ? D : F) / 32 : 0);
   p.total = off;
@@ -761,37 +761,56 @@ static int run_block_bf16(dit_model* m, int blk, float* x, const float* mod, con
   uint16_t* q = qkvh;
   uint16_t* k = qkvh + static_cast<size_t>(N) * D;
   uint16_t* v = qkvh + 2 * static_cast<size_t>(N) * D;
-  // MXFP8 model: each GEMM's bf16 input is re-quantized (E4M3 + E8M0 per 32)
-  // into the workspace, then multiplied on the scaled fp8 matrix cores
+  // MXFP8 model: the inputs of the QKV, O and MLP-in GEMMs (h, o, h2) are
+  // written in MXFP8 (E4M3 codes + E8M0 per 32) by the kernels that produce
+  // them -- the norms and the attention -- with the values a quantization of
+  // their bf16 form gives; m, which the MLP-in GEMM's SiLU epilogue writes in
+  // bf16, is quantized by its own kernel (quantizing inside the GEMM epilogue
+  // measured slower: its ALU work runs while the matrix cores idle).  All go
+  // to q8 / q8s, each consumed by the GEMM after it.
   const bool mx = c.gemm_format == DIT_GEMM_MXFP8;
   uint8_t* q8 = reinterpret_cast<uint8_t*>(ws + p.q8);
   uint8_t* q8s = reinterpret_cast<uint8_t*>(ws + p.q8s);
-  auto gemm = [&](int n, int kk, const void* A, const void* W, const uint8_t* Wsc, const float* bias, void* C,
-                  const GemmEpilogue& ep) -> hipError_t {
-    if (mx) {
-      const hipError_t e = quantize_mx8(N, kk, static_cast<const uint16_t*>(A), q8, q8s, s);
-      if (e != hipSuccess) return e;
-      return gemm_mx8(N, n, kk, q8, q8s, static_cast<const uint8_t*>(W), Wsc, bias, C, ep, s);
-    }
-    return gemm_bf16(N, n, kk, static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W), bias, C, ep, s);
-  };
   // The SiLU gate runs in the MLP-in GEMM's epilogue (the weight is staged in
   // [32 gate | 32 up] row groups), which writes m = silu(g) * u and never u:
   // every value is the one the separate kernel produces from a stored u.
   float* a = reinterpret_cast<float*>(ws + p.a);
   const GemmEpilogue to_bf16{kEpiBf16};
   const GemmEpilogue to_f32{kEpiF32};
+  if (mx) {
+    const GemmEpilogue silu{kEpiSiluGate};
+    // attention sub-layer
+    if (!h_ready) DIT_HIP(modnorm_mx8(c.norm, c.norm_eps, N, D, x, mod, 0, b->cond_dev, q8, q8s, s));
+    DIT_HIP(gemm_mx8(N, 3 * D, D, q8, q8s, static_cast<const uint8_t*>(w.qkv_w), w.qkv_s, w.qkv_b, big, to_bf16, s));
+    DIT_HIP(rope_split(true, N, H, hd, c.rot_dim, big, b->cos_dev, b->sin_dev, q, k, v, s));
+    DIT_HIP(attention_bf16(N, H, hd, b->n_segs, b->cu_dev, b->max_seqlen, q, k, v, o, s, q8, q8s));
+    DIT_HIP(gemm_mx8(N, D, D, q8, q8s, static_cast<const uint8_t*>(w.out_w), w.out_s, w.out_b, a, to_f32, s));
+    // MLP sub-layer
+    DIT_HIP(resid_modnorm_mx8(c.norm, c.norm_eps, N, D, x, a, mod, 0, mod, 1, b->cond_dev, q8, q8s, s));
+    DIT_HIP(gemm_mx8(N, 2 * F, D, q8, q8s, static_cast<const uint8_t*>(w.in_w), w.in_s, w.in_b, qkvh, silu, s));
+    DIT_HIP(quantize_mx8(N, F, qkvh, q8, q8s, s));
+    DIT_HIP(gemm_mx8(N, D, F, q8, q8s, static_cast<const uint8_t*>(w.mo_w), w.mo_s, w.mo_b, a, to_f32, s));
+    if (next_mod != nullptr)
+      DIT_HIP(resid_modnorm_mx8(c.norm, c.norm_eps, N, D, x, a, mod, 1, next_mod, 0, b->cond_dev, q8, q8s, s));
+    else
+      DIT_HIP(gated_residual(N, D, false, x, a, mod, 1, b->cond_dev, s));
+    return DIT_OK;
+  }
   const GemmEpilogue silu{kEpiSiluGate};
+  auto gemm = [&](int n, int kk, const void* A, const void* W, const float* bias, void* C,
+                  const GemmEpilogue& ep) -> hipError_t {
+    return gemm_bf16(N, n, kk, static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W), bias, C, ep, s);
+  };
   // attention sub-layer
   if (!h_ready) DIT_HIP(modnorm(true, c.norm, c.norm_eps, N, D, false, x, mod, 0, b->cond_dev, h, s));
-  DIT_HIP(gemm(3 * D, D, h, w.qkv_w, w.qkv_s, w.qkv_b, big, to_bf16));
+  DIT_HIP(gemm(3 * D, D, h, w.qkv_w, w.qkv_b, big, to_bf16));
   DIT_HIP(rope_split(true, N, H, hd, c.rot_dim, big, b->cos_dev, b->sin_dev, q, k, v, s));
   DIT_HIP(attention_bf16(N, H, hd, b->n_segs, b->cu_dev, b->max_seqlen, q, k, v, o, s));
-  DIT_HIP(gemm(D, D, o, w.out_w, w.out_s, w.out_b, a, to_f32));
+  DIT_HIP(gemm(D, D, o, w.out_w, w.out_b, a, to_f32));
   // MLP sub-layer: the attention's gated residual and the MLP norm in one pass
   DIT_HIP(resid_modnorm(c.norm, c.norm_eps, N, D, x, a, mod, 0, mod, 1, b->cond_dev, h, s));
-  DIT_HIP(gemm(2 * F, D, h, w.in_w, w.in_s, w.in_b, qkvh, silu));
-  DIT_HIP(gemm(D, F, qkvh, w.mo_w, w.mo_s, w.mo_b, a, to_f32));
+  DIT_HIP(gemm(2 * F, D, h, w.in_w, w.in_b, qkvh, silu));
+  DIT_HIP(gemm(D, F, qkvh, w.mo_w, w.mo_b, a, to_f32));
   if (next_mod != nullptr)
     DIT_HIP(resid_modnorm(c.norm, c.norm_eps, N, D, x, a, mod, 1, next_mod, 0, b->cond_dev, h, s));
   else

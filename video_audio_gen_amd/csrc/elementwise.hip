@@ -5,8 +5,11 @@
 // as wavefront butterfly shuffles; where a row spans several wavefronts (the
 // norms at width 6144: 64-512 threads per row) the partial sums meet in LDS
 // behind a workgroup barrier.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
+#include "mx8.h"
 
 namespace dit {
 
@@ -88,7 +91,8 @@ __global__ __launch_bounds__(TPR > 256 ? TPR : 256) void modnorm_kernel(int N, i
                                                      const float* __restrict__ mod, int shift_k,
                                                      int scale_k, const int32_t* __restrict__ cond_idx,
                                                      TO* __restrict__ h, float* xw, const float* __restrict__ a,
-                                                     const float* __restrict__ gmod, int gate_k) {
+                                                     const float* __restrict__ gmod, int gate_k,
+                                                     uint8_t* __restrict__ hs) {
   typedef typename norm_acc<TO>::T A;
   constexpr int WPR = TPR / 64, RPB = (TPR > 256 ? TPR : 256) / TPR;
   __shared__ A red[2][RPB * WPR];
@@ -204,7 +208,22 @@ __global__ __launch_bounds__(TPR > 256 ? TPR : 256) void modnorm_kernel(int N, i
             y2 = y2 * (A(1) + A(a.z)) + A(b.z);
             y3 = y3 * (A(1) + A(a.w)) + A(b.w);
           }
-          store4<TO>::st(hr + 4 * c, make_float4(float(y0), float(y1), float(y2), float(y3)));
+          if constexpr (std::is_same<TO, uint8_t>::value) {
+            // MXFP8 output (codes [N][D], scales [N][D/32]): the bf16 value of
+            // each output, as a stored bf16 h, quantized per 32 consecutive
+            // columns, which are this thread's 4 and those of the 7 threads
+            // beside it (chunks 8q .. 8q+7 of the row; D is a multiple of 32).
+            const float f[4] = {bf16_to_f32(f32_to_bf16(float(y0))), bf16_to_f32(f32_to_bf16(float(y1))),
+                                bf16_to_f32(f32_to_bf16(float(y2))), bf16_to_f32(f32_to_bf16(float(y3)))};
+            float am = nan_max(nan_max(fabsf(f[0]), fabsf(f[1])), nan_max(fabsf(f[2]), fabsf(f[3])));
+            am = mx_group8_max(am);
+            int div;
+            const uint32_t sb = mx_scale(am, &div);
+            *reinterpret_cast<uint32_t*>(hr + 4 * c) = mx_code4(f[0], f[1], f[2], f[3], sb, div);
+            if ((c & 7) == 0) hs[static_cast<size_t>(row) * (D / 32) + (c >> 3)] = static_cast<uint8_t>(sb);
+          } else {
+            store4<TO>::st(hr + 4 * c, make_float4(float(y0), float(y1), float(y2), float(y3)));
+          }
         }
       }
     }
@@ -216,7 +235,9 @@ bool modnorm_supported(int D) { return D > 0 && D % 4 == 0 && D <= 8192; }
 template <typename TX, typename TO, bool RES = false>
 static hipError_t modnorm_t(int norm, float eps, int N, int D, const TX* x, const float* mod,
                             int which, const int32_t* ci, TO* h, hipStream_t s, float* xw = nullptr,
-                            const float* a = nullptr, const float* gmod = nullptr, int gate_k = 0) {
+                            const float* a = nullptr, const float* gmod = nullptr, int gate_k = 0,
+                            uint8_t* hs = nullptr) {
+  if (std::is_same<TO, uint8_t>::value && D % 32 != 0) return hipErrorInvalidValue;
   const int d4 = D / 4;
   const int shift_k = which == 0 ? 0 : 3, scale_k = which == 0 ? 1 : 4;
   // two rows per workgroup once there are enough rows to fill the chip
@@ -227,10 +248,10 @@ static hipError_t modnorm_t(int norm, float eps, int N, int D, const TX* x, cons
     if (N >= 4096 * RPB) {                                                                            \
       const int nb = (N + RPB * R - 1) / (RPB * R);                                                   \
       hipLaunchKernelGGL((modnorm_kernel<TX, TO, TPR, K, R, 1, RES>), dim3(nb), dim3(NTH), 0, s, N, D, norm, \
-                         eps, x, mod, shift_k, scale_k, ci, h, xw, a, gmod, gate_k);                        \
+                         eps, x, mod, shift_k, scale_k, ci, h, xw, a, gmod, gate_k, hs);                        \
     } else {                                                                                          \
       hipLaunchKernelGGL((modnorm_kernel<TX, TO, TPR, K, 1, 1, RES>), dim3((N + RPB - 1) / RPB), dim3(NTH), 0, \
-                         s, N, D, norm, eps, x, mod, shift_k, scale_k, ci, h, xw, a, gmod, gate_k);         \
+                         s, N, D, norm, eps, x, mod, shift_k, scale_k, ci, h, xw, a, gmod, gate_k, hs);         \
     }                                                                                                 \
     return hipGetLastError();                                                                         \
   }
@@ -276,6 +297,26 @@ hipError_t resid_modnorm(int norm, float eps, int N, int D, float* x, const floa
   // x is read and written through xw only (the read-only pointer stays null)
   return modnorm_t<float, bf16_t, true>(norm, eps, N, D, static_cast<const float*>(nullptr), nmod, norm_which,
                                         cond_idx, h, s, x, a, gmod, gate_which == 0 ? 2 : 5);
+}
+
+// The same two kernels with h written in MXFP8 (codes [N][D], scales
+// [N][D/32]): the bf16 values a stored h would hold, quantized as
+// quantize_mx8 does, so the MXFP8 GEMM after them reads what it would read
+// from a separate quantization of h.
+hipError_t modnorm_mx8(int norm, float eps, int N, int D, const float* x, const float* mod, int which,
+                       const int32_t* cond_idx, uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  LaunchScope scope_(kCntModnorm, s);
+  return modnorm_t<float, uint8_t>(norm, eps, N, D, x, mod, which, cond_idx, codes, s, nullptr, nullptr, nullptr, 0,
+                                   scales);
+}
+hipError_t resid_modnorm_mx8(int norm, float eps, int N, int D, float* x, const float* a, const float* gmod,
+                             int gate_which, const float* nmod, int norm_which, const int32_t* cond_idx,
+                             uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  LaunchScope scope_(kCntResidModnorm, s);
+  return modnorm_t<float, uint8_t, true>(norm, eps, N, D, static_cast<const float*>(nullptr), nmod, norm_which,
+                                         cond_idx, codes, s, x, a, gmod, gate_which == 0 ? 2 : 5, scales);
 }
 
 // ============================================================================ RoPE + QKV split

@@ -73,9 +73,11 @@ bool gemm_bf16_supported(int M, int N, int K);
 bool gemm_f32_supported(int M, int N, int K);
 
 // ---- attention (q, k, v head-major [H, N, hd]; o [N, H*hd])
+// o8 / o8s non-null: o is written in MXFP8 instead (codes [N][H*hd], scales
+// [N][H*hd/32]; the bf16 values quantized as quantize_mx8 does) and `o` is unused.
 hipError_t attention_bf16(int N, int H, int hd, int n_docs, const int32_t* cu, int max_seqlen,
                           const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
-                          hipStream_t s);
+                          hipStream_t s, uint8_t* o8 = nullptr, uint8_t* o8s = nullptr);
 hipError_t attention_f32(int N, int H, int hd, int n_docs, const int32_t* cu, int max_seqlen,
                          const float* q, const float* k, const float* v, float* o, hipStream_t s);
 bool attention_supported(bool bf16, int hd);
@@ -95,6 +97,14 @@ hipError_t silu_gate(bool bf16, int N, int F, const void* u, void* m, hipStream_
 hipError_t resid_modnorm(int norm, float eps, int N, int D, float* x, const float* a, const float* gmod,
                          int gate_which, const float* nmod, int norm_which, const int32_t* cond_idx, uint16_t* h,
                          hipStream_t s);
+// MXFP8 model: the two kernels above with h written as E4M3 codes [N][D] and
+// E8M0 scales [N][D/32] (D a multiple of 32), bit-identical to quantize_mx8 of
+// the bf16 h they would store.
+hipError_t modnorm_mx8(int norm, float eps, int N, int D, const float* x, const float* mod, int which,
+                       const int32_t* cond_idx, uint8_t* codes, uint8_t* scales, hipStream_t s);
+hipError_t resid_modnorm_mx8(int norm, float eps, int N, int D, float* x, const float* a, const float* gmod,
+                             int gate_which, const float* nmod, int norm_which, const int32_t* cond_idx,
+                             uint8_t* codes, uint8_t* scales, hipStream_t s);
 hipError_t gated_residual(int N, int D, bool x_f64, void* x, const float* a, const float* mod, int which,
                           const int32_t* cond_idx, hipStream_t s);
 // ---- fused row kernels of the fp32 stream (fused_f32.hip); part: fp64 split-K

@@ -10,51 +10,9 @@
 // MX block scales natively instead.
 #include "common.h"
 #include "kernels.h"
+#include "mx8.h"
 
 namespace dit {
-
-// Nearest-even E4M3 of a finite y, clamped to +-448 (0x7E), sign kept.
-__device__ __forceinline__ uint32_t e4m3_rne(float y) {
-  const uint32_t sgn = (__float_as_uint(y) >> 24) & 0x80u;
-  const float a = fabsf(y);
-  uint32_t mag;
-  if (a >= 448.0f) {
-    mag = 0x7Eu;
-  } else if (a < 0.015625f) {  // below 2^-6: subnormal steps of 2^-9 (8 steps give code 0x08 = 2^-6)
-    mag = static_cast<uint32_t>(rintf(a * 512.0f));
-  } else {
-    const uint32_t ua = __float_as_uint(a);
-    int e = static_cast<int>(ua >> 23) - 127;
-    uint32_t keep = (ua >> 20) & 7u;
-    const uint32_t rem = ua & 0xFFFFFu;
-    if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) ++keep;
-    if (keep == 8u) {
-      keep = 0;
-      ++e;
-    }
-    mag = (static_cast<uint32_t>(e + 7) << 3) | keep;
-  }
-  return sgn | mag;
-}
-
-// The block's scale exponent s (byte s + 127), or 255 / 0 for a non-finite
-// / all-zero block; `div` receives the exponent the values are divided by.
-__device__ __forceinline__ uint32_t mx_scale(float amax, int* div) {
-  if (!(amax <= 3.40282347e38f)) {  // NaN or Inf
-    *div = 0;
-    return 255u;
-  }
-  if (amax == 0.0f) {
-    *div = 0;
-    return 0u;
-  }
-  int ef;
-  const float f = frexpf(amax, &ef);  // amax = f 2^ef, f in [0.5, 1): floor(log2 amax) = ef - 1
-  int s = ef - 1 - 8 + (f > 0.875f ? 1 : 0);  // leading digits above 1.75 would not fit 448 2^(ef-9)
-  s = s < -127 ? -127 : (s > 127 ? 127 : s);
-  *div = s;
-  return static_cast<uint32_t>(s + 127);
-}
 
 // One thread per 32-value block: four 16-byte loads of bf16, two 16-byte code
 // stores, one scale byte.
@@ -82,15 +40,7 @@ __global__ __launch_bounds__(256) void quantize_mx8_kernel(int64_t n_blocks, int
   const uint32_t sbyte = mx_scale(amax, &div);
   uint32_t packed[8];
 #pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    uint32_t p = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t c = sbyte == 255u ? 0u : e4m3_rne(ldexpf(v[4 * w + i], -div));
-      p |= c << (8 * i);
-    }
-    packed[w] = p;
-  }
+  for (int w = 0; w < 8; ++w) packed[w] = mx_code4(v[4 * w], v[4 * w + 1], v[4 * w + 2], v[4 * w + 3], sbyte, div);
   uint4* dst = reinterpret_cast<uint4*>(codes + t * 32);
   dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
   dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
