@@ -4,10 +4,11 @@
 // fp32 DiT onto the device, staged once", section "What moved, and onto what".
 //
 // bf16: v_mfma_f32_32x32x16_bf16, fp32 accumulation, 256x256x64 workgroup
-//   tiles, eight wavefronts of 128x64; A/B tiles stream HBM -> LDS by direct
-//   buffer loads (double-buffered, 128 KB) into an XOR-swizzled layout so the
-//   MFMA operand reads are bank-conflict free, and the next k-step's operands
-//   are read while the current MFMAs run.
+//   tiles, eight wavefronts of 128x64 in two groups that alternate between
+//   reading a K tile's operands from LDS into registers and running that
+//   tile's MFMAs from registers (one group of each per SIMD); A/B tiles
+//   stream HBM -> LDS by direct buffer loads (double-buffered, 128 KB) into an
+//   XOR-swizzled layout so the operand reads are bank-conflict free.
 // MXFP8: the same tiles of E4M3 bytes (128 K values per 128-byte tile row) on
 //   v_mfma_scale_f32_32x32x64_f8f6f4, with each row's E8M0 block scales.
 // (The fp32 stream's GEMM on int8 slices is in gemm_slices.hip.)
@@ -15,32 +16,22 @@
 // The value of C[i][j] depends only on row i of A, row j of B and K -- never
 // on M or on where row i sits in a tile -- so a document computed alone and
 // the same document inside a packed batch give bit-identical results.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace dit {
 
 // ============================================================================ bf16 GEMM
-#ifndef DIT_GEMM_BK
-#define DIT_GEMM_BK 64
-#endif
-#ifndef DIT_GEMM_STAGES
-#define DIT_GEMM_STAGES 2
-#endif
 namespace gb {
-constexpr int BM = 256, BN = 256, BK = DIT_GEMM_BK;
-constexpr int STAGES = DIT_GEMM_STAGES;       // LDS ring: tiles k+1 .. k+STAGES-1 load while k computes
-#ifndef DIT_GEMM_WAVES
-#define DIT_GEMM_WAVES 8
-#endif
-// 8 wavefronts of 128x64 (two per SIMD: one can issue MFMAs while the other
-// waits; measured 42-46% of peak against 37-40% for 4 of 128x128) or 4 of 128x128.
-constexpr int WM = 128, WN = DIT_GEMM_WAVES == 8 ? 64 : 128;  // per-wave tile
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int STAGES = 2;                     // LDS ring: tile k+1 (and the copy of k+2) while k is read
+constexpr int WM = 128, WN = 64;              // per-wave tile: 8 wavefronts, two per SIMD
 constexpr int NWAVE = (BM / WM) * (BN / WN);
-constexpr int NT = NWAVE * 64;                // 256 threads
+constexpr int NT = NWAVE * 64;                // 512 threads
 constexpr int TM = WM / 32, TN = WN / 32;     // 32x32 MFMA tiles per wave
-constexpr int CPR = BK / 8;                   // 16-byte chunks per tile row: 4
-constexpr int DMA_PER_WAVE = BM * CPR / 64 / NWAVE;  // buffer_load...lds per operand per wave per stage: 4
+constexpr int CPR = BK / 8;                   // 16-byte chunks per 128-byte tile row: 8
 }  // namespace gb
 
 // Chunk c of row r of a tile row of CPR 16-byte chunks lives at physical chunk
@@ -51,16 +42,15 @@ __device__ __forceinline__ int gb_swz(int r, int c) {
   constexpr int sh = gb_log2(16 / gb::CPR);
   return r * gb::CPR + (c ^ ((r >> sh) & (gb::CPR - 1)));
 }
-static_assert(gb::CPR == 4 || gb::CPR == 8, "tile rows of 4 or 8 16-byte chunks");
 static_assert(gb::WN == 64 && gb::BN % 64 == 0, "the SiLU-gate epilogue pairs a wave's two 32-column tiles");
 
 
 // Tiles move HBM -> LDS with buffer_load_dwordx4 ... lds (no VGPR staging, no
 // ds_write): lane l of one instruction writes its 16 bytes at LDS base + 16*l,
 // and a read past the buffer's num_records returns zero, which pads the M and N
-// tails.  A 256x32 tile is 16 such instructions; wave w issues 4w .. 4w+3.
-// Instruction i covers LDS chunks 64i .. 64i+63 = rows 16i .. 16i+15, so lane l
-// fetches row 16i + l/4 at the logical chunk whose swizzled position is l%4.
+// tails.  A 256-row tile of 128-byte rows is 32 such instructions, each
+// covering LDS chunks 64i .. 64i+63 = rows 8i .. 8i+7 (lane l: row 8i + l/8 at
+// the logical chunk whose swizzled position is l%8).
 //
 // MX (MXFP8) instantiation: A and B are OCP E4M3 bytes with one E8M0 scale per
 // 32 consecutive K values (Asc [M][K/32], Bsc [N][K/32]); a 128-byte tile row
@@ -80,8 +70,8 @@ __device__ __forceinline__ void gemm_tile_body(int M, int N, int K, const void* 
   using namespace gb;
   // bytes of one operand row; a tile row is always BK * 2 = 128 bytes
   const int rowb = MX ? K : 2 * K;
-  // STAGES x (A + B): 128 KB at 2 x 64 or 4 x 32; MX adds each stage's scale
-  // dwords of the A and B rows (STAGES x 2 KB)
+  // STAGES x (A + B): 128 KB; MX adds each stage's scale dwords of the A and
+  // B rows (STAGES x 2 KB)
   constexpr int SC_CHUNKS = MX ? STAGES * (BM + BN) / 4 : 0;
   __shared__ uint4 smem[STAGES * (BM + BN) * CPR + SC_CHUNKS];
   uint4* As = smem;
@@ -126,15 +116,19 @@ __device__ __forceinline__ void gemm_tile_body(int M, int N, int K, const void* 
       const_cast<char*>(A + static_cast<size_t>(m0) * rowb), 0, a_rows * rowb, 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<char*>(B + static_cast<size_t>(n0) * rowb), 0, b_rows * rowb, 0x00020000);
-  // Byte offset of this lane's chunk for instruction j of its wave: instruction
-  // i covers rows (64/CPR) i .. (64/CPR) i + 64/CPR - 1.
-  uint32_t voff[DMA_PER_WAVE];
+  // Copy instruction j of a wave covers tile rows 64 (wave % 4) + 8 j ..
+  // + 7, lane l fetching row 64 (wave % 4) + 8 j + l / 8 at the logical chunk
+  // that the swizzle stores at position l % 8.  The swizzle of row r + 8 j
+  // depends on j only through j % 2, so two lane offsets serve all eight
+  // instructions; the 8 j rows go into the scalar offset.
+  constexpr int DMA_G = BM * CPR / 64 / 4;  // per operand per wave of a group: 8
+  static_assert(CPR == 8, "the copy offsets below assume 128-byte tile rows of eight chunks");
+  uint32_t voff2[2];
 #pragma unroll
-  for (int j = 0; j < DMA_PER_WAVE; ++j) {
-    const int i = wave * DMA_PER_WAVE + j;
-    const int row = (64 / CPR) * i + lane / CPR;
-    const int c = gb_swz(row, lane % CPR) - row * CPR;  // logical chunk stored at position lane % CPR
-    voff[j] = static_cast<uint32_t>(row * rowb + c * 16);
+  for (int par = 0; par < 2; ++par) {
+    const int row = 64 * (wave & 3) + 8 * par + lane / CPR;
+    const int c = gb_swz(row, lane % CPR) - row * CPR;
+    voff2[par] = static_cast<uint32_t>((row - 8 * par) * rowb + c * 16);
   }
 
   f32x16_t acc[TM][TN];
@@ -145,30 +139,34 @@ __device__ __forceinline__ void gemm_tile_body(int M, int N, int K, const void* 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-// MX: wave w also copies the scale dwords of tile kt_ of 64 rows -- A rows
-// 64w.. for w < 4, B rows 64(w-4).. otherwise -- to Ss[stage][row] (lane l's
-// dword lands at the instruction's LDS base + 4l).
-#define GB_DMA(stage, kt_)                                                                              \
+// Half a tile per group: group 1 copies the A tile (and the A scales), group 0
+// the B tile (and the B scales); wave w of a group moves rows 64 (w % 4) ..
+#define GB_DMA_HALF(stage, kt_)                                                                         \
   {                                                                                                     \
     const int soff = (kt_) * (BK * 2);                                                                  \
-    _Pragma("unroll") for (int j = 0; j < DMA_PER_WAVE; ++j) {                                         \
-      const int i = wave * DMA_PER_WAVE + j;                                                            \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(As + (stage) * BM * CPR + i * 64), 16,  \
-                                               voff[j], soff, 0, 0);                                   \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(Bs + (stage) * BN * CPR + i * 64), 16,  \
-                                               voff[j], soff, 0, 0);                                   \
+    if (grp == 1) {                                                                                     \
+      _Pragma("unroll") for (int j = 0; j < DMA_G; ++j) {                                              \
+        const int i = (wave & 3) * DMA_G + j;                                                           \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(As + (stage) * BM * CPR + i * 64), 16,\
+                                                 voff2[j & 1], soff + 8 * j * rowb, 0, 0);             \
+      }                                                                                                 \
+      if constexpr (MX)                                                                                 \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(Ss + (stage) * (BM + BN) + 64 * (wave & 3)), \
+                                                 4, s_voff, 4 * (kt_), 0, 0);                          \
+    } else {                                                                                            \
+      _Pragma("unroll") for (int j = 0; j < DMA_G; ++j) {                                              \
+        const int i = (wave & 3) * DMA_G + j;                                                           \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(Bs + (stage) * BN * CPR + i * 64), 16,\
+                                                 voff2[j & 1], soff + 8 * j * rowb, 0, 0);             \
+      }                                                                                                 \
+      if constexpr (MX)                                                                                 \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                       \
+            rsb, (lds_ptr_t)(Ss + (stage) * (BM + BN) + BM + 64 * (wave & 3)), 4, s_voff, 4 * (kt_), 0, 0); \
     }                                                                                                   \
-    if constexpr (MX)                                                                                   \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wave < 4 ? rsa : rsb,                                   \
-                                               (lds_ptr_t)(Ss + (stage) * (BM + BN) + 64 * wave), 4,   \
-                                               s_voff, 4 * (kt_), 0, 0);                               \
   }
-
   const int KT = MX ? K / (2 * BK) : K / BK;
   const int lr = lane & 31, lg = lane >> 5;
-  // MX: scale rows [M][K/32] bytes; a tile's four scales of a row are one
-  // dword.  Rows past M or N read as zero (their outputs are not stored).
-  const int kb = K / 32;  // scale bytes per row
+  const int kb = K / 32;
   __amdgpu_buffer_rsrc_t rsa = ra, rsb = rb;
   uint32_t s_voff = 0;
   if constexpr (MX) {
@@ -178,123 +176,132 @@ __device__ __forceinline__ void gemm_tile_body(int M, int N, int K, const void* 
                                             0x00020000);
     s_voff = static_cast<uint32_t>((64 * (wave & 3) + lane) * kb);
   }
-  uint32_t sa[TM], sb[TN];
-
-// One BK tile of MFMAs from LDS stage `st`: the operands of k-step s+1 are
-// read while the 16 MFMAs of k-step s run.
-#define GB_COMPUTE(st)                                                                                  \
-  {                                                                                                     \
-    const uint4* a_ = As + (st) * BM * CPR;                                                             \
-    const uint4* b_ = Bs + (st) * BN * CPR;                                                             \
-    bf16x8_t fa[2][TM], fb[2][TN];                                                                      \
-    _Pragma("unroll") for (int i = 0; i < TM; ++i) fa[0][i] =                                          \
-        __builtin_bit_cast(bf16x8_t, a_[gb_swz(wr + i * 32 + lr, lg)]);                                 \
-    _Pragma("unroll") for (int j = 0; j < TN; ++j) fb[0][j] =                                          \
-        __builtin_bit_cast(bf16x8_t, b_[gb_swz(wc + j * 32 + lr, lg)]);                                 \
-    _Pragma("unroll") for (int ks = 0; ks < BK / 16; ++ks) {                                           \
-      const int cur = ks & 1;                                                                           \
-      if (ks + 1 < BK / 16) {                                                                           \
-        const int c_ = (ks + 1) * 2 + lg;                                                               \
-        _Pragma("unroll") for (int i = 0; i < TM; ++i) fa[cur ^ 1][i] =                                \
-            __builtin_bit_cast(bf16x8_t, a_[gb_swz(wr + i * 32 + lr, c_)]);                             \
-        _Pragma("unroll") for (int j = 0; j < TN; ++j) fb[cur ^ 1][j] =                                \
-            __builtin_bit_cast(bf16x8_t, b_[gb_swz(wc + j * 32 + lr, c_)]);                             \
-      }                                                                                                 \
-      _Pragma("unroll") for (int i = 0; i < TM; ++i)                                                   \
-        _Pragma("unroll") for (int j = 0; j < TN; ++j)                                                 \
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0); \
-    }                                                                                                   \
-  }
-
-// MX: one tile is two k-steps of 64; a lane's 32-byte operand is logical
-// chunks 4s + g and 4s + 2 + g of its row (bytes 16g.. of each 32-value block).
-// Byte 2s + g of the scale dword is this lane's block of step s.
-typedef int mx_v4i __attribute__((ext_vector_type(4)));
-typedef int mx_v8i __attribute__((ext_vector_type(8)));
-#define GB_MX_OPER(base, row, s_)                                                                       \
-  __builtin_shufflevector(__builtin_bit_cast(mx_v4i, (base)[gb_swz((row), 4 * (s_) + lg)]),            \
-                          __builtin_bit_cast(mx_v4i, (base)[gb_swz((row), 4 * (s_) + 2 + lg)]), 0, 1, 2,  \
-                          3, 4, 5, 6, 7)
-#define GB_MX_MFMA(s_)                                                                                  \
-  _Pragma("unroll") for (int i = 0; i < TM; ++i)                                                       \
-    _Pragma("unroll") for (int j = 0; j < TN; ++j)                                                     \
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                                     \
-          xa[s_][i], xb[s_][j], acc[i][j], 0, 0, 0,                                                    \
-          static_cast<int>((sa[i] >> (8 * (2 * (s_) + lg))) & 0xFFu), 0,                               \
-          static_cast<int>((sb[j] >> (8 * (2 * (s_) + lg))) & 0xFFu));
-#define GB_COMPUTE_MX(st)                                                                               \
-  {                                                                                                     \
-    const uint4* a_ = As + (st) * BM * CPR;                                                             \
-    const uint4* b_ = Bs + (st) * BN * CPR;                                                             \
-    mx_v8i xa[2][TM], xb[2][TN];                                                                        \
-    _Pragma("unroll") for (int i = 0; i < TM; ++i) xa[0][i] = GB_MX_OPER(a_, wr + i * 32 + lr, 0);     \
-    _Pragma("unroll") for (int j = 0; j < TN; ++j) xb[0][j] = GB_MX_OPER(b_, wc + j * 32 + lr, 0);     \
-    _Pragma("unroll") for (int i = 0; i < TM; ++i) xa[1][i] = GB_MX_OPER(a_, wr + i * 32 + lr, 1);     \
-    _Pragma("unroll") for (int j = 0; j < TN; ++j) xb[1][j] = GB_MX_OPER(b_, wc + j * 32 + lr, 1);     \
-    GB_MX_MFMA(0)                                                                                       \
-    GB_MX_MFMA(1)                                                                                       \
-  }
-
-  // Prologue: tiles 0 .. STAGES-2 in flight.
-#pragma unroll
-  for (int p = 0; p < STAGES - 1; ++p)
-    if (p < KT) GB_DMA(p, p)
-
-  for (int kt = 0; kt < KT; ++kt) {
-    const int st = kt % STAGES;
-    // Tile kt must have landed: the younger in-flight tiles (2*DMA_PER_WAVE
-    // loads each per wave) may stay outstanding.
-    const int younger = KT - 1 - kt < STAGES - 2 ? KT - 1 - kt : STAGES - 2;
-    constexpr int PER = 2 * DMA_PER_WAVE;
-#define GB_VMCNT(n) (0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
-    if (STAGES >= 4 && younger >= 2)
-      __builtin_amdgcn_s_waitcnt(GB_VMCNT(2 * PER < 63 ? 2 * PER : 63));
-    else if (STAGES >= 3 && younger >= 1)
-      __builtin_amdgcn_s_waitcnt(GB_VMCNT(PER));
-    else
-      __builtin_amdgcn_s_waitcnt(GB_VMCNT(0));
-#undef GB_VMCNT
-    go_barrier();  // every wave's part of tile kt is in LDS; stage (kt-1) is free
-    if (kt + STAGES - 1 < KT) GB_DMA((kt + STAGES - 1) % STAGES, kt + STAGES - 1)
+  const int grp = wave >> 2;
+  typedef int mx_v4i __attribute__((ext_vector_type(4)));
+  typedef int mx_v8i __attribute__((ext_vector_type(8)));
+  constexpr int KS = MX ? 2 : BK / 16;
+  typedef typename std::conditional<MX, mx_v8i, bf16x8_t>::type frag_t;
+  frag_t fa[KS][TM], fb[KS][TN];
+  uint32_t sa[TM / 2], sb[TN / 2];
+  auto read_tile = [&](int st) {
+    const uint4* a_ = As + st * BM * CPR;
+    const uint4* b_ = Bs + st * BN * CPR;
     if constexpr (MX) {
-      // tile kt's scale dwords: staged with its operands
+      // A row's tile scale dword holds its blocks 0-3; this lane's blocks for
+      // k-steps 0 and 1 are g and 2 + g.  Two rows (2r', 2r'+1) share one
+      // register: byte 2 (row % 2) + k-step, picked by the MFMAs' op_sel.
       const uint32_t* ss = Ss + st * (BM + BN);
+      const uint32_t sel = lg ? 0x07050301u : 0x06040200u;
 #pragma unroll
-      for (int i = 0; i < TM; ++i) sa[i] = ss[wr + i * 32 + lr];
+      for (int i = 0; i < TM / 2; ++i)
+        sa[i] = __builtin_amdgcn_perm(ss[wr + (2 * i + 1) * 32 + lr], ss[wr + 2 * i * 32 + lr], sel);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) sb[j] = ss[BM + wc + j * 32 + lr];
-      GB_COMPUTE_MX(st)
-      // The scale and step 0's operand reads, then step 0's MFMAs each
-      // followed by two reads of step 1's operands, then step 1's MFMAs.
-      __builtin_amdgcn_sched_group_barrier(0x100, TM + TN + 2 * (TM + TN), 0);
+      for (int j = 0; j < TN / 2; ++j)
+        sb[j] = __builtin_amdgcn_perm(ss[BM + wc + (2 * j + 1) * 32 + lr], ss[BM + wc + 2 * j * 32 + lr], sel);
 #pragma unroll
-      for (int t = 0; t < TM * TN; ++t) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (t < TM + TN) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      for (int s_ = 0; s_ < 2; ++s_) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          fa[s_][i] = __builtin_shufflevector(__builtin_bit_cast(mx_v4i, a_[gb_swz(wr + i * 32 + lr, 4 * s_ + lg)]),
+                                              __builtin_bit_cast(mx_v4i, a_[gb_swz(wr + i * 32 + lr, 4 * s_ + 2 + lg)]),
+                                              0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          fb[s_][j] = __builtin_shufflevector(__builtin_bit_cast(mx_v4i, b_[gb_swz(wc + j * 32 + lr, 4 * s_ + lg)]),
+                                              __builtin_bit_cast(mx_v4i, b_[gb_swz(wc + j * 32 + lr, 4 * s_ + 2 + lg)]),
+                                              0, 1, 2, 3, 4, 5, 6, 7);
       }
+    } else {
 #pragma unroll
-      for (int t = 0; t < TM * TN; ++t) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      continue;
-    }
-    GB_COMPUTE(st)
-    // Inside the block: the operand reads of k-step 0, then in each k-step the
-    // MFMAs, the first TM+TN of them each followed by one operand read of the
-    // next k-step.
-    __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
+      for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
+        for (int i = 0; i < TM; ++i) fa[ks][i] = __builtin_bit_cast(bf16x8_t, a_[gb_swz(wr + i * 32 + lr, ks * 2 + lg)]);
 #pragma unroll
-      for (int t = 0; t < TM * TN; ++t) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (ks + 1 < BK / 16 && t < TM + TN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int j = 0; j < TN; ++j) fb[ks][j] = __builtin_bit_cast(bf16x8_t, b_[gb_swz(wc + j * 32 + lr, ks * 2 + lg)]);
       }
     }
-  }
-#undef GB_COMPUTE
-#undef GB_COMPUTE_MX
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) asm volatile("" : "+v"(fa[ks][i]));
+#pragma unroll
+      for (int j = 0; j < TN; ++j) asm volatile("" : "+v"(fb[ks][j]));
+    }
+    if constexpr (MX) {
+#pragma unroll
+      for (int i = 0; i < TM / 2; ++i) asm volatile("" : "+v"(sa[i]));
+#pragma unroll
+      for (int j = 0; j < TN / 2; ++j) asm volatile("" : "+v"(sb[j]));
+    }
+  };
+  auto mfma_tile = [&]() {
+    if constexpr (MX) {
+#define GB_MX_MFMA(ks_, i_, j_)                                                                         \
+  acc[i_][j_] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                                       \
+      fa[ks_][i_], fb[ks_][j_], acc[i_][j_], 0, 0, 2 * ((i_) & 1) + (ks_), static_cast<int>(sa[(i_) / 2]), \
+      2 * ((j_) & 1) + (ks_), static_cast<int>(sb[(j_) / 2]));
+#define GB_MX_STEP(ks_)                                                                                 \
+  GB_MX_MFMA(ks_, 0, 0) GB_MX_MFMA(ks_, 0, 1) GB_MX_MFMA(ks_, 1, 0) GB_MX_MFMA(ks_, 1, 1)              \
+  GB_MX_MFMA(ks_, 2, 0) GB_MX_MFMA(ks_, 2, 1) GB_MX_MFMA(ks_, 3, 0) GB_MX_MFMA(ks_, 3, 1)
+      static_assert(TM == 4 && TN == 2, "the unrolled MX k-steps");
+      GB_MX_STEP(0)
+      GB_MX_STEP(1)
+#undef GB_MX_STEP
 #undef GB_MX_MFMA
-#undef GB_MX_OPER
-#undef GB_DMA
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) asm volatile("" : "+v"(acc[i][j]));
+  };
+  auto phase_barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    go_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // The K loop in phases one workgroup barrier apart.  Group 0 (waves 0-3)
+  // reads tile k's operands into registers in phase 2k and runs its MFMAs on
+  // them in phase 2k+1; group 1 (waves 4-7) does the same one phase later, so
+  // on every SIMD one wave streams MFMAs from registers while the other reads
+  // LDS (an MFMA wave alone keeps the matrix core busy).  Group 1 takes one
+  // extra barrier first and group 0 one after its last MFMAs, so every wave
+  // executes the same number.  Measured per 64-deep K tile: ~1,100 clocks of
+  // reads (and copy issue) against ~1,030 of MFMAs per group, where one
+  // barrier per tile with all eight waves reading and multiplying took
+  // ~3,500.
+  //
+  // Copies: tile t+2 goes into tile t's stage.  Group 1 issues its A half
+  // right after its own reads of tile t (group 0 read it a phase earlier),
+  // group 0 its B half after its reads of tile t+1 (a phase later) -- each
+  // after the reads of its phase, since the compiler makes any LDS read wait
+  // for the direct-to-LDS copies in flight.  Each group waits for its copies
+  // before the barrier ahead of the other group's first read of them: group 1
+  // at the end of its next MFMA phase, group 0 before its reads of tile t+1.
+  GB_DMA_HALF(0, 0)
+  if (KT > 1) GB_DMA_HALF(1, 1)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  if (grp == 1) phase_barrier();
+  for (int kt = 0; kt < KT; ++kt) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's copies into tile kt's stage are done
+    read_tile(kt & 1);
+    if (grp == 1 && kt + 2 < KT) GB_DMA_HALF(kt & 1, kt + 2)
+    if (grp == 0 && kt >= 1 && kt + 1 < KT) GB_DMA_HALF((kt + 1) & 1, kt + 1)
+    phase_barrier();
+    mfma_tile();
+    if (grp == 1) __builtin_amdgcn_s_waitcnt(0x0F70);  // its A half of tile kt+2 has landed
+    phase_barrier();
+  }
+  if (grp == 0) phase_barrier();
+#undef GB_DMA_HALF
 
   // Epilogue: lane l of a 32x32 tile holds column l%32, rows 8*(e/4) + 4*(l/32) + e%4.
   // Rows e and e+1 are adjacent, so lane pairs (2c, 2c+1) swap one value and
