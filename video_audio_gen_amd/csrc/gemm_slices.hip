@@ -42,35 +42,22 @@ namespace dit {
 //
 // Workgroup tile 192 x 64 (a few hundred rows of activations are covered by
 // one or two tiles, so each weight slice is read once per row tile), K step
-// 32, twelve wavefronts of 32 x 32 (three per SIMD); slices of A and B stream
-// HBM -> LDS by direct buffer loads into a three-stage ring (120 KB).
+// 32, eight wavefronts in two groups that alternate between reading a step's
+// slice fragments into registers and multiplying (below); slices of A and B
+// stream HBM -> LDS by direct buffer loads into a four-stage ring (160 KB).
 namespace go {
 constexpr int S = 5;                      // slices per operand
-constexpr int BM = 192, BN = 64, BK = 32, NW = 12, NT = 64 * NW, STAGES = 3;
+constexpr int BM = 192, BN = 64, BK = 32, NW = 8, NT = 64 * NW, STAGES = 4;
 constexpr int APLANE = BM * BK / 16;      // 16-byte chunks of one A slice tile: 384
 constexpr int BPLANE = BN * BK / 16;      // ... of one B slice tile: 128
 constexpr int AOPER = S * APLANE, BOPER = S * BPLANE;
 constexpr int STAGE = AOPER + BOPER;      // 2560 chunks = 40 KB
 constexpr int NDMA = STAGE / 64;          // 1 KB direct loads per stage: 40
 constexpr int AQ = AOPER / 64;            // the first 30 of them fill A
-constexpr int DMA_MAX = (NDMA + NW - 1) / NW;  // per wave: 4 (waves 0-3) or 3
+constexpr int DMA_W = NDMA / 4;          // per wave of the copying group: 10
 constexpr int KSPLIT_MAX = 16384;
 }  // namespace go
 
-
-// s_waitcnt vmcnt(n) for a run-time n (larger n waits for the n = 7 case).
-__device__ __forceinline__ void go_wait_vm(int n) {
-  switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
-    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
-    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
-    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
-    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F77); break;
-  }
-}
 
 // Padded K of the slice planes (a multiple of the K step; pad slices are zero).
 static inline int go_kp(int K) { return (K + go::BK - 1) / go::BK * go::BK; }
@@ -113,7 +100,7 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
                                                          double* __restrict__ part, int s1, int s2, int n1, int sps1,
                                                          int sps2, int tiles_m, int tiles_n) {
   using namespace go;
-  __shared__ uint4 smem[STAGES * STAGE];  // 120 KB
+  __shared__ uint4 smem[STAGES * STAGE];  // 160 KB
   // Work items: N tiles 0 .. n1-1 in s1 splits of sps1 K steps, then the other
   // N tiles in s2 splits of sps2 (the longer items first).  Workgroups go to
   // the 8 XCDs round-robin; each run of 256 gives XCD x the 32 consecutive
@@ -136,22 +123,34 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches and buffer descriptors
   const int lr = lane & 31, lg = lane >> 5;
-  const int wr = (wave % 6) * 32, wc = (wave / 6) * 32;
+  // Two groups of four wavefronts, one of each per SIMD (wave w runs on SIMD
+  // w % 4), alternate between reading a K step's slice fragments from LDS
+  // into registers and running that step's MFMAs from registers, one
+  // workgroup barrier per phase.  Of the tile's 6 x 2 blocks of 32 x 32, the
+  // wave of group 0 on SIMD k takes row blocks 3 (k / 2) and 3 (k / 2) + 1 of
+  // column block k % 2 (30 MFMAs per step), the wave of group 1 row block
+  // 3 (k / 2) + 2 (15 MFMAs), so while group 0 multiplies, group 1 reads its
+  // fragments and issues the copies, and while group 1 multiplies, group 0
+  // reads: each SIMD's matrix core runs 45 MFMAs per step with no phase in
+  // which it waits on LDS.
+  const int grp = wave >> 2, sk = wave & 3;
+  const int wc = (sk & 1) * 32;
+  const int nb = grp == 0 ? 2 : 1;                        // row blocks of this wave
+  const int wr0 = ((sk >> 1) * 3 + (grp == 0 ? 0 : 2)) * 32;  // its first row
 
-  // Direct loads: instruction q = wave + 12 j fills 1 KB = 32 rows of one
-  // slice plane: q < 30 row block q%6 of A plane q/6, else row block (q-30)%2
-  // of B plane (q-30)/2; lane l fetches row 32 (block) + l/2 at the logical
-  // chunk the swizzle stores at position l%2.  Rows past M or N get an offset
-  // past the buffer, which reads as zero.
+  // Copies (group 1 only): instruction q = 10 (wave % 4) + j fills 1 KB = 32
+  // rows of one slice plane: q < 30 row block q%6 of A plane q/6, else row
+  // block (q-30)%2 of B plane (q-30)/2; lane l fetches row 32 (block) + l/2
+  // at the logical chunk the swizzle stores at position l%2.  Rows past M or
+  // N get an offset past the buffer, which reads as zero.
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t*>(Ap), 0, static_cast<uint32_t>(S * static_cast<int64_t>(M) * Kp), 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t*>(Bp), 0, static_cast<uint32_t>(S * static_cast<int64_t>(N) * Kp), 0x00020000);
-  const int ndma = wave < NDMA - NW * (DMA_MAX - 1) ? DMA_MAX : DMA_MAX - 1;
-  uint32_t voff[DMA_MAX];
+  uint32_t voff[DMA_W];
 #pragma unroll
-  for (int j = 0; j < DMA_MAX; ++j) {
-    const int q = wave + NW * j;
+  for (int j = 0; j < DMA_W; ++j) {
+    const int q = sk * DMA_W + j;
     const bool a_op = q < AQ;
     const int plane = a_op ? q / 6 : (q - AQ) / 2;
     const int r = 32 * (a_op ? q % 6 : (q - AQ) % 2) + (lane >> 1);
@@ -159,131 +158,182 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
     const int grow = (a_op ? m0 : n0) + r;
     const int rows = a_op ? M : N;
     // slice layout [plane][K step][row][32 bytes]: one instruction reads 1 KB in a row
-    voff[j] = (q < NDMA && grow < rows)
-                  ? static_cast<uint32_t>((static_cast<int64_t>(plane) * (Kp / BK) * rows + grow) * BK + 16 * c)
-                  : 0xFFFFFFF0u;
+    voff[j] = grow < rows ? static_cast<uint32_t>((static_cast<int64_t>(plane) * (Kp / BK) * rows + grow) * BK + 16 * c)
+                          : 0xFFFFFFF0u;
   }
   const uint32_t a_step = static_cast<uint32_t>(M) * BK, b_step = static_cast<uint32_t>(N) * BK;  // bytes per K step
   auto dma = [&](int t, int st) {
 #pragma unroll
-    for (int j = 0; j < DMA_MAX; ++j) {
-      const int q = wave + NW * j;
-      if (j < ndma) {
-        const uint32_t off = voff[j] == 0xFFFFFFF0u ? voff[j] : voff[j] + static_cast<uint32_t>(t) * (q < AQ ? a_step : b_step);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(q < AQ ? ra : rb, (lds_ptr_t)(smem + st * STAGE + q * 64), 16, off, 0,
-                                                 0, 0);
-      }
+    for (int j = 0; j < DMA_W; ++j) {
+      const int q = sk * DMA_W + j;
+      const uint32_t off = voff[j] == 0xFFFFFFF0u ? voff[j] : voff[j] + static_cast<uint32_t>(t) * (q < AQ ? a_step : b_step);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(q < AQ ? ra : rb, (lds_ptr_t)(smem + st * STAGE + q * 64), 16, off, 0,
+                                               0, 0);
     }
+  };
+  // s_waitcnt vmcnt(n) for n = 0, 10 or 20 of this wave's copies still in flight
+  auto wait_copies = [&](int n) {
+    if (n >= 20)
+      __builtin_amdgcn_s_waitcnt(0x4F74);  // vmcnt(20): low bits 4, high bits 1
+    else if (n >= 10)
+      __builtin_amdgcn_s_waitcnt(0x0F7A);  // vmcnt(10)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   };
 
   typedef int v4i __attribute__((ext_vector_type(4)));
   typedef int v16i __attribute__((ext_vector_type(16)));
-  v16i acc[S];
+  v16i acc[2][S];
 #pragma unroll
-  for (int d = 0; d < S; ++d)
+  for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[d][e] = 0;
-
-  static_assert(STAGES == 3, "the wait counts below assume two copies in flight");
+    for (int d = 0; d < S; ++d)
 #pragma unroll
-  for (int p = 0; p < STAGES - 1; ++p)
-    if (p < nsteps) dma(t_begin + p, p);
-  for (int i = 0; i < nsteps; ++i) {
-    const int st = i % STAGES;
-    // Step i's copy landed once only the next step's copy (this wave's 3 or 4
-    // loads) is outstanding: loads complete in issue order.
-    go_wait_vm(i + 1 < nsteps ? ndma : 0);
-    // Every wave's share of step i is in LDS and stage (i-1) is free.  A bare
-    // s_barrier: __syncthreads() would also wait for the copy just issued
-    // for step i+1 (vmcnt(0)), which serialises the ring.
-    go_barrier();
-    if (i + STAGES - 1 < nsteps) dma(t_begin + i + STAGES - 1, (i + STAGES - 1) % STAGES);
+      for (int e = 0; e < 16; ++e) acc[b][d][e] = 0;
+  v4i fa[2][S], fb[S];
+  auto read_step = [&](int st) {
     const uint4* sa = smem + st * STAGE;
     const uint4* sb = sa + AOPER;
-    v4i fa[S], fb[S];
 #pragma unroll
     for (int p = 0; p < S; ++p) {
-      fa[p] = __builtin_bit_cast(v4i, sa[p * APLANE + go_swz(wr + lr, lg)]);
       fb[p] = __builtin_bit_cast(v4i, sb[p * BPLANE + go_swz(wc + lr, lg)]);
+      fa[0][p] = __builtin_bit_cast(v4i, sa[p * APLANE + go_swz(wr0 + lr, lg)]);
     }
-    // pair (s, t) accumulates in acc[s + t]; the order keeps two MFMAs on one
-    // accumulator at least two instructions apart (levels 4 3 2 4 3 2 4 3 2 4 3 1 4 0 1)
-#define GO_MFMA(s_, t_) acc[(s_) + (t_)] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[s_], fb[t_], acc[(s_) + (t_)], 0, 0, 0);
+    if (nb == 2) {
+#pragma unroll
+      for (int p = 0; p < S; ++p) fa[1][p] = __builtin_bit_cast(v4i, sa[p * APLANE + go_swz(wr0 + 32 + lr, lg)]);
+    }
+    // the reads complete inside the phase: the asm takes every fragment
+#pragma unroll
+    for (int p = 0; p < S; ++p) asm volatile("" : "+v"(fb[p]), "+v"(fa[0][p]), "+v"(fa[1][p]));
+  };
+  // pair (s, t) accumulates in level s + t; the order keeps two MFMAs on one
+  // accumulator at least two instructions apart (levels 4 3 2 4 3 2 4 3 2 4 3
+  // 1 4 0 1)
+  auto mfma_block = [&](v16i (&a)[S], const v4i (&A)[S]) {
+#define GO_MFMA(s_, t_) a[(s_) + (t_)] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[s_], fb[t_], a[(s_) + (t_)], 0, 0, 0);
     GO_MFMA(4, 0) GO_MFMA(3, 0) GO_MFMA(2, 0) GO_MFMA(3, 1) GO_MFMA(2, 1) GO_MFMA(1, 1) GO_MFMA(2, 2)
     GO_MFMA(1, 2) GO_MFMA(0, 2) GO_MFMA(1, 3) GO_MFMA(0, 3) GO_MFMA(1, 0) GO_MFMA(0, 4) GO_MFMA(0, 0)
     GO_MFMA(0, 1)
 #undef GO_MFMA
-  }
+  };
+  auto phase_barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    go_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
-  // Lane holds column wc + lr, rows wr + 8 (e/4) + 4 lg + e%4 of each level.
+  // Phases: group 0 reads step i in phase 2i and multiplies in 2i+1; group 1
+  // one phase later (an extra barrier first; group 0 takes one after its last
+  // MFMAs, so both execute the same number).  Group 1 issues the copies of
+  // step i+3 (into the stage of step i-1, which both groups finished reading
+  // by the barrier opening phase 2i) at the start of its read phase 2i+1,
+  // and at its end waits until only the copies of steps i+2 and i+3 are in
+  // flight: step i+1 has landed before the barrier ahead of group 0's read of
+  // it.  Loads complete in issue order.
+  static_assert(STAGES == 4 && DMA_W * 4 == NDMA, "the copy schedule and wait counts below");
+  if (grp == 1) {
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+      if (p < nsteps) dma(t_begin + p, p);
+    wait_copies(10 * ((nsteps > 1) + (nsteps > 2)));  // step 0 has landed
+  }
+  go_barrier();
+  if (grp == 1) phase_barrier();
+  for (int i = 0; i < nsteps; ++i) {
+    if (grp == 1 && i + 3 < nsteps) dma(t_begin + i + 3, (i + 3) % STAGES);
+    read_step(i % STAGES);
+    if (grp == 1) wait_copies(10 * ((i + 2 < nsteps) + (i + 3 < nsteps)));
+    phase_barrier();
+    mfma_block(acc[0], fa[0]);
+    if (nb == 2) mfma_block(acc[1], fa[1]);
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int d = 0; d < S; ++d) asm volatile("" : "+v"(acc[b][d]));
+    phase_barrier();
+  }
+  if (grp == 0) phase_barrier();
+
+  // Epilogue, per row block of the wave: lane holds column wc + lr, rows
+  // wr + 8 (e/4) + 4 lg + e%4 of each level.
   const int gn = n0 + wc + lr;
   // C null: fp64 partials for a consumer that sums them itself (any split count)
   const bool direct = s1 == 1 && s2 == 1 && C != nullptr;
-  if ((N & 1) == 0 && (reinterpret_cast<uintptr_t>(C) & 7) == 0) {
-    // Rows e and e+1 are adjacent: lanes 2c and 2c+1 swap one value, and each
-    // stores two adjacent columns of its row (16-byte partials, 8-byte C).
-    const bool odd = lr & 1;
-    const int gnc = gn < N ? gn : N - 1;
-    const int fe = Be[gnc];
-    const bool bad_col = fe == kSliceNonFinite;
-    const double bv = (direct && bias != nullptr) ? static_cast<double>(bias[gnc]) : 0.0;
-    const double bv_pair = __shfl_xor(bv, 1, 64);  // the partner column's bias
-    const int col = odd ? gn - 1 : gn;
+  const bool paired = (N & 1) == 0 && (reinterpret_cast<uintptr_t>(C) & 7) == 0;
 #pragma unroll
-    for (int e = 0; e < 16; e += 2) {
-      const int gm = m0 + wr + 8 * (e >> 2) + 4 * lg + (e & 3);
-      double v[2];
+  for (int b = 0; b < 2; ++b) {
+    if (b >= nb) break;  // uniform; b stays a constant so acc stays in registers
+    const int wr = wr0 + 32 * b;
+    const v16i (&ac)[S] = acc[b];
+    if (paired) {
+      // Rows e and e+1 are adjacent: lanes 2c and 2c+1 swap one value, and each
+      // stores two adjacent columns of its row (16-byte partials, 8-byte C).
+      const bool odd = lr & 1;
+      const int gnc = gn < N ? gn : N - 1;
+      const int fe = Be[gnc];
+      const bool bad_col = fe == kSliceNonFinite;
+      const double bv = (direct && bias != nullptr) ? static_cast<double>(bias[gnc]) : 0.0;
+      const double bv_pair = __shfl_xor(bv, 1, 64);  // the partner column's bias
+      const int col = odd ? gn - 1 : gn;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int r = gm + h < M ? gm + h : M - 1;
-        // sum_d acc_d 2^-7(d+2): each term exact in fp64, five terms
-        double x = 0.0;
+      for (int e = 0; e < 16; e += 2) {
+        const int gm = m0 + wr + 8 * (e >> 2) + 4 * lg + (e & 3);
+        double v[2];
 #pragma unroll
-        for (int d = S - 1; d >= 0; --d) x += ldexp(static_cast<double>(acc[d][e + h]), -7 * (d + 2));
-        const int ae = Ae[r];
-        v[h] = (bad_col || ae == kSliceNonFinite) ? __builtin_nan("") : ldexp(x, ae + fe);
-      }
-      const double recv = __shfl_xor(odd ? v[0] : v[1], 1, 64);
-      const int row = odd ? gm + 1 : gm;
-      if (row < M && col < N) {
-        const double lo = odd ? recv : v[0], hi = odd ? v[1] : recv;
-        if (direct) {
-          const double b_lo = odd ? bv_pair : bv, b_hi = odd ? bv : bv_pair;  // columns col, col + 1
-          *reinterpret_cast<float2*>(C + static_cast<size_t>(row) * N + col) =
-              make_float2(static_cast<float>(lo + b_lo), static_cast<float>(hi + b_hi));
-        } else {
-          *reinterpret_cast<double2*>(part + (static_cast<size_t>(sp) * M + row) * N + col) = make_double2(lo, hi);
+        for (int h = 0; h < 2; ++h) {
+          const int r = gm + h < M ? gm + h : M - 1;
+          // sum_d acc_d 2^-7(d+2): each term exact in fp64, five terms
+          double x = 0.0;
+#pragma unroll
+          for (int d = S - 1; d >= 0; --d) x += ldexp(static_cast<double>(ac[d][e + h]), -7 * (d + 2));
+          const int ae = Ae[r];
+          v[h] = (bad_col || ae == kSliceNonFinite) ? __builtin_nan("") : ldexp(x, ae + fe);
+        }
+        const double recv = __shfl_xor(odd ? v[0] : v[1], 1, 64);
+        const int row = odd ? gm + 1 : gm;
+        if (row < M && col < N) {
+          const double lo = odd ? recv : v[0], hi = odd ? v[1] : recv;
+          if (direct) {
+            const double b_lo = odd ? bv_pair : bv, b_hi = odd ? bv : bv_pair;  // columns col, col + 1
+            *reinterpret_cast<float2*>(C + static_cast<size_t>(row) * N + col) =
+                make_float2(static_cast<float>(lo + b_lo), static_cast<float>(hi + b_hi));
+          } else {
+            *reinterpret_cast<double2*>(part + (static_cast<size_t>(sp) * M + row) * N + col) = make_double2(lo, hi);
+          }
         }
       }
+      continue;
     }
-    return;
-  }
-  if (gn >= N) return;
-  const int fe = Be[gn];
-  const double bv = (direct && bias != nullptr) ? static_cast<double>(bias[gn]) : 0.0;
+    if (gn >= N) continue;
+    const int fe = Be[gn];
+    const double bv = (direct && bias != nullptr) ? static_cast<double>(bias[gn]) : 0.0;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int gm = m0 + wr + 8 * (e >> 2) + 4 * lg + (e & 3);
-    if (gm >= M) continue;
-    // sum_d acc_d 2^-7(d+2): each term exact in fp64, five terms
-    double v = 0.0;
+    for (int e = 0; e < 16; ++e) {
+      const int gm = m0 + wr + 8 * (e >> 2) + 4 * lg + (e & 3);
+      if (gm >= M) continue;
+      // sum_d acc_d 2^-7(d+2): each term exact in fp64, five terms
+      double v = 0.0;
 #pragma unroll
-    for (int d = S - 1; d >= 0; --d) v += ldexp(static_cast<double>(acc[d][e]), -7 * (d + 2));
-    const int ae = Ae[gm];
-    v = (fe == kSliceNonFinite || ae == kSliceNonFinite) ? __builtin_nan("") : ldexp(v, ae + fe);
-    if (direct)
-      C[static_cast<size_t>(gm) * N + gn] = static_cast<float>(v + bv);
-    else
-      part[(static_cast<size_t>(sp) * M + gm) * N + gn] = v;
+      for (int d = S - 1; d >= 0; --d) v += ldexp(static_cast<double>(ac[d][e]), -7 * (d + 2));
+      const int ae = Ae[gm];
+      v = (fe == kSliceNonFinite || ae == kSliceNonFinite) ? __builtin_nan("") : ldexp(v, ae + fe);
+      if (direct)
+        C[static_cast<size_t>(gm) * N + gn] = static_cast<float>(v + bv);
+      else
+        part[(static_cast<size_t>(sp) * M + gm) * N + gn] = v;
+    }
   }
 }
 
 // Split plan from (N, K) and the device alone, so a row's result never
-// depends on M.  One workgroup fits a CU (120 KB of LDS).  Measured on MI355X:
-// a K step takes ~1.1 us, a round of workgroups adds ~5 steps of fixed cost
-// (first copies in flight, epilogue), and each split adds an fp64 partial of
-// the row tile that is written and read back once (192 N 16 bytes at
-// ~4.5 TB/s, i.e. N / 1600 steps per slot).  Plans: every N tile in s splits
+// depends on M.  One workgroup fits a CU (160 KB of LDS).  The cost model
+// was measured on MI355X with a one-barrier-per-step form of this kernel: a
+// K step took ~1.1 us (~0.85 us in the two-group form), a round of
+// workgroups adds ~5 steps of fixed cost (first copies in flight,
+// epilogue), and each split adds an fp64 partial of the row tile that is
+// written and read back once (192 N 16 bytes at ~4.5 TB/s, i.e. N / 1600
+// steps per slot).  Plans: every N tile in s splits
 // (ceil(tiles_n s / CUs) rounds of ceil(steps / s) steps), or the first n1
 // tiles in s1 splits filling k whole rounds and the rest in s2 = 2..4 s1
 // splits after them, which evens out a last, partial round.  Splits have
