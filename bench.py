@@ -236,7 +236,8 @@ def measure(cfg, steps, warmup, no_graph=False, protocol_loops=5):
     import torch
 
     import synthetic as S  # noqa: F401
-    from video_audio_gen_amd import dit, harness
+    import harness
+    from video_audio_gen_amd import dit
 
     dev = torch.cuda.get_device_name(0)
     log(f"workload {cfg.name}: {cfg.n_blocks} blocks, hidden {cfg.hidden}, {cfg.n_tokens} tokens on {dev}")

@@ -15,7 +15,7 @@ from typing import Dict, Optional
 import numpy as np
 import torch
 
-from . import dit
+from video_audio_gen_amd import dit
 
 
 def stage_model(cfg, seed: int = 0, threads: int = 8, device: str = "cuda", log=None) -> dit.Model:

@@ -19,7 +19,8 @@ pytestmark = pytest.mark.gpu
 
 @pytest.fixture(scope="module")
 def H():
-    from video_audio_gen_amd import dit, harness
+    import harness
+    from video_audio_gen_amd import dit
     dit.load()
     return harness
 

@@ -165,7 +165,8 @@ def test_gemm_mx8_nonfinite_block_gives_nan_row(dit):
 
 @pytest.fixture(scope="module")
 def H():
-    from video_audio_gen_amd import dit, harness
+    import harness
+    from video_audio_gen_amd import dit
     dit.load()
     return harness
 

@@ -58,7 +58,8 @@ def _mod_row(cfg, w):
 
 @pytest.mark.parametrize("name", ["vit3d", "vit3d_ragged_docs"])
 def test_vit_block_matches_oracle(name):
-    from video_audio_gen_amd import dit, harness
+    import harness
+    from video_audio_gen_amd import dit
     cfg = S.get_config("vit")
     if name == "vit3d_ragged_docs":  # single-token and odd documents beside a larger one
         cfg = scaled(cfg, segments=(Segment(0, (1, 1, 1), 0), Segment(0, (3, 5, 7), 0), Segment(0, (1, 2, 3), 0)))
@@ -89,7 +90,8 @@ def test_vit_block_matches_oracle(name):
 def test_vit_block_per_head_rows_are_not_the_concatenated_reading():
     """The same weights staged as a [q_all | k_all | v_all] model give another
     block: the layout flag is what makes the per-head checkpoint correct."""
-    from video_audio_gen_amd import dit, harness
+    import harness
+    from video_audio_gen_amd import dit
     cfg = scaled(S.get_config("vit"), segments=(Segment(0, (1, 4, 6), 0),))
     w = _vit_weights(cfg, 63)
     outs = []
