@@ -453,8 +453,8 @@ __global__ __launch_bounds__(af::NT) void attention_f32_kernel(int N, int H, con
       sb[i] = sc;
       mt = fmax(mt, sc);
     }
-    mt = fmax(mt, __shfl_xor(mt, 16, 64));
-    mt = fmax(mt, __shfl_xor(mt, 32, 64));
+    mt = fmax(mt, xor_lane<16>(mt));
+    mt = fmax(mt, xor_lane<32>(mt));
     const double m_new = fmax(m_run, mt);
     const double alpha = exp(m_run - m_new);
     m_run = m_new;
@@ -480,8 +480,8 @@ __global__ __launch_bounds__(af::NT) void attention_f32_kernel(int N, int H, con
 
   // Merge the four wavefronts: m, l per query and O^T per (dim, query) go to
   // LDS; then thread t writes outputs (query, dim) = t + 256 j, dims fastest.
-  double l_w = l_run + __shfl_xor(l_run, 16, 64);
-  l_w += __shfl_xor(l_w, 32, 64);
+  double l_w = l_run + xor_lane<16>(l_run);
+  l_w += xor_lane<32>(l_w);
   __syncthreads();  // K/V space free
   double* mw = reinterpret_cast<double*>(KVs);       // [NW][QT]
   double* lw = mw + NW * QT;                          // [NW][QT]

@@ -72,22 +72,74 @@ template <> struct vec16<bf16_t> {
   }
 };
 
+// The value that lane (lane ^ M) of the wavefront holds, M a power of two up
+// to 32, moved without the LDS permute path: DPP quad permutations (M = 1,
+// 2), DPP rotations within rows of 16 lanes (M = 8; M = 4: a lane with bit 2
+// set takes the rotation that brings lane - 4, the others the one that brings
+// lane + 4), and the lane-half swaps v_permlane16_swap / v_permlane32_swap
+// (M = 16, 32: each returns both halves; the lane keeps its partner's).
+template <int M>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  if constexpr (M == 1) {
+    return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);  // quad_perm [1, 0, 3, 2]
+  } else if constexpr (M == 2) {
+    return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);  // quad_perm [2, 3, 0, 1]
+  } else if constexpr (M == 4) {
+    const uint32_t down = __builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, false);  // row_ror 4: lane - 4 (mod 16)
+    const uint32_t up = __builtin_amdgcn_mov_dpp(v, 0x12C, 0xF, 0xF, false);    // row_ror 12: lane + 4 (mod 16)
+    return (__lane_id() & 4) ? down : up;
+  } else if constexpr (M == 8) {
+    return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false);  // row_ror 8
+  } else if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);  // rows {0,0,2,2}, {1,1,3,3}
+    return (__lane_id() & 16) ? r[0] : r[1];
+  } else {
+    static_assert(M == 32, "lane masks 1 .. 32");
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);  // halves {0,0}, {1,1}
+    return (__lane_id() & 32) ? r[0] : r[1];
+  }
+}
+template <int M>
+__device__ __forceinline__ float xor_lane(float v) {
+  return __uint_as_float(xor_lane<M>(__float_as_uint(v)));
+}
+template <int M>
+__device__ __forceinline__ double xor_lane(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = xor_lane<M>(static_cast<uint32_t>(u)), hi = xor_lane<M>(static_cast<uint32_t>(u >> 32));
+  return __builtin_bit_cast(double, static_cast<uint64_t>(hi) << 32 | lo);
+}
+// the same for a mask known only at run time (uniform over the wavefront)
+template <typename T>
+__device__ __forceinline__ T xor_lane_rt(T v, int m) {
+  switch (m) {
+    case 1: return xor_lane<1>(v);
+    case 2: return xor_lane<2>(v);
+    case 4: return xor_lane<4>(v);
+    case 8: return xor_lane<8>(v);
+    case 16: return xor_lane<16>(v);
+    default: return xor_lane<32>(v);
+  }
+}
+
+// Butterfly sums: every lane adds its partner's partial at distance 32, 16,
+// .., 1, so all lanes end with the same value.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  v += xor_lane<32>(v); v += xor_lane<16>(v); v += xor_lane<8>(v);
+  v += xor_lane<4>(v); v += xor_lane<2>(v); v += xor_lane<1>(v);
   return v;
 }
 __device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  v += xor_lane<32>(v); v += xor_lane<16>(v); v += xor_lane<8>(v);
+  v += xor_lane<4>(v); v += xor_lane<2>(v); v += xor_lane<1>(v);
   return v;
 }
 // max that keeps a NaN from either side (fmaxf drops it), so a row max over
 // |x| reports a non-finite row as NaN or Inf
 __device__ __forceinline__ float nan_max(float a, float b) { return (a > b || a != a) ? a : b; }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = nan_max(v, __shfl_xor(v, o, 64));
+  v = nan_max(v, xor_lane<32>(v)); v = nan_max(v, xor_lane<16>(v)); v = nan_max(v, xor_lane<8>(v));
+  v = nan_max(v, xor_lane<4>(v)); v = nan_max(v, xor_lane<2>(v)); v = nan_max(v, xor_lane<1>(v));
   return v;
 }
 

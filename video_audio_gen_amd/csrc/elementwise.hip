@@ -45,8 +45,8 @@ template <> struct norm_acc<float> { typedef double T; };
 // wavefronts through LDS.
 template <typename A, int WPR>
 __device__ __forceinline__ A row_sum(A v, A* red, int wrow, int wsub, int lane) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  v += xor_lane<32>(v); v += xor_lane<16>(v); v += xor_lane<8>(v);
+  v += xor_lane<4>(v); v += xor_lane<2>(v); v += xor_lane<1>(v);
   if (WPR == 1) return v;
   __syncthreads();
   if (lane == 0) red[wrow * WPR + wsub] = v;
@@ -600,8 +600,8 @@ __global__ __launch_bounds__(256) void adaln_kernel(int six_d, int cond_dim, Ada
       for (int kk = 4 * kp; kk < cond_dim; kk += 4 * ADA_LPR)
         acc += dot4(wload4<TW>::ld(w + kk), *reinterpret_cast<const float4*>(ec + kk));
     }
-#pragma unroll
-    for (int o = ADA_LPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    static_assert(ADA_LPR == 8, "three butterfly steps");
+    acc += xor_lane<4>(acc); acc += xor_lane<2>(acc); acc += xor_lane<1>(acc);
     if (kp == 0 && live) out[static_cast<size_t>(c) * six_d + j] = static_cast<float>(acc + static_cast<double>(bias[j]));
   }
 }

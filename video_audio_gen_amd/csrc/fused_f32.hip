@@ -162,12 +162,25 @@ __global__ __launch_bounds__(1024) void resid_norm_slice_kernel(
   double* xr = x + static_cast<size_t>(row) * D;
   double v[NCH][4];
   double s = 0.0;
+  // the modulation of the norm, loaded with the row so its latency overlaps
+  const bool modulate = nmod != nullptr && (sl != nullptr || y != nullptr);
+  const float4* sh = nullptr;
+  const float4* sc = nullptr;
+  if (modulate) {
+    sh = reinterpret_cast<const float4*>(nmod + (static_cast<size_t>(cr) * 6 + shift_k) * D);
+    sc = reinterpret_cast<const float4*>(nmod + (static_cast<size_t>(cr) * 6 + scale_k) * D);
+  }
+  float4 msc[NCH], msh[NCH];
   // Every load is issued without a branch (a thread past the row's end reads
   // its last chunk and drops it), so all of them are in flight at once.
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int c = t + NT * i;
     const int cc = c < D4 ? c : D4 - 1;
+    if (modulate) {  // uniform
+      msc[i] = sc[cc];
+      msh[i] = sh[cc];
+    }
     const double2 x0 = reinterpret_cast<const double2*>(xr + 4 * cc)[0];
     const double2 x1 = reinterpret_cast<const double2*>(xr + 4 * cc)[1];
     v[i][0] = x0.x; v[i][1] = x0.y; v[i][2] = x1.x; v[i][3] = x1.y;
@@ -207,12 +220,6 @@ __global__ __launch_bounds__(1024) void resid_norm_slice_kernel(
   }
   ss = block_sum(ss, red);
   const double rstd = 1.0 / sqrt(ss * inv_d + static_cast<double>(eps));
-  const float4* sh = nullptr;
-  const float4* sc = nullptr;
-  if (nmod != nullptr) {
-    sh = reinterpret_cast<const float4*>(nmod + (static_cast<size_t>(cr) * 6 + shift_k) * D);
-    sc = reinterpret_cast<const float4*>(nmod + (static_cast<size_t>(cr) * 6 + scale_k) * D);
-  }
   float yv[NCH][4];
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
@@ -221,8 +228,8 @@ __global__ __launch_bounds__(1024) void resid_norm_slice_kernel(
       double z[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) z[e] = (v[i][e] - mean) * rstd;
-      if (nmod != nullptr) {
-        const float4 a = sc[c], b = sh[c];
+      if (modulate) {
+        const float4 a = msc[i], b = msh[i];
         z[0] = z[0] * (1.0 + static_cast<double>(a.x)) + static_cast<double>(b.x);
         z[1] = z[1] * (1.0 + static_cast<double>(a.y)) + static_cast<double>(b.y);
         z[2] = z[2] * (1.0 + static_cast<double>(a.z)) + static_cast<double>(b.z);
@@ -317,6 +324,12 @@ __global__ __launch_bounds__(256) void rope_part_kernel(int N, int H, int hd, in
   // i0..i0+7 (v, or q/k dims past rot)
   const int i0 = rotary ? j * 4 : (which == 2 ? 8 * j : rot + 8 * (j - half / 4));
   const int i1 = rotary ? half + j * 4 : i0 + 4;
+  // the rotation's cos/sin first, so their loads overlap the partials'
+  float4 c = make_float4(0.f, 0.f, 0.f, 0.f), sn = c;
+  if (rotary) {
+    c = *reinterpret_cast<const float4*>(cosb + static_cast<size_t>(n) * half + i0);
+    sn = *reinterpret_cast<const float4*>(sinb + static_cast<size_t>(n) * half + i0);
+  }
   float x1[4], x2[4];
   sum_parts4g<SF>(part, S, S_hi, cb, MN, src + i0, bias, col0 + i0, x1);
   sum_parts4g<SF>(part, S, S_hi, cb, MN, src + i1, bias, col0 + i1, x2);
@@ -325,12 +338,10 @@ __global__ __launch_bounds__(256) void rope_part_kernel(int N, int H, int hd, in
     double ss = 0.0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) ss += double(x1[e]) * double(x1[e]) + double(x2[e]) * double(x2[e]);
-    for (int o = 1; o < tph; o <<= 1) ss += __shfl_xor(ss, o, 64);
+    for (int o = 1; o < tph; o <<= 1) ss += xor_lane_rt(ss, o);
     if (which < 2) sc = 1.0 / sqrt(ss / hd + static_cast<double>(eps));
   }
   if (rotary) {
-    const float4 c = *reinterpret_cast<const float4*>(cosb + static_cast<size_t>(n) * half + i0);
-    const float4 sn = *reinterpret_cast<const float4*>(sinb + static_cast<size_t>(n) * half + i0);
     const float cc[4] = {c.x, c.y, c.z, c.w}, ssn[4] = {sn.x, sn.y, sn.z, sn.w};
     float o1[4], o2[4];
 #pragma unroll

@@ -334,7 +334,7 @@ __device__ __forceinline__ void gemm_tile_body(int M, int N, int K, const void* 
             const float u = bf16_to_f32(f32_to_bf16(acc[i][1][e + h] + bu));
             mv[h] = g / (1.0f + expf(-g)) * u;
           }
-          const float recv = __shfl_xor(odd ? mv[0] : mv[1], 1, 64);
+          const float recv = xor_lane<1>(odd ? mv[0] : mv[1]);
           const int row = odd ? gm + 1 : gm;
           if (row < M)
             *reinterpret_cast<uint32_t*>(Mo + static_cast<size_t>(row) * F + (odd ? f - 1 : f)) =
@@ -361,7 +361,7 @@ __device__ __forceinline__ void gemm_tile_body(int M, int N, int K, const void* 
         for (int e = 0; e < 16; e += 2) {
           const int gm = m0 + wr + i * 32 + 8 * (e >> 2) + 4 * lg + (e & 3);
           const float v0 = acc[i][j][e] + bv, v1 = acc[i][j][e + 1] + bv;
-          const float recv = __shfl_xor(odd ? v0 : v1, 1, 64);
+          const float recv = xor_lane<1>(odd ? v0 : v1);
           const int row = odd ? gm + 1 : gm;
           if (row < M && col < N) {
             const float lo = odd ? recv : v0, hi = odd ? v1 : recv;

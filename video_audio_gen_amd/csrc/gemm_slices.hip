@@ -137,6 +137,18 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
   const int wc = (sk & 1) * 32;
   const int nb = grp == 0 ? 2 : 1;                        // row blocks of this wave
   const int wr0 = ((sk >> 1) * 3 + (grp == 0 ? 0 : 2)) * 32;  // its first row
+  // The epilogue's scale exponents, loaded now so their latency hides under
+  // the K loop: column wc + lr, and rows wr0 + lr and wr0 + 32 + lr (lane
+  // l's value serves the other lanes of its row block through a shuffle).
+  const int gn = n0 + wc + lr;
+  const int gnc = gn < N ? gn : N - 1;
+  const int fe = Be[gnc];
+  int ae_row[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int gm = m0 + wr0 + 32 * b + lr;
+    ae_row[b] = b < nb ? Ae[gm < M ? gm : M - 1] : 0;
+  }
 
   // Copies (group 1 only): instruction q = 10 (wave % 4) + j fills 1 KB = 32
   // rows of one slice plane: q < 30 row block q%6 of A plane q/6, else row
@@ -257,43 +269,44 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
 
   // Epilogue, per row block of the wave: lane holds column wc + lr, rows
   // wr + 8 (e/4) + 4 lg + e%4 of each level.
-  const int gn = n0 + wc + lr;
   // C null: fp64 partials for a consumer that sums them itself (any split count)
   const bool direct = s1 == 1 && s2 == 1 && C != nullptr;
   const bool paired = (N & 1) == 0 && (reinterpret_cast<uintptr_t>(C) & 7) == 0;
+  const double bv = (direct && bias != nullptr) ? static_cast<double>(bias[gnc]) : 0.0;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     if (b >= nb) break;  // uniform; b stays a constant so acc stays in registers
     const int wr = wr0 + 32 * b;
     const v16i (&ac)[S] = acc[b];
+    // the exponents of this lane's 16 rows, from the lanes that loaded them
+    int aex[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) aex[e] = __shfl(ae_row[b], 8 * (e >> 2) + 4 * lg + (e & 3), 32);
+    // sum_d acc_d 2^-7(d+2), the smallest level first, times 2^(row + column
+    // exponent): every product by a power of two is exact, so each fma
+    // rounds as the addition of that term would
+    auto value = [&](int e) -> double {
+      double x = static_cast<double>(ac[4][e]) * 0x1p-42;
+      x = fma(static_cast<double>(ac[3][e]), 0x1p-35, x);
+      x = fma(static_cast<double>(ac[2][e]), 0x1p-28, x);
+      x = fma(static_cast<double>(ac[1][e]), 0x1p-21, x);
+      x = fma(static_cast<double>(ac[0][e]), 0x1p-14, x);
+      return (fe == kSliceNonFinite || aex[e] == kSliceNonFinite) ? __builtin_nan("") : ldexp(x, aex[e] + fe);
+    };
     if (paired) {
       // Rows e and e+1 are adjacent: lanes 2c and 2c+1 swap one value, and each
       // stores two adjacent columns of its row (16-byte partials, 8-byte C).
       const bool odd = lr & 1;
-      const int gnc = gn < N ? gn : N - 1;
-      const int fe = Be[gnc];
-      const bool bad_col = fe == kSliceNonFinite;
-      const double bv = (direct && bias != nullptr) ? static_cast<double>(bias[gnc]) : 0.0;
-      const double bv_pair = __shfl_xor(bv, 1, 64);  // the partner column's bias
+      const double bv_pair = xor_lane<1>(bv);  // the partner column's bias
       const int col = odd ? gn - 1 : gn;
 #pragma unroll
       for (int e = 0; e < 16; e += 2) {
         const int gm = m0 + wr + 8 * (e >> 2) + 4 * lg + (e & 3);
-        double v[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int r = gm + h < M ? gm + h : M - 1;
-          // sum_d acc_d 2^-7(d+2): each term exact in fp64, five terms
-          double x = 0.0;
-#pragma unroll
-          for (int d = S - 1; d >= 0; --d) x += ldexp(static_cast<double>(ac[d][e + h]), -7 * (d + 2));
-          const int ae = Ae[r];
-          v[h] = (bad_col || ae == kSliceNonFinite) ? __builtin_nan("") : ldexp(x, ae + fe);
-        }
-        const double recv = __shfl_xor(odd ? v[0] : v[1], 1, 64);
+        const double v0 = value(e), v1 = value(e + 1);
+        const double recv = xor_lane<1>(odd ? v0 : v1);
         const int row = odd ? gm + 1 : gm;
         if (row < M && col < N) {
-          const double lo = odd ? recv : v[0], hi = odd ? v[1] : recv;
+          const double lo = odd ? recv : v0, hi = odd ? v1 : recv;
           if (direct) {
             const double b_lo = odd ? bv_pair : bv, b_hi = odd ? bv : bv_pair;  // columns col, col + 1
             *reinterpret_cast<float2*>(C + static_cast<size_t>(row) * N + col) =
@@ -306,18 +319,11 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
       continue;
     }
     if (gn >= N) continue;
-    const int fe = Be[gn];
-    const double bv = (direct && bias != nullptr) ? static_cast<double>(bias[gn]) : 0.0;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int gm = m0 + wr + 8 * (e >> 2) + 4 * lg + (e & 3);
       if (gm >= M) continue;
-      // sum_d acc_d 2^-7(d+2): each term exact in fp64, five terms
-      double v = 0.0;
-#pragma unroll
-      for (int d = S - 1; d >= 0; --d) v += ldexp(static_cast<double>(ac[d][e]), -7 * (d + 2));
-      const int ae = Ae[gm];
-      v = (fe == kSliceNonFinite || ae == kSliceNonFinite) ? __builtin_nan("") : ldexp(v, ae + fe);
+      const double v = value(e);
       if (direct)
         C[static_cast<size_t>(gm) * N + gn] = static_cast<float>(v + bv);
       else
