@@ -279,23 +279,21 @@ def measure(cfg, steps, warmup, no_graph=False, protocol_loops=5):
         r.forward()
     torch.cuda.synchronize()
     log(f"warmup {warmup} done")
-    # One forward captured as a HIP graph (the ~500 launches of the music model
-    # replay without host round trips); its output is checked against the eager
-    # forward before timing.
+    # One forward captured by the library as a HIP graph (dit_forward_graph_create:
+    # the few hundred launches of the music model replay as one); its output is
+    # checked against the eager forward before timing.
     step = r.forward
     if not no_graph and not loop:
         eager = r.forward().clone()
         torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            r.forward()
-        graph.replay()
+        graph = dit.ForwardGraph(r.model, r.batch, r.x_in, r.cond, r.out, r.ws)
+        graph.launch()
         torch.cuda.synchronize()
         if not torch.equal(r.out, eager):
             log("graph replay differs from the eager forward; timing eager launches")
         else:
-            step = graph.replay
-            log("timing replays of one captured forward graph")
+            step = graph.launch
+            log(f"timing replays of one captured forward graph ({graph.nodes} nodes)")
 
     # timed region: exactly K forwards between two synchronisations
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -352,6 +352,30 @@ int dit_cfg_denoise_loop(dit_model* m, const dit_batch* b, float* latents_dev,
                          const float* cond_table_dev, const float* dt_table_dev, float w,
                          int n_steps, void* ws_dev, size_t ws_bytes, dit_stream_t stream);
 
+/* ------------------------------------------------------------------ captured forwards
+ * dit_forward recorded once as a HIP graph and replayed with one launch, so a
+ * forward's few hundred kernel launches cost the host one call (page "the
+ * 2.4B fp32 DiT onto the device, staged once", section "Speed": the device
+ * loop's fixed per-loop cost measured beside the per-forward slope).  The
+ * graph holds the kernels, their arguments and the buffer addresses given at
+ * creation: in_dev, cond_dev, out_dev and ws_dev must stay allocated while it
+ * lives, and each launch reads their contents as they are then (write new
+ * latents into in_dev and launch again).  Creation captures on a stream of
+ * its own and launches nothing; it returns the errors of dit_forward, and
+ * DIT_E_UNSUPPORTED while per-launch profiling (dit_profile_begin) or
+ * DIT_SYNC_CHECK is on.  The caller owns the graph (dit_graph_destroy).
+ * Launches of one graph on one stream run in order; two launches of it that
+ * overlap in time race on its workspace. */
+typedef struct dit_graph dit_graph;
+int dit_forward_graph_create(dit_model* m, const dit_batch* b, const float* in_dev, const float* cond_dev,
+                             float* out_dev, void* ws_dev, size_t ws_bytes, dit_graph** out);
+/* One replay of the captured forward, asynchronous on `stream`; DIT_E_HIP if
+ * the launch fails. */
+int dit_graph_launch(dit_graph* g, dit_stream_t stream);
+/* The number of nodes (kernels and copies) the graph holds. */
+int dit_graph_nodes(const dit_graph* g, size_t* nodes);
+void dit_graph_destroy(dit_graph* g);
+
 /* ------------------------------------------------------------------ op-level calls
  * The kernels the block is made of, exposed for per-op parity checks and
  * timing: the shared ops the pages compose the block from (page "port the

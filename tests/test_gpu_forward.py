@@ -680,3 +680,53 @@ def test_bf16_forward_equals_block_by_block_bits(H):
     torch.cuda.synchronize()
     assert (out - r.x_in).abs().max().item() > 1e-3
     assert torch.equal(out, x)
+
+
+@pytest.mark.parametrize("name", ["c1", "c4_small"])
+def test_forward_graph_replays_match_eager(H, name):
+    """dit_forward captured by the library as one HIP graph
+    (dit_forward_graph_create) replays equal to the eager forward bit for bit,
+    three times with eager forwards between; a replay after new latents are
+    written into the captured input equals the eager forward of those
+    latents."""
+    dit = H.dit
+    cfg = S.get_config("c1") if name == "c1" else C4_SMALL
+    w = S.all_weights(cfg, 0, threads=8)
+    r = H.Runner(cfg, 0, model=_stage(H, cfg, w))
+    eager = r.forward().clone()
+    torch.cuda.synchronize()
+    out = torch.empty_like(r.out)
+    g = dit.ForwardGraph(r.model, r.batch, r.x_in, r.cond, out, r.ws)
+    assert g.nodes > 0
+    for _ in range(3):
+        out.fill_(float("nan"))
+        g.launch()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+        again = r.forward()  # eager work on the same workspace between replays
+        torch.cuda.synchronize()
+        assert torch.equal(again, eager)
+    x0 = r.x_in.clone()
+    r.x_in.mul_(0.5)
+    want = r.forward().clone()
+    g.launch()
+    torch.cuda.synchronize()
+    assert torch.equal(out, want) and not torch.equal(want, eager)
+    r.x_in.copy_(x0)
+    g.close()
+
+
+def test_forward_graph_refused_while_profiling(H):
+    """Per-launch profiling records events at every launch, which a capture
+    would swallow: creating a graph then fails with DIT_E_UNSUPPORTED and
+    launches nothing."""
+    dit = H.dit
+    cfg = S.get_config("c1")
+    r = H.Runner(cfg, 0, model=_stage(H, cfg, S.all_weights(cfg, 0, threads=8)))
+    dit.dit_profile_begin()
+    try:
+        with pytest.raises(dit.DitError) as e:
+            dit.ForwardGraph(r.model, r.batch, r.x_in, r.cond, r.out, r.ws)
+        assert e.value.status == "DIT_E_UNSUPPORTED" and "profil" in str(e.value)
+    finally:
+        dit.dit_profile_end()

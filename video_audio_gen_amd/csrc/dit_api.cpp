@@ -1066,6 +1066,79 @@ extern "C" int dit_cfg_denoise_loop(dit_model* m, const dit_batch* b, float* lat
   return DIT_OK;
 }
 
+// ============================================================================ captured forwards
+// One forward's launches recorded once into a HIP graph and replayed as a
+// single launch: the kernels, their arguments and the buffers are fixed at
+// capture, the buffers' contents are read when the graph runs.
+struct dit_graph {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  size_t nodes = 0;
+};
+
+extern "C" int dit_forward_graph_create(dit_model* m, const dit_batch* b, const float* in_dev, const float* cond_dev,
+                                        float* out_dev, void* ws_dev, size_t ws_bytes, dit_graph** out) {
+  if (out == nullptr) return set_error(DIT_E_INVALID, "dit_forward_graph_create: null output handle");
+  *out = nullptr;
+  WsPlan p;
+  DIT_TRY(check_run(m, b, ws_dev, ws_bytes, &p));
+  if (in_dev == nullptr || cond_dev == nullptr || out_dev == nullptr)
+    return set_error(DIT_E_INVALID, "dit_forward_graph_create: null input, cond or output");
+  if (sync_check_enabled())
+    return set_error(DIT_E_UNSUPPORTED, "dit_forward_graph_create: DIT_SYNC_CHECK synchronises after every launch, "
+                                        "which a capture cannot record");
+  if (g_prof_on.load())
+    return set_error(DIT_E_UNSUPPORTED, "dit_forward_graph_create: per-launch profiling is on (dit_profile_begin); "
+                                        "end it before capturing");
+  hipStream_t cs = nullptr;
+  hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+  if (e != hipSuccess) return set_error(DIT_E_HIP, "dit_forward_graph_create: %s", hipGetErrorString(e));
+  e = hipStreamBeginCapture(cs, hipStreamCaptureModeRelaxed);
+  if (e != hipSuccess) {
+    (void)hipStreamDestroy(cs);
+    return set_error(DIT_E_HIP, "dit_forward_graph_create: begin capture: %s", hipGetErrorString(e));
+  }
+  const int r = run_forward(m, b, in_dev, cond_dev, out_dev, static_cast<char*>(ws_dev), p, cs);
+  hipGraph_t g = nullptr;
+  e = hipStreamEndCapture(cs, &g);  // always ends the capture, also after a failed launch
+  (void)hipStreamDestroy(cs);
+  if (r != DIT_OK || e != hipSuccess || g == nullptr) {
+    if (g != nullptr) (void)hipGraphDestroy(g);
+    return r != DIT_OK ? r : set_error(DIT_E_HIP, "dit_forward_graph_create: end capture: %s", hipGetErrorString(e));
+  }
+  hipGraphExec_t x = nullptr;
+  e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    return set_error(DIT_E_HIP, "dit_forward_graph_create: instantiate: %s", hipGetErrorString(e));
+  }
+  dit_graph* h = new dit_graph;
+  h->graph = g;
+  h->exec = x;
+  (void)hipGraphGetNodes(g, nullptr, &h->nodes);
+  *out = h;
+  return DIT_OK;
+}
+
+extern "C" int dit_graph_launch(dit_graph* g, dit_stream_t stream) {
+  if (g == nullptr) return set_error(DIT_E_INVALID, "dit_graph_launch: null graph");
+  DIT_HIP(hipGraphLaunch(g->exec, reinterpret_cast<hipStream_t>(stream)));
+  return DIT_OK;
+}
+
+extern "C" int dit_graph_nodes(const dit_graph* g, size_t* nodes) {
+  if (g == nullptr || nodes == nullptr) return set_error(DIT_E_INVALID, "dit_graph_nodes: null argument");
+  *nodes = g->nodes;
+  return DIT_OK;
+}
+
+extern "C" void dit_graph_destroy(dit_graph* g) {
+  if (g == nullptr) return;
+  if (g->exec != nullptr) (void)hipGraphExecDestroy(g->exec);
+  if (g->graph != nullptr) (void)hipGraphDestroy(g->graph);
+  delete g;
+}
+
 // ============================================================================ op-level calls
 
 extern "C" int dit_gemm_splits(int dtype, int N, int K, int* splits) {

@@ -108,8 +108,12 @@ _SIGS = {
     "dit_counters": [ctypes.POINTER(ctypes.c_int64), _I],
     "dit_profile_begin": [],
     "dit_profile_end": [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double), _I],
+    "dit_forward_graph_create": [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, ctypes.POINTER(ctypes.c_void_p)],
+    "dit_graph_launch": [_P, _P],
+    "dit_graph_nodes": [_P, ctypes.POINTER(ctypes.c_size_t)],
 }
-_VOID = {"dit_model_destroy": [_P], "dit_batch_destroy": [_P], "dit_counters_reset": []}
+_VOID = {"dit_model_destroy": [_P], "dit_batch_destroy": [_P], "dit_counters_reset": [],
+         "dit_graph_destroy": [_P]}
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -382,6 +386,39 @@ def dit_block_forward(model: Model, block: int, x, mod, batch: Batch, ws, stream
 def dit_forward(model: Model, batch: Batch, inp, cond, out, ws, stream=None):
     _check(load().dit_forward(model.handle, batch.handle, _ptr(inp), _ptr(cond), _ptr(out), _ptr(ws),
                               ws.numel() * ws.element_size(), _stream(stream)))
+
+
+class ForwardGraph:
+    """dit_forward captured once as a HIP graph (dit_forward_graph_create); launch() replays it.
+
+    Keeps the tensors it was captured on alive: a replay reads their current contents."""
+
+    def __init__(self, model: Model, batch: Batch, inp, cond, out, ws):
+        self._keep = (model, batch, inp, cond, out, ws)
+        h = ctypes.c_void_p()
+        _check(load().dit_forward_graph_create(model.handle, batch.handle, _ptr(inp), _ptr(cond), _ptr(out), _ptr(ws),
+                                               ws.numel() * ws.element_size(), ctypes.byref(h)))
+        self.handle = h
+
+    def launch(self, stream=None):
+        _check(load().dit_graph_launch(self.handle, _stream(stream)))
+
+    @property
+    def nodes(self) -> int:
+        n = ctypes.c_size_t()
+        _check(load().dit_graph_nodes(self.handle, ctypes.byref(n)))
+        return int(n.value)
+
+    def close(self):
+        if self.handle is not None and self.handle.value is not None:
+            load().dit_graph_destroy(self.handle)
+        self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def dit_denoise_step(model: Model, batch: Batch, latents, cond, dt, ws, stream=None):
