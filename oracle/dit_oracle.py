@@ -40,7 +40,9 @@ Precision modes:
              ``block_forward``).  The residual stream, the modulation table,
              the time embedding and the projections in and out stay fp32;
   'mxfp8' -- as 'bf16', with the four block GEMMs' operands re-quantized to
-             MXFP8 (``quantize_mx8``) and dequantized before the product.
+             MXFP8 (``quantize_mx8``) and dequantized before the product;
+  'mxfp4' -- as 'mxfp8', with the four block GEMMs' weights re-quantized to
+             MXFP4 (``quantize_mx4``) instead (activations stay MXFP8).
 
 Pins: tests/test_oracle_pins.py checks every function here against closed
 forms, invariants and brute force; tests/test_oracle_wiring_pins.py pins the
@@ -69,6 +71,7 @@ __all__ = [
     "denoise_step_conditions", "denoise_loop", "split_mlp", "cfg_pairs", "cfg_combine",
     "cfg_denoise_loop", "e4m3_value", "e8m0_value", "e4m3_encode", "e4m3_encode_array", "quantize_mx8", "dequantize_mx8",
     "linear_mx8", "centered_rope_cache", "rms_affine", "vit_block_forward",
+    "e2m1_value", "e2m1_encode", "e2m1_encode_array", "quantize_mx4", "dequantize_mx4", "pack_e2m1", "linear_mx4",
 ]
 
 
@@ -94,12 +97,12 @@ def round_f32(x: np.ndarray) -> np.ndarray:
 
 def _store(x: np.ndarray, mode: str) -> np.ndarray:
     """A bf16 storage point of the block stream (identity in 'fp64' mode)."""
-    return round_bf16(x) if mode in ("bf16", "mxfp8") else x
+    return round_bf16(x) if mode in ("bf16", "mxfp8", "mxfp4") else x
 
 
 def _store_f32(x: np.ndarray, mode: str) -> np.ndarray:
     """An fp32 storage point of a bf16 stream (identity in 'fp64' mode)."""
-    return round_f32(x) if mode in ("bf16", "mxfp8") else x
+    return round_f32(x) if mode in ("bf16", "mxfp8", "mxfp4") else x
 
 
 # ----------------------------------------------------------------------------- MX block scaling (fp8)
@@ -222,6 +225,112 @@ def linear_mx8(x: np.ndarray, W: np.ndarray, b: np.ndarray, accum: str = "fp64")
     dequantized, then the plain product (the scaled matrix cores' definition)."""
     xq = dequantize_mx8(*quantize_mx8(x))
     wq = dequantize_mx8(*quantize_mx8(W))
+    return linear(xq, wq, b, accum)
+
+
+# ----------------------------------------------------------------------------- MX block scaling (fp4 weights)
+#
+# The pages' FP4 path keeps the activations at 16 bits and quantizes the
+# weights to 4-bit values with block scales (W4A16; page "port the
+# MiniMax-H3 omni-modal video+audio DiT", update "NVFP4 arm grounded").  The
+# matrix cores here multiply an FP4 operand only against another MX operand,
+# so the reading taken: the four block GEMMs' weights re-quantized to MXFP4 at
+# staging -- OCP E2M1 values, one E8M0 scale per 32 along K -- against the
+# activations in MXFP8 as above (W4A8).  E2M1: a sign bit, two exponent bits
+# (bias 1) and one mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; no
+# Inf or NaN.  The scale of a block is the smallest power of two 2^s with
+# max|v| <= 6 2^s (the OCP rule 2^(floor(log2 max|v|) - 2) would clamp the
+# block maximum whenever its leading digits exceed 1.5), each value divided
+# by it is rounded to the nearest E2M1 value, ties to the even mantissa bit;
+# the zero and non-finite blocks as for MXFP8.  Stored two values per byte,
+# the value at even K in the low nibble.
+
+E2M1_MAX = 6.0
+
+
+def e2m1_value(code: int) -> float:
+    """Value of an OCP FP4 E2M1 nibble: sign (bit 3), 2 exponent bits (bias 1),
+    1 mantissa bit; exponent 0 is subnormal (m / 2)."""
+    code = int(code) & 0xF
+    sgn = -1.0 if code & 0x8 else 1.0
+    e, m = (code >> 1) & 3, code & 1
+    if e == 0:
+        return sgn * m * 0.5
+    return sgn * (1.0 + m / 2.0) * 2.0 ** (e - 1)
+
+
+def e2m1_encode(y: float) -> int:
+    """Round y to the nearest E2M1 value (ties to the even mantissa bit),
+    clamped to +-6; the sign of y kept, -0 included."""
+    sgn = 0x8 if math.copysign(1.0, y) < 0 else 0
+    a = abs(y)
+    if a >= E2M1_MAX:
+        return sgn | 0x7
+    if a < 1.0:                             # subnormal range: steps of 0.5 (two steps reach 1.0, code 2)
+        return sgn | _half_even(a * 2.0)
+    e = math.frexp(a)[1] - 1                # a = mant 2^e, mant in [1, 2), e in {0, 1, 2}
+    q = _half_even((a / 2.0 ** e - 1.0) * 2.0)
+    if q == 2:
+        e, q = e + 1, 0
+    return sgn | ((e + 1) << 1) | q
+
+
+def e2m1_encode_array(y: np.ndarray) -> np.ndarray:
+    """``e2m1_encode`` over an array (the same steps, vectorized: np.rint
+    rounds half to even)."""
+    y = np.asarray(y, np.float64)
+    sgn = np.where(np.signbit(y), 0x8, 0).astype(np.int64)
+    a = np.abs(y)
+    sub = a < 1.0
+    e = np.frexp(np.where(sub, 1.0, a))[1] - 1
+    q = np.rint((np.where(sub, 1.0, a) / np.exp2(e.astype(np.float64)) - 1.0) * 2.0).astype(np.int64)
+    carry = q == 2
+    e = np.where(carry, e + 1, e)
+    q = np.where(carry, 0, q)
+    mag = np.where(sub, np.rint(a * 2.0).astype(np.int64), ((e + 1) << 1) | q)
+    mag = np.where(a >= E2M1_MAX, 0x7, mag)
+    return (sgn | mag).astype(np.uint8)
+
+
+def quantize_mx4(v: np.ndarray):
+    """MXFP4 quantization of the rows of v [R, K] (K a multiple of 32):
+    returns (codes uint8 [R, K], one E2M1 code 0..15 per value, and
+    scales uint8 [R, K/32])."""
+    v = np.asarray(v, np.float64)
+    R, K = v.shape
+    assert K % MX_BLOCK == 0
+    blk = v.reshape(R, K // MX_BLOCK, MX_BLOCK)
+    finite = np.isfinite(blk).all(axis=2)
+    amax = np.where(finite, np.abs(np.where(np.isfinite(blk), blk, 0.0)).max(axis=2), 0.0)
+    e = np.frexp(amax)[1] - 1                                        # amax = m 2^e, m in [1, 2)
+    over = amax / np.exp2(e.astype(np.float64)) > E2M1_MAX / 4.0       # m > 1.5: 2^(e-2) would clamp
+    shared = np.clip(e - 2 + over, -127, 127)
+    scales = np.where(amax > 0, shared + 127, 0)
+    scales = np.where(finite, scales, 255).astype(np.uint8)
+    X = np.exp2(np.where(amax > 0, shared, 0).astype(np.float64))[..., None]
+    codes = e2m1_encode_array(np.where(finite[..., None], blk, 0.0) / X)
+    codes = np.where(finite[..., None], codes, 0).astype(np.uint8)
+    return codes.reshape(R, K), scales
+
+
+def dequantize_mx4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Values of MXFP4 rows: E2M1 value times its block's E8M0 scale."""
+    vals = np.array([e2m1_value(c) for c in range(16)], np.float64)[np.asarray(codes, np.uint8) & 0xF]
+    sc = np.array([e8m0_value(b) for b in range(256)], np.float64)[np.asarray(scales, np.uint8)]
+    return vals * np.repeat(sc, MX_BLOCK, axis=-1)
+
+
+def pack_e2m1(codes: np.ndarray) -> np.ndarray:
+    """Two E2M1 codes per byte, the code at even K in the low nibble: [R, K] -> [R, K/2]."""
+    c = np.asarray(codes, np.uint8) & 0xF
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def linear_mx4(x: np.ndarray, W: np.ndarray, b: np.ndarray, accum: str = "fp64") -> np.ndarray:
+    """y = Q8(x) Q4(W)^T + b: the activation quantized to MXFP8 and the weight
+    to MXFP4 along K, both dequantized, then the plain product."""
+    xq = dequantize_mx8(*quantize_mx8(x))
+    wq = dequantize_mx4(*quantize_mx4(W))
     return linear(xq, wq, b, accum)
 
 
@@ -557,9 +666,10 @@ def block_forward(cfg, x: np.ndarray, mod: np.ndarray, bw: Dict[str, np.ndarray]
     m  = gated SiLU of u                                        (bf16 store)
     x  = x + gate_mlp[c] * (m W_2^T + b)                        (fp32 store)
 
-    c = cond_idx of the token.  The storage points apply in 'bf16' and
-    'mxfp8' mode; in 'mxfp8' mode the four GEMMs run on MXFP8 re-quantized
-    operands (``linear_mx8``).  ``accum`` selects the GEMM accumulation (see
+    c = cond_idx of the token.  The storage points apply in 'bf16', 'mxfp8'
+    and 'mxfp4' mode; in 'mxfp8' mode the four GEMMs run on MXFP8 re-quantized
+    operands (``linear_mx8``), in 'mxfp4' mode on MXFP8 activations against
+    MXFP4 weights (``linear_mx4``).  ``accum`` selects the GEMM accumulation (see
     ``linear``).
     Reading taken: the residual stream and both projection outputs feeding it
     stay fp32, because a bf16 rounding of those values alone moves a block's
@@ -571,7 +681,7 @@ def block_forward(cfg, x: np.ndarray, mod: np.ndarray, bw: Dict[str, np.ndarray]
     m_tok = mod[ci]  # [N, 6, D]
     p = f"blocks.{b}."
     W = lambda n: bw[p + n]  # noqa: E731
-    gemm = linear_mx8 if mode == "mxfp8" else linear
+    gemm = linear_mx8 if mode == "mxfp8" else linear_mx4 if mode == "mxfp4" else linear
     lin = lambda a, w, bias: gemm(a, w, bias, accum)  # noqa: E731
 
     h = _store(modulate(norm(x, cfg.norm, cfg.norm_eps), m_tok[:, 0], m_tok[:, 1]), mode)
@@ -732,8 +842,8 @@ def forward(cfg, weights: Callable[[int], Dict[str, np.ndarray]], islands: Dict[
     only the fp32 output heads) -> gather -> fp32 out-projection -> unpatchify.
     Without: tokens in, tokens out.  Returns {'latent.{i}' or 'x': array}.
     """
-    mode = mode or ("fp64" if cfg.stream != "bf16" else ("mxfp8" if getattr(cfg, "gemm", "stream") == "mxfp8"
-                                                         else "bf16"))
+    gemm_fmt = getattr(cfg, "gemm", "stream")
+    mode = mode or ("fp64" if cfg.stream != "bf16" else (gemm_fmt if gemm_fmt in ("mxfp8", "mxfp4") else "bf16"))
     layout = pack_layout(cfg)
     cos, sin = rope_cache(cfg)
     cu = layout["cu_seqlens"]

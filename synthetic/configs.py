@@ -89,7 +89,7 @@ class DitConfig:
     denoise_steps: int = 0
     shifts: Tuple[float, ...] = field(default_factory=tuple)
     cfg_replicate_latent: bool = False  # segment j + P reads the latent of segment j (P = half the segments)
-    gemm: str = "stream"         # 'stream' | 'mxfp8': format of the four block GEMMs of a bf16 stream
+    gemm: str = "stream"         # 'stream' | 'mxfp8' | 'mxfp4' (MXFP4 weights, MXFP8 activations): the four block GEMMs of a bf16 stream
     qkv_layout: str = "concat"   # 'concat' [q_all | k_all | v_all] | 'per_head' [q k v of head 0 | ...]
     qk_norm: bool = False        # per-head RMS norm of q and k (no weight) before RoPE
 
@@ -155,6 +155,8 @@ C5 = DitConfig(
 # The 64-block model with its four block GEMMs on MXFP8 operands (the low-precision arm).
 C3_MX = replace(C3, name="c3_block_mxfp8", gemm="mxfp8")
 C4_MX = replace(C4, name="c4_full_mxfp8", gemm="mxfp8")
+C3_MX4 = replace(C3, name="c3_block_mxfp4", gemm="mxfp4")
+C4_MX4 = replace(C4, name="c4_full_mxfp4", gemm="mxfp4")
 
 # The video VAE decoder's ViT block at the pages' width (32 heads x 64, rotary
 # on 0.75 of each head split over 3 axes, theta 100, fp32): per-head qkv rows,
@@ -167,7 +169,8 @@ VIT = DitConfig(
     cond_rows=(CondRow(0, 0),), n_requests=1, io=False, qkv_layout="per_head", qk_norm=True)
 
 CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5, C3_MX, C4_MX, VIT)}
-_SHORT = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5, "c3_mxfp8": C3_MX, "c4_mxfp8": C4_MX, "vit": VIT}
+_SHORT = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5, "c3_mxfp8": C3_MX, "c4_mxfp8": C4_MX,
+          "c3_mxfp4": C3_MX4, "c4_mxfp4": C4_MX4, "vit": VIT}
 
 
 def get_config(name: str) -> DitConfig:

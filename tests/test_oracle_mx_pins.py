@@ -137,7 +137,7 @@ def test_linear_mx8_is_exact_on_representable_operands():
     assert (np.abs(got - ref) <= bound).all() and np.abs(got - ref).max() > 0
 
 
-@pytest.mark.parametrize("mode", ["bf16", "mxfp8"])
+@pytest.mark.parametrize("mode", ["bf16", "mxfp8", "mxfp4"])
 def test_zero_gate_block_identity_holds_in_mxfp8_mode(mode):
     import synthetic as S
     from synthetic.configs import scaled
@@ -172,3 +172,101 @@ def test_mx_step_control_accumulation():
     mag = sum(np.abs(x[:, k:k + 64]) @ np.abs(w[:, k:k + 64]).T for k in range(0, 256, 64))
     assert np.all(np.abs(got - exact) <= 2.0 ** -17 * mag + 4 * 2.0 ** -24 * mag)
     assert np.abs(got - exact).max() > 0
+
+
+# ---------------------------------------------------------------- MXFP4 (E2M1 values, E8M0 scales per 32)
+
+def test_e2m1_hand_codes():
+    # S.EE.M, bias 1; exponent 0 subnormal (m / 2); the OCP FP4 value table
+    table = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    for c in range(8):
+        assert O.e2m1_value(c) == table[c]
+        assert O.e2m1_value(c | 8) == -table[c]
+    assert math.copysign(1.0, O.e2m1_value(8)) == -1.0
+    assert O.e2m1_value(0x17) == 6.0          # only the low nibble is a code
+
+
+def _e2m1_by_search(y):
+    """Nearest E2M1 value to y by search over the 8 magnitudes, ties to the
+    code whose mantissa bit is 0, clamped to +-6."""
+    sgn = 8 if math.copysign(1.0, y) < 0 else 0
+    a = min(abs(y), 6.0)
+    best = None
+    for c in range(8):
+        d = abs(O.e2m1_value(c) - a)
+        if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+            best = (d, c)
+    return sgn | best[1]
+
+
+def test_e2m1_encode_is_nearest_even_by_brute_force():
+    rng = np.random.default_rng(10)
+    ys = list(rng.standard_normal(500) * 3) + list(rng.uniform(-7, 7, 500))
+    ys += [(O.e2m1_value(c) + O.e2m1_value(c + 1)) / 2 for c in range(7)]   # every tie
+    ys += [0.0, -0.0, 6.0, 6.5, 100.0, -100.0, 0.25, 0.7499999, 0.7500001]
+    for y in ys:
+        assert O.e2m1_encode(float(y)) == _e2m1_by_search(float(y)), y
+    # the ties by hand: 0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4
+    for y, v in [(0.25, 0.0), (0.75, 1.0), (1.25, 1.0), (1.75, 2.0), (2.5, 2.0), (3.5, 4.0), (5.0, 4.0)]:
+        assert O.e2m1_value(O.e2m1_encode(y)) == v
+    ys = np.array(ys, np.float64)
+    assert np.array_equal(O.e2m1_encode_array(ys), np.array([O.e2m1_encode(float(y)) for y in ys], np.uint8))
+
+
+def test_quantize_mx4_hand_blocks():
+    v = np.zeros((4, 64))
+    v[0, :3] = [1.0, 3.0, 0.3]     # max 3 = 1.5 2^1 -> scale 2^(1-2) = 2^-1: 2 -> code 4, 6 -> code 7, 0.6 -> 0.5 (code 1)
+    v[0, 32] = 1.6                 # max 1.6 = 1.6 2^0 > 1.5 2^0 -> scale 2^-1 (2^-2 would clamp it): 3.2 -> 3 (code 5)
+    v[1, 5] = -2.0 ** -140         # below the smallest scale: rounds to -0 (code 8)
+    v[2, 3] = np.nan
+    v[3, 40] = np.inf
+    v[3, 0] = 6.0                  # exactly 6: scale 2^0, code 7
+    codes, scales = O.quantize_mx4(v)
+    assert scales[0, 0] == 126 and list(codes[0, :3]) == [4, 7, 1]
+    assert scales[0, 1] == 126 and codes[0, 32] == 5
+    d = O.dequantize_mx4(codes, scales)
+    assert d[0, 0] == 1.0 and d[0, 1] == 3.0 and d[0, 2] == 0.25 and d[0, 32] == 1.5
+    assert scales[1, 0] == 0 and codes[1, 5] == 8 and scales[1, 1] == 0 and not codes[1, 32:].any()
+    assert scales[2, 0] == 255 and scales[3, 1] == 255 and not codes[2, :32].any() and not codes[3, 32:].any()
+    assert scales[3, 0] == 127 and codes[3, 0] == 7 and d[3, 0] == 6.0
+    assert np.isnan(d[2, :32]).all() and np.isnan(d[3, 32:]).all()
+    # packing: the code at even K in the low nibble
+    p = O.pack_e2m1(codes)
+    assert p.shape == (4, 32) and p[0, 0] == 4 | (7 << 4) and p[0, 1] == 1 and p[3, 0] == 7
+
+
+def test_quantize_mx4_scale_is_minimal_and_error_bounded():
+    rng = np.random.default_rng(11)
+    v = rng.standard_normal((50, 256)) * np.exp2(rng.integers(-20, 20, (50, 1)))
+    codes, scales = O.quantize_mx4(v)
+    d = O.dequantize_mx4(codes, scales)
+    blk = np.abs(v).reshape(50, 8, 32).max(axis=2)
+    X = np.exp2(scales.astype(np.float64) - 127)
+    assert (blk <= 6 * X).all() and (blk > 3 * X).all()            # 2^s is the smallest fitting power of two
+    # in units of X, the grid steps 0.5 below 2, 1 in [2, 4) and 2 in [4, 6]: half a step per binade
+    y = np.abs(v) / np.repeat(X, 32, axis=1)
+    half_step = np.where(y < 2, 0.25, np.where(y < 4, 0.5, 1.0))
+    assert (np.abs(d - v) <= half_step * np.repeat(X, 32, axis=1) * (1 + 1e-12)).all()
+    # relative to the block max the worst case is a max near 5 X, half way between 4 and 6: error 1 X in 5 X
+    r = (np.abs(d - v).reshape(50, 8, 32).max(axis=2) / blk).max()
+    assert 0.15 < r <= 1 / 5 + 1e-12
+
+
+def test_linear_mx4_is_exact_on_representable_operands():
+    # weights already on the MXFP4 grid and activations on the MXFP8 grid quantize
+    # to themselves: the product is the plain fp64 product of the same numbers
+    rng = np.random.default_rng(12)
+    codes_x = rng.integers(0, 0x7F, (5, 64)) | (rng.integers(0, 2, (5, 64)) << 7)
+    x = O.dequantize_mx8(codes_x.astype(np.uint8), np.full((5, 2), 120, np.uint8))
+    x[:, 0] = 448 * 2.0 ** -7
+    x[:, 32] = 448 * 2.0 ** -7
+    w = O.dequantize_mx4(rng.integers(0, 16, (7, 64)).astype(np.uint8), np.full((7, 2), 124, np.uint8))
+    w[:, 0] = 6 * 2.0 ** -3
+    w[:, 32] = -6 * 2.0 ** -3
+    b = rng.standard_normal(7)
+    assert np.array_equal(O.linear_mx4(x, w, b), x @ w.T + b)
+    # and MXFP4 weights move a random product more than MXFP8 weights do
+    xr, wr = rng.standard_normal((9, 128)), rng.standard_normal((11, 128)) * 0.02
+    e4 = np.abs(O.linear_mx4(xr, wr, np.zeros(11)) - xr @ wr.T).max()
+    e8 = np.abs(O.linear_mx8(xr, wr, np.zeros(11)) - xr @ wr.T).max()
+    assert e4 > 2 * e8 > 0
