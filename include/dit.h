@@ -51,11 +51,17 @@ typedef enum dit_status {
 } dit_status;
 
 enum { DIT_F32 = 0, DIT_BF16 = 1, DIT_F64 = 2 /* residual stream of an fp32 model only */,
-       DIT_MXFP8 = 3 /* OCP E4M3 values with one E8M0 scale per 32 along K (dit_gemm, dit_quantize_mx8) */ };
-/* Format of the four block GEMMs of a bf16-stream model: the stream dtype, or
+       DIT_MXFP8 = 3 /* OCP E4M3 values with one E8M0 scale per 32 along K (dit_gemm, dit_quantize_mx8) */,
+       DIT_MXFP4 = 4 /* OCP E2M1 values, two per byte (even K in the low nibble), one E8M0 scale per 32
+                        along K (dit_gemm's weight operand, dit_quantize_mx4) */ };
+/* Format of the four block GEMMs of a bf16-stream model: the stream dtype;
  * MXFP8 re-quantized operands (weights at staging, activations before each
- * GEMM) on the scaled fp8 matrix cores. */
-enum { DIT_GEMM_STREAM = 0, DIT_GEMM_MXFP8 = 1 };
+ * GEMM) on the scaled fp8 matrix cores; or MXFP4 weights (re-quantized at
+ * staging) against the same MXFP8 activations on the same matrix cores
+ * (page "port the MiniMax-H3 omni-modal video+audio DiT", update "NVFP4 arm
+ * grounded": 4-bit weights with block scales; here W4A8, the FP4 operand
+ * needing an MX partner). */
+enum { DIT_GEMM_STREAM = 0, DIT_GEMM_MXFP8 = 1, DIT_GEMM_MXFP4 = 2 };
 enum { DIT_NORM_RMS = 0, DIT_NORM_LAYER = 1 };
 enum { DIT_MLP_GATE_UP = 0, DIT_MLP_VALUE_GATE = 1 };
 enum { DIT_IO_NONE = 0, DIT_IO_PATCH3D = 1, DIT_IO_CHANNEL_MAJOR = 2 };
@@ -99,7 +105,7 @@ typedef struct dit_config {
   int n_mod;         /* modalities (one AdaLN linear and one projection pair each) */
   int io;            /* 1: latents in / velocities out through fp32 projections; 0: tokens in/out */
   dit_modality mod[DIT_MAX_MODALITIES];
-  int gemm_format;   /* DIT_GEMM_*: DIT_GEMM_MXFP8 needs a bf16 stream and hidden, ffn multiples of 128
+  int gemm_format;   /* DIT_GEMM_*: DIT_GEMM_MXFP8 / _MXFP4 need a bf16 stream and hidden, ffn multiples of 128
                         (the low-precision arm; page "port the MiniMax-H3 omni-modal video+audio DiT",
                         update "NVFP4 arm grounded": the pages' is NVFP4, this GPU's matrix cores take MX) */
   int qkv_layout;    /* DIT_QKV_* */
@@ -391,7 +397,10 @@ void dit_graph_destroy(dit_graph* g);
 /* C[M,N] = A[M,K] . B[N,K]^T + bias[N] (bias may be NULL).  bf16: A, B bf16,
  * fp32 accumulation, C in c_dtype.  DIT_MXFP8: A, B given as bf16, both
  * re-quantized as dit_quantize_mx8 into ws, then multiplied on the scaled fp8
- * matrix cores (K a multiple of 128), C in c_dtype.  f32: A, B float32 (K a multiple of 4),
+ * matrix cores (K a multiple of 128), C in c_dtype.  DIT_MXFP4: A, B given as
+ * bf16, A re-quantized as dit_quantize_mx8 and B as dit_quantize_mx4 into ws,
+ * then multiplied on the same matrix cores with B's format FP4 (K a multiple
+ * of 128), C in c_dtype.  f32: A, B float32 (K a multiple of 4),
  * each row scaled by a power of two and cut into five 7-bit integer slices,
  * the slice products summed exactly on the int8 matrix cores (pairs whose
  * weight is below 2^-32 of the product dropped), combined in fp64 and
@@ -436,6 +445,16 @@ int dit_gemm_f32_noalloc(int M, int N, int K, const float* A, const float* B, co
  * fp32 global scale); this GPU's matrix cores take MX block scales.  x and
  * codes 16-byte aligned; device pointers; asynchronous. */
 int dit_quantize_mx8(int R, int K, const void* x, void* codes, void* scales, dit_stream_t stream);
+/* MXFP4 re-quantization of bf16 rows x [R, K] (K a multiple of 32): per 32
+ * consecutive values the smallest power-of-two scale 2^s with max|v| <= 6 2^s
+ * (E8M0 byte s + 127 into scales [R, K/32]), each v / 2^s rounded to the
+ * nearest OCP FP4 E2M1 value, ties to the even mantissa bit (codes [R, K/2],
+ * two per byte, the value at even K in the low nibble); an all-zero block
+ * takes byte 0, a block holding a NaN or an Inf byte 255 and zero codes
+ * (page "port the MiniMax-H3 omni-modal video+audio DiT", update "NVFP4 arm
+ * grounded": FP4 values with block scales, here in the OCP MX form).  x and
+ * codes 16-byte aligned; asynchronous on `stream`. */
+int dit_quantize_mx4(int R, int K, const void* x, void* codes, void* scales, dit_stream_t stream);
 
 /* h[N,D] (dtype) = norm(x[N,D]) * (1 + mod[c][scale_k]) + mod[c][shift_k],
  * c = cond_idx[n]; mod [n_cond, 6, D] f32; which = 0 (msa: shift 0, scale 1) or

@@ -1,0 +1,221 @@
+"""The MXFP4-weight arm through the C ABI: the device MXFP4 quantizer bit for
+bit against the oracle's, the scaled GEMM with MXFP8 activations against
+MXFP4 weights against the oracle's product of the dequantized operands
+(exact on small-integer products, which pins the FP4 operand's nibble order
+against the fp8 operand's bytes), and whole bf16-stream blocks and forwards
+with their four GEMMs on MXFP4 weights against the oracle's 'mxfp4' mode and
+its control arm."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synthetic as S
+from gpu_util import assert_bf16_parity, from_dev, rms, to_bf16_dev
+from synthetic.configs import Segment, scaled
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dit():
+    from video_audio_gen_amd import dit as d
+    d.load()
+    return d
+
+
+def _bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).float().numpy().astype(np.float64)
+
+
+def _quantize_dev(dit, x):
+    R, K = x.shape
+    codes = torch.empty(R, K // 2, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(R, K // 32, dtype=torch.uint8, device="cuda")
+    dit.dit_quantize_mx4(torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).cuda(), codes, scales)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), scales.cpu().numpy()
+
+
+@pytest.mark.parametrize("R,K", [(7, 32), (300, 6144), (64, 16384), (1, 128)])
+def test_quantize_mx4_bit_exact(dit, R, K):
+    rng = np.random.default_rng(R + K + 4)
+    x = rng.standard_normal((R, K)) * np.exp2(rng.integers(-30, 30, (R, 1)))
+    if K >= 128 and R >= 6:
+        x[0, :32] = 0.0
+        x[0, 5] = -0.0                                 # all-zero block with a -0
+        x[1, 40] = np.nan                              # NaN block
+        x[2, 70] = -np.inf                             # Inf block
+        x[3, :32] = 0.01
+        x[3, 0] = 1.5                                  # max mantissa exactly 1.5: scale 2^-2
+        x[4, :32] = 0.01
+        x[4, 0] = 1.5078125                            # next bf16 above: scale 2^-1
+        x[5, :8] = [6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]   # scale 2^0 and every E2M1 tie
+    x = _bf16(x)
+    codes_o, scales_o = O.quantize_mx4(x)
+    codes, scales = _quantize_dev(dit, x)
+    assert np.array_equal(scales, scales_o)
+    assert np.array_equal(codes, O.pack_e2m1(codes_o))
+
+
+def test_quantize_mx4_every_bf16_value(dit):
+    """Every bf16 bit pattern (NaNs and infinities included) through the device
+    quantizer, bit for bit against the oracle: in blocks of 32 consecutive
+    patterns, shifted by 16, and in a seeded shuffle (mixed magnitudes: most
+    values of a block fall to zero or the smallest codes)."""
+    pats = np.arange(65536, dtype=np.uint32) << 16
+    with np.errstate(invalid="ignore"):
+        vals = pats.view(np.float32).astype(np.float64)
+    rng = np.random.default_rng(8)
+    x = np.concatenate([vals, np.roll(vals, 16), vals[rng.permutation(65536)]]).reshape(-1, 128)
+    codes_o, scales_o = O.quantize_mx4(x)
+    codes, scales = _quantize_dev(dit, x)
+    assert np.array_equal(scales, scales_o)
+    assert np.array_equal(codes, O.pack_e2m1(codes_o))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (300, 320, 256), (513, 768, 384), (65, 97, 128),
+                                   (26624 // 8, 18432 // 8, 6144), (200, 6144, 16384)])
+def test_gemm_mx4(dit, M, N, K):
+    rng = np.random.default_rng(M + N + K + 4)
+    A = _bf16(rng.standard_normal((M, K)))
+    B = _bf16(rng.standard_normal((N, K)) * 0.02)
+    bias = rng.standard_normal(N).astype(np.float32)
+    ref = O.linear_mx4(A, B, bias)
+    Ad, Bd = to_bf16_dev(A), to_bf16_dev(B)
+    C32 = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    dit.dit_gemm(Ad, Bd, torch.from_numpy(bias).cuda(), C32, mxfp4=True)
+    g = from_dev(C32)
+    Aq = O.dequantize_mx8(*O.quantize_mx8(A))
+    Bq = O.dequantize_mx4(*O.quantize_mx4(B))
+    mag = np.abs(Aq) @ np.abs(Bq).T
+    e = np.abs(g - ref) / mag
+    print(f"mx4 gemm {M}x{N}x{K}: max|d| {np.abs(g - ref).max():.3e} rms {rms(ref):.3e} "
+          f"err/sum|ab|: max {e.max():.3e} mean {e.mean():.3e} (2^{np.log2(max(e.max(), 1e-30)):.1f})")
+    # as for MXFP8: the instruction sums a step's 64 exact products on a grid
+    # well below fp32; the error is measured against their magnitude sum
+    assert e.max() <= 2.0 ** -14
+    C16 = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    dit.dit_gemm(Ad, Bd, torch.from_numpy(bias).cuda(), C16, mxfp4=True)
+    assert torch.equal(C16, C32.to(torch.bfloat16))
+
+
+def test_gemm_mx4_exact_on_small_integer_products(dit):
+    """A of small integers (MXFP8-exact), B of E2M1 values times one power of
+    two per block, every partial sum an integer multiple of 2^-2 below 2^14:
+    the product must come out exact.  A wrong nibble order inside a byte, a
+    wrong block, lane half or scale byte shows as a wrong value."""
+    rng = np.random.default_rng(6)
+    M, N, K = 96, 160, 256
+    A = rng.integers(-3, 4, (M, K)).astype(np.float64)
+    A[:, ::32] = 4.0
+    A *= np.exp2(rng.integers(0, 2, (M, K // 32))).repeat(32, axis=1)
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0])
+    B = grid[rng.integers(0, 7, (N, K))] * rng.choice([-1.0, 1.0], (N, K))
+    B[:, 1::32] = 6.0            # each block's max 6: its scale is 2^0 (times the block's power below)
+    B *= np.exp2(rng.integers(0, 2, (N, K // 32))).repeat(32, axis=1)
+    ref = A @ B.T
+    assert (np.abs(A) @ np.abs(B).T).max() < 2 ** 14
+    assert np.array_equal(O.linear_mx4(A, B, np.zeros(N)), ref)
+    C = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    dit.dit_gemm(to_bf16_dev(A), to_bf16_dev(B), None, C, mxfp4=True)
+    assert np.array_equal(from_dev(C), ref)
+
+
+def test_gemm_mx4_packed_equals_alone_bits(dit):
+    rng = np.random.default_rng(3)
+    A = to_bf16_dev(_bf16(rng.standard_normal((700, 256))))
+    B = to_bf16_dev(_bf16(rng.standard_normal((384, 256)) * 0.02))
+    full = torch.empty(700, 384, dtype=torch.float32, device="cuda")
+    part = torch.empty(123, 384, dtype=torch.float32, device="cuda")
+    dit.dit_gemm(A, B, None, full, mxfp4=True)
+    dit.dit_gemm(A[300:423].contiguous(), B, None, part, mxfp4=True)
+    torch.cuda.synchronize()
+    assert torch.equal(full[300:423], part)
+
+
+# ----------------------------------------------------------------------------- whole blocks and forwards
+
+@pytest.fixture(scope="module")
+def H():
+    import harness
+    from video_audio_gen_amd import dit
+    dit.load()
+    return harness
+
+
+def _stage(H, cfg, w):
+    from video_audio_gen_amd import dit
+    m = dit.Model(cfg)
+    dit.dit_stage_weights(m, w, as_bf16=True)
+    dit.dit_stage_finalize(m)
+    return m
+
+
+def _run(H, cfg):
+    w = S.all_weights(cfg, 0, threads=8)
+    r = H.Runner(cfg, 0, model=_stage(H, cfg, w))
+    r.forward()
+    return r, w, r.output_numpy()
+
+
+def _oracle(cfg, w, inp, accum="fp64"):
+    isl = {k: v for k, v in w.items() if not k.startswith("blocks.")}
+    return O.forward(cfg, lambda b: w, isl, inp, threads=8, accum=accum)
+
+
+# control arm as for MXFP8: each 64-product step accumulated on a fixed-point
+# grid 16 bits below its magnitude sum (oracle.linear, accum 'mx_step')
+MX_CONTROL = "mx_step"
+
+C3_MX4_SMALL = scaled(S.get_config("c3_mxfp4"), segments=(Segment(0, (2, 8, 16), 0), Segment(1, (64,), 1)))
+C4_MX4_SMALL = scaled(S.get_config("c4_mxfp4"), n_blocks=2,
+                      segments=(Segment(0, (1, 4, 8), 0), Segment(1, (24,), 1), Segment(0, (2, 2, 4), 2),
+                                Segment(1, (40,), 3)))
+
+
+def test_c3_block_mxfp4_parity(H):
+    cfg = C3_MX4_SMALL
+    r, w, got = _run(H, cfg)
+    c = H.dit.dit_counters()
+    assert c["gemm_mx4"] >= 4 and c["gemm_mx8"] == 0
+    ref = _oracle(cfg, w, r.inp)
+    ctl = _oracle(cfg, w, r.inp, accum=MX_CONTROL)
+    assert_bf16_parity(got["x"], ref["x"], ctl["x"], "c3 block mxfp4 (320 tokens)")
+    # FP4 weights move the block further from the bf16 one than FP8 weights do
+    bf = _oracle(scaled(cfg, gemm="stream"), w, r.inp)
+    m8 = _oracle(scaled(cfg, gemm="mxfp8"), w, r.inp)
+    d4 = np.abs(ref["x"] - bf["x"]).max() / rms(bf["x"])
+    d8 = np.abs(m8["x"] - bf["x"]).max() / rms(bf["x"])
+    print(f"vs the bf16 oracle: mxfp4 max|d|/rms {d4:.3e}, mxfp8 {d8:.3e}")
+    assert d4 > d8 > 1e-3
+
+
+def test_c4_io_mxfp4_parity(H):
+    cfg = C4_MX4_SMALL
+    r, w, got = _run(H, cfg)
+    ref = _oracle(cfg, w, r.inp)
+    ctl = _oracle(cfg, w, r.inp, accum=MX_CONTROL)
+    for k in ref:
+        assert_bf16_parity(got[k], ref[k], ctl[k], f"c4 mxfp4 small (2 blocks) {k}")
+
+
+def test_mxfp4_packed_equals_alone(H):
+    cfg = C3_MX4_SMALL
+    w = S.all_weights(cfg, 0, threads=8)
+    m = _stage(H, cfg, w)
+    r = H.Runner(cfg, 0, model=m)
+    r.forward()
+    packed = r.output_numpy()["x"]
+    lay = O.pack_layout(cfg)
+    for i, seg in enumerate(cfg.segments):
+        a, b = int(lay["cu_seqlens"][i]), int(lay["cu_seqlens"][i + 1])
+        one = scaled(cfg, segments=(seg,))
+        batch = H.dit.Batch(m, one.segments, H.cond_modality(cfg))
+        ws = H.dit.workspace(batch)
+        xi = r.x_in[a:b].contiguous()
+        out = torch.empty_like(xi)
+        H.dit.dit_forward(m, batch, xi, r.cond, out, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), packed[a:b]), f"segment {i}"

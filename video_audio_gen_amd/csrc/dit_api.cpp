@@ -171,10 +171,10 @@ static int check_config(const dit_config* c) {
   for (int m = 0; m < c->n_mod; ++m)
     if (c->mod[m].rope_grid != DIT_ROPE_INTEGER && c->mod[m].rope_grid != DIT_ROPE_CENTERED)
       return set_error(DIT_E_INVALID, "config: modality %d rope_grid %d", m, c->mod[m].rope_grid);
-  if (c->gemm_format != DIT_GEMM_STREAM && c->gemm_format != DIT_GEMM_MXFP8)
+  if (c->gemm_format != DIT_GEMM_STREAM && c->gemm_format != DIT_GEMM_MXFP8 && c->gemm_format != DIT_GEMM_MXFP4)
     return set_error(DIT_E_INVALID, "config: gemm_format %d", c->gemm_format);
-  if (c->gemm_format == DIT_GEMM_MXFP8 && (!bf || c->hidden % 128 || c->ffn % 128))
-    return set_error(DIT_E_UNSUPPORTED, "MXFP8 GEMMs need a bf16 stream and hidden, ffn multiples of 128");
+  if (c->gemm_format != DIT_GEMM_STREAM && (!bf || c->hidden % 128 || c->ffn % 128))
+    return set_error(DIT_E_UNSUPPORTED, "MX GEMMs need a bf16 stream and hidden, ffn multiples of 128");
   return DIT_OK;
 }
 
@@ -196,6 +196,13 @@ static size_t mx8_bytes(int64_t R, int64_t K) { return ((static_cast<size_t>(R *
 static const uint8_t* mx8_scales(const void* w, int64_t R, int64_t K) {
   return static_cast<const uint8_t*>(w) + ((static_cast<size_t>(R * K) + 255) & ~size_t(255));
 }
+// Slot dtype of an MXFP4 GEMM weight [R, K]: E2M1 codes [R, K/2], then
+// (256-byte aligned) E8M0 scales [R, K/32].
+constexpr int kMx4 = 18;
+static size_t mx4_bytes(int64_t R, int64_t K) { return ((static_cast<size_t>(R * K / 2) + 255) & ~size_t(255)) + R * K / 32; }
+static const uint8_t* mx4_scales(const void* w, int64_t R, int64_t K) {
+  return static_cast<const uint8_t*>(w) + ((static_cast<size_t>(R * K / 2) + 255) & ~size_t(255));
+}
 
 struct Slot {
   std::string name;
@@ -213,7 +220,7 @@ struct BlockPtrs {
   const float* adaln_b[DIT_MAX_MODALITIES];
   const void *qkv_w, *out_w, *in_w, *mo_w;
   const float *qkv_b, *out_b, *in_b, *mo_b;
-  const uint8_t *qkv_s, *out_s, *in_s, *mo_s;  // MXFP8 weights: their E8M0 scales (else null)
+  const uint8_t *qkv_s, *out_s, *in_s, *mo_s;  // MXFP8 / MXFP4 weights: their E8M0 scales (else null)
 };
 
 struct dit_model {
@@ -272,6 +279,7 @@ static void build_contract(const dit_config& c, std::vector<Slot>* slots, size_t
     const int64_t n = ndim == 1 ? s0 : s0 * s1;
     s.bytes = dtype == kSlicedF32 ? gemm_f32_slices_bytes(static_cast<int>(s0), static_cast<int>(s1))
               : dtype == kMx8     ? mx8_bytes(s0, s1)
+              : dtype == kMx4     ? mx4_bytes(s0, s1)
                                   : static_cast<size_t>(n) * (dtype == DIT_BF16 ? 2 : 4);
     s.offset = off;
     s.staged = false;
@@ -289,7 +297,8 @@ static void build_contract(const dit_config& c, std::vector<Slot>* slots, size_t
   }
   const int in_order = (c.mlp == DIT_MLP_VALUE_GATE ? kRowsSwapHalves : 0) | (sd == DIT_BF16 ? kRowsPairs32 : 0);
   // dtype of the GEMM weights
-  const int gd = sd == DIT_BF16 ? (c.gemm_format == DIT_GEMM_MXFP8 ? kMx8 : DIT_BF16) : kSlicedF32;
+  const int gd = sd == DIT_BF16 ? (c.gemm_format == DIT_GEMM_MXFP8 ? kMx8 : c.gemm_format == DIT_GEMM_MXFP4 ? kMx4 : DIT_BF16)
+                                 : kSlicedF32;
   for (int b = 0; b < c.n_blocks; ++b) {
     const std::string p = "blocks." + std::to_string(b) + ".";
     for (int m = 0; m < c.n_mod; ++m) {
@@ -373,7 +382,7 @@ extern "C" int dit_stage_weights(dit_model* m, const dit_weight_view* views, int
     const int64_t count = sl.ndim == 1 ? sl.shape[0] : sl.shape[0] * sl.shape[1];
     const void* src = v.host;
     const bool sliced = sl.dtype == kSlicedF32;
-    const bool mx = sl.dtype == kMx8;
+    const bool mx = sl.dtype == kMx8 || sl.dtype == kMx4;
     const bool need_conv = v.dtype != sl.dtype || sl.row_order != 0;
     if (need_conv) {
       // rows gathered (and widened or rounded) into the slot dtype; a sliced
@@ -404,13 +413,16 @@ extern "C" int dit_stage_weights(dit_model* m, const dit_weight_view* views, int
       }
       src = conv.data();
       if (mx) {
-        // an MXFP8 weight is re-quantized from the (bf16) values as given
+        // an MX weight is re-quantized from the (bf16) values as given
         sliced_buf.resize(sl.bytes);
         uint8_t* codes = reinterpret_cast<uint8_t*>(sliced_buf.data());
-        const int64_t bad = host_quantize_mx8(sl.shape[0], sl.shape[1], reinterpret_cast<const float*>(conv.data()), codes,
-                                              codes + (mx8_scales(codes, sl.shape[0], sl.shape[1]) - codes));
+        const float* xs = reinterpret_cast<const float*>(conv.data());
+        const int64_t bad =
+            sl.dtype == kMx8
+                ? host_quantize_mx8(sl.shape[0], sl.shape[1], xs, codes, codes + (mx8_scales(codes, sl.shape[0], sl.shape[1]) - codes))
+                : host_quantize_mx4(sl.shape[0], sl.shape[1], xs, codes, codes + (mx4_scales(codes, sl.shape[0], sl.shape[1]) - codes));
         if (bad >= 0)
-          return set_error(DIT_E_INVALID, "weight '%s': row %lld holds a NaN or an Inf (MXFP8 GEMM weights must be finite)",
+          return set_error(DIT_E_INVALID, "weight '%s': row %lld holds a NaN or an Inf (MX GEMM weights must be finite)",
                            v.name, static_cast<long long>(bad));
         src = sliced_buf.data();
       }
@@ -466,12 +478,16 @@ extern "C" int dit_stage_finalize(dit_model* m) {
     bp.in_b = reinterpret_cast<const float*>(ptr(p + "mlp.in.bias"));
     bp.mo_w = ptr(p + "mlp.out.weight");
     bp.mo_b = reinterpret_cast<const float*>(ptr(p + "mlp.out.bias"));
-    const bool mx = c.gemm_format == DIT_GEMM_MXFP8;
     const int64_t D = c.hidden, F = c.ffn;
-    bp.qkv_s = mx ? mx8_scales(bp.qkv_w, 3 * D, D) : nullptr;
-    bp.out_s = mx ? mx8_scales(bp.out_w, D, D) : nullptr;
-    bp.in_s = mx ? mx8_scales(bp.in_w, 2 * F, D) : nullptr;
-    bp.mo_s = mx ? mx8_scales(bp.mo_w, D, F) : nullptr;
+    auto scales = [&](const void* w, int64_t R, int64_t K) -> const uint8_t* {
+      return c.gemm_format == DIT_GEMM_MXFP8 ? mx8_scales(w, R, K)
+             : c.gemm_format == DIT_GEMM_MXFP4 ? mx4_scales(w, R, K)
+                                               : nullptr;
+    };
+    bp.qkv_s = scales(bp.qkv_w, 3 * D, D);
+    bp.out_s = scales(bp.out_w, D, D);
+    bp.in_s = scales(bp.in_w, 2 * F, D);
+    bp.mo_s = scales(bp.mo_w, D, F);
   }
   for (int mm = 0; mm < DIT_MAX_MODALITIES; ++mm) {
     const bool has = c.io && mm < c.n_mod;
@@ -551,8 +567,8 @@ static int check_gemm_shapes(const dit_config& c, int N, int max_seg_tokens) {
   const int shapes[4][2] = {{3 * D, D}, {D, D}, {2 * F, D}, {D, F}};
   for (const auto& sh : shapes) {
     const bool ok = c.stream_dtype == DIT_BF16
-                        ? (c.gemm_format == DIT_GEMM_MXFP8 ? gemm_mx8_supported(N, sh[0], sh[1])
-                                                           : gemm_bf16_supported(N, sh[0], sh[1]))
+                        ? (c.gemm_format != DIT_GEMM_STREAM ? gemm_mx8_supported(N, sh[0], sh[1])
+                                                            : gemm_bf16_supported(N, sh[0], sh[1]))
                         : gemm_f32_supported(N, sh[0], sh[1]);
     if (!ok)
       return set_error(DIT_E_UNSUPPORTED, "%s GEMM [%d x %d] x [%d x %d]^T of a %d-token batch is beyond the kernel's 32-bit offsets",
@@ -680,7 +696,7 @@ static WsPlan plan_ws(const dit_model* m, const dit_batch* b) {
   // residual stream: float32 (bf16 stream, with io) or float64 (fp32 stream)
   p.x = take(c.stream_dtype == DIT_BF16 ? (c.io ? sizeof(float) * N * D : 0) : sizeof(double) * N * D);
   const bool bf = c.stream_dtype == DIT_BF16;
-  const bool mx = c.gemm_format == DIT_GEMM_MXFP8;  // h and o then live in q8 (MXFP8) only
+  const bool mx = c.gemm_format != DIT_GEMM_STREAM;  // h and o then live in q8 (MXFP8) only
   p.h = take(bf && !mx ? es * N * D : 0);
   p.big = take(bf ? es * N * 3 * D : 0);  // the QKV GEMM's output (MLP-in's is consumed in its epilogue)
   p.qkvh = take(es * N * (3 * D > F ? 3 * D : F));
@@ -717,7 +733,7 @@ static WsPlan plan_ws(const dit_model* m, const dit_batch* b) {
   p.tok = take(tok);
   p.vtok = take(tok);
   p.vel = take(c.io ? sizeof(float) * b->latent_floats : 0);
-  // MXFP8 GEMMs: the input of the current GEMM in MXFP8 (h, o, h2: K = D; m: K = F)
+  // MX GEMMs: the input of the current GEMM in MXFP8 (h, o, h2: K = D; m: K = F)
   p.q8 = take(mx ? N * (D > F ? D : F) : 0);
   p.q8s = take(mx ? N * (D > F ? D : F) / 32 : 0);
   p.total = off;
@@ -767,8 +783,10 @@ static int run_block_bf16(dit_model* m, int blk, float* x, const float* mod, con
   // their bf16 form gives; m, which the MLP-in GEMM's SiLU epilogue writes in
   // bf16, is quantized by its own kernel (quantizing inside the GEMM epilogue
   // measured slower: its ALU work runs while the matrix cores idle).  All go
-  // to q8 / q8s, each consumed by the GEMM after it.
-  const bool mx = c.gemm_format == DIT_GEMM_MXFP8;
+  // to q8 / q8s, each consumed by the GEMM after it.  The MXFP4-weight model
+  // runs the same sequence with the weights' FP4 codes as the B operand.
+  const bool mx = c.gemm_format != DIT_GEMM_STREAM;
+  auto gemm_mx = c.gemm_format == DIT_GEMM_MXFP4 ? gemm_mx4 : gemm_mx8;
   uint8_t* q8 = reinterpret_cast<uint8_t*>(ws + p.q8);
   uint8_t* q8s = reinterpret_cast<uint8_t*>(ws + p.q8s);
   // The SiLU gate runs in the MLP-in GEMM's epilogue (the weight is staged in
@@ -781,15 +799,15 @@ static int run_block_bf16(dit_model* m, int blk, float* x, const float* mod, con
     const GemmEpilogue silu{kEpiSiluGate};
     // attention sub-layer
     if (!h_ready) DIT_HIP(modnorm_mx8(c.norm, c.norm_eps, N, D, x, mod, 0, b->cond_dev, q8, q8s, s));
-    DIT_HIP(gemm_mx8(N, 3 * D, D, q8, q8s, static_cast<const uint8_t*>(w.qkv_w), w.qkv_s, w.qkv_b, big, to_bf16, s));
+    DIT_HIP(gemm_mx(N, 3 * D, D, q8, q8s, static_cast<const uint8_t*>(w.qkv_w), w.qkv_s, w.qkv_b, big, to_bf16, s));
     DIT_HIP(rope_split(true, N, H, hd, c.rot_dim, big, b->cos_dev, b->sin_dev, q, k, v, s));
     DIT_HIP(attention_bf16(N, H, hd, b->n_segs, b->cu_dev, b->max_seqlen, q, k, v, o, s, q8, q8s));
-    DIT_HIP(gemm_mx8(N, D, D, q8, q8s, static_cast<const uint8_t*>(w.out_w), w.out_s, w.out_b, a, to_f32, s));
+    DIT_HIP(gemm_mx(N, D, D, q8, q8s, static_cast<const uint8_t*>(w.out_w), w.out_s, w.out_b, a, to_f32, s));
     // MLP sub-layer
     DIT_HIP(resid_modnorm_mx8(c.norm, c.norm_eps, N, D, x, a, mod, 0, mod, 1, b->cond_dev, q8, q8s, s));
-    DIT_HIP(gemm_mx8(N, 2 * F, D, q8, q8s, static_cast<const uint8_t*>(w.in_w), w.in_s, w.in_b, qkvh, silu, s));
+    DIT_HIP(gemm_mx(N, 2 * F, D, q8, q8s, static_cast<const uint8_t*>(w.in_w), w.in_s, w.in_b, qkvh, silu, s));
     DIT_HIP(quantize_mx8(N, F, qkvh, q8, q8s, s));
-    DIT_HIP(gemm_mx8(N, D, F, q8, q8s, static_cast<const uint8_t*>(w.mo_w), w.mo_s, w.mo_b, a, to_f32, s));
+    DIT_HIP(gemm_mx(N, D, F, q8, q8s, static_cast<const uint8_t*>(w.mo_w), w.mo_s, w.mo_b, a, to_f32, s));
     if (next_mod != nullptr)
       DIT_HIP(resid_modnorm_mx8(c.norm, c.norm_eps, N, D, x, a, mod, 1, next_mod, 0, b->cond_dev, q8, q8s, s));
     else
@@ -1150,9 +1168,10 @@ extern "C" int dit_gemm_splits(int dtype, int N, int K, int* splits) {
 extern "C" int dit_gemm_workspace_bytes(int dtype, int M, int N, int K, size_t* bytes) {
   if (bytes == nullptr || M < 0 || N <= 0 || K <= 0) return set_error(DIT_E_INVALID, "dit_gemm_workspace_bytes: bad argument");
   // f32: the slices of B, then the GEMM's own scratch (slices of A, split-K partials);
-  // MXFP8: both operands re-quantized (codes, then scales)
+  // MXFP8 / MXFP4: both operands re-quantized (codes, then scales)
   *bytes = dtype == DIT_BF16    ? gemm_bf16_ws_bytes(M, N, K)
            : dtype == DIT_MXFP8 ? (K % 32 ? 0 : mx8_bytes(M, K) + 256 + mx8_bytes(N, K))
+           : dtype == DIT_MXFP4 ? (K % 32 ? 0 : mx8_bytes(M, K) + 256 + mx4_bytes(N, K))
                                 : gemm_f32_slices_bytes(N, K) + gemm_f32_ws_bytes(M, N, K);
   return DIT_OK;
 }
@@ -1169,22 +1188,31 @@ extern "C" int dit_gemm(int dtype, int M, int N, int K, const void* A, const voi
     DIT_HIP(gemm_bf16(M, N, K, static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), bias, C, ep, s));
     return DIT_OK;
   }
-  if (dtype == DIT_MXFP8) {
-    // A [M,K] and B [N,K] bf16, re-quantized to MXFP8 into ws, then the scaled fp8 GEMM
-    if (!gemm_mx8_supported(M, N, K)) return set_error(DIT_E_UNSUPPORTED, "dit_gemm mxfp8: K=%d must be a multiple of 128", K);
+  if (dtype == DIT_MXFP8 || dtype == DIT_MXFP4) {
+    // A [M,K] and B [N,K] bf16, re-quantized into ws (A to MXFP8, B to MXFP8
+    // or MXFP4), then the scaled MX GEMM
+    const bool four = dtype == DIT_MXFP4;
+    const char* nm = four ? "mxfp4" : "mxfp8";
+    if (!gemm_mx8_supported(M, N, K)) return set_error(DIT_E_UNSUPPORTED, "dit_gemm %s: K=%d must be a multiple of 128", nm, K);
     if (c_dtype != DIT_F32 && c_dtype != DIT_BF16) return set_error(DIT_E_INVALID, "dit_gemm: c_dtype");
-    const size_t need = mx8_bytes(M, K) + 256 + mx8_bytes(N, K);
+    const size_t need = mx8_bytes(M, K) + 256 + (four ? mx4_bytes(N, K) : mx8_bytes(N, K));
     if (ws_bytes < need) return set_error(DIT_E_WORKSPACE, "dit_gemm: workspace of %zu bytes, %zu needed", ws_bytes, need);
     if (ws == nullptr) return set_error(DIT_E_INVALID, "dit_gemm: workspace is null");
     if (M == 0) return DIT_OK;
     uint8_t* qa = static_cast<uint8_t*>(ws);
     uint8_t* qb = qa + align256(mx8_bytes(M, K));
     const uint8_t* sa = mx8_scales(qa, M, K);
-    const uint8_t* sb = mx8_scales(qb, N, K);
+    const uint8_t* sb = four ? mx4_scales(qb, N, K) : mx8_scales(qb, N, K);
     DIT_HIP(quantize_mx8(M, K, static_cast<const uint16_t*>(A), qa, const_cast<uint8_t*>(sa), s));
-    DIT_HIP(quantize_mx8(N, K, static_cast<const uint16_t*>(B), qb, const_cast<uint8_t*>(sb), s));
+    if (four)
+      DIT_HIP(quantize_mx4(N, K, static_cast<const uint16_t*>(B), qb, const_cast<uint8_t*>(sb), s));
+    else
+      DIT_HIP(quantize_mx8(N, K, static_cast<const uint16_t*>(B), qb, const_cast<uint8_t*>(sb), s));
     const GemmEpilogue ep{c_dtype == DIT_F32 ? kEpiF32 : kEpiBf16};
-    DIT_HIP(gemm_mx8(M, N, K, qa, sa, qb, sb, bias, C, ep, s));
+    if (four)
+      DIT_HIP(gemm_mx4(M, N, K, qa, sa, qb, sb, bias, C, ep, s));
+    else
+      DIT_HIP(gemm_mx8(M, N, K, qa, sa, qb, sb, bias, C, ep, s));
     return DIT_OK;
   }
   if (dtype != DIT_F32) return set_error(DIT_E_INVALID, "dit_gemm: dtype");
@@ -1208,6 +1236,17 @@ extern "C" int dit_quantize_mx8(int R, int K, const void* x, void* codes, void* 
   if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(codes)) & 15)
     return set_error(DIT_E_INVALID, "dit_quantize_mx8: x and codes must be 16-byte aligned");
   DIT_HIP(quantize_mx8(R, K, static_cast<const uint16_t*>(x), static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales),
+                       reinterpret_cast<hipStream_t>(stream)));
+  return DIT_OK;
+}
+
+extern "C" int dit_quantize_mx4(int R, int K, const void* x, void* codes, void* scales, dit_stream_t stream) {
+  if (R < 0 || K <= 0 || K % 32) return set_error(DIT_E_INVALID, "dit_quantize_mx4: R=%d K=%d (K a multiple of 32)", R, K);
+  if (R > 0 && (x == nullptr || codes == nullptr || scales == nullptr))
+    return set_error(DIT_E_INVALID, "dit_quantize_mx4: null pointer");
+  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(codes)) & 15)
+    return set_error(DIT_E_INVALID, "dit_quantize_mx4: x and codes must be 16-byte aligned");
+  DIT_HIP(quantize_mx4(R, K, static_cast<const uint16_t*>(x), static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales),
                        reinterpret_cast<hipStream_t>(stream)));
   return DIT_OK;
 }

@@ -11,6 +11,8 @@
 //   XOR-swizzled layout so the operand reads are bank-conflict free.
 // MXFP8: the same tiles of E4M3 bytes (128 K values per 128-byte tile row) on
 //   v_mfma_scale_f32_32x32x64_f8f6f4, with each row's E8M0 block scales.
+// MXFP4 weights: A in MXFP8 as above, B as OCP E2M1 nibbles (128 K values per
+//   64-byte tile row) on the same instruction with B's format set to FP4.
 // (The fp32 stream's GEMM on int8 slices is in gemm_slices.hip.)
 //
 // The value of C[i][j] depends only on row i of A, row j of B and K -- never
@@ -43,6 +45,9 @@ __device__ __forceinline__ int gb_swz(int r, int c) {
   return r * gb::CPR + (c ^ ((r >> sh) & (gb::CPR - 1)));
 }
 static_assert(gb::WN == 64 && gb::BN % 64 == 0, "the SiLU-gate epilogue pairs a wave's two 32-column tiles");
+// FP4 B tile rows of four chunks: chunk c of row r at r*4 + (c ^ ((r / 4) % 4)).
+__device__ __forceinline__ int gb_swz4(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
+enum GemmFormat { kGemmBf16 = 0, kGemmMx8 = 1, kGemmMx4 = 2 };
 
 
 // Tiles move HBM -> LDS with buffer_load_dwordx4 ... lds (no VGPR staging, no
@@ -61,22 +66,38 @@ static_assert(gb::WN == 64 && gb::BN % 64 == 0, "the SiLU-gate epilogue pairs a 
 // values 16g .. 16g+15 of each block), and the scale of block g of row r.
 // The four scales of a row in a tile are one dword, staged through LDS with
 // the tile (one direct dword load per wave).
-template <bool MX>
+//
+// MXFP4-weight (B4) instantiation: B holds two E2M1 values per byte, the value
+// at even K in the low nibble, so a tile row is 64 bytes (four 16-byte chunks,
+// one per 32-value block).  The instruction takes an FP4 operand as 32
+// consecutive values of K per lane (lane half g: the k-step's K 32g ..
+// 32g+31) and an FP8 operand as two runs of 16 (bytes 0-15: K 16g .. 16g+15,
+// bytes 16-31: K 32+16g ..; measured with identity operands), so with A's
+// bytes placed as above (block 2s then block 2s+1, values 16g .. of each)
+// lane (r, g) passes B's whole block 2s + g -- one 16-byte chunk -- and each
+// FP4 value meets the FP8 value of the same K; the block scales stay as for
+// MXFP8 (lane g: block 2s + g).
+template <int FMT>  // kGemmBf16, kGemmMx8, kGemmMx4
 __device__ __forceinline__ void gemm_tile_body(int M, int N, int K, const void* __restrict__ Av,
                                                const void* __restrict__ Bv, const uint8_t* __restrict__ Asc,
                                                const uint8_t* __restrict__ Bsc, const float* __restrict__ bias,
                                                void* __restrict__ Cv, GemmEpilogue ep, int tiles_m, int tiles_n,
                                                int banded) {
   using namespace gb;
-  // bytes of one operand row; a tile row is always BK * 2 = 128 bytes
+  constexpr bool MX = FMT != kGemmBf16;
+  constexpr bool B4 = FMT == kGemmMx4;
+  constexpr int CPR_B = B4 ? CPR / 2 : CPR;  // 16-byte chunks per B tile row
+  // bytes of one operand row; an A tile row is always BK * 2 = 128 bytes, a B
+  // tile row too except for FP4 B (64 bytes)
   const int rowb = MX ? K : 2 * K;
-  // STAGES x (A + B): 128 KB; MX adds each stage's scale dwords of the A and
-  // B rows (STAGES x 2 KB)
+  const int rowb_b = B4 ? K / 2 : rowb;
+  // STAGES x (A + B): 128 KB (96 KB with FP4 B); MX adds each stage's scale
+  // dwords of the A and B rows (STAGES x 2 KB)
   constexpr int SC_CHUNKS = MX ? STAGES * (BM + BN) / 4 : 0;
-  __shared__ uint4 smem[STAGES * (BM + BN) * CPR + SC_CHUNKS];
+  __shared__ uint4 smem[STAGES * (BM * CPR + BN * CPR_B) + SC_CHUNKS];
   uint4* As = smem;
   uint4* Bs = smem + STAGES * BM * CPR;
-  uint32_t* Ss = reinterpret_cast<uint32_t*>(smem + STAGES * (BM + BN) * CPR);  // [stage][A rows | B rows]
+  uint32_t* Ss = reinterpret_cast<uint32_t*>(smem + STAGES * (BM * CPR + BN * CPR_B));  // [stage][A rows | B rows]
 
   const int bid = blockIdx.x;
   int tm, tn;
@@ -115,7 +136,7 @@ __device__ __forceinline__ void gemm_tile_body(int M, int N, int K, const void* 
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<char*>(A + static_cast<size_t>(m0) * rowb), 0, a_rows * rowb, 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char*>(B + static_cast<size_t>(n0) * rowb), 0, b_rows * rowb, 0x00020000);
+      const_cast<char*>(B + static_cast<size_t>(n0) * rowb_b), 0, b_rows * rowb_b, 0x00020000);
   // Copy instruction j of a wave covers tile rows 64 (wave % 4) + 8 j ..
   // + 7, lane l fetching row 64 (wave % 4) + 8 j + l / 8 at the logical chunk
   // that the swizzle stores at position l % 8.  The swizzle of row r + 8 j
@@ -129,6 +150,17 @@ __device__ __forceinline__ void gemm_tile_body(int M, int N, int K, const void* 
     const int row = 64 * (wave & 3) + 8 * par + lane / CPR;
     const int c = gb_swz(row, lane % CPR) - row * CPR;
     voff2[par] = static_cast<uint32_t>((row - 8 * par) * rowb + c * 16);
+  }
+  // FP4 B: instruction j of a group-0 wave covers B tile rows 64 (wave % 4) +
+  // 16 j .. + 15, lane l row 64 (wave % 4) + 16 j + l / 4 at the logical chunk
+  // that the four-chunk swizzle stores at position l % 4; the swizzle of those
+  // rows does not depend on j, so one lane offset serves all four.
+  constexpr int DMA_B4 = BN * CPR_B / 64 / 4;  // per wave of group 0: 4
+  uint32_t voff_b4 = 0;
+  if constexpr (B4) {
+    const int row = 64 * (wave & 3) + lane / CPR_B;
+    const int c = gb_swz4(row, lane % CPR_B) - row * CPR_B;
+    voff_b4 = static_cast<uint32_t>(row * rowb_b + c * 16);
   }
 
   f32x16_t acc[TM][TN];
@@ -153,6 +185,14 @@ __device__ __forceinline__ void gemm_tile_body(int M, int N, int K, const void* 
       if constexpr (MX)                                                                                 \
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(Ss + (stage) * (BM + BN) + 64 * (wave & 3)), \
                                                  4, s_voff, 4 * (kt_), 0, 0);                          \
+    } else if constexpr (B4) {                                                                          \
+      _Pragma("unroll") for (int j = 0; j < DMA_B4; ++j) {                                             \
+        const int i = (wave & 3) * DMA_B4 + j;                                                          \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(Bs + (stage) * BN * CPR_B + i * 64),  \
+                                                 16, voff_b4, (kt_) * BK + 16 * j * rowb_b, 0, 0);     \
+      }                                                                                                 \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                         \
+          rsb, (lds_ptr_t)(Ss + (stage) * (BM + BN) + BM + 64 * (wave & 3)), 4, s_voff, 4 * (kt_), 0, 0); \
     } else {                                                                                            \
       _Pragma("unroll") for (int j = 0; j < DMA_G; ++j) {                                              \
         const int i = (wave & 3) * DMA_G + j;                                                           \
@@ -185,7 +225,7 @@ __device__ __forceinline__ void gemm_tile_body(int M, int N, int K, const void* 
   uint32_t sa[TM / 2], sb[TN / 2];
   auto read_tile = [&](int st) {
     const uint4* a_ = As + st * BM * CPR;
-    const uint4* b_ = Bs + st * BN * CPR;
+    const uint4* b_ = Bs + st * BN * CPR_B;
     if constexpr (MX) {
       // A row's tile scale dword holds its blocks 0-3; this lane's blocks for
       // k-steps 0 and 1 are g and 2 + g.  Two rows (2r', 2r'+1) share one
@@ -206,10 +246,18 @@ __device__ __forceinline__ void gemm_tile_body(int M, int N, int K, const void* 
                                               __builtin_bit_cast(mx_v4i, a_[gb_swz(wr + i * 32 + lr, 4 * s_ + 2 + lg)]),
                                               0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          fb[s_][j] = __builtin_shufflevector(__builtin_bit_cast(mx_v4i, b_[gb_swz(wc + j * 32 + lr, 4 * s_ + lg)]),
-                                              __builtin_bit_cast(mx_v4i, b_[gb_swz(wc + j * 32 + lr, 4 * s_ + 2 + lg)]),
-                                              0, 1, 2, 3, 4, 5, 6, 7);
+        for (int j = 0; j < TN; ++j) {
+          if constexpr (B4) {
+            // the whole 32-value block 2s + g of the row (chunk 2s + g)
+            const mx_v4i z = {0, 0, 0, 0};
+            fb[s_][j] = __builtin_shufflevector(__builtin_bit_cast(mx_v4i, b_[gb_swz4(wc + j * 32 + lr, 2 * s_ + lg)]), z,
+                                                0, 1, 2, 3, 4, 5, 6, 7);
+          } else {
+            fb[s_][j] = __builtin_shufflevector(__builtin_bit_cast(mx_v4i, b_[gb_swz(wc + j * 32 + lr, 4 * s_ + lg)]),
+                                                __builtin_bit_cast(mx_v4i, b_[gb_swz(wc + j * 32 + lr, 4 * s_ + 2 + lg)]),
+                                                0, 1, 2, 3, 4, 5, 6, 7);
+          }
+        }
       }
     } else {
 #pragma unroll
@@ -238,7 +286,7 @@ __device__ __forceinline__ void gemm_tile_body(int M, int N, int K, const void* 
     if constexpr (MX) {
 #define GB_MX_MFMA(ks_, i_, j_)                                                                         \
   acc[i_][j_] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                                       \
-      fa[ks_][i_], fb[ks_][j_], acc[i_][j_], 0, 0, 2 * ((i_) & 1) + (ks_), static_cast<int>(sa[(i_) / 2]), \
+      fa[ks_][i_], fb[ks_][j_], acc[i_][j_], 0, B4 ? 4 : 0, 2 * ((i_) & 1) + (ks_), static_cast<int>(sa[(i_) / 2]), \
       2 * ((j_) & 1) + (ks_), static_cast<int>(sb[(j_) / 2]));
 #define GB_MX_STEP(ks_)                                                                                 \
   GB_MX_MFMA(ks_, 0, 0) GB_MX_MFMA(ks_, 0, 1) GB_MX_MFMA(ks_, 1, 0) GB_MX_MFMA(ks_, 1, 1)              \
@@ -405,7 +453,7 @@ __global__ __launch_bounds__(gb::NT) void gemm_bf16_kernel(int M, int N, int K, 
                                                               const float* __restrict__ bias,
                                                               void* __restrict__ Cv, GemmEpilogue ep, int tiles_m,
                                                               int tiles_n, int banded) {
-  gemm_tile_body<false>(M, N, K, A, B, nullptr, nullptr, bias, Cv, ep, tiles_m, tiles_n, banded);
+  gemm_tile_body<kGemmBf16>(M, N, K, A, B, nullptr, nullptr, bias, Cv, ep, tiles_m, tiles_n, banded);
 }
 
 __global__ __launch_bounds__(gb::NT) void gemm_mx8_kernel(int M, int N, int K, const uint8_t* __restrict__ A,
@@ -414,7 +462,16 @@ __global__ __launch_bounds__(gb::NT) void gemm_mx8_kernel(int M, int N, int K, c
                                                              const uint8_t* __restrict__ Bsc,
                                                              const float* __restrict__ bias, void* __restrict__ Cv,
                                                              GemmEpilogue ep, int tiles_m, int tiles_n, int banded) {
-  gemm_tile_body<true>(M, N, K, A, B, Asc, Bsc, bias, Cv, ep, tiles_m, tiles_n, banded);
+  gemm_tile_body<kGemmMx8>(M, N, K, A, B, Asc, Bsc, bias, Cv, ep, tiles_m, tiles_n, banded);
+}
+
+__global__ __launch_bounds__(gb::NT) void gemm_mx4_kernel(int M, int N, int K, const uint8_t* __restrict__ A,
+                                                             const uint8_t* __restrict__ Asc,
+                                                             const uint8_t* __restrict__ B,
+                                                             const uint8_t* __restrict__ Bsc,
+                                                             const float* __restrict__ bias, void* __restrict__ Cv,
+                                                             GemmEpilogue ep, int tiles_m, int tiles_n, int banded) {
+  gemm_tile_body<kGemmMx4>(M, N, K, A, B, Asc, Bsc, bias, Cv, ep, tiles_m, tiles_n, banded);
 }
 
 // K a multiple of the 64-wide K tile; a 256-row tile of either operand must fit 32-bit buffer offsets.
@@ -457,6 +514,22 @@ hipError_t gemm_mx8(int M, int N, int K, const uint8_t* A, const uint8_t* Asc, c
   const int banded = tiles_n <= 32 || (a_bytes > 256.0 * (1 << 20) && tiles_n <= 96);
   const int nblk = banded ? (tiles_m * tiles_n + 127) / 128 * 128 : tiles_m * tiles_n;
   hipLaunchKernelGGL(gemm_mx8_kernel, dim3(nblk), dim3(gb::NT), 0, s, M, N, K, A, Asc, B, Bsc, bias, C, ep, tiles_m,
+                     tiles_n, banded);
+  return hipGetLastError();
+}
+
+// MXFP4 weights: A as for gemm_mx8, B [N, K/2] two E2M1 codes per byte (even K
+// in the low nibble) with E8M0 scales [N][K/32].
+hipError_t gemm_mx4(int M, int N, int K, const uint8_t* A, const uint8_t* Asc, const uint8_t* B, const uint8_t* Bsc,
+                    const float* bias, void* C, const GemmEpilogue& ep, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (ep.mode == kEpiSiluGate && N % 64 != 0) return hipErrorInvalidValue;
+  LaunchScope scope_(kCntGemmMx4, s);
+  const int tiles_m = (M + gb::BM - 1) / gb::BM, tiles_n = (N + gb::BN - 1) / gb::BN;
+  const double a_bytes = 1.0 * M * K;
+  const int banded = tiles_n <= 32 || (a_bytes > 256.0 * (1 << 20) && tiles_n <= 96);
+  const int nblk = banded ? (tiles_m * tiles_n + 127) / 128 * 128 : tiles_m * tiles_n;
+  hipLaunchKernelGGL(gemm_mx4_kernel, dim3(nblk), dim3(gb::NT), 0, s, M, N, K, A, Asc, B, Bsc, bias, C, ep, tiles_m,
                      tiles_n, banded);
   return hipGetLastError();
 }

@@ -239,24 +239,89 @@ static int64_t quantize_mx8_rows(int64_t r0, int64_t r1, int64_t K, const float*
   return -1;
 }
 
+// ---------------------------------------------------------------- MXFP4 weights
+// The staging-time MXFP4 quantizer: per 32 consecutive K values, the smallest
+// power-of-two scale 2^s with max|v| <= 6 2^s (E8M0 byte s + 127; byte 0 for
+// an all-zero block), then v 2^-s rounded to the nearest OCP FP4 E2M1 value
+// (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), ties to the even mantissa bit, the
+// sign kept; two codes per byte, the one at even K in the low nibble.  Every
+// step is exact in float.
+static uint8_t host_e2m1(float y) {
+  const float a = std::fabs(y);
+  int m;
+  if (a >= 6.0f) {
+    m = 7;
+  } else if (a < 1.0f) {
+    m = static_cast<int>(std::nearbyint(a * 2.0f));  // steps of 0.5: codes 0, 1 and 2 (= 1.0)
+  } else {
+    int e;
+    const float f = std::frexp(a, &e);  // a = 2f 2^(e-1), 2f in [1, 2)
+    int q = static_cast<int>(std::nearbyint((2.0f * f - 1.0f) * 2.0f));
+    int b = e - 1;
+    if (q == 2) {
+      q = 0;
+      ++b;
+    }
+    m = ((b + 1) << 1) | q;
+  }
+  return static_cast<uint8_t>((std::signbit(y) ? 8 : 0) | m);
+}
+
+static int64_t quantize_mx4_rows(int64_t r0, int64_t r1, int64_t K, const float* X, uint8_t* codes, uint8_t* scales) {
+  const int64_t kb = K / 32;
+  for (int64_t r = r0; r < r1; ++r) {
+    for (int64_t b = 0; b < kb; ++b) {
+      const float* v = X + r * K + b * 32;
+      float amax = 0.0f;
+      for (int i = 0; i < 32; ++i) {
+        if (!std::isfinite(v[i])) return r;
+        amax = std::fmax(amax, std::fabs(v[i]));
+      }
+      int s = 0;
+      uint8_t byte = 0;
+      if (amax > 0.0f) {
+        int ef;
+        const float f = std::frexp(amax, &ef);
+        s = ef - 1 - 2 + (f > 0.75f ? 1 : 0);
+        s = s < -127 ? -127 : (s > 127 ? 127 : s);
+        byte = static_cast<uint8_t>(s + 127);
+      }
+      scales[r * kb + b] = byte;
+      uint8_t* c = codes + r * (K / 2) + b * 16;
+      for (int i = 0; i < 16; ++i)
+        c[i] = static_cast<uint8_t>(host_e2m1(std::ldexp(v[2 * i], -s)) | (host_e2m1(std::ldexp(v[2 * i + 1], -s)) << 4));
+    }
+  }
+  return -1;
+}
+
 // Rows in parallel over the host's cores (each row is independent; the
 // result does not depend on the split).
-int64_t host_quantize_mx8(int64_t R, int64_t K, const float* X, uint8_t* codes, uint8_t* scales) {
+template <typename RowFn>
+static int64_t quantize_rows_parallel(int64_t R, int64_t K, RowFn rows) {
   unsigned nt = std::thread::hardware_concurrency();
   nt = nt == 0 ? 1 : (nt > 16 ? 16 : nt);
-  if (R * K < (int64_t(1) << 22) || nt == 1) return quantize_mx8_rows(0, R, K, X, codes, scales);
+  if (R * K < (int64_t(1) << 22) || nt == 1) return rows(0, R);
   std::vector<int64_t> bad(nt, -1);
   std::vector<std::thread> pool;
   const int64_t per = (R + nt - 1) / nt;
   for (unsigned t = 0; t < nt; ++t) {
     const int64_t r0 = per * t, r1 = r0 + per < R ? r0 + per : R;
     if (r0 >= r1) break;
-    pool.emplace_back([=, &bad] { bad[t] = quantize_mx8_rows(r0, r1, K, X, codes, scales); });
+    pool.emplace_back([=, &bad] { bad[t] = rows(r0, r1); });
   }
   for (auto& th : pool) th.join();
   for (int64_t b : bad)
     if (b >= 0) return b;  // threads cover rows in order: the first one found is the smallest
   return -1;
+}
+
+int64_t host_quantize_mx8(int64_t R, int64_t K, const float* X, uint8_t* codes, uint8_t* scales) {
+  return quantize_rows_parallel(R, K, [=](int64_t r0, int64_t r1) { return quantize_mx8_rows(r0, r1, K, X, codes, scales); });
+}
+
+int64_t host_quantize_mx4(int64_t R, int64_t K, const float* X, uint8_t* codes, uint8_t* scales) {
+  return quantize_rows_parallel(R, K, [=](int64_t r0, int64_t r1) { return quantize_mx4_rows(r0, r1, K, X, codes, scales); });
 }
 
 }  // namespace dit

@@ -16,4 +16,6 @@ int64_t host_slice_rows(int64_t R, int64_t K, int64_t Kp, const float* X, int8_t
 // multiple of 32), the same arithmetic as the device quantizer; returns -1, or
 // the first row holding a NaN or an Inf (output then incomplete).
 int64_t host_quantize_mx8(int64_t R, int64_t K, const float* X, uint8_t* codes, uint8_t* scales);
+// MXFP4 (E2M1 codes [R, K/2], two per byte, even K low; E8M0 scales [R, K/32]); the first non-finite row, or -1
+int64_t host_quantize_mx4(int64_t R, int64_t K, const float* X, uint8_t* codes, uint8_t* scales);
 }  // namespace dit

@@ -12,7 +12,7 @@ enum Counter {
   kCntGemmBf16 = 0, kCntGemmF32, kCntAttnBf16, kCntAttnF32, kCntModnorm, kCntRopeSplit,
   kCntSiluGate, kCntGatedResidual, kCntAdaln, kCntPatchIn, kCntPatchOut, kCntEuler,
   kCntGemmF32Reduce, kCntConvert, kCntResidNormSlice, kCntSiluSlice, kCntCfgEuler, kCntResidModnorm,
-  kCntGemmMx8, kCntQuantMx8, kCntNum
+  kCntGemmMx8, kCntQuantMx8, kCntGemmMx4, kCntQuantMx4, kCntNum
 };
 void count_launch(Counter c);
 
@@ -46,6 +46,13 @@ hipError_t gemm_bf16(int M, int N, int K, const uint16_t* A, const uint16_t* B, 
 hipError_t gemm_mx8(int M, int N, int K, const uint8_t* A, const uint8_t* Asc, const uint8_t* B, const uint8_t* Bsc,
                     const float* bias, void* C, const GemmEpilogue& ep, hipStream_t s);
 bool gemm_mx8_supported(int M, int N, int K);
+// MXFP4 weights: A as for gemm_mx8; B [N, K/2] two OCP E2M1 codes per byte
+// (the value at even K in the low nibble) with E8M0 scales [N][K/32]
+// (quantize_mx4); K a multiple of 128; epilogues as gemm_bf16.
+hipError_t gemm_mx4(int M, int N, int K, const uint8_t* A, const uint8_t* Asc, const uint8_t* B, const uint8_t* Bsc,
+                    const float* bias, void* C, const GemmEpilogue& ep, hipStream_t s);
+// bf16 rows [R, K] (K a multiple of 32) -> E2M1 codes [R, K/2] + E8M0 scales [R, K/32]
+hipError_t quantize_mx4(int R, int K, const uint16_t* x, uint8_t* codes, uint8_t* scales, hipStream_t s);
 // bf16 rows [R, K] (K a multiple of 32) -> E4M3 codes [R, K] + E8M0 scales [R, K/32]
 hipError_t quantize_mx8(int R, int K, const uint16_t* x, uint8_t* codes, uint8_t* scales, hipStream_t s);
 // f32: B is given as its int8 slices (slice_rows layout: 5 planes of

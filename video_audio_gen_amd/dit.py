@@ -24,8 +24,8 @@ LIB_PATH = os.path.join(HERE, "libdit.so")
 DIT_OK = 0
 STATUS = {0: "DIT_OK", 1: "DIT_E_INVALID", 2: "DIT_E_STATE", 3: "DIT_E_UNKNOWN_WEIGHT", 4: "DIT_E_SHAPE",
           5: "DIT_E_DTYPE", 6: "DIT_E_MISSING_WEIGHT", 7: "DIT_E_WORKSPACE", 8: "DIT_E_HIP", 9: "DIT_E_UNSUPPORTED"}
-DIT_F32, DIT_BF16, DIT_F64, DIT_MXFP8 = 0, 1, 2, 3
-DIT_GEMM_STREAM, DIT_GEMM_MXFP8 = 0, 1
+DIT_F32, DIT_BF16, DIT_F64, DIT_MXFP8, DIT_MXFP4 = 0, 1, 2, 3, 4
+DIT_GEMM_STREAM, DIT_GEMM_MXFP8, DIT_GEMM_MXFP4 = 0, 1, 2
 DIT_NORM_RMS, DIT_NORM_LAYER = 0, 1
 DIT_MLP_GATE_UP, DIT_MLP_VALUE_GATE = 0, 1
 DIT_IO_NONE, DIT_IO_PATCH3D, DIT_IO_CHANNEL_MAJOR = 0, 1, 2
@@ -33,7 +33,7 @@ MAX_MOD = 4
 COUNTER_NAMES = ["gemm_bf16", "gemm_f32", "attention_bf16", "attention_f32", "modnorm", "rope_split",
                  "silu_gate", "gated_residual", "adaln", "patch_in", "patch_out", "euler",
                  "gemm_f32_reduce", "convert", "resid_norm_slice", "silu_slice", "cfg_euler",
-                 "resid_modnorm", "gemm_mx8", "quantize_mx8"]
+                 "resid_modnorm", "gemm_mx8", "quantize_mx8", "gemm_mx4", "quantize_mx4"]
 
 
 class DitError(RuntimeError):
@@ -100,6 +100,7 @@ _SIGS = {
     "dit_gemm": [_I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _SZ, _P],
     "dit_gemm_f32_noalloc": [_I, _I, _I, _P, _P, _P, _P, _P],
     "dit_quantize_mx8": [_I, _I, _P, _P, _P, _P],
+    "dit_quantize_mx4": [_I, _I, _P, _P, _P, _P],
     "dit_modnorm": [_I, _I, ctypes.c_float, _I, _I, _P, _I, _P, _I, _P, _P, _P],
     "dit_rope_split": [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P],
     "dit_attention": [_I, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P],
@@ -181,7 +182,7 @@ def make_config(spec) -> dit_config:
     c.cond_dim = spec.cond_dim
     c.n_mod = len(spec.modalities)
     c.io = 1 if spec.io else 0
-    c.gemm_format = DIT_GEMM_MXFP8 if getattr(spec, "gemm", "stream") == "mxfp8" else DIT_GEMM_STREAM
+    c.gemm_format = {"mxfp8": DIT_GEMM_MXFP8, "mxfp4": DIT_GEMM_MXFP4}.get(getattr(spec, "gemm", "stream"), DIT_GEMM_STREAM)
     c.qkv_layout = 1 if getattr(spec, "qkv_layout", "concat") == "per_head" else 0
     c.qk_norm = 1 if getattr(spec, "qk_norm", False) else 0
     for i, m in enumerate(spec.modalities):
@@ -455,11 +456,18 @@ def dit_quantize_mx8(x, codes, scales, stream=None):
     _check(load().dit_quantize_mx8(R, K, _ptr(x), _ptr(codes), _ptr(scales), _stream(stream)))
 
 
-def dit_gemm(A, B, bias, C, stream=None, mxfp8=False):
-    """C[M,N] = A[M,K] . B[N,K]^T + bias (mxfp8: bf16 A, B re-quantized to MXFP8 first)."""
+def dit_quantize_mx4(x, codes, scales, stream=None):
+    """bf16 rows x [R, K] -> E2M1 codes [R, K/2] (uint8, two per byte) and E8M0 scales [R, K/32] (uint8)."""
+    R, K = x.shape
+    _check(load().dit_quantize_mx4(R, K, _ptr(x), _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def dit_gemm(A, B, bias, C, stream=None, mxfp8=False, mxfp4=False):
+    """C[M,N] = A[M,K] . B[N,K]^T + bias (mxfp8: bf16 A, B re-quantized to MXFP8 first;
+    mxfp4: A to MXFP8 and B to MXFP4)."""
     M, K = A.shape
     N = B.shape[0]
-    dt = DIT_MXFP8 if mxfp8 else _dt(A)
+    dt = DIT_MXFP4 if mxfp4 else DIT_MXFP8 if mxfp8 else _dt(A)
     ws_bytes = ctypes.c_size_t()
     _check(load().dit_gemm_workspace_bytes(dt, M, N, K, ctypes.byref(ws_bytes)))
     ws = torch.empty(max(int(ws_bytes.value), 1), dtype=torch.uint8, device=A.device)
