@@ -46,6 +46,7 @@ PEAK = {"mfma_f64": 78.6, "mfma_bf16": 2500.0, "mfma_f32": 157.3, "mfma_i8": 500
 GEMM_FAMILY_PEAK = {"gemm_f32": ("mfma_i8_slices", "int8 MFMA 5.0 POP/s / 15 slice products per fp32 product"),
                     "gemm_bf16": ("mfma_bf16", "bf16 MFMA"),
                     "gemm_mx8": ("mfma_fp8", "fp8 MFMA (MXFP8 operands)"),
+                    "gemm_mx4": ("mfma_fp8", "fp8 MFMA (MXFP8 activations x MXFP4 weights run at the fp8 rate)"),
                     "attention_bf16": ("mfma_bf16", "bf16 MFMA")}
 
 
@@ -60,7 +61,7 @@ def _source_digest(path):
 
 
 KERNEL_SOURCE = {"gemm_f32": "video_audio_gen_amd/csrc/gemm_slices.hip", "gemm_bf16": "video_audio_gen_amd/csrc/gemm.hip",
-                 "gemm_mx8": "video_audio_gen_amd/csrc/gemm.hip",
+                 "gemm_mx8": "video_audio_gen_amd/csrc/gemm.hip", "gemm_mx4": "video_audio_gen_amd/csrc/gemm.hip",
                  "attention_bf16": "video_audio_gen_amd/csrc/attention.hip"}
 
 
@@ -116,10 +117,13 @@ def family_work(cfg, splits=None):
     islands = sum(2.0 * m * n * k for m, n, k in gemm_shapes(cfg, blocks=False))
     out = {
         # block GEMMs run in the stream dtype; the projections in and out are fp32
-        "gemm_bf16": (blocks if cfg.stream == "bf16" and cfg.gemm != "mxfp8" else 0.0, "flop"),
+        "gemm_bf16": (blocks if cfg.stream == "bf16" and cfg.gemm == "stream" else 0.0, "flop"),
         "gemm_mx8": (blocks if cfg.gemm == "mxfp8" else 0.0, "flop"),
-        # MXFP8: each GEMM input re-quantized (bf16 read, E4M3 + one scale byte per 32 written)
-        "quantize_mx8": ((L * N * (3 * D + F) * (2 + 1 + 1 / 32)) if cfg.gemm == "mxfp8" else 0.0, "byte"),
+        "gemm_mx4": (blocks if cfg.gemm == "mxfp4" else 0.0, "flop"),
+        # MX models: the MLP-out GEMM's input m re-quantized once per block (bf16
+        # read, E4M3 + one scale byte per 32 written); h, o, h2 come quantized
+        # from their producers
+        "quantize_mx8": ((L * N * F * (2 + 1 + 1 / 32)) if cfg.gemm in ("mxfp8", "mxfp4") else 0.0, "byte"),
         "gemm_f32": ((islands if cfg.stream == "bf16" else blocks + islands), "flop"),
         "attention": (attention_flops(cfg), "flop"),
         # x read (f32) + h written: the first block's attention norm (every
@@ -365,7 +369,7 @@ def measure(cfg, steps, warmup, no_graph=False, protocol_loops=5):
             kernels[k] = {"GB/s": round(rate / 1e9, 1), "frac_hbm": round(rate / 1e9 / PEAK["hbm_gbs"], 4),
                           "avg_us": round(t / n * 1e3, 2)}
         else:
-            peak = (PEAK["mfma_i8_slices"] if k == "gemm_f32" else PEAK["mfma_fp8"] if k == "gemm_mx8"
+            peak = (PEAK["mfma_i8_slices"] if k == "gemm_f32" else PEAK["mfma_fp8"] if k in ("gemm_mx8", "gemm_mx4")
                     else PEAK["mfma_bf16"] if k.endswith("bf16") else None)
             kernels[k] = {"TFLOP/s": round(rate / 1e12, 2), "avg_us": round(t / n * 1e3, 2)}
             if peak:
@@ -373,7 +377,7 @@ def measure(cfg, steps, warmup, no_graph=False, protocol_loops=5):
         log(f"  {k:16s} {kernels[k]}")
     fam = max(prof.items(), key=lambda kv: kv[1][1])[0]
     n_launch, fam_ms = prof[fam]
-    if fam in ("gemm_f32", "gemm_bf16", "gemm_mx8"):
+    if fam in ("gemm_f32", "gemm_bf16", "gemm_mx8", "gemm_mx4"):
         flops = work[fam][0] * steps
         peak_key, peak_note = GEMM_FAMILY_PEAK[fam]
         achieved = flops / (fam_ms * 1e-3) / 1e12
@@ -415,7 +419,7 @@ def main(argv=None):
                          "the FETCH_SIZE / WRITE_SIZE counters), then exit")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch every kernel from the host instead of replaying one captured HIP graph")
-    ap.add_argument("--extra", default="c4,c4_mxfp8",
+    ap.add_argument("--extra", default="c4,c4_mxfp8,c4_mxfp4",
                     help="comma-separated workloads timed after the headline one, each in its own timed "
                          "region, reported under their own keys ('none' for none)")
     ap.add_argument("--extra-steps", type=int, default=5)
@@ -489,7 +493,7 @@ def main(argv=None):
             ecfg = S.get_config(w)
             e = measure(ecfg, a.extra_steps, a.extra_warmup, a.no_graph, protocol_loops=0)
             line["extra"][w] = {
-                "workload": ecfg.name, "dtype": "f32" if ecfg.stream == "f32" else ("mxfp8" if ecfg.gemm == "mxfp8" else "bf16"),
+                "workload": ecfg.name, "dtype": "f32" if ecfg.stream == "f32" else (ecfg.gemm if ecfg.gemm != "stream" else "bf16"),
                 "ms_per_forward" if not e["loop"] else "ms_per_step": round(e["ms"], 4),
                 "tokens_per_s": round(ecfg.n_tokens / (e["ms"] * 1e-3), 2),
                 "steps": a.extra_steps, "warmup": a.extra_warmup, "launch": e["launch"],
