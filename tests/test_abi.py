@@ -211,3 +211,39 @@ def test_vit_config_validation(dit):
                 scaled(good, head_dim=48, n_heads=32, hidden=1536, rot_dim=48)):  # head lanes not a power of two
         c = dit.make_config(bad)
         assert lib.dit_weight_bytes(ctypes.byref(c), ctypes.byref(n)) != 0
+
+
+def test_graph_and_mx4_calls_reject_bad_arguments_on_the_host(dit):
+    """The captured-forward and MXFP4 calls refuse bad arguments by status
+    before any device call: a null output handle or batch, a null graph, a K
+    that is not a multiple of 32 for the MXFP4 quantizer, an MXFP4 model
+    whose widths are not multiples of 128, or one with an fp32 stream."""
+    lib = dit.load()
+    cfg = S.get_config("c1")
+    h, _ = _fake_model(dit, cfg)
+    assert lib.dit_forward_graph_create(h, None, 1, 1, 1, None, 0, None) == 1       # null output handle
+    out = ctypes.c_void_p()
+    assert lib.dit_forward_graph_create(h, None, 1, 1, 1, None, 0, ctypes.byref(out)) == 1  # null batch
+    assert out.value is None
+    lib.dit_model_destroy(h)
+    assert lib.dit_graph_launch(None, None) == 1
+    n = ctypes.c_size_t()
+    assert lib.dit_graph_nodes(None, ctypes.byref(n)) == 1
+    lib.dit_graph_destroy(None)                                                         # no-op
+    assert lib.dit_quantize_mx4(4, 48, 16, 16, 16, None) == 1                           # K % 32
+    assert lib.dit_quantize_mx4(0, 64, None, None, None, None) == 0                     # nothing to do
+    for bad in (scaled(S.get_config("c3_mxfp4"), ffn=16384 + 64),
+                scaled(S.get_config("c1"), gemm="mxfp4")):
+        c = dit.make_config(bad)
+        nb = ctypes.c_size_t()
+        assert lib.dit_weight_bytes(ctypes.byref(c), ctypes.byref(nb)) == 9  # DIT_E_UNSUPPORTED
+        assert b"MX GEMMs" in lib.dit_last_error()
+    # the weight contract of an MXFP4 model: half a byte per weight plus a scale byte per 32
+    c = dit.make_config(S.get_config("c3_mxfp4"))
+    c8 = dit.make_config(S.get_config("c3_mxfp8"))
+    n4, n8 = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.dit_weight_bytes(ctypes.byref(c), ctypes.byref(n4)) == 0
+    assert lib.dit_weight_bytes(ctypes.byref(c8), ctypes.byref(n8)) == 0
+    D, F = 6144, 16384
+    per_block = 3 * D * D + D * D + 2 * F * D + D * F
+    assert 0 < n8.value - n4.value and abs((n8.value - n4.value) - per_block / 2) < 1 << 20
