@@ -862,17 +862,17 @@ static int run_block_f32(dit_model* m, int blk, double* x, const float* mod, con
   float* k = q + static_cast<size_t>(N) * D;
   float* v = k + static_cast<size_t>(N) * D;
   float* o = reinterpret_cast<float*>(ws + p.o);
-  DIT_HIP(gemm_f32_sliced(N, 3 * D, D, sl, w.qkv_w, part, s));
+  DIT_HIP(gemm_f32_sliced(N, 3 * D, D, sl, w.qkv_w, w.qkv_b, part, s));
   DIT_HIP(rope_part(N, H, hd, c.rot_dim, gemm_f32_split_groups(3 * D, D), part, w.qkv_b, b->cos_dev, b->sin_dev, q, k, v,
                     c.qk_norm, c.norm_eps, s));
   DIT_HIP(attention_f32(N, H, hd, b->n_segs, b->cu_dev, b->max_seqlen, q, k, v, o, s));
   DIT_HIP(slice_rows(N, D, o, sl, s));
-  DIT_HIP(gemm_f32_sliced(N, D, D, sl, w.out_w, part, s));
+  DIT_HIP(gemm_f32_sliced(N, D, D, sl, w.out_w, w.out_b, part, s));
   DIT_HIP(resid_norm_slice(N, D, gemm_f32_split_groups(D, D), part, w.out_b, mod, 0, mod, 1, c.norm, c.norm_eps, b->cond_dev, x,
                            sl, nullptr, s));
-  DIT_HIP(gemm_f32_sliced(N, 2 * F, D, sl, w.in_w, part, s));
+  DIT_HIP(gemm_f32_sliced(N, 2 * F, D, sl, w.in_w, w.in_b, part, s));
   DIT_HIP(silu_slice(N, F, gemm_f32_split_groups(2 * F, D), part, w.in_b, sl, s));
-  DIT_HIP(gemm_f32_sliced(N, D, F, sl, w.mo_w, part, s));
+  DIT_HIP(gemm_f32_sliced(N, D, F, sl, w.mo_w, w.mo_b, part, s));
   DIT_HIP(resid_norm_slice(N, D, gemm_f32_split_groups(D, F), part, w.mo_b, mod, 1, next_mod, 0, c.norm, c.norm_eps,
                            b->cond_dev, x, next_mod != nullptr ? sl : nullptr, y, s));
   return DIT_OK;

@@ -73,15 +73,29 @@ __device__ __forceinline__ void sum_parts4(const double* __restrict__ part, int 
   for (int e = 0; e < 4; ++e) out[e] = static_cast<float>(v[e]);
 }
 
+// Columns col..col+3 of a one-split group: the GEMM stored them finished
+// (bias added, rounded once) as floats at the start of the row's slot-0
+// doubles.
+__device__ __forceinline__ void own_parts4(const double* __restrict__ part, size_t off, int col, float* out) {
+  const float4 v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(part + (off - col)) + col);
+  out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+}
+
 // Columns below cb carry s_lo partials, the others s_hi (the GEMM's split
 // groups); SF is the compile-time form of s_lo.
 template <int SF>
 __device__ __forceinline__ void sum_parts4g(const double* __restrict__ part, int s_lo, int s_hi, int cb, size_t MN,
                                             size_t off, const float* __restrict__ bias, int col, float* out) {
-  if (col < cb)
-    sum_parts4<SF>(part, s_lo, MN, off, bias, col, out);
-  else
+  if (col < cb) {
+    if (SF == 1 || (SF == 0 && s_lo == 1))
+      own_parts4(part, off, col, out);
+    else
+      sum_parts4<SF>(part, s_lo, MN, off, bias, col, out);
+  } else if (s_hi == 1) {
+    own_parts4(part, off, col, out);
+  } else {
     sum_parts4<0>(part, s_hi, MN, off, bias, col, out);
+  }
 }
 
 // Workgroup barrier for LDS only: waits for this wave's LDS operations, not

@@ -143,6 +143,12 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
   const int gn = n0 + wc + lr;
   const int gnc = gn < N ? gn : N - 1;
   const int fe = Be[gnc];
+  // A one-split item rounds its own result: C (every item one split), or,
+  // with C null and a bias, the fp32 values in the partial buffer that a
+  // consumer of the partials reads in their place.
+  const bool direct = s1 == 1 && s2 == 1 && C != nullptr;
+  const bool own32 = direct || (C == nullptr && bias != nullptr && (first ? s1 : s2) == 1);
+  const float bias_v = (own32 && bias != nullptr) ? bias[gnc] : 0.f;
   int ae_row[2];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
@@ -269,10 +275,15 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
 
   // Epilogue, per row block of the wave: lane holds column wc + lr, rows
   // wr + 8 (e/4) + 4 lg + e%4 of each level.
-  // C null: fp64 partials for a consumer that sums them itself (any split count)
-  const bool direct = s1 == 1 && s2 == 1 && C != nullptr;
+  // C null: fp64 partials for a consumer that sums them itself (any split
+  // count); a one-split item given a bias stores float(value + bias) instead,
+  // packed at the start of the row's first partial row (row r's columns at
+  // float index c of the doubles r N .. r N + N - 1 of slot 0, which no item
+  // of a multi-split group writes).
   const bool paired = (N & 1) == 0 && (reinterpret_cast<uintptr_t>(C) & 7) == 0;
-  const double bv = (direct && bias != nullptr) ? static_cast<double>(bias[gnc]) : 0.0;
+  const double bv = static_cast<double>(bias_v);
+  float* const own = direct ? C : reinterpret_cast<float*>(part);
+  const size_t own_ld = direct ? static_cast<size_t>(N) : 2 * static_cast<size_t>(N);  // floats per row
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     if (b >= nb) break;  // uniform; b stays a constant so acc stays in registers
@@ -307,9 +318,9 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
         const int row = odd ? gm + 1 : gm;
         if (row < M && col < N) {
           const double lo = odd ? recv : v0, hi = odd ? v1 : recv;
-          if (direct) {
+          if (own32) {
             const double b_lo = odd ? bv_pair : bv, b_hi = odd ? bv : bv_pair;  // columns col, col + 1
-            *reinterpret_cast<float2*>(C + static_cast<size_t>(row) * N + col) =
+            *reinterpret_cast<float2*>(own + static_cast<size_t>(row) * own_ld + col) =
                 make_float2(static_cast<float>(lo + b_lo), static_cast<float>(hi + b_hi));
           } else {
             *reinterpret_cast<double2*>(part + (static_cast<size_t>(sp) * M + row) * N + col) = make_double2(lo, hi);
@@ -324,8 +335,8 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
       const int gm = m0 + wr + 8 * (e >> 2) + 4 * lg + (e & 3);
       if (gm >= M) continue;
       const double v = value(e);
-      if (direct)
-        C[static_cast<size_t>(gm) * N + gn] = static_cast<float>(v + bv);
+      if (own32)
+        own[static_cast<size_t>(gm) * own_ld + gn] = static_cast<float>(v + bv);
       else
         part[(static_cast<size_t>(sp) * M + gm) * N + gn] = v;
     }
@@ -459,14 +470,16 @@ static hipError_t launch_gemm_f32(int M, int N, int kp, const int8_t* Ap, const 
   return hipGetLastError();
 }
 
-hipError_t gemm_f32_sliced(int M, int N, int K, const void* As, const void* Bs, double* part, hipStream_t s) {
+hipError_t gemm_f32_sliced(int M, int N, int K, const void* As, const void* Bs, const float* bias, double* part,
+                           hipStream_t s) {
+  if (bias == nullptr) return hipErrorInvalidValue;  // one-split groups store finished values
   if (M == 0) return hipSuccess;
   const int kp = go_kp(K);
   const int8_t* Ap = static_cast<const int8_t*>(As);
   const int32_t* Ae = reinterpret_cast<const int32_t*>(Ap + al256(static_cast<size_t>(go::S) * M * kp));
   const int8_t* Bp = static_cast<const int8_t*>(Bs);
   const int32_t* Be = reinterpret_cast<const int32_t*>(Bp + al256(static_cast<size_t>(go::S) * N * kp));
-  return launch_gemm_f32(M, N, kp, Ap, Ae, Bp, Be, nullptr, nullptr, part, go_split(N, K), s);
+  return launch_gemm_f32(M, N, kp, Ap, Ae, Bp, Be, bias, nullptr, part, go_split(N, K), s);
 }
 
 hipError_t gemm_f32(int M, int N, int K, const float* A, const void* Bs, const float* bias, float* C,

@@ -66,15 +66,18 @@ hipError_t gemm_f32(int M, int N, int K, const float* A, const void* B_slices, c
 // A also given as slices; the product goes to fp64 split-K partials
 // part[slot][M][N] (no bias) that the consumer sums in split order: columns
 // below col_split have s_lo partials, the others s_hi; gemm_f32_splits is the
-// layout's slot count, max(s_lo, s_hi).
+// layout's slot count, max(s_lo, s_hi).  A group of one split is stored
+// finished instead: float(value + bias[col]) at float index col of the
+// doubles part[0][row][0 .. N) (row stride 2N floats), which the consumer
+// reads as is.
 struct F32Splits {
   int s_lo, s_hi, col_split;
 };
 int gemm_f32_splits(int N, int K);
 F32Splits gemm_f32_split_groups(int N, int K);
 size_t gemm_f32_part_bytes(int M, int N, int K);
-hipError_t gemm_f32_sliced(int M, int N, int K, const void* A_slices, const void* B_slices, double* part,
-                           hipStream_t s);
+hipError_t gemm_f32_sliced(int M, int N, int K, const void* A_slices, const void* B_slices, const float* bias,
+                           double* part, hipStream_t s);
 // Which K, N the GEMMs accept (checked by the ABI layer before launching).
 bool gemm_bf16_supported(int M, int N, int K);
 bool gemm_f32_supported(int M, int N, int K);
@@ -116,7 +119,7 @@ hipError_t gated_residual(int N, int D, bool x_f64, void* x, const float* a, con
                           const int32_t* cond_idx, hipStream_t s);
 // ---- fused row kernels of the fp32 stream (fused_f32.hip); part: fp64 split-K
 // partials [S][N][cols] of the preceding gemm_f32_sliced, bias (required with
-// part) added after them.
+// part) added after them; a one-split group's columns are read finished.
 // resid_norm_slice: with part, x += gate(gmod, which) * a; then the norm of x,
 // modulated from nmod (which) unless nmod is null, sliced into `slices` (rows
 // N, K = D) or stored to y, or neither when both are null.
