@@ -101,14 +101,16 @@ def gemm_shapes(cfg, blocks=True, islands=True):
     return out
 
 
-def family_work(cfg, splits=None):
+def family_work(cfg, split_groups=None):
     """Algorithmic work of one forward per kernel family: (amount, unit).
 
     GEMM and attention count flops (2MNK; 4*hd*H*sum L_d^2); the bandwidth-bound
     kernels count the bytes they must move once (inputs read + outputs written).
-    In the fp32 stream a GEMM result reaches the row kernel after it as
-    `splits(n, k)` fp64 split-K partials, which that kernel must read; int8
-    slices are 5 bytes per value."""
+    In the fp32 stream a GEMM result reaches the row kernel after it as fp64
+    split-K partials, which that kernel must read: `split_groups(n, k)` gives
+    (s_lo, s_hi, col_split), columns below col_split in s_lo splits, and a
+    group of one split arrives finished as 4-byte floats; int8 slices are 5
+    bytes per value."""
     N, D, F, H, hd = cfg.n_tokens, cfg.hidden, cfg.ffn, cfg.n_heads, cfg.head_dim
     es = 2 if cfg.stream == "bf16" else 4
     L = cfg.n_blocks
@@ -140,16 +142,19 @@ def family_work(cfg, splits=None):
         "gated_residual": (N * D * 12 if L else 0, "byte"),
         "adaln": (L * cfg.n_mod * 6 * D * cfg.cond_dim * w_es, "byte"),
     }
-    if cfg.stream == "f32" and splits is not None:
-        s_qkv, s_o, s_in, s_out = splits(3 * D, D), splits(D, D), splits(2 * F, D), splits(D, F)
+    if cfg.stream == "f32" and split_groups is not None:
+        def part_bytes(n, k):  # one GEMM result [N, n] as its consumer reads it
+            s_lo, s_hi, cb = split_groups(n, k)
+            per = lambda sp: 4 if sp == 1 else 8 * sp
+            return N * (cb * per(s_lo) + (n - cb) * per(s_hi))
         nd = N * D
         # rope_part: partials of q|k|v in, q, k, v out, cos/sin rows
-        out["rope_split"] = (L * (s_qkv * 3 * nd * 8 + 3 * nd * 4 + N * cfg.rot_dim * 4), "byte")
+        out["rope_split"] = (L * (part_bytes(3 * D, D) + 3 * nd * 4 + N * cfg.rot_dim * 4), "byte")
         # residual (fp64) read + written, partials in, slices out; the prologue
         # reads x and slices it; with io the last one stores the fp32 norm instead
-        rn = L * ((s_o + s_out) * nd * 8 + 2 * 16 * nd + 2 * 5 * nd) + (8 * nd + 5 * nd if L else 0)
+        rn = L * (part_bytes(D, D) + part_bytes(D, F) + 2 * 16 * nd + 2 * 5 * nd) + (8 * nd + 5 * nd if L else 0)
         out["resid_norm_slice"] = (rn, "byte")
-        out["silu_slice"] = (L * (s_in * 2 * N * F * 8 + 5 * N * F), "byte")
+        out["silu_slice"] = (L * (part_bytes(2 * F, D) + 5 * N * F), "byte")
         # slice_rows of each attention output (fp32 in, slices out); the residual
         # widened on entry and, without io, narrowed on exit; with io the slices
         # of the in-projection's tokens and of the final norm
@@ -355,7 +360,7 @@ def measure(cfg, steps, warmup, no_graph=False, protocol_loops=5):
         if n:
             log(f"  {k:16s} launches {n:6d}  total {t:9.3f} ms  avg {t / n * 1e3:9.2f} us  "
                 f"share {t / total_dev * 100:5.1f}%")
-    work = family_work(cfg, dit.dit_gemm_splits if cfg.stream == "f32" else None)
+    work = family_work(cfg, dit.dit_gemm_split_groups if cfg.stream == "f32" else None)
     kernels = {}
     for k, (n, t) in prof.items():
         if not n:

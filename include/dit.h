@@ -414,6 +414,14 @@ int dit_gemm_workspace_bytes(int dtype, int M, int N, int K, size_t* bytes);
  * Chosen from N, K and the compute-unit count only, so a row's result never
  * depends on M.  dtype must be DIT_F32. */
 int dit_gemm_splits(int dtype, int N, int K, int* splits);
+/* The same plan as two column groups: columns [0, col_split) of the product
+ * in s_lo splits, the rest in s_hi.  A group of one split hands the row kernel
+ * after the GEMM finished fp32 values (the bias added, one rounding: 4 bytes
+ * per value), any other group its fp64 partials (8 bytes per split and value).
+ * dtype must be DIT_F32; no device work.  (Page "the 2.4B fp32 DiT onto the
+ * device, staged once", section "What moved, and onto what": the fp32
+ * MatmulBT.) */
+int dit_gemm_split_groups(int dtype, int N, int K, int* s_lo, int* s_hi, int* col_split);
 int dit_gemm(int dtype, int M, int N, int K, const void* A, const void* B, const float* bias,
              void* C, int c_dtype, void* ws, size_t ws_bytes, dit_stream_t stream);
 

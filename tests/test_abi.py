@@ -154,6 +154,25 @@ def test_gemm_splits_query(dit):
     assert lib.dit_gemm_splits(dit.DIT_F32, 2560, 10240, None) == 1
 
 
+@pytest.mark.parametrize("n,k", [(7680, 2560), (2560, 2560), (20480, 2560), (2560, 10240), (256, 256), (1000, 4000)])
+def test_gemm_split_groups_query(dit, n, k):
+    # the two column groups agree with the slot count: columns [0, col_split)
+    # in s_lo splits, the rest in s_hi >= s_lo, and the slot count is the larger
+    lo, hi, cb = dit.dit_gemm_split_groups(n, k)
+    assert 1 <= lo <= hi and 0 < cb <= n and (cb == n or cb % 64 == 0)
+    assert max(lo, hi) == dit.dit_gemm_splits(n, k)
+    if cb == n:
+        assert lo == hi
+
+
+def test_gemm_split_groups_rejects_bad_arguments(dit):
+    lib = dit.load()
+    a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    assert lib.dit_gemm_split_groups(dit.DIT_BF16, 2560, 2560, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)) == 1
+    assert lib.dit_gemm_split_groups(dit.DIT_F32, 0, 2560, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)) == 1
+    assert lib.dit_gemm_split_groups(dit.DIT_F32, 2560, 2560, None, ctypes.byref(b), ctypes.byref(c)) == 1
+
+
 def test_nonfinite_fp32_gemm_weight_is_rejected_by_name(dit):
     # an fp32 GEMM weight is cut into int8 slices on the host; a NaN or an Inf
     # has no slicing and must fail the call (before any device copy), not

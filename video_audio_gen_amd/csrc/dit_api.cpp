@@ -1165,6 +1165,16 @@ extern "C" int dit_gemm_splits(int dtype, int N, int K, int* splits) {
   return DIT_OK;
 }
 
+extern "C" int dit_gemm_split_groups(int dtype, int N, int K, int* s_lo, int* s_hi, int* col_split) {
+  if (s_lo == nullptr || s_hi == nullptr || col_split == nullptr || dtype != DIT_F32 || N <= 0 || K <= 0)
+    return set_error(DIT_E_INVALID, "dit_gemm_split_groups: bad argument");
+  const F32Splits g = gemm_f32_split_groups(N, K);
+  *s_lo = g.s_lo;
+  *s_hi = g.s_hi;
+  *col_split = g.col_split;
+  return DIT_OK;
+}
+
 extern "C" int dit_gemm_workspace_bytes(int dtype, int M, int N, int K, size_t* bytes) {
   if (bytes == nullptr || M < 0 || N <= 0 || K <= 0) return set_error(DIT_E_INVALID, "dit_gemm_workspace_bytes: bad argument");
   // f32: the slices of B, then the GEMM's own scratch (slices of A, split-K partials);

@@ -97,6 +97,7 @@ _SIGS = {
     "dit_cfg_denoise_loop": [_P, _P, _P, _P, _P, ctypes.c_float, _I, _P, _SZ, _P],
     "dit_gemm_workspace_bytes": [_I, _I, _I, _I, ctypes.POINTER(_SZ)],
     "dit_gemm_splits": [_I, _I, _I, ctypes.POINTER(_I)],
+    "dit_gemm_split_groups": [_I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I), ctypes.POINTER(_I)],
     "dit_gemm": [_I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _SZ, _P],
     "dit_gemm_f32_noalloc": [_I, _I, _I, _P, _P, _P, _P, _P],
     "dit_quantize_mx8": [_I, _I, _P, _P, _P, _P],
@@ -492,6 +493,13 @@ def dit_gemm_splits(N: int, K: int) -> int:
     s = ctypes.c_int()
     _check(load().dit_gemm_splits(DIT_F32, N, K, ctypes.byref(s)))
     return int(s.value)
+
+
+def dit_gemm_split_groups(N: int, K: int):
+    """(s_lo, s_hi, col_split) of the fp32 GEMM for an [N, K] weight on the current device."""
+    a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(load().dit_gemm_split_groups(DIT_F32, N, K, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    return int(a.value), int(b.value), int(c.value)
 
 
 def dit_modnorm(norm: int, eps: float, x, mod, which: int, cond_idx, h, stream=None):
