@@ -14,6 +14,8 @@
 // device's compute-unit count (the split-K plan) -- never on M or on where row
 // i sits in a tile -- so a document computed alone and the same document
 // inside a packed batch give bit-identical results.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "slices.h"
@@ -40,14 +42,15 @@ namespace dit {
 // so results are bit-reproducible on devices with the same number of CUs (a
 // device with another count may round a different set of partials).
 //
-// Workgroup tile 192 x 64 (a few hundred rows of activations are covered by
+// Workgroup tile 176 x 64 (a few hundred rows of activations are covered by
 // one or two tiles, so each weight slice is read once per row tile), K step
 // 32, eight wavefronts in two groups that alternate between reading a step's
 // slice fragments into registers and multiplying (below); slices of A and B
 // stream HBM -> LDS by direct buffer loads into a four-stage ring (160 KB).
 namespace go {
 constexpr int S = 5;                      // slices per operand
-constexpr int BM = 192, BN = 64, BK = 32, NW = 8, NT = 64 * NW, STAGES = 4;
+constexpr int BM = 192, BN = 64, BK = 32, NW = 8, NT = 64 * NW, STAGES = 4;  // BM: rows of an A slice tile in LDS
+constexpr int BMT = 176;                  // rows a tile computes: 5 blocks of 32, one of 16 (LDS rows 176.. read zero)
 constexpr int APLANE = BM * BK / 16;      // 16-byte chunks of one A slice tile: 384
 constexpr int BPLANE = BN * BK / 16;      // ... of one B slice tile: 128
 constexpr int AOPER = S * APLANE, BOPER = S * BPLANE;
@@ -114,7 +117,7 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
   const int tn = first ? it % n1 : n1 + (it - items1) % (tiles_n - n1);
   const int sp = first ? it / n1 : (it - items1) / (tiles_n - n1);
   const int steps_per_split = first ? sps1 : sps2;
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = tm * BMT, n0 = tn * BN;
   const int ksteps = Kp / BK;
   const int t_begin = sp * steps_per_split;
   const int t_end = t_begin + steps_per_split < ksteps ? t_begin + steps_per_split : ksteps;
@@ -126,17 +129,30 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
   // Two groups of four wavefronts, one of each per SIMD (wave w runs on SIMD
   // w % 4), alternate between reading a K step's slice fragments from LDS
   // into registers and running that step's MFMAs from registers, one
-  // workgroup barrier per phase.  Of the tile's 6 x 2 blocks of 32 x 32, the
-  // wave of group 0 on SIMD k takes row blocks 3 (k / 2) and 3 (k / 2) + 1 of
-  // column block k % 2 (30 MFMAs per step), the wave of group 1 row block
-  // 3 (k / 2) + 2 (15 MFMAs), so while group 0 multiplies, group 1 reads its
-  // fragments and issues the copies, and while group 1 multiplies, group 0
-  // reads: each SIMD's matrix core runs 45 MFMAs per step with no phase in
-  // which it waits on LDS.
+  // workgroup barrier per phase.  The tile's rows are five blocks of 32 and
+  // one of 16 (rows 160-175).  Of column block k % 2, the wave of group 0 on
+  // SIMD k takes row blocks 3 (k / 2) and 3 (k / 2) + 1 (30 MFMAs per step);
+  // of group 1, the wave on SIMD 0 or 1 (role 1) takes the slice pairs of
+  // levels 2-4 of row block 2 (12 MFMAs), the wave on SIMD 2 or 3 (role 2) the
+  // 16-row block (9) and the pairs of levels 0-1 of row block 2 (3), which it
+  // hands to role 1 through LDS at the end.  While group 0 multiplies, group
+  // 1 reads its fragments and issues the copies, and while group 1
+  // multiplies, group 0 reads: each SIMD's matrix core runs 42 MFMAs per step
+  // with no phase in which it waits on LDS.
+  //
+  // The 16-row block: A's rows 0-15 are the tile's rows 160-175 of slice s and
+  // its rows 16-31 the same rows of slice s + 1, so one MFMA against slice t
+  // of B adds pair (s, t) to rows 0-15 (accumulator elements 0-7) and pair
+  // (s + 1, t) to rows 16-31 (elements 8-15) of accumulator set s + t: its
+  // lower half sums level s + t, its upper half level s + t + 1.  With s in
+  // {0, 2, 4} and s + t <= 4, nine MFMAs cover the 15 kept pairs; level d is
+  // the lower half of set d plus the upper half of set d - 1 (set 4's upper
+  // half, level 5, is never read).
   const int grp = wave >> 2, sk = wave & 3;
+  const int role = grp == 0 ? 0 : 1 + (sk >> 1);
   const int wc = (sk & 1) * 32;
-  const int nb = grp == 0 ? 2 : 1;                        // row blocks of this wave
-  const int wr0 = ((sk >> 1) * 3 + (grp == 0 ? 0 : 2)) * 32;  // its first row
+  const int nb = grp == 0 ? 2 : 1;                                     // row blocks this wave stores
+  const int wr0 = grp == 0 ? (sk >> 1) * 96 : (role == 1 ? 64 : 160);  // its first row
   // The epilogue's scale exponents, loaded now so their latency hides under
   // the K loop: column wc + lr, and rows wr0 + lr and wr0 + 32 + lr (lane
   // l's value serves the other lanes of its row block through a shuffle).
@@ -165,27 +181,29 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
       const_cast<int8_t*>(Ap), 0, static_cast<uint32_t>(S * static_cast<int64_t>(M) * Kp), 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t*>(Bp), 0, static_cast<uint32_t>(S * static_cast<int64_t>(N) * Kp), 0x00020000);
-  uint32_t voff[DMA_W];
-#pragma unroll
-  for (int j = 0; j < DMA_W; ++j) {
-    const int q = sk * DMA_W + j;
-    const bool a_op = q < AQ;
-    const int plane = a_op ? q / 6 : (q - AQ) / 2;
-    const int r = 32 * (a_op ? q % 6 : (q - AQ) % 2) + (lane >> 1);
-    const int c = (lane & 1) ^ ((r >> 3) & 1);
-    const int grow = (a_op ? m0 : n0) + r;
-    const int rows = a_op ? M : N;
-    // slice layout [plane][K step][row][32 bytes]: one instruction reads 1 KB in a row
-    voff[j] = grow < rows ? static_cast<uint32_t>((static_cast<int64_t>(plane) * (Kp / BK) * rows + grow) * BK + 16 * c)
-                          : 0xFFFFFFF0u;
-  }
+  // Lane l's part of every copy's offset: row l/2 of the 32-row block, at the
+  // chunk the swizzle stores at position l%2 (rows 32 blk + l/2 share bit 3
+  // with l/2, so the swizzle is the same for every block).  The rest of an
+  // offset is uniform and formed at issue, so the ten copies share one VGPR.
+  const uint32_t lane_off = static_cast<uint32_t>((lane >> 1) * BK + 16 * ((lane & 1) ^ ((lane >> 4) & 1)));
   const uint32_t a_step = static_cast<uint32_t>(M) * BK, b_step = static_cast<uint32_t>(N) * BK;  // bytes per K step
   auto dma = [&](int t, int st) {
 #pragma unroll
     for (int j = 0; j < DMA_W; ++j) {
       const int q = sk * DMA_W + j;
-      const uint32_t off = voff[j] == 0xFFFFFFF0u ? voff[j] : voff[j] + static_cast<uint32_t>(t) * (q < AQ ? a_step : b_step);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(q < AQ ? ra : rb, (lds_ptr_t)(smem + st * STAGE + q * 64), 16, off, 0,
+      const bool a_op = q < AQ;
+      const int plane = a_op ? q / 6 : (q - AQ) / 2;
+      const int blk = a_op ? q % 6 : (q - AQ) % 2;
+      const int rows = a_op ? M : N;
+      const int row0 = (a_op ? m0 : n0) + 32 * blk;
+      // rows of this block that exist (A rows past the tile's 176 read zero)
+      int valid = rows - row0;
+      if (a_op && BMT - 32 * blk < valid) valid = BMT - 32 * blk;
+      // slice layout [plane][K step][row][32 bytes]: one instruction reads 1 KB in a row
+      const uint32_t sbase = static_cast<uint32_t>((static_cast<int64_t>(plane) * (Kp / BK) * rows + row0) * BK) +
+                             static_cast<uint32_t>(t) * (a_op ? a_step : b_step);
+      const uint32_t off = (lane >> 1) < valid ? sbase + lane_off : 0xFFFFFFF0u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_op ? ra : rb, (lds_ptr_t)(smem + st * STAGE + q * 64), 16, off, 0,
                                                0, 0);
     }
   };
@@ -209,21 +227,42 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[b][d][e] = 0;
   v4i fa[2][S], fb[S];
-  auto read_step = [&](int st) {
+  // LDS chunk bases of this lane's A reads (+ p APLANE for slice p): role 0
+  // rows wr0 + lr and wr0 + 32 + lr; role 1 row 64 + lr; role 2 the 16-row
+  // block's dual rows (lanes 16-31 of a half one slice further on: plane 5,
+  // read for the never-used upper half of set 4, is the start of the B
+  // planes) and row block 2's row 64 + lr.
+  const int abase0 = role == 2 ? go_swz(160 + (lr & 15), lg) + ((lr >> 4) & 1) * APLANE : go_swz(wr0 + lr, lg);
+  const int abase1 = role == 2 ? go_swz(64 + lr, lg) : abase0 + 64;
+  // The role is a compile-time constant of each K loop below (one loop per
+  // role), so a loop holds only that role's fragments and accumulators.
+  auto read_step = [&](int st, auto role_c) {
+    constexpr int R = decltype(role_c)::value;
     const uint4* sa = smem + st * STAGE;
     const uint4* sb = sa + AOPER;
 #pragma unroll
-    for (int p = 0; p < S; ++p) {
-      fb[p] = __builtin_bit_cast(v4i, sb[p * BPLANE + go_swz(wc + lr, lg)]);
-      fa[0][p] = __builtin_bit_cast(v4i, sa[p * APLANE + go_swz(wr0 + lr, lg)]);
-    }
-    if (nb == 2) {
+    for (int p = 0; p < S; ++p) fb[p] = __builtin_bit_cast(v4i, sb[p * BPLANE + go_swz(wc + lr, lg)]);
+    if constexpr (R != 2) {
 #pragma unroll
-      for (int p = 0; p < S; ++p) fa[1][p] = __builtin_bit_cast(v4i, sa[p * APLANE + go_swz(wr0 + 32 + lr, lg)]);
+      for (int p = 0; p < S; ++p) fa[0][p] = __builtin_bit_cast(v4i, sa[abase0 + p * APLANE]);
+      if constexpr (R == 0) {
+#pragma unroll
+        for (int p = 0; p < S; ++p) fa[1][p] = __builtin_bit_cast(v4i, sa[abase1 + p * APLANE]);
+      }
+    } else {
+      // the 16-row block as slice pairs (0, 1), (2, 3), (4, -), then row
+      // block 2's slices 0 and 1
+#pragma unroll
+      for (int j = 0; j < 3; ++j) fa[0][j] = __builtin_bit_cast(v4i, sa[abase0 + 2 * j * APLANE]);
+      fa[0][3] = __builtin_bit_cast(v4i, sa[abase1]);
+      fa[0][4] = __builtin_bit_cast(v4i, sa[abase1 + APLANE]);
     }
     // the reads complete inside the phase: the asm takes every fragment
 #pragma unroll
-    for (int p = 0; p < S; ++p) asm volatile("" : "+v"(fb[p]), "+v"(fa[0][p]), "+v"(fa[1][p]));
+    for (int p = 0; p < S; ++p) {
+      asm volatile("" : "+v"(fb[p]), "+v"(fa[0][p]));
+      if constexpr (R == 0) asm volatile("" : "+v"(fa[1][p]));
+    }
   };
   // pair (s, t) accumulates in level s + t; the order keeps two MFMAs on one
   // accumulator at least two instructions apart (levels 4 3 2 4 3 2 4 3 2 4 3
@@ -234,6 +273,24 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
     GO_MFMA(1, 2) GO_MFMA(0, 2) GO_MFMA(1, 3) GO_MFMA(0, 3) GO_MFMA(1, 0) GO_MFMA(0, 4) GO_MFMA(0, 0)
     GO_MFMA(0, 1)
 #undef GO_MFMA
+  };
+  // role 1: row block 2's pairs of levels 2-4 (levels 4 3 2 4 3 2 4 3 2 4 3 4)
+  auto mfma_upper = [&](v16i (&a)[S], const v4i (&A)[S]) {
+#define GO_MFMA(s_, t_) a[(s_) + (t_)] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[s_], fb[t_], a[(s_) + (t_)], 0, 0, 0);
+    GO_MFMA(4, 0) GO_MFMA(3, 0) GO_MFMA(2, 0) GO_MFMA(3, 1) GO_MFMA(2, 1) GO_MFMA(1, 1) GO_MFMA(2, 2)
+    GO_MFMA(1, 2) GO_MFMA(0, 2) GO_MFMA(1, 3) GO_MFMA(0, 3) GO_MFMA(0, 4)
+#undef GO_MFMA
+  };
+  // role 2: the 16-row block's sets (pair (2j, t) and (2j+1, t) into set
+  // 2j + t of a) and row block 2's pairs (0,0), (1,0), (0,1) into levels of b
+  // (sets 0 2 4 1 3 b0 2 4 b1 3 b1 4)
+  auto mfma_tail = [&](v16i (&a)[S], v16i (&b)[S], const v4i (&A)[S]) {
+#define GO_T(j_, t_) a[2 * (j_) + (t_)] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[j_], fb[t_], a[2 * (j_) + (t_)], 0, 0, 0);
+#define GO_B(s_, t_) b[(s_) + (t_)] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[3 + (s_)], fb[t_], b[(s_) + (t_)], 0, 0, 0);
+    GO_T(0, 0) GO_T(1, 0) GO_T(2, 0) GO_T(0, 1) GO_T(1, 1) GO_B(0, 0) GO_T(0, 2) GO_T(1, 2) GO_B(1, 0) GO_T(0, 3)
+    GO_B(0, 1) GO_T(0, 4)
+#undef GO_T
+#undef GO_B
   };
   auto phase_barrier = [&]() {
     __builtin_amdgcn_sched_barrier(0);
@@ -258,23 +315,63 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
   }
   go_barrier();
   if (grp == 1) phase_barrier();
-  for (int i = 0; i < nsteps; ++i) {
-    if (grp == 1 && i + 3 < nsteps) dma(t_begin + i + 3, (i + 3) % STAGES);
-    read_step(i % STAGES);
-    if (grp == 1) wait_copies(10 * ((i + 2 < nsteps) + (i + 3 < nsteps)));
-    phase_barrier();
-    mfma_block(acc[0], fa[0]);
-    if (nb == 2) mfma_block(acc[1], fa[1]);
+  auto k_loop = [&](auto role_c) {
+    constexpr int R = decltype(role_c)::value;
+    for (int i = 0; i < nsteps; ++i) {
+      if (R != 0 && i + 3 < nsteps) dma(t_begin + i + 3, (i + 3) % STAGES);
+      read_step(i % STAGES, role_c);
+      if (R != 0) wait_copies(10 * ((i + 2 < nsteps) + (i + 3 < nsteps)));
+      phase_barrier();
+      if constexpr (R == 0) {
+        mfma_block(acc[0], fa[0]);
+        mfma_block(acc[1], fa[1]);
+      } else if constexpr (R == 1) {
+        mfma_upper(acc[0], fa[0]);
+      } else {
+        mfma_tail(acc[0], acc[1], fa[0]);
+      }
+      // the MFMAs complete inside the phase: the asm takes every accumulator
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int d = 0; d < S; ++d) asm volatile("" : "+v"(acc[b][d]));
-    phase_barrier();
-  }
+      for (int d = 0; d < S; ++d) {
+        if (R != 1 || d >= 2) asm volatile("" : "+v"(acc[0][d]));
+        if (R == 0 || (R == 2 && d < 2)) asm volatile("" : "+v"(acc[1][d]));
+      }
+      phase_barrier();
+    }
+  };
+  if (role == 0)
+    k_loop(std::integral_constant<int, 0>{});
+  else if (role == 1)
+    k_loop(std::integral_constant<int, 1>{});
+  else
+    k_loop(std::integral_constant<int, 2>{});
   if (grp == 0) phase_barrier();
 
+  // Row block 2's levels 0 and 1 go from the role-2 wave to the role-1 wave
+  // of the same column block through LDS, free now (every wave is past its
+  // last read); the role-2 wave turns its 16-row block's sets into levels.
+  int32_t* const xch = reinterpret_cast<int32_t*>(smem) + (sk & 1) * (2 * 16 * 64);
+  if (role == 2) {
+#pragma unroll
+    for (int d = 0; d < 2; ++d)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) xch[(d * 16 + e) * 64 + lane] = acc[1][d][e];
+#pragma unroll
+    for (int d = S - 1; d >= 1; --d)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[0][d][e] += acc[0][d - 1][e + 8];
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the LDS writes are done
+  go_barrier();
+  if (role == 1) {
+#pragma unroll
+    for (int d = 0; d < 2; ++d)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[0][d][e] = xch[(d * 16 + e) * 64 + lane];
+  }
+
   // Epilogue, per row block of the wave: lane holds column wc + lr, rows
-  // wr + 8 (e/4) + 4 lg + e%4 of each level.
+  // wr + 8 (e/4) + 4 lg + e%4 of each level (the 16-row block: e < 8 only).
   // C null: fp64 partials for a consumer that sums them itself (any split
   // count); a one-split item given a bias stores float(value + bias) instead,
   // packed at the start of the row's first partial row (row r's columns at
@@ -288,6 +385,7 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
   for (int b = 0; b < 2; ++b) {
     if (b >= nb) break;  // uniform; b stays a constant so acc stays in registers
     const int wr = wr0 + 32 * b;
+    const int ne = role == 2 ? 8 : 16;  // uniform
     const v16i (&ac)[S] = acc[b];
     // the exponents of this lane's 16 rows, from the lanes that loaded them
     int aex[16];
@@ -312,6 +410,7 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
       const int col = odd ? gn - 1 : gn;
 #pragma unroll
       for (int e = 0; e < 16; e += 2) {
+        if (e >= ne) break;
         const int gm = m0 + wr + 8 * (e >> 2) + 4 * lg + (e & 3);
         const double v0 = value(e), v1 = value(e + 1);
         const double recv = xor_lane<1>(odd ? v0 : v1);
@@ -332,6 +431,7 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
     if (gn >= N) continue;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
+      if (e >= ne) break;
       const int gm = m0 + wr + 8 * (e >> 2) + 4 * lg + (e & 3);
       if (gm >= M) continue;
       const double v = value(e);
@@ -350,7 +450,8 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
 // workgroups adds ~5 steps of fixed cost (first copies in flight,
 // epilogue), and each split adds an fp64 partial of the row tile that is
 // written and read back once (192 N 16 bytes at ~4.5 TB/s, i.e. N / 1600
-// steps per slot).  Plans: every N tile in s splits
+// steps per slot; costed with 192-row tiles and kept for the 176-row ones,
+// so the plans, and with them the results, did not change).  Plans: every N tile in s splits
 // (ceil(tiles_n s / CUs) rounds of ceil(steps / s) steps), or the first n1
 // tiles in s1 splits filling k whole rounds and the rest in s2 = 2..4 s1
 // splits after them, which evens out a last, partial round.  Splits have
@@ -459,7 +560,7 @@ static hipError_t launch_gemm_f32(int M, int N, int kp, const int8_t* Ap, const 
                                   hipStream_t s) {
   const int steps = kp / go::BK;
   const int sps1 = (steps + g.s1 - 1) / g.s1, sps2 = (steps + g.s2 - 1) / g.s2;
-  const int tiles_m = (M + go::BM - 1) / go::BM, tiles_n = (N + go::BN - 1) / go::BN;
+  const int tiles_m = (M + go::BMT - 1) / go::BMT, tiles_n = (N + go::BN - 1) / go::BN;
   const int64_t work = static_cast<int64_t>(tiles_m) * (static_cast<int64_t>(g.n1) * g.s1 +
                                                         static_cast<int64_t>(tiles_n - g.n1) * g.s2);
   if (work >= (int64_t(1) << 31) - 256) return hipErrorInvalidValue;
