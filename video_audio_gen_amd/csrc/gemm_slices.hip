@@ -410,7 +410,7 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
       const int col = odd ? gn - 1 : gn;
 #pragma unroll
       for (int e = 0; e < 16; e += 2) {
-        if (e >= ne) break;
+        if (e >= ne) continue;  // uniform; e stays a constant
         const int gm = m0 + wr + 8 * (e >> 2) + 4 * lg + (e & 3);
         const double v0 = value(e), v1 = value(e + 1);
         const double recv = xor_lane<1>(odd ? v0 : v1);
@@ -431,7 +431,7 @@ __global__ __launch_bounds__(go::NT) void gemm_f32_kernel(int M, int N, int Kp,
     if (gn >= N) continue;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      if (e >= ne) break;
+      if (e >= ne) continue;  // uniform; e stays a constant
       const int gm = m0 + wr + 8 * (e >> 2) + 4 * lg + (e & 3);
       if (gm >= M) continue;
       const double v = value(e);
