@@ -49,10 +49,13 @@ def test_gemm_bf16(dit, M, N, K):
 
 
 # (172, 20480, 2560): the music model's MLP-in projection; (60, 6144, 16384):
-# a long K with several splits.
+# a long K with several splits.  Tiles are 176 rows, the last 16 of them a
+# block that runs two slices per MFMA: M = 160, 175, 176, 177, 352, 353, 528
+# put the matrix end before, inside, at and past that block and tile edges.
 @pytest.mark.parametrize("M,N,K", [(1, 4, 4), (100, 70, 36), (172, 2560, 2560), (172, 2560, 10240), (160, 1024, 128),
                                    (400, 300, 96), (70, 130, 20000), (172, 20480, 2560), (60, 6144, 16384),
-                                   (37, 33, 64), (173, 97, 2560)])
+                                   (37, 33, 64), (173, 97, 2560), (175, 64, 96), (176, 130, 64), (177, 66, 128),
+                                   (352, 64, 64), (353, 70, 160), (528, 128, 96)])
 def test_gemm_f32_int8_slices(dit, M, N, K):
     rng = np.random.default_rng(M * 7 + N + K)
     A = rng.standard_normal((M, K)).astype(np.float32)
