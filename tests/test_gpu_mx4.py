@@ -177,9 +177,10 @@ C4_MX4_SMALL = scaled(S.get_config("c4_mxfp4"), n_blocks=2,
 
 def test_c3_block_mxfp4_parity(H):
     cfg = C3_MX4_SMALL
+    H.dit.dit_counters_reset()  # the launch counts below are this forward's alone
     r, w, got = _run(H, cfg)
     c = H.dit.dit_counters()
-    assert c["gemm_mx4"] >= 4 and c["gemm_mx8"] == 0
+    assert c["gemm_mx4"] == 4 * cfg.n_blocks and c["gemm_mx8"] == 0 and c["quantize_mx8"] == cfg.n_blocks
     ref = _oracle(cfg, w, r.inp)
     ctl = _oracle(cfg, w, r.inp, accum=MX_CONTROL)
     assert_bf16_parity(got["x"], ref["x"], ctl["x"], "c3 block mxfp4 (320 tokens)")
