@@ -48,6 +48,12 @@ static_assert(gb::WN == 64 && gb::BN % 64 == 0, "the SiLU-gate epilogue pairs a 
 // FP4 B tile rows of four chunks: chunk c of row r at r*4 + (c ^ ((r / 4) % 4)).
 __device__ __forceinline__ int gb_swz4(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
 enum GemmFormat { kGemmBf16 = 0, kGemmMx8 = 1, kGemmMx4 = 2 };
+// bf16 results staged through LDS before their 16-byte stores: 16-byte chunk
+// c of tile row r at c ^ (4 * ((r & 1) | ((r >> 1) & 2))).  One write
+// instruction of the MFMA layout covers rows r, r+1, r+4, r+5 (r = 0 or 2 mod
+// 8) at four consecutive chunks 4k .. 4k+3 each; the xor sends the four rows
+// to four different 64-byte bank groups.
+__device__ __forceinline__ int gb_stage_chunk(int r, int c) { return c ^ (4 * ((r & 1) | ((r >> 1) & 2))); }
 
 
 // Tiles move HBM -> LDS with buffer_load_dwordx4 ... lds (no VGPR staging, no
@@ -355,40 +361,97 @@ __device__ __forceinline__ void gemm_tile_body(int M, int N, int K, const void* 
   // Rows e and e+1 are adjacent, so lane pairs (2c, 2c+1) swap one value and
   // store two adjacent columns each (measured: 1.7-2.9% off the four block
   // GEMMs against one 2- or 4-byte store per element).
+  // bf16 results go through LDS (free: every wave is past its last read of
+  // the ring) so that each lane stores 16 bytes and each store instruction
+  // writes whole rows of the tile: from the MFMA layout a lane could store
+  // only 4 bytes, and an instruction wrote 64-byte pieces of four rows (the
+  // epilogue took ~7 us of a 256 x 256 tile's ~150).
+  char* const st_lds = reinterpret_cast<char*>(smem);
+  auto stage_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_s_barrier();
+  };
+  static_assert(sizeof(smem) >= BM * (BN / 2) * 2, "the SiLU-gate epilogue stages 256 rows x 128 bf16 features");
   if (ep.mode == kEpiSiluGate) {
     // Columns come in 64-wide groups [32 gate | 32 up] of the same 32 MLP
     // features (the staged row order), so a wave's two 32-column tiles hold
     // the gate and the up value of one output: both rounded to bf16 as a
-    // stored u would be, then silu(g) * up in fp32, rounded to bf16.
+    // stored u would be, then silu(g) * up in fp32, rounded to bf16.  The
+    // tile's 128 features of a row (256 bytes, 16 chunks) are staged, then
+    // stored by rows.
+    const int F = N >> 1;
     const int gn = n0 + wc + lr;  // gate column; its up column is gn + 32
-    if (gn < N) {
-      const int F = N >> 1;
-      const int f = ((n0 + wc) >> 1) + lr;
-      const float bg = bias != nullptr ? bias[gn] : 0.f;
-      const float bu = bias != nullptr ? bias[gn + 32] : 0.f;
-      bf16_t* Mo = static_cast<bf16_t*>(Cv);
-      // feature pairs (F is a multiple of 32): lanes 2c and 2c+1 trade one
-      // value so each stores two adjacent outputs of its row in 4 bytes
-      const bool odd = lane & 1;
+    const float bg = bias != nullptr && gn < N ? bias[gn] : 0.f;
+    const float bu = bias != nullptr && gn < N ? bias[gn + 32] : 0.f;
+    const int fl = (wc >> 1) + lr;  // feature within the tile
+    // feature pairs: lanes 2c and 2c+1 trade one value so each writes two
+    // adjacent outputs of its row in 4 bytes
+    const bool odd = lane & 1;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        const int r = wr + i * 32 + 8 * (e >> 2) + 4 * lg + (e & 3);
+        float mv[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float g = bf16_to_f32(f32_to_bf16(acc[i][0][e + h] + bg));
+          const float u = bf16_to_f32(f32_to_bf16(acc[i][1][e + h] + bu));
+          mv[h] = g / (1.0f + expf(-g)) * u;
+        }
+        const float recv = xor_lane<1>(odd ? mv[0] : mv[1]);
+        const int row = odd ? r + 1 : r;
+        const int f = odd ? fl - 1 : fl;
+        *reinterpret_cast<uint32_t*>(st_lds + row * 256 + gb_stage_chunk(row, f >> 3) * 16 + (f & 7) * 2) =
+            odd ? pack_bf16x2(recv, mv[1]) : pack_bf16x2(mv[0], recv);
+      }
+    }
+    stage_barrier();
+    bf16_t* Mo = static_cast<bf16_t*>(Cv);
+    const int f0 = n0 >> 1;
+#pragma unroll
+    for (int p = 0; p < BM * 16 / NT; ++p) {
+      const int row = p * (NT / 16) + (tid >> 4), k = tid & 15;
+      const uint4 v = *reinterpret_cast<const uint4*>(st_lds + row * 256 + gb_stage_chunk(row, k) * 16);
+      if (m0 + row < M && f0 + 8 * k < F)
+        *reinterpret_cast<uint4*>(Mo + static_cast<size_t>(m0 + row) * F + f0 + 8 * k) = v;
+    }
+    return;
+  }
+  // (the whole bf16 tile, 128 KB, fits the ring of the bf16 and MXFP8 forms;
+  // the MXFP4 form's 98 KB ring keeps the direct stores below)
+  constexpr bool kStageTile = sizeof(smem) >= BM * BN * 2;
+  if (kStageTile && ep.mode == kEpiBf16 && (N & 7) == 0 && (reinterpret_cast<uintptr_t>(Cv) & 15) == 0) {
+    // The tile's 256 columns of a row (512 bytes, 32 chunks) staged, then
+    // stored by rows; lanes 2c and 2c+1 trade one value as below.
+    const bool odd = lane & 1;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int gn = n0 + wc + j * 32 + lr;
+      const float bv = bias != nullptr && gn < N ? bias[gn] : 0.f;
+      const int col = wc + j * 32 + (odd ? lr - 1 : lr);
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
 #pragma unroll
         for (int e = 0; e < 16; e += 2) {
-          const int gm = m0 + wr + i * 32 + 8 * (e >> 2) + 4 * lg + (e & 3);
-          float mv[2];
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const float g = bf16_to_f32(f32_to_bf16(acc[i][0][e + h] + bg));
-            const float u = bf16_to_f32(f32_to_bf16(acc[i][1][e + h] + bu));
-            mv[h] = g / (1.0f + expf(-g)) * u;
-          }
-          const float recv = xor_lane<1>(odd ? mv[0] : mv[1]);
-          const int row = odd ? gm + 1 : gm;
-          if (row < M)
-            *reinterpret_cast<uint32_t*>(Mo + static_cast<size_t>(row) * F + (odd ? f - 1 : f)) =
-                odd ? pack_bf16x2(recv, mv[1]) : pack_bf16x2(mv[0], recv);
+          const int r = wr + i * 32 + 8 * (e >> 2) + 4 * lg + (e & 3);
+          const float v0 = acc[i][j][e] + bv, v1 = acc[i][j][e + 1] + bv;
+          const float recv = xor_lane<1>(odd ? v0 : v1);
+          const int row = odd ? r + 1 : r;
+          const float lo = odd ? recv : v0, hi = odd ? v1 : recv;
+          *reinterpret_cast<uint32_t*>(st_lds + row * 512 + gb_stage_chunk(row, col >> 3) * 16 + (col & 7) * 2) =
+              pack_bf16x2(lo, hi);
         }
       }
+    }
+    stage_barrier();
+    bf16_t* Co = static_cast<bf16_t*>(Cv);
+#pragma unroll
+    for (int p = 0; p < BM * 32 / NT; ++p) {
+      const int row = p * (NT / 32) + (tid >> 5), k = tid & 31;
+      const uint4 v = *reinterpret_cast<const uint4*>(st_lds + row * 512 + gb_stage_chunk(row, k) * 16);
+      if (m0 + row < M && n0 + 8 * k < N)
+        *reinterpret_cast<uint4*>(Co + static_cast<size_t>(m0 + row) * N + n0 + 8 * k) = v;
     }
     return;
   }
@@ -483,7 +546,8 @@ size_t gemm_bf16_ws_bytes(int, int, int) { return 0; }
 hipError_t gemm_bf16(int M, int N, int K, const uint16_t* A, const uint16_t* B, const float* bias,
                      void* C, const GemmEpilogue& ep, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  if (ep.mode == kEpiSiluGate && N % 64 != 0) return hipErrorInvalidValue;
+  // SiLU-gate output rows are stored in 16-byte pieces
+  if (ep.mode == kEpiSiluGate && (N % 64 != 0 || (reinterpret_cast<uintptr_t>(C) & 15) != 0)) return hipErrorInvalidValue;
   LaunchScope scope_(kCntGemmBf16, s);
   const int tiles_m = (M + gb::BM - 1) / gb::BM, tiles_n = (N + gb::BN - 1) / gb::BN;
   // Tile order from the shapes (measured on the 6144-wide block's GEMMs at
@@ -506,7 +570,8 @@ bool gemm_mx8_supported(int M, int N, int K) {
 hipError_t gemm_mx8(int M, int N, int K, const uint8_t* A, const uint8_t* Asc, const uint8_t* B, const uint8_t* Bsc,
                     const float* bias, void* C, const GemmEpilogue& ep, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  if (ep.mode == kEpiSiluGate && N % 64 != 0) return hipErrorInvalidValue;
+  // SiLU-gate output rows are stored in 16-byte pieces
+  if (ep.mode == kEpiSiluGate && (N % 64 != 0 || (reinterpret_cast<uintptr_t>(C) & 15) != 0)) return hipErrorInvalidValue;
   LaunchScope scope_(kCntGemmMx8, s);
   const int tiles_m = (M + gb::BM - 1) / gb::BM, tiles_n = (N + gb::BN - 1) / gb::BN;
   // tile order as the bf16 GEMM's, with A's bytes at one per value
@@ -523,7 +588,8 @@ hipError_t gemm_mx8(int M, int N, int K, const uint8_t* A, const uint8_t* Asc, c
 hipError_t gemm_mx4(int M, int N, int K, const uint8_t* A, const uint8_t* Asc, const uint8_t* B, const uint8_t* Bsc,
                     const float* bias, void* C, const GemmEpilogue& ep, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  if (ep.mode == kEpiSiluGate && N % 64 != 0) return hipErrorInvalidValue;
+  // SiLU-gate output rows are stored in 16-byte pieces
+  if (ep.mode == kEpiSiluGate && (N % 64 != 0 || (reinterpret_cast<uintptr_t>(C) & 15) != 0)) return hipErrorInvalidValue;
   LaunchScope scope_(kCntGemmMx4, s);
   const int tiles_m = (M + gb::BM - 1) / gb::BM, tiles_n = (N + gb::BN - 1) / gb::BN;
   const double a_bytes = 1.0 * M * K;
