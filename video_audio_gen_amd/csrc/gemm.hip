@@ -418,40 +418,48 @@ __device__ __forceinline__ void gemm_tile_body(int M, int N, int K, const void* 
     }
     return;
   }
-  // (the whole bf16 tile, 128 KB, fits the ring of the bf16 and MXFP8 forms;
-  // the MXFP4 form's 98 KB ring keeps the direct stores below)
-  constexpr bool kStageTile = sizeof(smem) >= BM * BN * 2;
-  if (kStageTile && ep.mode == kEpiBf16 && (N & 7) == 0 && (reinterpret_cast<uintptr_t>(Cv) & 15) == 0) {
+  // The tile goes through LDS in passes of RP rows: the whole tile (128 KB)
+  // in the bf16 and MXFP8 forms' rings, halves in the MXFP4 form's 98 KB one.
+  constexpr int RP = sizeof(smem) >= BM * BN * 2 ? BM : BM / 2;
+  static_assert(RP % WM == 0 || WM % RP == 0, "a pass holds whole row blocks of the waves");
+  if (ep.mode == kEpiBf16 && (N & 7) == 0 && (reinterpret_cast<uintptr_t>(Cv) & 15) == 0) {
     // The tile's 256 columns of a row (512 bytes, 32 chunks) staged, then
     // stored by rows; lanes 2c and 2c+1 trade one value as below.
     const bool odd = lane & 1;
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int gn = n0 + wc + j * 32 + lr;
-      const float bv = bias != nullptr && gn < N ? bias[gn] : 0.f;
-      const int col = wc + j * 32 + (odd ? lr - 1 : lr);
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-#pragma unroll
-        for (int e = 0; e < 16; e += 2) {
-          const int r = wr + i * 32 + 8 * (e >> 2) + 4 * lg + (e & 3);
-          const float v0 = acc[i][j][e] + bv, v1 = acc[i][j][e + 1] + bv;
-          const float recv = xor_lane<1>(odd ? v0 : v1);
-          const int row = odd ? r + 1 : r;
-          const float lo = odd ? recv : v0, hi = odd ? v1 : recv;
-          *reinterpret_cast<uint32_t*>(st_lds + row * 512 + gb_stage_chunk(row, col >> 3) * 16 + (col & 7) * 2) =
-              pack_bf16x2(lo, hi);
-        }
-      }
-    }
-    stage_barrier();
     bf16_t* Co = static_cast<bf16_t*>(Cv);
 #pragma unroll
-    for (int p = 0; p < BM * 32 / NT; ++p) {
-      const int row = p * (NT / 32) + (tid >> 5), k = tid & 31;
-      const uint4 v = *reinterpret_cast<const uint4*>(st_lds + row * 512 + gb_stage_chunk(row, k) * 16);
-      if (m0 + row < M && n0 + 8 * k < N)
-        *reinterpret_cast<uint4*>(Co + static_cast<size_t>(m0 + row) * N + n0 + 8 * k) = v;
+    for (int pass = 0; pass < BM / RP; ++pass) {
+      if (pass > 0) stage_barrier();  // the previous pass's rows have been read
+      if (wr / RP == pass) {          // uniform: this wave's rows are in the pass
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int gn = n0 + wc + j * 32 + lr;
+          const float bv = bias != nullptr && gn < N ? bias[gn] : 0.f;
+          const int col = wc + j * 32 + (odd ? lr - 1 : lr);
+#pragma unroll
+          for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int e = 0; e < 16; e += 2) {
+              const int r = wr - pass * RP + i * 32 + 8 * (e >> 2) + 4 * lg + (e & 3);
+              const float v0 = acc[i][j][e] + bv, v1 = acc[i][j][e + 1] + bv;
+              const float recv = xor_lane<1>(odd ? v0 : v1);
+              const int row = odd ? r + 1 : r;
+              const float lo = odd ? recv : v0, hi = odd ? v1 : recv;
+              *reinterpret_cast<uint32_t*>(st_lds + row * 512 + gb_stage_chunk(row, col >> 3) * 16 + (col & 7) * 2) =
+                  pack_bf16x2(lo, hi);
+            }
+          }
+        }
+      }
+      stage_barrier();
+#pragma unroll
+      for (int p = 0; p < RP * 32 / NT; ++p) {
+        const int row = p * (NT / 32) + (tid >> 5), k = tid & 31;
+        const uint4 v = *reinterpret_cast<const uint4*>(st_lds + row * 512 + gb_stage_chunk(row, k) * 16);
+        const int grow = m0 + pass * RP + row;
+        if (grow < M && n0 + 8 * k < N)
+          *reinterpret_cast<uint4*>(Co + static_cast<size_t>(grow) * N + n0 + 8 * k) = v;
+      }
     }
     return;
   }
