@@ -837,7 +837,8 @@ static int run_block_bf16(dit_model* m, int blk, float* x, const float* mod, con
 }
 
 // fp32 stream, x the float64 residual.  Each GEMM reads its input as int8
-// slices and leaves fp64 split-K partials that the next row kernel sums:
+// slices and leaves fp64 split-K partials that the next row kernel sums (one-
+// split column groups finished as fp32, the bias added by the GEMM):
 //   (slices of the attention norm, made by the previous block or f32_prologue)
 //   QKV GEMM -> rope_part -> attention -> slice_rows -> O GEMM ->
 //   resid_norm_slice (gate MSA, MLP norm) -> in GEMM -> silu_slice -> out GEMM ->

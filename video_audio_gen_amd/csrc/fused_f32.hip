@@ -2,9 +2,11 @@
 // leaves fp64 split-K partials; the kernel after it sums them in split order,
 // adds the bias and rounds once to fp32 (the value a stand-alone reduction
 // would store), applies its own operation and, where the next GEMM reads the
-// result, cuts that GEMM's int8 slices directly (slices.h).  A block then runs
-// 11 launches instead of 17, and the fp32 GEMM outputs, the modulated norms
-// and the SiLU product never make a round trip through HBM as fp32.
+// result, cuts that GEMM's int8 slices directly (slices.h).  Columns the
+// GEMM's split plan gives one split arrive already finished (the same
+// rounding, done by the GEMM) as 4-byte floats.  A block then runs 11
+// launches instead of 17, and the modulated norms and the SiLU product never
+// make a round trip through HBM as fp32.
 //
 //   resid_norm_slice  x += gate * a (fp64 residual), then the AdaLN-modulated
 //                     norm of the next sub-layer, sliced; or the plain final
