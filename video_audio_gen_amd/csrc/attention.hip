@@ -485,7 +485,10 @@ __global__ __launch_bounds__(af::NT) void attention_f32_kernel(int N, int H, con
   __syncthreads();  // K/V space free
   double* mw = reinterpret_cast<double*>(KVs);       // [NW][QT]
   double* lw = mw + NW * QT;                          // [NW][QT]
-  double* ow = lw + NW * QT;                          // [NW][HD][QT]
+  // [NW][HD][QT], query slot qq of dim d at qq ^ (d % 16): the merge below
+  // reads 64 consecutive dims of one query, which would otherwise all fall 128
+  // bytes apart on the same banks
+  double* ow = lw + NW * QT;
   if (g == 0) {
     mw[wave * QT + r16] = m_run;
     lw[wave * QT + r16] = l_w;
@@ -493,7 +496,7 @@ __global__ __launch_bounds__(af::NT) void attention_f32_kernel(int N, int H, con
 #pragma unroll
   for (int b = 0; b < NDB; ++b)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ow[(wave * HD + b * 16 + 4 * i + g) * QT + r16] = acc[b][i];
+    for (int i = 0; i < 4; ++i) ow[(wave * HD + b * 16 + 4 * i + g) * QT + (r16 ^ (4 * i + g))] = acc[b][i];
   __syncthreads();
   // Per query: each wavefront's factor exp(m_w - m) (0 for a wavefront that saw
   // no key of the document) and the merged denominator, once per query.
@@ -522,7 +525,7 @@ __global__ __launch_bounds__(af::NT) void attention_f32_kernel(int N, int H, con
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       if (mw[w * QT + qq] == -INFINITY) continue;
-      num += fw[w * QT + qq] * ow[(w * HD + dim) * QT + qq];
+      num += fw[w * QT + qq] * ow[(w * HD + dim) * QT + (qq ^ (dim & 15))];
     }
     o[static_cast<size_t>(s0 + q0 + qq) * H * HD + static_cast<size_t>(h) * HD + dim] = static_cast<float>(num / dw[qq]);
   }
